@@ -1,0 +1,377 @@
+"""fp64 reference implementation of the DiT denoiser forward pass.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Every array is
+converted to float64 on entry; no intermediate rounding is applied.  Library
+primitives used as steps: numpy matmul, exp, tanh, sin, cos, sqrt.
+
+Citations use the page keys listed in ``oracle/__init__.py``.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Patchify / unpatchify
+# [DiT-wiki] Structure / Latent space and patchify: an I x I x C latent is cut
+# into p x p patches, each linearly mapped to a d-dim token, T = (I/p)^2; the
+# decoder emits p x p x 2C values per token that are put back in the spatial
+# layout.  [Sora-obs] Architecture details / spacetime patch tokenisation:
+# video latents are cut into (time x height x width) patches.
+# Reading taken: raster token order over (frame, row, col); patch vector order
+# (frame offset, row offset, col offset, channel) with channel fastest, at
+# both ends.
+
+def token_grid(F, H, W, p, pt=1):
+    """(frames, rows, cols) of the token grid."""
+    if F % pt or H % p or W % p:
+        raise ValueError("latent extent not divisible by the patch size")
+    return F // pt, H // p, W // p
+
+
+def patchify(x, p, pt=1):
+    """x: [B, C, H, W] or [B, C, F, H, W]  ->  P: [B, T, pt*p*p*C].
+
+    P[b, (f*gh + i)*gw + j, ((a*p + py)*p + px)*C + c]
+        = x[b, c, f*pt + a, i*p + py, j*p + px]
+    """
+    x = np.asarray(x)
+    if x.ndim == 4:
+        x = x[:, :, None]
+    B, C, F, H, W = x.shape
+    gf, gh, gw = token_grid(F, H, W, p, pt)
+    v = x.reshape(B, C, gf, pt, gh, p, gw, p)
+    # -> [B, gf, gh, gw, pt, py, px, C]
+    v = v.transpose(0, 2, 4, 6, 3, 5, 7, 1)
+    return np.ascontiguousarray(v.reshape(B, gf * gh * gw, pt * p * p * C))
+
+
+def unpatchify(Y, Cout, F, H, W, p, pt=1, frames_axis=None):
+    """Y: [B, T, pt*p*p*Cout] -> out [B, Cout, H, W] (F == 1 and
+    frames_axis falsy) or [B, Cout, F, H, W].  Inverse index map of
+    :func:`patchify`."""
+    Y = np.asarray(Y)
+    B = Y.shape[0]
+    gf, gh, gw = token_grid(F, H, W, p, pt)
+    v = Y.reshape(B, gf, gh, gw, pt, p, p, Cout)
+    # -> [B, Cout, gf, pt, gh, py, gw, px]
+    v = v.transpose(0, 7, 1, 4, 2, 5, 3, 6)
+    out = np.ascontiguousarray(v.reshape(B, Cout, F, H, W))
+    if frames_axis is None:
+        frames_axis = F > 1
+    return out if frames_axis else out[:, :, 0]
+
+
+# ---------------------------------------------------------------------------
+# Embeddings
+
+def timestep_embedding(t, dim=256, max_period=10000.0):
+    """[Sora-cvl] / [DiT-wiki] adaLN-Zero: c is the sum of a timestep
+    embedding and a class embedding.  The pages give no formula; the reading
+    taken is the 256-dim sinusoid [cos(t f_k) | sin(t f_k)] with
+    f_k = max_period^(-k/(dim/2)), k = 0..dim/2-1, t used as given."""
+    t = _f64(t).reshape(-1)
+    half = dim // 2
+    k = np.arange(half, dtype=np.float64)
+    freqs = np.exp(-math.log(max_period) * k / half)
+    args = t[:, None] * freqs[None, :]
+    return np.concatenate([np.cos(args), np.sin(args)], axis=1)
+
+
+def pos_embed_2d(gh, gw, d):
+    """[DiT-wiki] Structure / Latent space and patchify, and [Sora-cvl]
+    Method (patchify bullet): ViT-style fixed 2-D sine-cosine position
+    embedding added to every token.  Reading taken: d/4 frequencies
+    w_k = 10000^(-k/(d/4)); token (i, j) gets
+    [sin(i w) | cos(i w) | sin(j w) | cos(j w)], row axis first."""
+    if d % 4:
+        raise ValueError("d must be a multiple of 4")
+    dq = d // 4
+    omega = 1.0 / 10000.0 ** (np.arange(dq, dtype=np.float64) / dq)
+    ii, jj = np.meshgrid(np.arange(gh, dtype=np.float64),
+                         np.arange(gw, dtype=np.float64), indexing="ij")
+    i = ii.reshape(-1)[:, None] * omega[None, :]
+    j = jj.reshape(-1)[:, None] * omega[None, :]
+    return np.concatenate([np.sin(i), np.cos(i), np.sin(j), np.cos(j)], axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Elementwise pieces
+
+def layer_norm(z, eps=1e-6):
+    """[DiT-wiki] adaLN-Zero: LN has no learnable affine parameters;
+    Implementation / adaLN-Zero block: eps = 1e-6.  Biased variance over the
+    last axis, eps inside the square root."""
+    z = _f64(z)
+    mu = z.mean(axis=-1, keepdims=True)
+    var = ((z - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (z - mu) / np.sqrt(var + eps)
+
+
+def modulate(h, shift, scale):
+    """[DiT-wiki] adaLN-Zero equations: LN(x)(1 + gamma) + beta, the same
+    (gamma, beta) for every token of a row.  h: [B, T, d]; shift, scale:
+    [B, d]."""
+    return h * (1.0 + scale[:, None, :]) + shift[:, None, :]
+
+
+def silu(z):
+    z = _f64(z)
+    return z / (1.0 + np.exp(-z))
+
+
+def gelu_tanh(z):
+    """[DiT-wiki] Implementation / adaLN-Zero block: the MLP uses the
+    tanh-approximate GELU."""
+    z = _f64(z)
+    return 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
+
+
+def linear(x, w, b=None):
+    """x @ w.T + b with w stored [out, in]."""
+    y = _f64(x) @ _f64(w).T
+    if b is not None:
+        y = y + _f64(b)
+    return y
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# [DiT-wiki] Implementation / adaLN-Zero block: nn.MultiheadAttention(d, heads),
+# i.e. packed q|k|v projection with bias, per-head softmax(q k^T / sqrt(dh)) v,
+# heads as contiguous dh-slices, output projection with bias.  [Goku] 2.2:
+# full attention over every spacetime token.
+
+def attention(q, k, v, q_chunk=2048):
+    """q, k, v: [B, H, T, dh] -> [B, H, T, dh].  Queries are processed in
+    chunks only to bound memory; each query row's arithmetic is unchanged."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hh, T, dh = q.shape
+    out = np.empty_like(q)
+    scale = 1.0 / math.sqrt(dh)
+    for b in range(B):
+        for h in range(Hh):
+            kt = k[b, h].T
+            for s in range(0, T, q_chunk):
+                e = min(T, s + q_chunk)
+                sc = (q[b, h, s:e] @ kt) * scale
+                sc = sc - sc.max(axis=1, keepdims=True)
+                pr = np.exp(sc)
+                pr /= pr.sum(axis=1, keepdims=True)
+                out[b, h, s:e] = pr @ v[b, h]
+    return out
+
+
+def qk_layernorm(x, eps=1e-6):
+    """[Goku] 2.2 Q-K normalisation (the variant [DiT-wiki] MMDiT names is
+    RMSNorm).  Reading taken: LayerNorm without affine over each head's
+    dh-vector, eps 1e-6, applied to q and k before the rotary embedding."""
+    return layer_norm(x, eps)
+
+
+def rope3d_tables(gf, gh, gw, dh, base=10000.0):
+    """cos/sin tables [T, dh/2] for the 3-D rotary embedding.
+
+    [Goku] 2.2 3D RoPE over (time, height, width).  Reading taken: dh is
+    split into three equal segments (frame, row, col) of size da = dh/3
+    (even); pair k of a segment rotates by angle pos * base^(-2k/da), with
+    integer positions; pairs are adjacent elements (x_2k, x_2k+1)."""
+    if dh % 6:
+        raise ValueError("3-D RoPE needs dh divisible by 6")
+    da = dh // 3
+    theta = base ** (-2.0 * np.arange(da // 2, dtype=np.float64) / da)
+    ff, ii, jj = np.meshgrid(np.arange(gf, dtype=np.float64),
+                             np.arange(gh, dtype=np.float64),
+                             np.arange(gw, dtype=np.float64), indexing="ij")
+    pos = [ff.reshape(-1), ii.reshape(-1), jj.reshape(-1)]
+    ang = np.concatenate([p[:, None] * theta[None, :] for p in pos], axis=1)
+    return np.cos(ang), np.sin(ang)
+
+
+def rope3d(x, cos, sin):
+    """x: [B, H, T, dh]; cos/sin: [T, dh/2].  Rotates pairs (x_2k, x_2k+1)."""
+    x = _f64(x)
+    xe = x[..., 0::2]
+    xo = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = xe * cos - xo * sin
+    out[..., 1::2] = xe * sin + xo * cos
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Conditioning
+
+def embed_condition(cfg, w, t, y=None, pooled=None):
+    """c = t_emb + y_emb (+ pooled projection).
+
+    [DiT-wiki] adaLN-Zero: c is the sum of the time embedding and the class
+    embedding; [Sora-cvl] Method (CFG bullet): the null label is a class of its
+    own; [DiT-wiki] MMDiT: a pooled vector and the time embedding enter through
+    adaLN.  Readings taken: t_emb = Linear(d,d)(SiLU(Linear(256,d)(e(t))));
+    the class table has num_classes + 1 rows, the last being the null label;
+    the pooled vector enters through one Linear(cond_dim, d).
+    Returns (e, t_emb, c)."""
+    e = timestep_embedding(t, cfg["freq_dim"])
+    temb = linear(silu(linear(e, w["t1_w"], w["t1_b"])), w["t2_w"], w["t2_b"])
+    c = temb.copy()
+    if cfg["num_classes"] > 0:
+        y = np.asarray(y).astype(np.int64)
+        if np.any(y < 0) or np.any(y > cfg["num_classes"]):
+            raise ValueError("class label out of range")
+        c = c + _f64(w["y_table"])[y]
+    if cfg["cond_dim"] > 0:
+        c = c + linear(pooled, w["pool_w"], w["pool_b"])
+    return e, temb, c
+
+
+def modulation(cfg, w, c):
+    """[DiT-wiki] adaLN-Zero: (beta1, gamma1, alpha1, beta2, gamma2, alpha2)
+    = MLP(c); Implementation: the MLP is SiLU followed by Linear(d, 6d).
+    All blocks' rows and the final layer's (beta_f, gamma_f) rows are stacked
+    in one weight.  Returns [B, (6N+2) d]."""
+    return linear(silu(c), w["ada_w"], w["ada_b"])
+
+
+# ---------------------------------------------------------------------------
+# Transformer block
+
+def block(cfg, wl, X, mod_l, rope=None):
+    """One adaLN-Zero DiT block.
+
+    [DiT-wiki] adaLN-Zero equations:
+        x <- x + alpha1 * Attn(LN(x)(1 + gamma1) + beta1)
+        x <- x + alpha2 * FFN(LN(x)(1 + gamma2) + beta2)
+    with the six vectors in the order (beta1, gamma1, alpha1, beta2, gamma2,
+    alpha2) (same page, Implementation / adaLN-Zero block: shift, scale, gate
+    twice).  FFN = Linear(d, 4d), tanh-GELU, Linear(4d, d).
+
+    wl: dict with qkv_w [3d,d], qkv_b, o_w, o_b, fc1_w, fc1_b, fc2_w, fc2_b.
+    X: [B, T, d]; mod_l: [B, 6d].  Returns (X_out, o, f) where o and f are the
+    attention and FFN branches before their gates.
+    """
+    X = _f64(X)
+    B, T, d = X.shape
+    Hh = cfg["heads"]
+    dh = d // Hh
+    eps = cfg["ln_eps"]
+    sh1, sc1, g1, sh2, sc2, g2 = np.split(_f64(mod_l), 6, axis=1)
+
+    h = modulate(layer_norm(X, eps), sh1, sc1)
+    qkv = linear(h, wl["qkv_w"], wl["qkv_b"])
+    q, k, v = (qkv[..., i * d:(i + 1) * d].reshape(B, T, Hh, dh).transpose(0, 2, 1, 3)
+               for i in range(3))
+    if cfg["qk_norm"]:
+        q, k = qk_layernorm(q, eps), qk_layernorm(k, eps)
+    if cfg["rope3d"]:
+        cos, sin = rope
+        q, k = rope3d(q, cos, sin), rope3d(k, cos, sin)
+    a = attention(q, k, v).transpose(0, 2, 1, 3).reshape(B, T, d)
+    o = linear(a, wl["o_w"], wl["o_b"])
+    X = X + g1[:, None, :] * o
+
+    h = modulate(layer_norm(X, eps), sh2, sc2)
+    f = linear(gelu_tanh(linear(h, wl["fc1_w"], wl["fc1_b"])), wl["fc2_w"], wl["fc2_b"])
+    X = X + g2[:, None, :] * f
+    return X, o, f
+
+
+def block_weights(w, l):
+    return {k: w[k][l] for k in ("qkv_w", "qkv_b", "o_w", "o_b", "fc1_w", "fc1_b",
+                                 "fc2_w", "fc2_b")}
+
+
+# ---------------------------------------------------------------------------
+# Whole denoiser
+
+def forward(cfg, w, x_t, t, y=None, pooled=None, taps=None, blocks=None):
+    """eps_theta(x_t, t, c) for a batch of rows.
+
+    [Sora-cvl] Method and architecture; [DiT-wiki] Structure: patchify +
+    linear embedding + position embedding, N adaLN-Zero blocks, final norm
+    followed by a linear decoder to p x p x 2C per token, unpatchify.
+    Reading taken for the final layer: LayerNorm (no affine), adaLN modulate
+    with (beta_f, gamma_f) regressed from c, then Linear(d, p*p*Cout).
+    Video ([Goku] 2.2): no additive position embedding; 3-D RoPE and QK
+    normalisation inside attention.
+
+    x_t: [B, C, H, W] or [B, C, F, H, W]; t: [B]; y: [B] ints in
+    [0, num_classes] (num_classes is the null label); pooled: [B, cond_dim].
+    ``taps`` (a dict) receives intermediate tensors.  ``blocks`` limits the
+    number of blocks run (default: all N).
+    Returns out [B, Cout, H, W] or [B, Cout, F, H, W].
+    """
+    x = _f64(x_t)
+    video = x.ndim == 5
+    x5 = x if video else x[:, :, None]
+    B = x5.shape[0]
+    C, F, H, W = cfg["C"], cfg["F"], cfg["H"], cfg["W"]
+    p, pt, d, N = cfg["p"], cfg["pt"], cfg["d"], cfg["N"]
+    if x5.shape[1:] != (C, F, H, W):
+        raise ValueError(f"x_t shape {x.shape} does not match the config")
+    gf, gh, gw = token_grid(F, H, W, p, pt)
+
+    P = patchify(x5, p, pt)
+    X = linear(P, w["pe_w"], w["pe_b"])
+    rope = None
+    if cfg["rope3d"]:
+        rope = rope3d_tables(gf, gh, gw, d // cfg["heads"])
+    else:
+        if gf != 1:
+            raise ValueError("2-D position embedding needs a single frame")
+        X = X + pos_embed_2d(gh, gw, d)[None]
+
+    e, temb, c = embed_condition(cfg, w, t, y, pooled)
+    mod = modulation(cfg, w, c)
+    if taps is not None:
+        taps.update(e=e, temb=temb, c=c, mod=mod, X0=X.copy(), X=[], o=[], f=[])
+
+    nb = N if blocks is None else blocks
+    for l in range(nb):
+        X, o, f = block(cfg, block_weights(w, l), X, mod[:, 6 * d * l:6 * d * (l + 1)], rope)
+        if taps is not None:
+            taps["X"].append(X.copy())
+            taps["o"].append(o)
+            taps["f"].append(f)
+
+    shf = mod[:, 6 * d * N:6 * d * N + d]
+    scf = mod[:, 6 * d * N + d:6 * d * N + 2 * d]
+    Hf = modulate(layer_norm(X, cfg["ln_eps"]), shf, scf)
+    Y = linear(Hf, w["out_w"], w["out_b"])
+    out = unpatchify(Y, cfg["Cout"], F, H, W, p, pt, frames_axis=video)
+    if taps is not None:
+        taps.update(Hf=Hf, Y=Y, out=out)
+    return out
+
+
+def cfg_combine(cond, uncond, s, guided):
+    """[Sora-cvl] Method (classifier-free guidance bullet):
+        eps_hat = eps(x, null) + s * (eps(x, c) - eps(x, null)).
+    [DiT-wiki] Results / ImageNet notes: the official code guides only the
+    first three output channels; guiding all channels is standard.  Channels
+    >= ``guided`` are taken from the conditional output."""
+    cond, uncond = _f64(cond), _f64(uncond)
+    out = cond.copy()
+    g = guided
+    out[:, :g] = uncond[:, :g] + s * (cond[:, :g] - uncond[:, :g])
+    return out
+
+
+def cfg_forward(cfg, w, x_t, t, y, s, guided, taps=None, blocks=None):
+    """Guided prediction for Bh rows: the trunk runs 2*Bh rows
+    [(x_t, t, y) ; (x_t, t, null)], then :func:`cfg_combine`."""
+    x = _f64(x_t)
+    Bh = x.shape[0]
+    t = _f64(t).reshape(-1)
+    y = np.asarray(y).astype(np.int64).reshape(-1)
+    x2 = np.concatenate([x, x], axis=0)
+    t2 = np.concatenate([t, t])
+    y2 = np.concatenate([y, np.full(Bh, cfg["num_classes"], dtype=np.int64)])
+    both = forward(cfg, w, x2, t2, y2, taps=taps, blocks=blocks)
+    return cfg_combine(both[:Bh], both[Bh:], s, guided)
