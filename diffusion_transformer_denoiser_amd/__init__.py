@@ -1,0 +1,12 @@
+"""MI355X (gfx950) DiT denoiser forward pass: a C-ABI HIP library
+(``libdit.so``, interface in ``include/dit.h``) and its Python binding.
+
+The binding only marshals arguments; every step of the forward pass runs in
+the library's kernels.  Importing the package does not load the library;
+``DiT(...)`` and the standalone functions do, and fail loudly if it has not
+been built.
+"""
+from ._lib import (DIT_BF16, DIT_EPI_BIAS, DIT_EPI_GATED, DIT_EPI_GELU, DIT_F32,  # noqa: F401
+                   DitError, load)
+from .model import (DiT, attention, config_struct, linear, patchify, timestep_embed,  # noqa: F401
+                    torch_dtype, unpatchify, upload)

@@ -1,0 +1,529 @@
+// Host side of the C ABI: configuration checks, workspace layout and the launch
+// sequence of the DiT forward pass.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "dit.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return DIT_OK;
+}
+
+#define DIT_HIP(call)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (call);                                                             \
+    if (e_ != hipSuccess) return fail(DIT_EHIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace
+
+struct dit_handle {
+  dit_config cfg;
+  dit_weights w;
+  int d, N, heads, dh, hid, ncls, cond_dim, freq, dtype, es;
+  float eps;
+  int gf, gh, gw, T, kin, kout, mod_stride;
+  PatchGeom gin, gout;
+};
+
+namespace {
+
+struct WsLayout {
+  size_t e, th, c, sc, mod, X, H, q, k, v, o, G, Y, total;
+};
+
+WsLayout ws_layout(const dit_handle* h, int rows) {
+  WsLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t es = h->es, R = (size_t)rows, M = R * h->T;
+  const size_t ldv = h->dtype == DIT_BF16 ? (size_t)round_up(h->T, 64) : (size_t)h->T;
+  L.e = take(R * h->freq * 4);
+  L.th = take(R * h->d * 4);
+  L.c = take(R * h->d * 4);
+  L.sc = take(R * h->d * es);
+  L.mod = take(R * h->mod_stride * 4);
+  L.X = take(M * h->d * 4);
+  L.H = take(M * h->d * es);
+  L.q = take(R * h->heads * h->T * h->dh * es);
+  L.k = take(R * h->heads * h->T * h->dh * es);
+  L.v = take(R * h->heads * ldv * h->dh * es);
+  L.o = take(M * h->d * es);
+  L.G = take(M * h->hid * es);
+  L.Y = take(M * h->kout * 4);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+const void* woff(const void* base, size_t elems, int es) {
+  return (const char*)base + elems * es;
+}
+
+EpiParams epi0() {
+  EpiParams ep;
+  memset(&ep, 0, sizeof ep);
+  return ep;
+}
+
+// One linear layer: MFMA for bf16, VALU for fp32.
+hipError_t linear(const dit_handle* h, int epi, const void* A, int lda, const void* W, int M,
+                  int N, int K, const EpiParams& ep, hipStream_t s) {
+  if (h->dtype == DIT_BF16)
+    return launch_gemm_mfma(epi, (const bf16_t*)A, lda, (const bf16_t*)W, M, N, K, ep, s);
+  ALoad a;
+  memset(&a, 0, sizeof a);
+  a.ptr = A;
+  a.lda = lda;
+  a.a_dtype = 0;
+  a.src_rows = M;
+  return launch_gemm_valu(epi, A_PLAIN, a, W, 0, M, N, K, ep, s);
+}
+
+// One adaLN-Zero block on the residual stream X [rows*T, d] (fp32, in place).
+// mod + base points at this block's (b1, g1, a1, b2, g2, a2) in rows of mod_stride.
+int run_block(const dit_handle* h, int l, int rows, float* X, const float* mod, int mod_stride,
+              int base, void* ws, const WsLayout& L, float* o_branch, float* f_branch,
+              hipStream_t s) {
+  const int d = h->d, T = h->T, M = rows * T, es = h->es;
+  void* Hb = at<void>(ws, L.H);
+  void* O = at<void>(ws, L.o);
+  void* G = at<void>(ws, L.G);
+  void* q = at<void>(ws, L.q);
+  void* k = at<void>(ws, L.k);
+  void* v = at<void>(ws, L.v);
+
+  DIT_HIP(launch_ln_modulate(X, M, T, d, mod, mod_stride, base, base + d, h->eps, Hb, h->dtype, s));
+
+  EpiParams ep = epi0();
+  ep.bias = h->w.qkv_b + (size_t)l * 3 * d;
+  ep.q = q; ep.k = k; ep.v = v;
+  ep.heads = h->heads; ep.dh = h->dh; ep.d = d; ep.T = T;
+  ep.ldv = h->dtype == DIT_BF16 ? round_up(T, 64) : 0;
+  DIT_HIP(linear(h, EPI_QKV, Hb, d, woff(h->w.qkv_w, (size_t)l * 3 * d * d, es), M, 3 * d, d, ep, s));
+
+  if (h->cfg.qk_norm || h->cfg.rope3d)
+    DIT_HIP(launch_qk_norm_rope(q, k, rows, h->heads, T, h->dh, h->dtype, h->cfg.qk_norm, h->eps,
+                                h->cfg.rope3d, h->gf, h->gh, h->gw, s));
+  DIT_HIP(launch_attention(q, k, v, rows, h->heads, T, h->dh, h->dtype, O, s));
+
+  const void* ow = woff(h->w.o_w, (size_t)l * d * d, es);
+  if (o_branch) {
+    EpiParams eb = epi0();
+    eb.bias = h->w.o_b + (size_t)l * d;
+    eb.out = o_branch; eb.ldo = d;
+    DIT_HIP(linear(h, EPI_BIAS_F32, O, d, ow, M, d, d, eb, s));
+  }
+  ep = epi0();
+  ep.bias = h->w.o_b + (size_t)l * d;
+  ep.out = X; ep.ldo = d;
+  ep.mod = mod; ep.mod_stride = mod_stride; ep.gate_off = base + 2 * d; ep.T = T;
+  DIT_HIP(linear(h, EPI_GATED, O, d, ow, M, d, d, ep, s));
+
+  DIT_HIP(launch_ln_modulate(X, M, T, d, mod, mod_stride, base + 3 * d, base + 4 * d, h->eps, Hb,
+                             h->dtype, s));
+  ep = epi0();
+  ep.bias = h->w.fc1_b + (size_t)l * h->hid;
+  ep.out = G; ep.ldo = h->hid;
+  DIT_HIP(linear(h, EPI_GELU, Hb, d, woff(h->w.fc1_w, (size_t)l * h->hid * d, es), M, h->hid, d,
+                 ep, s));
+
+  const void* w2 = woff(h->w.fc2_w, (size_t)l * d * h->hid, es);
+  if (f_branch) {
+    EpiParams eb = epi0();
+    eb.bias = h->w.fc2_b + (size_t)l * d;
+    eb.out = f_branch; eb.ldo = d;
+    DIT_HIP(linear(h, EPI_BIAS_F32, G, h->hid, w2, M, d, h->hid, eb, s));
+  }
+  ep = epi0();
+  ep.bias = h->w.fc2_b + (size_t)l * d;
+  ep.out = X; ep.ldo = d;
+  ep.mod = mod; ep.mod_stride = mod_stride; ep.gate_off = base + 5 * d; ep.T = T;
+  DIT_HIP(linear(h, EPI_GATED, G, h->hid, w2, M, d, h->hid, ep, s));
+  return DIT_OK;
+}
+
+// Trunk of `rows` rows.  Row r reads latent/time/pooled row r % src_rows; rows
+// r >= null_from take the null label.  Leaves the decoder output in ws Y.
+int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_t* y,
+              const float* pooled, int rows, int src_rows, int null_from, void* ws,
+              const WsLayout& L, const dit_taps* taps, hipStream_t s) {
+  const int d = h->d, T = h->T, M = rows * T;
+  float* e = at<float>(ws, L.e);
+  float* th = at<float>(ws, L.th);
+  float* c = at<float>(ws, L.c);
+  void* sc = at<void>(ws, L.sc);
+  float* mod = at<float>(ws, L.mod);
+  float* X = at<float>(ws, L.X);
+  void* Hb = at<void>(ws, L.H);
+  float* Y = at<float>(ws, L.Y);
+
+  // c = t_emb (+ pooled projection) (+ class row); sc = SiLU(c) in the GEMM dtype.
+  DIT_HIP(launch_timestep_embed(t, rows, src_rows, h->freq, e, s));
+  ALoad a;
+  memset(&a, 0, sizeof a);
+  EpiParams ep = epi0();
+  if (h->cond_dim > 0) {
+    a.ptr = pooled; a.lda = h->cond_dim; a.a_dtype = 0; a.src_rows = src_rows;
+    ep.bias = h->w.pool_b; ep.out = c; ep.ldo = d;
+    DIT_HIP(launch_gemm_valu(EPI_BIAS_F32, A_PLAIN, a, h->w.pool_w, h->dtype, rows, d,
+                             h->cond_dim, ep, s));
+  }
+  a.ptr = e; a.lda = h->freq; a.a_dtype = 0; a.src_rows = rows;
+  ep = epi0();
+  ep.bias = h->w.t1_b; ep.out = th; ep.ldo = d;
+  DIT_HIP(launch_gemm_valu(EPI_BIAS_SILU, A_PLAIN, a, h->w.t1_w, h->dtype, rows, d, h->freq, ep, s));
+  a.ptr = th; a.lda = d;
+  ep = epi0();
+  ep.bias = h->w.t2_b; ep.out = c; ep.ldo = d; ep.silu_out = sc;
+  ep.add_prev = h->cond_dim > 0;
+  if (h->ncls > 0) {
+    ep.table = h->w.y_table; ep.labels = y; ep.label_rows = src_rows;
+    ep.null_from = null_from; ep.ncls = h->ncls;
+  }
+  DIT_HIP(launch_gemm_valu(EPI_COND, A_PLAIN, a, h->w.t2_w, h->dtype, rows, d, d, ep, s));
+
+  // All modulation vectors (every block and the final layer) in one GEMM.
+  ep = epi0();
+  ep.bias = h->w.ada_b; ep.out = mod; ep.ldo = h->mod_stride;
+  DIT_HIP(linear(h, EPI_BIAS_F32, sc, d, h->w.ada_w, rows, h->mod_stride, d, ep, s));
+
+  // Patchify gather + patch embedding + bias + 2-D position embedding.
+  memset(&a, 0, sizeof a);
+  a.ptr = x_t; a.a_dtype = h->dtype; a.src_rows = src_rows; a.g = h->gin;
+  ep = epi0();
+  ep.bias = h->w.pe_b; ep.out = X; ep.ldo = d; ep.T = T;
+  ep.pe = h->cfg.rope3d ? 0 : 1; ep.gh = h->gh; ep.gw = h->gw;
+  DIT_HIP(launch_gemm_valu(EPI_PATCH, A_PATCH, a, h->w.pe_w, h->dtype, M, d, h->kin, ep, s));
+
+  if (taps) {
+    if (taps->c) DIT_HIP(hipMemcpyAsync(taps->c, c, (size_t)rows * d * 4, hipMemcpyDeviceToDevice, s));
+    if (taps->mod)
+      DIT_HIP(hipMemcpyAsync(taps->mod, mod, (size_t)rows * h->mod_stride * 4,
+                             hipMemcpyDeviceToDevice, s));
+    if (taps->x_embed)
+      DIT_HIP(hipMemcpyAsync(taps->x_embed, X, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s));
+  }
+
+  for (int l = 0; l < h->N; ++l) {
+    int rc = run_block(h, l, rows, X, mod, h->mod_stride, 6 * d * l, ws, L, nullptr, nullptr, s);
+    if (rc) return rc;
+    if (taps && taps->x_blocks)
+      DIT_HIP(hipMemcpyAsync(taps->x_blocks + (size_t)l * M * d, X, (size_t)M * d * 4,
+                             hipMemcpyDeviceToDevice, s));
+  }
+
+  // Final layer: LN + modulation (b_f, g_f), linear decoder.
+  const int fb = 6 * d * h->N;
+  DIT_HIP(launch_ln_modulate(X, M, T, d, mod, h->mod_stride, fb, fb + d, h->eps, Hb, h->dtype, s));
+  memset(&a, 0, sizeof a);
+  a.ptr = Hb; a.lda = d; a.a_dtype = h->dtype; a.src_rows = M;
+  ep = epi0();
+  ep.bias = h->w.out_b; ep.out = Y; ep.ldo = h->kout;
+  DIT_HIP(launch_gemm_valu(EPI_BIAS_F32, A_PLAIN, a, h->w.out_w, h->dtype, M, h->kout, d, ep, s));
+  if (taps && taps->y_final)
+    DIT_HIP(hipMemcpyAsync(taps->y_final, Y, (size_t)M * h->kout * 4, hipMemcpyDeviceToDevice, s));
+  return DIT_OK;
+}
+
+int check_ws(const dit_handle* h, int rows, const void* ws, size_t ws_bytes, WsLayout* L) {
+  if ((int64_t)rows * h->T > (1LL << 30)) return fail(DIT_EINVAL, "rows * T too large");
+  if ((int64_t)rows * h->heads > 65535)
+    return fail(DIT_EUNSUPPORTED, "rows * heads > 65535 (attention grid limit)");
+  *L = ws_layout(h, rows);
+  if (!ws) return fail(DIT_EWORKSPACE, "workspace pointer is NULL");
+  if (ws_bytes < L->total)
+    return fail(DIT_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L->total);
+  if ((uintptr_t)ws & 255) return fail(DIT_EWORKSPACE, "workspace must be 256-byte aligned");
+  return DIT_OK;
+}
+
+int forward_impl(dit_handle* h, const void* x_t, const float* t, const int32_t* y,
+                 const float* pooled, int B, float* out, const dit_taps* taps, void* ws,
+                 size_t ws_bytes, void* stream) {
+  if (!h) return fail(DIT_EINVAL, "handle is NULL");
+  if (!x_t || !t || !out) return fail(DIT_EINVAL, "x_t, t and out must be non-NULL");
+  if (B <= 0) return fail(DIT_EINVAL, "B must be positive (got %d)", B);
+  if (h->ncls > 0 && !y) return fail(DIT_EINVAL, "class labels y are required");
+  if (h->cond_dim > 0 && !pooled) return fail(DIT_EINVAL, "pooled conditioning is required");
+  WsLayout L;
+  int rc = check_ws(h, B, ws, ws_bytes, &L);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  rc = run_trunk(h, x_t, t, y, pooled, B, B, B, ws, L, taps, s);
+  if (rc) return rc;
+  DIT_HIP(launch_unpatchify(at<float>(ws, L.Y), B, 0, h->gout, h->cfg.out_channels, 0, 0.0f, 0,
+                            out, s));
+  return ok();
+}
+
+int cfg_forward_impl(dit_handle* h, const void* x_t, const float* t, const int32_t* y, int Bh,
+                     float scale, int guided, float* out, const dit_taps* taps, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!h) return fail(DIT_EINVAL, "handle is NULL");
+  if (!x_t || !t || !y || !out) return fail(DIT_EINVAL, "x_t, t, y and out must be non-NULL");
+  if (Bh <= 0 || Bh > (1 << 29)) return fail(DIT_EINVAL, "Bh must be positive (got %d)", Bh);
+  if (h->ncls <= 0) return fail(DIT_EINVAL, "guidance needs a class table with a null label");
+  if (h->cond_dim > 0) return fail(DIT_EUNSUPPORTED, "guidance with pooled conditioning");
+  if (guided < 1 || guided > h->cfg.out_channels)
+    return fail(DIT_EINVAL, "guided_channels must be in [1, %d]", h->cfg.out_channels);
+  if (!std::isfinite(scale)) return fail(DIT_EINVAL, "guidance scale must be finite");
+  WsLayout L;
+  int rc = check_ws(h, 2 * Bh, ws, ws_bytes, &L);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  rc = run_trunk(h, x_t, t, y, nullptr, 2 * Bh, Bh, Bh, ws, L, taps, s);
+  if (rc) return rc;
+  DIT_HIP(launch_unpatchify(at<float>(ws, L.Y), Bh, Bh, h->gout, h->cfg.out_channels, guided,
+                            scale, 1, out, s));
+  return ok();
+}
+
+PatchGeom make_geom(int C, int F, int H, int W, int p, int pt) {
+  PatchGeom g;
+  g.C = C; g.F = F; g.H = H; g.W = W; g.p = p; g.pt = pt;
+  g.gh = H / p; g.gw = W / p;
+  g.T = (F / pt) * g.gh * g.gw;
+  g.K = pt * p * p * C;
+  return g;
+}
+
+int check_geom(int B, int C, int F, int H, int W, int p, int pt) {
+  if (B <= 0 || C <= 0 || F <= 0 || H <= 0 || W <= 0 || p <= 0 || pt <= 0)
+    return fail(DIT_EINVAL, "sizes must be positive");
+  if (H % p || W % p || F % pt)
+    return fail(DIT_EINVAL, "latent extents (%d, %d, %d) not divisible by patch (%d, %d, %d)", F,
+                H, W, pt, p, p);
+  if ((int64_t)B * C * F * H * W > (1LL << 40)) return fail(DIT_EINVAL, "latent too large");
+  return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dit_status_string(int status) {
+  switch (status) {
+    case DIT_OK: return "ok";
+    case DIT_EINVAL: return "invalid argument";
+    case DIT_EUNSUPPORTED: return "unsupported configuration";
+    case DIT_EWORKSPACE: return "workspace missing or too small";
+    case DIT_EHIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+const char* dit_last_error_message(void) { return g_err.c_str(); }
+
+int dit_create(const dit_config* cfg, const dit_weights* w, dit_handle** out) {
+  if (!cfg || !w || !out) return fail(DIT_EINVAL, "cfg, w and out must be non-NULL");
+  *out = nullptr;
+  const dit_config& c = *cfg;
+  if (c.in_channels <= 0 || c.out_channels <= 0 || c.frames <= 0 || c.height <= 0 ||
+      c.width <= 0 || c.patch <= 0 || c.patch_t <= 0 || c.hidden <= 0 || c.depth <= 0 ||
+      c.heads <= 0 || c.mlp_hidden <= 0 || c.freq_dim <= 0 || c.num_classes < 0 ||
+      c.cond_dim < 0)
+    return fail(DIT_EINVAL, "config sizes must be positive");
+  if (c.freq_dim % 2) return fail(DIT_EINVAL, "freq_dim must be even");
+  if (c.dtype != DIT_F32 && c.dtype != DIT_BF16) return fail(DIT_EINVAL, "dtype must be F32 or BF16");
+  if (!(c.ln_eps > 0.0f) || !std::isfinite(c.ln_eps)) return fail(DIT_EINVAL, "ln_eps must be > 0");
+  if (c.height % c.patch || c.width % c.patch || c.frames % c.patch_t)
+    return fail(DIT_EINVAL, "latent extents not divisible by the patch size");
+  if (c.hidden % c.heads) return fail(DIT_EINVAL, "hidden %% heads != 0");
+  const int dh = c.hidden / c.heads;
+  if (dh != 64 && dh != 72) return fail(DIT_EUNSUPPORTED, "head dim %d (supported: 64, 72)", dh);
+  if (c.hidden % 128 || c.hidden > 2048)
+    return fail(DIT_EUNSUPPORTED, "hidden %d (supported: multiple of 128, <= 2048)", c.hidden);
+  if (c.mlp_hidden % 64) return fail(DIT_EUNSUPPORTED, "mlp_hidden must be a multiple of 64");
+  const int gf = c.frames / c.patch_t;
+  if (!c.rope3d && gf != 1)
+    return fail(DIT_EUNSUPPORTED, "2-D position embedding needs frames / patch_t == 1");
+  if (c.rope3d && (dh % 6 || (dh / 3) % 2))
+    return fail(DIT_EUNSUPPORTED, "3-D RoPE needs head dim divisible by 6 with even thirds");
+  if (c.qk_norm != 0 && c.qk_norm != 1) return fail(DIT_EINVAL, "qk_norm must be 0 or 1");
+  if (c.rope3d != 0 && c.rope3d != 1) return fail(DIT_EINVAL, "rope3d must be 0 or 1");
+  if (!w->pe_w || !w->pe_b || !w->t1_w || !w->t1_b || !w->t2_w || !w->t2_b || !w->ada_w ||
+      !w->ada_b || !w->qkv_w || !w->qkv_b || !w->o_w || !w->o_b || !w->fc1_w || !w->fc1_b ||
+      !w->fc2_w || !w->fc2_b || !w->out_w || !w->out_b)
+    return fail(DIT_EINVAL, "a required weight pointer is NULL");
+  if (c.num_classes > 0 && !w->y_table) return fail(DIT_EINVAL, "y_table is NULL");
+  if (c.cond_dim > 0 && (!w->pool_w || !w->pool_b)) return fail(DIT_EINVAL, "pool_w/pool_b NULL");
+  const void* ptrs[] = {w->qkv_w, w->o_w, w->fc1_w, w->fc2_w, w->ada_w};
+  for (const void* p : ptrs)
+    if ((uintptr_t)p & 15) return fail(DIT_EINVAL, "GEMM weights must be 16-byte aligned");
+  const int64_t T = (int64_t)gf * (c.height / c.patch) * (c.width / c.patch);
+  if (T > (1 << 26)) return fail(DIT_EINVAL, "too many tokens");
+
+  dit_handle* h = new (std::nothrow) dit_handle;
+  if (!h) return fail(DIT_EINVAL, "out of host memory");
+  h->cfg = c;
+  h->w = *w;
+  h->d = c.hidden; h->N = c.depth; h->heads = c.heads; h->dh = dh; h->hid = c.mlp_hidden;
+  h->ncls = c.num_classes; h->cond_dim = c.cond_dim; h->freq = c.freq_dim; h->dtype = c.dtype;
+  h->es = c.dtype == DIT_BF16 ? 2 : 4;
+  h->eps = c.ln_eps;
+  h->gf = gf; h->gh = c.height / c.patch; h->gw = c.width / c.patch;
+  h->T = (int)T;
+  h->kin = c.patch_t * c.patch * c.patch * c.in_channels;
+  h->kout = c.patch_t * c.patch * c.patch * c.out_channels;
+  h->mod_stride = (6 * c.depth + 2) * c.hidden;
+  h->gin = make_geom(c.in_channels, c.frames, c.height, c.width, c.patch, c.patch_t);
+  h->gout = make_geom(c.out_channels, c.frames, c.height, c.width, c.patch, c.patch_t);
+  *out = h;
+  return ok();
+}
+
+void dit_destroy(dit_handle* h) { delete h; }
+
+int dit_workspace_size(const dit_handle* h, int rows, size_t* bytes) {
+  if (!h || !bytes) return fail(DIT_EINVAL, "handle and bytes must be non-NULL");
+  if (rows <= 0) return fail(DIT_EINVAL, "rows must be positive");
+  *bytes = ws_layout(h, rows).total;
+  return ok();
+}
+
+int dit_forward(dit_handle* h, const void* x_t, const float* t, const int32_t* y,
+                const float* pooled, int B, float* out, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(h, x_t, t, y, pooled, B, out, nullptr, ws, ws_bytes, stream);
+}
+
+int dit_forward_taps(dit_handle* h, const void* x_t, const float* t, const int32_t* y,
+                     const float* pooled, int B, float* out, const dit_taps* taps, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return forward_impl(h, x_t, t, y, pooled, B, out, taps, ws, ws_bytes, stream);
+}
+
+int dit_cfg_forward(dit_handle* h, const void* x_t, const float* t, const int32_t* y, int Bh,
+                    float s, int guided_channels, float* out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  return cfg_forward_impl(h, x_t, t, y, Bh, s, guided_channels, out, nullptr, ws, ws_bytes,
+                          stream);
+}
+
+int dit_cfg_forward_taps(dit_handle* h, const void* x_t, const float* t, const int32_t* y,
+                         int Bh, float s, int guided_channels, float* out,
+                         const dit_taps* taps, void* ws, size_t ws_bytes, void* stream) {
+  return cfg_forward_impl(h, x_t, t, y, Bh, s, guided_channels, out, taps, ws, ws_bytes, stream);
+}
+
+int dit_patchify(const void* x, int B, int C, int F, int H, int W, int p, int pt, int dtype,
+                 void* P, void* stream) {
+  if (!x || !P) return fail(DIT_EINVAL, "x and P must be non-NULL");
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return fail(DIT_EINVAL, "dtype");
+  int rc = check_geom(B, C, F, H, W, p, pt);
+  if (rc) return rc;
+  DIT_HIP(launch_patchify(x, B, make_geom(C, F, H, W, p, pt), dtype, P, (hipStream_t)stream));
+  return ok();
+}
+
+int dit_unpatchify(const float* Y, int B, int Cout, int F, int H, int W, int p, int pt,
+                   float* out, void* stream) {
+  if (!Y || !out) return fail(DIT_EINVAL, "Y and out must be non-NULL");
+  int rc = check_geom(B, Cout, F, H, W, p, pt);
+  if (rc) return rc;
+  DIT_HIP(launch_unpatchify(Y, B, 0, make_geom(Cout, F, H, W, p, pt), Cout, 0, 0.0f, 0, out,
+                            (hipStream_t)stream));
+  return ok();
+}
+
+int dit_timestep_embed(const float* t, int B, int dim, float* e, void* stream) {
+  if (!t || !e) return fail(DIT_EINVAL, "t and e must be non-NULL");
+  if (B <= 0 || dim <= 0 || dim % 2) return fail(DIT_EINVAL, "B > 0 and even dim > 0 required");
+  DIT_HIP(launch_timestep_embed(t, B, B, dim, e, (hipStream_t)stream));
+  return ok();
+}
+
+int dit_attention(const void* q, const void* k, const void* v, int B, int H, int T, int dh,
+                  int dtype, void* o, void* stream) {
+  if (!q || !k || !v || !o) return fail(DIT_EINVAL, "q, k, v and o must be non-NULL");
+  if (B <= 0 || H <= 0 || T <= 0) return fail(DIT_EINVAL, "B, H, T must be positive");
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return fail(DIT_EINVAL, "dtype");
+  if (dh != 64 && dh != 72) return fail(DIT_EUNSUPPORTED, "head dim %d", dh);
+  if ((int64_t)B * H > 65535) return fail(DIT_EUNSUPPORTED, "B * H > 65535");
+  DIT_HIP(launch_attention(q, k, v, B, H, T, dh, dtype, o, (hipStream_t)stream));
+  return ok();
+}
+
+int dit_linear(int epilogue, const void* A, const void* W, const float* bias, int M, int N,
+               int K, int dtype, void* out, const float* gate, int gate_stride, int T,
+               void* stream) {
+  if (!A || !W || !out) return fail(DIT_EINVAL, "A, W and out must be non-NULL");
+  if (M <= 0 || N <= 0 || K <= 0) return fail(DIT_EINVAL, "M, N, K must be positive");
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return fail(DIT_EINVAL, "dtype");
+  int epi;
+  switch (epilogue) {
+    case DIT_EPI_BIAS: epi = EPI_BIAS_F32; break;
+    case DIT_EPI_GELU: epi = EPI_GELU; break;
+    case DIT_EPI_GATED: epi = EPI_GATED; break;
+    default: return fail(DIT_EINVAL, "unknown epilogue %d", epilogue);
+  }
+  if (epilogue == DIT_EPI_GATED && (!gate || T <= 0 || gate_stride < N))
+    return fail(DIT_EINVAL, "gated epilogue needs gate, T > 0 and gate_stride >= N");
+  if (dtype == DIT_BF16 && (K % 64 || ((uintptr_t)A & 15) || ((uintptr_t)W & 15)))
+    return fail(DIT_EUNSUPPORTED, "bf16 linear needs K %% 64 == 0 and 16-byte aligned A, W");
+  EpiParams ep = epi0();
+  ep.bias = bias; ep.out = out; ep.ldo = N;
+  ep.mod = gate; ep.mod_stride = gate_stride; ep.gate_off = 0; ep.T = T > 0 ? T : 1;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == DIT_BF16) {
+    DIT_HIP(launch_gemm_mfma(epi, (const bf16_t*)A, K, (const bf16_t*)W, M, N, K, ep, s));
+  } else {
+    ALoad a;
+    memset(&a, 0, sizeof a);
+    a.ptr = A; a.lda = K; a.a_dtype = 0; a.src_rows = M;
+    DIT_HIP(launch_gemm_valu(epi, A_PLAIN, a, W, 0, M, N, K, ep, s));
+  }
+  return ok();
+}
+
+int dit_block_forward(dit_handle* h, int layer, int B, const float* X_in, const float* mod,
+                      float* X_out, float* o_branch, float* f_branch, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!h) return fail(DIT_EINVAL, "handle is NULL");
+  if (!X_in || !mod || !X_out) return fail(DIT_EINVAL, "X_in, mod and X_out must be non-NULL");
+  if (layer < 0 || layer >= h->N) return fail(DIT_EINVAL, "layer %d out of range", layer);
+  if (B <= 0) return fail(DIT_EINVAL, "B must be positive");
+  WsLayout L;
+  int rc = check_ws(h, B, ws, ws_bytes, &L);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if (X_out != X_in)
+    DIT_HIP(hipMemcpyAsync(X_out, X_in, (size_t)B * h->T * h->d * 4, hipMemcpyDeviceToDevice, s));
+  rc = run_block(h, layer, B, X_out, mod, 6 * h->d, 0, ws, L, o_branch, f_branch, s);
+  if (rc) return rc;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// Shared device helpers and launcher declarations for the DiT forward kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+// bf16 <-> fp32.  fp32 -> bf16 rounds to nearest even; NaN stays NaN.
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// tanh-approximate GELU: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))
+__device__ __forceinline__ float gelu_tanh_f(float z) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  float u = k0 * (z + 0.044715f * z * z * z);
+  return 0.5f * z * (1.0f + tanhf(u));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Patch index maps (shared by the gather prologue of the patch embedding, the
+// standalone patchify kernel and the unpatchify kernel).
+struct PatchGeom {
+  int C, F, H, W, p, pt;  // latent extents and patch sizes
+  int gh, gw, T, K;       // token grid rows/cols, tokens per row, patch vector length
+};
+
+// Offset into a [.., C, F, H, W] latent row for token tau and patch element k.
+__device__ __forceinline__ int64_t patch_src_offset(const PatchGeom& g, int tau, int k) {
+  int ghw = g.gh * g.gw;
+  int f = tau / ghw, rem = tau - f * ghw;
+  int i = rem / g.gw, j = rem - i * g.gw;
+  int c = k % g.C, r = k / g.C;
+  int px = r % g.p; r /= g.p;
+  int py = r % g.p; int a = r / g.p;
+  return (((int64_t)c * g.F + (f * g.pt + a)) * g.H + (i * g.p + py)) * g.W + (j * g.p + px);
+}
+
+// ---------------------------------------------------------------------------
+// GEMM epilogues.  C = A W^T computed in fp32; the epilogue consumes C[m, n].
+enum EpiKind {
+  EPI_BIAS_F32 = 0,     // out_f32[m, n] = C + bias[n]
+  EPI_BIAS_SILU = 1,    // out_f32[m, n] = SiLU(C + bias[n])                   (timestep MLP)
+  EPI_COND = 2,         // c = C + bias (+ c_prev) (+ table[label]); writes c and SiLU(c) (dtype)
+  EPI_QKV = 3,          // C + bias scattered to q, k [B,H,T,dh] and v (bf16: [B,H,dh,ldv])
+  EPI_GATED = 4,        // X[m, n] += gate[b, n] * (C + bias[n])                (fp32 residual)
+  EPI_GELU = 5,         // out_dtype[m, n] = GELU_tanh(C + bias[n])
+  EPI_PATCH = 6,        // X[m, n] = C + bias[n] (+ 2-D sin-cos PE(tau, n))
+};
+
+struct EpiParams {
+  const float* bias;
+  void* out;            // output (type depends on the epilogue)
+  int ldo;              // leading dimension of out (elements)
+  // gated residual: gate = mod + (m / T) * mod_stride + gate_off
+  const float* mod;
+  int mod_stride;
+  int gate_off;
+  int T;                // tokens per row (rows of A per batch row)
+  // qkv scatter
+  void* q; void* k; void* v;
+  int heads, dh, d, ldv;
+  // conditioning
+  const float* table;   // class table [ncls + 1, d] or null
+  const int32_t* labels;
+  int label_rows;       // rows of `labels` (source rows); row b reads labels[b % label_rows]
+  int null_from;        // rows b >= null_from use the null label
+  int ncls;
+  int add_prev;         // 1: add the current content of out (pooled projection)
+  void* silu_out;       // SiLU(c) in the GEMM operand dtype
+  // patch embedding position term
+  int pe, gh, gw;
+};
+
+// ---------------------------------------------------------------------------
+// Launchers (each returns hipGetLastError() after the launch).
+hipError_t launch_timestep_embed(const float* t, int rows, int src_rows, int dim, float* e,
+                                 hipStream_t s);
+hipError_t launch_patchify(const void* x, int B, const PatchGeom& g, int dtype, void* P,
+                           hipStream_t s);
+hipError_t launch_unpatchify(const float* Y, int Bout, int Bh_offset, const PatchGeom& g,
+                             int Cout, int guided, float scale, int guide, float* out,
+                             hipStream_t s);
+
+// A-operand sources of the VALU GEMM.
+enum ASrc { A_PLAIN = 0, A_PATCH = 1 };
+struct ALoad {
+  const void* ptr;      // A matrix (or latent for A_PATCH)
+  int lda;
+  int a_dtype;          // 0 fp32, 1 bf16
+  int src_rows;         // A_PLAIN: row r reads row r % src_rows; A_PATCH: latent rows
+  PatchGeom g;          // A_PATCH only
+};
+hipError_t launch_gemm_valu(int epi, int asrc, const ALoad& a, const void* W, int w_dtype,
+                            int M, int N, int K, const EpiParams& ep, hipStream_t s);
+hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, int M, int N,
+                            int K, const EpiParams& ep, hipStream_t s);
+
+hipError_t launch_ln_modulate(const float* X, int M, int T, int d, const float* mod,
+                              int mod_stride, int shift_off, int scale_off, float eps,
+                              void* H, int dtype, hipStream_t s);
+hipError_t launch_qk_norm_rope(void* q, void* k, int B, int heads, int T, int dh, int dtype,
+                               int qk_norm, float eps, int rope, int gf, int gh, int gw,
+                               hipStream_t s);
+hipError_t launch_attention(const void* q, const void* k, const void* v, int B, int heads,
+                            int T, int dh, int dtype, void* o, hipStream_t s);
+
+static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }

@@ -1,0 +1,63 @@
+// GEMM epilogues fused into the producing kernels (bias, SiLU, conditioning
+// sum, QKV head split, alpha-gated residual, tanh-GELU, patch position term).
+#pragma once
+#include "common.h"
+
+// log2(10000)
+#define DIT_LOG2_1E4 13.287712379549449f
+
+// 2-D sine-cosine position embedding of token (i, j), feature n of d:
+// d/4 frequencies w_k = 10000^(-k/(d/4)); [sin(i w) | cos(i w) | sin(j w) | cos(j w)].
+__device__ __forceinline__ float pos_embed_2d(int i, int j, int n, int d) {
+  int dq = d >> 2;
+  int seg = n / dq, kk = n - seg * dq;
+  float w = exp2f(-(float)kk / (float)dq * DIT_LOG2_1E4);
+  float ang = (float)(seg < 2 ? i : j) * w;
+  return (seg & 1) ? cosf(ang) : sinf(ang);
+}
+
+template <int EPI, typename DT>
+__device__ __forceinline__ void epi_apply(const EpiParams& ep, int m, int n, float acc) {
+  float v = acc + (ep.bias ? ep.bias[n] : 0.0f);
+  if constexpr (EPI == EPI_BIAS_F32) {
+    ((float*)ep.out)[(int64_t)m * ep.ldo + n] = v;
+  } else if constexpr (EPI == EPI_BIAS_SILU) {
+    ((float*)ep.out)[(int64_t)m * ep.ldo + n] = silu_f(v);
+  } else if constexpr (EPI == EPI_COND) {
+    float* c = (float*)ep.out;
+    int64_t o = (int64_t)m * ep.ldo + n;
+    if (ep.add_prev) v += c[o];
+    if (ep.table) {
+      int lbl = (m >= ep.null_from) ? ep.ncls : ep.labels[m % ep.label_rows];
+      if (lbl < 0 || lbl > ep.ncls) v = __builtin_nanf("");
+      else v += ep.table[(int64_t)lbl * ep.ldo + n];
+    }
+    c[o] = v;
+    ((DT*)ep.silu_out)[o] = from_f<DT>(silu_f(v));
+  } else if constexpr (EPI == EPI_QKV) {
+    int b = m / ep.T, t = m - b * ep.T;
+    int which = n / ep.d, r = n - which * ep.d;
+    int h = r / ep.dh, e = r - h * ep.dh;
+    int64_t bh = (int64_t)b * ep.heads + h;
+    DT val = from_f<DT>(v);
+    if (which == 0) ((DT*)ep.q)[(bh * ep.T + t) * ep.dh + e] = val;
+    else if (which == 1) ((DT*)ep.k)[(bh * ep.T + t) * ep.dh + e] = val;
+    else if (ep.ldv) ((DT*)ep.v)[(bh * ep.dh + e) * ep.ldv + t] = val;   // keys fastest
+    else ((DT*)ep.v)[(bh * ep.T + t) * ep.dh + e] = val;
+  } else if constexpr (EPI == EPI_GATED) {
+    int b = m / ep.T;
+    float g = ep.mod[(int64_t)b * ep.mod_stride + ep.gate_off + n];
+    float* X = (float*)ep.out;
+    int64_t o = (int64_t)m * ep.ldo + n;
+    X[o] = X[o] + g * v;
+  } else if constexpr (EPI == EPI_GELU) {
+    ((DT*)ep.out)[(int64_t)m * ep.ldo + n] = from_f<DT>(gelu_tanh_f(v));
+  } else if constexpr (EPI == EPI_PATCH) {
+    if (ep.pe) {
+      int tau = m % ep.T;
+      int i = tau / ep.gw, j = tau - i * ep.gw;
+      v += pos_embed_2d(i, j, n, ep.ldo);
+    }
+    ((float*)ep.out)[(int64_t)m * ep.ldo + n] = v;
+  }
+}

@@ -1,0 +1,122 @@
+// fp32-arithmetic tiled GEMM C = A W^T on the vector ALUs.
+//
+// Serves the small products of the forward pass (timestep MLP, pooled
+// projection, patch embedding with its patchify gather, linear decoder) and
+// every product of the fp32 model path.  64x64 tile, BK = 16, 256 threads,
+// 4x4 outputs per thread, sequential fp32 accumulation over k (deterministic).
+#include "common.h"
+#include "epilogue.h"
+
+namespace {
+
+constexpr int BM = 64, BN = 64, BK = 16;
+
+template <int ASRC, typename AT>
+__device__ __forceinline__ float load_a(const ALoad& a, int m, int k) {
+  if constexpr (ASRC == A_PATCH) {
+    int b = m / a.g.T, tau = m - b * a.g.T;
+    int64_t row = (int64_t)a.g.C * a.g.F * a.g.H * a.g.W;
+    return to_f<AT>(((const AT*)a.ptr)[(int64_t)(b % a.src_rows) * row +
+                                       patch_src_offset(a.g, tau, k)]);
+  } else {
+    return to_f<AT>(((const AT*)a.ptr)[(int64_t)(m % a.src_rows) * a.lda + k]);
+  }
+}
+
+template <int EPI, int ASRC, typename AT, typename WT, typename DT>
+__global__ __launch_bounds__(256) void gemm_valu_kernel(ALoad a, const WT* __restrict__ W, int M,
+                                                         int N, int K, EpiParams ep) {
+  __shared__ __attribute__((aligned(16))) float As[BK][BM + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[BK][BN + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int lr = tid >> 2, lk = (tid & 3) * 4;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    const int m = m0 + lr, n = n0 + lr;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int k = k0 + lk + u;
+      As[lk + u][lr] = (m < M && k < K) ? load_a<ASRC, AT>(a, m, k) : 0.0f;
+      Bs[lk + u][lr] = (n < N && k < K) ? to_f<WT>(W[(int64_t)n * K + k]) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float4 av = *(const float4*)&As[kk][ty * 4];
+      float4 bv = *(const float4*)&Bs[kk][tx * 4];
+      float ar[4] = {av.x, av.y, av.z, av.w};
+      float br[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ar[i], br[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int n = n0 + tx * 4 + j;
+      if (n < N) epi_apply<EPI, DT>(ep, m, n, acc[i][j]);
+    }
+  }
+}
+
+template <int EPI, int ASRC, typename AT, typename WT, typename DT>
+hipError_t run(const ALoad& a, const void* W, int M, int N, int K, const EpiParams& ep,
+               hipStream_t s) {
+  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+  gemm_valu_kernel<EPI, ASRC, AT, WT, DT><<<grid, 256, 0, s>>>(a, (const WT*)W, M, N, K, ep);
+  return hipGetLastError();
+}
+
+// The model dtype fixes the weight dtype and the dtype of dtype-valued outputs
+// (SiLU(c), q/k/v, GELU).  The A operand is fp32 (embedding tables, pooled
+// vectors) or the model dtype (activations, latent).
+template <int EPI, int ASRC, typename DT>
+hipError_t dispatch_a(const ALoad& a, const void* W, int M, int N, int K, const EpiParams& ep,
+                      hipStream_t s) {
+  if (a.a_dtype == 1) return run<EPI, ASRC, bf16_t, DT, DT>(a, W, M, N, K, ep, s);
+  return run<EPI, ASRC, float, DT, DT>(a, W, M, N, K, ep, s);
+}
+
+template <int EPI, typename DT>
+hipError_t dispatch_src(int asrc, const ALoad& a, const void* W, int M, int N, int K,
+                        const EpiParams& ep, hipStream_t s) {
+  if (asrc == A_PATCH) return dispatch_a<EPI, A_PATCH, DT>(a, W, M, N, K, ep, s);
+  return dispatch_a<EPI, A_PLAIN, DT>(a, W, M, N, K, ep, s);
+}
+
+template <typename DT>
+hipError_t dispatch_epi(int epi, int asrc, const ALoad& a, const void* W, int M, int N, int K,
+                        const EpiParams& ep, hipStream_t s) {
+  switch (epi) {
+    case EPI_BIAS_F32: return dispatch_src<EPI_BIAS_F32, DT>(asrc, a, W, M, N, K, ep, s);
+    case EPI_BIAS_SILU: return dispatch_src<EPI_BIAS_SILU, DT>(asrc, a, W, M, N, K, ep, s);
+    case EPI_COND: return dispatch_src<EPI_COND, DT>(asrc, a, W, M, N, K, ep, s);
+    case EPI_QKV: return dispatch_src<EPI_QKV, DT>(asrc, a, W, M, N, K, ep, s);
+    case EPI_GATED: return dispatch_src<EPI_GATED, DT>(asrc, a, W, M, N, K, ep, s);
+    case EPI_GELU: return dispatch_src<EPI_GELU, DT>(asrc, a, W, M, N, K, ep, s);
+    case EPI_PATCH: return dispatch_src<EPI_PATCH, DT>(asrc, a, W, M, N, K, ep, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_valu(int epi, int asrc, const ALoad& a, const void* W, int w_dtype,
+                            int M, int N, int K, const EpiParams& ep, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (w_dtype == 1) return dispatch_epi<bf16_t>(epi, asrc, a, W, M, N, K, ep, s);
+  return dispatch_epi<float>(epi, asrc, a, W, M, N, K, ep, s);
+}

@@ -1,0 +1,162 @@
+// LayerNorm (no affine) fused with adaLN modulation, and the per-head Q-K
+// LayerNorm + 3-D rotary embedding of spacetime attention.
+#include "common.h"
+
+#define DIT_LOG2_1E4 13.287712379549449f
+
+// H[m, :] = LN(X[m, :]) * (1 + scale[b, :]) + shift[b, :],  b = m / T.
+// One wave per row; each lane holds NV float2 (d = 128 NV), so the row is read
+// from HBM once and both moments come from registers.
+template <int NV, typename DT>
+__global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restrict__ X, int M,
+                                                          int T, const float* __restrict__ mod,
+                                                          int mod_stride, int shift_off,
+                                                          int scale_off, float eps,
+                                                          DT* __restrict__ H) {
+  constexpr int D = 128 * NV;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const float2* x2 = (const float2*)(X + (int64_t)row * D);
+  float2 v[NV];
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    v[i] = x2[lane + 64 * i];
+    s += v[i].x + v[i].y;
+  }
+  const float mean = wave_sum(s) * (1.0f / D);
+  float q = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float a = v[i].x - mean, b = v[i].y - mean;
+    q += a * a + b * b;
+  }
+  const float var = wave_sum(q) * (1.0f / D);
+  const float rstd = 1.0f / sqrtf(var + eps);
+  const int b = row / T;
+  const float2* sh = (const float2*)(mod + (int64_t)b * mod_stride + shift_off);
+  const float2* sc = (const float2*)(mod + (int64_t)b * mod_stride + scale_off);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    int c = lane + 64 * i;
+    float2 g = sc[c], t = sh[c];
+    float h0 = (v[i].x - mean) * rstd * (1.0f + g.x) + t.x;
+    float h1 = (v[i].y - mean) * rstd * (1.0f + g.y) + t.y;
+    if constexpr (sizeof(DT) == 2) {
+      uint32_t packed = (uint32_t)f2bf(h0) | ((uint32_t)f2bf(h1) << 16);
+      ((uint32_t*)(H + (int64_t)row * D))[c] = packed;
+    } else {
+      ((float2*)(H + (int64_t)row * D))[c] = make_float2(h0, h1);
+    }
+  }
+}
+
+template <typename DT>
+static hipError_t ln_dispatch(const float* X, int M, int T, int d, const float* mod,
+                              int mod_stride, int shift_off, int scale_off, float eps, DT* H,
+                              hipStream_t s) {
+  dim3 grid((M + 3) / 4);
+#define DIT_LN_CASE(NV)                                                                      \
+  case NV:                                                                                   \
+    ln_modulate_kernel<NV, DT><<<grid, 256, 0, s>>>(X, M, T, mod, mod_stride, shift_off,    \
+                                                    scale_off, eps, H);                     \
+    break;
+  switch (d / 128) {
+    DIT_LN_CASE(1) DIT_LN_CASE(2) DIT_LN_CASE(3) DIT_LN_CASE(4) DIT_LN_CASE(5) DIT_LN_CASE(6)
+    DIT_LN_CASE(7) DIT_LN_CASE(8) DIT_LN_CASE(9) DIT_LN_CASE(10) DIT_LN_CASE(11)
+    DIT_LN_CASE(12) DIT_LN_CASE(13) DIT_LN_CASE(14) DIT_LN_CASE(15) DIT_LN_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef DIT_LN_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_modulate(const float* X, int M, int T, int d, const float* mod,
+                              int mod_stride, int shift_off, int scale_off, float eps, void* H,
+                              int dtype, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (d % 128 || d > 2048) return hipErrorInvalidValue;
+  if (dtype == 1)
+    return ln_dispatch<bf16_t>(X, M, T, d, mod, mod_stride, shift_off, scale_off, eps,
+                               (bf16_t*)H, s);
+  return ln_dispatch<float>(X, M, T, d, mod, mod_stride, shift_off, scale_off, eps, (float*)H,
+                            s);
+}
+
+// Per-head q/k post-processing for spacetime attention, in place on
+// [B, H, T, DH] rows: LayerNorm over the DH features (no affine), then the 3-D
+// rotary embedding: DH splits into (frame, row, col) thirds of da = DH/3; pair
+// (x_2k, x_2k+1) of a third rotates by pos * 10000^(-2k/da).
+template <int DH, typename DT>
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(DT* __restrict__ q, DT* __restrict__ k,
+                                                           int64_t rows, int T, int qk_norm,
+                                                           float eps, int rope, int gh, int gw) {
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= 2 * rows) return;
+  int64_t r = idx < rows ? idx : idx - rows;
+  DT* p = (idx < rows ? q : k) + r * DH;
+  float x[DH];
+#pragma unroll
+  for (int e = 0; e < DH; ++e) x[e] = to_f<DT>(p[e]);
+  if (qk_norm) {
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DH; ++e) s += x[e];
+    float mean = s * (1.0f / DH), v = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DH; ++e) v += (x[e] - mean) * (x[e] - mean);
+    float rstd = 1.0f / sqrtf(v * (1.0f / DH) + eps);
+#pragma unroll
+    for (int e = 0; e < DH; ++e) x[e] = (x[e] - mean) * rstd;
+  }
+  if constexpr (DH % 6 == 0) {
+    if (rope) {
+      constexpr int DA = DH / 3;
+      int t = (int)(r % T);
+      int pos[3] = {t / (gh * gw), (t / gw) % gh, t % gw};
+#pragma unroll
+      for (int a = 0; a < 3; ++a) {
+#pragma unroll
+        for (int kk = 0; kk < DA / 2; ++kk) {
+          float theta = exp2f(-2.0f * kk / DA * DIT_LOG2_1E4);
+          float sn, cs;
+          sincosf((float)pos[a] * theta, &sn, &cs);
+          float x0 = x[a * DA + 2 * kk], x1 = x[a * DA + 2 * kk + 1];
+          x[a * DA + 2 * kk] = x0 * cs - x1 * sn;
+          x[a * DA + 2 * kk + 1] = x0 * sn + x1 * cs;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < DH; ++e) p[e] = from_f<DT>(x[e]);
+}
+
+hipError_t launch_qk_norm_rope(void* q, void* k, int B, int heads, int T, int dh, int dtype,
+                               int qk_norm, float eps, int rope, int gf, int gh, int gw,
+                               hipStream_t s) {
+  (void)gf;
+  int64_t rows = (int64_t)B * heads * T;
+  int blocks = (int)((2 * rows + 255) / 256);
+  if (rows <= 0) return hipSuccess;
+  if (dh == 72) {
+    if (dtype == 1)
+      qk_norm_rope_kernel<72, bf16_t><<<blocks, 256, 0, s>>>((bf16_t*)q, (bf16_t*)k, rows, T,
+                                                             qk_norm, eps, rope, gh, gw);
+    else
+      qk_norm_rope_kernel<72, float><<<blocks, 256, 0, s>>>((float*)q, (float*)k, rows, T,
+                                                            qk_norm, eps, rope, gh, gw);
+  } else if (dh == 64) {
+    if (rope) return hipErrorInvalidValue;
+    if (dtype == 1)
+      qk_norm_rope_kernel<64, bf16_t><<<blocks, 256, 0, s>>>((bf16_t*)q, (bf16_t*)k, rows, T,
+                                                             qk_norm, eps, 0, gh, gw);
+    else
+      qk_norm_rope_kernel<64, float><<<blocks, 256, 0, s>>>((float*)q, (float*)k, rows, T,
+                                                            qk_norm, eps, 0, gh, gw);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}

@@ -1,0 +1,226 @@
+"""Python binding over the C ABI: device memory and streams come from torch;
+every step of the forward pass runs in the HIP library.
+
+    model = DiT(cfg, weights)          # uploads weights, dit_create
+    eps = model.forward(x_t, t, y)     # dit_forward
+    eps = model.cfg_forward(x_t, t, y, scale=1.5, guided=4)   # dit_cfg_forward
+
+``cfg`` is a dict with keys C, Cout, F, H, W, p, pt, d, N, heads, mlp_hidden,
+num_classes, cond_dim, freq_dim, qk_norm, rope3d, dtype (0 fp32, 1 bf16),
+ln_eps.  ``weights`` maps the names of ``dit_weights`` to arrays in the
+layouts of ``include/dit.h``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+import torch
+
+from . import _lib
+
+GEMM_WEIGHTS = ("pe_w", "t1_w", "t2_w", "pool_w", "ada_w", "qkv_w", "o_w", "fc1_w", "fc2_w",
+                "out_w")
+
+
+def torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == _lib.DIT_BF16 else torch.float32
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> C.c_void_p:
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def config_struct(cfg: dict) -> _lib.DitConfig:
+    return _lib.DitConfig(
+        in_channels=cfg["C"], out_channels=cfg["Cout"], frames=cfg["F"], height=cfg["H"],
+        width=cfg["W"], patch=cfg["p"], patch_t=cfg["pt"], hidden=cfg["d"], depth=cfg["N"],
+        heads=cfg["heads"], mlp_hidden=cfg["mlp_hidden"], num_classes=cfg["num_classes"],
+        cond_dim=cfg["cond_dim"], freq_dim=cfg["freq_dim"], qk_norm=cfg["qk_norm"],
+        rope3d=cfg["rope3d"], dtype=cfg["dtype"], ln_eps=cfg["ln_eps"])
+
+
+def upload(a, dtype: torch.dtype, device) -> torch.Tensor:
+    """Host array -> contiguous device tensor of ``dtype``."""
+    if isinstance(a, torch.Tensor):
+        return a.to(device=device, dtype=dtype).contiguous()
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dtype).to(device)
+
+
+class DiT:
+    def __init__(self, cfg: dict, weights: dict, device="cuda"):
+        self.lib = _lib.load()
+        self.cfg = dict(cfg)
+        self.device = torch.device(device)
+        self.dtype = torch_dtype(cfg["dtype"])
+        self.tensors = {}
+        for k, a in weights.items():
+            dt = self.dtype if k in GEMM_WEIGHTS else torch.float32
+            self.tensors[k] = upload(a, dt, self.device)
+        self._config = config_struct(cfg)
+        self._weights = _lib.DitWeights(**{
+            k: (self.tensors[k].data_ptr() if k in self.tensors else None)
+            for k in _lib.WEIGHT_FIELDS})
+        h = C.c_void_p()
+        _lib.check(self.lib.dit_create(C.byref(self._config), C.byref(self._weights), C.byref(h)))
+        self.handle = h
+        self._ws = None
+        self.T = (cfg["F"] // cfg["pt"]) * (cfg["H"] // cfg["p"]) * (cfg["W"] // cfg["p"])
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            self.lib.dit_destroy(h)
+            self.handle = None
+
+    # -- memory ---------------------------------------------------------------
+    def workspace_bytes(self, rows: int) -> int:
+        n = C.c_size_t()
+        _lib.check(self.lib.dit_workspace_size(self.handle, rows, C.byref(n)))
+        return n.value
+
+    def workspace(self, rows: int) -> torch.Tensor:
+        n = self.workspace_bytes(rows)
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = None
+            self._ws = torch.empty(n, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def out_shape(self, rows: int):
+        c = self.cfg
+        if c["F"] > 1 or c["rope3d"]:
+            return (rows, c["Cout"], c["F"], c["H"], c["W"])
+        return (rows, c["Cout"], c["H"], c["W"])
+
+    def make_taps(self, rows: int) -> dict:
+        c, M = self.cfg, rows * self.T
+        kout = c["pt"] * c["p"] * c["p"] * c["Cout"]
+        f = dict(device=self.device, dtype=torch.float32)
+        return dict(c=torch.empty(rows, c["d"], **f),
+                    mod=torch.empty(rows, (6 * c["N"] + 2) * c["d"], **f),
+                    x_embed=torch.empty(M, c["d"], **f),
+                    x_blocks=torch.empty(c["N"], M, c["d"], **f),
+                    y_final=torch.empty(M, kout, **f))
+
+    @staticmethod
+    def _taps_struct(taps):
+        if taps is None:
+            return None
+        return C.byref(_lib.DitTaps(**{k: (v.data_ptr() if v is not None else None)
+                                        for k, v in taps.items()}))
+
+    # -- forward passes ----------------------------------------------------------
+    def forward(self, x_t, t, y=None, pooled=None, out=None, taps=None) -> torch.Tensor:
+        B = x_t.shape[0]
+        self._check_input(x_t, t, y, pooled, B)
+        if out is None:
+            out = torch.empty(self.out_shape(B), device=self.device, dtype=torch.float32)
+        ws = self.workspace(B)
+        if taps is None:
+            rc = self.lib.dit_forward(self.handle, _ptr(x_t), _ptr(t), _ptr(y), _ptr(pooled), B,
+                                      _ptr(out), _ptr(ws), ws.numel(), _stream(self.device))
+        else:
+            rc = self.lib.dit_forward_taps(self.handle, _ptr(x_t), _ptr(t), _ptr(y), _ptr(pooled),
+                                           B, _ptr(out), self._taps_struct(taps), _ptr(ws),
+                                           ws.numel(), _stream(self.device))
+        _lib.check(rc)
+        return out
+
+    def cfg_forward(self, x_t, t, y, scale: float, guided: int, out=None, taps=None):
+        Bh = x_t.shape[0]
+        self._check_input(x_t, t, y, None, Bh)
+        if out is None:
+            out = torch.empty(self.out_shape(Bh), device=self.device, dtype=torch.float32)
+        ws = self.workspace(2 * Bh)
+        if taps is None:
+            rc = self.lib.dit_cfg_forward(self.handle, _ptr(x_t), _ptr(t), _ptr(y), Bh,
+                                          float(scale), int(guided), _ptr(out), _ptr(ws),
+                                          ws.numel(), _stream(self.device))
+        else:
+            rc = self.lib.dit_cfg_forward_taps(self.handle, _ptr(x_t), _ptr(t), _ptr(y), Bh,
+                                               float(scale), int(guided), _ptr(out),
+                                               self._taps_struct(taps), _ptr(ws), ws.numel(),
+                                               _stream(self.device))
+        _lib.check(rc)
+        return out
+
+    def block_forward(self, layer: int, X, mod, X_out=None, o_branch=None, f_branch=None):
+        B = mod.shape[0]
+        if X_out is None:
+            X_out = torch.empty_like(X)
+        ws = self.workspace(B)
+        _lib.check(self.lib.dit_block_forward(self.handle, layer, B, _ptr(X), _ptr(mod),
+                                              _ptr(X_out), _ptr(o_branch), _ptr(f_branch),
+                                              _ptr(ws), ws.numel(), _stream(self.device)))
+        return X_out
+
+    def _check_input(self, x_t, t, y, pooled, B):
+        for name, a in (("x_t", x_t), ("t", t), ("y", y), ("pooled", pooled)):
+            if a is not None and (a.device != self.device or not a.is_contiguous()):
+                raise ValueError(f"{name} must be a contiguous tensor on {self.device}")
+        if x_t.dtype != self.dtype:
+            raise TypeError(f"x_t must be {self.dtype}")
+        if t.dtype != torch.float32 or t.numel() != B:
+            raise TypeError("t must be float32 with one entry per row")
+        if y is not None and (y.dtype != torch.int32 or y.numel() != B):
+            raise TypeError("y must be int32 with one entry per row")
+        if pooled is not None and pooled.dtype != torch.float32:
+            raise TypeError("pooled must be float32")
+
+
+# ---------------------------------------------------------------------------
+# Standalone steps (the same device code as the fused forward pass)
+
+def patchify(x: torch.Tensor, p: int, pt: int = 1) -> torch.Tensor:
+    lib = _lib.load()
+    x5 = x if x.dim() == 5 else x.unsqueeze(2)
+    B, Cc, F, H, W = x5.shape
+    code = _lib.DIT_BF16 if x.dtype == torch.bfloat16 else _lib.DIT_F32
+    T, K = (F // pt) * (H // p) * (W // p), pt * p * p * Cc
+    P = torch.empty(B, T, K, dtype=x.dtype, device=x.device)
+    _lib.check(lib.dit_patchify(_ptr(x5.contiguous()), B, Cc, F, H, W, p, pt, code, _ptr(P),
+                                _stream(x.device)))
+    return P
+
+
+def unpatchify(Y: torch.Tensor, Cout: int, F: int, H: int, W: int, p: int, pt: int = 1):
+    lib = _lib.load()
+    B = Y.shape[0]
+    out = torch.empty(B, Cout, F, H, W, dtype=torch.float32, device=Y.device)
+    _lib.check(lib.dit_unpatchify(_ptr(Y.contiguous()), B, Cout, F, H, W, p, pt, _ptr(out),
+                                  _stream(Y.device)))
+    return out
+
+
+def timestep_embed(t: torch.Tensor, dim: int = 256) -> torch.Tensor:
+    lib = _lib.load()
+    e = torch.empty(t.numel(), dim, dtype=torch.float32, device=t.device)
+    _lib.check(lib.dit_timestep_embed(_ptr(t.contiguous()), t.numel(), dim, _ptr(e),
+                                      _stream(t.device)))
+    return e
+
+
+def attention(q, k, v_lib, T: int) -> torch.Tensor:
+    """q, k [B, H, T, dh]; v_lib in the library's V layout (bf16: [B, H, dh, ldv],
+    ldv = T rounded up to 64; fp32: [B, H, T, dh]).  Returns [B, T, H*dh]."""
+    lib = _lib.load()
+    B, H, _, dh = q.shape
+    code = _lib.DIT_BF16 if q.dtype == torch.bfloat16 else _lib.DIT_F32
+    o = torch.empty(B, T, H * dh, dtype=q.dtype, device=q.device)
+    _lib.check(lib.dit_attention(_ptr(q), _ptr(k), _ptr(v_lib), B, H, T, dh, code, _ptr(o),
+                                 _stream(q.device)))
+    return o
+
+
+def linear(epilogue: int, A, W, bias, out, gate=None, gate_stride=0, T=1):
+    lib = _lib.load()
+    M, K = A.shape
+    N = W.shape[0]
+    code = _lib.DIT_BF16 if A.dtype == torch.bfloat16 else _lib.DIT_F32
+    _lib.check(lib.dit_linear(epilogue, _ptr(A), _ptr(W), _ptr(bias), M, N, K, code, _ptr(out),
+                              _ptr(gate), gate_stride, T, _stream(A.device)))
+    return out

@@ -1,0 +1,232 @@
+/*
+ * dit.h - C ABI of the MI355X (gfx950) DiT denoiser forward library.
+ *
+ * The library computes the Diffusion Transformer (DiT) denoiser forward pass
+ * and the classifier-free-guidance combine on one GPU:
+ *
+ *   patchify of a noisy latent into T = (I/p)^2 tokens, linear embedding and
+ *   2-D sine-cosine position embedding
+ *     (itwiki "확산 트랜스포머" (Diffusion Transformer), section Structure /
+ *      Latent space and patchify; cv-learn "Sora / DiT", Method bullets);
+ *   conditioning vector c = timestep embedding + class embedding
+ *     (same itwiki page, section adaLN-Zero);
+ *   N adaLN-Zero blocks
+ *       x <- x + a1 * Attn(LN(x)(1 + g1) + b1)
+ *       x <- x + a2 * FFN(LN(x)(1 + g2) + b2),  (b1,g1,a1,b2,g2,a2) = Linear(SiLU(c))
+ *     (same page, adaLN-Zero equations and Implementation / adaLN-Zero block);
+ *   final LayerNorm + adaLN modulation + linear decoder to p x p x Cout per
+ *   token, unpatchify (same page, Latent space and patchify);
+ *   guidance  eps_hat = eps(null) + s * (eps(c) - eps(null))
+ *     (cv-learn "Sora / DiT", classifier-free guidance bullet), optionally on
+ *     the first channels only (itwiki page, ImageNet results notes);
+ *   spacetime latents: 3-D patches, full attention with Q-K normalisation and
+ *   3-D rotary embedding, pooled-vector conditioning
+ *     (blog.outta.ai GOKU review, section 2.2; itwiki page, MMDiT section).
+ *
+ * Conventions
+ *   - Every entry point returns an int status (DIT_OK or a negative code).
+ *     All arguments are validated before the first kernel launch; on an error
+ *     nothing is launched and nothing is written.  dit_last_error_message()
+ *     returns a thread-local description of the last error.
+ *   - Device pointers are plain HIP device addresses owned by the caller
+ *     (weights, inputs, outputs, workspace).  They must stay valid until the
+ *     enqueued work has completed.  The library never allocates or frees
+ *     device memory and never changes the current device.
+ *   - Work is enqueued on the caller's stream (a hipStream_t passed as void*;
+ *     NULL is the default stream) and never synchronises it.  A device fault
+ *     surfaces at the caller's next synchronisation.
+ *   - A handle is immutable after dit_create; it may be used from several
+ *     threads/streams at once if every call has its own workspace.
+ *   - No C++ exception crosses this interface.
+ *
+ * Tensor layouts (row-major, last index fastest)
+ *   Linear weights      [out, in]   in the model dtype (fp32 or bf16)
+ *   biases, class table fp32
+ *   x_t                 [B, C, H, W] (frames == 1) or [B, C, F, H, W], model dtype
+ *   t                   [B] fp32 (diffusion step 0..999, or flow time in (0,1))
+ *   y                   [B] int32 class ids in [0, num_classes]; num_classes is
+ *                       the null label.  Labels are not read on the host: a
+ *                       label out of range makes that row's output NaN.
+ *   pooled              [B, cond_dim] fp32
+ *   out                 [B, Cout, H, W] or [B, Cout, F, H, W] fp32
+ *   token order         raster over (frame, row, col) of the patch grid
+ *   patch vector order  (frame offset, row offset, col offset, channel), channel
+ *                       fastest, for pe_w's input and out_w's output.
+ */
+#ifndef DIT_H
+#define DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define DIT_OK            0
+#define DIT_EINVAL       -1  /* null pointer, bad size, shape not divisible, ... */
+#define DIT_EUNSUPPORTED -2  /* valid but without a kernel (head dim, width, dtype) */
+#define DIT_EWORKSPACE   -3  /* workspace pointer null or too small */
+#define DIT_EHIP         -4  /* a HIP launch reported an error */
+
+/* dtypes */
+#define DIT_F32  0
+#define DIT_BF16 1
+
+/* Model configuration.  Supported: hidden % 128 == 0, hidden <= 2048,
+ * head dim hidden/heads in {64, 72}, mlp_hidden % 64 == 0, freq_dim even.
+ * rope3d needs head dim divisible by 6 with an even third (72 works);
+ * without rope3d a 2-D sin-cos position embedding is added and the latent
+ * must have frames / patch_t == 1. */
+typedef struct dit_config {
+  int in_channels;   /* C */
+  int out_channels;  /* Cout (2C: noise + diagonal covariance; C for velocity) */
+  int frames;        /* F (1 for images) */
+  int height;        /* H (= I for square images) */
+  int width;         /* W */
+  int patch;         /* p */
+  int patch_t;       /* temporal patch extent (1 for images) */
+  int hidden;        /* d */
+  int depth;         /* N blocks */
+  int heads;
+  int mlp_hidden;    /* FFN hidden width (4d) */
+  int num_classes;   /* class table rows - 1 (row num_classes = null label); 0 = no table */
+  int cond_dim;      /* pooled conditioning width (0 = none) */
+  int freq_dim;      /* timestep sinusoid width (256) */
+  int qk_norm;       /* 1: LayerNorm over each head's q and k before attention */
+  int rope3d;        /* 1: 3-D rotary embedding on q,k; no additive position embedding */
+  int dtype;         /* DIT_F32 or DIT_BF16: GEMM operand / activation dtype */
+  float ln_eps;      /* LayerNorm epsilon (1e-6) */
+} dit_config;
+
+/* Caller-owned device pointers.  "W" = model dtype, "f32" = float.
+ * Shapes with N = depth, d = hidden, Kin = patch_t*patch*patch*C,
+ * Kout = patch_t*patch*patch*Cout, hid = mlp_hidden. */
+typedef struct dit_weights {
+  const void*  pe_w;    /* W   [d, Kin]       patch embedding */
+  const float* pe_b;    /* f32 [d] */
+  const void*  t1_w;    /* W   [d, freq_dim]  timestep MLP layer 1 */
+  const float* t1_b;    /* f32 [d] */
+  const void*  t2_w;    /* W   [d, d]         timestep MLP layer 2 */
+  const float* t2_b;    /* f32 [d] */
+  const float* y_table; /* f32 [num_classes + 1, d] (NULL if num_classes == 0) */
+  const void*  pool_w;  /* W   [d, cond_dim]  (NULL if cond_dim == 0) */
+  const float* pool_b;  /* f32 [d]            (NULL if cond_dim == 0) */
+  const void*  ada_w;   /* W   [(6N + 2) d, d] modulation of all blocks, then final layer;
+                           block l rows: b1, g1, a1, b2, g2, a2 (d rows each) at 6 d l;
+                           final rows: b_f, g_f at 6 d N */
+  const float* ada_b;   /* f32 [(6N + 2) d] */
+  const void*  qkv_w;   /* W   [N, 3d, d]  packed q | k | v, heads as contiguous slices */
+  const float* qkv_b;   /* f32 [N, 3d] */
+  const void*  o_w;     /* W   [N, d, d] */
+  const float* o_b;     /* f32 [N, d] */
+  const void*  fc1_w;   /* W   [N, hid, d] */
+  const float* fc1_b;   /* f32 [N, hid] */
+  const void*  fc2_w;   /* W   [N, d, hid] */
+  const float* fc2_b;   /* f32 [N, d] */
+  const void*  out_w;   /* W   [Kout, d]  linear decoder */
+  const float* out_b;   /* f32 [Kout] */
+} dit_weights;
+
+typedef struct dit_handle dit_handle;
+
+/* Optional intermediate outputs of the trunk (device pointers, any may be
+ * NULL).  M = trunk rows * T. */
+typedef struct dit_taps {
+  float* c;         /* [rows, d]            conditioning vector */
+  float* mod;       /* [rows, (6N + 2) d]   all modulation vectors */
+  float* x_embed;   /* [M, d]               tokens after patch + position embedding */
+  float* x_blocks;  /* [N, M, d]            residual stream after each block */
+  float* y_final;   /* [M, Kout]            decoder output before unpatchify */
+} dit_taps;
+
+/* Validate cfg, record the weight pointers and plan the kernels.  Allocates
+ * only the host-side handle.  Returns DIT_EINVAL / DIT_EUNSUPPORTED on a bad
+ * or unsupported configuration. */
+int dit_create(const dit_config* cfg, const dit_weights* w, dit_handle** out);
+
+/* Free the host handle (NULL is ignored). */
+void dit_destroy(dit_handle* h);
+
+/* Workspace bytes for a trunk of `rows` rows (dit_forward: rows = B;
+ * dit_cfg_forward: rows = 2 * Bh). */
+int dit_workspace_size(const dit_handle* h, int rows, size_t* bytes);
+
+/* eps_theta(x_t, t, c) for B rows.  y must be non-NULL iff num_classes > 0,
+ * pooled non-NULL iff cond_dim > 0.  out: [B, Cout, (F,) H, W] fp32. */
+int dit_forward(dit_handle* h, const void* x_t, const float* t, const int32_t* y,
+                const float* pooled, int B, float* out, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* Guided prediction for Bh rows.  The trunk runs 2 Bh rows: row i < Bh with
+ * label y[i], row Bh + i with the null label, both reading x_t[i] and t[i].
+ * out[i, ch] = u + s (c - u) for ch < guided_channels (c = conditional row,
+ * u = null row), out[i, ch] = c for ch >= guided_channels.
+ * Needs num_classes > 0 and 1 <= guided_channels <= Cout. */
+int dit_cfg_forward(dit_handle* h, const void* x_t, const float* t, const int32_t* y, int Bh,
+                    float s, int guided_channels, float* out, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* dit_forward / dit_cfg_forward that also write the taps (may be NULL). */
+int dit_forward_taps(dit_handle* h, const void* x_t, const float* t, const int32_t* y,
+                     const float* pooled, int B, float* out, const dit_taps* taps, void* ws,
+                     size_t ws_bytes, void* stream);
+int dit_cfg_forward_taps(dit_handle* h, const void* x_t, const float* t, const int32_t* y,
+                         int Bh, float s, int guided_channels, float* out,
+                         const dit_taps* taps, void* ws, size_t ws_bytes, void* stream);
+
+const char* dit_status_string(int status);
+const char* dit_last_error_message(void);
+
+/* ---- Standalone entry points of single path steps (tests, benchmarks) ----
+ * Each runs the same device code as the fused forward. */
+
+/* P[b, tau, k] = x[b, c, f*pt + a, i*p + py, j*p + px], tau = (f*gh + i)*gw + j,
+ * k = ((a*p + py)*p + px)*C + c.  x: [B, C, F, H, W]; P: [B, T, pt*p*p*C], both
+ * in `dtype` (a bit-exact copy). */
+int dit_patchify(const void* x, int B, int C, int F, int H, int W, int p, int pt, int dtype,
+                 void* P, void* stream);
+
+/* Inverse index map for Cout channels: out[b, c, f, y, x] = Y[b, tau, k].
+ * Y: [B, T, pt*p*p*Cout] fp32; out: [B, Cout, F, H, W] fp32. */
+int dit_unpatchify(const float* Y, int B, int Cout, int F, int H, int W, int p, int pt,
+                   float* out, void* stream);
+
+/* e[b] = [cos(t_b f_k) | sin(t_b f_k)], f_k = 10000^(-k/(dim/2)), dim even.
+ * t: [B] fp32; e: [B, dim] fp32. */
+int dit_timestep_embed(const float* t, int B, int dim, float* e, void* stream);
+
+/* Multi-head attention core softmax(q k^T / sqrt(dh)) v for every (b, h).
+ * q, k: [B, H, T, dh].  v: bf16 -> [B, H, dh, ldv] (keys fastest, ldv =
+ * T rounded up to a multiple of 64); fp32 -> [B, H, T, dh].
+ * o: [B, T, H*dh] (token-major, heads concatenated), same dtype.  dh in {64, 72}. */
+int dit_attention(const void* q, const void* k, const void* v, int B, int H, int T, int dh,
+                  int dtype, void* o, void* stream);
+
+/* Linear layer with one of the fused epilogues of the forward pass,
+ * out = epilogue(A W^T + bias): A [M, K] and W [N, K] in `dtype`.
+ *   DIT_EPI_BIAS:  out fp32 [M, N] = A W^T + bias
+ *   DIT_EPI_GELU:  out dtype [M, N] = GELU_tanh(A W^T + bias)
+ *   DIT_EPI_GATED: out fp32 [M, N] += gate[(m / T) * gate_stride + n] * (A W^T + bias)
+ * bf16 requires K % 64 == 0.  Uses the kernels and tiles of the forward pass. */
+#define DIT_EPI_BIAS  0
+#define DIT_EPI_GELU  1
+#define DIT_EPI_GATED 2
+int dit_linear(int epilogue, const void* A, const void* W, const float* bias, int M, int N,
+               int K, int dtype, void* out, const float* gate, int gate_stride, int T,
+               void* stream);
+
+/* One block, teacher-forced: X_out = block_l(X_in) with the given modulation
+ * vectors mod [B, 6d] (b1, g1, a1, b2, g2, a2).  X_in, X_out: [B*T, d] fp32
+ * (may alias).  o_branch / f_branch (fp32 [B*T, d], may be NULL) receive the
+ * attention and FFN branches before their gates.  ws as for dit_forward with
+ * rows = B. */
+int dit_block_forward(dit_handle* h, int layer, int B, const float* X_in, const float* mod,
+                      float* X_out, float* o_branch, float* f_branch, void* ws,
+                      size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DIT_H */

@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/dit.h, and rejects bad arguments before any launch."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit.h")
+
+from diffusion_transformer_denoiser_amd import _lib  # noqa: E402
+
+needs_lib = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                               reason="libdit.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dit_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("dit_create", "dit_destroy", "dit_workspace_size", "dit_forward", "dit_cfg_forward",
+              "dit_status_string", "dit_patchify", "dit_unpatchify", "dit_timestep_embed",
+              "dit_attention", "dit_linear", "dit_block_forward"):
+        assert n in names
+    assert set(names) == set(_lib.EXPORTS), "binding and header disagree"
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = C.CDLL(_lib.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+@needs_lib
+def test_config_struct_size_matches_header():
+    # 17 ints + 1 float
+    assert C.sizeof(_lib.DitConfig) == 18 * 4
+    assert C.sizeof(_lib.DitWeights) == 21 * C.sizeof(C.c_void_p)
+
+
+def _cfg(**kw):
+    base = dict(in_channels=4, out_channels=8, frames=1, height=32, width=32, patch=2, patch_t=1,
+                hidden=1152, depth=2, heads=16, mlp_hidden=4608, num_classes=1000, cond_dim=0,
+                freq_dim=256, qk_norm=0, rope3d=0, dtype=1, ln_eps=1e-6)
+    base.update(kw)
+    return _lib.DitConfig(**base)
+
+
+def _weights(**null):
+    # dummy, 256-aligned, never dereferenced by the host code
+    w = _lib.DitWeights(**{k: 0x100000 + 256 * i for i, k in enumerate(_lib.WEIGHT_FIELDS)})
+    for k in null:
+        setattr(w, k, None)
+    return w
+
+
+def _create(cfg, w):
+    lib = _lib.load()
+    h = C.c_void_p()
+    rc = lib.dit_create(C.byref(cfg), C.byref(w), C.byref(h))
+    return rc, h
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(height=33), _lib.DIT_EINVAL),            # I % p != 0
+    (dict(hidden=1150), _lib.DIT_EINVAL),          # d % heads != 0
+    (dict(heads=12), _lib.DIT_EUNSUPPORTED),       # head dim 96
+    (dict(hidden=576, heads=9), _lib.DIT_EUNSUPPORTED),   # d % 128 != 0
+    (dict(dtype=7), _lib.DIT_EINVAL),
+    (dict(freq_dim=255), _lib.DIT_EINVAL),
+    (dict(depth=0), _lib.DIT_EINVAL),
+    (dict(frames=4), _lib.DIT_EUNSUPPORTED),       # 2-D PE with several frames
+    (dict(rope3d=1, hidden=1024), _lib.DIT_EUNSUPPORTED),  # RoPE thirds of dh 64
+    (dict(ln_eps=0.0), _lib.DIT_EINVAL),
+])
+def test_create_rejects_bad_configs(kw, code):
+    rc, h = _create(_cfg(**kw), _weights())
+    assert rc == code and not h.value
+    assert _lib.load().dit_last_error_message()
+
+
+@needs_lib
+def test_create_rejects_missing_weights():
+    rc, _ = _create(_cfg(), _weights(y_table=1))
+    assert rc == _lib.DIT_EINVAL
+    rc, _ = _create(_cfg(), _weights(fc2_w=1))
+    assert rc == _lib.DIT_EINVAL
+    rc, _ = _create(_cfg(cond_dim=4096), _weights(pool_w=1))
+    assert rc == _lib.DIT_EINVAL
+
+
+@needs_lib
+def test_forward_validates_before_launch():
+    lib = _lib.load()
+    rc, h = _create(_cfg(), _weights())
+    assert rc == _lib.DIT_OK
+    try:
+        need = C.c_size_t()
+        assert lib.dit_workspace_size(h, 64, C.byref(need)) == 0
+        assert need.value > 100 << 20            # ~0.4 GB at this size
+        p = C.c_void_p(0x200000)
+        # B <= 0, null pointers, missing labels, small workspace: no launch, codes only.
+        assert lib.dit_forward(h, p, p, p, None, 0, p, p, need.value, None) == _lib.DIT_EINVAL
+        assert lib.dit_forward(h, None, p, p, None, 4, p, p, need.value, None) == _lib.DIT_EINVAL
+        assert lib.dit_forward(h, p, p, None, None, 4, p, p, need.value, None) == _lib.DIT_EINVAL
+        assert lib.dit_forward(h, p, p, p, None, 64, p, p, need.value - 1, None) == _lib.DIT_EWORKSPACE
+        assert lib.dit_forward(h, p, p, p, None, 64, p, None, need.value, None) == _lib.DIT_EWORKSPACE
+        assert lib.dit_cfg_forward(h, p, p, p, 32, 1.5, 0, p, p, need.value, None) == _lib.DIT_EINVAL
+        assert lib.dit_cfg_forward(h, p, p, p, 32, 1.5, 9, p, p, need.value, None) == _lib.DIT_EINVAL
+        assert lib.dit_cfg_forward(h, p, p, p, 32, float("nan"), 4, p, p, need.value, None) == _lib.DIT_EINVAL
+        assert lib.dit_cfg_forward(h, p, p, p, 33, 1.5, 4, p, p, need.value, None) == _lib.DIT_EWORKSPACE
+        assert lib.dit_block_forward(h, 2, 4, p, p, p, None, None, p, need.value, None) == _lib.DIT_EINVAL
+    finally:
+        lib.dit_destroy(h)
+
+
+@needs_lib
+def test_standalone_steps_validate_before_launch():
+    lib = _lib.load()
+    p = C.c_void_p(0x200000)
+    assert lib.dit_patchify(p, 1, 4, 1, 33, 32, 2, 1, 1, p, None) == _lib.DIT_EINVAL
+    assert lib.dit_patchify(None, 1, 4, 1, 32, 32, 2, 1, 1, p, None) == _lib.DIT_EINVAL
+    assert lib.dit_unpatchify(p, 1, 8, 3, 32, 32, 2, 2, p, None) == _lib.DIT_EINVAL
+    assert lib.dit_timestep_embed(p, 4, 255, p, None) == _lib.DIT_EINVAL
+    assert lib.dit_attention(p, p, p, 1, 2, 16, 96, 1, p, None) == _lib.DIT_EUNSUPPORTED
+    assert lib.dit_linear(9, p, p, None, 4, 4, 64, 1, p, None, 0, 1, None) == _lib.DIT_EINVAL
+    assert lib.dit_linear(0, p, p, None, 4, 4, 48, 1, p, None, 0, 1, None) == _lib.DIT_EUNSUPPORTED
+    assert lib.dit_linear(2, p, p, None, 4, 4, 64, 1, p, None, 0, 1, None) == _lib.DIT_EINVAL
+    assert lib.dit_status_string(_lib.DIT_EWORKSPACE) == b"workspace missing or too small"

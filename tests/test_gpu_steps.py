@@ -1,0 +1,168 @@
+"""GPU parity of single path steps against the oracle, through the C ABI.
+
+Bit-exact: patchify / unpatchify (index work).  fp32 steps: relative L2
+<= 1e-4 (the timestep sinusoid: absolute 1e-6).  bf16 products: compared with
+fp64 products of the same bf16-rounded operands.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dit_inputs
+import oracle
+from tests.parity import log, np_, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+dmod = pytest.importorskip("diffusion_transformer_denoiser_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dmod.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _bf16(a):
+    return dit_inputs.bf16_round(np.asarray(a, dtype=np.float32))
+
+
+# --- patchify / unpatchify: bit-exact ------------------------------------------------
+
+@pytest.mark.parametrize("shape,p,pt,dt", [
+    ((2, 4, 1, 32, 32), 8, 1, torch.float32), ((32, 4, 1, 32, 32), 2, 1, torch.bfloat16),
+    ((8, 4, 1, 64, 64), 2, 1, torch.bfloat16), ((1, 16, 16, 60, 104), 2, 1, torch.bfloat16),
+    ((3, 5, 4, 6, 10), 2, 2, torch.float32), ((1, 3, 1, 6, 6), 3, 1, torch.float32)])
+def test_patchify_bit_exact(shape, p, pt, dt):
+    log(f"patchify {shape} p={p} pt={pt} {dt}")
+    rng = np.random.default_rng(sum(shape))
+    x = rng.standard_normal(shape).astype(np.float32)
+    if dt == torch.bfloat16:
+        x = _bf16(x)
+    xd = torch.from_numpy(x).to(dt).cuda()
+    P = np_(dmod.patchify(xd, p, pt))
+    ref = oracle.patchify(x, p, pt)
+    assert P.shape == ref.shape and np.array_equal(P, ref)
+
+
+@pytest.mark.parametrize("B,Cout,F,H,W,p,pt", [(2, 8, 1, 32, 32, 8, 1), (64, 8, 1, 32, 32, 2, 1),
+                                               (1, 16, 16, 60, 104, 2, 1), (2, 3, 4, 6, 10, 2, 2)])
+def test_unpatchify_bit_exact_and_round_trip(B, Cout, F, H, W, p, pt):
+    log(f"unpatchify B={B} Cout={Cout} F={F} H={H} W={W} p={p} pt={pt}")
+    T = (F // pt) * (H // p) * (W // p)
+    rng = np.random.default_rng(T)
+    Y = rng.standard_normal((B, T, pt * p * p * Cout)).astype(np.float32)
+    out = np_(dmod.unpatchify(torch.from_numpy(Y).cuda(), Cout, F, H, W, p, pt))
+    ref = oracle.unpatchify(Y, Cout, F, H, W, p, pt, frames_axis=True)
+    assert np.array_equal(out, ref)
+    back = np_(dmod.patchify(torch.from_numpy(out).cuda(), p, pt))
+    assert np.array_equal(back, Y)
+
+
+# --- timestep sinusoid ----------------------------------------------------------------
+
+def test_timestep_embedding():
+    t = np.array([0, 1, 17, 500, 999, 0.25, 0.731], dtype=np.float32)
+    e = np_(dmod.timestep_embed(torch.from_numpy(t).cuda(), 256))
+    ref = oracle.timestep_embedding(t.astype(np.float64), 256)
+    err = np.abs(e - ref).max()
+    log(f"timestep max abs err {err:.2e}")
+    assert err <= 1e-6
+    assert np.array_equal(e[0, :128], np.ones(128, np.float32))
+
+
+# --- linear layers (bf16 MFMA, fp32 VALU) ------------------------------------------------
+
+LIN_SHAPES = [(64, 128, 64), (300, 200, 128), (257, 1152, 1152), (1024, 4608, 1152),
+              (512, 1152, 4608), (64, 3456, 1152), (33, 96, 320)]
+
+
+@pytest.mark.parametrize("M,N,K", LIN_SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_linear_epilogues(M, N, K, dtype):
+    if dtype == "bf16" and K % 64:
+        pytest.skip("bf16 needs K % 64 == 0")
+    log(f"linear {dtype} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 7 + N + K)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    W = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    if dtype == "bf16":
+        A, W = _bf16(A), _bf16(W)
+    Ad = torch.from_numpy(A).to(tdt).cuda()
+    Wd = torch.from_numpy(W).to(tdt).cuda()
+    bd = torch.from_numpy(bias).cuda()
+    ref = A.astype(np.float64) @ W.astype(np.float64).T + bias
+    tol = 2e-6 if dtype == "f32" else 1e-5
+
+    out = torch.full((M, N), float("nan"), device="cuda")
+    dmod.linear(dmod.DIT_EPI_BIAS, Ad, Wd, bd, out)
+    e1 = rel_l2(np_(out), ref)
+
+    g = torch.empty((M, N), device="cuda", dtype=tdt)
+    dmod.linear(dmod.DIT_EPI_GELU, Ad, Wd, bd, g)
+    e2 = rel_l2(np_(g), oracle.gelu_tanh(ref))
+
+    T = 16
+    rows = (M + T - 1) // T
+    gate = rng.standard_normal((rows, N + 8)).astype(np.float32)
+    X0 = rng.standard_normal((M, N)).astype(np.float32)
+    X = torch.from_numpy(X0).cuda()
+    dmod.linear(dmod.DIT_EPI_GATED, Ad, Wd, bd, X, gate=torch.from_numpy(gate).cuda(),
+                gate_stride=N + 8, T=T)
+    gref = X0 + gate[np.arange(M) // T, :N] * ref
+    e3 = rel_l2(np_(X) - X0, gref - X0)
+    log(f"  rel-L2 bias={e1:.2e} gelu={e2:.2e} gated-increment={e3:.2e}")
+    assert e1 <= tol and e3 <= tol
+    assert e2 <= (tol if dtype == "f32" else 4e-3)     # bf16 output rounding
+
+
+# --- attention ---------------------------------------------------------------------------
+
+def _v_layout(v, dtype):
+    if dtype == torch.bfloat16:
+        B, H, T, dh = v.shape
+        ldv = (T + 63) // 64 * 64
+        vt = torch.zeros(B, H, dh, ldv, dtype=v.dtype, device=v.device)
+        vt[..., :T] = v.transpose(2, 3)
+        return vt.contiguous()
+    return v.contiguous()
+
+
+@pytest.mark.parametrize("T", [1, 2, 16, 17, 64, 65, 129, 256, 300])
+@pytest.mark.parametrize("dh", [64, 72])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_attention_matches_oracle(T, dh, dtype):
+    if dtype == torch.float32 and T > 129:
+        pytest.skip("small shapes only for the fp32 path")
+    log(f"attention T={T} dh={dh} {dtype}")
+    B, H = 2, 3
+    rng = np.random.default_rng(T * 100 + dh)
+    q, k, v = (rng.standard_normal((B, H, T, dh)).astype(np.float32) * s for s in (1.0, 1.0, 1.0))
+    if dtype == torch.bfloat16:
+        q, k, v = _bf16(q), _bf16(k), _bf16(v)
+    qd, kd, vd = (torch.from_numpy(a).to(dtype).cuda() for a in (q, k, v))
+    o = np_(dmod.attention(qd, kd, _v_layout(vd, dtype), T))
+    ref = oracle.attention(q, k, v).transpose(0, 2, 1, 3).reshape(B, T, H * dh)
+    err = rel_l2(o, ref)
+    log(f"  rel-L2 {err:.2e}")
+    assert err <= (1e-5 if dtype == torch.float32 else 1e-2)
+
+
+def test_attention_special_cases_bf16():
+    # all keys equal => uniform weights => mean of v; T = 1 => v.
+    B, H, T, dh = 1, 2, 100, 72
+    rng = np.random.default_rng(5)
+    q = _bf16(rng.standard_normal((B, H, T, dh)))
+    k = np.repeat(_bf16(rng.standard_normal((B, H, 1, dh))), T, axis=2)
+    v = _bf16(rng.standard_normal((B, H, T, dh)))
+    qd, kd, vd = (torch.from_numpy(a).to(torch.bfloat16).cuda() for a in (q, k, v))
+    o = np_(dmod.attention(qd, kd, _v_layout(vd, torch.bfloat16), T)).reshape(B, T, H, dh)
+    mean = v.astype(np.float64).mean(axis=2)          # [B, H, dh]
+    assert np.abs(o - mean[:, None]).max() < 2e-2
