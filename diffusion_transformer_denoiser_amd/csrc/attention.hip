@@ -4,7 +4,9 @@
 // bf16 path (MFMA, dh in {64, 72}).  A workgroup of 4 waves owns 128 queries of
 // one (batch, head); each wave 32 queries.  Per 64-key tile, staged in LDS:
 //   S^T[key, q] = K Q^T  with v_mfma_f32_16x16x32_bf16 (dh 64..71 of dh = 72 by
-//                        one v_mfma_f32_16x16x16_bf16 with lanes past 72 zeroed),
+//                        a third 16x16x32 step whose lanes past dh 72 hold zeros,
+//                        so every S accumulation is one chain of the same
+//                        instruction, accumulated in place),
 //   online softmax per query column in the exp2 domain,
 //   O^T[dh, q] += V^T P^T with v_mfma_f32_16x16x32_bf16.
 // Computing S transposed leaves each lane holding keys 4g..4g+3 of four 16-key
@@ -18,7 +20,6 @@
 #include "common.h"
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short shortx4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 namespace {
@@ -48,9 +49,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
   const bf16_t* Vb = Vt + (int64_t)bh * DH * ldv;
 
   const bf16x8_t z8 = {};
-  const shortx4_t z4 = {};
   bf16x8_t qf[2][2];
-  shortx4_t qt[2];
+  bf16x8_t qt[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     int q = q0 + 16 * qb + c16;
@@ -58,9 +58,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
 #pragma unroll
     for (int c = 0; c < 2; ++c)
       qf[qb][c] = ok ? *(const bf16x8_t*)(Qb + (int64_t)q * DH + 32 * c + 8 * g) : z8;
-    qt[qb] = z4;
+    qt[qb] = z8;   // dh 64..71 in lanes g == 0, zeros elsewhere
     if constexpr (TAIL)
-      if (ok && g < 2) qt[qb] = *(const shortx4_t*)(Qb + (int64_t)q * DH + 64 + 4 * g);
+      if (ok && g == 0) qt[qb] = *(const bf16x8_t*)(Qb + (int64_t)q * DH + 64);
   }
 
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
@@ -111,15 +111,15 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
       const bf16_t* kr = &sK[(16 * kb + c16) * KLD];
       bf16x8_t k0 = *(const bf16x8_t*)(kr + 8 * g);
       bf16x8_t k1 = *(const bf16x8_t*)(kr + 32 + 8 * g);
-      shortx4_t kt = z4;
+      bf16x8_t kt = z8;
       if constexpr (TAIL)
-        if (g < 2) kt = *(const shortx4_t*)(kr + 64 + 4 * g);
+        if (g == 0) kt = *(const bf16x8_t*)(kr + 64);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         floatx4 a = {0.0f, 0.0f, 0.0f, 0.0f};
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[qb][0], a, 0, 0, 0);
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[qb][1], a, 0, 0, 0);
-        if constexpr (TAIL) a = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kt, qt[qb], a, 0, 0, 0);
+        if constexpr (TAIL) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, qt[qb], a, 0, 0, 0);
         s[kb][qb] = a;
       }
     }

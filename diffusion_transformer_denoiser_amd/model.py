@@ -55,7 +55,10 @@ class DiT:
     def __init__(self, cfg: dict, weights: dict, device="cuda"):
         self.lib = _lib.load()
         self.cfg = dict(cfg)
-        self.device = torch.device(device)
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
         self.dtype = torch_dtype(cfg["dtype"])
         self.tensors = {}
         for k, a in weights.items():

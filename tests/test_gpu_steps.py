@@ -101,7 +101,7 @@ def test_linear_epilogues(M, N, K, dtype):
     ref = A.astype(np.float64) @ W.astype(np.float64).T + bias
     tol = 2e-6 if dtype == "f32" else 1e-5
 
-    out = torch.full((M, N), float("nan"), device="cuda")
+    out = torch.full((M, N), float("nan"), device="cuda", dtype=torch.float32)
     dmod.linear(dmod.DIT_EPI_BIAS, Ad, Wd, bd, out)
     e1 = rel_l2(np_(out), ref)
 

@@ -21,7 +21,16 @@ from einops import rearrange
 import dit_inputs
 import oracle
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _float64_default():
+    # fp64 torch modules for this module's tests only; restored afterwards so the
+    # GPU tests collected in the same session keep torch's fp32 default.
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(old)
 
 
 def tiny_image_cfg(**kw):
