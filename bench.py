@@ -1,0 +1,199 @@
+"""Benchmark: DiT-XL/2 denoiser forwards/s with classifier-free guidance on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one guided forward pass of the whole hot path (dit_cfg_forward):
+32 conditional + 32 null-label rows of a 32x32x4 latent (DiT-XL/2, p = 2,
+T = 256, d = 1152, 28 blocks, 16 heads), guidance scale 1.5 on all 4 noise
+channels; seeded synthetic inputs and N(0, 0.02) weights, resident in HBM
+before timing starts.  Prints one JSON line.
+
+Besides the headline number the line carries
+  roofline      the dominant kernel, timed alone with HIP events on the same
+                stream and launch configuration as in the forward pass;
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on
+                this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "DiT-XL/2 denoiser forwards/s + TFLOP/s (% MFMA peak) on 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dit_xl2_256_cfg")
+    ap.add_argument("--kernel-launches", type=int, default=50,
+                    help="launches of the dominant kernel timed alone")
+    ap.add_argument("--cpu-rows", type=int, default=2,
+                    help="guided rows of the workload the oracle runs for the CPU baseline")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline(cfg, w, inp, rows: int, trunk_rows: int):
+    """fp64 oracle on `rows` guided rows (2*rows trunk rows) of the workload."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.cfg_forward(cfg, w, inp["x_t"][:rows], inp["t"][:rows], inp["y"][:rows],
+                       cfg["scale"], cfg["guided"])
+    dt = time.perf_counter() - t0
+    frac = (2 * rows) / trunk_rows
+    return {"value": frac / dt, "unit": "forwards/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"oracle.cfg_forward (fp64 NumPy) on {rows} of {trunk_rows // 2} guided rows "
+                      f"({2 * rows} of {trunk_rows} trunk rows, all 28 blocks): {dt:.2f} s; "
+                      f"value scaled to whole {trunk_rows}-row forwards"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
+                                   "supported (use --gpus 1)"}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import dit_inputs
+    import diffusion_transformer_denoiser_amd as dm
+    from oracle import flops as oflops   # closed-form MAC count (numbers only)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dm.load()
+    dev = torch.device("cuda", torch.cuda.current_device())
+    cfg = dit_inputs.workload(args.workload)
+    Bh = cfg["batch"]
+    rows = 2 * Bh if cfg["cfg"] else Bh
+    T = dit_inputs.tokens(cfg)
+    w = dit_inputs.make_weights(cfg)
+    inp = dit_inputs.make_inputs(cfg)
+    model = dm.DiT(cfg, w, dev)
+    dt = dm.torch_dtype(cfg["dtype"])
+    x = torch.from_numpy(inp["x_t"]).to(dt).to(dev)
+    t = torch.from_numpy(inp["t"]).to(dev)
+    y = torch.from_numpy(inp["y"]).to(dev) if inp["y"] is not None else None
+    pooled = torch.from_numpy(inp["pooled"]).to(dev) if inp["pooled"] is not None else None
+    out = torch.empty(model.out_shape(Bh), device=dev, dtype=torch.float32)
+
+    def step():
+        if cfg["cfg"]:
+            model.cfg_forward(x, t, y, cfg["scale"], cfg["guided"], out=out)
+        else:
+            model.forward(x, t, y, pooled, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    assert torch.isfinite(out).all().item(), "non-finite output"
+
+    gmac_row = oflops.gmac_for(cfg)
+    flop_fwd = 2.0 * gmac_row * 1e9 * rows
+    tflops = flop_fwd / (ms * 1e-3) / 1e12
+
+    # Dominant kernel: the FFN up-projection (M = rows*T, N = 4d, K = d, bias + tanh-GELU
+    # epilogue), the same MFMA kernel and tile as in the forward pass, timed alone.
+    d, hid = cfg["d"], cfg["mlp_hidden"]
+    M = rows * T
+    A = torch.randn(M, d, device=dev).to(dt)
+    W1 = model.tensors["fc1_w"][0]
+    b1 = model.tensors["fc1_b"][0]
+    G = torch.empty(M, hid, device=dev, dtype=dt)
+    for _ in range(3):
+        dm.linear(dm.DIT_EPI_GELU, A, W1, b1, G)
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    k0.record()
+    for _ in range(args.kernel_launches):
+        dm.linear(dm.DIT_EPI_GELU, A, W1, b1, G)
+    k1.record()
+    torch.cuda.synchronize()
+    kms = k0.elapsed_time(k1) / args.kernel_launches
+    kflop = 2.0 * M * hid * d
+    k_tflops = kflop / (kms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": None,
+                "kernel": f"gemm_mfma_kernel<EPI_GELU,128,128> (FFN fc1: M={M}, N={hid}, K={d})",
+                "avg_launch_ms": round(kms, 4)}
+
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.skip_cpu_baseline:
+        cpu = cpu_baseline(cfg, w, inp, min(args.cpu_rows, Bh), rows)
+
+    line = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms, 3),
+        "unit": "forwards/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg["dtype"] == dit_inputs.DTYPE_BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) latents, U{0..999} t and labels, N(0,0.02) weights)",
+        "config": {"workload": cfg["name"], "guided_rows": Bh, "trunk_rows": rows, "tokens": T,
+                   "guidance_scale": cfg["scale"], "guided_channels": cfg["guided"],
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 1),
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "tokens_per_s": round(rows * T * 1000.0 / ms, 1),
+        "images_per_s": round(Bh * 1000.0 / ms, 1),
+        "gflop_per_forward": round(flop_fwd / 1e9, 1),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

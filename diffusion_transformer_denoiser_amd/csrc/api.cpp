@@ -53,7 +53,7 @@ struct dit_handle {
 namespace {
 
 struct WsLayout {
-  size_t e, th, c, sc, mod, X, H, q, k, v, o, G, Y, total;
+  size_t e, th, c, sc, mod, X, H, qkv, o, G, Y, total;
 };
 
 WsLayout ws_layout(const dit_handle* h, int rows) {
@@ -65,7 +65,6 @@ WsLayout ws_layout(const dit_handle* h, int rows) {
     return o;
   };
   const size_t es = h->es, R = (size_t)rows, M = R * h->T;
-  const size_t ldv = h->dtype == DIT_BF16 ? (size_t)round_up(h->T, 64) : (size_t)h->T;
   L.e = take(R * h->freq * 4);
   L.th = take(R * h->d * 4);
   L.c = take(R * h->d * 4);
@@ -73,9 +72,7 @@ WsLayout ws_layout(const dit_handle* h, int rows) {
   L.mod = take(R * h->mod_stride * 4);
   L.X = take(M * h->d * 4);
   L.H = take(M * h->d * es);
-  L.q = take(R * h->heads * h->T * h->dh * es);
-  L.k = take(R * h->heads * h->T * h->dh * es);
-  L.v = take(R * h->heads * ldv * h->dh * es);
+  L.qkv = take(M * 3 * h->d * es);
   L.o = take(M * h->d * es);
   L.G = take(M * h->hid * es);
   L.Y = take(M * h->kout * 4);
@@ -121,23 +118,21 @@ int run_block(const dit_handle* h, int l, int rows, float* X, const float* mod, 
   void* Hb = at<void>(ws, L.H);
   void* O = at<void>(ws, L.o);
   void* G = at<void>(ws, L.G);
-  void* q = at<void>(ws, L.q);
-  void* k = at<void>(ws, L.k);
-  void* v = at<void>(ws, L.v);
+  void* qkv = at<void>(ws, L.qkv);
 
   DIT_HIP(launch_ln_modulate(X, M, T, d, mod, mod_stride, base, base + d, h->eps, Hb, h->dtype, s));
 
+  // Packed in-projection q | k | v [M, 3d] (heads as contiguous dh slices).
   EpiParams ep = epi0();
   ep.bias = h->w.qkv_b + (size_t)l * 3 * d;
-  ep.q = q; ep.k = k; ep.v = v;
-  ep.heads = h->heads; ep.dh = h->dh; ep.d = d; ep.T = T;
-  ep.ldv = h->dtype == DIT_BF16 ? round_up(T, 64) : 0;
-  DIT_HIP(linear(h, EPI_QKV, Hb, d, woff(h->w.qkv_w, (size_t)l * 3 * d * d, es), M, 3 * d, d, ep, s));
+  ep.out = qkv; ep.ldo = 3 * d;
+  DIT_HIP(linear(h, EPI_BIAS_DT, Hb, d, woff(h->w.qkv_w, (size_t)l * 3 * d * d, es), M, 3 * d, d,
+                 ep, s));
 
   if (h->cfg.qk_norm || h->cfg.rope3d)
-    DIT_HIP(launch_qk_norm_rope(q, k, rows, h->heads, T, h->dh, h->dtype, h->cfg.qk_norm, h->eps,
-                                h->cfg.rope3d, h->gf, h->gh, h->gw, s));
-  DIT_HIP(launch_attention(q, k, v, rows, h->heads, T, h->dh, h->dtype, O, s));
+    DIT_HIP(launch_qk_norm_rope(qkv, rows, h->heads, T, h->dh, h->dtype, h->cfg.qk_norm, h->eps,
+                                h->cfg.rope3d, h->gh, h->gw, s));
+  DIT_HIP(launch_attention(qkv, rows, h->heads, T, h->dh, h->dtype, O, s));
 
   const void* ow = woff(h->w.o_w, (size_t)l * d * d, es);
   if (o_branch) {
@@ -465,14 +460,15 @@ int dit_timestep_embed(const float* t, int B, int dim, float* e, void* stream) {
   return ok();
 }
 
-int dit_attention(const void* q, const void* k, const void* v, int B, int H, int T, int dh,
-                  int dtype, void* o, void* stream) {
-  if (!q || !k || !v || !o) return fail(DIT_EINVAL, "q, k, v and o must be non-NULL");
+int dit_attention(const void* qkv, int B, int H, int T, int dh, int dtype, void* o,
+                  void* stream) {
+  if (!qkv || !o) return fail(DIT_EINVAL, "qkv and o must be non-NULL");
   if (B <= 0 || H <= 0 || T <= 0) return fail(DIT_EINVAL, "B, H, T must be positive");
   if (dtype != DIT_F32 && dtype != DIT_BF16) return fail(DIT_EINVAL, "dtype");
   if (dh != 64 && dh != 72) return fail(DIT_EUNSUPPORTED, "head dim %d", dh);
   if ((int64_t)B * H > 65535) return fail(DIT_EUNSUPPORTED, "B * H > 65535");
-  DIT_HIP(launch_attention(q, k, v, B, H, T, dh, dtype, o, (hipStream_t)stream));
+  if ((uintptr_t)qkv & 15) return fail(DIT_EINVAL, "qkv must be 16-byte aligned");
+  DIT_HIP(launch_attention(qkv, B, H, T, dh, dtype, o, (hipStream_t)stream));
   return ok();
 }
 

@@ -13,8 +13,12 @@
 // blocks for one query, which is exactly a B operand of the P V^T product once
 // the key order inside each 32-key step is permuted the same way for V (the
 // contraction is a sum, so any consistent key order is correct).  P therefore
-// never leaves registers; V is stored transposed (keys fastest) so its operand
+// never leaves registers.  The V tile is transposed while it is staged into
+// LDS (4 keys x 4 features per thread, transposed in registers) so its operand
 // is two 8-byte LDS reads.
+//
+// Input: the packed in-projection output qkv [B, T, 3 H dh] (q | k | v, heads as
+// contiguous dh slices), read with its row stride; output o [B, T, H dh].
 //
 // fp32 path: one thread per query, keys streamed through LDS (small shapes).
 #include "common.h"
@@ -25,11 +29,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 namespace {
 
 template <int DH>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict__ Q,
-                                                        const bf16_t* __restrict__ K,
-                                                        const bf16_t* __restrict__ Vt,
+__global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict__ QKV,
                                                         bf16_t* __restrict__ O, int H, int T,
-                                                        int ldv, float sl2) {
+                                                        float sl2) {
   constexpr int KV = 64;                 // keys per tile
   constexpr int KLD = 72;                // K tile row stride (elements), 144 B
   constexpr int VLD = KV + 4;            // V^T tile row stride (elements), 136 B
@@ -44,9 +46,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh - b * H;
   const int q0 = blockIdx.x * 128 + wave * 32;
-  const bf16_t* Qb = Q + (int64_t)bh * T * DH;
-  const bf16_t* Kb = K + (int64_t)bh * T * DH;
-  const bf16_t* Vb = Vt + (int64_t)bh * DH * ldv;
+  const int64_t ld = 3LL * H * DH;                       // packed row stride
+  const bf16_t* Qb = QKV + (int64_t)b * T * ld + h * DH;   // + t * ld
+  const bf16_t* Kb = Qb + (int64_t)H * DH;
+  const bf16_t* Vb = Qb + 2LL * H * DH;
 
   const bf16x8_t z8 = {};
   bf16x8_t qf[2][2];
@@ -57,10 +60,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
     bool ok = q < T;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      qf[qb][c] = ok ? *(const bf16x8_t*)(Qb + (int64_t)q * DH + 32 * c + 8 * g) : z8;
+      qf[qb][c] = ok ? *(const bf16x8_t*)(Qb + q * ld + 32 * c + 8 * g) : z8;
     qt[qb] = z8;   // dh 64..71 in lanes g == 0, zeros elsewhere
     if constexpr (TAIL)
-      if (ok && g == 0) qt[qb] = *(const bf16x8_t*)(Qb + (int64_t)q * DH + 64);
+      if (ok && g == 0) qt[qb] = *(const bf16x8_t*)(Qb + q * ld + 64);
   }
 
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
@@ -72,35 +75,36 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
 
   for (int kv0 = 0; kv0 < T; kv0 += KV) {
     __syncthreads();
-    // K tile: KV rows of DH, contiguous in HBM.
+    // K tile: KV rows of DH (one 144- or 128-byte segment per key).
     constexpr int KCH = KV * DH / 8;
     for (int idx = tid; idx < KCH; idx += 256) {
       int row = idx / (DH / 8), col = (idx - row * (DH / 8)) * 8;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (kv0 + row < T) v = *(const uint4*)(Kb + (int64_t)(kv0 + row) * DH + col);
+      if (kv0 + row < T) v = *(const uint4*)(Kb + (kv0 + row) * ld + col);
       *(uint4*)&sK[row * KLD + col] = v;
     }
-    // V^T tile: DH rows of KV keys (row stride ldv in HBM).
-    constexpr int VCH = DH * KV / 8;
-    for (int idx = tid; idx < VCH; idx += 256) {
-      int row = idx / (KV / 8), col = (idx - row * (KV / 8)) * 8;
-      int kv = kv0 + col;
-      const bf16_t* src = Vb + (int64_t)row * ldv + kv;
-      uint4 v;
-      if (kv + 8 <= T) {
-        v = *(const uint4*)src;
-      } else {
-        uint16_t e[8];
+    // V tile, transposed into sV[dh][key]: each item is 4 keys x 4 features,
+    // read as four 8-byte row pieces (consecutive items -> consecutive features,
+    // so a key row is read contiguously) and written as four 8-byte key runs.
+    constexpr int VB = (KV / 4) * (DH / 4);
+    for (int idx = tid; idx < VB; idx += 256) {
+      const int kb4 = idx / (DH / 4), d4 = (idx - kb4 * (DH / 4)) * 4;
+      uint2 r[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) e[u] = (kv + u < T) ? src[u] : (uint16_t)0;
-        v.x = e[0] | ((uint32_t)e[1] << 16);
-        v.y = e[2] | ((uint32_t)e[3] << 16);
-        v.z = e[4] | ((uint32_t)e[5] << 16);
-        v.w = e[6] | ((uint32_t)e[7] << 16);
+      for (int u = 0; u < 4; ++u) {
+        int kv = kv0 + 4 * kb4 + u;
+        r[u] = kv < T ? *(const uint2*)(Vb + kv * ld + d4) : make_uint2(0, 0);
       }
-      uint2* dst = (uint2*)&sV[row * VLD + col];
-      dst[0] = make_uint2(v.x, v.y);
-      dst[1] = make_uint2(v.z, v.w);
+      // r[u] holds features d4..d4+3 of key u; column e = (r[0].e, r[1].e, r[2].e, r[3].e)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t sh = (e & 1) * 16;
+        uint32_t k0 = ((e < 2 ? r[0].x : r[0].y) >> sh) & 0xffffu;
+        uint32_t k1 = ((e < 2 ? r[1].x : r[1].y) >> sh) & 0xffffu;
+        uint32_t k2 = ((e < 2 ? r[2].x : r[2].y) >> sh) & 0xffffu;
+        uint32_t k3 = ((e < 2 ? r[3].x : r[3].y) >> sh) & 0xffffu;
+        *(uint2*)&sV[(d4 + e) * VLD + 4 * kb4] = make_uint2(k0 | (k1 << 16), k2 | (k3 << 16));
+      }
     }
     __syncthreads();
 
@@ -206,22 +210,21 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
 }
 
 template <int DH>
-__global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ Q,
-                                                      const float* __restrict__ K,
-                                                      const float* __restrict__ V,
+__global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ QKV,
                                                       float* __restrict__ O, int H, int T,
                                                       float scale) {
   constexpr int KT = 32;
   __shared__ float sK[KT][DH], sV[KT][DH];
   const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
   const int qi = blockIdx.x * 64 + threadIdx.x;
-  const float* Qb = Q + (int64_t)bh * T * DH;
-  const float* Kb = K + (int64_t)bh * T * DH;
-  const float* Vb = V + (int64_t)bh * T * DH;
+  const int64_t ld = 3LL * H * DH;
+  const float* Qb = QKV + (int64_t)b * T * ld + h * DH;
+  const float* Kb = Qb + (int64_t)H * DH;
+  const float* Vb = Qb + 2LL * H * DH;
   float qv[DH], acc[DH];
 #pragma unroll
   for (int e = 0; e < DH; ++e) {
-    qv[e] = qi < T ? Qb[(int64_t)qi * DH + e] : 0.0f;
+    qv[e] = qi < T ? Qb[qi * ld + e] : 0.0f;
     acc[e] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f;
@@ -230,8 +233,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
     for (int e = threadIdx.x; e < KT * DH; e += 64) {
       int r = e / DH, c = e - r * DH;
       bool ok = kv0 + r < T;
-      sK[r][c] = ok ? Kb[(int64_t)(kv0 + r) * DH + c] : 0.0f;
-      sV[r][c] = ok ? Vb[(int64_t)(kv0 + r) * DH + c] : 0.0f;
+      sK[r][c] = ok ? Kb[(kv0 + r) * ld + c] : 0.0f;
+      sV[r][c] = ok ? Vb[(kv0 + r) * ld + c] : 0.0f;
     }
     __syncthreads();
     const int nv = min(KT, T - kv0);
@@ -258,30 +261,25 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_attention(const void* q, const void* k, const void* v, int B, int heads,
-                            int T, int dh, int dtype, void* o, hipStream_t s) {
+hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, int dtype, void* o,
+                            hipStream_t s) {
   if (B <= 0 || T <= 0) return hipSuccess;
   if (dtype == 1) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)dh);
     dim3 grid((T + 127) / 128, B * heads);
-    int ldv = round_up(T, 64);
     if (dh == 64)
-      attn_bf16_kernel<64><<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)k,
-                                                (const bf16_t*)v, (bf16_t*)o, heads, T, ldv, sl2);
+      attn_bf16_kernel<64><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o, heads, T, sl2);
     else if (dh == 72)
-      attn_bf16_kernel<72><<<grid, 256, 0, s>>>((const bf16_t*)q, (const bf16_t*)k,
-                                                (const bf16_t*)v, (bf16_t*)o, heads, T, ldv, sl2);
+      attn_bf16_kernel<72><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o, heads, T, sl2);
     else
       return hipErrorInvalidValue;
   } else {
     const float scale = 1.0f / sqrtf((float)dh);
     dim3 grid((T + 63) / 64, B * heads);
     if (dh == 64)
-      attn_f32_kernel<64><<<grid, 64, 0, s>>>((const float*)q, (const float*)k, (const float*)v,
-                                              (float*)o, heads, T, scale);
+      attn_f32_kernel<64><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, T, scale);
     else if (dh == 72)
-      attn_f32_kernel<72><<<grid, 64, 0, s>>>((const float*)q, (const float*)k, (const float*)v,
-                                              (float*)o, heads, T, scale);
+      attn_f32_kernel<72><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, T, scale);
     else
       return hipErrorInvalidValue;
   }

@@ -21,12 +21,18 @@ template <typename T> __device__ __forceinline__ T from_f(float v);
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
-// tanh-approximate GELU: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))
+// exp2 and reciprocal on the hardware units (v_exp_f32, v_rcp_f32: ~1 ulp).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float silu_f(float z) {
+  return z * fast_rcp(1.0f + fast_exp2(-1.4426950408889634f * z));
+}
+// tanh-approximate GELU: 0.5 z (1 + tanh(u)), u = sqrt(2/pi) (z + 0.044715 z^3),
+// evaluated through the identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)).
 __device__ __forceinline__ float gelu_tanh_f(float z) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  float u = k0 * (z + 0.044715f * z * z * z);
-  return 0.5f * z * (1.0f + tanhf(u));
+  const float k2 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  float u2 = k2 * (z + 0.044715f * z * z * z);                          // -2u log2(e)
+  return z * fast_rcp(1.0f + fast_exp2(u2));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -60,7 +66,7 @@ enum EpiKind {
   EPI_BIAS_F32 = 0,     // out_f32[m, n] = C + bias[n]
   EPI_BIAS_SILU = 1,    // out_f32[m, n] = SiLU(C + bias[n])                   (timestep MLP)
   EPI_COND = 2,         // c = C + bias (+ c_prev) (+ table[label]); writes c and SiLU(c) (dtype)
-  EPI_QKV = 3,          // C + bias scattered to q, k [B,H,T,dh] and v (bf16: [B,H,dh,ldv])
+  EPI_BIAS_DT = 3,      // out_dtype[m, n] = C + bias[n]            (packed q | k | v)
   EPI_GATED = 4,        // X[m, n] += gate[b, n] * (C + bias[n])                (fp32 residual)
   EPI_GELU = 5,         // out_dtype[m, n] = GELU_tanh(C + bias[n])
   EPI_PATCH = 6,        // X[m, n] = C + bias[n] (+ 2-D sin-cos PE(tau, n))
@@ -75,9 +81,6 @@ struct EpiParams {
   int mod_stride;
   int gate_off;
   int T;                // tokens per row (rows of A per batch row)
-  // qkv scatter
-  void* q; void* k; void* v;
-  int heads, dh, d, ldv;
   // conditioning
   const float* table;   // class table [ncls + 1, d] or null
   const int32_t* labels;
@@ -117,10 +120,9 @@ hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, 
 hipError_t launch_ln_modulate(const float* X, int M, int T, int d, const float* mod,
                               int mod_stride, int shift_off, int scale_off, float eps,
                               void* H, int dtype, hipStream_t s);
-hipError_t launch_qk_norm_rope(void* q, void* k, int B, int heads, int T, int dh, int dtype,
-                               int qk_norm, float eps, int rope, int gf, int gh, int gw,
-                               hipStream_t s);
-hipError_t launch_attention(const void* q, const void* k, const void* v, int B, int heads,
-                            int T, int dh, int dtype, void* o, hipStream_t s);
+hipError_t launch_qk_norm_rope(void* qkv, int B, int heads, int T, int dh, int dtype,
+                               int qk_norm, float eps, int rope, int gh, int gw, hipStream_t s);
+hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, int dtype, void* o,
+                            hipStream_t s);
 
 static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }

@@ -1,5 +1,5 @@
 // GEMM epilogues fused into the producing kernels (bias, SiLU, conditioning
-// sum, QKV head split, alpha-gated residual, tanh-GELU, patch position term).
+// sum, alpha-gated residual, tanh-GELU, patch position term).
 #pragma once
 #include "common.h"
 
@@ -34,16 +34,8 @@ __device__ __forceinline__ void epi_apply(const EpiParams& ep, int m, int n, flo
     }
     c[o] = v;
     ((DT*)ep.silu_out)[o] = from_f<DT>(silu_f(v));
-  } else if constexpr (EPI == EPI_QKV) {
-    int b = m / ep.T, t = m - b * ep.T;
-    int which = n / ep.d, r = n - which * ep.d;
-    int h = r / ep.dh, e = r - h * ep.dh;
-    int64_t bh = (int64_t)b * ep.heads + h;
-    DT val = from_f<DT>(v);
-    if (which == 0) ((DT*)ep.q)[(bh * ep.T + t) * ep.dh + e] = val;
-    else if (which == 1) ((DT*)ep.k)[(bh * ep.T + t) * ep.dh + e] = val;
-    else if (ep.ldv) ((DT*)ep.v)[(bh * ep.dh + e) * ep.ldv + t] = val;   // keys fastest
-    else ((DT*)ep.v)[(bh * ep.T + t) * ep.dh + e] = val;
+  } else if constexpr (EPI == EPI_BIAS_DT) {
+    ((DT*)ep.out)[(int64_t)m * ep.ldo + n] = from_f<DT>(v);
   } else if constexpr (EPI == EPI_GATED) {
     int b = m / ep.T;
     float g = ep.mod[(int64_t)b * ep.mod_stride + ep.gate_off + n];

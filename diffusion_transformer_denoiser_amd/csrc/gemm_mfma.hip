@@ -1,66 +1,113 @@
 // bf16 GEMM C = A W^T on the CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16),
 // fp32 accumulation, fused epilogues.
 //
-// A [M, K] and W [N, K] are both K-contiguous (row-major activations,
-// [out, in] weights).  A BM x BN block tile is split over 4 waves (2 x 2); each
-// wave owns (BM/2) x (BN/2) outputs as 32x32 MFMA blocks.  K is staged through
-// LDS in 64-wide slices, double-buffered: the next slice is fetched from HBM
-// into registers while the current one feeds the MFMAs.  LDS rows are 128 B
-// (64 bf16); the 16-byte chunk c of row r is stored at chunk c ^ (r & 7), so
-// the 32 rows read by one MFMA operand fetch spread over all banks.
+// A [M, K] (row stride lda) and W [N, K] are both K-contiguous (row-major
+// activations, [out, in] weights).  A BM x BN block tile is split over 4 waves
+// (2 x 2); each wave owns (BM/2) x (BN/2) outputs as 32x32 MFMA blocks.
+//
+// K is consumed in 64-wide slices through a ring of STAGES LDS buffers filled
+// by direct global->LDS loads (global_load_lds_dwordx4: each lane moves 16 bytes
+// straight into LDS at base + 16*lane), so the next STAGES-1 slices are in
+// flight while the current one feeds the MFMAs and no registers stage the
+// copy.  LDS rows are 128 B (64 bf16); the 16-byte chunk c of row r sits at
+// chunk c ^ ((r >> 1) & 7), which spreads the rows of one MFMA operand fetch
+// over all 64 banks; each lane therefore fetches the global chunk that belongs
+// in its LDS slot.  Rows past M or N read a clamped (valid) row and are never stored.
+// Within a slice the operand fragments of the next 16-wide k step are read
+// from LDS while the current step's MFMAs run.
 #include "common.h"
 #include "epilogue.h"
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
+typedef __attribute__((address_space(3))) void lds_void;
 
 namespace {
 
 constexpr int BK = 64;
 
-template <int EPI, int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(const bf16_t* __restrict__ A, int lda,
-                                                         const bf16_t* __restrict__ W, int M,
-                                                         int N, int K, EpiParams ep) {
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Tile order.  Workgroups are dispatched round-robin over the 8 XCDs (each with
+// its own L2): with SWZ, workgroup b runs logical tile (b % 8) * (n / 8) + b / 8,
+// so each XCD walks a contiguous range of logical tiles, and logical tiles are
+// ordered in groups of G row-tiles (column-major inside a group) so the tiles
+// resident on one XCD at a time share A and W tiles.  Needs n % 8 == 0.
+template <int SWZ>
+__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  if constexpr (SWZ) {
+    const int n = tiles_m * tiles_n;
+    const int logical = (b & 7) * (n >> 3) + (b >> 3);
+    constexpr int G = 8;
+    const int per_group = G * tiles_n;
+    const int grp = logical / per_group, in = logical - grp * per_group;
+    const int rows = min(G, tiles_m - grp * G);
+    tm = grp * G + in % rows;
+    tn = in / rows;
+  } else {
+    tm = b / tiles_n;
+    tn = b - tm * tiles_n;
+  }
+}
+
+// LDS row swizzle: the 16-byte chunk c of row r is stored at c ^ key(r).
+// RSW = 0: key = r & 7; RSW = 1: key = (r >> 1) & 7, which makes any 16
+// consecutive rows (the lanes served together by 64 four-byte banks) touch every
+// bank once.
+template <int RSW>
+__device__ __forceinline__ int row_key(int r) { return RSW ? (r >> 1) & 7 : r & 7; }
+
+template <int EPI, int BM, int BN, int STAGES, int MINWG, int SWZ, int RSW = 1>
+__global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __restrict__ A, int lda,
+                                                                const bf16_t* __restrict__ W, int M,
+                                                                int N, int K, EpiParams ep) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int CA = BM * BK / 8 / 256;  // 16-byte chunks per thread per slice
-  constexpr int CB = BN * BK / 8 / 256;
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * BK];
+  constexpr int NA = BM / 32, NB = BN / 32;      // 1 KB LDS loads per wave per slice
+  constexpr int L = NA + NB;
+  constexpr int A_BYTES = BM * BK * 2, STAGE_BYTES = (BM + BN) * BK * 2;
+  static_assert(STAGES == 2 || STAGES == 3, "stages");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_n = (N + BN - 1) / BN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+  int tm, tn;
+  tile_coords<SWZ>(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  uint4 ra[CA], rb[CB];
-  auto gload = [&](int k0) {
+  // Per-lane source of each direct LDS load: slot s of the tile holds row s/8,
+  // stored chunk s%8 = logical chunk (s%8) ^ (row & 7).
+  const bf16_t* pa[NA];
+  const bf16_t* pb[NB];
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      int idx = tid + i * 256, row = idx >> 3, ch = idx & 7;
-      int m = m0 + row;
-      ra[i] = (m < M) ? *(const uint4*)(A + (int64_t)m * lda + k0 + ch * 8) : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < NA; ++i) {
+    int s = (w * NA + i) * 64 + lane, r = s >> 3, c = (s & 7) ^ row_key<RSW>(r);
+    int m = min(m0 + r, M - 1);
+    pa[i] = A + (int64_t)m * lda + c * 8;
+  }
 #pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      int idx = tid + i * 256, row = idx >> 3, ch = idx & 7;
-      int n = n0 + row;
-      rb[i] = (n < N) ? *(const uint4*)(W + (int64_t)n * K + k0 + ch * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int buf) {
+  for (int i = 0; i < NB; ++i) {
+    int s = (w * NB + i) * 64 + lane, r = s >> 3, c = (s & 7) ^ row_key<RSW>(r);
+    int n = min(n0 + r, N - 1);
+    pb[i] = W + (int64_t)n * K + c * 8;
+  }
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % STAGES) * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      int idx = tid + i * 256, row = idx >> 3, ch = idx & 7;
-      *(uint4*)&sA[buf][row * BK + ((ch ^ (row & 7)) << 3)] = ra[i];
-    }
+    for (int i = 0; i < NA; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(pa[i] + kt * BK),
+                                       (lds_void*)(st + (w * NA + i) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      int idx = tid + i * 256, row = idx >> 3, ch = idx & 7;
-      *(uint4*)&sB[buf][row * BK + ((ch ^ (row & 7)) << 3)] = rb[i];
-    }
+    for (int i = 0; i < NB; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(pb[i] + kt * BK),
+                                       (lds_void*)(st + A_BYTES + (w * NB + i) * 1024), 16, 0, 0);
   };
 
   floatx16 acc[TM][TN];
@@ -71,36 +118,55 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const bf16_t* __restrict
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // LDS byte offsets of this lane's operand rows (fixed over the loop).
+  int offa[TM], offb[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) offa[i] = (wm * WM + i * 32 + (lane & 31)) * 128;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) offb[j] = A_BYTES + (wn * WN + j * 32 + (lane & 31)) * 128;
+  // every fragment row is a multiple of 32 plus (lane & 31): its key depends on lane only
+  const int rsw = row_key<RSW>(lane & 31);
+  const int half = lane >> 5;
+
   const int nk = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s);
+
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    // Slice kt has landed in LDS once this wave's copies of it are done (the
+    // copies of the next slice may stay in flight) and every wave has passed
+    // the barrier.  A bare s_barrier is used: __syncthreads() would add a
+    // release fence that drains all outstanding copies.  The stage refilled
+    // below was last read in iteration kt-1; those LDS reads completed before
+    // their MFMAs, which each wave issued before reaching this barrier.
+    if (STAGES == 3 && kt + 1 < nk) wait_vmcnt<(STAGES - 2) * L>();
+    else wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    const char* st = smem + (kt % STAGES) * STAGE_BYTES;
+
+    bf16x8_t fa[2][TM], fb[2][TN];
+    auto fetch = [&](int buf, int kk) {
+      const int ch = ((kk * 2 + half) ^ rsw) << 4;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[buf][i] = *(const bf16x8_t*)(st + offa[i] + ch);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[buf][j] = *(const bf16x8_t*)(st + offb[j] + ch);
+    };
+    fetch(0, 0);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      // lane supplies row (lane % 32), k = kk*16 + 8*(lane/32) .. +8
-      const int ch = kk * 2 + (lane >> 5);
-      bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        int row = wm * WM + i * 32 + (lane & 31);
-        af[i] = *(const bf16x8_t*)&sA[buf][row * BK + ((ch ^ (row & 7)) << 3)];
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        int row = wn * WN + j * 32 + (lane & 31);
-        bfr[j] = *(const bf16x8_t*)&sB[buf][row * BK + ((ch ^ (row & 7)) << 3)];
-      }
+      if (kk + 1 < BK / 16) fetch((kk + 1) & 1, kk + 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
+                                                              acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
   }
 
   // 32x32 accumulator layout: lane holds column (lane % 32); register r holds
@@ -111,18 +177,28 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(const bf16_t* __restrict
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
         int col = n0 + wn * WN + j * 32 + (lane & 31);
         if (row < M && col < N) epi_apply<EPI, bf16_t>(ep, row, col, acc[i][j][r]);
       }
 }
 
-template <int EPI, int BM, int BN>
+template <int EPI, int BM, int BN, int STAGES, int MINWG>
 hipError_t run(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
                const EpiParams& ep, hipStream_t s) {
   int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  gemm_mfma_kernel<EPI, BM, BN><<<tiles, 256, 0, s>>>(A, lda, W, M, N, K, ep);
+  if (tiles % 8 == 0)
+    gemm_bf16_kernel<EPI, BM, BN, STAGES, MINWG, 1><<<tiles, 256, 0, s>>>(A, lda, W, M, N, K, ep);
+  else
+    gemm_bf16_kernel<EPI, BM, BN, STAGES, MINWG, 0><<<tiles, 256, 0, s>>>(A, lda, W, M, N, K, ep);
   return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t pick(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
+                const EpiParams& ep, hipStream_t s) {
+  if (N % 192 == 0) return run<EPI, 128, 192, 2, 2>(A, lda, W, M, N, K, ep, s);
+  return run<EPI, 128, 128, 2, 2>(A, lda, W, M, N, K, ep, s);
 }
 
 }  // namespace
@@ -130,12 +206,12 @@ hipError_t run(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
 hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, int M, int N,
                             int K, const EpiParams& ep, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (K % BK) return hipErrorInvalidValue;
+  if (K % BK || lda % 8) return hipErrorInvalidValue;
   switch (epi) {
-    case EPI_BIAS_F32: return run<EPI_BIAS_F32, 128, 128>(A, lda, W, M, N, K, ep, s);
-    case EPI_QKV: return run<EPI_QKV, 128, 128>(A, lda, W, M, N, K, ep, s);
-    case EPI_GATED: return run<EPI_GATED, 128, 128>(A, lda, W, M, N, K, ep, s);
-    case EPI_GELU: return run<EPI_GELU, 128, 128>(A, lda, W, M, N, K, ep, s);
+    case EPI_BIAS_F32: return pick<EPI_BIAS_F32>(A, lda, W, M, N, K, ep, s);
+    case EPI_BIAS_DT: return pick<EPI_BIAS_DT>(A, lda, W, M, N, K, ep, s);
+    case EPI_GATED: return pick<EPI_GATED>(A, lda, W, M, N, K, ep, s);
+    case EPI_GELU: return pick<EPI_GELU>(A, lda, W, M, N, K, ep, s);
   }
   return hipErrorInvalidValue;
 }

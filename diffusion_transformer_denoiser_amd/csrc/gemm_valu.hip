@@ -104,7 +104,7 @@ hipError_t dispatch_epi(int epi, int asrc, const ALoad& a, const void* W, int M,
     case EPI_BIAS_F32: return dispatch_src<EPI_BIAS_F32, DT>(asrc, a, W, M, N, K, ep, s);
     case EPI_BIAS_SILU: return dispatch_src<EPI_BIAS_SILU, DT>(asrc, a, W, M, N, K, ep, s);
     case EPI_COND: return dispatch_src<EPI_COND, DT>(asrc, a, W, M, N, K, ep, s);
-    case EPI_QKV: return dispatch_src<EPI_QKV, DT>(asrc, a, W, M, N, K, ep, s);
+    case EPI_BIAS_DT: return dispatch_src<EPI_BIAS_DT, DT>(asrc, a, W, M, N, K, ep, s);
     case EPI_GATED: return dispatch_src<EPI_GATED, DT>(asrc, a, W, M, N, K, ep, s);
     case EPI_GELU: return dispatch_src<EPI_GELU, DT>(asrc, a, W, M, N, K, ep, s);
     case EPI_PATCH: return dispatch_src<EPI_PATCH, DT>(asrc, a, W, M, N, K, ep, s);

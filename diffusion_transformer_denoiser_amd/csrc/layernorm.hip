@@ -84,18 +84,22 @@ hipError_t launch_ln_modulate(const float* X, int M, int T, int d, const float* 
                             s);
 }
 
-// Per-head q/k post-processing for spacetime attention, in place on
-// [B, H, T, DH] rows: LayerNorm over the DH features (no affine), then the 3-D
-// rotary embedding: DH splits into (frame, row, col) thirds of da = DH/3; pair
-// (x_2k, x_2k+1) of a third rotates by pos * 10000^(-2k/da).
+// Per-head q/k post-processing for spacetime attention, in place on the packed
+// in-projection output qkv [B*T, 3 H DH]: LayerNorm over each head's DH
+// features (no affine), then the 3-D rotary embedding: DH splits into
+// (frame, row, col) thirds of da = DH/3; pair (x_2k, x_2k+1) of a third rotates
+// by pos * 10000^(-2k/da).  One thread per (q or k, token, head).
 template <int DH, typename DT>
-__global__ __launch_bounds__(256) void qk_norm_rope_kernel(DT* __restrict__ q, DT* __restrict__ k,
-                                                           int64_t rows, int T, int qk_norm,
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(DT* __restrict__ qkv, int64_t rows,
+                                                           int heads, int T, int qk_norm,
                                                            float eps, int rope, int gh, int gw) {
   int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= 2 * rows) return;
-  int64_t r = idx < rows ? idx : idx - rows;
-  DT* p = (idx < rows ? q : k) + r * DH;
+  const int which = idx >= rows;                 // 0: q, 1: k
+  const int64_t r = idx - which * rows;           // (token, head)
+  const int64_t bt = r / heads;
+  const int h = (int)(r - bt * heads);
+  DT* p = qkv + bt * 3 * heads * DH + (int64_t)which * heads * DH + h * DH;
   float x[DH];
 #pragma unroll
   for (int e = 0; e < DH; ++e) x[e] = to_f<DT>(p[e]);
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(DT* __restrict__ q, D
   if constexpr (DH % 6 == 0) {
     if (rope) {
       constexpr int DA = DH / 3;
-      int t = (int)(r % T);
+      int t = (int)(bt % T);
       int pos[3] = {t / (gh * gw), (t / gw) % gh, t % gw};
 #pragma unroll
       for (int a = 0; a < 3; ++a) {
@@ -133,28 +137,26 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(DT* __restrict__ q, D
   for (int e = 0; e < DH; ++e) p[e] = from_f<DT>(x[e]);
 }
 
-hipError_t launch_qk_norm_rope(void* q, void* k, int B, int heads, int T, int dh, int dtype,
-                               int qk_norm, float eps, int rope, int gf, int gh, int gw,
-                               hipStream_t s) {
-  (void)gf;
-  int64_t rows = (int64_t)B * heads * T;
-  int blocks = (int)((2 * rows + 255) / 256);
+hipError_t launch_qk_norm_rope(void* qkv, int B, int heads, int T, int dh, int dtype,
+                               int qk_norm, float eps, int rope, int gh, int gw, hipStream_t s) {
+  int64_t rows = (int64_t)B * T * heads;
   if (rows <= 0) return hipSuccess;
+  int blocks = (int)((2 * rows + 255) / 256);
   if (dh == 72) {
     if (dtype == 1)
-      qk_norm_rope_kernel<72, bf16_t><<<blocks, 256, 0, s>>>((bf16_t*)q, (bf16_t*)k, rows, T,
+      qk_norm_rope_kernel<72, bf16_t><<<blocks, 256, 0, s>>>((bf16_t*)qkv, rows, heads, T,
                                                              qk_norm, eps, rope, gh, gw);
     else
-      qk_norm_rope_kernel<72, float><<<blocks, 256, 0, s>>>((float*)q, (float*)k, rows, T,
-                                                            qk_norm, eps, rope, gh, gw);
+      qk_norm_rope_kernel<72, float><<<blocks, 256, 0, s>>>((float*)qkv, rows, heads, T, qk_norm,
+                                                            eps, rope, gh, gw);
   } else if (dh == 64) {
     if (rope) return hipErrorInvalidValue;
     if (dtype == 1)
-      qk_norm_rope_kernel<64, bf16_t><<<blocks, 256, 0, s>>>((bf16_t*)q, (bf16_t*)k, rows, T,
+      qk_norm_rope_kernel<64, bf16_t><<<blocks, 256, 0, s>>>((bf16_t*)qkv, rows, heads, T,
                                                              qk_norm, eps, 0, gh, gw);
     else
-      qk_norm_rope_kernel<64, float><<<blocks, 256, 0, s>>>((float*)q, (float*)k, rows, T,
-                                                            qk_norm, eps, 0, gh, gw);
+      qk_norm_rope_kernel<64, float><<<blocks, 256, 0, s>>>((float*)qkv, rows, heads, T, qk_norm,
+                                                            eps, 0, gh, gw);
   } else {
     return hipErrorInvalidValue;
   }

@@ -207,15 +207,16 @@ def timestep_embed(t: torch.Tensor, dim: int = 256) -> torch.Tensor:
     return e
 
 
-def attention(q, k, v_lib, T: int) -> torch.Tensor:
-    """q, k [B, H, T, dh]; v_lib in the library's V layout (bf16: [B, H, dh, ldv],
-    ldv = T rounded up to 64; fp32: [B, H, T, dh]).  Returns [B, T, H*dh]."""
+def attention(qkv: torch.Tensor, heads: int) -> torch.Tensor:
+    """qkv [B, T, 3*heads*dh] packed q | k | v (heads as contiguous slices).
+    Returns [B, T, heads*dh]."""
     lib = _lib.load()
-    B, H, _, dh = q.shape
-    code = _lib.DIT_BF16 if q.dtype == torch.bfloat16 else _lib.DIT_F32
-    o = torch.empty(B, T, H * dh, dtype=q.dtype, device=q.device)
-    _lib.check(lib.dit_attention(_ptr(q), _ptr(k), _ptr(v_lib), B, H, T, dh, code, _ptr(o),
-                                 _stream(q.device)))
+    B, T, three_d = qkv.shape
+    dh = three_d // (3 * heads)
+    code = _lib.DIT_BF16 if qkv.dtype == torch.bfloat16 else _lib.DIT_F32
+    o = torch.empty(B, T, heads * dh, dtype=qkv.dtype, device=qkv.device)
+    _lib.check(lib.dit_attention(_ptr(qkv.contiguous()), B, heads, T, dh, code, _ptr(o),
+                                 _stream(qkv.device)))
     return o
 
 

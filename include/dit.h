@@ -197,12 +197,12 @@ int dit_unpatchify(const float* Y, int B, int Cout, int F, int H, int W, int p, 
  * t: [B] fp32; e: [B, dim] fp32. */
 int dit_timestep_embed(const float* t, int B, int dim, float* e, void* stream);
 
-/* Multi-head attention core softmax(q k^T / sqrt(dh)) v for every (b, h).
- * q, k: [B, H, T, dh].  v: bf16 -> [B, H, dh, ldv] (keys fastest, ldv =
- * T rounded up to a multiple of 64); fp32 -> [B, H, T, dh].
- * o: [B, T, H*dh] (token-major, heads concatenated), same dtype.  dh in {64, 72}. */
-int dit_attention(const void* q, const void* k, const void* v, int B, int H, int T, int dh,
-                  int dtype, void* o, void* stream);
+/* Multi-head attention core softmax(q k^T / sqrt(dh)) v for every (b, h)
+ * (itwiki "확산 트랜스포머", Implementation: nn.MultiheadAttention(d, heads)).
+ * qkv: [B, T, 3*H*dh] packed in-projection output, q | k | v, each with heads as
+ * contiguous dh slices (16-byte aligned); o: [B, T, H*dh] (token-major, heads
+ * concatenated), same dtype.  dh in {64, 72}; B*H <= 65535. */
+int dit_attention(const void* qkv, int B, int H, int T, int dh, int dtype, void* o, void* stream);
 
 /* Linear layer with one of the fused epilogues of the forward pass,
  * out = epilogue(A W^T + bias): A [M, K] and W [N, K] in `dtype`.

@@ -129,7 +129,8 @@ def test_standalone_steps_validate_before_launch():
     assert lib.dit_patchify(None, 1, 4, 1, 32, 32, 2, 1, 1, p, None) == _lib.DIT_EINVAL
     assert lib.dit_unpatchify(p, 1, 8, 3, 32, 32, 2, 2, p, None) == _lib.DIT_EINVAL
     assert lib.dit_timestep_embed(p, 4, 255, p, None) == _lib.DIT_EINVAL
-    assert lib.dit_attention(p, p, p, 1, 2, 16, 96, 1, p, None) == _lib.DIT_EUNSUPPORTED
+    assert lib.dit_attention(p, 1, 2, 16, 96, 1, p, None) == _lib.DIT_EUNSUPPORTED
+    assert lib.dit_attention(None, 1, 2, 16, 64, 1, p, None) == _lib.DIT_EINVAL
     assert lib.dit_linear(9, p, p, None, 4, 4, 64, 1, p, None, 0, 1, None) == _lib.DIT_EINVAL
     assert lib.dit_linear(0, p, p, None, 4, 4, 48, 1, p, None, 0, 1, None) == _lib.DIT_EUNSUPPORTED
     assert lib.dit_linear(2, p, p, None, 4, 4, 64, 1, p, None, 0, 1, None) == _lib.DIT_EINVAL

@@ -265,11 +265,9 @@ def test_video_full_length_attention_sampled_queries():
     rng = np.random.default_rng(11)
     q, k, v = (dit_inputs.bf16_round(rng.standard_normal((B, H, T, dh)).astype(np.float32))
                for _ in range(3))
-    qd, kd, vd = (torch.from_numpy(a).to(torch.bfloat16).cuda() for a in (q, k, v))
-    ldv = (T + 63) // 64 * 64
-    vt = torch.zeros(B, H, dh, ldv, dtype=torch.bfloat16, device="cuda")
-    vt[..., :T] = vd.transpose(2, 3)
-    o = dmod.attention(qd, kd, vt.contiguous(), T)
+    packed = np.concatenate([a.transpose(0, 2, 1, 3).reshape(B, T, H * dh) for a in (q, k, v)],
+                            axis=2)
+    o = dmod.attention(torch.from_numpy(packed).to(torch.bfloat16).cuda(), H)
     torch.cuda.synchronize()
     qs = np.array([0, 1, 127, 128, 12345, 24895, 24959])
     errs = []

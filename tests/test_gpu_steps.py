@@ -125,14 +125,11 @@ def test_linear_epilogues(M, N, K, dtype):
 
 # --- attention ---------------------------------------------------------------------------
 
-def _v_layout(v, dtype):
-    if dtype == torch.bfloat16:
-        B, H, T, dh = v.shape
-        ldv = (T + 63) // 64 * 64
-        vt = torch.zeros(B, H, dh, ldv, dtype=v.dtype, device=v.device)
-        vt[..., :T] = v.transpose(2, 3)
-        return vt.contiguous()
-    return v.contiguous()
+def _pack(q, k, v):
+    """[B, H, T, dh] x 3 -> packed in-projection layout [B, T, 3*H*dh] (q | k | v)."""
+    B, H, T, dh = q.shape
+    return np.concatenate([a.transpose(0, 2, 1, 3).reshape(B, T, H * dh) for a in (q, k, v)],
+                          axis=2)
 
 
 @pytest.mark.parametrize("T", [1, 2, 16, 17, 64, 65, 129, 256, 300])
@@ -147,8 +144,8 @@ def test_attention_matches_oracle(T, dh, dtype):
     q, k, v = (rng.standard_normal((B, H, T, dh)).astype(np.float32) * s for s in (1.0, 1.0, 1.0))
     if dtype == torch.bfloat16:
         q, k, v = _bf16(q), _bf16(k), _bf16(v)
-    qd, kd, vd = (torch.from_numpy(a).to(dtype).cuda() for a in (q, k, v))
-    o = np_(dmod.attention(qd, kd, _v_layout(vd, dtype), T))
+    qkv = torch.from_numpy(_pack(q, k, v)).to(dtype).cuda()
+    o = np_(dmod.attention(qkv, H))
     ref = oracle.attention(q, k, v).transpose(0, 2, 1, 3).reshape(B, T, H * dh)
     err = rel_l2(o, ref)
     log(f"  rel-L2 {err:.2e}")
@@ -162,7 +159,7 @@ def test_attention_special_cases_bf16():
     q = _bf16(rng.standard_normal((B, H, T, dh)))
     k = np.repeat(_bf16(rng.standard_normal((B, H, 1, dh))), T, axis=2)
     v = _bf16(rng.standard_normal((B, H, T, dh)))
-    qd, kd, vd = (torch.from_numpy(a).to(torch.bfloat16).cuda() for a in (q, k, v))
-    o = np_(dmod.attention(qd, kd, _v_layout(vd, torch.bfloat16), T)).reshape(B, T, H, dh)
+    qkv = torch.from_numpy(_pack(q, k, v)).to(torch.bfloat16).cuda()
+    o = np_(dmod.attention(qkv, H)).reshape(B, T, H, dh)
     mean = v.astype(np.float64).mean(axis=2)          # [B, H, dh]
     assert np.abs(o - mean[:, None]).max() < 2e-2
