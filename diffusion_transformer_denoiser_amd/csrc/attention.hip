@@ -29,17 +29,22 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 namespace {
 
 template <int DH>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict__ QKV,
-                                                        bf16_t* __restrict__ O, int H, int T,
-                                                        float sl2) {
-  constexpr int KV = 64;                 // keys per tile
-  constexpr int KLD = 72;                // K tile row stride (elements), 144 B
-  constexpr int VLD = KV + 4;            // V^T tile row stride (elements), 136 B
-  constexpr int NDB = (DH + 15) / 16;    // 16-row blocks of the O^T accumulator
-  constexpr bool TAIL = (DH % 32) != 0;  // dh = 72: columns 64..71
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restrict__ QKV,
+                                                           bf16_t* __restrict__ O, int H, int T,
+                                                           float sl2) {
+  constexpr int KV = 64;                  // keys per tile
+  constexpr int KLD = 72;                 // K tile row stride (elements), 144 B
+  constexpr int VLD = KV + 4;             // V^T tile row stride (elements), 136 B
+  constexpr int NDB = (DH + 15) / 16;     // 16-row blocks of the O^T accumulator
+  constexpr bool TAIL = (DH % 32) != 0;   // dh = 72: columns 64..71
+  constexpr int KCH = KV * DH / 8;        // 16-byte chunks of a K tile
+  constexpr int KPT = (KCH + 255) / 256;  // ... per thread
+  constexpr int VB = (KV / 4) * (DH / 4); // 4x4 (key x feature) items of a V tile
+  constexpr int VPT = (VB + 255) / 256;   // ... per thread
+  constexpr float RESCALE_SLACK = 8.0f;   // log2 headroom before the running max is raised
   static_assert(DH == 64 || DH == 72, "head dim");
-  __shared__ __attribute__((aligned(16))) bf16_t sK[KV * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[DH * VLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KV * KLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[2][DH * VLD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -66,6 +71,65 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
       if (ok && g == 0) qt[qb] = *(const bf16x8_t*)(Qb + q * ld + 64);
   }
 
+  // Tile staging: global -> registers (issued one tile ahead) -> LDS.
+  uint4 kreg[KPT];
+  uint2 vreg[VPT][4];
+  auto gload = [&](int kv0) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int idx = tid + u * 256;
+      kreg[u] = make_uint4(0, 0, 0, 0);
+      if (idx < KCH) {
+        const int row = idx / (DH / 8), col = (idx - row * (DH / 8)) * 8;
+        if (kv0 + row < T) kreg[u] = *(const uint4*)(Kb + (kv0 + row) * ld + col);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int idx = tid + u * 256;
+      const int kb4 = idx / (DH / 4), d4 = (idx - kb4 * (DH / 4)) * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int kv = kv0 + 4 * kb4 + q;
+        vreg[u][q] = (idx < VB && kv < T) ? *(const uint2*)(Vb + kv * ld + d4) : make_uint2(0, 0);
+      }
+    }
+  };
+  // K rows as they are; V transposed into sV[dh][key]: vreg[u][q] holds features
+  // d4..d4+3 of key 4*kb4+q, column e is (vreg[u][0].e, .., vreg[u][3].e).
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int idx = tid + u * 256;
+      if (idx < KCH) {
+        const int row = idx / (DH / 8), col = (idx - row * (DH / 8)) * 8;
+        *(uint4*)&sK[buf][row * KLD + col] = kreg[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int idx = tid + u * 256;
+      if (idx < VB) {
+        const int kb4 = idx / (DH / 4), d4 = (idx - kb4 * (DH / 4)) * 4;
+        const uint2* r = vreg[u];
+        // pairs of features packed per key: x = (f0, f1), y = (f2, f3)
+        uint32_t lo01 = __builtin_amdgcn_perm(r[1].x, r[0].x, 0x05040100u);  // f0 of keys 0,1
+        uint32_t hi01 = __builtin_amdgcn_perm(r[3].x, r[2].x, 0x05040100u);  // f0 of keys 2,3
+        uint32_t lo11 = __builtin_amdgcn_perm(r[1].x, r[0].x, 0x07060302u);  // f1 of keys 0,1
+        uint32_t hi11 = __builtin_amdgcn_perm(r[3].x, r[2].x, 0x07060302u);  // f1 of keys 2,3
+        uint32_t lo02 = __builtin_amdgcn_perm(r[1].y, r[0].y, 0x05040100u);  // f2
+        uint32_t hi02 = __builtin_amdgcn_perm(r[3].y, r[2].y, 0x05040100u);
+        uint32_t lo13 = __builtin_amdgcn_perm(r[1].y, r[0].y, 0x07060302u);  // f3
+        uint32_t hi13 = __builtin_amdgcn_perm(r[3].y, r[2].y, 0x07060302u);
+        bf16_t* base = &sV[buf][d4 * VLD + 4 * kb4];
+        *(uint2*)(base + 0 * VLD) = make_uint2(lo01, hi01);
+        *(uint2*)(base + 1 * VLD) = make_uint2(lo11, hi11);
+        *(uint2*)(base + 2 * VLD) = make_uint2(lo02, hi02);
+        *(uint2*)(base + 3 * VLD) = make_uint2(lo13, hi13);
+      }
+    }
+  };
+
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
   floatx4 oacc[NDB][2];
 #pragma unroll
@@ -73,46 +137,19 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int kv0 = 0; kv0 < T; kv0 += KV) {
-    __syncthreads();
-    // K tile: KV rows of DH (one 144- or 128-byte segment per key).
-    constexpr int KCH = KV * DH / 8;
-    for (int idx = tid; idx < KCH; idx += 256) {
-      int row = idx / (DH / 8), col = (idx - row * (DH / 8)) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kv0 + row < T) v = *(const uint4*)(Kb + (kv0 + row) * ld + col);
-      *(uint4*)&sK[row * KLD + col] = v;
-    }
-    // V tile, transposed into sV[dh][key]: each item is 4 keys x 4 features,
-    // read as four 8-byte row pieces (consecutive items -> consecutive features,
-    // so a key row is read contiguously) and written as four 8-byte key runs.
-    constexpr int VB = (KV / 4) * (DH / 4);
-    for (int idx = tid; idx < VB; idx += 256) {
-      const int kb4 = idx / (DH / 4), d4 = (idx - kb4 * (DH / 4)) * 4;
-      uint2 r[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        int kv = kv0 + 4 * kb4 + u;
-        r[u] = kv < T ? *(const uint2*)(Vb + kv * ld + d4) : make_uint2(0, 0);
-      }
-      // r[u] holds features d4..d4+3 of key u; column e = (r[0].e, r[1].e, r[2].e, r[3].e)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t sh = (e & 1) * 16;
-        uint32_t k0 = ((e < 2 ? r[0].x : r[0].y) >> sh) & 0xffffu;
-        uint32_t k1 = ((e < 2 ? r[1].x : r[1].y) >> sh) & 0xffffu;
-        uint32_t k2 = ((e < 2 ? r[2].x : r[2].y) >> sh) & 0xffffu;
-        uint32_t k3 = ((e < 2 ? r[3].x : r[3].y) >> sh) & 0xffffu;
-        *(uint2*)&sV[(d4 + e) * VLD + 4 * kb4] = make_uint2(k0 | (k1 << 16), k2 | (k3 << 16));
-      }
-    }
-    __syncthreads();
+  const int ntiles = (T + KV - 1) / KV;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1, kv0 = it * KV;
+    if (it + 1 < ntiles) gload(kv0 + KV);   // next tile in flight during this one
 
     // S^T blocks: 4 key blocks x 2 query blocks of 16x16.
     floatx4 s[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const bf16_t* kr = &sK[(16 * kb + c16) * KLD];
+      const bf16_t* kr = &sK[buf][(16 * kb + c16) * KLD];
       bf16x8_t k0 = *(const bf16x8_t*)(kr + 8 * g);
       bf16x8_t k1 = *(const bf16x8_t*)(kr + 32 + 8 * g);
       bf16x8_t kt = z8;
@@ -127,9 +164,22 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
         s[kb][qb] = a;
       }
     }
+    if (kv0 + KV > T) {                      // ragged last tile: drop keys >= T
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kv0 + 16 * kb + 4 * g + r >= T) {
+            s[kb][0][r] = -INFINITY;
+            s[kb][1][r] = -INFINITY;
+          }
+    }
 
-    // Online softmax (log2 domain).  Lane holds query column c16 of block qb and
-    // keys 16 kb + 4 g + r; the 4 lanes sharing c16 are combined by xor 16, 32.
+    // Online softmax in the exp2 domain.  Lane holds query column c16 of block
+    // qb and keys 16 kb + 4 g + r; the 4 lanes sharing c16 combine by xor 16, 32.
+    // The running max m_run (scaled) is raised only when some query's tile max
+    // exceeds it by RESCALE_SLACK, so P stays <= 2^RESCALE_SLACK and O, l are
+    // rescaled rarely; l and O always share the same reference m_run.
     bf16x8_t pf[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -137,32 +187,36 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int kv = kv0 + 16 * kb + 4 * g + r;
-          float v = s[kb][qb][r] * sl2;
-          v = kv < T ? v : -INFINITY;
-          s[kb][qb][r] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][qb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[qb], mx);
-      const float alpha = exp2f(m_run[qb] - m_new);
-      m_run[qb] = m_new;
-      l_run[qb] *= alpha;
+      const float mxs = mx * sl2;
+      if (__any(mxs > m_run[qb] + RESCALE_SLACK)) {
+        const float m_new = fmaxf(m_run[qb], mxs);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[db][qb][r] *= alpha;
+          for (int r = 0; r < 4; ++r) oacc[db][qb][r] *= alpha;
+      }
+      const float mneg = -m_run[qb];
       float ls = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; kb += 2) {
+        float p[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          bf16_t pb = f2bf(exp2f(s[kb][qb][r] - m_new));
-          ls += bf2f(pb);
-          pf[qb][kb >> 1][(kb & 1) * 4 + r] = __builtin_bit_cast(__bf16, pb);
+          p[r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], sl2, mneg));
+          p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s[kb + 1][qb][r], sl2, mneg));
         }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) ls += p[r];
+        uint4 u = make_uint4(f2bf2(p[0], p[1]), f2bf2(p[2], p[3]), f2bf2(p[4], p[5]),
+                             f2bf2(p[6], p[7]));
+        pf[qb][kb >> 1] = __builtin_bit_cast(bf16x8_t, u);
+      }
       l_run[qb] += ls;
     }
 
@@ -175,16 +229,20 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
       for (int j = 0; j < 2; ++j) {
         bf16x8_t vf = z8;
         if (dr < DH) {
-          uint2 lo = *(const uint2*)&sV[dr * VLD + 32 * j + 4 * g];
-          uint2 hi = *(const uint2*)&sV[dr * VLD + 32 * j + 16 + 4 * g];
-          uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          vf = __builtin_bit_cast(bf16x8_t, u);
+          uint2 lo = *(const uint2*)&sV[buf][dr * VLD + 32 * j + 4 * g];
+          uint2 hi = *(const uint2*)&sV[buf][dr * VLD + 32 * j + 16 + 4 * g];
+          vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb][j], oacc[db][qb], 0, 0, 0);
       }
     }
+
+    // Stage the prefetched tile into the other buffer (last read in iteration it-1,
+    // which every wave finished before the previous barrier).
+    if (it + 1 < ntiles) sstore(buf ^ 1);
+    __syncthreads();
   }
 
   // Normalise and store O[b, q, h*DH + dh] (token-major, heads concatenated).
@@ -200,11 +258,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const bf16_t* __restrict
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       int d0 = 16 * db + 4 * g;
-      if (d0 + 3 < DH) {
-        uint32_t lo = (uint32_t)f2bf(oacc[db][qb][0] * inv) | ((uint32_t)f2bf(oacc[db][qb][1] * inv) << 16);
-        uint32_t hi = (uint32_t)f2bf(oacc[db][qb][2] * inv) | ((uint32_t)f2bf(oacc[db][qb][3] * inv) << 16);
-        *(uint2*)(orow + d0) = make_uint2(lo, hi);
-      }
+      if (d0 + 3 < DH)
+        *(uint2*)(orow + d0) = make_uint2(f2bf2(oacc[db][qb][0] * inv, oacc[db][qb][1] * inv),
+                                          f2bf2(oacc[db][qb][2] * inv, oacc[db][qb][3] * inv));
     }
   }
 }
