@@ -152,7 +152,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": None,
-                "kernel": f"gemm_bf16_kernel<EPI_GELU,128,192,32,2,3> (FFN fc1: M={M}, N={hid}, K={d})",
+                "kernel": f"gemm_bf16_kernel<EPI_GELU,128,192,64> (FFN fc1: M={M}, N={hid}, K={d})",
                 "avg_launch_ms": round(kms, 4)}
 
     if args.copy_mib:

@@ -3,22 +3,27 @@
 //
 // A [M, K] (row stride lda) and W [N, K] are both K-contiguous (row-major
 // activations, [out, in] weights).  A BM x BN block tile is split over 4 waves
-// (2 x 2); each wave owns (BM/2) x (BN/2) outputs as 32x32 MFMA blocks.
+// (2 x 2); each wave owns (BM/2) x (BN/2) outputs as 32x32 MFMA blocks, in
+// which a lane holds one output column and 16 rows, so each store instruction
+// of the epilogue covers whole 128-byte row segments.
 //
-// K is consumed in 64-wide slices through a ring of STAGES LDS buffers filled
-// by direct global->LDS loads (global_load_lds_dwordx4: each lane moves 16 bytes
-// straight into LDS at base + 16*lane), so the next STAGES-1 slices are in
-// flight while the current one feeds the MFMAs and no registers stage the
-// copy.  LDS rows are 128 B (64 bf16); the 16-byte chunk c of row r sits at
-// chunk c ^ ((r >> 1) & 7), which spreads the rows of one MFMA operand fetch
-// over all 64 banks; each lane therefore fetches the global chunk that belongs
-// in its LDS slot.  Rows past M or N read a clamped (valid) row and are never stored.
-// Within a slice the operand fragments of the next 16-wide k step are read
-// from LDS while the current step's MFMAs run.
+// K is consumed in BK-wide slices through two LDS buffers filled by direct
+// global->LDS loads (global_load_lds_dwordx4: each lane moves 16 bytes straight
+// into LDS at base + 16*lane), so no registers stage the copy.  LDS rows are
+// BK bf16; 16-byte chunk c of row r sits at chunk c ^ key(r), which spreads the
+// rows of one operand fetch over all 64 banks; each lane therefore fetches the
+// global chunk that belongs in its LDS slot.  Rows past M or N read a clamped
+// (valid) row and are never stored.
+//
+// Schedule (one flat sequence of 16-wide k steps): the operand fragments of
+// step s+1 are read from LDS while the MFMAs of step s run.  The one barrier
+// per slice sits before the slice's last step: by then every fragment of the
+// slice is in registers, so after it (a) the first fragments of the next slice
+// can be read under the last step's MFMAs and (b) the copies of slice kt+2 can
+// refill the buffer of slice kt, interleaved with those MFMAs.
 #include <type_traits>
 
 #include "common.h"
-#include "epilogue.h"
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
@@ -36,17 +41,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Wait until at most `left` slices of this wave's copies are in flight
-// (left < STAGES - 1; each slice is L copies).
-template <int L, int STAGES>
-__device__ __forceinline__ void wait_slices(int left) {
-  if constexpr (STAGES >= 4) {
-    if (left >= 2) { wait_vmcnt<2 * L>(); return; }
-  }
-  if constexpr (STAGES >= 3) {
-    if (left >= 1) { wait_vmcnt<L>(); return; }
-  }
-  wait_vmcnt<0>();
+// s_waitcnt with only the LDS/scalar counter constrained to 0.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier without the release fence of __syncthreads() (which would
+// drain every outstanding copy); callers order memory with explicit waits.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs (each with
@@ -82,25 +87,25 @@ __device__ __forceinline__ int row_key(int r) {
   else return (r >> 2) & 3;
 }
 
-// s_waitcnt with only the LDS/scalar counter constrained to 0.
-__device__ __forceinline__ void wait_lgkm0() {
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
-}
-
-template <int EPI, int BM, int BN, int BK, int STAGES, int MINWG, int SWZ, int FP = 0>
+// vec: the output is 4-byte aligned with an even row stride (bf16 column pairs
+// may be stored as words).
+template <int EPI, int BM, int BN, int BK, int MINWG, int SWZ, int ILV>
 __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __restrict__ A, int lda,
                                                                 const bf16_t* __restrict__ W, int M,
-                                                                int N, int K, EpiParams ep) {
+                                                                int N, int K, EpiParams ep, int vec) {
   static_assert(BK == 32 || BK == 64, "slice width");
-  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
   constexpr int CPR = BK / 8;                    // 16-byte chunks per LDS row
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int NA = BM * CPR / 256, NB = BN * CPR / 256;   // 1 KB copies per wave per slice
   constexpr int L = NA + NB;
+  constexpr int KK = BK / 16;                    // MFMA k steps per slice (even)
+  constexpr int NF = TM + TN;                    // fragments per step
+  constexpr int NMF = TM * TN;                   // MFMAs per step
   constexpr int ROWB = BK * 2;                   // LDS row bytes
   constexpr int A_BYTES = BM * ROWB, STAGE_BYTES = (BM + BN) * ROWB;
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+  static_assert(NF <= NMF + 1 && (L + NMF - 1) / NMF <= 4, "interleave shape");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -108,227 +113,252 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
   int tm, tn;
   tile_coords<SWZ>(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
+  const int half = lane >> 5;
+
+  // Accumulators start at the bias.  acc[i][j][r] is output column
+  // ncol + 32 j, row mrow + 32 i + 8 (r / 4) + (r % 4).
+  const int ncol = n0 + wn * WN + (lane & 31);
+  const int mrow = m0 + wm * WM + 4 * half;
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = ncol + j * 32;
+    const float b = ep.bias ? (col < N ? 1.0f : 0.0f) * ep.bias[min(col, N - 1)] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = b;
+  }
 
   // Per-lane source of each direct LDS copy: slot s of the tile is row s / CPR,
   // stored chunk s % CPR = logical chunk (s % CPR) ^ key(row).
-  const bf16_t* pa[NA];
-  const bf16_t* pb[NB];
+  const bf16_t* src[L];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    int s = (w * NA + i) * 64 + lane, r = s / CPR, c = (s % CPR) ^ row_key<BK>(r);
-    int m = min(m0 + r, M - 1);
-    pa[i] = A + (int64_t)m * lda + c * 8;
+  for (int c = 0; c < L; ++c) {
+    const bool is_a = c < NA;
+    const int s = (w * (is_a ? NA : NB) + (is_a ? c : c - NA)) * 64 + lane;
+    const int r = s / CPR, ch = (s % CPR) ^ row_key<BK>(r);
+    src[c] = is_a ? A + (int64_t)min(m0 + r, M - 1) * lda + ch * 8
+                  : W + (int64_t)min(n0 + r, N - 1) * K + ch * 8;
   }
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    int s = (w * NB + i) * 64 + lane, r = s / CPR, c = (s % CPR) ^ row_key<BK>(r);
-    int n = min(n0 + r, N - 1);
-    pb[i] = W + (int64_t)n * K + c * 8;
-  }
-  auto issue = [&](int kt) {
-    char* st = smem + (kt % STAGES) * STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < NA; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(pa[i] + kt * BK),
-                                       (lds_void*)(st + (w * NA + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(pb[i] + kt * BK),
-                                       (lds_void*)(st + A_BYTES + (w * NB + i) * 1024), 16, 0, 0);
+  auto copy = [&](int kt, int c) {
+    char* st = smem + (kt & 1) * STAGE_BYTES +
+               (c < NA ? (w * NA + c) * 1024 : A_BYTES + (w * NB + c - NA) * 1024);
+    __builtin_amdgcn_global_load_lds((const void*)(src[c] + kt * BK), (lds_void*)st, 16, 0, 0);
   };
-
-  floatx16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // LDS byte offsets of this lane's operand rows (fixed over the loop); every
   // fragment row is a multiple of 32 plus (lane & 31), so its key depends on
   // the lane only.
-  int offa[TM], offb[TN];
+  int off[NF];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) offa[i] = (wm * WM + i * 32 + (lane & 31)) * ROWB;
-#pragma unroll
-  for (int j = 0; j < TN; ++j) offb[j] = A_BYTES + (wn * WN + j * 32 + (lane & 31)) * ROWB;
+  for (int f = 0; f < NF; ++f)
+    off[f] = f < TM ? (wm * WM + f * 32 + (lane & 31)) * ROWB
+                    : A_BYTES + (wn * WN + (f - TM) * 32 + (lane & 31)) * ROWB;
   const int key = row_key<BK>(lane & 31);
-  const int half = lane >> 5;
+
+  // Fragment slots are read in the order of their first use by the MFMAs of a
+  // step (A0, B0 .. B(TN-1), A1 .. A(TM-1)), so each MFMA waits only for the
+  // reads it needs.
+  bf16x8_t frag[2][NF];
+  auto slot = [](int q) { return q == 0 ? 0 : (q <= TN ? TM + q - 1 : q - TN); };
+  auto fetch = [&](int buf, int kt, int kk, int q) {
+    const int f = slot(q);
+    const char* st = smem + (kt & 1) * STAGE_BYTES;
+    frag[buf][f] = *(const bf16x8_t*)(st + off[f] + ((((kk * 2 + half) ^ key)) << 4));
+  };
 
   const int nk = K / BK;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s);
-
-  if constexpr (FP == 0) {
-    for (int kt = 0; kt < nk; ++kt) {
-      // Slice kt has landed in LDS once this wave's copies of it are done (later
-      // slices may stay in flight) and every wave has passed the barrier.  A bare
-      // s_barrier is used: __syncthreads() would add a release fence that drains
-      // all outstanding copies.  The stage refilled below was last read in
-      // iteration kt-1; those LDS reads completed before their MFMAs, which each
-      // wave issued before reaching this barrier.
-      wait_slices<L, STAGES>(min(STAGES - 2, nk - 1 - kt));
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-      const char* st = smem + (kt % STAGES) * STAGE_BYTES;
-
-      bf16x8_t fa[2][TM], fb[2][TN];
-      auto fetch = [&](int buf, int kk) {
-        const int ch = ((kk * 2 + half) ^ key) << 4;
+  for (int c = 0; c < L; ++c) copy(0, c);
+  if (nk > 1) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[buf][i] = *(const bf16x8_t*)(st + offa[i] + ch);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb[buf][j] = *(const bf16x8_t*)(st + offb[j] + ch);
-      };
-      fetch(0, 0);
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        if (kk + 1 < BK / 16) fetch((kk + 1) & 1, kk + 1);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
-                                                                acc[i][j], 0, 0, 0);
-      }
-    }
+    for (int c = 0; c < L; ++c) copy(1, c);
+    wait_vmcnt<L>();
   } else {
-    // Slice-ahead operand prefetch: iteration kt reads all fragments of slice
-    // kt+1 from LDS while the MFMAs of slice kt run on fragments read one
-    // iteration earlier.  Needs STAGES >= 3: the stage refilled in iteration kt
-    // holds slice kt-1, whose fragments every wave finished reading (and waited
-    // for) before this iteration's barrier.
-    static_assert(STAGES >= 3, "slice-ahead prefetch needs 3 stages");
-    constexpr int KK = BK / 16;
-    bf16x8_t fa[2][KK][TM], fb[2][KK][TN];
-    auto fetch_slice = [&](int buf, int kt) {
-      const char* st = smem + (kt % STAGES) * STAGE_BYTES;
+    wait_vmcnt<0>();
+  }
+  bare_barrier();
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int ch = ((kk * 2 + half) ^ key) << 4;
+  for (int q = 0; q < NF; ++q) fetch(0, 0, 0, q);
+
+  // One slice; MORE: slice kt+1 exists, DMA: slice kt+2 exists.
+  auto slice = [&](int kt, auto more_c, auto dma_c) {
+    constexpr bool MORE = decltype(more_c)::value, DMA = decltype(dma_c)::value;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[buf][kk][i] = *(const bf16x8_t*)(st + offa[i] + ch);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb[buf][kk][j] = *(const bf16x8_t*)(st + offb[j] + ch);
-      }
-    };
-    wait_slices<L, STAGES>(min(STAGES - 2, nk - 1));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    fetch_slice(0, 0);
-    // One step per slice; the register buffer index must be a compile-time
-    // constant (a runtime index would turn the fragment arrays into memory), so
-    // the loop runs two slices per trip with the buffers swapped.
-    auto step = [&](auto cur_c, int kt) {
-      constexpr int cur = decltype(cur_c)::value;
-      if (kt + 1 < nk) {
-        // the fragments of slice kt are in registers; slice kt+1 must be in LDS
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;   // KK is even: step parity = kk parity
+      const bool last = kk == KK - 1;
+      if (last && MORE) {
+        // Every fragment of slice kt is in registers once this wave's reads
+        // are done; slice kt+1 has landed once this wave's copies of it (the
+        // only ones in flight) are done and all waves pass the barrier.
         wait_lgkm0();
-        wait_slices<L, STAGES>(min(STAGES - 3, nk - 2 - kt));
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-        fetch_slice(cur ^ 1, kt + 1);
+        wait_vmcnt<0>();
+        bare_barrier();
       }
+      const bool nfetch = !last || MORE;
+      const int fkt = last ? kt + 1 : kt, fkk = last ? 0 : kk + 1;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
+      for (int q = 0; q < NMF; ++q) {
+        const int i = q / TN, j = q % TN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[cur][i], frag[cur][TM + j],
+                                                            acc[i][j], 0, 0, 0);
+        if (q < NF && nfetch) fetch(nxt, fkt, fkk, q);
+        if (last && DMA) {
+          constexpr int PER = (L + NMF - 1) / NMF;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+          for (int u = 0; u < PER; ++u)
+            if (q * PER + u < L) copy(kt + 2, q * PER + u);
+        }
+        if constexpr (ILV) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) slice(kt, T_{}, T_{});
+  if (kt + 1 < nk) slice(kt++, T_{}, F_{});
+  slice(kt, F_{}, F_{});
+
+  // Epilogue.
+  const bool full = m0 + BM <= M && n0 + BN <= N;
+  if constexpr (EPI == EPI_GATED) {
+    // In-place read-modify-write of the fp32 residual.  The compiler must
+    // assume the stores alias later loads, and one counter tracks both, so
+    // loads interleaved with stores would each wait a full round trip.  Whole
+    // tiles whose 32-row blocks each lie in one batch row (T % 32 == 0) run a
+    // two-deep pipeline over batches of 4 rows x TN columns per lane instead:
+    // batch q+1 is loaded before batch q is stored.
+    if (full && ep.T % 32 == 0) {
+      float gv[TM][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const float* g = ep.mod + (int64_t)((mrow + i * 32) / ep.T) * ep.mod_stride + ep.gate_off;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) gv[i][j] = g[ncol + j * 32];
+      }
+      float* xt = (float*)ep.out + (int64_t)mrow * ep.ldo + ncol;
+      constexpr int NQ = TM * 4;   // batch q: block q / 4, register group q % 4
+      auto xaddr = [&](int q, int r4, int j) {
+        return xt + (int64_t)((q >> 2) * 32 + 8 * (q & 3) + r4) * ep.ldo + j * 32;
+      };
+      float xv[2][4][TN];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) xv[0][r4][j] = *xaddr(0, r4, j);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        if (q + 1 < NQ) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) xv[(q + 1) & 1][r4][j] = *xaddr(q + 1, r4, j);
+        }
+        const int i = q >> 2;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][kk][i], fb[cur][kk][j],
-                                                                acc[i][j], 0, 0, 0);
-    };
-    for (int kt = 0; kt < nk; kt += 2) {
-      step(std::integral_constant<int, 0>{}, kt);
-      if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
-    }
-  }
-
-  // Epilogue.  32x32 accumulator layout: lane holds column (lane % 32);
-  // register r holds row 8*(r/4) + 4*(lane/32) + (r % 4).  Per-column values
-  // (bias, and the gate when the tile lies in one batch row) are loaded once.
-  const int col0 = n0 + wn * WN + (lane & 31);
-  const int row0 = m0 + wm * WM + 4 * half;
-  float bcol[TN];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    int col = col0 + j * 32;
-    bcol[j] = (ep.bias && col < N) ? ep.bias[col] : 0.0f;
-  }
-  if constexpr (EPI == EPI_GATED) {
-    const int mlast = min(m0 + BM, M) - 1;
-    const bool one_b = (m0 / ep.T) == (mlast / ep.T);
-    float gcol[TN];
-    if (one_b) {
-      const float* g = ep.mod + (int64_t)(m0 / ep.T) * ep.mod_stride + ep.gate_off;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) gcol[j] = (col0 + j * 32 < N) ? g[col0 + j * 32] : 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + i * 32 + 8 * (r >> 2) + (r & 3);
-        if (row >= M) continue;
-        float* xr = (float*)ep.out + (int64_t)row * ep.ldo;
-        const float* g = ep.mod + (int64_t)(row / ep.T) * ep.mod_stride + ep.gate_off;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = col0 + j * 32;
-          if (col < N) {
-            const float gv = one_b ? gcol[j] : g[col];
-            xr[col] = xr[col] + gv * (acc[i][j][r] + bcol[j]);
-          }
-        }
+            *xaddr(q, r4, j) = xv[q & 1][r4][j] + gv[i][j] * acc[i][j][(q & 3) * 4 + r4];
       }
+      return;
+    }
+  } else if constexpr (EPI == EPI_BIAS_F32) {
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float* o = (float*)ep.out + (int64_t)(mrow + i * 32 + 8 * (r >> 2) + (r & 3)) * ep.ldo + ncol;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) o[j * 32] = acc[i][j][r];
+        }
+      return;
+    }
   } else {
+    // bf16 outputs: neighbouring lanes (columns 2c, 2c+1) trade one value of
+    // each pair of adjacent rows, so every lane stores two adjacent columns
+    // of one row as a 4-byte word.
+    if (full && vec) {
+      const bool odd = lane & 1;
+      bf16_t* ot = (bf16_t*)ep.out + (int64_t)(mrow + odd) * ep.ldo + (ncol & ~1);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + i * 32 + 8 * (r >> 2) + (r & 3);
-        if (row >= M) continue;
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = col0 + j * 32;
-          if (col >= N) continue;
-          float v = acc[i][j][r] + bcol[j];
-          const int64_t o = (int64_t)row * ep.ldo + col;
-          if constexpr (EPI == EPI_BIAS_F32) ((float*)ep.out)[o] = v;
-          else if constexpr (EPI == EPI_BIAS_DT) ((bf16_t*)ep.out)[o] = f2bf(v);
-          else if constexpr (EPI == EPI_GELU) ((bf16_t*)ep.out)[o] = f2bf(gelu_tanh_f(v));
-          else static_assert(EPI == EPI_BIAS_F32, "epilogue");
+          for (int p = 0; p < 8; ++p) {
+            const int r = (p >> 1) * 4 + (p & 1) * 2;     // rows r, r+1 of a register group
+            float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
+            if constexpr (EPI == EPI_GELU) {
+              v0 = gelu_tanh_f(v0);
+              v1 = gelu_tanh_f(v1);
+            } else {
+              static_assert(EPI == EPI_BIAS_DT, "epilogue");
+            }
+            // quad_perm [1, 0, 3, 2]: exchange with the neighbouring lane
+            const float send = odd ? v0 : v1;
+            const float recv = __builtin_bit_cast(
+                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF,
+                                                   false));
+            const uint32_t word = odd ? f2bf2(recv, v1) : f2bf2(v0, recv);
+            *(uint32_t*)(ot + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ep.ldo + j * 32) = word;
+          }
+      return;
+    }
+  }
+  // Ragged or unaligned tiles: element by element with bounds checks.
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = mrow + i * 32 + 8 * (r >> 2) + (r & 3);
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = ncol + j * 32;
+        if (n >= N) continue;
+        const float v = acc[i][j][r];
+        const int64_t o = (int64_t)m * ep.ldo + n;
+        if constexpr (EPI == EPI_BIAS_F32) {
+          ((float*)ep.out)[o] = v;
+        } else if constexpr (EPI == EPI_BIAS_DT) {
+          ((bf16_t*)ep.out)[o] = f2bf(v);
+        } else if constexpr (EPI == EPI_GELU) {
+          ((bf16_t*)ep.out)[o] = f2bf(gelu_tanh_f(v));
+        } else {
+          static_assert(EPI == EPI_GATED, "epilogue");
+          const float g = ep.mod[(int64_t)(m / ep.T) * ep.mod_stride + ep.gate_off + n];
+          float* X = (float*)ep.out;
+          X[o] = X[o] + g * v;
         }
       }
-  }
+    }
 }
 
-template <int EPI, int BM, int BN, int BK, int STAGES, int MINWG>
+template <int EPI, int BM, int BN, int BK, int MINWG>
 hipError_t run(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
                const EpiParams& ep, hipStream_t s) {
-  int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  // bf16 outputs are stored as 4-byte column pairs
+  const int vec = ((uintptr_t)ep.out & 3) == 0 && ep.ldo % 2 == 0;
   if (tiles % 8 == 0)
-    gemm_bf16_kernel<EPI, BM, BN, BK, STAGES, MINWG, 1><<<tiles, 256, 0, s>>>(A, lda, W, M, N, K, ep);
+    gemm_bf16_kernel<EPI, BM, BN, BK, MINWG, 1, 1><<<tiles, 256, 0, s>>>(A, lda, W, M, N, K, ep, vec);
   else
-    gemm_bf16_kernel<EPI, BM, BN, BK, STAGES, MINWG, 0><<<tiles, 256, 0, s>>>(A, lda, W, M, N, K, ep);
+    gemm_bf16_kernel<EPI, BM, BN, BK, MINWG, 0, 1><<<tiles, 256, 0, s>>>(A, lda, W, M, N, K, ep, vec);
   return hipGetLastError();
 }
 
 template <int EPI>
 hipError_t pick(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
                 const EpiParams& ep, hipStream_t s) {
-  // 128x192 tiles, 32-wide K slices, 2 LDS stages (40 KB): three workgroups fit
-  // on a CU, and M = 16384 with N in {1152, 3456, 4608} gives 1, 3 and 4 full
-  // rounds of 768 resident workgroups on 256 CUs.
-  if (N % 192 == 0) return run<EPI, 128, 192, 32, 2, 3>(A, lda, W, M, N, K, ep, s);
-  return run<EPI, 128, 128, 32, 2, 3>(A, lda, W, M, N, K, ep, s);
+  // 128x192 tiles, 64-wide K slices, two LDS buffers (80 KB): two workgroups
+  // per CU.
+  if (N % 192 == 0) return run<EPI, 128, 192, 64, 2>(A, lda, W, M, N, K, ep, s);
+  return run<EPI, 128, 128, 64, 2>(A, lda, W, M, N, K, ep, s);
 }
 
 }  // namespace
