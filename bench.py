@@ -49,6 +49,22 @@ def parse():
     return ap.parse_args()
 
 
+def measured_traffic(src_rel: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record (each scaled by the factor a plain copy of known size gave),
+    or None when there is no record or the kernel source changed since."""
+    import hashlib
+    rec_path = os.path.join(ROOT, "profiles", "gemm_fc1_hbm_counters.json")
+    try:
+        rec = json.load(open(rec_path))
+        src = open(os.path.join(ROOT, src_rel), "rb").read()
+    except OSError:
+        return None
+    if rec.get("kernel") != kernel or rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return int(rec["traffic_bytes"])
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -149,9 +165,12 @@ def main():
     kms = k0.elapsed_time(k1) / args.kernel_launches
     kflop = 2.0 * M * hid * d
     k_tflops = kflop / (kms * 1e-3) / 1e12
+    traffic = measured_traffic("diffusion_transformer_denoiser_amd/csrc/gemm_mfma.hip",
+                               "gemm_bf16_kernel<5, 128, 192, 64, 2, 1, 1>")
     roofline = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": None,
+                "traffic": traffic, "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE)",
+                "algorithmic_bytes": (M * d + hid * d) * 2 + hid * 4 + M * hid * 2,
                 "kernel": f"gemm_bf16_kernel<EPI_GELU,128,192,64> (FFN fc1: M={M}, N={hid}, K={d})",
                 "avg_launch_ms": round(kms, 4)}
 
