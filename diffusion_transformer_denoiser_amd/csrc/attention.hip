@@ -45,12 +45,20 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
   static_assert(DH == 64 || DH == 72, "head dim");
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][KV * KLD];
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][DH * VLD];
+  // 16 zero bytes: operand lanes past dh read here instead of taking a branch
+  __shared__ __attribute__((aligned(16))) uint4 zslot;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int bh = blockIdx.y;
+  // Workgroups are dispatched round-robin over the 8 XCDs; when their count
+  // allows, workgroup i runs logical block (i % 8) * (n / 8) + i / 8, so the
+  // query blocks of one (row, head) run on one XCD and share its L2 copy of K, V.
+  const int nwg = gridDim.x * gridDim.y;
+  int lin = blockIdx.y * gridDim.x + blockIdx.x;
+  if ((nwg & 7) == 0) lin = (lin & 7) * (nwg >> 3) + (lin >> 3);
+  const int bh = lin / gridDim.x;
   const int b = bh / H, h = bh - b * H;
-  const int q0 = blockIdx.x * 128 + wave * 32;
+  const int q0 = (lin - bh * gridDim.x) * 128 + wave * 32;
   const int64_t ld = 3LL * H * DH;                       // packed row stride
   const bf16_t* Qb = QKV + (int64_t)b * T * ld + h * DH;   // + t * ld
   const bf16_t* Kb = Qb + (int64_t)H * DH;
@@ -71,29 +79,43 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
       if (ok && g == 0) qt[qb] = *(const bf16x8_t*)(Qb + q * ld + 64);
   }
 
-  // Tile staging: global -> registers (issued one tile ahead) -> LDS.
+  // Tile staging: global -> registers (issued one tile ahead) -> LDS.  Loads
+  // are raw buffer loads on this (batch row)'s slice of qkv: keys at or past T
+  // lie outside the buffer range and read as zeros, so the loop carries no
+  // bounds tests.  Each thread's byte offsets inside a tile are fixed; a tile
+  // adds kv0 * row stride.
+  const int nrec = (int)((int64_t)T * ld * 2);
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Kb, (short)0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Vb, (short)0, nrec, 0x00020000);
+  int koff[KPT], voff[VPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int idx = min(tid + u * 256, KCH - 1);
+    const int row = idx / (DH / 8), col = (idx - row * (DH / 8)) * 8;
+    koff[u] = (int)((row * ld + col) * 2);
+  }
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int idx = min(tid + u * 256, VB - 1);
+    const int kb4 = idx / (DH / 4), d4 = (idx - kb4 * (DH / 4)) * 4;
+    voff[u] = (int)((4 * kb4 * ld + d4) * 2);
+  }
+  const int ldb = (int)(ld * 2);
   uint4 kreg[KPT];
   uint2 vreg[VPT][4];
   auto gload = [&](int kv0) {
+    const int t0 = kv0 * ldb;
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int idx = tid + u * 256;
-      kreg[u] = make_uint4(0, 0, 0, 0);
-      if (idx < KCH) {
-        const int row = idx / (DH / 8), col = (idx - row * (DH / 8)) * 8;
-        if (kv0 + row < T) kreg[u] = *(const uint4*)(Kb + (kv0 + row) * ld + col);
-      }
-    }
+    for (int u = 0; u < KPT; ++u)
+      kreg[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, koff[u] + t0, 0, 0));
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int idx = tid + u * 256;
-      const int kb4 = idx / (DH / 4), d4 = (idx - kb4 * (DH / 4)) * 4;
+    for (int u = 0; u < VPT; ++u)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int kv = kv0 + 4 * kb4 + q;
-        vreg[u][q] = (idx < VB && kv < T) ? *(const uint2*)(Vb + kv * ld + d4) : make_uint2(0, 0);
-      }
-    }
+      for (int q = 0; q < 4; ++q)
+        vreg[u][q] = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[u] + t0 + q * ldb, 0, 0));
   };
   // K rows as they are; V transposed into sV[dh][key]: vreg[u][q] holds features
   // d4..d4+3 of key 4*kb4+q, column e is (vreg[u][0].e, .., vreg[u][3].e).
@@ -138,6 +160,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
     for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int ntiles = (T + KV - 1) / KV;
+  if (tid == 0) zslot = make_uint4(0, 0, 0, 0);
   gload(0);
   sstore(0);
   __syncthreads();
@@ -154,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
       bf16x8_t k1 = *(const bf16x8_t*)(kr + 32 + 8 * g);
       bf16x8_t kt = z8;
       if constexpr (TAIL)
-        if (g == 0) kt = *(const bf16x8_t*)(kr + 64);
+        kt = *(const bf16x8_t*)(g == 0 ? kr + 64 : (const bf16_t*)&zslot);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         floatx4 a = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -227,12 +250,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
       const int dr = 16 * db + c16;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        bf16x8_t vf = z8;
-        if (dr < DH) {
-          uint2 lo = *(const uint2*)&sV[buf][dr * VLD + 32 * j + 4 * g];
-          uint2 hi = *(const uint2*)&sV[buf][dr * VLD + 32 * j + 16 + 4 * g];
-          vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        }
+        const bool in = dr < DH;
+        const uint2 lo = *(const uint2*)(in ? &sV[buf][dr * VLD + 32 * j + 4 * g] : (const bf16_t*)&zslot);
+        const uint2 hi = *(const uint2*)(in ? &sV[buf][dr * VLD + 32 * j + 16 + 4 * g] : (const bf16_t*)&zslot);
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb][j], oacc[db][qb], 0, 0, 0);
