@@ -53,7 +53,7 @@ struct dit_handle {
 namespace {
 
 struct WsLayout {
-  size_t e, th, c, sc, mod, X, H, qkv, o, G, Y, total;
+  size_t e, th, c, sc, pp, pe, mod, X, H, qkv, o, G, Y, total;
 };
 
 WsLayout ws_layout(const dit_handle* h, int rows) {
@@ -69,6 +69,8 @@ WsLayout ws_layout(const dit_handle* h, int rows) {
   L.th = take(R * h->d * 4);
   L.c = take(R * h->d * 4);
   L.sc = take(R * h->d * es);
+  L.pp = take(h->cond_dim > 0 ? R * h->d * 4 : 0);          // pooled projection
+  L.pe = take(h->cfg.rope3d ? 0 : (size_t)h->T * h->d * 4);  // 2-D position table
   L.mod = take(R * h->mod_stride * 4);
   L.X = take(M * h->d * 4);
   L.H = take(M * h->d * es);
@@ -186,41 +188,71 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
   float* Y = at<float>(ws, L.Y);
 
   // c = t_emb (+ pooled projection) (+ class row); sc = SiLU(c) in the GEMM dtype.
-  DIT_HIP(launch_timestep_embed(t, rows, src_rows, h->freq, e, s));
   ALoad a;
   memset(&a, 0, sizeof a);
   EpiParams ep = epi0();
-  if (h->cond_dim > 0) {
-    a.ptr = pooled; a.lda = h->cond_dim; a.a_dtype = 0; a.src_rows = src_rows;
-    ep.bias = h->w.pool_b; ep.out = c; ep.ldo = d;
-    DIT_HIP(launch_gemm_valu(EPI_BIAS_F32, A_PLAIN, a, h->w.pool_w, h->dtype, rows, d,
-                             h->cond_dim, ep, s));
+  if (h->dtype == DIT_BF16 && h->freq % 64 == 0) {
+    // bf16: the sinusoid and SiLU(hidden) are bf16 GEMM operands on the MFMA
+    // path; the class row and the pooled projection are added afterwards.
+    bf16_t* eb = at<bf16_t>(ws, L.e);
+    bf16_t* thb = at<bf16_t>(ws, L.th);
+    DIT_HIP(launch_timestep_embed_bf16(t, rows, src_rows, h->freq, eb, s));
+    ep.bias = h->w.t1_b; ep.out = thb; ep.ldo = d;
+    DIT_HIP(linear(h, EPI_SILU_DT, eb, h->freq, h->w.t1_w, rows, d, h->freq, ep, s));
+    ep = epi0();
+    ep.bias = h->w.t2_b; ep.out = c; ep.ldo = d;
+    DIT_HIP(linear(h, EPI_BIAS_F32, thb, d, h->w.t2_w, rows, d, d, ep, s));
+    float* pp = nullptr;
+    if (h->cond_dim > 0) {
+      pp = at<float>(ws, L.pp);
+      a.ptr = pooled; a.lda = h->cond_dim; a.a_dtype = 0; a.src_rows = src_rows;
+      ep = epi0();
+      ep.bias = h->w.pool_b; ep.out = pp; ep.ldo = d;
+      DIT_HIP(launch_gemm_valu(EPI_BIAS_F32, A_PLAIN, a, h->w.pool_w, h->dtype, rows, d,
+                               h->cond_dim, ep, s));
+    }
+    DIT_HIP(launch_cond_finish(c, rows, d, h->ncls > 0 ? h->w.y_table : nullptr, y, src_rows,
+                               null_from, h->ncls, pp, sc, h->dtype, s));
+  } else {
+    DIT_HIP(launch_timestep_embed(t, rows, src_rows, h->freq, e, s));
+    if (h->cond_dim > 0) {
+      a.ptr = pooled; a.lda = h->cond_dim; a.a_dtype = 0; a.src_rows = src_rows;
+      ep.bias = h->w.pool_b; ep.out = c; ep.ldo = d;
+      DIT_HIP(launch_gemm_valu(EPI_BIAS_F32, A_PLAIN, a, h->w.pool_w, h->dtype, rows, d,
+                               h->cond_dim, ep, s));
+    }
+    a.ptr = e; a.lda = h->freq; a.a_dtype = 0; a.src_rows = rows;
+    ep = epi0();
+    ep.bias = h->w.t1_b; ep.out = th; ep.ldo = d;
+    DIT_HIP(launch_gemm_valu(EPI_BIAS_SILU, A_PLAIN, a, h->w.t1_w, h->dtype, rows, d, h->freq,
+                             ep, s));
+    a.ptr = th; a.lda = d;
+    ep = epi0();
+    ep.bias = h->w.t2_b; ep.out = c; ep.ldo = d; ep.silu_out = sc;
+    ep.add_prev = h->cond_dim > 0;
+    if (h->ncls > 0) {
+      ep.table = h->w.y_table; ep.labels = y; ep.label_rows = src_rows;
+      ep.null_from = null_from; ep.ncls = h->ncls;
+    }
+    DIT_HIP(launch_gemm_valu(EPI_COND, A_PLAIN, a, h->w.t2_w, h->dtype, rows, d, d, ep, s));
   }
-  a.ptr = e; a.lda = h->freq; a.a_dtype = 0; a.src_rows = rows;
-  ep = epi0();
-  ep.bias = h->w.t1_b; ep.out = th; ep.ldo = d;
-  DIT_HIP(launch_gemm_valu(EPI_BIAS_SILU, A_PLAIN, a, h->w.t1_w, h->dtype, rows, d, h->freq, ep, s));
-  a.ptr = th; a.lda = d;
-  ep = epi0();
-  ep.bias = h->w.t2_b; ep.out = c; ep.ldo = d; ep.silu_out = sc;
-  ep.add_prev = h->cond_dim > 0;
-  if (h->ncls > 0) {
-    ep.table = h->w.y_table; ep.labels = y; ep.label_rows = src_rows;
-    ep.null_from = null_from; ep.ncls = h->ncls;
-  }
-  DIT_HIP(launch_gemm_valu(EPI_COND, A_PLAIN, a, h->w.t2_w, h->dtype, rows, d, d, ep, s));
 
   // All modulation vectors (every block and the final layer) in one GEMM.
   ep = epi0();
   ep.bias = h->w.ada_b; ep.out = mod; ep.ldo = h->mod_stride;
   DIT_HIP(linear(h, EPI_BIAS_F32, sc, d, h->w.ada_w, rows, h->mod_stride, d, ep, s));
 
-  // Patchify gather + patch embedding + bias + 2-D position embedding.
+  // Patchify gather + patch embedding + bias + 2-D position embedding (from a
+  // table of the T x d embedding, computed once per call).
   memset(&a, 0, sizeof a);
   a.ptr = x_t; a.a_dtype = h->dtype; a.src_rows = src_rows; a.g = h->gin;
   ep = epi0();
   ep.bias = h->w.pe_b; ep.out = X; ep.ldo = d; ep.T = T;
-  ep.pe = h->cfg.rope3d ? 0 : 1; ep.gh = h->gh; ep.gw = h->gw;
+  if (!h->cfg.rope3d) {
+    float* pe = at<float>(ws, L.pe);
+    DIT_HIP(launch_pos_embed_table(h->gh, h->gw, d, pe, s));
+    ep.pe_tab = pe;
+  }
   DIT_HIP(launch_gemm_valu(EPI_PATCH, A_PATCH, a, h->w.pe_w, h->dtype, M, d, h->kin, ep, s));
 
   if (taps) {
@@ -243,11 +275,9 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
   // Final layer: LN + modulation (b_f, g_f), linear decoder.
   const int fb = 6 * d * h->N;
   DIT_HIP(launch_ln_modulate(X, M, T, d, mod, h->mod_stride, fb, fb + d, h->eps, Hb, h->dtype, s));
-  memset(&a, 0, sizeof a);
-  a.ptr = Hb; a.lda = d; a.a_dtype = h->dtype; a.src_rows = M;
   ep = epi0();
   ep.bias = h->w.out_b; ep.out = Y; ep.ldo = h->kout;
-  DIT_HIP(launch_gemm_valu(EPI_BIAS_F32, A_PLAIN, a, h->w.out_w, h->dtype, M, h->kout, d, ep, s));
+  DIT_HIP(linear(h, EPI_BIAS_F32, Hb, d, h->w.out_w, M, h->kout, d, ep, s));
   if (taps && taps->y_final)
     DIT_HIP(hipMemcpyAsync(taps->y_final, Y, (size_t)M * h->kout * 4, hipMemcpyDeviceToDevice, s));
   return DIT_OK;

@@ -72,7 +72,8 @@ enum EpiKind {
   EPI_BIAS_DT = 3,      // out_dtype[m, n] = C + bias[n]            (packed q | k | v)
   EPI_GATED = 4,        // X[m, n] += gate[b, n] * (C + bias[n])                (fp32 residual)
   EPI_GELU = 5,         // out_dtype[m, n] = GELU_tanh(C + bias[n])
-  EPI_PATCH = 6,        // X[m, n] = C + bias[n] (+ 2-D sin-cos PE(tau, n))
+  EPI_PATCH = 6,        // X[m, n] = C + bias[n] (+ pe_tab[m % T, n])
+  EPI_SILU_DT = 7,      // out_dtype[m, n] = SiLU(C + bias[n])                  (timestep MLP)
 };
 
 struct EpiParams {
@@ -92,14 +93,25 @@ struct EpiParams {
   int ncls;
   int add_prev;         // 1: add the current content of out (pooled projection)
   void* silu_out;       // SiLU(c) in the GEMM operand dtype
-  // patch embedding position term
-  int pe, gh, gw;
+  // patch embedding position term: table [T, ldo] of the 2-D sin-cos embedding
+  const float* pe_tab;
 };
 
 // ---------------------------------------------------------------------------
 // Launchers (each returns hipGetLastError() after the launch).
 hipError_t launch_timestep_embed(const float* t, int rows, int src_rows, int dim, float* e,
                                  hipStream_t s);
+// Same sinusoid rounded to bf16 (operand of the bf16 timestep MLP).
+hipError_t launch_timestep_embed_bf16(const float* t, int rows, int src_rows, int dim, bf16_t* e,
+                                      hipStream_t s);
+// pe[tau, n] = 2-D sin-cos position embedding of token tau of a gh x gw grid, d wide.
+hipError_t launch_pos_embed_table(int gh, int gw, int d, float* pe, hipStream_t s);
+// c[m, :] += table[label(m), :] (+ pooled[m, :]); sc = SiLU(c) in dtype.  label(m) is
+// the null label ncls for m >= null_from, else labels[m % label_rows]; a label
+// outside [0, ncls] makes the row NaN.
+hipError_t launch_cond_finish(float* c, int rows, int d, const float* table, const int32_t* labels,
+                              int label_rows, int null_from, int ncls, const float* pooled,
+                              void* sc, int dtype, hipStream_t s);
 hipError_t launch_patchify(const void* x, int B, const PatchGeom& g, int dtype, void* P,
                            hipStream_t s);
 hipError_t launch_unpatchify(const float* Y, int Bout, int Bh_offset, const PatchGeom& g,

@@ -1,12 +1,15 @@
-// Timestep sinusoid, standalone patchify, and unpatchify fused with the
-// classifier-free-guidance combine.
+// Timestep sinusoid, position-embedding table, conditioning-vector finish,
+// standalone patchify, and unpatchify fused with the classifier-free-guidance
+// combine.
 #include "common.h"
+#include "epilogue.h"
 
 // e[b, k] = cos(t f_k) (k < dim/2), sin(t f_{k - dim/2}) (k >= dim/2),
 // f_k = 10000^(-k/(dim/2)).  Arguments are formed and reduced in fp64 (t can be
 // 999, so an fp32 angle would lose ~1e-4 rad); the table is B x dim, tiny.
+template <typename OT>
 __global__ void timestep_embed_kernel(const float* __restrict__ t, int rows, int src_rows,
-                                      int dim, float* __restrict__ e) {
+                                      int dim, OT* __restrict__ e) {
   int idx = blockIdx.x * blockDim.x + threadIdx.x;
   int half = dim >> 1;
   if (idx >= rows * dim) return;
@@ -14,13 +17,68 @@ __global__ void timestep_embed_kernel(const float* __restrict__ t, int rows, int
   int kf = k < half ? k : k - half;
   double f = exp(-9.210340371976184 * (double)kf / (double)half);  // ln(10000)
   double a = (double)t[b % src_rows] * f;
-  e[idx] = (float)(k < half ? cos(a) : sin(a));
+  e[idx] = from_f<OT>((float)(k < half ? cos(a) : sin(a)));
 }
 
 hipError_t launch_timestep_embed(const float* t, int rows, int src_rows, int dim, float* e,
                                  hipStream_t s) {
   int n = rows * dim;
-  timestep_embed_kernel<<<(n + 255) / 256, 256, 0, s>>>(t, rows, src_rows, dim, e);
+  timestep_embed_kernel<float><<<(n + 255) / 256, 256, 0, s>>>(t, rows, src_rows, dim, e);
+  return hipGetLastError();
+}
+
+hipError_t launch_timestep_embed_bf16(const float* t, int rows, int src_rows, int dim, bf16_t* e,
+                                      hipStream_t s) {
+  int n = rows * dim;
+  timestep_embed_kernel<bf16_t><<<(n + 255) / 256, 256, 0, s>>>(t, rows, src_rows, dim, e);
+  return hipGetLastError();
+}
+
+// Table of the 2-D sin-cos position embedding, pe[tau, n] for tau = i * gw + j.
+__global__ void pos_embed_table_kernel(int gh, int gw, int d, float* __restrict__ pe) {
+  int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= gh * gw * d) return;
+  int tau = idx / d, n = idx - tau * d;
+  int i = tau / gw, j = tau - i * gw;
+  pe[idx] = pos_embed_2d(i, j, n, d);
+}
+
+hipError_t launch_pos_embed_table(int gh, int gw, int d, float* pe, hipStream_t s) {
+  int n = gh * gw * d;
+  pos_embed_table_kernel<<<(n + 255) / 256, 256, 0, s>>>(gh, gw, d, pe);
+  return hipGetLastError();
+}
+
+// Conditioning vector: c += class row (+ pooled projection); sc = SiLU(c).
+template <typename DT>
+__global__ void cond_finish_kernel(float* __restrict__ c, int rows, int d,
+                                   const float* __restrict__ table, const int32_t* __restrict__ labels,
+                                   int label_rows, int null_from, int ncls,
+                                   const float* __restrict__ pooled, DT* __restrict__ sc) {
+  int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * d) return;
+  int m = idx / d, n = idx - m * d;
+  float v = c[idx];
+  if (pooled) v += pooled[idx];
+  if (table) {
+    int lbl = (m >= null_from) ? ncls : labels[m % label_rows];
+    if (lbl < 0 || lbl > ncls) v = __builtin_nanf("");
+    else v += table[(int64_t)lbl * d + n];
+  }
+  c[idx] = v;
+  sc[idx] = from_f<DT>(silu_f(v));
+}
+
+hipError_t launch_cond_finish(float* c, int rows, int d, const float* table, const int32_t* labels,
+                              int label_rows, int null_from, int ncls, const float* pooled,
+                              void* sc, int dtype, hipStream_t s) {
+  int n = rows * d;
+  if (dtype == 1)
+    cond_finish_kernel<bf16_t><<<(n + 255) / 256, 256, 0, s>>>(
+        c, rows, d, table, labels, label_rows, null_from, ncls, pooled, (bf16_t*)sc);
+  else
+    cond_finish_kernel<float><<<(n + 255) / 256, 256, 0, s>>>(
+        c, rows, d, table, labels, label_rows, null_from, ncls, pooled, (float*)sc);
   return hipGetLastError();
 }
 

@@ -45,11 +45,9 @@ __device__ __forceinline__ void epi_apply(const EpiParams& ep, int m, int n, flo
   } else if constexpr (EPI == EPI_GELU) {
     ((DT*)ep.out)[(int64_t)m * ep.ldo + n] = from_f<DT>(gelu_tanh_f(v));
   } else if constexpr (EPI == EPI_PATCH) {
-    if (ep.pe) {
-      int tau = m % ep.T;
-      int i = tau / ep.gw, j = tau - i * ep.gw;
-      v += pos_embed_2d(i, j, n, ep.ldo);
-    }
+    if (ep.pe_tab) v += ep.pe_tab[(int64_t)(m % ep.T) * ep.ldo + n];
     ((float*)ep.out)[(int64_t)m * ep.ldo + n] = v;
+  } else if constexpr (EPI == EPI_SILU_DT) {
+    ((DT*)ep.out)[(int64_t)m * ep.ldo + n] = from_f<DT>(silu_f(v));
   }
 }

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
   constexpr int NMF = TM * TN;                   // MFMAs per step
   constexpr int ROWB = BK * 2;                   // LDS row bytes
   constexpr int A_BYTES = BM * ROWB, STAGE_BYTES = (BM + BN) * ROWB;
-  static_assert(NF <= NMF + 1 && (L + NMF - 1) / NMF <= 4, "interleave shape");
+  static_assert((L + NMF - 1) / NMF <= 4, "interleave shape");
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -204,7 +204,14 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
         const int i = q / TN, j = q % TN;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[cur][i], frag[cur][TM + j],
                                                             acc[i][j], 0, 0, 0);
-        if (q < NF && nfetch) fetch(nxt, fkt, fkk, q);
+        if (nfetch) {
+          // one fragment per MFMA; a step with more fragments than MFMAs
+          // (a single 32-row block per wave) reads the rest after its last MFMA
+          if (q < NF) fetch(nxt, fkt, fkk, q);
+          if (q == NMF - 1)
+#pragma unroll
+            for (int qq = NMF; qq < NF; ++qq) fetch(nxt, fkt, fkk, qq);
+        }
         if (last && DMA) {
           constexpr int PER = (L + NMF - 1) / NMF;
 #pragma unroll
@@ -296,6 +303,9 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
             if constexpr (EPI == EPI_GELU) {
               v0 = gelu_tanh_f(v0);
               v1 = gelu_tanh_f(v1);
+            } else if constexpr (EPI == EPI_SILU_DT) {
+              v0 = silu_f(v0);
+              v1 = silu_f(v1);
             } else {
               static_assert(EPI == EPI_BIAS_DT, "epilogue");
             }
@@ -329,6 +339,8 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
           ((bf16_t*)ep.out)[o] = f2bf(v);
         } else if constexpr (EPI == EPI_GELU) {
           ((bf16_t*)ep.out)[o] = f2bf(gelu_tanh_f(v));
+        } else if constexpr (EPI == EPI_SILU_DT) {
+          ((bf16_t*)ep.out)[o] = f2bf(silu_f(v));
         } else {
           static_assert(EPI == EPI_GATED, "epilogue");
           const float g = ep.mod[(int64_t)(m / ep.T) * ep.mod_stride + ep.gate_off + n];
@@ -356,7 +368,12 @@ template <int EPI>
 hipError_t pick(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
                 const EpiParams& ep, hipStream_t s) {
   // 128x192 tiles, 64-wide K slices, two LDS buffers (80 KB): two workgroups
-  // per CU.
+  // per CU.  At most 64 rows (the per-row conditioning products) take 64-row
+  // tiles, so no MFMA work or LDS traffic goes to padding rows.
+  if (M <= 64) {
+    if (N % 192 == 0) return run<EPI, 64, 192, 64, 2>(A, lda, W, M, N, K, ep, s);
+    return run<EPI, 64, 128, 64, 2>(A, lda, W, M, N, K, ep, s);
+  }
   if (N % 192 == 0) return run<EPI, 128, 192, 64, 2>(A, lda, W, M, N, K, ep, s);
   return run<EPI, 128, 128, 64, 2>(A, lda, W, M, N, K, ep, s);
 }
@@ -372,6 +389,7 @@ hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, 
     case EPI_BIAS_DT: return pick<EPI_BIAS_DT>(A, lda, W, M, N, K, ep, s);
     case EPI_GATED: return pick<EPI_GATED>(A, lda, W, M, N, K, ep, s);
     case EPI_GELU: return pick<EPI_GELU>(A, lda, W, M, N, K, ep, s);
+    case EPI_SILU_DT: return pick<EPI_SILU_DT>(A, lda, W, M, N, K, ep, s);
   }
   return hipErrorInvalidValue;
 }

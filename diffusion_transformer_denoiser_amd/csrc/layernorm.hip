@@ -5,49 +5,57 @@
 #define DIT_LOG2_1E4 13.287712379549449f
 
 // H[m, :] = LN(X[m, :]) * (1 + scale[b, :]) + shift[b, :],  b = m / T.
-// One wave per row; each lane holds NV float2 (d = 128 NV), so the row is read
-// from HBM once and both moments come from registers.
-template <int NV, typename DT>
+// One wave per R consecutive rows; each lane holds NV float2 of every row
+// (d = 128 NV), so a row is read from HBM once and both moments come from
+// registers.  The loads of all R rows are issued before the first reduction,
+// which keeps R rows of memory traffic in flight per wave.
+template <int NV, typename DT, int R>
 __global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restrict__ X, int M,
                                                           int T, const float* __restrict__ mod,
                                                           int mod_stride, int shift_off,
                                                           int scale_off, float eps,
                                                           DT* __restrict__ H) {
   constexpr int D = 128 * NV;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
   const int lane = threadIdx.x & 63;
-  if (row >= M) return;
-  const float2* x2 = (const float2*)(X + (int64_t)row * D);
-  float2 v[NV];
-  float s = 0.0f;
+  if (row0 >= M) return;
+  float2 v[R][NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    v[i] = x2[lane + 64 * i];
-    s += v[i].x + v[i].y;
+  for (int r = 0; r < R; ++r) {
+    const float2* x2 = (const float2*)(X + (int64_t)min(row0 + r, M - 1) * D);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[r][i] = x2[lane + 64 * i];
   }
-  const float mean = wave_sum(s) * (1.0f / D);
-  float q = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    float a = v[i].x - mean, b = v[i].y - mean;
-    q += a * a + b * b;
-  }
-  const float var = wave_sum(q) * (1.0f / D);
-  const float rstd = 1.0f / sqrtf(var + eps);
-  const int b = row / T;
-  const float2* sh = (const float2*)(mod + (int64_t)b * mod_stride + shift_off);
-  const float2* sc = (const float2*)(mod + (int64_t)b * mod_stride + scale_off);
+  for (int r = 0; r < R; ++r) {
+    const int row = row0 + r;
+    if (row >= M) break;
+    float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    int c = lane + 64 * i;
-    float2 g = sc[c], t = sh[c];
-    float h0 = (v[i].x - mean) * rstd * (1.0f + g.x) + t.x;
-    float h1 = (v[i].y - mean) * rstd * (1.0f + g.y) + t.y;
-    if constexpr (sizeof(DT) == 2) {
-      uint32_t packed = (uint32_t)f2bf(h0) | ((uint32_t)f2bf(h1) << 16);
-      ((uint32_t*)(H + (int64_t)row * D))[c] = packed;
-    } else {
-      ((float2*)(H + (int64_t)row * D))[c] = make_float2(h0, h1);
+    for (int i = 0; i < NV; ++i) s += v[r][i].x + v[r][i].y;
+    const float mean = wave_sum(s) * (1.0f / D);
+    float q = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      float a = v[r][i].x - mean, b = v[r][i].y - mean;
+      q += a * a + b * b;
+    }
+    const float var = wave_sum(q) * (1.0f / D);
+    const float rstd = 1.0f / sqrtf(var + eps);
+    const int b = row / T;
+    const float2* sh = (const float2*)(mod + (int64_t)b * mod_stride + shift_off);
+    const float2* sc = (const float2*)(mod + (int64_t)b * mod_stride + scale_off);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int c = lane + 64 * i;
+      float2 g = sc[c], t = sh[c];
+      float h0 = (v[r][i].x - mean) * rstd * (1.0f + g.x) + t.x;
+      float h1 = (v[r][i].y - mean) * rstd * (1.0f + g.y) + t.y;
+      if constexpr (sizeof(DT) == 2) {
+        ((uint32_t*)(H + (int64_t)row * D))[c] = f2bf2(h0, h1);
+      } else {
+        ((float2*)(H + (int64_t)row * D))[c] = make_float2(h0, h1);
+      }
     }
   }
 }
@@ -56,11 +64,12 @@ template <typename DT>
 static hipError_t ln_dispatch(const float* X, int M, int T, int d, const float* mod,
                               int mod_stride, int shift_off, int scale_off, float eps, DT* H,
                               hipStream_t s) {
-  dim3 grid((M + 3) / 4);
+  constexpr int R = 2;
+  dim3 grid((M + 4 * R - 1) / (4 * R));
 #define DIT_LN_CASE(NV)                                                                      \
   case NV:                                                                                   \
-    ln_modulate_kernel<NV, DT><<<grid, 256, 0, s>>>(X, M, T, mod, mod_stride, shift_off,    \
-                                                    scale_off, eps, H);                     \
+    ln_modulate_kernel<NV, DT, R><<<grid, 256, 0, s>>>(X, M, T, mod, mod_stride, shift_off, \
+                                                       scale_off, eps, H);                  \
     break;
   switch (d / 128) {
     DIT_LN_CASE(1) DIT_LN_CASE(2) DIT_LN_CASE(3) DIT_LN_CASE(4) DIT_LN_CASE(5) DIT_LN_CASE(6)
