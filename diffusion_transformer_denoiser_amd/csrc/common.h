@@ -34,7 +34,8 @@ __device__ __forceinline__ float silu_f(float z) {
 // evaluated through the identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)).
 __device__ __forceinline__ float gelu_tanh_f(float z) {
   const float k2 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
-  float u2 = k2 * (z + 0.044715f * z * z * z);                          // -2u log2(e)
+  const float k3 = k2 * 0.044715f;
+  const float u2 = z * fmaf(z * z, k3, k2);                             // -2u log2(e)
   return z * fast_rcp(1.0f + fast_exp2(u2));
 }
 

@@ -286,11 +286,12 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
       return;
     }
   } else {
-    // bf16 outputs: neighbouring lanes (columns 2c, 2c+1) trade one value of
-    // each pair of adjacent rows, so every lane stores two adjacent columns
-    // of one row as a 4-byte word.
+    // bf16 outputs: each lane packs rows r, r+1 of its column; neighbouring
+    // lanes (columns 2c, 2c+1) exchange those words (one DPP move) and each
+    // keeps one row of the column pair, stored as a 4-byte word.
     if (full && vec) {
       const bool odd = lane & 1;
+      const uint32_t sel = odd ? 0x03020706u : 0x05040100u;   // (q.hi, p.hi) : (p.lo, q.lo)
       bf16_t* ot = (bf16_t*)ep.out + (int64_t)(mrow + odd) * ep.ldo + (ncol & ~1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -309,12 +310,11 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
             } else {
               static_assert(EPI == EPI_BIAS_DT, "epilogue");
             }
-            // quad_perm [1, 0, 3, 2]: exchange with the neighbouring lane
-            const float send = odd ? v0 : v1;
-            const float recv = __builtin_bit_cast(
-                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF,
-                                                   false));
-            const uint32_t word = odd ? f2bf2(recv, v1) : f2bf2(v0, recv);
+            const uint32_t mine = f2bf2(v0, v1);
+            // quad_perm [1, 0, 3, 2]: the neighbouring lane's word
+            const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xB1, 0xF,
+                                                                         0xF, false);
+            const uint32_t word = __builtin_amdgcn_perm(other, mine, sel);
             *(uint32_t*)(ot + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ep.ldo + j * 32) = word;
           }
       return;

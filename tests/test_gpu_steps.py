@@ -78,8 +78,10 @@ def test_timestep_embedding():
 
 # --- linear layers (bf16 MFMA, fp32 VALU) ------------------------------------------------
 
+# M <= 64 takes 64-row tiles (one 32-row block per wave); (17, 192, 256) is a
+# single ragged tile of that kind.
 LIN_SHAPES = [(64, 128, 64), (300, 200, 128), (257, 1152, 1152), (1024, 4608, 1152),
-              (512, 1152, 4608), (64, 3456, 1152), (33, 96, 320)]
+              (512, 1152, 4608), (64, 3456, 1152), (33, 96, 320), (17, 192, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", LIN_SHAPES)
