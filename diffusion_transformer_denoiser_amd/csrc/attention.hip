@@ -1,7 +1,7 @@
 // Multi-head attention core O = softmax(Q K^T / sqrt(dh)) V, flash style:
 // keys are streamed in tiles with an online softmax, so memory is O(T).
 //
-// bf16 path (MFMA, dh in {64, 72}).  A workgroup of 4 waves owns 128 queries of
+// bf16 path (MFMA, dh in {64, 72}).  A workgroup of NWV waves owns 32 NWV queries of
 // one (batch, head); each wave 32 queries.  Per 64-key tile, staged in LDS:
 //   S^T[key, q] = K Q^T  with v_mfma_f32_16x16x32_bf16 (dh 64..71 of dh = 72 by
 //                        a third 16x16x32 step whose lanes past dh 72 hold zeros,
@@ -28,8 +28,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 namespace {
 
-template <int DH>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restrict__ QKV,
+template <int DH, int NWV>
+__global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16_t* __restrict__ QKV,
                                                            bf16_t* __restrict__ O, int H, int T,
                                                            float sl2) {
   constexpr int KV = 64;                  // keys per tile
@@ -38,9 +38,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
   constexpr int NDB = (DH + 15) / 16;     // 16-row blocks of the O^T accumulator
   constexpr bool TAIL = (DH % 32) != 0;   // dh = 72: columns 64..71
   constexpr int KCH = KV * DH / 8;        // 16-byte chunks of a K tile
-  constexpr int KPT = (KCH + 255) / 256;  // ... per thread
+  constexpr int NTH = 64 * NWV;           // threads of the workgroup
+  constexpr int QPB = 32 * NWV;           // queries per workgroup
+  constexpr int KPT = (KCH + NTH - 1) / NTH;  // ... per thread
   constexpr int VB = (KV / 4) * (DH / 4); // 4x4 (key x feature) items of a V tile
-  constexpr int VPT = (VB + 255) / 256;   // ... per thread
+  constexpr int VPT = (VB + NTH - 1) / NTH;   // ... per thread
   constexpr float RESCALE_SLACK = 8.0f;   // log2 headroom before the running max is raised
   static_assert(DH == 64 || DH == 72, "head dim");
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][KV * KLD];
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
   if ((nwg & 7) == 0) lin = (lin & 7) * (nwg >> 3) + (lin >> 3);
   const int bh = lin / gridDim.x;
   const int b = bh / H, h = bh - b * H;
-  const int q0 = (lin - bh * gridDim.x) * 128 + wave * 32;
+  const int q0 = (lin - bh * gridDim.x) * QPB + wave * 32;
   const int64_t ld = 3LL * H * DH;                       // packed row stride
   const bf16_t* Qb = QKV + (int64_t)b * T * ld + h * DH;   // + t * ld
   const bf16_t* Kb = Qb + (int64_t)H * DH;
@@ -92,13 +94,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
   int koff[KPT], voff[VPT];
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
-    const int idx = min(tid + u * 256, KCH - 1);
+    const int idx = min(tid + u * NTH, KCH - 1);
     const int row = idx / (DH / 8), col = (idx - row * (DH / 8)) * 8;
     koff[u] = (int)((row * ld + col) * 2);
   }
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
-    const int idx = min(tid + u * 256, VB - 1);
+    const int idx = min(tid + u * NTH, VB - 1);
     const int kb4 = idx / (DH / 4), d4 = (idx - kb4 * (DH / 4)) * 4;
     voff[u] = (int)((4 * kb4 * ld + d4) * 2);
   }
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-      const int idx = tid + u * 256;
+      const int idx = tid + u * NTH;
       if (idx < KCH) {
         const int row = idx / (DH / 8), col = (idx - row * (DH / 8)) * 8;
         *(uint4*)&sK[buf][row * KLD + col] = kreg[u];
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const bf16_t* __restr
     }
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      const int idx = tid + u * 256;
+      const int idx = tid + u * NTH;
       if (idx < VB) {
         const int kb4 = idx / (DH / 4), d4 = (idx - kb4 * (DH / 4)) * 4;
         const uint2* r = vreg[u];
@@ -343,11 +345,14 @@ hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, in
   if (B <= 0 || T <= 0) return hipSuccess;
   if (dtype == 1) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)dh);
-    dim3 grid((T + 127) / 128, B * heads);
+    // 4 waves (128 queries) per workgroup, two workgroups per CU (8 waves of
+    // 256 queries per workgroup measured slower at every length).
+    constexpr int NWV = 4;
+    dim3 grid((T + 32 * NWV - 1) / (32 * NWV), B * heads);
     if (dh == 64)
-      attn_bf16_kernel<64><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o, heads, T, sl2);
+      attn_bf16_kernel<64, NWV><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o, heads, T, sl2);
     else if (dh == 72)
-      attn_bf16_kernel<72><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o, heads, T, sl2);
+      attn_bf16_kernel<72, NWV><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o, heads, T, sl2);
     else
       return hipErrorInvalidValue;
   } else {
