@@ -45,8 +45,14 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
   constexpr int VPT = (VB + NTH - 1) / NTH;   // ... per thread
   constexpr float RESCALE_SLACK = 8.0f;   // log2 headroom before the running max is raised
   static_assert(DH == 64 || DH == 72, "head dim");
+  // dh = 72: K and V tiles are copied into LDS as they are (dense [key][72]
+  // rows) by buffer->LDS loads, and the V^T operand of the P V product is read
+  // with transposing LDS reads.  dh = 64: registers stage the tiles and V is
+  // transposed on the way into LDS.
+  constexpr bool DMA = DH == 72;
+  constexpr int VSZ = DMA ? KV * DH + 16 : DH * VLD;   // + 16: reads past the last row stay inside
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][KV * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[2][DH * VLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[2][VSZ];
   // 16 zero bytes: operand lanes past dh read here instead of taking a branch
   __shared__ __attribute__((aligned(16))) uint4 zslot;
 
@@ -119,6 +125,35 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
         vreg[u][q] = __builtin_bit_cast(
             uint2, __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[u] + t0 + q * ldb, 0, 0));
   };
+  // DMA staging (dh = 72): each tile is 2 x 9 direct global->LDS copies of 64
+  // lanes x 16 bytes (chunk c of a tile is row c / 9, 16-byte column c % 9, at
+  // LDS byte 16 c); copy u of wave w is number w + NWV u.  Rows past T read
+  // row T - 1 instead: finite data whose scores are masked.
+  constexpr int NCP = 2 * KV * DH / 512;
+  constexpr int CPW = (NCP + NWV - 1) / NWV;
+  int drow[CPW], dcol[CPW];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    const int ci = (wave + NWV * u) % (NCP / 2);
+    const int c = ci * 64 + lane;
+    drow[u] = c / (DH / 8);
+    dcol[u] = (c - drow[u] * (DH / 8)) * 8;
+  }
+  auto dma = [&](int kv0, int buf) {
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int ii = wave + NWV * u;                // wave-uniform
+      if (ii < NCP) {
+        const bool isv = ii >= NCP / 2;
+        const int ci = isv ? ii - NCP / 2 : ii;
+        char* dst = (isv ? (char*)sV[buf] : (char*)sK[buf]) + ci * 1024;
+        const bf16_t* src = (isv ? Vb : Kb) + (int64_t)min(kv0 + drow[u], T - 1) * ld + dcol[u];
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      }
+    }
+  };
+
   // K rows as they are; V transposed into sV[dh][key]: vreg[u][q] holds features
   // d4..d4+3 of key 4*kb4+q, column e is (vreg[u][0].e, .., vreg[u][3].e).
   auto sstore = [&](int buf) {
@@ -163,12 +198,25 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
 
   const int ntiles = (T + KV - 1) / KV;
   if (tid == 0) zslot = make_uint4(0, 0, 0, 0);
-  gload(0);
-  sstore(0);
+  if constexpr (DMA) {
+    // Zero both tile buffers once: the pad after each V tile (read only by
+    // operand lanes past dh 72) then holds finite values.
+    for (int i = tid; i < 2 * KV * KLD / 8; i += NTH) ((uint4*)sK)[i] = make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < 2 * VSZ / 8; i += NTH) ((uint4*)sV)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+    dma(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed
+  } else {
+    gload(0);
+    sstore(0);
+  }
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1, kv0 = it * KV;
-    if (it + 1 < ntiles) gload(kv0 + KV);   // next tile in flight during this one
+    if (it + 1 < ntiles) {                   // next tile in flight during this one
+      if constexpr (DMA) dma(kv0 + KV, buf ^ 1);
+      else gload(kv0 + KV);
+    }
 
     // S^T blocks: 4 key blocks x 2 query blocks of 16x16.
     floatx4 s[4][2];
@@ -252,10 +300,27 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
       const int dr = 16 * db + c16;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const bool in = dr < DH;
-        const uint2 lo = *(const uint2*)(in ? &sV[buf][dr * VLD + 32 * j + 4 * g] : (const bf16_t*)&zslot);
-        const uint2 hi = *(const uint2*)(in ? &sV[buf][dr * VLD + 32 * j + 16 + 4 * g] : (const bf16_t*)&zslot);
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        bf16x8_t vf;
+        if constexpr (DMA) {
+          // Transposing reads: lane s of 16-lane group g points at
+          // V[key 32 j + 4 g + s / 4 (+16)][dh 16 db + 4 (s % 4)]; lane s then
+          // holds dh 16 db + s of keys 32 j + 4 g .. +3 (and 16 + those).
+          // Lanes past dh 72 read neighbouring finite data that only reaches
+          // O^T rows past dh, which are never stored.
+          typedef short v4i16 __attribute__((ext_vector_type(4)));
+          const bf16_t* vb = &sV[buf][(32 * j + 4 * g + (c16 >> 2)) * DH + 16 * db + 4 * (c16 & 3)];
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)vb);
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(vb + 16 * DH));
+          vf = __builtin_bit_cast(bf16x8_t, (__attribute__((ext_vector_type(8))) short){
+                                                lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        } else {
+          const bool in = dr < DH;
+          const uint2 lo = *(const uint2*)(in ? &sV[buf][dr * VLD + 32 * j + 4 * g] : (const bf16_t*)&zslot);
+          const uint2 hi = *(const uint2*)(in ? &sV[buf][dr * VLD + 32 * j + 16 + 4 * g] : (const bf16_t*)&zslot);
+          vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb][j], oacc[db][qb], 0, 0, 0);
@@ -264,7 +329,11 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
 
     // Stage the prefetched tile into the other buffer (last read in iteration it-1,
     // which every wave finished before the previous barrier).
-    if (it + 1 < ntiles) sstore(buf ^ 1);
+    if constexpr (DMA) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the next tile's copies have landed
+    } else {
+      if (it + 1 < ntiles) sstore(buf ^ 1);
+    }
     __syncthreads();
   }
 
