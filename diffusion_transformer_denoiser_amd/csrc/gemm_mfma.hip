@@ -88,8 +88,10 @@ __device__ __forceinline__ int row_key(int r) {
 }
 
 // vec: the output is 4-byte aligned with an even row stride (bf16 column pairs
-// may be stored as words).
-template <int EPI, int BM, int BN, int BK, int MINWG, int SWZ, int ILV>
+// may be stored as words).  BUF: the copies address A and W through buffer
+// descriptors (scalar base + 32-bit lane offset), which takes less of the
+// address unit than 64-bit lane addresses; needs both operands under 2 GiB.
+template <int EPI, int BM, int BN, int BK, int MINWG, int SWZ, int ILV, int BUF>
 __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __restrict__ A, int lda,
                                                                 const bf16_t* __restrict__ W, int M,
                                                                 int N, int K, EpiParams ep, int vec) {
@@ -141,10 +143,29 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
     src[c] = is_a ? A + (int64_t)min(m0 + r, M - 1) * lda + ch * 8
                   : W + (int64_t)min(n0 + r, N - 1) * K + ch * 8;
   }
+  int boff[L];
+#pragma unroll
+  for (int c = 0; c < L; ++c)
+    boff[c] = (int)((const char*)src[c] - (c < NA ? (const char*)A : (const char*)W));
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)A, (short)0, (int)(((int64_t)(M - 1) * lda + K) * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)((int64_t)N * K * 2), 0x00020000);
   auto copy = [&](int kt, int c) {
     char* st = smem + (kt & 1) * STAGE_BYTES +
                (c < NA ? (w * NA + c) * 1024 : A_BYTES + (w * NB + c - NA) * 1024);
-    __builtin_amdgcn_global_load_lds((const void*)(src[c] + kt * BK), (lds_void*)st, 16, 0, 0);
+    if constexpr (BUF) {
+      // The buffer->LDS builtin exists only for the device; the host pass keeps
+      // just the launch stub of this kernel.
+#if defined(__HIP_DEVICE_COMPILE__)
+      if (c < NA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void*)st, 16, boff[c], kt * BK * 2, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_void*)st, 16, boff[c], kt * BK * 2, 0, 0);
+#endif
+    } else {
+      __builtin_amdgcn_global_load_lds((const void*)(src[c] + kt * BK), (lds_void*)st, 16, 0, 0);
+    }
   };
 
   // LDS byte offsets of this lane's operand rows (fixed over the loop); every
@@ -357,10 +378,18 @@ hipError_t run(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   // bf16 outputs are stored as 4-byte column pairs
   const int vec = ((uintptr_t)ep.out & 3) == 0 && ep.ldo % 2 == 0;
-  if (tiles % 8 == 0)
-    gemm_bf16_kernel<EPI, BM, BN, BK, MINWG, 1, 1><<<tiles, 256, 0, s>>>(A, lda, W, M, N, K, ep, vec);
-  else
-    gemm_bf16_kernel<EPI, BM, BN, BK, MINWG, 0, 1><<<tiles, 256, 0, s>>>(A, lda, W, M, N, K, ep, vec);
+  const bool buf = ((int64_t)(M - 1) * lda + K) * 2 < (1LL << 31) && (int64_t)N * K * 2 < (1LL << 31);
+#define DIT_GEMM_LAUNCH(SWZ, BUF)                                                                 \
+  gemm_bf16_kernel<EPI, BM, BN, BK, MINWG, SWZ, 1, BUF><<<tiles, 256, 0, s>>>(A, lda, W, M, N, K, \
+                                                                           ep, vec)
+  if (tiles % 8 == 0) {
+    if (buf) DIT_GEMM_LAUNCH(1, 1);
+    else DIT_GEMM_LAUNCH(1, 0);
+  } else {
+    if (buf) DIT_GEMM_LAUNCH(0, 1);
+    else DIT_GEMM_LAUNCH(0, 0);
+  }
+#undef DIT_GEMM_LAUNCH
   return hipGetLastError();
 }
 
