@@ -125,6 +125,40 @@ def test_batch_row_independence():
         assert np.array_equal(one[0], full[i])
 
 
+@pytest.mark.parametrize("name", ["dit_s8_f32", "dit_b4_bf16"])
+def test_out_of_range_label_poisons_only_its_row(name):
+    # Labels are not read on the host: a label outside [0, num_classes] makes
+    # that row's conditioning, and so its output, NaN; the other rows are
+    # unaffected (bitwise equal to a run with a valid label there).  The fp32
+    # and bf16 models take different conditioning kernels.
+    cfg = dit_inputs.workload(name, N=2, batch=3)
+    w = dit_inputs.make_weights(cfg)
+    inp = dit_inputs.make_inputs(cfg, batch=3)
+    m = _model(cfg, w)
+    x, t, y, _ = device_inputs(cfg, inp)
+    good = np_(m.forward(x, t, y))
+    for bad in (cfg["num_classes"] + 1, -1):
+        yb = y.clone()
+        yb[1] = bad
+        out = np_(m.forward(x, t, yb))
+        log(f"{name} label {bad}: row 1 all-NaN {np.isnan(out[1]).all()}")
+        assert np.isnan(out[1]).all()
+        assert np.array_equal(out[0], good[0]) and np.array_equal(out[2], good[2])
+
+
+def test_bf16_single_row_matches_oracle():
+    cfg = dit_inputs.workload("dit_b4_bf16", N=3, batch=1)
+    w = dit_inputs.make_weights(cfg)
+    inp = dit_inputs.make_inputs(cfg, batch=1)
+    m = _model(cfg, w)
+    x, t, y, _ = device_inputs(cfg, inp)
+    out = np_(m.forward(x, t, y))
+    ref, _ = oracle_taps(cfg, w, inp)
+    err = rel_l2(out, ref)
+    log(f"bf16 B/4 depth 3, one row: rel-L2 {err:.2e}")
+    assert err <= BF16_TOL
+
+
 # --- teacher-forced blocks --------------------------------------------------------------------
 
 def _block_case(cfg, w, layer, B, rows, gate_bias=None, seed=7):
