@@ -6,11 +6,18 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
 #include "dit.h"
 #include "common.h"
+
+// Independent row groups of a call run on this many streams (the caller's and
+// DIT_SPLIT - 1 of the library's own).
+#ifndef DIT_SPLIT
+#define DIT_SPLIT 2
+#endif
 
 namespace {
 
@@ -48,7 +55,34 @@ struct dit_handle {
   float eps;
   int gf, gh, gw, T, kin, kout, mod_stride;
   PatchGeom gin, gout;
+  // Second stream for the two independent halves of a batch (created on the
+  // first forward, on the device current then), and the fork / join events.
+  // The mutex makes each call's fork-enqueue-join sequence atomic, so calls
+  // from several threads can share them.
+  mutable std::mutex mu;
+  mutable hipStream_t aux[DIT_SPLIT - 1] = {};
+  mutable hipEvent_t ev_fork = nullptr, ev_join[DIT_SPLIT - 1] = {};
+  mutable bool aux_ready = false, aux_failed = false;
 };
+
+namespace {
+// Lazily creates the extra streams (default priority) and the events.
+bool ensure_aux(const dit_handle* h) {
+  if (h->aux_ready) return true;
+  if (h->aux_failed) return false;
+  bool ok_ = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) == hipSuccess;
+  for (int i = 0; ok_ && i < DIT_SPLIT - 1; ++i)
+    ok_ = hipStreamCreateWithFlags(&h->aux[i], hipStreamNonBlocking) == hipSuccess &&
+          hipEventCreateWithFlags(&h->ev_join[i], hipEventDisableTiming) == hipSuccess;
+  if (!ok_) {
+    (void)hipGetLastError();
+    h->aux_failed = true;   // fall back to one stream
+    return false;
+  }
+  h->aux_ready = true;
+  return true;
+}
+}  // namespace
 
 namespace {
 
@@ -264,6 +298,59 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
       DIT_HIP(hipMemcpyAsync(taps->x_embed, X, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s));
   }
 
+  // Blocks and the final layer (LN + modulation (b_f, g_f), linear decoder).
+  // Rows are independent from here on: without taps, the rows split into up
+  // to DIT_SPLIT groups, the first on the caller's stream and the others on
+  // the library's streams, forked and joined with events, so one group's
+  // memory-bound kernels (LN, attention) run beside another group's GEMMs.
+  // Each group uses its own rows of every workspace region.
+  const int fb = 6 * d * h->N;
+  auto blocks_and_final = [&](int r0, int nr, hipStream_t st) -> int {
+    const size_t m0 = (size_t)r0 * T, es = h->es;
+    WsLayout Lh = L;
+    Lh.H += m0 * d * es;
+    Lh.qkv += m0 * 3 * d * es;
+    Lh.o += m0 * d * es;
+    Lh.G += m0 * h->hid * es;
+    float* Xh = X + m0 * d;
+    const float* modh = mod + (size_t)r0 * h->mod_stride;
+    for (int l = 0; l < h->N; ++l) {
+      int rc = run_block(h, l, nr, Xh, modh, h->mod_stride, 6 * d * l, ws, Lh, nullptr, nullptr, st);
+      if (rc) return rc;
+    }
+    const int Mh = nr * T;
+    void* Hh = at<void>(ws, Lh.H);
+    DIT_HIP(launch_ln_modulate(Xh, Mh, T, d, modh, h->mod_stride, fb, fb + d, h->eps, Hh, h->dtype,
+                               st));
+    EpiParams ef = epi0();
+    ef.bias = h->w.out_b; ef.out = Y + m0 * h->kout; ef.ldo = h->kout;
+    DIT_HIP(linear(h, EPI_BIAS_F32, Hh, d, h->w.out_w, Mh, h->kout, d, ef, st));
+    return DIT_OK;
+  };
+
+  const int parts = rows < DIT_SPLIT ? rows : DIT_SPLIT;
+  if (!taps && parts >= 2) {
+    std::lock_guard<std::mutex> lock(h->mu);
+    if (ensure_aux(h)) {
+      DIT_HIP(hipEventRecord(h->ev_fork, s));
+      for (int i = 0; i < parts - 1; ++i) DIT_HIP(hipStreamWaitEvent(h->aux[i], h->ev_fork, 0));
+      int rc = DIT_OK;
+      for (int i = 0; i < parts && !rc; ++i) {
+        const int r0 = (int)((int64_t)rows * i / parts), r1 = (int)((int64_t)rows * (i + 1) / parts);
+        rc = blocks_and_final(r0, r1 - r0, i == 0 ? s : h->aux[i - 1]);
+      }
+      // join even after an error, so the caller's stream still orders after
+      // everything that was enqueued on the other streams
+      bool joined = true;
+      for (int i = 0; i < parts - 1; ++i)
+        joined = hipEventRecord(h->ev_join[i], h->aux[i]) == hipSuccess &&
+                 hipStreamWaitEvent(s, h->ev_join[i], 0) == hipSuccess && joined;
+      if (rc) return rc;
+      if (!joined) return fail(DIT_EHIP, "stream join failed");
+      return DIT_OK;
+    }
+  }
+
   for (int l = 0; l < h->N; ++l) {
     int rc = run_block(h, l, rows, X, mod, h->mod_stride, 6 * d * l, ws, L, nullptr, nullptr, s);
     if (rc) return rc;
@@ -271,9 +358,6 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
       DIT_HIP(hipMemcpyAsync(taps->x_blocks + (size_t)l * M * d, X, (size_t)M * d * 4,
                              hipMemcpyDeviceToDevice, s));
   }
-
-  // Final layer: LN + modulation (b_f, g_f), linear decoder.
-  const int fb = 6 * d * h->N;
   DIT_HIP(launch_ln_modulate(X, M, T, d, mod, h->mod_stride, fb, fb + d, h->eps, Hb, h->dtype, s));
   ep = epi0();
   ep.bias = h->w.out_b; ep.out = Y; ep.ldo = h->kout;
@@ -430,7 +514,15 @@ int dit_create(const dit_config* cfg, const dit_weights* w, dit_handle** out) {
   return ok();
 }
 
-void dit_destroy(dit_handle* h) { delete h; }
+void dit_destroy(dit_handle* h) {
+  if (!h) return;
+  for (int i = 0; i < DIT_SPLIT - 1; ++i) {
+    if (h->aux[i]) (void)hipStreamDestroy(h->aux[i]);
+    if (h->ev_join[i]) (void)hipEventDestroy(h->ev_join[i]);
+  }
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  delete h;
+}
 
 int dit_workspace_size(const dit_handle* h, int rows, size_t* bytes) {
   if (!h || !bytes) return fail(DIT_EINVAL, "handle and bytes must be non-NULL");

@@ -34,7 +34,12 @@
  *     device memory and never changes the current device.
  *   - Work is enqueued on the caller's stream (a hipStream_t passed as void*;
  *     NULL is the default stream) and never synchronises it.  A device fault
- *     surfaces at the caller's next synchronisation.
+ *     surfaces at the caller's next synchronisation.  A forward without taps
+ *     runs half of its rows on a second stream the handle owns (created at
+ *     the first forward, default priority, on the device current then),
+ *     forked from and joined back into the caller's stream with events: the
+ *     call is still ordered after earlier and before later work on the
+ *     caller's stream.
  *   - A handle is immutable after dit_create; it may be used from several
  *     threads/streams at once if every call has its own workspace.
  *   - No C++ exception crosses this interface.
