@@ -49,10 +49,10 @@ def parse():
     return ap.parse_args()
 
 
-def measured_traffic(src_rel: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE record (each scaled by the factor a plain copy of known size gave),
-    or None when there is no record or the kernel source changed since."""
+def measured_traffic(src_rel: str, kernel: str, shape):
+    """HBM bytes per launch of `kernel` at `shape` (M, N, K) from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE record (each scaled by the factor a plain copy of known size
+    gave), or None when there is no record for this shape or the kernel source changed."""
     import hashlib
     rec_path = os.path.join(ROOT, "profiles", "gemm_fc1_hbm_counters.json")
     try:
@@ -60,7 +60,8 @@ def measured_traffic(src_rel: str, kernel: str):
         src = open(os.path.join(ROOT, src_rel), "rb").read()
     except OSError:
         return None
-    if rec.get("kernel") != kernel or rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+    if (rec.get("kernel") != kernel or rec.get("shape") != list(shape)
+            or rec.get("source_sha256") != hashlib.sha256(src).hexdigest()):
         return None
     return int(rec["traffic_bytes"])
 
@@ -145,10 +146,11 @@ def main():
     flop_fwd = 2.0 * gmac_row * 1e9 * rows
     tflops = flop_fwd / (ms * 1e-3) / 1e12
 
-    # Dominant kernel: the FFN up-projection (M = rows*T, N = 4d, K = d, bias + tanh-GELU
-    # epilogue), the same MFMA kernel and tile as in the forward pass, timed alone.
+    # Dominant kernel: the FFN up-projection (N = 4d, K = d, bias + tanh-GELU epilogue), the
+    # same MFMA kernel, tile and shape as in the forward pass, timed alone.  The forward runs
+    # the two halves of its rows on two streams, so each launch there covers M = rows/2 * T.
     d, hid = cfg["d"], cfg["mlp_hidden"]
-    M = rows * T
+    M = (rows // 2 if rows >= 2 else rows) * T
     A = torch.randn(M, d, device=dev).to(dt)
     W1 = model.tensors["fc1_w"][0]
     b1 = model.tensors["fc1_b"][0]
@@ -166,12 +168,12 @@ def main():
     kflop = 2.0 * M * hid * d
     k_tflops = kflop / (kms * 1e-3) / 1e12
     traffic = measured_traffic("diffusion_transformer_denoiser_amd/csrc/gemm_mfma.hip",
-                               "gemm_bf16_kernel<5, 128, 192, 64, 2, 1, 1>")
+                               "gemm_bf16_kernel<5, 128, 192, 64, 2, 1, 1, 1>", (M, hid, d))
     roofline = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE)",
                 "algorithmic_bytes": (M * d + hid * d) * 2 + hid * 4 + M * hid * 2,
-                "kernel": f"gemm_bf16_kernel<EPI_GELU,128,192,64> (FFN fc1: M={M}, N={hid}, K={d})",
+                "kernel": f"gemm_bf16_kernel<EPI_GELU,128,192,64> (FFN fc1 of one row half: M={M}, N={hid}, K={d})",
                 "avg_launch_ms": round(kms, 4)}
 
     if args.copy_mib:
