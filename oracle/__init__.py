@@ -32,6 +32,13 @@ Pins (what each function is checked against, in tests/test_oracle_*.py):
                              independence; token-permutation equivariance
   cfg_combine                s=0 / s=1 / affine-in-s / channel-mask cases
   flops.gmac_per_image       the pages' printed Gflops table
+  sampler_oracle             forward process composed step by step (schedule);
+                             Gaussian conditioning of (x_s, x_t | x_0) (reverse
+                             mean and variance); learned-variance endpoints;
+                             closed-form Gaussian-data laws and flow maps
+                             (ancestral chain returns the data law, DDIM and
+                             Euler first order, DPM-Solver++(2M) second
+                             order, point masses hit exactly); DDIM identity
 Full-size forward values: parity unpinned beyond the stage pins above
 (the pages print no output tensors and no trained weights exist).
 """
@@ -42,3 +49,4 @@ from .dit_oracle import (  # noqa: F401
     cfg_combine, token_grid,
 )
 from . import flops  # noqa: F401
+from . import sampler_oracle  # noqa: F401
