@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdit.so")
 DIT_OK, DIT_EINVAL, DIT_EUNSUPPORTED, DIT_EWORKSPACE, DIT_EHIP = 0, -1, -2, -3, -4
 DIT_F32, DIT_BF16 = 0, 1
 DIT_EPI_BIAS, DIT_EPI_GELU, DIT_EPI_GATED = 0, 1, 2
+DIT_SAMPLER_DDPM, DIT_SAMPLER_DPMPP_2M, DIT_SAMPLER_RF_EULER = 0, 1, 2
 
 
 class DitConfig(C.Structure):
@@ -33,6 +34,12 @@ class DitWeights(C.Structure):
 
 class DitTaps(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("c", "mod", "x_embed", "x_blocks", "y_final")]
+
+
+class DitSampler(C.Structure):
+    _fields_ = [("kind", C.c_int), ("num_steps", C.c_int),
+                ("timesteps", C.POINTER(C.c_int32)), ("times", C.POINTER(C.c_double)),
+                ("train_steps", C.c_int), ("beta_start", C.c_double), ("beta_end", C.c_double)]
 
 
 EXPORTS = {
@@ -62,6 +69,16 @@ EXPORTS = {
     "dit_block_forward": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                     C.c_void_p]),
+    "dit_sampler_coefficients": (C.c_int, [C.POINTER(DitSampler), C.c_int,
+                                           C.POINTER(C.c_double), C.POINTER(C.c_double)]),
+    "dit_sampler_step": (C.c_int, [C.POINTER(DitSampler), C.c_int, C.c_void_p, C.c_void_p,
+                                   C.c_int, C.c_int, C.c_int, C.c_int64, C.c_void_p, C.c_void_p,
+                                   C.c_void_p, C.c_void_p]),
+    "dit_sample_workspace_size": (C.c_int, [C.c_void_p, C.POINTER(DitSampler), C.c_int, C.c_int,
+                                            C.POINTER(C.c_size_t)]),
+    "dit_sample": (C.c_int, [C.c_void_p, C.POINTER(DitSampler), C.c_void_p, C.c_void_p,
+                             C.c_void_p, C.c_int, C.c_float, C.c_int, C.c_void_p, C.c_void_p,
+                             C.c_size_t, C.c_void_p]),
 }
 
 _lib = None

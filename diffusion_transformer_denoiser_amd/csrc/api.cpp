@@ -9,6 +9,7 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "dit.h"
 #include "common.h"
@@ -367,16 +368,26 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
   return DIT_OK;
 }
 
-int check_ws(const dit_handle* h, int rows, const void* ws, size_t ws_bytes, WsLayout* L) {
+int check_rows(const dit_handle* h, int rows) {
   if ((int64_t)rows * h->T > (1LL << 30)) return fail(DIT_EINVAL, "rows * T too large");
   if ((int64_t)rows * h->heads > 65535)
     return fail(DIT_EUNSUPPORTED, "rows * heads > 65535 (attention grid limit)");
-  *L = ws_layout(h, rows);
+  return DIT_OK;
+}
+
+int check_ws_bytes(const void* ws, size_t ws_bytes, size_t need) {
   if (!ws) return fail(DIT_EWORKSPACE, "workspace pointer is NULL");
-  if (ws_bytes < L->total)
-    return fail(DIT_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L->total);
+  if (ws_bytes < need)
+    return fail(DIT_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
   if ((uintptr_t)ws & 255) return fail(DIT_EWORKSPACE, "workspace must be 256-byte aligned");
   return DIT_OK;
+}
+
+int check_ws(const dit_handle* h, int rows, const void* ws, size_t ws_bytes, WsLayout* L) {
+  int rc = check_rows(h, rows);
+  if (rc) return rc;
+  *L = ws_layout(h, rows);
+  return check_ws_bytes(ws, ws_bytes, L->total);
 }
 
 int forward_impl(dit_handle* h, const void* x_t, const float* t, const int32_t* y,
@@ -436,6 +447,192 @@ int check_geom(int B, int C, int F, int H, int W, int p, int pt) {
     return fail(DIT_EINVAL, "latent extents (%d, %d, %d) not divisible by patch (%d, %d, %d)", F,
                 H, W, pt, p, p);
   if ((int64_t)B * C * F * H * W > (1LL << 40)) return fail(DIT_EINVAL, "latent too large");
+  return DIT_OK;
+}
+
+
+// ---------------------------------------------------------------------------
+// Sampler schedule (host, fp64).  Sources: the forward process and the learned
+// reverse covariance (cv-learn "Sora / DiT", Method, training objective
+// bullet), the multistep DPM-Solver used for inference (itwiki page, inference
+// with diffusers), the rectified-flow interpolation and velocity target
+// (blog.outta.ai GOKU review, section 2.3).  Readings where the pages stop:
+// beta linear from beta_start to beta_end over train_steps, abar the running
+// product of (1 - beta); kept steps tau_0 > ... > tau_{S-1}, step k going to
+// tau_{k+1} and the last one to the clean latent (abar = 1); learned variance
+// exp(f log beta + (1 - f) log beta_tilde), f = (v + 1) / 2; no x0 clipping.
+
+struct StepCoef {
+  double model_t;
+  double c[8];
+};
+
+int check_sampler(const dit_sampler* sp) {
+  if (!sp) return fail(DIT_EINVAL, "sampler is NULL");
+  const int S = sp->num_steps;
+  if (S < 1 || S > 1000000) return fail(DIT_EINVAL, "num_steps must be in [1, 1e6] (got %d)", S);
+  if (sp->kind == DIT_SAMPLER_DDPM || sp->kind == DIT_SAMPLER_DPMPP_2M) {
+    const int Tn = sp->train_steps;
+    if (Tn < 1 || Tn > 1000000) return fail(DIT_EINVAL, "train_steps must be in [1, 1e6]");
+    if (!(sp->beta_start > 0.0 && sp->beta_start < 1.0 && sp->beta_end > 0.0 &&
+          sp->beta_end < 1.0))
+      return fail(DIT_EINVAL, "betas must lie in (0, 1)");
+    if (sp->timesteps) {
+      for (int k = 0; k < S; ++k) {
+        const int t = sp->timesteps[k];
+        if (t < 0 || t >= Tn) return fail(DIT_EINVAL, "timesteps[%d] = %d outside [0, %d)", k, t, Tn);
+        if (k && t >= sp->timesteps[k - 1])
+          return fail(DIT_EINVAL, "timesteps must be strictly decreasing (index %d)", k);
+      }
+    } else if (S > Tn) {
+      return fail(DIT_EINVAL, "num_steps %d > train_steps %d", S, Tn);
+    }
+  } else if (sp->kind == DIT_SAMPLER_RF_EULER) {
+    if (sp->times) {
+      for (int k = 0; k <= S; ++k) {
+        if (!std::isfinite(sp->times[k])) return fail(DIT_EINVAL, "times[%d] not finite", k);
+        if (k && !(sp->times[k] > sp->times[k - 1]))
+          return fail(DIT_EINVAL, "times must be strictly increasing (index %d)", k);
+      }
+    }
+  } else {
+    return fail(DIT_EINVAL, "unknown sampler kind %d", sp->kind);
+  }
+  return DIT_OK;
+}
+
+// abar_t = prod_{j <= t} (1 - beta_j), beta on a straight line.
+std::vector<double> abar_table(const dit_sampler* sp) {
+  const int Tn = sp->train_steps;
+  std::vector<double> ab(Tn);
+  double prod = 1.0;
+  for (int j = 0; j < Tn; ++j) {
+    const double beta =
+        Tn == 1 ? sp->beta_start
+                : (j == Tn - 1 ? sp->beta_end
+                               : sp->beta_start + j * ((sp->beta_end - sp->beta_start) / (Tn - 1)));
+    prod *= 1.0 - beta;
+    ab[j] = prod;
+  }
+  return ab;
+}
+
+// Kept step k: the given list, or S steps spread evenly over [0, train_steps),
+// rounded half up, largest first.
+int kept_step(const dit_sampler* sp, int k) {
+  if (sp->timesteps) return sp->timesteps[k];
+  const int S = sp->num_steps, Tn = sp->train_steps;
+  if (S == 1) return Tn - 1;
+  const int j = S - 1 - k;
+  return (int)std::floor((double)j * (Tn - 1) / (S - 1) + 0.5);
+}
+
+double flow_time(const dit_sampler* sp, int k) {
+  return sp->times ? sp->times[k] : (double)k / sp->num_steps;
+}
+
+// log(alpha / sigma) of a VP level; +inf at abar = 1.
+double half_log_snr(double ab) {
+  return ab >= 1.0 ? INFINITY : 0.5 * std::log(ab) - 0.5 * std::log1p(-ab);
+}
+
+void step_coef(const dit_sampler* sp, const std::vector<double>& ab, int k, StepCoef* o) {
+  const int S = sp->num_steps;
+  for (double& v : o->c) v = 0.0;
+  if (sp->kind == DIT_SAMPLER_RF_EULER) {
+    o->model_t = flow_time(sp, k);
+    o->c[0] = flow_time(sp, k + 1) - flow_time(sp, k);
+    return;
+  }
+  const int tk = kept_step(sp, k);
+  o->model_t = tk;
+  const double at = ab[tk];
+  const double as = k + 1 < S ? ab[kept_step(sp, k + 1)] : 1.0;
+  if (sp->kind == DIT_SAMPLER_DDPM) {
+    const double beta = 1.0 - at / as;
+    const double c_x0 = beta * std::sqrt(as) / (1.0 - at);
+    const double c_xt = (1.0 - as) * std::sqrt(1.0 - beta) / (1.0 - at);
+    // mean = c_x0 x0 + c_xt x with x0 = (x - sqrt(1 - abar_t) eps) / sqrt(abar_t)
+    o->c[0] = c_x0 / std::sqrt(at) + c_xt;
+    o->c[1] = c_x0 * std::sqrt(1.0 - at) / std::sqrt(at);
+    o->c[2] = std::log(beta);
+    if (as < 1.0) {
+      o->c[3] = std::log(beta * (1.0 - as) / (1.0 - at));
+      o->c[4] = 1.0;
+    } else if (S >= 2) {
+      // last step: beta_tilde is 0 there; take the previous step's (no noise is added)
+      const double a0 = ab[kept_step(sp, S - 2)], a1 = ab[kept_step(sp, S - 1)];
+      const double b1 = 1.0 - a0 / a1;
+      o->c[3] = std::log(b1 * (1.0 - a1) / (1.0 - a0));
+    } else {
+      o->c[3] = o->c[2];
+    }
+    return;
+  }
+  // DPM-Solver++ in data prediction: alpha = sqrt(abar), sigma = sqrt(1 - abar).
+  const double al_t = std::sqrt(at), sg_t = std::sqrt(1.0 - at);
+  o->c[0] = 1.0 / al_t;
+  o->c[1] = sg_t / al_t;
+  if (as >= 1.0) {          // into sigma = 0: x' = x0 (first order)
+    o->c[3] = 1.0;
+    return;
+  }
+  const double al_s = std::sqrt(as), sg_s = std::sqrt(1.0 - as);
+  const double h = half_log_snr(as) - half_log_snr(at);
+  const double b = al_s * -std::expm1(-h);
+  o->c[2] = sg_s / sg_t;
+  if (k >= 1) {
+    const double ap = ab[kept_step(sp, k - 1)];
+    const double r = (half_log_snr(at) - half_log_snr(ap)) / h;
+    o->c[3] = b * (1.0 + 0.5 / r);
+    o->c[4] = b * (-0.5 / r);
+    o->c[5] = 1.0;
+  } else {
+    o->c[3] = b;
+  }
+}
+
+void fill_step_args(SamplerStepArgs* a, int kind, const StepCoef& sc) {
+  a->kind = kind;
+  for (int i = 0; i < 5; ++i) a->k[i] = (float)sc.c[i];
+  if (kind == DIT_SAMPLER_DDPM) {
+    a->add_noise = sc.c[4] != 0.0;
+  } else if (kind == DIT_SAMPLER_DPMPP_2M) {
+    a->has_prev = sc.c[5] != 0.0;
+  }
+}
+
+struct SampleLayout {
+  WsLayout L;
+  size_t tvec, xm, hist, total;
+};
+
+SampleLayout sample_layout(const dit_handle* h, int kind, int B, int rows) {
+  SampleLayout S;
+  S.L = ws_layout(h, rows);
+  size_t off = S.L.total;
+  const size_t n = (size_t)B * h->cfg.in_channels * h->gin.F * h->gin.H * h->gin.W;
+  S.tvec = off; off += align256((size_t)B * 4);
+  S.xm = off; off += align256(h->dtype == DIT_BF16 ? n * 2 : 0);
+  S.hist = off; off += align256(kind == DIT_SAMPLER_DPMPP_2M ? n * 4 : 0);
+  S.total = off;
+  return S;
+}
+
+int check_sample_model(int C, int Cout) {
+  if (Cout != C && Cout != 2 * C)
+    return fail(DIT_EUNSUPPORTED, "sampler needs Cout == C or 2C (got C = %d, Cout = %d)", C, Cout);
+  return DIT_OK;
+}
+int sample_rows(const dit_handle* h, int B, int guided, int* rows) {
+  if (B <= 0 || B > (1 << 29)) return fail(DIT_EINVAL, "B must be positive (got %d)", B);
+  if (guided < 0 || guided > h->cfg.out_channels)
+    return fail(DIT_EINVAL, "guided_channels must be in [0, %d]", h->cfg.out_channels);
+  if (guided > 0) {
+    if (h->ncls <= 0) return fail(DIT_EINVAL, "guidance needs a class table with a null label");
+    if (h->cond_dim > 0) return fail(DIT_EUNSUPPORTED, "guidance with pooled conditioning");
+  }
+  *rows = guided > 0 ? 2 * B : B;
   return DIT_OK;
 }
 
@@ -641,6 +838,132 @@ int dit_block_forward(dit_handle* h, int layer, int B, const float* X_in, const 
     DIT_HIP(hipMemcpyAsync(X_out, X_in, (size_t)B * h->T * h->d * 4, hipMemcpyDeviceToDevice, s));
   rc = run_block(h, layer, B, X_out, mod, 6 * h->d, 0, ws, L, o_branch, f_branch, s);
   if (rc) return rc;
+  return ok();
+}
+
+
+int dit_sampler_coefficients(const dit_sampler* sp, int k, double* model_t, double coef[8]) {
+  int rc = check_sampler(sp);
+  if (rc) return rc;
+  if (k < 0 || k >= sp->num_steps) return fail(DIT_EINVAL, "step %d outside [0, %d)", k, sp->num_steps);
+  if (!model_t || !coef) return fail(DIT_EINVAL, "model_t and coef must be non-NULL");
+  std::vector<double> ab;
+  if (sp->kind != DIT_SAMPLER_RF_EULER) ab = abar_table(sp);
+  StepCoef sc;
+  step_coef(sp, ab, k, &sc);
+  *model_t = sc.model_t;
+  for (int i = 0; i < 8; ++i) coef[i] = sc.c[i];
+  return ok();
+}
+
+int dit_sampler_step(const dit_sampler* sp, int k, const float* x, const float* model_out, int B,
+                     int C, int Cout, int64_t spatial, const float* z, float* x0_hist,
+                     float* x_out, void* stream) {
+  int rc = check_sampler(sp);
+  if (rc) return rc;
+  if (k < 0 || k >= sp->num_steps) return fail(DIT_EINVAL, "step %d outside [0, %d)", k, sp->num_steps);
+  if (!x || !model_out || !x_out) return fail(DIT_EINVAL, "x, model_out and x_out must be non-NULL");
+  if (B <= 0 || C <= 0 || spatial <= 0) return fail(DIT_EINVAL, "B, C and spatial must be positive");
+  rc = check_sample_model(C, Cout);
+  if (rc) return rc;
+  const int64_t n = (int64_t)B * C * spatial;
+  if (n > (1LL << 38)) return fail(DIT_EINVAL, "state too large");
+  std::vector<double> ab;
+  if (sp->kind != DIT_SAMPLER_RF_EULER) ab = abar_table(sp);
+  StepCoef sc;
+  step_coef(sp, ab, k, &sc);
+  SamplerStepArgs a;
+  memset(&a, 0, sizeof a);
+  fill_step_args(&a, sp->kind, sc);
+  if (a.add_noise && !z) return fail(DIT_EINVAL, "this DDPM step needs noise z");
+  if (sp->kind == DIT_SAMPLER_DPMPP_2M && !x0_hist)
+    return fail(DIT_EINVAL, "DPM-Solver++ needs the x0 history buffer");
+  a.x = x; a.x_out = x_out; a.mo = model_out; a.z = z;
+  a.hist = sp->kind == DIT_SAMPLER_DPMPP_2M ? x0_hist : nullptr;
+  a.n = n; a.S = spatial; a.C = C; a.Cout = Cout;
+  a.learned = Cout == 2 * C;
+  DIT_HIP(launch_sampler_step(a, (hipStream_t)stream));
+  return ok();
+}
+
+
+int dit_sample_workspace_size(const dit_handle* h, const dit_sampler* sp, int B,
+                              int guided_channels, size_t* bytes) {
+  if (!h || !bytes) return fail(DIT_EINVAL, "handle and bytes must be non-NULL");
+  int rc = check_sampler(sp);
+  if (rc) return rc;
+  int rows;
+  rc = sample_rows(h, B, guided_channels, &rows);
+  if (rc) return rc;
+  rc = check_rows(h, rows);
+  if (rc) return rc;
+  *bytes = sample_layout(h, sp->kind, B, rows).total;
+  return ok();
+}
+
+int dit_sample(dit_handle* h, const dit_sampler* sp, float* x, const int32_t* y,
+               const float* pooled, int B, float scale, int guided_channels, const float* noise,
+               void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return fail(DIT_EINVAL, "handle is NULL");
+  int rc = check_sampler(sp);
+  if (rc) return rc;
+  if (!x) return fail(DIT_EINVAL, "x must be non-NULL");
+  const int C = h->cfg.in_channels, Cout = h->cfg.out_channels, S = sp->num_steps;
+  rc = check_sample_model(C, Cout);
+  if (rc) return rc;
+  int rows;
+  rc = sample_rows(h, B, guided_channels, &rows);
+  if (rc) return rc;
+  if (h->ncls > 0 && !y) return fail(DIT_EINVAL, "class labels y are required");
+  if (guided_channels == 0 && h->cond_dim > 0 && !pooled)
+    return fail(DIT_EINVAL, "pooled conditioning is required");
+  if (guided_channels > 0 && !std::isfinite(scale))
+    return fail(DIT_EINVAL, "guidance scale must be finite");
+  if (sp->kind == DIT_SAMPLER_DDPM && S >= 2 && !noise)
+    return fail(DIT_EINVAL, "DDPM sampling needs noise [S, B, C, F, H, W]");
+  rc = check_rows(h, rows);
+  if (rc) return rc;
+  const SampleLayout SL = sample_layout(h, sp->kind, B, rows);
+  rc = check_ws_bytes(ws, ws_bytes, SL.total);
+  if (rc) return rc;
+  const WsLayout& L = SL.L;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t n = (int64_t)B * C * h->gin.F * h->gin.H * h->gin.W;
+  std::vector<double> ab;
+  if (sp->kind != DIT_SAMPLER_RF_EULER) ab = abar_table(sp);
+  std::vector<StepCoef> co(S);
+  for (int k = 0; k < S; ++k) step_coef(sp, ab, k, &co[k]);
+
+  float* tvec = at<float>(ws, SL.tvec);
+  bf16_t* xm = h->dtype == DIT_BF16 ? at<bf16_t>(ws, SL.xm) : nullptr;
+  float* hist = sp->kind == DIT_SAMPLER_DPMPP_2M ? at<float>(ws, SL.hist) : nullptr;
+  DIT_HIP(launch_sampler_prologue(x, n, xm, tvec, B, (float)co[0].model_t, s));
+  const void* x_in = xm ? (const void*)xm : (const void*)x;
+  for (int k = 0; k < S; ++k) {
+    if (guided_channels > 0)
+      rc = run_trunk(h, x_in, tvec, y, nullptr, rows, B, B, ws, L, nullptr, s);
+    else
+      rc = run_trunk(h, x_in, tvec, y, pooled, B, B, B, ws, L, nullptr, s);
+    if (rc) return rc;
+    SamplerStepArgs a;
+    memset(&a, 0, sizeof a);
+    fill_step_args(&a, sp->kind, co[k]);
+    const bool more = k + 1 < S;
+    a.from_y = 1;
+    a.x = x; a.x_out = x;
+    a.x_model = more ? xm : nullptr;
+    a.mo = at<float>(ws, L.Y);
+    a.z = a.add_noise ? noise + (size_t)k * n : nullptr;
+    a.hist = hist;
+    a.tvec = more ? tvec : nullptr;
+    a.tvec_rows = more ? B : 0;
+    a.t_next = more ? (float)co[k + 1].model_t : 0.0f;
+    a.n = n; a.S = (int64_t)h->gin.F * h->gin.H * h->gin.W;
+    a.C = C; a.Cout = Cout; a.g = h->gout;
+    a.null_off = B; a.guided = guided_channels; a.scale = scale;
+    a.learned = Cout == 2 * C;
+    DIT_HIP(launch_sampler_step(a, s));
+  }
   return ok();
 }
 

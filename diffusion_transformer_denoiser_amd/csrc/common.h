@@ -142,3 +142,39 @@ hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, in
                             hipStream_t s);
 
 static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// ---------------------------------------------------------------------------
+// Sampler update (sampler.hip).  kind 0: DDPM ancestral step
+//   x' = k0 x - k1 eps [+ exp(0.5 lv) z],  lv = fr k2 + (1 - fr) k3,
+//   fr = (v + 1) / 2 from the covariance channel C + c when `learned`, else lv = k3;
+// kind 1: DPM-Solver++ step  x0 = k0 x - k1 eps,  x' = k2 x + k3 x0 [+ k4 hist],
+//   hist <- x0;
+// kind 2: rectified-flow Euler  x' = x + k0 v.
+// The prediction comes from `mo` as [B, Cout, S] (from_y == 0) or from the
+// decoder output [rows, T, Kout] (from_y == 1) with the guidance combine of
+// rows b and b + null_off on channels < guided.
+struct SamplerStepArgs {
+  int kind;
+  int from_y;
+  const float* x;       // [B, C, S] state
+  float* x_out;         // [B, C, S] (may alias x)
+  void* x_model;        // bf16 copy of x_out, or null
+  const float* mo;      // prediction
+  const float* z;       // [B, C, S] noise (kind 0 with add_noise)
+  float* hist;          // [B, C, S] x0 history (kind 1), or null
+  float* tvec;          // tvec[0..tvec_rows) = t_next (next model time), or null
+  int tvec_rows;
+  float t_next;
+  int64_t n;            // B * C * S
+  int64_t S;            // F * H * W
+  int C, Cout;
+  PatchGeom g;          // decoder geometry (from_y)
+  int null_off, guided;
+  float scale;
+  int add_noise, learned, has_prev;
+  float k[5];
+};
+hipError_t launch_sampler_step(const SamplerStepArgs& a, hipStream_t s);
+// x_model = bf16(x) over n elements (skipped when x_model is null); tvec[0..rows) = t.
+hipError_t launch_sampler_prologue(const float* x, int64_t n, bf16_t* x_model, float* tvec,
+                                   int rows, float t, hipStream_t s);

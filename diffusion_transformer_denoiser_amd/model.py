@@ -4,6 +4,7 @@ every step of the forward pass runs in the HIP library.
     model = DiT(cfg, weights)          # uploads weights, dit_create
     eps = model.forward(x_t, t, y)     # dit_forward
     eps = model.cfg_forward(x_t, t, y, scale=1.5, guided=4)   # dit_cfg_forward
+    x0 = model.sample(Sampler("ddpm", 250), x_T, y, scale=4.0, guided=4, noise=z)  # dit_sample
 
 ``cfg`` is a dict with keys C, Cout, F, H, W, p, pt, d, N, heads, mlp_hidden,
 num_classes, cond_dim, freq_dim, qk_norm, rope3d, dtype (0 fp32, 1 bf16),
@@ -49,6 +50,55 @@ def upload(a, dtype: torch.dtype, device) -> torch.Tensor:
     if isinstance(a, torch.Tensor):
         return a.to(device=device, dtype=dtype).contiguous()
     return torch.from_numpy(np.ascontiguousarray(a)).to(dtype).to(device)
+
+
+class Sampler:
+    """Host-side description of a sampler (``dit_sampler``).
+
+    kind: "ddpm", "dpmpp_2m" or "rf_euler"; steps: S.  ``timesteps`` (diffusion
+    kinds, S ints, decreasing) and ``times`` (RF, S + 1 floats, increasing)
+    default to the library's even grids."""
+    KINDS = {"ddpm": _lib.DIT_SAMPLER_DDPM, "dpmpp_2m": _lib.DIT_SAMPLER_DPMPP_2M,
+             "rf_euler": _lib.DIT_SAMPLER_RF_EULER}
+
+    def __init__(self, kind: str, steps: int, timesteps=None, times=None, train_steps=1000,
+                 beta_start=1e-4, beta_end=0.02):
+        self.kind, self.steps = kind, int(steps)
+        self._ts = None if timesteps is None else (C.c_int32 * len(timesteps))(*map(int, timesteps))
+        self._tm = None if times is None else (C.c_double * len(times))(*map(float, times))
+        if self._ts is not None and len(self._ts) != self.steps:
+            raise ValueError("timesteps needs one entry per step")
+        if self._tm is not None and len(self._tm) != self.steps + 1:
+            raise ValueError("times needs steps + 1 entries")
+        self.struct = _lib.DitSampler(
+            kind=self.KINDS[kind], num_steps=self.steps,
+            timesteps=C.cast(self._ts, C.POINTER(C.c_int32)) if self._ts is not None else None,
+            times=C.cast(self._tm, C.POINTER(C.c_double)) if self._tm is not None else None,
+            train_steps=int(train_steps), beta_start=float(beta_start), beta_end=float(beta_end))
+
+    def coefficients(self, k: int):
+        """(model time, 8 coefficients) of step k, from the library's host code."""
+        lib = _lib.load()
+        mt = C.c_double()
+        co = (C.c_double * 8)()
+        _lib.check(lib.dit_sampler_coefficients(C.byref(self.struct), int(k), C.byref(mt), co))
+        return mt.value, list(co)
+
+    def step(self, k: int, x, model_out, z=None, x0_hist=None, out=None):
+        """Step k on [B, C, ...] fp32 device tensors (``dit_sampler_step``)."""
+        lib = _lib.load()
+        B, Cc = x.shape[0], x.shape[1]
+        spatial = x[0, 0].numel()
+        if out is None:
+            out = torch.empty_like(x)
+        for name, a in (("x", x), ("model_out", model_out), ("z", z), ("x0_hist", x0_hist),
+                        ("out", out)):
+            if a is not None and (a.dtype != torch.float32 or not a.is_contiguous()):
+                raise TypeError(f"{name} must be a contiguous float32 tensor")
+        _lib.check(lib.dit_sampler_step(C.byref(self.struct), int(k), _ptr(x), _ptr(model_out),
+                                        B, Cc, model_out.shape[1], spatial, _ptr(z),
+                                        _ptr(x0_hist), _ptr(out), _stream(x.device)))
+        return out
 
 
 class DiT:
@@ -150,6 +200,31 @@ class DiT:
                                                _stream(self.device))
         _lib.check(rc)
         return out
+
+    def sample(self, sampler: "Sampler", x, y=None, pooled=None, scale: float = 1.0,
+               guided: int = 0, noise=None):
+        """Full sampling loop (``dit_sample``) in place on the fp32 state x
+        [B, C, (F,) H, W]; returns x.  guided > 0 applies classifier-free
+        guidance to that many output channels."""
+        B = x.shape[0]
+        for name, a in (("x", x), ("y", y), ("pooled", pooled), ("noise", noise)):
+            if a is not None and (a.device != self.device or not a.is_contiguous()):
+                raise ValueError(f"{name} must be a contiguous tensor on {self.device}")
+        if x.dtype != torch.float32 or (noise is not None and noise.dtype != torch.float32):
+            raise TypeError("x and noise must be float32")
+        if y is not None and (y.dtype != torch.int32 or y.numel() != B):
+            raise TypeError("y must be int32 with one entry per row")
+        n = C.c_size_t()
+        _lib.check(self.lib.dit_sample_workspace_size(self.handle, C.byref(sampler.struct), B,
+                                                      int(guided), C.byref(n)))
+        if self._ws is None or self._ws.numel() < n.value:
+            self._ws = None
+            self._ws = torch.empty(n.value, dtype=torch.uint8, device=self.device)
+        ws = self._ws
+        _lib.check(self.lib.dit_sample(self.handle, C.byref(sampler.struct), _ptr(x), _ptr(y),
+                                       _ptr(pooled), B, float(scale), int(guided), _ptr(noise),
+                                       _ptr(ws), ws.numel(), _stream(self.device)))
+        return x
 
     def block_forward(self, layer: int, X, mod, X_out=None, o_branch=None, f_branch=None):
         B = mod.shape[0]

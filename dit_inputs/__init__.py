@@ -249,3 +249,26 @@ def make_inputs(cfg: dict, seed: int | None = None, batch: int | None = None) ->
         res["y"] = rng.integers(0, cfg["num_classes"], size=B).astype(np.int32)
         res["pooled"] = None
     return res
+
+
+def make_sampler_inputs(cfg: dict, steps: int, seed: int | None = None,
+                        batch: int | None = None) -> dict:
+    """Seeded inputs of a sampling loop: the starting state x ~ N(0,1)
+    [B, C, (F,) H, W] and the per-step noise z ~ N(0,1) [steps, B, C, ...],
+    both fp32; class labels U{0..num_classes-1} or pooled vectors N(0,1) as
+    in :func:`make_inputs`."""
+    if seed is None:
+        seed = 3000 + cfg["seed_idx"]
+    B = cfg["batch"] if batch is None else batch
+    rng = np.random.default_rng(seed)
+    C, F, H, W = cfg["C"], cfg["F"], cfg["H"], cfg["W"]
+    shape = (B, C, F, H, W) if (F > 1 or cfg["rope3d"]) else (B, C, H, W)
+    res = {"x": f32_round(rng.standard_normal(shape)),
+           "noise": f32_round(rng.standard_normal((steps,) + shape))}
+    if cfg["num_classes"] > 0:
+        res["y"] = rng.integers(0, cfg["num_classes"], size=B).astype(np.int32)
+    else:
+        res["y"] = None
+    res["pooled"] = (f32_round(rng.standard_normal((B, cfg["cond_dim"])))
+                     if cfg["cond_dim"] > 0 else None)
+    return res

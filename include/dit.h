@@ -231,6 +231,87 @@ int dit_block_forward(dit_handle* h, int layer, int B, const float* X_in, const 
                       float* X_out, float* o_branch, float* f_branch, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* ---- Sampling around the denoiser ----
+ * One reverse step updates the fp32 latent state x [B, C, F, H, W] from the
+ * model's prediction.  Kinds:
+ *   DIT_SAMPLER_DDPM      ancestral step of the diffusion model whose forward
+ *                         process is x_t = sqrt(abar_t) x_0 + sqrt(1 - abar_t) eps
+ *                         and whose reverse covariance is learned (cv-learn
+ *                         "Sora / DiT", Method, training objective bullet).
+ *                         Channels [0, C) are eps; with Cout == 2C channel C + c
+ *                         is the raw covariance value v and the variance is
+ *                         exp(f log beta + (1 - f) log beta_tilde), f = (v + 1)/2;
+ *                         with Cout == C it is beta_tilde.  Adds noise z except
+ *                         on the last step, which lands on the clean latent.
+ *   DIT_SAMPLER_DPMPP_2M  DPM-Solver++ second-order multistep in data
+ *                         prediction, deterministic (the multistep DPM-Solver of
+ *                         the itwiki page, inference with diffusers); the first
+ *                         step and the last one (into sigma = 0) are first order.
+ *   DIT_SAMPLER_RF_EULER  explicit Euler on the predicted rectified-flow
+ *                         velocity, x <- x + (t_{k+1} - t_k) v, from t = 0
+ *                         (noise) to t = 1 (data) (blog.outta.ai GOKU review,
+ *                         section 2.3); channels [0, C) are the velocity.
+ * Schedule (the pages give none): beta linear from beta_start to beta_end over
+ * train_steps, abar_t = prod_{j <= t} (1 - beta_j); step k evaluates the model
+ * at t = tau_k and moves to tau_{k+1} (the clean latent, abar = 1, after the
+ * last kept step).  No clipping of the predicted x_0. */
+#define DIT_SAMPLER_DDPM      0
+#define DIT_SAMPLER_DPMPP_2M  1
+#define DIT_SAMPLER_RF_EULER  2
+
+typedef struct dit_sampler {
+  int kind;                  /* DIT_SAMPLER_* */
+  int num_steps;             /* S >= 1 */
+  const int32_t* timesteps;  /* host [S] kept diffusion steps tau_0 > ... > tau_{S-1} in
+                                [0, train_steps); NULL: S steps spread evenly over
+                                [0, train_steps - 1] (j (train_steps-1)/(S-1), rounded
+                                half up), largest first */
+  const double* times;       /* host [S + 1] flow times t_0 < ... < t_S (RF); NULL: k / S */
+  int train_steps;           /* diffusion kinds: schedule length (1000) */
+  double beta_start;         /* 1e-4 */
+  double beta_end;           /* 0.02 */
+} dit_sampler;
+
+/* Host only (no device work): the model time of step k and the fp64
+ * coefficients the step kernel applies (rounded to fp32 there):
+ *   DDPM:   x' = c0 x - c1 eps + c4 * exp(0.5 (f c2 + (1 - f) c3)) z;
+ *           c0, c1 fold the posterior mean and the x_0 prediction, c2 = log beta,
+ *           c3 = log beta_tilde (at the last step the previous step's value; it
+ *           is unused there), c4 = 1 if noise is added else 0.
+ *   DPM++:  x0 = c0 x - c1 eps,  x' = c2 x + c3 x0 + c4 x0_prev; c5 = 1 if
+ *           x0_prev is read (second order) else 0.
+ *   RF:     x' = x + c0 v.
+ * Unused entries are 0. */
+int dit_sampler_coefficients(const dit_sampler* sp, int k, double* model_t, double coef[8]);
+
+/* Step k of `sp` on device buffers: x, x_out [B, C, spatial] fp32 (may alias),
+ * model_out [B, Cout, spatial] fp32 (Cout == C or 2C), z [B, C, spatial] fp32
+ * (DDPM steps that add noise; else may be NULL), x0_hist [B, C, spatial] fp32
+ * (DPM++ only: read as x0 of step k-1 when c5 = 1, overwritten with x0 of
+ * step k).  spatial = F * H * W. */
+int dit_sampler_step(const dit_sampler* sp, int k, const float* x, const float* model_out,
+                     int B, int C, int Cout, int64_t spatial, const float* z, float* x0_hist,
+                     float* x_out, void* stream);
+
+/* Workspace bytes of dit_sample (the forward's workspace for its rows plus
+ * the model time vector, a model-dtype copy of the state and the DPM++
+ * history). */
+int dit_sample_workspace_size(const dit_handle* h, const dit_sampler* sp, int B,
+                              int guided_channels, size_t* bytes);
+
+/* Full sampling loop of S steps on the caller's stream: each step runs the
+ * denoiser on the state (rounded to the model dtype) at the step's model time
+ * and applies the update, reading the decoder output directly (no separate
+ * unpatchify).  x: [B, C, F, H, W] fp32, in: the starting noise, out: the
+ * sample.  guided_channels > 0: classifier-free guidance as dit_cfg_forward
+ * (2B trunk rows, scale s, needs num_classes > 0 and no pooled conditioning);
+ * 0: the plain forward (y / pooled as for dit_forward).  noise: DDPM with
+ * S >= 2: [S, B, C, F, H, W] fp32, slice k is step k's z (the last slice is
+ * not read); otherwise may be NULL.  Needs Cout == C or 2C. */
+int dit_sample(dit_handle* h, const dit_sampler* sp, float* x, const int32_t* y,
+               const float* pooled, int B, float s, int guided_channels, const float* noise,
+               void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("dit_create", "dit_destroy", "dit_workspace_size", "dit_forward", "dit_cfg_forward",
               "dit_status_string", "dit_patchify", "dit_unpatchify", "dit_timestep_embed",
-              "dit_attention", "dit_linear", "dit_block_forward"):
+              "dit_attention", "dit_linear", "dit_block_forward", "dit_sampler_coefficients",
+              "dit_sampler_step", "dit_sample_workspace_size", "dit_sample"):
         assert n in names
     assert set(names) == set(_lib.EXPORTS), "binding and header disagree"
 
@@ -117,6 +118,48 @@ def test_forward_validates_before_launch():
         assert lib.dit_cfg_forward(h, p, p, p, 32, float("nan"), 4, p, p, need.value, None) == _lib.DIT_EINVAL
         assert lib.dit_cfg_forward(h, p, p, p, 33, 1.5, 4, p, p, need.value, None) == _lib.DIT_EWORKSPACE
         assert lib.dit_block_forward(h, 2, 4, p, p, p, None, None, p, need.value, None) == _lib.DIT_EINVAL
+    finally:
+        lib.dit_destroy(h)
+
+
+@needs_lib
+def test_sample_validates_before_launch():
+    lib = _lib.load()
+    rc, h = _create(_cfg(), _weights())
+    assert rc == _lib.DIT_OK
+    try:
+        sp = _lib.DitSampler(kind=_lib.DIT_SAMPLER_DDPM, num_steps=4, train_steps=1000,
+                             beta_start=1e-4, beta_end=0.02)
+        st = C.byref(sp)
+        need = C.c_size_t()
+        assert lib.dit_sample_workspace_size(h, st, 32, 4, C.byref(need)) == 0
+        fwd = C.c_size_t()
+        assert lib.dit_workspace_size(h, 64, C.byref(fwd)) == 0
+        assert need.value > fwd.value   # forward workspace of 2B rows plus the loop's buffers
+        assert lib.dit_sample_workspace_size(h, st, 32, 9, C.byref(need)) == _lib.DIT_EINVAL
+        assert lib.dit_sample_workspace_size(h, st, 32, 4, C.byref(need)) == 0
+        p = C.c_void_p(0x200000)
+        n = need.value
+        assert lib.dit_sample(h, st, p, p, None, 32, 4.0, 4, None, p, n, None) == _lib.DIT_EINVAL
+        assert lib.dit_sample(h, st, None, p, None, 32, 4.0, 4, p, p, n, None) == _lib.DIT_EINVAL
+        assert lib.dit_sample(h, st, p, None, None, 32, 4.0, 4, p, p, n, None) == _lib.DIT_EINVAL
+        assert lib.dit_sample(h, st, p, p, None, 32, float("inf"), 4, p, p, n, None) == _lib.DIT_EINVAL
+        assert lib.dit_sample(h, st, p, p, None, 32, 4.0, 4, p, p, n - 1, None) == _lib.DIT_EWORKSPACE
+        assert lib.dit_sample(h, st, p, p, None, 32, 4.0, 4, p, None, n, None) == _lib.DIT_EWORKSPACE
+        assert lib.dit_sample(h, st, p, p, None, 0, 4.0, 4, p, p, n, None) == _lib.DIT_EINVAL
+        bad = _lib.DitSampler(kind=_lib.DIT_SAMPLER_DDPM, num_steps=4, train_steps=3,
+                              beta_start=1e-4, beta_end=0.02)
+        assert lib.dit_sample(h, C.byref(bad), p, p, None, 32, 4.0, 4, p, p, n, None) == _lib.DIT_EINVAL
+    finally:
+        lib.dit_destroy(h)
+    # Cout must be C or 2C
+    rc, h = _create(_cfg(out_channels=5), _weights())
+    assert rc == _lib.DIT_OK
+    try:
+        rf = _lib.DitSampler(kind=_lib.DIT_SAMPLER_RF_EULER, num_steps=4)
+        p = C.c_void_p(0x200000)
+        assert lib.dit_sample(h, C.byref(rf), p, p, None, 2, 1.0, 0, None, p, 1 << 40,
+                              None) == _lib.DIT_EUNSUPPORTED
     finally:
         lib.dit_destroy(h)
 
