@@ -10,7 +10,8 @@ before timing starts.  Prints one JSON line.
 
 Besides the headline number the line carries
   roofline      the dominant kernel, timed alone with HIP events on the same
-                stream and launch configuration as in the forward pass;
+                stream and launch configuration as in the forward pass, right
+                after the forward loop (at the same sustained clocks);
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on
                 this host's cores.
 """
@@ -37,15 +38,19 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dit_xl2_256_cfg")
-    ap.add_argument("--kernel-launches", type=int, default=50,
-                    help="launches of the dominant kernel timed alone")
+    ap.add_argument("--kernel-launches", type=int, default=200,
+                    help="launches of the dominant kernel timed alone (after as many untimed)")
     ap.add_argument("--cpu-rows", type=int, default=2,
                     help="guided rows of the workload the oracle runs for the CPU baseline")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (HBM counter calibration)")
+    ap.add_argument("--sample", choices=("ddpm", "dpmpp_2m", "rf_euler"), default=None,
+                    help="time whole sampling loops (dit_sample) instead of single forwards")
+    ap.add_argument("--sample-steps", type=int, default=25,
+                    help="denoiser evaluations per sampling loop")
     return ap.parse_args()
 
 
@@ -91,6 +96,103 @@ def cpu_baseline(cfg, w, inp, rows: int, trunk_rows: int):
                       f"value scaled to whole {trunk_rows}-row forwards"}
 
 
+def sample_main(args, cfg, model, dev):
+    """Sampling loops: each timed step is one dit_sample call of S denoiser
+    evaluations plus S update kernels on the workload's batch."""
+    import torch
+    import dit_inputs
+    import diffusion_transformer_denoiser_amd as dm
+    from oracle import flops as oflops
+
+    S = args.sample_steps
+    Bh = cfg["batch"]
+    rows = 2 * Bh if cfg["cfg"] else Bh
+    guided = cfg["guided"] if cfg["cfg"] else 0
+    scale = cfg["scale"] if cfg["cfg"] else 1.0
+    inp = dit_inputs.make_sampler_inputs(cfg, S)
+    x0 = torch.from_numpy(inp["x"]).to(dev)
+    x = x0.clone()
+    y = torch.from_numpy(inp["y"]).to(dev) if inp["y"] is not None else None
+    pooled = torch.from_numpy(inp["pooled"]).to(dev) if inp["pooled"] is not None else None
+    noise = torch.from_numpy(inp["noise"]).to(dev) if args.sample == "ddpm" else None
+    sp = dm.Sampler(args.sample, S)
+
+    def loop():
+        x.copy_(x0)
+        model.sample(sp, x, y=y, pooled=pooled, scale=scale, guided=guided, noise=noise)
+
+    for _ in range(args.warmup):
+        loop()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        loop()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    assert torch.isfinite(x).all().item(), "non-finite sample"
+
+    # The update kernel alone (the plain-input variant of the same kernel, via
+    # dit_sampler_step) at the loop's state size.  One launch takes a few
+    # microseconds, less than issuing it from Python, so the launches are
+    # captured in a HIP graph and the graph replays are timed with HIP events.
+    n_el = x.numel()
+    learned = cfg["Cout"] == 2 * cfg["C"]
+    mo = torch.randn((x.shape[0], cfg["Cout"]) + tuple(x.shape[2:]), device=dev)
+    z = torch.randn_like(x)
+    hist = torch.zeros_like(x)
+    xs = x0.clone()
+    for _ in range(3):
+        sp.step(0, xs, mo, z=z, x0_hist=hist, out=xs)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.kernel_launches):
+            sp.step(0, xs, mo, z=z, x0_hist=hist, out=xs)
+    graph.replay()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    k0.record()
+    for _ in range(3):
+        graph.replay()
+    k1.record()
+    torch.cuda.synchronize()
+    kms = k0.elapsed_time(k1) / (3 * args.kernel_launches)
+    # algorithmic bytes per element of step 0: read x and the prediction channel(s),
+    # the noise (DDPM) or the x0 history slot (DPM++ writes it), write x
+    per = {"ddpm": 4 * (3 + (1 if learned else 0)) + 4, "dpmpp_2m": 4 * 2 + 4 + 4,
+           "rf_euler": 4 * 2 + 4}[args.sample]
+    gbs = per * n_el / (kms * 1e-3) / 1e9
+    gmac_row = oflops.gmac_for(cfg)
+    flop_loop = 2.0 * gmac_row * 1e9 * rows * S
+    line = {
+        "metric": f"DiT sampling loop images/s ({args.sample}, {S} steps) on 1 MI355X",
+        "value": round(Bh * 1000.0 / ms, 3),
+        "unit": "images/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg["dtype"] == dit_inputs.DTYPE_BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) start state and noise, random labels, N(0,0.02) weights)",
+        "config": {"workload": cfg["name"], "sampler": args.sample, "sampling_steps": S,
+                   "images_per_loop": Bh, "trunk_rows": rows, "guidance_scale": scale,
+                   "guided_channels": guided, "parallelism": "single GPU"},
+        "ms_per_denoiser_step": round(ms / S, 4),
+        "tflops": round(flop_loop / (ms * 1e-3) / 1e12, 1),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": per * n_el,
+                     "kernel": f"sampler_step_kernel ({args.sample}, plain input, {n_el} elements)",
+                     "avg_launch_ms": round(kms, 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -120,6 +222,8 @@ def main():
     y = torch.from_numpy(inp["y"]).to(dev) if inp["y"] is not None else None
     pooled = torch.from_numpy(inp["pooled"]).to(dev) if inp["pooled"] is not None else None
     out = torch.empty(model.out_shape(Bh), device=dev, dtype=torch.float32)
+    if args.sample:
+        return sample_main(args, cfg, model, dev)
 
     def step():
         if cfg["cfg"]:
@@ -127,10 +231,26 @@ def main():
         else:
             model.forward(x, t, y, pooled, out=out)
 
+    # Dominant kernel: the FFN up-projection (N = 4d, K = d, bias + tanh-GELU epilogue), the
+    # same MFMA kernel, tile and shape as in the forward pass, timed alone.  The forward runs
+    # the two halves of its rows on two streams, so each launch there covers M = rows/2 * T.
+    # Its buffers are set up before the forward is timed, and it is timed right after the
+    # forward loop, with a warm-up of its own, so it runs at the same sustained clocks as
+    # inside the forward (an idle GPU needs ~0.1 s of load to reach them).
+    # Consecutive launches cycle through the model's per-block weights, as the forward does,
+    # so no launch finds its weight matrix already cached.
+    d, hid = cfg["d"], cfg["mlp_hidden"]
+    M = (rows // 2 if rows >= 2 else rows) * T
+    A = torch.randn(M, d, device=dev).to(dt)
+    W1 = [model.tensors["fc1_w"][l] for l in range(cfg["N"])]
+    b1 = [model.tensors["fc1_b"][l] for l in range(cfg["N"])]
+    G = torch.empty(M, hid, device=dev, dtype=dt)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev0.record()
@@ -139,32 +259,21 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    nb = len(W1)
+    for i in range(args.kernel_launches):
+        dm.linear(dm.DIT_EPI_GELU, A, W1[i % nb], b1[i % nb], G)
+    k0.record()
+    for i in range(args.kernel_launches):
+        dm.linear(dm.DIT_EPI_GELU, A, W1[i % nb], b1[i % nb], G)
+    k1.record()
+    torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    kms = k0.elapsed_time(k1) / args.kernel_launches
     assert torch.isfinite(out).all().item(), "non-finite output"
 
     gmac_row = oflops.gmac_for(cfg)
     flop_fwd = 2.0 * gmac_row * 1e9 * rows
     tflops = flop_fwd / (ms * 1e-3) / 1e12
-
-    # Dominant kernel: the FFN up-projection (N = 4d, K = d, bias + tanh-GELU epilogue), the
-    # same MFMA kernel, tile and shape as in the forward pass, timed alone.  The forward runs
-    # the two halves of its rows on two streams, so each launch there covers M = rows/2 * T.
-    d, hid = cfg["d"], cfg["mlp_hidden"]
-    M = (rows // 2 if rows >= 2 else rows) * T
-    A = torch.randn(M, d, device=dev).to(dt)
-    W1 = model.tensors["fc1_w"][0]
-    b1 = model.tensors["fc1_b"][0]
-    G = torch.empty(M, hid, device=dev, dtype=dt)
-    for _ in range(3):
-        dm.linear(dm.DIT_EPI_GELU, A, W1, b1, G)
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    k0.record()
-    for _ in range(args.kernel_launches):
-        dm.linear(dm.DIT_EPI_GELU, A, W1, b1, G)
-    k1.record()
-    torch.cuda.synchronize()
-    kms = k0.elapsed_time(k1) / args.kernel_launches
     kflop = 2.0 * M * hid * d
     k_tflops = kflop / (kms * 1e-3) / 1e12
     traffic = measured_traffic("diffusion_transformer_denoiser_amd/csrc/gemm_mfma.hip",
