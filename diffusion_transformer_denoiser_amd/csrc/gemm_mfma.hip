@@ -57,8 +57,9 @@ __device__ __forceinline__ void bare_barrier() {
 // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs (each with
 // its own L2): with SWZ, workgroup b runs logical tile (b % 8) * (n / 8) + b / 8,
 // so each XCD walks a contiguous range of logical tiles, and logical tiles are
-// ordered in groups of G row-tiles (column-major inside a group) so the tiles
-// resident on one XCD at a time share A and W tiles.  Needs n % 8 == 0.
+// ordered in groups of G row-tiles (column-major inside a group, the column
+// index rotated per XCD) so the tiles resident on one XCD at a time share A
+// and W tiles.  Needs n % 8 == 0.
 template <int SWZ>
 __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
   if constexpr (SWZ) {
@@ -69,7 +70,14 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
     const int grp = logical / per_group, in = logical - grp * per_group;
     const int rows = min(G, tiles_m - grp * G);
     tm = grp * G + in % rows;
-    tn = in / rows;
+    // The column walk of a group starts 1/8 of the way further along for each
+    // XCD (the XCD of the group's first tile, so all tiles of a group share
+    // one rotation and the map stays one-to-one): at any moment the XCDs fetch
+    // different W columns, so a weight tile comes from HBM once and later XCDs
+    // find it in the Infinity Cache (-8% per launch when the weights are not
+    // cached yet, as in a forward).
+    const int xg = (grp * per_group) / (n >> 3);
+    tn = (in / rows + (xg & 7) * tiles_n / 8) % tiles_n;
   } else {
     tm = b / tiles_n;
     tn = b - tm * tiles_n;

@@ -80,8 +80,11 @@ def test_timestep_embedding():
 
 # M <= 64 takes 64-row tiles (one 32-row block per wave); (17, 192, 256) is a
 # single ragged tile of that kind.
+# Includes shapes whose groups of 8 row-tiles span several XCDs' tile ranges
+# (2048 x 2304, 3072 x 1152) and one XCD range per group (8192 x 1152).
 LIN_SHAPES = [(64, 128, 64), (300, 200, 128), (257, 1152, 1152), (1024, 4608, 1152),
-              (512, 1152, 4608), (64, 3456, 1152), (33, 96, 320), (17, 192, 256)]
+              (512, 1152, 4608), (64, 3456, 1152), (33, 96, 320), (17, 192, 256),
+              (2048, 2304, 768), (3072, 1152, 1152), (8192, 1152, 1152)]
 
 
 @pytest.mark.parametrize("M,N,K", LIN_SHAPES)
