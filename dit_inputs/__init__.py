@@ -28,6 +28,11 @@ import numpy as np
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
+# Conditioning designs (mirrors the C header's codes): adaLN-Zero, the time and
+# class embeddings as two extra tokens, or as a cross-attended context
+# (itwiki page, Conditioning methods table).
+COND_ADALN_ZERO, COND_IN_CONTEXT, COND_CROSS_ATTENTION = 0, 1, 2
+
 # Model sizes: (depth N, width d, heads) from the Model sizes table.
 MODEL_SIZES = {
     "S": (12, 384, 6),
@@ -43,7 +48,7 @@ def _image_config(size, p, I, dtype, batch, cfg_guidance, name):
         name=name, C=4, Cout=8, F=1, H=I, W=I, p=p, pt=1, d=d, N=N,
         heads=heads, mlp_hidden=4 * d, num_classes=1000, cond_dim=0,
         freq_dim=256, qk_norm=0, rope3d=0, dtype=dtype, ln_eps=1e-6,
-        batch=batch, cfg=cfg_guidance, scale=1.5, guided=4,
+        batch=batch, cfg=cfg_guidance, scale=1.5, guided=4, conditioning=COND_ADALN_ZERO,
     )
 
 
@@ -66,7 +71,17 @@ WORKLOADS = {
         C=16, Cout=16, F=16, H=60, W=104, p=2, pt=1, d=1152, N=28, heads=16,
         mlp_hidden=4608, num_classes=0, cond_dim=4096, freq_dim=256, qk_norm=1,
         rope3d=1, dtype=DTYPE_BF16, ln_eps=1e-6, batch=1, cfg=False, scale=1.0,
-        guided=16, seed_idx=5),
+        guided=16, conditioning=COND_ADALN_ZERO, seed_idx=5),
+    # The other two conditioning designs of the Conditioning methods table, at
+    # the DiT-XL/2 256x256 + CFG shape.
+    "dit_xl2_256_cfg_in_context": dict(
+        _image_config("XL", 2, 32, DTYPE_BF16, 32, True,
+                      "DiT-XL/2 256x256 in-context conditioning + CFG, 32 cond + 32 null rows"),
+        conditioning=COND_IN_CONTEXT, seed_idx=6),
+    "dit_xl2_256_cfg_cross_attention": dict(
+        _image_config("XL", 2, 32, DTYPE_BF16, 32, True,
+                      "DiT-XL/2 256x256 cross-attention conditioning + CFG, 32 cond + 32 null rows"),
+        conditioning=COND_CROSS_ATTENTION, seed_idx=7),
 }
 
 
@@ -144,19 +159,30 @@ def weight_shapes(cfg: dict) -> dict:
     if cfg["cond_dim"] > 0:
         shapes["pool_w"] = (d, cfg["cond_dim"])
         shapes["pool_b"] = (d,)
+    cond = cfg.get("conditioning", COND_ADALN_ZERO)
+    if cond == COND_ADALN_ZERO:
+        shapes.update({"ada_w": ((6 * N + 2) * d, d), "ada_b": ((6 * N + 2) * d,)})
     shapes.update({
-        "ada_w": ((6 * N + 2) * d, d), "ada_b": ((6 * N + 2) * d,),
         "qkv_w": (N, 3 * d, d), "qkv_b": (N, 3 * d),
         "o_w": (N, d, d), "o_b": (N, d),
         "fc1_w": (N, hid, d), "fc1_b": (N, hid),
         "fc2_w": (N, d, hid), "fc2_b": (N, d),
-        "out_w": (kout, d), "out_b": (kout,),
     })
+    if cond != COND_ADALN_ZERO:
+        # per block: (shift, scale) of each LayerNorm (2 for in-context, 3 with
+        # the cross-attention layer); the final layer's LayerNorm
+        n_ln = 2 if cond == COND_IN_CONTEXT else 3
+        shapes.update({"ln_p": (N, n_ln, 2, d), "final_ln": (2, d)})
+    if cond == COND_CROSS_ATTENTION:
+        shapes.update({"xq_w": (N, d, d), "xq_b": (N, d),
+                       "xkv_w": (N, 2 * d, d), "xkv_b": (N, 2 * d),
+                       "xo_w": (N, d, d), "xo_b": (N, d)})
+    shapes.update({"out_w": (kout, d), "out_b": (kout,)})
     return shapes
 
 
 GEMM_WEIGHTS = ("pe_w", "t1_w", "t2_w", "pool_w", "ada_w", "qkv_w", "o_w",
-                "fc1_w", "fc2_w", "out_w")
+                "fc1_w", "fc2_w", "out_w", "xq_w", "xkv_w", "xo_w")
 
 
 def make_weights(cfg: dict, seed: int | None = None, std: float = 0.02) -> dict:

@@ -46,7 +46,8 @@ from .dit_oracle import (  # noqa: F401
     patchify, unpatchify, timestep_embedding, pos_embed_2d, layer_norm,
     modulate, silu, gelu_tanh, linear, attention, qk_layernorm, rope3d,
     rope3d_tables, embed_condition, modulation, block, forward, cfg_forward,
-    cfg_combine, token_grid,
+    cfg_combine, token_grid, block_in_context, block_cross_attention, cross_attention,
+    class_embedding, block_weights, IN_CONTEXT, CROSS_ATTENTION,
 )
 from . import flops  # noqa: F401
 from . import sampler_oracle  # noqa: F401

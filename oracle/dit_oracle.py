@@ -283,8 +283,92 @@ def block(cfg, wl, X, mod_l, rope=None):
 
 
 def block_weights(w, l):
-    return {k: w[k][l] for k in ("qkv_w", "qkv_b", "o_w", "o_b", "fc1_w", "fc1_b",
-                                 "fc2_w", "fc2_b")}
+    keys = ("qkv_w", "qkv_b", "o_w", "o_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b",
+            "ln_p", "xq_w", "xq_b", "xkv_w", "xkv_b", "xo_w", "xo_b")
+    return {k: w[k][l] for k in keys if k in w}
+
+
+# ---------------------------------------------------------------------------
+# The other two conditioning designs ([DiT-wiki] Conditioning methods table;
+# [DiT-coin] DiT block description).  Both use standard pre-LN blocks without
+# regressed modulation.  Readings taken: each LayerNorm has a learned affine
+# written like the adaLN form with constants, LN(x)(1 + g) + b, with
+# ln_p[l, i] = (b, g) for the i-th LN of block l; residual adds have no gate.
+
+IN_CONTEXT, CROSS_ATTENTION = 1, 2
+
+
+def _self_attention(cfg, wl, h):
+    B, T, d = h.shape
+    Hh = cfg["heads"]
+    dh = d // Hh
+    qkv = linear(h, wl["qkv_w"], wl["qkv_b"])
+    q, k, v = (qkv[..., i * d:(i + 1) * d].reshape(B, T, Hh, dh).transpose(0, 2, 1, 3)
+               for i in range(3))
+    a = attention(q, k, v).transpose(0, 2, 1, 3).reshape(B, T, d)
+    return linear(a, wl["o_w"], wl["o_b"])
+
+
+def cross_attention(cfg, wl, h, ctx):
+    """Multi-head attention of the tokens h [B, T, d] over the context tokens
+    ctx [B, S, d]: q = Linear(d, d)(h), [k | v] = Linear(d, 2d)(ctx), per head
+    softmax(q k^T / sqrt(dh)) v, output Linear(d, d).  ([DiT-coin]: a
+    multi-head cross-attention layer added after the self-attention layer.)"""
+    B, T, d = h.shape
+    S = ctx.shape[1]
+    Hh = cfg["heads"]
+    dh = d // Hh
+    q = linear(h, wl["xq_w"], wl["xq_b"]).reshape(B, T, Hh, dh).transpose(0, 2, 1, 3)
+    kv = linear(ctx, wl["xkv_w"], wl["xkv_b"])
+    k = kv[..., :d].reshape(B, S, Hh, dh).transpose(0, 2, 1, 3)
+    v = kv[..., d:].reshape(B, S, Hh, dh).transpose(0, 2, 1, 3)
+    a = attention(q, k, v).transpose(0, 2, 1, 3).reshape(B, T, d)
+    return linear(a, wl["xo_w"], wl["xo_b"])
+
+
+def _ffn(wl, h):
+    return linear(gelu_tanh(linear(h, wl["fc1_w"], wl["fc1_b"])), wl["fc2_w"], wl["fc2_b"])
+
+
+def _affine_ln(X, lnp_i, eps):
+    B = X.shape[0]
+    b = np.broadcast_to(_f64(lnp_i[0]), (B, X.shape[-1]))
+    g = np.broadcast_to(_f64(lnp_i[1]), (B, X.shape[-1]))
+    return modulate(layer_norm(X, eps), b, g)
+
+
+def block_in_context(cfg, wl, X):
+    """[DiT-wiki] Conditioning methods, in-context row: the time and class
+    embeddings ride along as two extra tokens of the sequence (like ViT's cls
+    token) through standard blocks:
+        x <- x + Attn(LN1(x)),  x <- x + FFN(LN2(x)).
+    X: [B, T + 2, d].  Returns X."""
+    X = _f64(X)
+    eps = cfg["ln_eps"]
+    X = X + _self_attention(cfg, wl, _affine_ln(X, wl["ln_p"][0], eps))
+    return X + _ffn(wl, _affine_ln(X, wl["ln_p"][1], eps))
+
+
+def block_cross_attention(cfg, wl, X, ctx):
+    """[DiT-wiki] Conditioning methods, cross-attention row; [DiT-coin]: the
+    time and class embeddings form a separate length-2 sequence, and each block
+    gains a multi-head cross-attention layer after its self-attention:
+        x <- x + Attn(LN1(x)),  x <- x + CrossAttn(LN2(x), ctx),
+        x <- x + FFN(LN3(x)).
+    X: [B, T, d]; ctx: [B, 2, d].  Returns X."""
+    X = _f64(X)
+    eps = cfg["ln_eps"]
+    X = X + _self_attention(cfg, wl, _affine_ln(X, wl["ln_p"][0], eps))
+    X = X + cross_attention(cfg, wl, _affine_ln(X, wl["ln_p"][1], eps), _f64(ctx))
+    return X + _ffn(wl, _affine_ln(X, wl["ln_p"][2], eps))
+
+
+def class_embedding(cfg, w, y):
+    """Row y of the class table (num_classes + 1 rows, the last the null label)."""
+    y = np.asarray(y).astype(np.int64)
+    if np.any(y < 0) or np.any(y > cfg["num_classes"]):
+        raise ValueError("class label out of range")
+    return _f64(w["y_table"])[y]
 
 
 # ---------------------------------------------------------------------------
@@ -327,6 +411,10 @@ def forward(cfg, w, x_t, t, y=None, pooled=None, taps=None, blocks=None):
             raise ValueError("2-D position embedding needs a single frame")
         X = X + pos_embed_2d(gh, gw, d)[None]
 
+    cond = cfg.get("conditioning", 0)
+    if cond in (IN_CONTEXT, CROSS_ATTENTION):
+        return _forward_variant(cfg, w, X, t, y, taps, blocks, (F, H, W, video))
+
     e, temb, c = embed_condition(cfg, w, t, y, pooled)
     mod = modulation(cfg, w, c)
     if taps is not None:
@@ -343,6 +431,42 @@ def forward(cfg, w, x_t, t, y=None, pooled=None, taps=None, blocks=None):
     shf = mod[:, 6 * d * N:6 * d * N + d]
     scf = mod[:, 6 * d * N + d:6 * d * N + 2 * d]
     Hf = modulate(layer_norm(X, cfg["ln_eps"]), shf, scf)
+    Y = linear(Hf, w["out_w"], w["out_b"])
+    out = unpatchify(Y, cfg["Cout"], F, H, W, p, pt, frames_axis=video)
+    if taps is not None:
+        taps.update(Hf=Hf, Y=Y, out=out)
+    return out
+
+
+def _forward_variant(cfg, w, X, t, y, taps, blocks, geom):
+    """The in-context and cross-attention designs after the patch embedding X
+    [B, T, d].  Readings taken: the time-embedding token is the timestep MLP's
+    output and the class token is the class table's row, both without a
+    position embedding; in-context appends them after the T patch tokens;
+    the final layer is LN (learned affine) + Linear on the T patch tokens."""
+    F, H, W, video = geom
+    p, pt, N = cfg["p"], cfg["pt"], cfg["N"]
+    if cfg["cond_dim"] > 0 or cfg["num_classes"] <= 0:
+        raise ValueError("the in-context and cross-attention designs are class-conditional")
+    T = X.shape[1]
+    e = timestep_embedding(t, cfg["freq_dim"])
+    temb = linear(silu(linear(e, w["t1_w"], w["t1_b"])), w["t2_w"], w["t2_b"])
+    yemb = class_embedding(cfg, w, y)
+    in_ctx = cfg["conditioning"] == IN_CONTEXT
+    ctx = None
+    if in_ctx:
+        X = np.concatenate([X, temb[:, None, :], yemb[:, None, :]], axis=1)
+    else:
+        ctx = np.stack([temb, yemb], axis=1)
+    if taps is not None:
+        taps.update(e=e, temb=temb, yemb=yemb, X0=X.copy(), X=[])
+    nb = N if blocks is None else blocks
+    for l in range(nb):
+        wl = block_weights(w, l)
+        X = block_in_context(cfg, wl, X) if in_ctx else block_cross_attention(cfg, wl, X, ctx)
+        if taps is not None:
+            taps["X"].append(X.copy())
+    Hf = _affine_ln(X[:, :T], w["final_ln"], cfg["ln_eps"])
     Y = linear(Hf, w["out_w"], w["out_b"])
     out = unpatchify(Y, cfg["Cout"], F, H, W, p, pt, frames_axis=video)
     if taps is not None:

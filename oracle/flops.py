@@ -50,9 +50,16 @@ def gmac_per_image(N, d, T, p, C, Cout, freq_dim=256, pt=1, conditioning="adaLN-
     return (blocks + embed + decode + temb + final) / 1e9
 
 
-def gmac_for(cfg, conditioning="adaLN-Zero"):
+COND_NAMES = {0: "adaLN-Zero", 1: "in-context", 2: "cross-attention"}
+
+
+def gmac_for(cfg, conditioning=None):
     """GMAC per row for a workload dict (keys N, d, F, H, W, p, pt, C, Cout,
-    freq_dim, mlp_hidden).  Adds the pooled-vector projection when present."""
+    freq_dim, mlp_hidden, and the conditioning design code, 0 = adaLN-Zero,
+    1 = in-context, 2 = cross-attention).  Adds the pooled-vector projection
+    when present."""
+    if conditioning is None:
+        conditioning = COND_NAMES[cfg.get("conditioning", 0)]
     T = (cfg["F"] // cfg["pt"]) * (cfg["H"] // cfg["p"]) * (cfg["W"] // cfg["p"])
     g = gmac_per_image(cfg["N"], cfg["d"], T, cfg["p"], cfg["C"], cfg["Cout"],
                        cfg["freq_dim"], cfg["pt"], conditioning,
