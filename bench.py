@@ -240,7 +240,7 @@ def main():
     # Consecutive launches cycle through the model's per-block weights, as the forward does,
     # so no launch finds its weight matrix already cached.
     d, hid = cfg["d"], cfg["mlp_hidden"]
-    M = (rows // 2 if rows >= 2 else rows) * T
+    M = (rows // 2 if rows >= 2 else rows) * model.Tt   # tokens per trunk row
     A = torch.randn(M, d, device=dev).to(dt)
     W1 = [model.tensors["fc1_w"][l] for l in range(cfg["N"])]
     b1 = [model.tensors["fc1_b"][l] for l in range(cfg["N"])]

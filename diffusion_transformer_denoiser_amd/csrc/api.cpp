@@ -55,7 +55,11 @@ struct dit_handle {
   int d, N, heads, dh, hid, ncls, cond_dim, freq, dtype, es;
   float eps;
   int gf, gh, gw, T, kin, kout, mod_stride;
+  // conditioning design; tokens per trunk row (T + 2 in-context, else T);
+  // LayerNorms per block of the in-context / cross-attention designs
+  int cond, Tt, nln;
   PatchGeom gin, gout;
+  PatchGeom gouty;   // gout with T = Tt: the decoder output's row stride
   // Second stream for the two independent halves of a batch (created on the
   // first forward, on the device current then), and the fork / join events.
   // The mutex makes each call's fork-enqueue-join sequence atomic, so calls
@@ -88,7 +92,7 @@ bool ensure_aux(const dit_handle* h) {
 namespace {
 
 struct WsLayout {
-  size_t e, th, c, sc, pp, pe, mod, X, H, qkv, o, G, Y, total;
+  size_t e, th, c, sc, pp, pe, mod, ctx, kv, X, H, qkv, o, G, Y, total;
 };
 
 WsLayout ws_layout(const dit_handle* h, int rows) {
@@ -99,14 +103,16 @@ WsLayout ws_layout(const dit_handle* h, int rows) {
     off += align256(bytes);
     return o;
   };
-  const size_t es = h->es, R = (size_t)rows, M = R * h->T;
+  const size_t es = h->es, R = (size_t)rows, M = R * h->Tt;
   L.e = take(R * h->freq * 4);
   L.th = take(R * h->d * 4);
   L.c = take(R * h->d * 4);
   L.sc = take(R * h->d * es);
   L.pp = take(h->cond_dim > 0 ? R * h->d * 4 : 0);          // pooled projection
   L.pe = take(h->cfg.rope3d ? 0 : (size_t)h->T * h->d * 4);  // 2-D position table
-  L.mod = take(R * h->mod_stride * 4);
+  L.mod = take(R * h->mod_stride * 4);                        // 0 without adaLN
+  L.ctx = take(h->cond == DIT_COND_CROSS_ATTN ? R * 2 * h->d * es : 0);      // context tokens
+  L.kv = take(h->cond == DIT_COND_CROSS_ATTN ? R * 2 * 2 * h->d * es : 0);   // their k | v
   L.X = take(M * h->d * 4);
   L.H = take(M * h->d * es);
   L.qkv = take(M * 3 * h->d * es);
@@ -207,12 +213,73 @@ int run_block(const dit_handle* h, int l, int rows, float* X, const float* mod, 
   return DIT_OK;
 }
 
+// One block of the in-context or cross-attention design on X [rows * Tt, d]
+// (fp32, in place).  Each LayerNorm's affine (b, g) is applied as a modulation
+// that is the same for every row (row stride 0); residual adds have no gate.
+// kv: this row group's context keys | values [rows, 2, 2d] (cross-attention).
+int run_block_variant(const dit_handle* h, int l, int rows, float* X, const void* ctx, void* kv,
+                      void* ws, const WsLayout& L, hipStream_t s) {
+  const int d = h->d, Tt = h->Tt, M = rows * Tt, es = h->es;
+  void* Hb = at<void>(ws, L.H);
+  void* O = at<void>(ws, L.o);
+  void* G = at<void>(ws, L.G);
+  void* qkv = at<void>(ws, L.qkv);
+  const float* lnp = h->w.ln_p + (size_t)l * h->nln * 2 * d;
+
+  DIT_HIP(launch_ln_modulate(X, M, Tt, d, lnp, 0, 0, d, h->eps, Hb, h->dtype, s));
+  EpiParams ep = epi0();
+  ep.bias = h->w.qkv_b + (size_t)l * 3 * d;
+  ep.out = qkv; ep.ldo = 3 * d;
+  DIT_HIP(linear(h, EPI_BIAS_DT, Hb, d, woff(h->w.qkv_w, (size_t)l * 3 * d * d, es), M, 3 * d, d,
+                 ep, s));
+  DIT_HIP(launch_attention(qkv, rows, h->heads, Tt, h->dh, h->dtype, O, s));
+  ep = epi0();
+  ep.bias = h->w.o_b + (size_t)l * d;
+  ep.out = X; ep.ldo = d; ep.T = Tt;
+  DIT_HIP(linear(h, EPI_GATED, O, d, woff(h->w.o_w, (size_t)l * d * d, es), M, d, d, ep, s));
+
+  int li = 1;
+  if (h->cond == DIT_COND_CROSS_ATTN) {
+    DIT_HIP(launch_ln_modulate(X, M, Tt, d, lnp, 0, 2 * d, 3 * d, h->eps, Hb, h->dtype, s));
+    ep = epi0();
+    ep.bias = h->w.xq_b + (size_t)l * d;
+    ep.out = qkv; ep.ldo = d;
+    DIT_HIP(linear(h, EPI_BIAS_DT, Hb, d, woff(h->w.xq_w, (size_t)l * d * d, es), M, d, d, ep, s));
+    ep = epi0();
+    ep.bias = h->w.xkv_b + (size_t)l * 2 * d;
+    ep.out = kv; ep.ldo = 2 * d;
+    DIT_HIP(linear(h, EPI_BIAS_DT, ctx, d, woff(h->w.xkv_w, (size_t)l * 2 * d * d, es), 2 * rows,
+                   2 * d, d, ep, s));
+    DIT_HIP(launch_cross_attention2(qkv, kv, rows, Tt, h->heads, h->dh, h->dtype, O, s));
+    ep = epi0();
+    ep.bias = h->w.xo_b + (size_t)l * d;
+    ep.out = X; ep.ldo = d; ep.T = Tt;
+    DIT_HIP(linear(h, EPI_GATED, O, d, woff(h->w.xo_w, (size_t)l * d * d, es), M, d, d, ep, s));
+    li = 2;
+  }
+
+  DIT_HIP(launch_ln_modulate(X, M, Tt, d, lnp, 0, 2 * d * li, 2 * d * li + d, h->eps, Hb, h->dtype,
+                             s));
+  ep = epi0();
+  ep.bias = h->w.fc1_b + (size_t)l * h->hid;
+  ep.out = G; ep.ldo = h->hid;
+  DIT_HIP(linear(h, EPI_GELU, Hb, d, woff(h->w.fc1_w, (size_t)l * h->hid * d, es), M, h->hid, d,
+                 ep, s));
+  ep = epi0();
+  ep.bias = h->w.fc2_b + (size_t)l * d;
+  ep.out = X; ep.ldo = d; ep.T = Tt;
+  DIT_HIP(linear(h, EPI_GATED, G, h->hid, woff(h->w.fc2_w, (size_t)l * d * h->hid, es), M, d,
+                 h->hid, ep, s));
+  return DIT_OK;
+}
+
 // Trunk of `rows` rows.  Row r reads latent/time/pooled row r % src_rows; rows
 // r >= null_from take the null label.  Leaves the decoder output in ws Y.
 int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_t* y,
               const float* pooled, int rows, int src_rows, int null_from, void* ws,
               const WsLayout& L, const dit_taps* taps, hipStream_t s) {
-  const int d = h->d, T = h->T, M = rows * T;
+  const int d = h->d, T = h->T, Tt = h->Tt, M = rows * Tt;
+  const bool ada = h->cond == DIT_COND_ADALN_ZERO;
   float* e = at<float>(ws, L.e);
   float* th = at<float>(ws, L.th);
   float* c = at<float>(ws, L.c);
@@ -246,8 +313,21 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
       DIT_HIP(launch_gemm_valu(EPI_BIAS_F32, A_PLAIN, a, h->w.pool_w, h->dtype, rows, d,
                                h->cond_dim, ep, s));
     }
-    DIT_HIP(launch_cond_finish(c, rows, d, h->ncls > 0 ? h->w.y_table : nullptr, y, src_rows,
-                               null_from, h->ncls, pp, sc, h->dtype, s));
+    if (ada)
+      DIT_HIP(launch_cond_finish(c, rows, d, h->ncls > 0 ? h->w.y_table : nullptr, y, src_rows,
+                                 null_from, h->ncls, pp, sc, h->dtype, s));
+  } else if (!ada) {
+    // time embedding alone (the class row becomes a token of its own)
+    DIT_HIP(launch_timestep_embed(t, rows, src_rows, h->freq, e, s));
+    a.ptr = e; a.lda = h->freq; a.a_dtype = 0; a.src_rows = rows;
+    ep = epi0();
+    ep.bias = h->w.t1_b; ep.out = th; ep.ldo = d;
+    DIT_HIP(launch_gemm_valu(EPI_BIAS_SILU, A_PLAIN, a, h->w.t1_w, h->dtype, rows, d, h->freq,
+                             ep, s));
+    a.ptr = th; a.lda = d;
+    ep = epi0();
+    ep.bias = h->w.t2_b; ep.out = c; ep.ldo = d;
+    DIT_HIP(launch_gemm_valu(EPI_BIAS_F32, A_PLAIN, a, h->w.t2_w, h->dtype, rows, d, d, ep, s));
   } else {
     DIT_HIP(launch_timestep_embed(t, rows, src_rows, h->freq, e, s));
     if (h->cond_dim > 0) {
@@ -272,27 +352,37 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
     DIT_HIP(launch_gemm_valu(EPI_COND, A_PLAIN, a, h->w.t2_w, h->dtype, rows, d, d, ep, s));
   }
 
-  // All modulation vectors (every block and the final layer) in one GEMM.
-  ep = epi0();
-  ep.bias = h->w.ada_b; ep.out = mod; ep.ldo = h->mod_stride;
-  DIT_HIP(linear(h, EPI_BIAS_F32, sc, d, h->w.ada_w, rows, h->mod_stride, d, ep, s));
+  if (ada) {
+    // All modulation vectors (every block and the final layer) in one GEMM.
+    ep = epi0();
+    ep.bias = h->w.ada_b; ep.out = mod; ep.ldo = h->mod_stride;
+    DIT_HIP(linear(h, EPI_BIAS_F32, sc, d, h->w.ada_w, rows, h->mod_stride, d, ep, s));
+  } else {
+    // The time and class embeddings as two tokens after each row's patch
+    // tokens (in-context) or as each row's two context tokens.
+    const bool in_ctx = h->cond == DIT_COND_IN_CONTEXT;
+    DIT_HIP(launch_cond_tokens(c, rows, d, h->w.y_table, y, src_rows, null_from, h->ncls,
+                               in_ctx ? 0 : 1, in_ctx ? (void*)X : at<void>(ws, L.ctx), T,
+                               h->dtype, s));
+  }
 
   // Patchify gather + patch embedding + bias + 2-D position embedding (from a
   // table of the T x d embedding, computed once per call).
   memset(&a, 0, sizeof a);
   a.ptr = x_t; a.a_dtype = h->dtype; a.src_rows = src_rows; a.g = h->gin;
   ep = epi0();
-  ep.bias = h->w.pe_b; ep.out = X; ep.ldo = d; ep.T = T;
+  ep.bias = h->w.pe_b; ep.out = X; ep.ldo = d; ep.T = T; ep.out_skip = Tt - T;
   if (!h->cfg.rope3d) {
     float* pe = at<float>(ws, L.pe);
     DIT_HIP(launch_pos_embed_table(h->gh, h->gw, d, pe, s));
     ep.pe_tab = pe;
   }
-  DIT_HIP(launch_gemm_valu(EPI_PATCH, A_PATCH, a, h->w.pe_w, h->dtype, M, d, h->kin, ep, s));
+  DIT_HIP(launch_gemm_valu(EPI_PATCH, A_PATCH, a, h->w.pe_w, h->dtype, rows * T, d, h->kin, ep,
+                           s));
 
   if (taps) {
     if (taps->c) DIT_HIP(hipMemcpyAsync(taps->c, c, (size_t)rows * d * 4, hipMemcpyDeviceToDevice, s));
-    if (taps->mod)
+    if (taps->mod && ada)
       DIT_HIP(hipMemcpyAsync(taps->mod, mod, (size_t)rows * h->mod_stride * 4,
                              hipMemcpyDeviceToDevice, s));
     if (taps->x_embed)
@@ -306,8 +396,31 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
   // memory-bound kernels (LN, attention) run beside another group's GEMMs.
   // Each group uses its own rows of every workspace region.
   const int fb = 6 * d * h->N;
+  char* kv_base = at<char>(ws, L.kv);
+  const char* ctx_base = at<char>(ws, L.ctx);
+  // Final layer: LN + (adaLN modulation or the learned affine) + decoder.
+  auto final_layer = [&](float* Xg, const float* modg, int Mg, void* Hg, float* Yg,
+                         hipStream_t st) -> int {
+    if (ada)
+      DIT_HIP(launch_ln_modulate(Xg, Mg, Tt, d, modg, h->mod_stride, fb, fb + d, h->eps, Hg,
+                                 h->dtype, st));
+    else
+      DIT_HIP(launch_ln_modulate(Xg, Mg, Tt, d, h->w.final_ln, 0, 0, d, h->eps, Hg, h->dtype, st));
+    EpiParams ef = epi0();
+    ef.bias = h->w.out_b; ef.out = Yg; ef.ldo = h->kout;
+    DIT_HIP(linear(h, EPI_BIAS_F32, Hg, d, h->w.out_w, Mg, h->kout, d, ef, st));
+    return DIT_OK;
+  };
+  auto one_block = [&](int l, int r0, int nr, float* Xg, const float* modg, const WsLayout& Lg,
+                       hipStream_t st) -> int {
+    if (ada) return run_block(h, l, nr, Xg, modg, h->mod_stride, 6 * d * l, ws, Lg, nullptr,
+                              nullptr, st);
+    const size_t es = h->es;
+    return run_block_variant(h, l, nr, Xg, ctx_base + (size_t)r0 * 2 * d * es,
+                             kv_base + (size_t)r0 * 4 * d * es, ws, Lg, st);
+  };
   auto blocks_and_final = [&](int r0, int nr, hipStream_t st) -> int {
-    const size_t m0 = (size_t)r0 * T, es = h->es;
+    const size_t m0 = (size_t)r0 * Tt, es = h->es;
     WsLayout Lh = L;
     Lh.H += m0 * d * es;
     Lh.qkv += m0 * 3 * d * es;
@@ -316,17 +429,10 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
     float* Xh = X + m0 * d;
     const float* modh = mod + (size_t)r0 * h->mod_stride;
     for (int l = 0; l < h->N; ++l) {
-      int rc = run_block(h, l, nr, Xh, modh, h->mod_stride, 6 * d * l, ws, Lh, nullptr, nullptr, st);
+      int rc = one_block(l, r0, nr, Xh, modh, Lh, st);
       if (rc) return rc;
     }
-    const int Mh = nr * T;
-    void* Hh = at<void>(ws, Lh.H);
-    DIT_HIP(launch_ln_modulate(Xh, Mh, T, d, modh, h->mod_stride, fb, fb + d, h->eps, Hh, h->dtype,
-                               st));
-    EpiParams ef = epi0();
-    ef.bias = h->w.out_b; ef.out = Y + m0 * h->kout; ef.ldo = h->kout;
-    DIT_HIP(linear(h, EPI_BIAS_F32, Hh, d, h->w.out_w, Mh, h->kout, d, ef, st));
-    return DIT_OK;
+    return final_layer(Xh, modh, nr * Tt, at<void>(ws, Lh.H), Y + m0 * h->kout, st);
   };
 
   const int parts = rows < DIT_SPLIT ? rows : DIT_SPLIT;
@@ -353,23 +459,23 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
   }
 
   for (int l = 0; l < h->N; ++l) {
-    int rc = run_block(h, l, rows, X, mod, h->mod_stride, 6 * d * l, ws, L, nullptr, nullptr, s);
+    int rc = one_block(l, 0, rows, X, mod, L, s);
     if (rc) return rc;
     if (taps && taps->x_blocks)
       DIT_HIP(hipMemcpyAsync(taps->x_blocks + (size_t)l * M * d, X, (size_t)M * d * 4,
                              hipMemcpyDeviceToDevice, s));
   }
-  DIT_HIP(launch_ln_modulate(X, M, T, d, mod, h->mod_stride, fb, fb + d, h->eps, Hb, h->dtype, s));
-  ep = epi0();
-  ep.bias = h->w.out_b; ep.out = Y; ep.ldo = h->kout;
-  DIT_HIP(linear(h, EPI_BIAS_F32, Hb, d, h->w.out_w, M, h->kout, d, ep, s));
+  {
+    int rc = final_layer(X, mod, M, Hb, Y, s);
+    if (rc) return rc;
+  }
   if (taps && taps->y_final)
     DIT_HIP(hipMemcpyAsync(taps->y_final, Y, (size_t)M * h->kout * 4, hipMemcpyDeviceToDevice, s));
   return DIT_OK;
 }
 
 int check_rows(const dit_handle* h, int rows) {
-  if ((int64_t)rows * h->T > (1LL << 30)) return fail(DIT_EINVAL, "rows * T too large");
+  if ((int64_t)rows * h->Tt > (1LL << 30)) return fail(DIT_EINVAL, "rows * T too large");
   if ((int64_t)rows * h->heads > 65535)
     return fail(DIT_EUNSUPPORTED, "rows * heads > 65535 (attention grid limit)");
   return DIT_OK;
@@ -404,7 +510,7 @@ int forward_impl(dit_handle* h, const void* x_t, const float* t, const int32_t* 
   hipStream_t s = (hipStream_t)stream;
   rc = run_trunk(h, x_t, t, y, pooled, B, B, B, ws, L, taps, s);
   if (rc) return rc;
-  DIT_HIP(launch_unpatchify(at<float>(ws, L.Y), B, 0, h->gout, h->cfg.out_channels, 0, 0.0f, 0,
+  DIT_HIP(launch_unpatchify(at<float>(ws, L.Y), B, 0, h->gouty, h->cfg.out_channels, 0, 0.0f, 0,
                             out, s));
   return ok();
 }
@@ -426,7 +532,7 @@ int cfg_forward_impl(dit_handle* h, const void* x_t, const float* t, const int32
   hipStream_t s = (hipStream_t)stream;
   rc = run_trunk(h, x_t, t, y, nullptr, 2 * Bh, Bh, Bh, ws, L, taps, s);
   if (rc) return rc;
-  DIT_HIP(launch_unpatchify(at<float>(ws, L.Y), Bh, Bh, h->gout, h->cfg.out_channels, guided,
+  DIT_HIP(launch_unpatchify(at<float>(ws, L.Y), Bh, Bh, h->gouty, h->cfg.out_channels, guided,
                             scale, 1, out, s));
   return ok();
 }
@@ -680,13 +786,26 @@ int dit_create(const dit_config* cfg, const dit_weights* w, dit_handle** out) {
     return fail(DIT_EUNSUPPORTED, "3-D RoPE needs head dim divisible by 6 with even thirds");
   if (c.qk_norm != 0 && c.qk_norm != 1) return fail(DIT_EINVAL, "qk_norm must be 0 or 1");
   if (c.rope3d != 0 && c.rope3d != 1) return fail(DIT_EINVAL, "rope3d must be 0 or 1");
-  if (!w->pe_w || !w->pe_b || !w->t1_w || !w->t1_b || !w->t2_w || !w->t2_b || !w->ada_w ||
-      !w->ada_b || !w->qkv_w || !w->qkv_b || !w->o_w || !w->o_b || !w->fc1_w || !w->fc1_b ||
-      !w->fc2_w || !w->fc2_b || !w->out_w || !w->out_b)
+  if (c.conditioning < DIT_COND_ADALN_ZERO || c.conditioning > DIT_COND_CROSS_ATTN)
+    return fail(DIT_EINVAL, "unknown conditioning design %d", c.conditioning);
+  const bool ada = c.conditioning == DIT_COND_ADALN_ZERO;
+  const bool xattn = c.conditioning == DIT_COND_CROSS_ATTN;
+  if (!ada && (c.num_classes <= 0 || c.cond_dim > 0))
+    return fail(DIT_EUNSUPPORTED,
+                "the in-context and cross-attention designs need a class table and no pooled "
+                "conditioning");
+  if (!w->pe_w || !w->pe_b || !w->t1_w || !w->t1_b || !w->t2_w || !w->t2_b || !w->qkv_w ||
+      !w->qkv_b || !w->o_w || !w->o_b || !w->fc1_w || !w->fc1_b || !w->fc2_w || !w->fc2_b ||
+      !w->out_w || !w->out_b)
     return fail(DIT_EINVAL, "a required weight pointer is NULL");
+  if (ada && (!w->ada_w || !w->ada_b)) return fail(DIT_EINVAL, "ada_w/ada_b NULL");
+  if (!ada && (!w->ln_p || !w->final_ln)) return fail(DIT_EINVAL, "ln_p/final_ln NULL");
+  if (xattn && (!w->xq_w || !w->xq_b || !w->xkv_w || !w->xkv_b || !w->xo_w || !w->xo_b))
+    return fail(DIT_EINVAL, "a cross-attention weight pointer is NULL");
   if (c.num_classes > 0 && !w->y_table) return fail(DIT_EINVAL, "y_table is NULL");
   if (c.cond_dim > 0 && (!w->pool_w || !w->pool_b)) return fail(DIT_EINVAL, "pool_w/pool_b NULL");
-  const void* ptrs[] = {w->qkv_w, w->o_w, w->fc1_w, w->fc2_w, w->ada_w};
+  const void* ptrs[] = {w->qkv_w, w->o_w, w->fc1_w, w->fc2_w, w->ada_w, w->xq_w, w->xkv_w,
+                        w->xo_w};
   for (const void* p : ptrs)
     if ((uintptr_t)p & 15) return fail(DIT_EINVAL, "GEMM weights must be 16-byte aligned");
   const int64_t T = (int64_t)gf * (c.height / c.patch) * (c.width / c.patch);
@@ -704,9 +823,14 @@ int dit_create(const dit_config* cfg, const dit_weights* w, dit_handle** out) {
   h->T = (int)T;
   h->kin = c.patch_t * c.patch * c.patch * c.in_channels;
   h->kout = c.patch_t * c.patch * c.patch * c.out_channels;
-  h->mod_stride = (6 * c.depth + 2) * c.hidden;
+  h->cond = c.conditioning;
+  h->Tt = h->T + (c.conditioning == DIT_COND_IN_CONTEXT ? 2 : 0);
+  h->nln = xattn ? 3 : 2;
+  h->mod_stride = ada ? (6 * c.depth + 2) * c.hidden : 0;
   h->gin = make_geom(c.in_channels, c.frames, c.height, c.width, c.patch, c.patch_t);
   h->gout = make_geom(c.out_channels, c.frames, c.height, c.width, c.patch, c.patch_t);
+  h->gouty = h->gout;
+  h->gouty.T = h->Tt;
   *out = h;
   return ok();
 }
@@ -830,6 +954,8 @@ int dit_block_forward(dit_handle* h, int layer, int B, const float* X_in, const 
   if (!X_in || !mod || !X_out) return fail(DIT_EINVAL, "X_in, mod and X_out must be non-NULL");
   if (layer < 0 || layer >= h->N) return fail(DIT_EINVAL, "layer %d out of range", layer);
   if (B <= 0) return fail(DIT_EINVAL, "B must be positive");
+  if (h->cond != DIT_COND_ADALN_ZERO)
+    return fail(DIT_EUNSUPPORTED, "dit_block_forward runs adaLN-Zero blocks only");
   WsLayout L;
   int rc = check_ws(h, B, ws, ws_bytes, &L);
   if (rc) return rc;
@@ -959,7 +1085,7 @@ int dit_sample(dit_handle* h, const dit_sampler* sp, float* x, const int32_t* y,
     a.tvec_rows = more ? B : 0;
     a.t_next = more ? (float)co[k + 1].model_t : 0.0f;
     a.n = n; a.S = (int64_t)h->gin.F * h->gin.H * h->gin.W;
-    a.C = C; a.Cout = Cout; a.g = h->gout;
+    a.C = C; a.Cout = Cout; a.g = h->gouty;
     a.null_off = B; a.guided = guided_channels; a.scale = scale;
     a.learned = Cout == 2 * C;
     DIT_HIP(launch_sampler_step(a, s));

@@ -436,3 +436,68 @@ hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, in
   }
   return hipGetLastError();
 }
+
+// ---------------------------------------------------------------------------
+// Cross-attention of every token over the two context tokens of its row (the
+// cross-attention conditioning design): per head, softmax over two scores.
+// One thread per (token, head); fp32 arithmetic.
+namespace {
+template <typename DT, int DH>
+__global__ __launch_bounds__(256) void cross_attn2_kernel(const DT* __restrict__ q,
+                                                          const DT* __restrict__ kv, int64_t n,
+                                                          int T, int heads,
+                                                          DT* __restrict__ o) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int h = (int)(idx % heads);
+  const int64_t m = idx / heads;
+  const int64_t b = m / T;
+  const int D = heads * DH;
+  const DT* qp = q + m * D + h * DH;
+  const DT* k0 = kv + (b * 2) * 2 * D + h * DH;
+  const DT* k1 = k0 + 2 * D;
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll 8
+  for (int i = 0; i < DH; ++i) {
+    const float a = to_f<DT>(qp[i]);
+    s0 = fmaf(a, to_f<DT>(k0[i]), s0);
+    s1 = fmaf(a, to_f<DT>(k1[i]), s1);
+  }
+  const float scale = 1.0f / sqrtf((float)DH);
+  s0 *= scale;
+  s1 *= scale;
+  const float mx = fmaxf(s0, s1);
+  const float e0 = expf(s0 - mx), e1 = expf(s1 - mx);
+  const float inv = 1.0f / (e0 + e1);
+  const float p0 = e0 * inv, p1 = e1 * inv;
+  const DT* v0 = k0 + D;
+  const DT* v1 = k1 + D;
+  DT* op = o + m * D + h * DH;
+#pragma unroll 8
+  for (int i = 0; i < DH; ++i)
+    op[i] = from_f<DT>(fmaf(p0, to_f<DT>(v0[i]), p1 * to_f<DT>(v1[i])));
+}
+
+template <typename DT>
+hipError_t cross2_dispatch(const void* q, const void* kv, int rows, int T, int heads, int dh,
+                           void* o, hipStream_t s) {
+  const int64_t n = (int64_t)rows * T * heads;
+  const int blocks = (int)((n + 255) / 256);
+  if (dh == 72)
+    cross_attn2_kernel<DT, 72><<<blocks, 256, 0, s>>>((const DT*)q, (const DT*)kv, n, T, heads,
+                                                     (DT*)o);
+  else if (dh == 64)
+    cross_attn2_kernel<DT, 64><<<blocks, 256, 0, s>>>((const DT*)q, (const DT*)kv, n, T, heads,
+                                                     (DT*)o);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_cross_attention2(const void* q, const void* kv, int rows, int T, int heads,
+                                   int dh, int dtype, void* o, hipStream_t s) {
+  if (rows <= 0 || T <= 0) return hipSuccess;
+  return dtype == 1 ? cross2_dispatch<bf16_t>(q, kv, rows, T, heads, dh, o, s)
+                    : cross2_dispatch<float>(q, kv, rows, T, heads, dh, o, s);
+}

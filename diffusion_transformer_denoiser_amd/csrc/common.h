@@ -71,9 +71,9 @@ enum EpiKind {
   EPI_BIAS_SILU = 1,    // out_f32[m, n] = SiLU(C + bias[n])                   (timestep MLP)
   EPI_COND = 2,         // c = C + bias (+ c_prev) (+ table[label]); writes c and SiLU(c) (dtype)
   EPI_BIAS_DT = 3,      // out_dtype[m, n] = C + bias[n]            (packed q | k | v)
-  EPI_GATED = 4,        // X[m, n] += gate[b, n] * (C + bias[n])                (fp32 residual)
+  EPI_GATED = 4,        // X[m, n] += gate[b, n] * (C + bias[n]) (fp32 residual; gate 1 if mod null)
   EPI_GELU = 5,         // out_dtype[m, n] = GELU_tanh(C + bias[n])
-  EPI_PATCH = 6,        // X[m, n] = C + bias[n] (+ pe_tab[m % T, n])
+  EPI_PATCH = 6,        // X[m + (m / T) out_skip, n] = C + bias[n] (+ pe_tab[m % T, n])
   EPI_SILU_DT = 7,      // out_dtype[m, n] = SiLU(C + bias[n])                  (timestep MLP)
 };
 
@@ -96,6 +96,8 @@ struct EpiParams {
   void* silu_out;       // SiLU(c) in the GEMM operand dtype
   // patch embedding position term: table [T, ldo] of the 2-D sin-cos embedding
   const float* pe_tab;
+  // patch embedding: rows of out skipped after every T rows (extra tokens of a row)
+  int out_skip;
 };
 
 // ---------------------------------------------------------------------------
@@ -115,6 +117,18 @@ hipError_t launch_cond_finish(float* c, int rows, int d, const float* table, con
                               void* sc, int dtype, hipStream_t s);
 hipError_t launch_patchify(const void* x, int B, const PatchGeom& g, int dtype, void* P,
                            hipStream_t s);
+// Conditioning tokens of the in-context and cross-attention designs: for trunk
+// row r, the time embedding temb[r] and the class embedding table[label(r)]
+// (label(r) as in launch_cond_finish; a label out of range gives NaN).
+// mode 0: X[r, T, :] = temb[r], X[r, T + 1, :] = class row (fp32 residual
+// stream, rows of T + 2 tokens); mode 1: ctx[r, 0, :], ctx[r, 1, :] in dtype.
+hipError_t launch_cond_tokens(const float* temb, int rows, int d, const float* table,
+                              const int32_t* labels, int label_rows, int null_from, int ncls,
+                              int mode, void* dst, int T, int dtype, hipStream_t s);
+// Cross-attention over two context tokens per row: q [rows * T, H * dh] and
+// kv [rows, 2, 2 * H * dh] (k | v of each token) in dtype; o [rows * T, H * dh].
+hipError_t launch_cross_attention2(const void* q, const void* kv, int rows, int T, int heads,
+                                   int dh, int dtype, void* o, hipStream_t s);
 hipError_t launch_unpatchify(const float* Y, int Bout, int Bh_offset, const PatchGeom& g,
                              int Cout, int guided, float scale, int guide, float* out,
                              hipStream_t s);

@@ -69,6 +69,46 @@ __global__ void cond_finish_kernel(float* __restrict__ c, int rows, int d,
   sc[idx] = from_f<DT>(silu_f(v));
 }
 
+// Conditioning tokens of the in-context and cross-attention designs: token 0
+// is the time embedding, token 1 the class row.  One thread per element.
+template <typename DT>
+__global__ void cond_tokens_kernel(const float* __restrict__ temb, int rows, int d,
+                                   const float* __restrict__ table,
+                                   const int32_t* __restrict__ labels, int label_rows,
+                                   int null_from, int ncls, int mode, void* __restrict__ dst,
+                                   int T) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)rows * 2 * d) return;
+  const int m = (int)(idx / (2 * d));
+  const int rem = (int)(idx - (int64_t)m * 2 * d);
+  const int which = rem / d, n = rem - which * d;
+  float v;
+  if (which == 0) {
+    v = temb[(int64_t)m * d + n];
+  } else {
+    const int lbl = (m >= null_from) ? ncls : labels[m % label_rows];
+    v = (lbl < 0 || lbl > ncls) ? __builtin_nanf("") : table[(int64_t)lbl * d + n];
+  }
+  if (mode == 0)
+    ((float*)dst)[((int64_t)m * (T + 2) + T + which) * d + n] = v;
+  else
+    ((DT*)dst)[((int64_t)m * 2 + which) * d + n] = from_f<DT>(v);
+}
+
+hipError_t launch_cond_tokens(const float* temb, int rows, int d, const float* table,
+                              const int32_t* labels, int label_rows, int null_from, int ncls,
+                              int mode, void* dst, int T, int dtype, hipStream_t s) {
+  const int64_t n = (int64_t)rows * 2 * d;
+  const int blocks = (int)((n + 255) / 256);
+  if (dtype == 1)
+    cond_tokens_kernel<bf16_t><<<blocks, 256, 0, s>>>(temb, rows, d, table, labels, label_rows,
+                                                      null_from, ncls, mode, dst, T);
+  else
+    cond_tokens_kernel<float><<<blocks, 256, 0, s>>>(temb, rows, d, table, labels, label_rows,
+                                                     null_from, ncls, mode, dst, T);
+  return hipGetLastError();
+}
+
 hipError_t launch_cond_finish(float* c, int rows, int d, const float* table, const int32_t* labels,
                               int label_rows, int null_from, int ncls, const float* pooled,
                               void* sc, int dtype, hipStream_t s) {

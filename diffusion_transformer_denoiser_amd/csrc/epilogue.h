@@ -38,7 +38,7 @@ __device__ __forceinline__ void epi_apply(const EpiParams& ep, int m, int n, flo
     ((DT*)ep.out)[(int64_t)m * ep.ldo + n] = from_f<DT>(v);
   } else if constexpr (EPI == EPI_GATED) {
     int b = m / ep.T;
-    float g = ep.mod[(int64_t)b * ep.mod_stride + ep.gate_off + n];
+    float g = ep.mod ? ep.mod[(int64_t)b * ep.mod_stride + ep.gate_off + n] : 1.0f;
     float* X = (float*)ep.out;
     int64_t o = (int64_t)m * ep.ldo + n;
     X[o] = X[o] + g * v;
@@ -46,7 +46,8 @@ __device__ __forceinline__ void epi_apply(const EpiParams& ep, int m, int n, flo
     ((DT*)ep.out)[(int64_t)m * ep.ldo + n] = from_f<DT>(gelu_tanh_f(v));
   } else if constexpr (EPI == EPI_PATCH) {
     if (ep.pe_tab) v += ep.pe_tab[(int64_t)(m % ep.T) * ep.ldo + n];
-    ((float*)ep.out)[(int64_t)m * ep.ldo + n] = v;
+    const int64_t orow = m + (int64_t)(m / ep.T) * ep.out_skip;
+    ((float*)ep.out)[orow * ep.ldo + n] = v;
   } else if constexpr (EPI == EPI_SILU_DT) {
     ((DT*)ep.out)[(int64_t)m * ep.ldo + n] = from_f<DT>(silu_f(v));
   }

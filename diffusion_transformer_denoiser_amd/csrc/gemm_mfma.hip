@@ -264,16 +264,19 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
     // In-place read-modify-write of the fp32 residual.  The compiler must
     // assume the stores alias later loads, and one counter tracks both, so
     // loads interleaved with stores would each wait a full round trip.  Whole
-    // tiles whose 32-row blocks each lie in one batch row (T % 32 == 0) run a
-    // two-deep pipeline over batches of 4 rows x TN columns per lane instead:
-    // batch q+1 is loaded before batch q is stored.
-    if (full && ep.T % 32 == 0) {
+    // tiles whose 32-row blocks each lie in one batch row (T % 32 == 0), or
+    // that have no gate (plain residual add), run a two-deep pipeline over
+    // batches of 4 rows x TN columns per lane instead: batch q+1 is loaded
+    // before batch q is stored.
+    if (full && (!ep.mod || ep.T % 32 == 0)) {
       float gv[TM][TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const float* g = ep.mod + (int64_t)((mrow + i * 32) / ep.T) * ep.mod_stride + ep.gate_off;
+        const float* g = ep.mod ? ep.mod + (int64_t)((mrow + i * 32) / ep.T) * ep.mod_stride +
+                                      ep.gate_off
+                                : nullptr;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) gv[i][j] = g[ncol + j * 32];
+        for (int j = 0; j < TN; ++j) gv[i][j] = g ? g[ncol + j * 32] : 1.0f;
       }
       float* xt = (float*)ep.out + (int64_t)mrow * ep.ldo + ncol;
       constexpr int NQ = TM * 4;   // batch q: block q / 4, register group q % 4
@@ -372,7 +375,8 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
           ((bf16_t*)ep.out)[o] = f2bf(silu_f(v));
         } else {
           static_assert(EPI == EPI_GATED, "epilogue");
-          const float g = ep.mod[(int64_t)(m / ep.T) * ep.mod_stride + ep.gate_off + n];
+          const float g =
+              ep.mod ? ep.mod[(int64_t)(m / ep.T) * ep.mod_stride + ep.gate_off + n] : 1.0f;
           float* X = (float*)ep.out;
           X[o] = X[o] + g * v;
         }

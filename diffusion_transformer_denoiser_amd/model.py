@@ -21,7 +21,7 @@ import torch
 from . import _lib
 
 GEMM_WEIGHTS = ("pe_w", "t1_w", "t2_w", "pool_w", "ada_w", "qkv_w", "o_w", "fc1_w", "fc2_w",
-                "out_w")
+                "out_w", "xq_w", "xkv_w", "xo_w")
 
 
 def torch_dtype(code: int) -> torch.dtype:
@@ -42,7 +42,8 @@ def config_struct(cfg: dict) -> _lib.DitConfig:
         width=cfg["W"], patch=cfg["p"], patch_t=cfg["pt"], hidden=cfg["d"], depth=cfg["N"],
         heads=cfg["heads"], mlp_hidden=cfg["mlp_hidden"], num_classes=cfg["num_classes"],
         cond_dim=cfg["cond_dim"], freq_dim=cfg["freq_dim"], qk_norm=cfg["qk_norm"],
-        rope3d=cfg["rope3d"], dtype=cfg["dtype"], ln_eps=cfg["ln_eps"])
+        rope3d=cfg["rope3d"], dtype=cfg["dtype"], ln_eps=cfg["ln_eps"],
+        conditioning=cfg.get("conditioning", _lib.DIT_COND_ADALN_ZERO))
 
 
 def upload(a, dtype: torch.dtype, device) -> torch.Tensor:
@@ -123,6 +124,8 @@ class DiT:
         self.handle = h
         self._ws = None
         self.T = (cfg["F"] // cfg["pt"]) * (cfg["H"] // cfg["p"]) * (cfg["W"] // cfg["p"])
+        # tokens per trunk row: the in-context design appends two
+        self.Tt = self.T + (2 if cfg.get("conditioning", 0) == _lib.DIT_COND_IN_CONTEXT else 0)
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -150,11 +153,12 @@ class DiT:
         return (rows, c["Cout"], c["H"], c["W"])
 
     def make_taps(self, rows: int) -> dict:
-        c, M = self.cfg, rows * self.T
+        c, M = self.cfg, rows * self.Tt
         kout = c["pt"] * c["p"] * c["p"] * c["Cout"]
         f = dict(device=self.device, dtype=torch.float32)
         return dict(c=torch.empty(rows, c["d"], **f),
-                    mod=torch.empty(rows, (6 * c["N"] + 2) * c["d"], **f),
+                    mod=(torch.empty(rows, (6 * c["N"] + 2) * c["d"], **f)
+                         if c.get("conditioning", 0) == _lib.DIT_COND_ADALN_ZERO else None),
                     x_embed=torch.empty(M, c["d"], **f),
                     x_blocks=torch.empty(c["N"], M, c["d"], **f),
                     y_final=torch.empty(M, kout, **f))

@@ -79,6 +79,26 @@ extern "C" {
 #define DIT_F32  0
 #define DIT_BF16 1
 
+/* Conditioning designs (itwiki "확산 트랜스포머", Conditioning methods table):
+ *   DIT_COND_ADALN_ZERO   adaLN-Zero blocks (regressed shift / scale / gate)
+ *   DIT_COND_IN_CONTEXT   the time and class embeddings are two extra tokens
+ *                         after the T patch tokens (T + 2 tokens through the
+ *                         blocks); standard pre-LN blocks
+ *                             x <- x + Attn(LN1(x)),  x <- x + FFN(LN2(x))
+ *   DIT_COND_CROSS_ATTN   the two embeddings form a length-2 context that a
+ *                         multi-head cross-attention layer after each
+ *                         self-attention reads (cointeeth DiT article, block
+ *                         description):
+ *                             x <- x + Attn(LN1(x)),  x <- x + XAttn(LN2(x), ctx),
+ *                             x <- x + FFN(LN3(x))
+ * In the last two, every LayerNorm has a learned affine written
+ * LN(x)(1 + g) + b, residual adds have no gate, and the final layer is
+ * LN (affine) + the linear decoder on the patch tokens.  Both need a class
+ * table and no pooled conditioning. */
+#define DIT_COND_ADALN_ZERO 0
+#define DIT_COND_IN_CONTEXT 1
+#define DIT_COND_CROSS_ATTN 2
+
 /* Model configuration.  Supported: hidden % 128 == 0, hidden <= 2048,
  * head dim hidden/heads in {64, 72}, mlp_hidden % 64 == 0, freq_dim even.
  * rope3d needs head dim divisible by 6 with an even third (72 works);
@@ -103,6 +123,7 @@ typedef struct dit_config {
   int rope3d;        /* 1: 3-D rotary embedding on q,k; no additive position embedding */
   int dtype;         /* DIT_F32 or DIT_BF16: GEMM operand / activation dtype */
   float ln_eps;      /* LayerNorm epsilon (1e-6) */
+  int conditioning;  /* DIT_COND_* */
 } dit_config;
 
 /* Caller-owned device pointers.  "W" = model dtype, "f32" = float.
@@ -132,16 +153,30 @@ typedef struct dit_weights {
   const float* fc2_b;   /* f32 [N, d] */
   const void*  out_w;   /* W   [Kout, d]  linear decoder */
   const float* out_b;   /* f32 [Kout] */
+  /* in-context / cross-attention designs only (NULL otherwise; ada_w and
+   * ada_b are then NULL): */
+  const float* ln_p;     /* f32 [N, nLN, 2, d] (b, g) of each block LayerNorm; nLN = 2
+                            in-context, 3 cross-attention (LN1, LN2, LN3) */
+  const float* final_ln; /* f32 [2, d] (b, g) of the final LayerNorm */
+  /* cross-attention design only: */
+  const void*  xq_w;    /* W   [N, d, d]   query projection */
+  const float* xq_b;    /* f32 [N, d] */
+  const void*  xkv_w;   /* W   [N, 2d, d]  key | value projection of the context tokens */
+  const float* xkv_b;   /* f32 [N, 2d] */
+  const void*  xo_w;    /* W   [N, d, d]   output projection */
+  const float* xo_b;    /* f32 [N, d] */
 } dit_weights;
 
 typedef struct dit_handle dit_handle;
 
 /* Optional intermediate outputs of the trunk (device pointers, any may be
- * NULL).  M = trunk rows * T. */
+ * NULL).  M = trunk rows * Tt, Tt = T + 2 for the in-context design, else T. */
 typedef struct dit_taps {
-  float* c;         /* [rows, d]            conditioning vector */
-  float* mod;       /* [rows, (6N + 2) d]   all modulation vectors */
-  float* x_embed;   /* [M, d]               tokens after patch + position embedding */
+  float* c;         /* [rows, d]            conditioning vector (the time embedding in
+                                            the in-context / cross-attention designs) */
+  float* mod;       /* [rows, (6N + 2) d]   all modulation vectors (adaLN-Zero only) */
+  float* x_embed;   /* [M, d]               tokens after patch + position embedding
+                                            (and the two conditioning tokens) */
   float* x_blocks;  /* [N, M, d]            residual stream after each block */
   float* y_final;   /* [M, Kout]            decoder output before unpatchify */
 } dit_taps;
@@ -222,7 +257,8 @@ int dit_linear(int epilogue, const void* A, const void* W, const float* bias, in
                int K, int dtype, void* out, const float* gate, int gate_stride, int T,
                void* stream);
 
-/* One block, teacher-forced: X_out = block_l(X_in) with the given modulation
+/* One adaLN-Zero block (DIT_EUNSUPPORTED for the other designs),
+ * teacher-forced: X_out = block_l(X_in) with the given modulation
  * vectors mod [B, 6d] (b1, g1, a1, b2, g2, a2).  X_in, X_out: [B*T, d] fp32
  * (may alias).  o_branch / f_branch (fp32 [B*T, d], may be NULL) receive the
  * attention and FFN branches before their gates.  ws as for dit_forward with

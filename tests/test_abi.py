@@ -40,15 +40,15 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_config_struct_size_matches_header():
-    # 17 ints + 1 float
-    assert C.sizeof(_lib.DitConfig) == 18 * 4
-    assert C.sizeof(_lib.DitWeights) == 21 * C.sizeof(C.c_void_p)
+    # 17 ints + 1 float + 1 int
+    assert C.sizeof(_lib.DitConfig) == 19 * 4
+    assert C.sizeof(_lib.DitWeights) == 29 * C.sizeof(C.c_void_p)
 
 
 def _cfg(**kw):
     base = dict(in_channels=4, out_channels=8, frames=1, height=32, width=32, patch=2, patch_t=1,
                 hidden=1152, depth=2, heads=16, mlp_hidden=4608, num_classes=1000, cond_dim=0,
-                freq_dim=256, qk_norm=0, rope3d=0, dtype=1, ln_eps=1e-6)
+                freq_dim=256, qk_norm=0, rope3d=0, dtype=1, ln_eps=1e-6, conditioning=0)
     base.update(kw)
     return _lib.DitConfig(**base)
 
@@ -80,11 +80,35 @@ def _create(cfg, w):
     (dict(frames=4), _lib.DIT_EUNSUPPORTED),       # 2-D PE with several frames
     (dict(rope3d=1, hidden=1024), _lib.DIT_EUNSUPPORTED),  # RoPE thirds of dh 64
     (dict(ln_eps=0.0), _lib.DIT_EINVAL),
+    (dict(conditioning=3), _lib.DIT_EINVAL),
+    (dict(conditioning=1, num_classes=0), _lib.DIT_EUNSUPPORTED),   # needs a class table
+    (dict(conditioning=2, cond_dim=4096), _lib.DIT_EUNSUPPORTED),   # no pooled conditioning
 ])
 def test_create_rejects_bad_configs(kw, code):
     rc, h = _create(_cfg(**kw), _weights())
     assert rc == code and not h.value
     assert _lib.load().dit_last_error_message()
+
+
+@needs_lib
+def test_conditioning_designs_check_their_weights():
+    lib = _lib.load()
+    # the two other designs need no adaLN weights, but their LayerNorm affines
+    rc, h = _create(_cfg(conditioning=1), _weights(ada_w=1, ada_b=1))
+    assert rc == _lib.DIT_OK
+    p = C.c_void_p(0x200000)
+    need = C.c_size_t()
+    assert lib.dit_workspace_size(h, 4, C.byref(need)) == 0
+    assert lib.dit_block_forward(h, 0, 4, p, p, p, None, None, p, need.value,
+                                 None) == _lib.DIT_EUNSUPPORTED
+    lib.dit_destroy(h)
+    rc, _ = _create(_cfg(conditioning=1), _weights(ln_p=1))
+    assert rc == _lib.DIT_EINVAL
+    rc, _ = _create(_cfg(conditioning=2), _weights(xkv_w=1))
+    assert rc == _lib.DIT_EINVAL
+    rc, h = _create(_cfg(conditioning=0), _weights(ln_p=1, final_ln=1, xq_w=1))
+    assert rc == _lib.DIT_OK
+    lib.dit_destroy(h)
 
 
 @needs_lib
