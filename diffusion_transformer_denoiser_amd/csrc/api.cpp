@@ -112,7 +112,8 @@ WsLayout ws_layout(const dit_handle* h, int rows) {
   L.pe = take(h->cfg.rope3d ? 0 : (size_t)h->T * h->d * 4);  // 2-D position table
   L.mod = take(R * h->mod_stride * 4);                        // 0 without adaLN
   L.ctx = take(h->cond == DIT_COND_CROSS_ATTN ? R * 2 * h->d * es : 0);      // context tokens
-  L.kv = take(h->cond == DIT_COND_CROSS_ATTN ? R * 2 * 2 * h->d * es : 0);   // their k | v
+  // k | v of the context tokens for every block: [rows, 2, N, 2d]
+  L.kv = take(h->cond == DIT_COND_CROSS_ATTN ? R * 2 * h->N * 2 * h->d * es : 0);
   L.X = take(M * h->d * 4);
   L.H = take(M * h->d * es);
   L.qkv = take(M * 3 * h->d * es);
@@ -216,9 +217,10 @@ int run_block(const dit_handle* h, int l, int rows, float* X, const float* mod, 
 // One block of the in-context or cross-attention design on X [rows * Tt, d]
 // (fp32, in place).  Each LayerNorm's affine (b, g) is applied as a modulation
 // that is the same for every row (row stride 0); residual adds have no gate.
-// kv: this row group's context keys | values [rows, 2, 2d] (cross-attention).
-int run_block_variant(const dit_handle* h, int l, int rows, float* X, const void* ctx, void* kv,
-                      void* ws, const WsLayout& L, hipStream_t s) {
+// kv: block l's context keys | values of this row group's first row, rows of
+// stride N * 2d elements (cross-attention).
+int run_block_variant(const dit_handle* h, int l, int rows, float* X, const void* kv, void* ws,
+                      const WsLayout& L, hipStream_t s) {
   const int d = h->d, Tt = h->Tt, M = rows * Tt, es = h->es;
   void* Hb = at<void>(ws, L.H);
   void* O = at<void>(ws, L.o);
@@ -245,12 +247,8 @@ int run_block_variant(const dit_handle* h, int l, int rows, float* X, const void
     ep.bias = h->w.xq_b + (size_t)l * d;
     ep.out = qkv; ep.ldo = d;
     DIT_HIP(linear(h, EPI_BIAS_DT, Hb, d, woff(h->w.xq_w, (size_t)l * d * d, es), M, d, d, ep, s));
-    ep = epi0();
-    ep.bias = h->w.xkv_b + (size_t)l * 2 * d;
-    ep.out = kv; ep.ldo = 2 * d;
-    DIT_HIP(linear(h, EPI_BIAS_DT, ctx, d, woff(h->w.xkv_w, (size_t)l * 2 * d * d, es), 2 * rows,
-                   2 * d, d, ep, s));
-    DIT_HIP(launch_cross_attention2(qkv, kv, rows, Tt, h->heads, h->dh, h->dtype, O, s));
+    DIT_HIP(launch_cross_attention2(qkv, kv, (int64_t)h->N * 2 * d, rows, Tt, h->heads, h->dh,
+                                    h->dtype, O, s));
     ep = epi0();
     ep.bias = h->w.xo_b + (size_t)l * d;
     ep.out = X; ep.ldo = d; ep.T = Tt;
@@ -364,6 +362,14 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
     DIT_HIP(launch_cond_tokens(c, rows, d, h->w.y_table, y, src_rows, null_from, h->ncls,
                                in_ctx ? 0 : 1, in_ctx ? (void*)X : at<void>(ws, L.ctx), T,
                                h->dtype, s));
+    if (!in_ctx) {
+      // keys | values of the context tokens for all blocks in one GEMM (they
+      // depend on the conditioning only): [rows * 2, N * 2d]
+      ep = epi0();
+      ep.bias = h->w.xkv_b; ep.out = at<void>(ws, L.kv); ep.ldo = h->N * 2 * d;
+      DIT_HIP(linear(h, EPI_BIAS_DT, at<void>(ws, L.ctx), d, h->w.xkv_w, 2 * rows, h->N * 2 * d, d,
+                     ep, s));
+    }
   }
 
   // Patchify gather + patch embedding + bias + 2-D position embedding (from a
@@ -396,8 +402,7 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
   // memory-bound kernels (LN, attention) run beside another group's GEMMs.
   // Each group uses its own rows of every workspace region.
   const int fb = 6 * d * h->N;
-  char* kv_base = at<char>(ws, L.kv);
-  const char* ctx_base = at<char>(ws, L.ctx);
+  const char* kv_base = at<char>(ws, L.kv);
   // Final layer: LN + (adaLN modulation or the learned affine) + decoder.
   auto final_layer = [&](float* Xg, const float* modg, int Mg, void* Hg, float* Yg,
                          hipStream_t st) -> int {
@@ -416,8 +421,9 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
     if (ada) return run_block(h, l, nr, Xg, modg, h->mod_stride, 6 * d * l, ws, Lg, nullptr,
                               nullptr, st);
     const size_t es = h->es;
-    return run_block_variant(h, l, nr, Xg, ctx_base + (size_t)r0 * 2 * d * es,
-                             kv_base + (size_t)r0 * 4 * d * es, ws, Lg, st);
+    return run_block_variant(h, l, nr, Xg,
+                             kv_base + ((size_t)r0 * 2 * h->N * 2 * d + (size_t)l * 2 * d) * es,
+                             ws, Lg, st);
   };
   auto blocks_and_final = [&](int r0, int nr, hipStream_t st) -> int {
     const size_t m0 = (size_t)r0 * Tt, es = h->es;

@@ -414,16 +414,32 @@ hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, in
   if (B <= 0 || T <= 0) return hipSuccess;
   if (dtype == 1) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)dh);
-    // 4 waves (128 queries) per workgroup, two workgroups per CU (8 waves of
-    // 256 queries per workgroup measured slower at every length).
-    constexpr int NWV = 4;
-    dim3 grid((T + 32 * NWV - 1) / (32 * NWV), B * heads);
-    if (dh == 64)
-      attn_bf16_kernel<64, NWV><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o, heads, T, sl2);
-    else if (dh == 72)
-      attn_bf16_kernel<72, NWV><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o, heads, T, sl2);
-    else
-      return hipErrorInvalidValue;
+    // 4 waves (128 queries) per workgroup (8 waves of 256 queries measured
+    // slower at every length).  When T leaves a mostly empty last block of
+    // 128 queries (T = 258 with two conditioning tokens), 3 or 2 waves per
+    // workgroup waste fewer query slots: pick the fewest wasted, then the most
+    // waves.
+    int nwv = 4;
+    int64_t best = (T + 127) / 128 * 128 - T;
+    for (int c : {3, 2}) {
+      const int64_t waste = (T + 32 * c - 1) / (32 * c) * (32 * c) - T;
+      if (waste < best) { best = waste; nwv = c; }
+    }
+    if (dh != 64 && dh != 72) return hipErrorInvalidValue;
+#define DIT_ATTN_LAUNCH(NWV)                                                                  \
+  {                                                                                           \
+    dim3 grid((T + 32 * NWV - 1) / (32 * NWV), B * heads);                                    \
+    if (dh == 64)                                                                             \
+      attn_bf16_kernel<64, NWV><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o,     \
+                                                          heads, T, sl2);                     \
+    else                                                                                      \
+      attn_bf16_kernel<72, NWV><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o,     \
+                                                          heads, T, sl2);                     \
+  }
+    if (nwv == 4) DIT_ATTN_LAUNCH(4)
+    else if (nwv == 3) DIT_ATTN_LAUNCH(3)
+    else DIT_ATTN_LAUNCH(2)
+#undef DIT_ATTN_LAUNCH
   } else {
     const float scale = 1.0f / sqrtf((float)dh);
     dim3 grid((T + 63) / 64, B * heads);
@@ -440,13 +456,47 @@ hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, in
 // ---------------------------------------------------------------------------
 // Cross-attention of every token over the two context tokens of its row (the
 // cross-attention conditioning design): per head, softmax over two scores.
-// One thread per (token, head); fp32 arithmetic.
+// One thread per (token, head), 16-byte loads and stores; fp32 arithmetic.
 namespace {
+// 16 bytes of DT as floats: 8 bf16 or 4 fp32.
+template <typename DT> struct Vec16;
+template <> struct Vec16<bf16_t> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void load(const bf16_t* p, float* f) {
+    const uint4 u = *(const uint4*)p;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(bf16_t* p, const float* f) {
+    uint4 u;
+    u.x = f2bf2(f[0], f[1]); u.y = f2bf2(f[2], f[3]);
+    u.z = f2bf2(f[4], f[5]); u.w = f2bf2(f[6], f[7]);
+    *(uint4*)p = u;
+  }
+};
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void load(const float* p, float* f) {
+    const float4 v = *(const float4*)p;
+    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float* f) {
+    *(float4*)p = make_float4(f[0], f[1], f[2], f[3]);
+  }
+};
+
 template <typename DT, int DH>
 __global__ __launch_bounds__(256) void cross_attn2_kernel(const DT* __restrict__ q,
-                                                          const DT* __restrict__ kv, int64_t n,
-                                                          int T, int heads,
-                                                          DT* __restrict__ o) {
+                                                          const DT* __restrict__ kv,
+                                                          int64_t kv_stride, int64_t n, int T,
+                                                          int heads, DT* __restrict__ o) {
+  using V = Vec16<DT>;
+  constexpr int NC = DH / V::N;
+  static_assert(DH % V::N == 0, "head dim");
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n) return;
   const int h = (int)(idx % heads);
@@ -454,14 +504,20 @@ __global__ __launch_bounds__(256) void cross_attn2_kernel(const DT* __restrict__
   const int64_t b = m / T;
   const int D = heads * DH;
   const DT* qp = q + m * D + h * DH;
-  const DT* k0 = kv + (b * 2) * 2 * D + h * DH;
-  const DT* k1 = k0 + 2 * D;
+  const DT* k0 = kv + (b * 2) * kv_stride + h * DH;
+  const DT* k1 = k0 + kv_stride;
   float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll 8
-  for (int i = 0; i < DH; ++i) {
-    const float a = to_f<DT>(qp[i]);
-    s0 = fmaf(a, to_f<DT>(k0[i]), s0);
-    s1 = fmaf(a, to_f<DT>(k1[i]), s1);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float a[V::N], x0[V::N], x1[V::N];
+    V::load(qp + c * V::N, a);
+    V::load(k0 + c * V::N, x0);
+    V::load(k1 + c * V::N, x1);
+#pragma unroll
+    for (int i = 0; i < V::N; ++i) {
+      s0 = fmaf(a[i], x0[i], s0);
+      s1 = fmaf(a[i], x1[i], s1);
+    }
   }
   const float scale = 1.0f / sqrtf((float)DH);
   s0 *= scale;
@@ -470,34 +526,38 @@ __global__ __launch_bounds__(256) void cross_attn2_kernel(const DT* __restrict__
   const float e0 = expf(s0 - mx), e1 = expf(s1 - mx);
   const float inv = 1.0f / (e0 + e1);
   const float p0 = e0 * inv, p1 = e1 * inv;
-  const DT* v0 = k0 + D;
-  const DT* v1 = k1 + D;
   DT* op = o + m * D + h * DH;
-#pragma unroll 8
-  for (int i = 0; i < DH; ++i)
-    op[i] = from_f<DT>(fmaf(p0, to_f<DT>(v0[i]), p1 * to_f<DT>(v1[i])));
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    float v0[V::N], v1[V::N], r[V::N];
+    V::load(k0 + D + c * V::N, v0);
+    V::load(k1 + D + c * V::N, v1);
+#pragma unroll
+    for (int i = 0; i < V::N; ++i) r[i] = fmaf(p0, v0[i], p1 * v1[i]);
+    V::store(op + c * V::N, r);
+  }
 }
 
 template <typename DT>
-hipError_t cross2_dispatch(const void* q, const void* kv, int rows, int T, int heads, int dh,
-                           void* o, hipStream_t s) {
+hipError_t cross2_dispatch(const void* q, const void* kv, int64_t kv_stride, int rows, int T,
+                           int heads, int dh, void* o, hipStream_t s) {
   const int64_t n = (int64_t)rows * T * heads;
   const int blocks = (int)((n + 255) / 256);
   if (dh == 72)
-    cross_attn2_kernel<DT, 72><<<blocks, 256, 0, s>>>((const DT*)q, (const DT*)kv, n, T, heads,
-                                                     (DT*)o);
+    cross_attn2_kernel<DT, 72><<<blocks, 256, 0, s>>>((const DT*)q, (const DT*)kv, kv_stride, n,
+                                                     T, heads, (DT*)o);
   else if (dh == 64)
-    cross_attn2_kernel<DT, 64><<<blocks, 256, 0, s>>>((const DT*)q, (const DT*)kv, n, T, heads,
-                                                     (DT*)o);
+    cross_attn2_kernel<DT, 64><<<blocks, 256, 0, s>>>((const DT*)q, (const DT*)kv, kv_stride, n,
+                                                     T, heads, (DT*)o);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_cross_attention2(const void* q, const void* kv, int rows, int T, int heads,
-                                   int dh, int dtype, void* o, hipStream_t s) {
+hipError_t launch_cross_attention2(const void* q, const void* kv, int64_t kv_stride, int rows,
+                                   int T, int heads, int dh, int dtype, void* o, hipStream_t s) {
   if (rows <= 0 || T <= 0) return hipSuccess;
-  return dtype == 1 ? cross2_dispatch<bf16_t>(q, kv, rows, T, heads, dh, o, s)
-                    : cross2_dispatch<float>(q, kv, rows, T, heads, dh, o, s);
+  return dtype == 1 ? cross2_dispatch<bf16_t>(q, kv, kv_stride, rows, T, heads, dh, o, s)
+                    : cross2_dispatch<float>(q, kv, kv_stride, rows, T, heads, dh, o, s);
 }

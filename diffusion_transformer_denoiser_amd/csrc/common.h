@@ -126,9 +126,11 @@ hipError_t launch_cond_tokens(const float* temb, int rows, int d, const float* t
                               const int32_t* labels, int label_rows, int null_from, int ncls,
                               int mode, void* dst, int T, int dtype, hipStream_t s);
 // Cross-attention over two context tokens per row: q [rows * T, H * dh] and
-// kv [rows, 2, 2 * H * dh] (k | v of each token) in dtype; o [rows * T, H * dh].
-hipError_t launch_cross_attention2(const void* q, const void* kv, int rows, int T, int heads,
-                                   int dh, int dtype, void* o, hipStream_t s);
+// o [rows * T, H * dh] in dtype; context token j of row b has its keys at
+// kv + (2 b + j) * kv_stride and its values H * dh elements further on
+// (kv_stride in elements, a multiple of 8; all offsets 16-byte aligned).
+hipError_t launch_cross_attention2(const void* q, const void* kv, int64_t kv_stride, int rows,
+                                   int T, int heads, int dh, int dtype, void* o, hipStream_t s);
 hipError_t launch_unpatchify(const float* Y, int Bout, int Bh_offset, const PatchGeom& g,
                              int Cout, int guided, float scale, int guide, float* out,
                              hipStream_t s);

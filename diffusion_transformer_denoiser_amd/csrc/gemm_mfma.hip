@@ -55,16 +55,18 @@ __device__ __forceinline__ void bare_barrier() {
 }
 
 // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs (each with
-// its own L2): with SWZ, workgroup b runs logical tile (b % 8) * (n / 8) + b / 8,
-// so each XCD walks a contiguous range of logical tiles, and logical tiles are
-// ordered in groups of G row-tiles (column-major inside a group, the column
-// index rotated per XCD) so the tiles resident on one XCD at a time share A
-// and W tiles.  Needs n % 8 == 0.
+// its own L2): with SWZ, XCD x = b % 8 runs workgroups b = x, x + 8, ..., and
+// they take one contiguous range of logical tiles (the first n % 8 XCDs one
+// tile more than the others), so each XCD walks its own range.  Logical tiles
+// are ordered in groups of G row-tiles (column-major inside a group, the
+// column index rotated per XCD) so the tiles resident on one XCD at a time
+// share A and W tiles.
 template <int SWZ>
 __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
   if constexpr (SWZ) {
     const int n = tiles_m * tiles_n;
-    const int logical = (b & 7) * (n >> 3) + (b >> 3);
+    const int q = n >> 3, r = n & 7, x = b & 7;
+    const int logical = x * q + min(x, r) + (b >> 3);
     constexpr int G = 8;
     const int per_group = G * tiles_n;
     const int grp = logical / per_group, in = logical - grp * per_group;
@@ -76,7 +78,8 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
     // different W columns, so a weight tile comes from HBM once and later XCDs
     // find it in the Infinity Cache (-8% per launch when the weights are not
     // cached yet, as in a forward).
-    const int xg = (grp * per_group) / (n >> 3);
+    const int l0 = grp * per_group;   // the group's first tile, and the XCD whose range holds it
+    const int xg = l0 < r * (q + 1) ? l0 / (q + 1) : r + (l0 - r * (q + 1)) / max(q, 1);
     tn = (in / rows + (xg & 7) * tiles_n / 8) % tiles_n;
   } else {
     tm = b / tiles_n;
@@ -394,13 +397,8 @@ hipError_t run(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
 #define DIT_GEMM_LAUNCH(SWZ, BUF)                                                                 \
   gemm_bf16_kernel<EPI, BM, BN, BK, MINWG, SWZ, 1, BUF><<<tiles, 256, 0, s>>>(A, lda, W, M, N, K, \
                                                                            ep, vec)
-  if (tiles % 8 == 0) {
-    if (buf) DIT_GEMM_LAUNCH(1, 1);
-    else DIT_GEMM_LAUNCH(1, 0);
-  } else {
-    if (buf) DIT_GEMM_LAUNCH(0, 1);
-    else DIT_GEMM_LAUNCH(0, 0);
-  }
+  if (buf) DIT_GEMM_LAUNCH(1, 1);
+  else DIT_GEMM_LAUNCH(1, 0);
 #undef DIT_GEMM_LAUNCH
   return hipGetLastError();
 }
