@@ -51,6 +51,10 @@ def parse():
                     help="time whole sampling loops (dit_sample) instead of single forwards")
     ap.add_argument("--sample-steps", type=int, default=25,
                     help="denoiser evaluations per sampling loop")
+    ap.add_argument("--packed", action="store_true",
+                    help="time packed mixed-resolution forwards (dit_forward_packed): 16 latents "
+                         "of 32x32 and 4 of 64x64 in one call, against the same work as two "
+                         "batched calls")
     return ap.parse_args()
 
 
@@ -193,6 +197,72 @@ def sample_main(args, cfg, model, dev):
     print(json.dumps(line), flush=True)
 
 
+def packed_main(args, cfg, model, dev):
+    """Packed sequences: one dit_forward_packed call over 16 latents of 32x32
+    (256x256 images) and 4 of 64x64 (512x512), 8192 tokens, against the same
+    sequences as two batched dit_forward calls."""
+    import torch
+    import dit_inputs
+    import diffusion_transformer_denoiser_amd as dm
+    from oracle import flops as oflops
+
+    shapes = ([(64, 64)] + [(32, 32)] * 4) * 4
+    rng = np.random.default_rng(4242)
+    dt = dm.torch_dtype(cfg["dtype"])
+    xs = [torch.from_numpy(dit_inputs.cast_to(rng.standard_normal((cfg["C"],) + hw), cfg["dtype"]))
+          .to(dt).to(dev) for hw in shapes]
+    n = len(shapes)
+    t = torch.from_numpy(rng.integers(0, 1000, size=n).astype(np.float32)).to(dev)
+    y = torch.from_numpy(rng.integers(0, cfg["num_classes"], size=n).astype(np.int32)).to(dev)
+    small = [i for i, hw in enumerate(shapes) if hw == (32, 32)]
+    large = [i for i, hw in enumerate(shapes) if hw == (64, 64)]
+    xs_s = torch.stack([xs[i] for i in small]); xs_l = torch.stack([xs[i] for i in large])
+    t_s, t_l = t[small].contiguous(), t[large].contiguous()
+    y_s, y_l = y[small].contiguous(), y[large].contiguous()
+    cfg_l = dict(cfg, H=64, W=64)
+    model_l = dm.DiT(cfg_l, dit_inputs.make_weights(cfg), dev)   # same weights, 64x64 grid
+
+    def packed():
+        model.forward_packed(xs, t, y)
+
+    def separate():
+        model.forward(xs_s, t_s, y_s)
+        model_l.forward(xs_l, t_l, y_l)
+
+    res = {}
+    for name, fn in (("packed", packed), ("separate", separate)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / args.steps
+    tokens = sum((h // cfg["p"]) * (w // cfg["p"]) for h, w in shapes)
+    gmac = sum(oflops.gmac_for(dict(cfg, H=h, W=w)) for h, w in shapes)
+    ms = res["packed"]
+    line = {
+        "metric": "DiT-XL/2 packed mixed-resolution forward tokens/s on 1 MI355X",
+        "value": round(tokens * 1000.0 / ms, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg["dtype"] == dit_inputs.DTYPE_BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) latents, random t and labels, N(0,0.02) weights)",
+        "config": {"workload": "DiT-XL/2 packed: 16 latents of 32x32x4 + 4 of 64x64x4 in one call",
+                   "sequences": n, "tokens": tokens, "parallelism": "single GPU"},
+        "tflops": round(2.0 * gmac * 1e9 / (ms * 1e-3) / 1e12, 1),
+        "separate_batched_ms": round(res["separate"], 4),
+        "packed_over_separate": round(res["separate"] / ms, 4),
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -224,6 +294,8 @@ def main():
     out = torch.empty(model.out_shape(Bh), device=dev, dtype=torch.float32)
     if args.sample:
         return sample_main(args, cfg, model, dev)
+    if args.packed:
+        return packed_main(args, cfg, model, dev)
 
     def step():
         if cfg["cfg"]:

@@ -81,6 +81,11 @@ EXPORTS = {
     "dit_sample": (C.c_int, [C.c_void_p, C.POINTER(DitSampler), C.c_void_p, C.c_void_p,
                              C.c_void_p, C.c_int, C.c_float, C.c_int, C.c_void_p, C.c_void_p,
                              C.c_size_t, C.c_void_p]),
+    "dit_packed_workspace_size": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_int32),
+                                            C.POINTER(C.c_size_t)]),
+    "dit_forward_packed": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_int32), C.c_void_p,
+                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                     C.c_size_t, C.c_void_p]),
 }
 
 _lib = None

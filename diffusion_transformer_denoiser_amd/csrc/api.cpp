@@ -2,7 +2,9 @@
 // sequence of the DiT forward pass.  No device memory is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -92,10 +94,12 @@ bool ensure_aux(const dit_handle* h) {
 namespace {
 
 struct WsLayout {
-  size_t e, th, c, sc, pp, pe, mod, ctx, kv, X, H, qkv, o, G, Y, total;
+  size_t e, th, c, sc, pp, pe, mod, ctx, kv, X, H, qkv, o, G, Y, seg, total;
 };
 
-WsLayout ws_layout(const dit_handle* h, int rows) {
+// rows: conditioning rows; M: token rows of the trunk; packed: M tokens of
+// packed sequences (position table and token -> sequence map for all of them).
+WsLayout ws_layout_m(const dit_handle* h, int rows, size_t M, bool packed) {
   WsLayout L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -103,13 +107,13 @@ WsLayout ws_layout(const dit_handle* h, int rows) {
     off += align256(bytes);
     return o;
   };
-  const size_t es = h->es, R = (size_t)rows, M = R * h->Tt;
+  const size_t es = h->es, R = (size_t)rows;
   L.e = take(R * h->freq * 4);
   L.th = take(R * h->d * 4);
   L.c = take(R * h->d * 4);
   L.sc = take(R * h->d * es);
   L.pp = take(h->cond_dim > 0 ? R * h->d * 4 : 0);          // pooled projection
-  L.pe = take(h->cfg.rope3d ? 0 : (size_t)h->T * h->d * 4);  // 2-D position table
+  L.pe = take(h->cfg.rope3d ? 0 : (packed ? M : (size_t)h->T) * h->d * 4);  // 2-D position table
   L.mod = take(R * h->mod_stride * 4);                        // 0 without adaLN
   L.ctx = take(h->cond == DIT_COND_CROSS_ATTN ? R * 2 * h->d * es : 0);      // context tokens
   // k | v of the context tokens for every block: [rows, 2, N, 2d]
@@ -120,8 +124,13 @@ WsLayout ws_layout(const dit_handle* h, int rows) {
   L.o = take(M * h->d * es);
   L.G = take(M * h->hid * es);
   L.Y = take(M * h->kout * 4);
+  L.seg = take(packed ? M * 4 : 0);
   L.total = off;
   return L;
+}
+
+WsLayout ws_layout(const dit_handle* h, int rows) {
+  return ws_layout_m(h, rows, (size_t)rows * h->Tt, false);
 }
 
 template <typename T>
@@ -155,16 +164,26 @@ hipError_t linear(const dit_handle* h, int epi, const void* A, int lda, const vo
 
 // One adaLN-Zero block on the residual stream X [rows*T, d] (fp32, in place).
 // mod + base points at this block's (b1, g1, a1, b2, g2, a2) in rows of mod_stride.
+// Packed sequences: token rows, token -> sequence map (the modulation row of
+// each token) and the sequence table for block-diagonal attention.
+struct Packed {
+  int M;
+  const int* tok_seg;
+  SeqTable seqs;
+};
+
 int run_block(const dit_handle* h, int l, int rows, float* X, const float* mod, int mod_stride,
               int base, void* ws, const WsLayout& L, float* o_branch, float* f_branch,
-              hipStream_t s) {
-  const int d = h->d, T = h->T, M = rows * T, es = h->es;
+              hipStream_t s, const Packed* pk = nullptr) {
+  const int d = h->d, T = h->T, M = pk ? pk->M : rows * T, es = h->es;
+  const int* ts = pk ? pk->tok_seg : nullptr;
   void* Hb = at<void>(ws, L.H);
   void* O = at<void>(ws, L.o);
   void* G = at<void>(ws, L.G);
   void* qkv = at<void>(ws, L.qkv);
 
-  DIT_HIP(launch_ln_modulate(X, M, T, d, mod, mod_stride, base, base + d, h->eps, Hb, h->dtype, s));
+  DIT_HIP(launch_ln_modulate(X, M, T, d, mod, mod_stride, base, base + d, h->eps, Hb, h->dtype, s,
+                             ts));
 
   // Packed in-projection q | k | v [M, 3d] (heads as contiguous dh slices).
   EpiParams ep = epi0();
@@ -173,10 +192,17 @@ int run_block(const dit_handle* h, int l, int rows, float* X, const float* mod, 
   DIT_HIP(linear(h, EPI_BIAS_DT, Hb, d, woff(h->w.qkv_w, (size_t)l * 3 * d * d, es), M, 3 * d, d,
                  ep, s));
 
-  if (h->cfg.qk_norm || h->cfg.rope3d)
-    DIT_HIP(launch_qk_norm_rope(qkv, rows, h->heads, T, h->dh, h->dtype, h->cfg.qk_norm, h->eps,
-                                h->cfg.rope3d, h->gh, h->gw, s));
-  DIT_HIP(launch_attention(qkv, rows, h->heads, T, h->dh, h->dtype, O, s));
+  if (pk) {
+    if (h->cfg.qk_norm)   // per-token LayerNorm of q and k (no rotary embedding when packed)
+      DIT_HIP(launch_qk_norm_rope(qkv, 1, h->heads, M, h->dh, h->dtype, 1, h->eps, 0, h->gh,
+                                  h->gw, s));
+    DIT_HIP(launch_attention_packed(qkv, pk->seqs, h->heads, h->dh, h->dtype, O, s));
+  } else {
+    if (h->cfg.qk_norm || h->cfg.rope3d)
+      DIT_HIP(launch_qk_norm_rope(qkv, rows, h->heads, T, h->dh, h->dtype, h->cfg.qk_norm, h->eps,
+                                  h->cfg.rope3d, h->gh, h->gw, s));
+    DIT_HIP(launch_attention(qkv, rows, h->heads, T, h->dh, h->dtype, O, s));
+  }
 
   const void* ow = woff(h->w.o_w, (size_t)l * d * d, es);
   if (o_branch) {
@@ -189,10 +215,11 @@ int run_block(const dit_handle* h, int l, int rows, float* X, const float* mod, 
   ep.bias = h->w.o_b + (size_t)l * d;
   ep.out = X; ep.ldo = d;
   ep.mod = mod; ep.mod_stride = mod_stride; ep.gate_off = base + 2 * d; ep.T = T;
+  ep.tok_seg = ts;
   DIT_HIP(linear(h, EPI_GATED, O, d, ow, M, d, d, ep, s));
 
   DIT_HIP(launch_ln_modulate(X, M, T, d, mod, mod_stride, base + 3 * d, base + 4 * d, h->eps, Hb,
-                             h->dtype, s));
+                             h->dtype, s, ts));
   ep = epi0();
   ep.bias = h->w.fc1_b + (size_t)l * h->hid;
   ep.out = G; ep.ldo = h->hid;
@@ -210,6 +237,7 @@ int run_block(const dit_handle* h, int l, int rows, float* X, const float* mod, 
   ep.bias = h->w.fc2_b + (size_t)l * d;
   ep.out = X; ep.ldo = d;
   ep.mod = mod; ep.mod_stride = mod_stride; ep.gate_off = base + 5 * d; ep.T = T;
+  ep.tok_seg = ts;
   DIT_HIP(linear(h, EPI_GATED, G, h->hid, w2, M, d, h->hid, ep, s));
   return DIT_OK;
 }
@@ -273,10 +301,15 @@ int run_block_variant(const dit_handle* h, int l, int rows, float* X, const void
 
 // Trunk of `rows` rows.  Row r reads latent/time/pooled row r % src_rows; rows
 // r >= null_from take the null label.  Leaves the decoder output in ws Y.
-int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_t* y,
-              const float* pooled, int rows, int src_rows, int null_from, void* ws,
-              const WsLayout& L, const dit_taps* taps, hipStream_t s) {
-  const int d = h->d, T = h->T, Tt = h->Tt, M = rows * Tt;
+// Conditioning of `rows` rows: c (time embedding, + class row, + pooled
+// projection), SiLU(c) and all modulation vectors for adaLN-Zero; the two
+// conditioning tokens (and the context keys / values) for the other designs.
+// Row r reads time / pooled row r % src_rows; rows r >= null_from take the
+// null label.
+int run_conditioning(const dit_handle* h, const float* t, const int32_t* y, const float* pooled,
+                     int rows, int src_rows, int null_from, void* ws, const WsLayout& L,
+                     hipStream_t s) {
+  const int d = h->d, T = h->T;
   const bool ada = h->cond == DIT_COND_ADALN_ZERO;
   float* e = at<float>(ws, L.e);
   float* th = at<float>(ws, L.th);
@@ -284,8 +317,6 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
   void* sc = at<void>(ws, L.sc);
   float* mod = at<float>(ws, L.mod);
   float* X = at<float>(ws, L.X);
-  void* Hb = at<void>(ws, L.H);
-  float* Y = at<float>(ws, L.Y);
 
   // c = t_emb (+ pooled projection) (+ class row); sc = SiLU(c) in the GEMM dtype.
   ALoad a;
@@ -372,6 +403,25 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
     }
   }
 
+  return DIT_OK;
+}
+
+int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_t* y,
+              const float* pooled, int rows, int src_rows, int null_from, void* ws,
+              const WsLayout& L, const dit_taps* taps, hipStream_t s) {
+  const int d = h->d, T = h->T, Tt = h->Tt, M = rows * Tt;
+  const bool ada = h->cond == DIT_COND_ADALN_ZERO;
+  float* c = at<float>(ws, L.c);
+  float* mod = at<float>(ws, L.mod);
+  float* X = at<float>(ws, L.X);
+  void* Hb = at<void>(ws, L.H);
+  float* Y = at<float>(ws, L.Y);
+  {
+    int rc = run_conditioning(h, t, y, pooled, rows, src_rows, null_from, ws, L, s);
+    if (rc) return rc;
+  }
+  ALoad a;
+  EpiParams ep;
   // Patchify gather + patch embedding + bias + 2-D position embedding (from a
   // table of the T x d embedding, computed once per call).
   memset(&a, 0, sizeof a);
@@ -748,6 +798,37 @@ int sample_rows(const dit_handle* h, int B, int guided, int* rows) {
   return DIT_OK;
 }
 
+// Packed sequences: validation and token offsets.  seq_fhw: host [nseq, 3].
+int check_packed(const dit_handle* h, int nseq, const int32_t* seq_fhw, SeqTable* st,
+                 int64_t* x_elems, int64_t* out_elems) {
+  if (!seq_fhw) return fail(DIT_EINVAL, "seq_fhw must be non-NULL");
+  if (nseq < 1 || nseq > kMaxSeq) return fail(DIT_EINVAL, "nseq must be in [1, %d]", kMaxSeq);
+  if (h->cond != DIT_COND_ADALN_ZERO)
+    return fail(DIT_EUNSUPPORTED, "packed sequences need the adaLN-Zero design");
+  if (h->cfg.rope3d) return fail(DIT_EUNSUPPORTED, "packed sequences need 2-D position embedding");
+  const dit_config& c = h->cfg;
+  st->n = nseq;
+  st->tok[0] = 0;
+  int64_t xe = 0, oe = 0;
+  for (int j = 0; j < nseq; ++j) {
+    const int F = seq_fhw[3 * j], H = seq_fhw[3 * j + 1], W = seq_fhw[3 * j + 2];
+    if (F != c.patch_t || H <= 0 || W <= 0 || H % c.patch || W % c.patch)
+      return fail(DIT_EINVAL, "sequence %d: extents (%d, %d, %d) need F = %d and H, W divisible by %d",
+                  j, F, H, W, c.patch_t, c.patch);
+    const int64_t T = (int64_t)(H / c.patch) * (W / c.patch);
+    if (T % 32) return fail(DIT_EUNSUPPORTED, "sequence %d: %lld tokens, not a multiple of 32", j,
+                            (long long)T);
+    if (st->tok[j] + T > (1 << 26)) return fail(DIT_EINVAL, "too many packed tokens");
+    st->tok[j + 1] = (int)(st->tok[j] + T);
+    xe += (int64_t)c.in_channels * F * H * W;
+    oe += (int64_t)c.out_channels * F * H * W;
+  }
+  if ((int64_t)st->tok[nseq] * h->heads > (1LL << 31)) return fail(DIT_EINVAL, "too many tokens");
+  *x_elems = xe;
+  *out_elems = oe;
+  return DIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1095,6 +1176,133 @@ int dit_sample(dit_handle* h, const dit_sampler* sp, float* x, const int32_t* y,
     a.null_off = B; a.guided = guided_channels; a.scale = scale;
     a.learned = Cout == 2 * C;
     DIT_HIP(launch_sampler_step(a, s));
+  }
+  return ok();
+}
+
+
+int dit_packed_workspace_size(const dit_handle* h, int nseq, const int32_t* seq_fhw,
+                              size_t* bytes) {
+  if (!h || !bytes) return fail(DIT_EINVAL, "handle and bytes must be non-NULL");
+  SeqTable st;
+  int64_t xe, oe;
+  int rc = check_packed(h, nseq, seq_fhw, &st, &xe, &oe);
+  if (rc) return rc;
+  *bytes = ws_layout_m(h, nseq, (size_t)st.tok[nseq], true).total;
+  return ok();
+}
+
+int dit_forward_packed(dit_handle* h, int nseq, const int32_t* seq_fhw, const void* x,
+                       const float* t, const int32_t* y, const float* pooled, float* out,
+                       void* ws, size_t ws_bytes, void* stream) {
+  if (!h) return fail(DIT_EINVAL, "handle is NULL");
+  if (!x || !t || !out) return fail(DIT_EINVAL, "x, t and out must be non-NULL");
+  if (h->ncls > 0 && !y) return fail(DIT_EINVAL, "class labels y are required");
+  if (h->cond_dim > 0 && !pooled) return fail(DIT_EINVAL, "pooled conditioning is required");
+  Packed pk;
+  int64_t xe, oe;
+  int rc = check_packed(h, nseq, seq_fhw, &pk.seqs, &xe, &oe);
+  if (rc) return rc;
+  pk.M = pk.seqs.tok[nseq];
+  const WsLayout L = ws_layout_m(h, nseq, (size_t)pk.M, true);
+  rc = check_ws_bytes(ws, ws_bytes, L.total);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const int d = h->d, C = h->cfg.in_channels, Cout = h->cfg.out_channels;
+  const int p = h->cfg.patch, pt = h->cfg.patch_t;
+  float* X = at<float>(ws, L.X);
+  float* Y = at<float>(ws, L.Y);
+  float* pe = at<float>(ws, L.pe);
+  int* seg = at<int>(ws, L.seg);
+  pk.tok_seg = seg;
+
+  rc = run_conditioning(h, t, y, pooled, nseq, nseq, nseq, ws, L, s);
+  if (rc) return rc;
+  // Per sequence: its token -> sequence map, its position table and its patch
+  // embedding (the patch gather reads its own latent extents).
+  int64_t xoff = 0;
+  for (int j = 0; j < nseq; ++j) {
+    const int F = seq_fhw[3 * j], H = seq_fhw[3 * j + 1], W = seq_fhw[3 * j + 2];
+    const int t0 = pk.seqs.tok[j], Tj = pk.seqs.tok[j + 1] - t0;
+    DIT_HIP(launch_fill_int(seg + t0, Tj, j, s));
+    DIT_HIP(launch_pos_embed_table(H / p, W / p, d, pe + (size_t)t0 * d, s));
+    ALoad a;
+    memset(&a, 0, sizeof a);
+    a.ptr = (const char*)x + xoff * h->es;
+    a.a_dtype = h->dtype; a.src_rows = 1; a.g = make_geom(C, F, H, W, p, pt);
+    EpiParams ep = epi0();
+    ep.bias = h->w.pe_b; ep.out = X + (size_t)t0 * d; ep.ldo = d; ep.T = Tj;
+    ep.pe_tab = pe + (size_t)t0 * d;
+    DIT_HIP(launch_gemm_valu(EPI_PATCH, A_PATCH, a, h->w.pe_w, h->dtype, Tj, d, h->kin, ep, s));
+    xoff += (int64_t)C * F * H * W;
+  }
+  const float* mod = at<float>(ws, L.mod);
+  const int fb = 6 * d * h->N;
+  // Blocks and the final layer of the sequences [j0, j1): their tokens are a
+  // contiguous range, so every workspace region is offset by its first token.
+  auto group = [&](int j0, int j1, hipStream_t st) -> int {
+    Packed g;
+    const int tok0 = pk.seqs.tok[j0];
+    g.seqs.n = j1 - j0;
+    for (int j = j0; j <= j1; ++j) g.seqs.tok[j - j0] = pk.seqs.tok[j] - tok0;
+    g.M = g.seqs.tok[g.seqs.n];
+    g.tok_seg = seg + tok0;
+    const size_t m0 = tok0, es = h->es;
+    WsLayout Lg = L;
+    Lg.H += m0 * d * es;
+    Lg.qkv += m0 * 3 * d * es;
+    Lg.o += m0 * d * es;
+    Lg.G += m0 * h->hid * es;
+    float* Xg = X + m0 * d;
+    for (int l = 0; l < h->N; ++l) {
+      int r = run_block(h, l, g.seqs.n, Xg, mod, h->mod_stride, 6 * d * l, ws, Lg, nullptr,
+                        nullptr, st, &g);
+      if (r) return r;
+    }
+    void* Hg = at<void>(ws, Lg.H);
+    DIT_HIP(launch_ln_modulate(Xg, g.M, h->T, d, mod, h->mod_stride, fb, fb + d, h->eps, Hg,
+                               h->dtype, st, g.tok_seg));
+    EpiParams ef = epi0();
+    ef.bias = h->w.out_b; ef.out = Y + m0 * h->kout; ef.ldo = h->kout;
+    DIT_HIP(linear(h, EPI_BIAS_F32, Hg, d, h->w.out_w, g.M, h->kout, d, ef, st));
+    return DIT_OK;
+  };
+  // Two groups of about equal token counts on two streams (as the batched
+  // forward does with its two row halves), forked and joined with events.
+  int split = 0;
+  if (nseq >= 2) {
+    int64_t best = INT64_MAX;
+    for (int j = 1; j < nseq; ++j) {
+      const int64_t diff = std::llabs(2LL * pk.seqs.tok[j] - pk.M);
+      if (diff < best) { best = diff; split = j; }
+    }
+  }
+  bool forked = false;
+  if (split > 0) {
+    std::lock_guard<std::mutex> lock(h->mu);
+    if (ensure_aux(h)) {
+      forked = true;
+      DIT_HIP(hipEventRecord(h->ev_fork, s));
+      DIT_HIP(hipStreamWaitEvent(h->aux[0], h->ev_fork, 0));
+      rc = group(0, split, s);
+      if (!rc) rc = group(split, nseq, h->aux[0]);
+      const bool joined = hipEventRecord(h->ev_join[0], h->aux[0]) == hipSuccess &&
+                          hipStreamWaitEvent(s, h->ev_join[0], 0) == hipSuccess;
+      if (rc) return rc;
+      if (!joined) return fail(DIT_EHIP, "stream join failed");
+    }
+  }
+  if (!forked) {
+    rc = group(0, nseq, s);
+    if (rc) return rc;
+  }
+  int64_t ooff = 0;
+  for (int j = 0; j < nseq; ++j) {
+    const int F = seq_fhw[3 * j], H = seq_fhw[3 * j + 1], W = seq_fhw[3 * j + 2];
+    const PatchGeom g = make_geom(Cout, F, H, W, p, pt);
+    DIT_HIP(launch_unpatchify(Y + (size_t)pk.seqs.tok[j] * h->kout, 1, 0, g, Cout, 0, 0.0f, 0,
+                              out + ooff, s));
+    ooff += (int64_t)Cout * F * H * W;
   }
   return ok();
 }

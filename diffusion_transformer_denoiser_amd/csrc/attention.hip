@@ -28,10 +28,13 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 namespace {
 
-template <int DH, int NWV>
+// PK: packed sequences.  The grid is (query blocks of all sequences, heads);
+// a block finds its sequence in the by-value table and attends over that
+// sequence's tokens only.
+template <int DH, int NWV, bool PK = false>
 __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16_t* __restrict__ QKV,
-                                                           bf16_t* __restrict__ O, int H, int T,
-                                                           float sl2) {
+                                                           bf16_t* __restrict__ O, int H,
+                                                           int T_rows, float sl2, SeqTable seqs) {
   constexpr int KV = 64;                  // keys per tile
   constexpr int KLD = 72;                 // K tile row stride (elements), 144 B
   constexpr int VLD = KV + 4;             // V^T tile row stride (elements), 136 B
@@ -66,9 +69,19 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
   if ((nwg & 7) == 0) lin = (lin & 7) * (nwg >> 3) + (lin >> 3);
   const int bh = lin / gridDim.x;
   const int b = bh / H, h = bh - b * H;
-  const int q0 = (lin - bh * gridDim.x) * QPB + wave * 32;
+  int qblk = lin - bh * gridDim.x;
+  int T = T_rows;                      // tokens of this block's row / sequence
+  int64_t tok0 = (int64_t)b * T_rows;  // its first token in the packed rows
+  if constexpr (PK) {
+    int j = 0;
+    while (j + 1 < seqs.n && seqs.blk[j + 1] <= qblk) ++j;
+    qblk -= seqs.blk[j];
+    tok0 = seqs.tok[j];
+    T = seqs.tok[j + 1] - seqs.tok[j];
+  }
+  const int q0 = qblk * QPB + wave * 32;
   const int64_t ld = 3LL * H * DH;                       // packed row stride
-  const bf16_t* Qb = QKV + (int64_t)b * T * ld + h * DH;   // + t * ld
+  const bf16_t* Qb = QKV + tok0 * ld + h * DH;           // + t * ld
   const bf16_t* Kb = Qb + (int64_t)H * DH;
   const bf16_t* Vb = Qb + 2LL * H * DH;
 
@@ -346,7 +359,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
     const float inv = 1.0f / l;
     const int q = q0 + 16 * qb + c16;
     if (q >= T) continue;
-    bf16_t* orow = O + ((int64_t)b * T + q) * H * DH + h * DH;
+    bf16_t* orow = O + (tok0 + q) * H * DH + h * DH;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       int d0 = 16 * db + 4 * g;
@@ -357,16 +370,26 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
   }
 }
 
-template <int DH>
+template <int DH, bool PK = false>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ QKV,
-                                                      float* __restrict__ O, int H, int T,
-                                                      float scale) {
+                                                      float* __restrict__ O, int H, int T_rows,
+                                                      float scale, SeqTable seqs) {
   constexpr int KT = 32;
   __shared__ float sK[KT][DH], sV[KT][DH];
   const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
-  const int qi = blockIdx.x * 64 + threadIdx.x;
+  int qblk = blockIdx.x;
+  int T = T_rows;
+  int64_t tok0 = (int64_t)b * T_rows;
+  if constexpr (PK) {   // grid (query blocks of all sequences, heads)
+    int j = 0;
+    while (j + 1 < seqs.n && seqs.blk[j + 1] <= qblk) ++j;
+    qblk -= seqs.blk[j];
+    tok0 = seqs.tok[j];
+    T = seqs.tok[j + 1] - seqs.tok[j];
+  }
+  const int qi = qblk * 64 + threadIdx.x;
   const int64_t ld = 3LL * H * DH;
-  const float* Qb = QKV + (int64_t)b * T * ld + h * DH;
+  const float* Qb = QKV + tok0 * ld + h * DH;
   const float* Kb = Qb + (int64_t)H * DH;
   const float* Vb = Qb + 2LL * H * DH;
   float qv[DH], acc[DH];
@@ -400,7 +423,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
     }
   }
   if (qi < T) {
-    float* orow = O + ((int64_t)b * T + qi) * H * DH + h * DH;
+    float* orow = O + (tok0 + qi) * H * DH + h * DH;
     float inv = 1.0f / l;
 #pragma unroll
     for (int e = 0; e < DH; ++e) orow[e] = acc[e] * inv;
@@ -426,15 +449,17 @@ hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, in
       if (waste < best) { best = waste; nwv = c; }
     }
     if (dh != 64 && dh != 72) return hipErrorInvalidValue;
+    SeqTable none;
+    none.n = 0;
 #define DIT_ATTN_LAUNCH(NWV)                                                                  \
   {                                                                                           \
     dim3 grid((T + 32 * NWV - 1) / (32 * NWV), B * heads);                                    \
     if (dh == 64)                                                                             \
       attn_bf16_kernel<64, NWV><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o,     \
-                                                          heads, T, sl2);                     \
+                                                          heads, T, sl2, none);               \
     else                                                                                      \
       attn_bf16_kernel<72, NWV><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o,     \
-                                                          heads, T, sl2);                     \
+                                                          heads, T, sl2, none);               \
   }
     if (nwv == 4) DIT_ATTN_LAUNCH(4)
     else if (nwv == 3) DIT_ATTN_LAUNCH(3)
@@ -443,13 +468,60 @@ hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, in
   } else {
     const float scale = 1.0f / sqrtf((float)dh);
     dim3 grid((T + 63) / 64, B * heads);
+    SeqTable none;
+    none.n = 0;
     if (dh == 64)
-      attn_f32_kernel<64><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, T, scale);
+      attn_f32_kernel<64><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, T, scale, none);
     else if (dh == 72)
-      attn_f32_kernel<72><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, T, scale);
+      attn_f32_kernel<72><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, T, scale, none);
     else
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_packed(const void* qkv, const SeqTable& seqs_in, int heads, int dh,
+                                   int dtype, void* o, hipStream_t s) {
+  if (seqs_in.n <= 0 || seqs_in.n > kMaxSeq) return hipErrorInvalidValue;
+  if (dh != 64 && dh != 72) return hipErrorInvalidValue;
+  SeqTable seqs = seqs_in;
+  const int QPB = dtype == 1 ? 128 : 64;   // queries per workgroup
+  seqs.blk[0] = 0;
+  for (int j = 0; j < seqs.n; ++j)
+    seqs.blk[j + 1] = seqs.blk[j] + (seqs.tok[j + 1] - seqs.tok[j] + QPB - 1) / QPB;
+  if (dtype != 1) {
+    const float scale = 1.0f / sqrtf((float)dh);
+    dim3 grid(seqs.blk[seqs.n], heads);
+    if (dh == 64)
+      attn_f32_kernel<64, true><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, 0,
+                                                    scale, seqs);
+    else
+      attn_f32_kernel<72, true><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, 0,
+                                                    scale, seqs);
+    return hipGetLastError();
+  }
+  constexpr int NWV = 4;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)dh);
+  dim3 grid(seqs.blk[seqs.n], heads);
+  if (dh == 64)
+    attn_bf16_kernel<64, NWV, true><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o,
+                                                              heads, 0, sl2, seqs);
+  else
+    attn_bf16_kernel<72, NWV, true><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o,
+                                                              heads, 0, sl2, seqs);
+  return hipGetLastError();
+}
+
+namespace {
+__global__ void fill_int_kernel(int* __restrict__ out, int64_t n, int v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = v;
+}
+}  // namespace
+
+hipError_t launch_fill_int(int* out, int64_t n, int v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fill_int_kernel<<<(int)((n + 255) / 256), 256, 0, s>>>(out, n, v);
   return hipGetLastError();
 }
 

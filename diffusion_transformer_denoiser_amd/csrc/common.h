@@ -98,6 +98,9 @@ struct EpiParams {
   const float* pe_tab;
   // patch embedding: rows of out skipped after every T rows (extra tokens of a row)
   int out_skip;
+  // gated residual of packed sequences: the gate row of output row m is
+  // tok_seg[m] (sequences start at multiples of 32 rows); else m / T
+  const int* tok_seg;
 };
 
 // ---------------------------------------------------------------------------
@@ -149,13 +152,29 @@ hipError_t launch_gemm_valu(int epi, int asrc, const ALoad& a, const void* W, in
 hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, int M, int N,
                             int K, const EpiParams& ep, hipStream_t s);
 
+// Row m's modulation row is tok_seg[m] when tok_seg is given (packed
+// sequences), else m / T.
 hipError_t launch_ln_modulate(const float* X, int M, int T, int d, const float* mod,
                               int mod_stride, int shift_off, int scale_off, float eps,
-                              void* H, int dtype, hipStream_t s);
+                              void* H, int dtype, hipStream_t s, const int* tok_seg = nullptr);
 hipError_t launch_qk_norm_rope(void* qkv, int B, int heads, int T, int dh, int dtype,
                                int qk_norm, float eps, int rope, int gh, int gw, hipStream_t s);
 hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, int dtype, void* o,
                             hipStream_t s);
+
+// Packed sequences: sequence j owns tokens [tok[j], tok[j + 1]) of the packed
+// rows; attention stays inside each sequence (block-diagonal).  At most
+// kMaxSeq sequences; the table travels by value in the kernel arguments.
+constexpr int kMaxSeq = 64;
+struct SeqTable {
+  int n;
+  int tok[kMaxSeq + 1];   // token offsets, tok[0] = 0
+  int blk[kMaxSeq + 1];   // query-block offsets (filled by the attention launcher)
+};
+hipError_t launch_attention_packed(const void* qkv, const SeqTable& seqs, int heads, int dh,
+                                   int dtype, void* o, hipStream_t s);
+// out[i] = v for i in [0, n)
+hipError_t launch_fill_int(int* out, int64_t n, int v, hipStream_t s);
 
 static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 

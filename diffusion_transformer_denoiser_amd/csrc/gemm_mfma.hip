@@ -271,13 +271,12 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
     // that have no gate (plain residual add), run a two-deep pipeline over
     // batches of 4 rows x TN columns per lane instead: batch q+1 is loaded
     // before batch q is stored.
-    if (full && (!ep.mod || ep.T % 32 == 0)) {
+    if (full && (!ep.mod || ep.tok_seg || ep.T % 32 == 0)) {
       float gv[TM][TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const float* g = ep.mod ? ep.mod + (int64_t)((mrow + i * 32) / ep.T) * ep.mod_stride +
-                                      ep.gate_off
-                                : nullptr;
+        const int grow = ep.tok_seg ? ep.tok_seg[mrow + i * 32] : (mrow + i * 32) / ep.T;
+        const float* g = ep.mod ? ep.mod + (int64_t)grow * ep.mod_stride + ep.gate_off : nullptr;
 #pragma unroll
         for (int j = 0; j < TN; ++j) gv[i][j] = g ? g[ncol + j * 32] : 1.0f;
       }
@@ -378,8 +377,8 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
           ((bf16_t*)ep.out)[o] = f2bf(silu_f(v));
         } else {
           static_assert(EPI == EPI_GATED, "epilogue");
-          const float g =
-              ep.mod ? ep.mod[(int64_t)(m / ep.T) * ep.mod_stride + ep.gate_off + n] : 1.0f;
+          const int grow = ep.tok_seg ? ep.tok_seg[m] : m / ep.T;
+          const float g = ep.mod ? ep.mod[(int64_t)grow * ep.mod_stride + ep.gate_off + n] : 1.0f;
           float* X = (float*)ep.out;
           X[o] = X[o] + g * v;
         }

@@ -14,7 +14,8 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restric
                                                           int T, const float* __restrict__ mod,
                                                           int mod_stride, int shift_off,
                                                           int scale_off, float eps,
-                                                          DT* __restrict__ H) {
+                                                          DT* __restrict__ H,
+                                                          const int* __restrict__ tok_seg) {
   constexpr int D = 128 * NV;
   const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
   const int lane = threadIdx.x & 63;
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restric
     }
     const float var = wave_sum(q) * (1.0f / D);
     const float rstd = 1.0f / sqrtf(var + eps);
-    const int b = row / T;
+    const int b = tok_seg ? tok_seg[row] : row / T;
     const float2* sh = (const float2*)(mod + (int64_t)b * mod_stride + shift_off);
     const float2* sc = (const float2*)(mod + (int64_t)b * mod_stride + scale_off);
 #pragma unroll
@@ -63,13 +64,13 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restric
 template <typename DT>
 static hipError_t ln_dispatch(const float* X, int M, int T, int d, const float* mod,
                               int mod_stride, int shift_off, int scale_off, float eps, DT* H,
-                              hipStream_t s) {
+                              const int* tok_seg, hipStream_t s) {
   constexpr int R = 2;
   dim3 grid((M + 4 * R - 1) / (4 * R));
 #define DIT_LN_CASE(NV)                                                                      \
   case NV:                                                                                   \
     ln_modulate_kernel<NV, DT, R><<<grid, 256, 0, s>>>(X, M, T, mod, mod_stride, shift_off, \
-                                                       scale_off, eps, H);                  \
+                                                       scale_off, eps, H, tok_seg);         \
     break;
   switch (d / 128) {
     DIT_LN_CASE(1) DIT_LN_CASE(2) DIT_LN_CASE(3) DIT_LN_CASE(4) DIT_LN_CASE(5) DIT_LN_CASE(6)
@@ -83,14 +84,14 @@ static hipError_t ln_dispatch(const float* X, int M, int T, int d, const float* 
 
 hipError_t launch_ln_modulate(const float* X, int M, int T, int d, const float* mod,
                               int mod_stride, int shift_off, int scale_off, float eps, void* H,
-                              int dtype, hipStream_t s) {
+                              int dtype, hipStream_t s, const int* tok_seg) {
   if (M <= 0) return hipSuccess;
   if (d % 128 || d > 2048) return hipErrorInvalidValue;
   if (dtype == 1)
     return ln_dispatch<bf16_t>(X, M, T, d, mod, mod_stride, shift_off, scale_off, eps,
-                               (bf16_t*)H, s);
+                               (bf16_t*)H, tok_seg, s);
   return ln_dispatch<float>(X, M, T, d, mod, mod_stride, shift_off, scale_off, eps, (float*)H,
-                            s);
+                            tok_seg, s);
 }
 
 // Per-head q/k post-processing for spacetime attention, in place on the packed

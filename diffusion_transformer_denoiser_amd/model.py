@@ -205,6 +205,36 @@ class DiT:
         _lib.check(rc)
         return out
 
+    def forward_packed(self, xs, t, y=None, pooled=None):
+        """Packed sequences (``dit_forward_packed``): xs is a list of latents
+        [C, H_i, W_i] (device tensors, model dtype); t [n] fp32, y [n] int32,
+        pooled [n, cond_dim].  Returns the list of outputs [Cout, H_i, W_i]."""
+        n = len(xs)
+        fhw = []
+        for a in xs:
+            if a.dtype != self.dtype or a.device != self.device:
+                raise TypeError(f"latents must be {self.dtype} on {self.device}")
+            dims = tuple(a.shape[1:])
+            fhw.extend((self.cfg["pt"],) + dims if len(dims) == 2 else dims)
+        self._check_input(xs[0], t, y, pooled, n)
+        tab = (C.c_int32 * (3 * n))(*fhw)
+        x = torch.cat([a.reshape(-1) for a in xs])
+        sizes = [self.cfg["Cout"] * a[0].numel() for a in xs]
+        out = torch.empty(sum(sizes), device=self.device, dtype=torch.float32)
+        nb = C.c_size_t()
+        _lib.check(self.lib.dit_packed_workspace_size(self.handle, n, tab, C.byref(nb)))
+        if self._ws is None or self._ws.numel() < nb.value:
+            self._ws = None
+            self._ws = torch.empty(nb.value, dtype=torch.uint8, device=self.device)
+        _lib.check(self.lib.dit_forward_packed(self.handle, n, tab, _ptr(x), _ptr(t), _ptr(y),
+                                               _ptr(pooled), _ptr(out), _ptr(self._ws),
+                                               self._ws.numel(), _stream(self.device)))
+        outs, o = [], 0
+        for a, sz in zip(xs, sizes):
+            outs.append(out[o:o + sz].view((self.cfg["Cout"],) + tuple(a.shape[1:])))
+            o += sz
+        return outs
+
     def sample(self, sampler: "Sampler", x, y=None, pooled=None, scale: float = 1.0,
                guided: int = 0, noise=None):
         """Full sampling loop (``dit_sample``) in place on the fp32 state x

@@ -348,6 +348,27 @@ int dit_sample(dit_handle* h, const dit_sampler* sp, float* x, const int32_t* y,
                const float* pooled, int B, float s, int guided_channels, const float* noise,
                void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Packed sequences ----
+ * nseq latents of different extents in one call, their tokens packed one
+ * sequence after another; attention stays inside each sequence (the Patch n'
+ * Pack batching of blog.outta.ai GOKU review, section 2.2).  Each sequence has
+ * its own time step, label / pooled vector and 2-D position grid, and the
+ * result equals running each sequence on its own.
+ *   seq_fhw  host [nseq, 3]: latent extents (F_i, H_i, W_i), F_i = patch_t
+ *   x        device: the latents one after another, each [C, F_i, H_i, W_i],
+ *            model dtype
+ *   t, y, pooled  device, one entry (row) per sequence, as for dit_forward
+ *   out      device: the outputs one after another, each [Cout, F_i, H_i, W_i] fp32
+ * Needs the adaLN-Zero design with the 2-D position embedding, 1 <= nseq <= 64
+ * and (H_i / p)(W_i / p) a multiple of 32 tokens for every sequence.
+ * Like dit_forward, runs the blocks of two groups of sequences (split at about
+ * half the tokens) on the caller's stream and the handle's second stream. */
+int dit_packed_workspace_size(const dit_handle* h, int nseq, const int32_t* seq_fhw,
+                              size_t* bytes);
+int dit_forward_packed(dit_handle* h, int nseq, const int32_t* seq_fhw, const void* x,
+                       const float* t, const int32_t* y, const float* pooled, float* out,
+                       void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

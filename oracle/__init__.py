@@ -47,7 +47,7 @@ from .dit_oracle import (  # noqa: F401
     modulate, silu, gelu_tanh, linear, attention, qk_layernorm, rope3d,
     rope3d_tables, embed_condition, modulation, block, forward, cfg_forward,
     cfg_combine, token_grid, block_in_context, block_cross_attention, cross_attention,
-    class_embedding, block_weights, IN_CONTEXT, CROSS_ATTENTION,
+    class_embedding, block_weights, forward_packed, IN_CONTEXT, CROSS_ATTENTION,
 )
 from . import flops  # noqa: F401
 from . import sampler_oracle  # noqa: F401

@@ -499,3 +499,25 @@ def cfg_forward(cfg, w, x_t, t, y, s, guided, taps=None, blocks=None):
     y2 = np.concatenate([y, np.full(Bh, cfg["num_classes"], dtype=np.int64)])
     both = forward(cfg, w, x2, t2, y2, taps=taps, blocks=blocks)
     return cfg_combine(both[:Bh], both[Bh:], s, guided)
+
+
+# ---------------------------------------------------------------------------
+# Packed sequences ([Goku] 2.2 Patch n' Pack: images and videos of different
+# sizes share one sequence batch, each attending only to its own tokens).
+# The packed forward is, by definition, every sequence's own forward; the
+# packing is a layout of the same computation.
+
+def forward_packed(cfg, w, latents, t, y=None, pooled=None):
+    """latents: list of [C, H_i, W_i] (or [C, F_i, H_i, W_i]) arrays; t, y,
+    pooled: one entry per sequence.  Returns the list of outputs
+    [Cout, H_i, W_i] (or [Cout, F_i, H_i, W_i])."""
+    outs = []
+    for i, x in enumerate(latents):
+        x = _f64(x)
+        dims = x.shape[1:]
+        F, H, W = (1,) + tuple(dims) if len(dims) == 2 else tuple(dims)
+        ci = dict(cfg, F=F, H=H, W=W)
+        yi = None if y is None else np.asarray(y)[i:i + 1]
+        pi = None if pooled is None else _f64(pooled)[i:i + 1]
+        outs.append(forward(ci, w, x[None], _f64(t)[i:i + 1], yi, pi)[0])
+    return outs

@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
     for n in ("dit_create", "dit_destroy", "dit_workspace_size", "dit_forward", "dit_cfg_forward",
               "dit_status_string", "dit_patchify", "dit_unpatchify", "dit_timestep_embed",
               "dit_attention", "dit_linear", "dit_block_forward", "dit_sampler_coefficients",
-              "dit_sampler_step", "dit_sample_workspace_size", "dit_sample"):
+              "dit_sampler_step", "dit_sample_workspace_size", "dit_sample",
+              "dit_packed_workspace_size", "dit_forward_packed"):
         assert n in names
     assert set(names) == set(_lib.EXPORTS), "binding and header disagree"
 
@@ -202,3 +203,41 @@ def test_standalone_steps_validate_before_launch():
     assert lib.dit_linear(0, p, p, None, 4, 4, 48, 1, p, None, 0, 1, None) == _lib.DIT_EUNSUPPORTED
     assert lib.dit_linear(2, p, p, None, 4, 4, 64, 1, p, None, 0, 1, None) == _lib.DIT_EINVAL
     assert lib.dit_status_string(_lib.DIT_EWORKSPACE) == b"workspace missing or too small"
+
+
+@needs_lib
+def test_packed_forward_validates_before_launch():
+    lib = _lib.load()
+    rc, h = _create(_cfg(), _weights())
+    assert rc == _lib.DIT_OK
+    try:
+        fhw = (C.c_int32 * 6)(1, 32, 32, 1, 64, 64)
+        need = C.c_size_t()
+        assert lib.dit_packed_workspace_size(h, 2, fhw, C.byref(need)) == 0
+        one = C.c_size_t()
+        assert lib.dit_workspace_size(h, 5, C.byref(one)) == 0
+        assert need.value > 0
+        p = C.c_void_p(0x200000)
+        n = need.value
+        bad = (C.c_int32 * 3)(1, 31, 32)          # H not divisible by p
+        assert lib.dit_forward_packed(h, 1, bad, p, p, p, None, p, p, n, None) == _lib.DIT_EINVAL
+        odd = (C.c_int32 * 3)(1, 10, 10)          # 25 tokens: not a multiple of 32
+        assert lib.dit_forward_packed(h, 1, odd, p, p, p, None, p, p, n, None) == _lib.DIT_EUNSUPPORTED
+        two_frames = (C.c_int32 * 3)(2, 32, 32)
+        assert lib.dit_forward_packed(h, 1, two_frames, p, p, p, None, p, p, n,
+                                      None) == _lib.DIT_EINVAL
+        assert lib.dit_forward_packed(h, 0, fhw, p, p, p, None, p, p, n, None) == _lib.DIT_EINVAL
+        assert lib.dit_forward_packed(h, 65, fhw, p, p, p, None, p, p, n, None) == _lib.DIT_EINVAL
+        assert lib.dit_forward_packed(h, 2, fhw, p, p, None, None, p, p, n, None) == _lib.DIT_EINVAL
+        assert lib.dit_forward_packed(h, 2, fhw, p, p, p, None, p, p, n - 1,
+                                      None) == _lib.DIT_EWORKSPACE
+        assert lib.dit_forward_packed(h, 2, None, p, p, p, None, p, p, n, None) == _lib.DIT_EINVAL
+    finally:
+        lib.dit_destroy(h)
+    rc, h = _create(_cfg(conditioning=1), _weights())
+    try:
+        fhw = (C.c_int32 * 3)(1, 32, 32)
+        need = C.c_size_t()
+        assert lib.dit_packed_workspace_size(h, 1, fhw, C.byref(need)) == _lib.DIT_EUNSUPPORTED
+    finally:
+        lib.dit_destroy(h)
