@@ -164,6 +164,23 @@ hipError_t linear(const dit_handle* h, int epi, const void* A, int lda, const vo
 
 // One adaLN-Zero block on the residual stream X [rows*T, d] (fp32, in place).
 // mod + base points at this block's (b1, g1, a1, b2, g2, a2) in rows of mod_stride.
+// Patch embedding of M tokens (see launch_patch_embed); patch vectors whose
+// length is not a multiple of 16 go through the VALU GEMM with the patch
+// gather as its A loader.
+hipError_t patch_embed(const dit_handle* h, const void* x, int src_rows, const PatchGeom& g,
+                       const float* pe, int M, int out_skip, float* X, hipStream_t s) {
+  if (h->kin % 16 == 0 && ((uintptr_t)h->w.pe_w & 15) == 0)
+    return launch_patch_embed(x, src_rows, g, h->dtype, h->w.pe_w, h->w.pe_b, pe, M, h->d,
+                              out_skip, X, s);
+  ALoad a;
+  memset(&a, 0, sizeof a);
+  a.ptr = x; a.a_dtype = h->dtype; a.src_rows = src_rows; a.g = g;
+  EpiParams ep = epi0();
+  ep.bias = h->w.pe_b; ep.out = X; ep.ldo = h->d; ep.T = g.T; ep.out_skip = out_skip;
+  ep.pe_tab = pe;
+  return launch_gemm_valu(EPI_PATCH, A_PATCH, a, h->w.pe_w, h->dtype, M, h->d, h->kin, ep, s);
+}
+
 // Packed sequences: token rows, token -> sequence map (the modulation row of
 // each token) and the sequence table for block-diagonal attention.
 struct Packed {
@@ -420,21 +437,14 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
     int rc = run_conditioning(h, t, y, pooled, rows, src_rows, null_from, ws, L, s);
     if (rc) return rc;
   }
-  ALoad a;
-  EpiParams ep;
   // Patchify gather + patch embedding + bias + 2-D position embedding (from a
   // table of the T x d embedding, computed once per call).
-  memset(&a, 0, sizeof a);
-  a.ptr = x_t; a.a_dtype = h->dtype; a.src_rows = src_rows; a.g = h->gin;
-  ep = epi0();
-  ep.bias = h->w.pe_b; ep.out = X; ep.ldo = d; ep.T = T; ep.out_skip = Tt - T;
+  float* pe = nullptr;
   if (!h->cfg.rope3d) {
-    float* pe = at<float>(ws, L.pe);
+    pe = at<float>(ws, L.pe);
     DIT_HIP(launch_pos_embed_table(h->gh, h->gw, d, pe, s));
-    ep.pe_tab = pe;
   }
-  DIT_HIP(launch_gemm_valu(EPI_PATCH, A_PATCH, a, h->w.pe_w, h->dtype, rows * T, d, h->kin, ep,
-                           s));
+  DIT_HIP(patch_embed(h, x_t, src_rows, h->gin, pe, rows * T, Tt - T, X, s));
 
   if (taps) {
     if (taps->c) DIT_HIP(hipMemcpyAsync(taps->c, c, (size_t)rows * d * 4, hipMemcpyDeviceToDevice, s));
@@ -1226,14 +1236,8 @@ int dit_forward_packed(dit_handle* h, int nseq, const int32_t* seq_fhw, const vo
     const int t0 = pk.seqs.tok[j], Tj = pk.seqs.tok[j + 1] - t0;
     DIT_HIP(launch_fill_int(seg + t0, Tj, j, s));
     DIT_HIP(launch_pos_embed_table(H / p, W / p, d, pe + (size_t)t0 * d, s));
-    ALoad a;
-    memset(&a, 0, sizeof a);
-    a.ptr = (const char*)x + xoff * h->es;
-    a.a_dtype = h->dtype; a.src_rows = 1; a.g = make_geom(C, F, H, W, p, pt);
-    EpiParams ep = epi0();
-    ep.bias = h->w.pe_b; ep.out = X + (size_t)t0 * d; ep.ldo = d; ep.T = Tj;
-    ep.pe_tab = pe + (size_t)t0 * d;
-    DIT_HIP(launch_gemm_valu(EPI_PATCH, A_PATCH, a, h->w.pe_w, h->dtype, Tj, d, h->kin, ep, s));
+    DIT_HIP(patch_embed(h, (const char*)x + xoff * h->es, 1, make_geom(C, F, H, W, p, pt),
+                        pe + (size_t)t0 * d, Tj, 0, X + (size_t)t0 * d, s));
     xoff += (int64_t)C * F * H * W;
   }
   const float* mod = at<float>(ws, L.mod);

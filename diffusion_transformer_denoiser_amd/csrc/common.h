@@ -120,6 +120,12 @@ hipError_t launch_cond_finish(float* c, int rows, int d, const float* table, con
                               void* sc, int dtype, hipStream_t s);
 hipError_t launch_patchify(const void* x, int B, const PatchGeom& g, int dtype, void* P,
                            hipStream_t s);
+// X[m + (m / T) out_skip, :] = patch vector of token m (gathered from the
+// latent x of src_rows rows; row b of the tokens reads latent row b % src_rows)
+// times W^T + bias (+ pe[m % T, :]).  W [d, g.K] and x in `dtype`; X fp32.
+hipError_t launch_patch_embed(const void* x, int src_rows, const PatchGeom& g, int dtype,
+                              const void* W, const float* bias, const float* pe, int M, int d,
+                              int out_skip, float* X, hipStream_t s);
 // Conditioning tokens of the in-context and cross-attention designs: for trunk
 // row r, the time embedding temb[r] and the class embedding table[label(r)]
 // (label(r) as in launch_cond_finish; a label out of range gives NaN).

@@ -122,6 +122,107 @@ hipError_t launch_cond_finish(float* c, int rows, int d, const float* table, con
   return hipGetLastError();
 }
 
+// 16 consecutive elements of a 16-byte aligned row, as floats.
+__device__ __forceinline__ void load16(const bf16_t* p, float* f) {
+  const uint4 a = ((const uint4*)p)[0], b = ((const uint4*)p)[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load16(const float* p, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 v = ((const float4*)p)[i];
+    f[4 * i] = v.x; f[4 * i + 1] = v.y; f[4 * i + 2] = v.z; f[4 * i + 3] = v.w;
+  }
+}
+
+// Patch embedding X[row(m), n] = sum_k P[m, k] W[n, k] + bias[n] (+ pe[m % T, n])
+// for token rows m of a [B, C, F, H, W] latent, P the patch vectors (gathered
+// from the latent; never stored).  row(m) = m + (m / T) out_skip.  A workgroup
+// handles TM tokens: it gathers their patch vectors into LDS; each thread then
+// owns 4 consecutive output features, reads their weights 16 k at a time into
+// registers once and applies them to all TM tokens (products in order k = 0 ..
+// K-1), and stores 16 bytes per token.  K % 16 == 0; W 16-byte aligned.
+template <typename AT, int TM>
+__global__ __launch_bounds__(256) void patch_embed_kernel(const AT* __restrict__ x, int src_rows,
+                                                          PatchGeom g, const AT* __restrict__ W,
+                                                          const float* __restrict__ bias,
+                                                          const float* __restrict__ pe, int M,
+                                                          int d, int out_skip,
+                                                          float* __restrict__ X) {
+  extern __shared__ float sP[];   // [TM][K]
+  const int K = g.K, T = g.T;
+  const int m0 = blockIdx.x * TM;
+  const int64_t lrow = (int64_t)g.C * g.F * g.H * g.W;
+  for (int e = threadIdx.x; e < TM * K; e += blockDim.x) {
+    const int r = e / K, k = e - r * K;
+    const int m = min(m0 + r, M - 1);
+    const int b = m / T, tau = m - b * T;
+    sP[e] = to_f<AT>(x[(int64_t)(b % src_rows) * lrow + patch_src_offset(g, tau, k)]);
+  }
+  __syncthreads();
+  for (int grp = threadIdx.x; grp < d / 4; grp += blockDim.x) {
+    const int n = grp * 4;
+    float acc[TM][4];
+#pragma unroll
+    for (int r = 0; r < TM; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[r][j] = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      float w[4][16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) load16(W + (int64_t)(n + j) * K + k0, w[j]);
+#pragma unroll
+      for (int r = 0; r < TM; ++r) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float pv = sP[r * K + k0 + k];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[r][j] = fmaf(pv, w[j][k], acc[r][j]);
+        }
+      }
+    }
+    const float4 bv = *(const float4*)(bias + n);
+#pragma unroll
+    for (int r = 0; r < TM; ++r) {
+      const int m = m0 + r;
+      if (m >= M) break;
+      float4 v = make_float4(acc[r][0] + bv.x, acc[r][1] + bv.y, acc[r][2] + bv.z,
+                             acc[r][3] + bv.w);
+      if (pe) {
+        const float4 q = *(const float4*)(pe + (int64_t)(m % T) * d + n);
+        v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+      }
+      const int64_t row = m + (int64_t)(m / T) * out_skip;
+      *(float4*)(X + row * d + n) = v;
+    }
+  }
+}
+
+hipError_t launch_patch_embed(const void* x, int src_rows, const PatchGeom& g, int dtype,
+                              const void* W, const float* bias, const float* pe, int M, int d,
+                              int out_skip, float* X, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (d % 4 || g.K % 16 || ((uintptr_t)W & 15)) return hipErrorInvalidValue;
+  constexpr int TM = 8;
+  const size_t lds = (size_t)TM * g.K * sizeof(float);
+  if (lds > 64 * 1024) return hipErrorInvalidValue;
+  const int blocks = (M + TM - 1) / TM;
+  if (dtype == 1)
+    patch_embed_kernel<bf16_t, TM><<<blocks, 256, lds, s>>>((const bf16_t*)x, src_rows, g,
+                                                           (const bf16_t*)W, bias, pe, M, d,
+                                                           out_skip, X);
+  else
+    patch_embed_kernel<float, TM><<<blocks, 256, lds, s>>>((const float*)x, src_rows, g,
+                                                          (const float*)W, bias, pe, M, d,
+                                                          out_skip, X);
+  return hipGetLastError();
+}
+
 // P[b, tau, k] = x[b, c, f*pt + a, i*p + py, j*p + px]; one thread per element of
 // P, consecutive threads write consecutive k.
 template <typename T>

@@ -342,3 +342,21 @@ def test_video_block_teacher_forced_full_length():
     log(f"video full-length block: attention branch sampled rel-L2 {err:.2e}")
     assert err <= BF16_TOL
     assert np.isfinite(Xo).all()
+
+
+def test_fp32_narrow_decoder_uses_fused_final_layer():
+    """p = 2 gives p^2 Cout = 32 decoder outputs per token: the final LayerNorm,
+    modulation and decoder run fused (one wave per token); fp32 path."""
+    cfg = dit_inputs.workload("dit_s8_f32", p=2, N=2)
+    w = dit_inputs.make_weights(cfg)
+    inp = dit_inputs.make_inputs(cfg)
+    log("fp32 DiT-S p=2 (T=256, 32 decoder outputs) B=2")
+    m = _model(cfg, w)
+    x, t, y, _ = device_inputs(cfg, inp)
+    taps = m.make_taps(2)
+    out = np_(m.forward(x, t, y, taps=taps))
+    ref, otaps = oracle_taps(cfg, w, inp)
+    err = rel_l2(out, ref)
+    log(f"  out rel-L2 {err:.2e}")
+    assert err <= F32_TOL
+    compare_taps(cfg, taps, otaps, F32_TOL, "fp32 S p=2")
