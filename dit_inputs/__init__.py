@@ -32,6 +32,9 @@ DTYPE_BF16 = 1
 # class embeddings as two extra tokens, or as a cross-attended context
 # (itwiki page, Conditioning methods table).
 COND_ADALN_ZERO, COND_IN_CONTEXT, COND_CROSS_ATTENTION = 0, 1, 2
+# MMDiT (itwiki page, MMDiT section): text and image streams with their own
+# weights, joint attention, pooled-vector + time adaLN.
+COND_MMDIT = 3
 
 # Model sizes: (depth N, width d, heads) from the Model sizes table.
 MODEL_SIZES = {
@@ -78,6 +81,15 @@ WORKLOADS = {
         _image_config("XL", 2, 32, DTYPE_BF16, 32, True,
                       "DiT-XL/2 256x256 in-context conditioning + CFG, 32 cond + 32 null rows"),
         conditioning=COND_IN_CONTEXT, seed_idx=6),
+    # MMDiT at depth 24 (hidden 64 x 24, 24 heads: the page's size rule),
+    # 512x512 images as a 64x64x16 latent with p = 2, 333 text tokens of a
+    # 4096-wide text encoder and a 2048-wide pooled vector, velocity output.
+    "mmdit_d24_512": dict(
+        name="MMDiT depth 24 (d 1536, 24 heads), 64x64x16 latent, 333 text tokens, batch 8",
+        C=16, Cout=16, F=1, H=64, W=64, p=2, pt=1, d=1536, N=24, heads=24, mlp_hidden=6144,
+        num_classes=0, cond_dim=2048, freq_dim=256, qk_norm=0, rope3d=0, dtype=DTYPE_BF16,
+        ln_eps=1e-6, batch=8, cfg=False, scale=1.0, guided=16, conditioning=COND_MMDIT,
+        ctx_len=333, ctx_dim=4096, seed_idx=8),
     "dit_xl2_256_cfg_cross_attention": dict(
         _image_config("XL", 2, 32, DTYPE_BF16, 32, True,
                       "DiT-XL/2 256x256 cross-attention conditioning + CFG, 32 cond + 32 null rows"),
@@ -160,7 +172,7 @@ def weight_shapes(cfg: dict) -> dict:
         shapes["pool_w"] = (d, cfg["cond_dim"])
         shapes["pool_b"] = (d,)
     cond = cfg.get("conditioning", COND_ADALN_ZERO)
-    if cond == COND_ADALN_ZERO:
+    if cond in (COND_ADALN_ZERO, COND_MMDIT):
         shapes.update({"ada_w": ((6 * N + 2) * d, d), "ada_b": ((6 * N + 2) * d,)})
     shapes.update({
         "qkv_w": (N, 3 * d, d), "qkv_b": (N, 3 * d),
@@ -168,7 +180,7 @@ def weight_shapes(cfg: dict) -> dict:
         "fc1_w": (N, hid, d), "fc1_b": (N, hid),
         "fc2_w": (N, d, hid), "fc2_b": (N, d),
     })
-    if cond != COND_ADALN_ZERO:
+    if cond in (COND_IN_CONTEXT, COND_CROSS_ATTENTION):
         # per block: (shift, scale) of each LayerNorm (2 for in-context, 3 with
         # the cross-attention layer); the final layer's LayerNorm
         n_ln = 2 if cond == COND_IN_CONTEXT else 3
@@ -177,12 +189,22 @@ def weight_shapes(cfg: dict) -> dict:
         shapes.update({"xq_w": (N, d, d), "xq_b": (N, d),
                        "xkv_w": (N, 2 * d, d), "xkv_b": (N, 2 * d),
                        "xo_w": (N, d, d), "xo_b": (N, d)})
+    if cond == COND_MMDIT:
+        dh = d // cfg["heads"]
+        shapes.update({"ctx_w": (d, cfg["ctx_dim"]), "ctx_b": (d,),
+                       "cada_w": (6 * N * d, d), "cada_b": (6 * N * d,),
+                       "cqkv_w": (N, 3 * d, d), "cqkv_b": (N, 3 * d),
+                       "co_w": (N, d, d), "co_b": (N, d),
+                       "cfc1_w": (N, hid, d), "cfc1_b": (N, hid),
+                       "cfc2_w": (N, d, hid), "cfc2_b": (N, d),
+                       "qk_rms": (N, 4, dh)})
     shapes.update({"out_w": (kout, d), "out_b": (kout,)})
     return shapes
 
 
 GEMM_WEIGHTS = ("pe_w", "t1_w", "t2_w", "pool_w", "ada_w", "qkv_w", "o_w",
-                "fc1_w", "fc2_w", "out_w", "xq_w", "xkv_w", "xo_w")
+                "fc1_w", "fc2_w", "out_w", "xq_w", "xkv_w", "xo_w", "ctx_w", "cada_w",
+                "cqkv_w", "co_w", "cfc1_w", "cfc2_w")
 
 
 def make_weights(cfg: dict, seed: int | None = None, std: float = 0.02) -> dict:
@@ -298,3 +320,17 @@ def make_sampler_inputs(cfg: dict, steps: int, seed: int | None = None,
     res["pooled"] = (f32_round(rng.standard_normal((B, cfg["cond_dim"])))
                      if cfg["cond_dim"] > 0 else None)
     return res
+
+
+def make_mmdit_inputs(cfg: dict, seed: int | None = None, batch: int | None = None) -> dict:
+    """Seeded inputs of an MMDiT call: image latent x_t ~ N(0,1) [B, C, H, W]
+    and text embeddings ~ N(0,1) [B, ctx_len, ctx_dim], both in the model
+    dtype; flow time t ~ U(0,1); pooled vector ~ N(0,1) [B, cond_dim] fp32."""
+    if seed is None:
+        seed = 2000 + cfg["seed_idx"]
+    B = cfg["batch"] if batch is None else batch
+    rng = np.random.default_rng(seed)
+    return {"x_t": cast_to(rng.standard_normal((B, cfg["C"], cfg["H"], cfg["W"])), cfg["dtype"]),
+            "t": f32_round(rng.uniform(0.0, 1.0, size=B)),
+            "ctx": cast_to(rng.standard_normal((B, cfg["ctx_len"], cfg["ctx_dim"])), cfg["dtype"]),
+            "pooled": f32_round(rng.standard_normal((B, cfg["cond_dim"])))}

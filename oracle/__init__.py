@@ -48,6 +48,7 @@ from .dit_oracle import (  # noqa: F401
     rope3d_tables, embed_condition, modulation, block, forward, cfg_forward,
     cfg_combine, token_grid, block_in_context, block_cross_attention, cross_attention,
     class_embedding, block_weights, forward_packed, IN_CONTEXT, CROSS_ATTENTION,
+    MMDIT, rms_norm, mmdit_block, mmdit_block_weights, mmdit_forward,
 )
 from . import flops  # noqa: F401
 from . import sampler_oracle  # noqa: F401

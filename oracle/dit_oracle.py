@@ -521,3 +521,102 @@ def forward_packed(cfg, w, latents, t, y=None, pooled=None):
         pi = None if pooled is None else _f64(pooled)[i:i + 1]
         outs.append(forward(ci, w, x[None], _f64(t)[i:i + 1], yi, pi)[0])
     return outs
+
+
+# ---------------------------------------------------------------------------
+# MMDiT ([DiT-wiki] MMDiT section): text tokens and image patch tokens are one
+# sequence for attention, but each modality keeps its own weights for the
+# normalisation, the QKV projection and the MLP (two transformers that meet
+# only inside attention); the pooled vector and the time embedding still enter
+# through adaLN modulation; Q and K get RMSNorm.
+# Readings taken: each stream has its own adaLN-Zero modulation (six vectors
+# per block from SiLU(c)) and output projection; the context tokens are a
+# Linear(ctx_dim, d) of the given text embeddings, without position embedding,
+# and come first in the joint sequence; QK RMSNorm is per head, eps 1e-6, with
+# a learned scale 1 + g (g a dh-vector per stream for q and for k, written
+# like the LayerNorm affines); the final layer reads the image stream only.
+
+MMDIT = 3
+
+
+def rms_norm(x, w, eps=1e-6):
+    """x / sqrt(mean(x^2) + eps) * w over the last axis."""
+    x = _f64(x)
+    return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps) * _f64(w)
+
+
+def mmdit_block(cfg, wl, Xc, Xi, mod_c, mod_i):
+    """One MMDiT block.  Xc: [B, L, d] context stream, Xi: [B, T, d] image
+    stream; mod_c, mod_i: [B, 6d] (beta1, gamma1, alpha1, beta2, gamma2,
+    alpha2) of each stream.  wl holds the image stream's qkv/o/fc1/fc2 weights,
+    the context stream's c-prefixed ones, and qk_rms [4, dh] (g of q, k of the
+    image stream, then of the context stream).  Returns (Xc, Xi)."""
+    Xc, Xi = _f64(Xc), _f64(Xi)
+    B, L, d = Xc.shape
+    T = Xi.shape[1]
+    Hh = cfg["heads"]
+    dh = d // Hh
+    eps = cfg["ln_eps"]
+    mc = np.split(_f64(mod_c), 6, axis=1)
+    mi = np.split(_f64(mod_i), 6, axis=1)
+    rms = _f64(wl["qk_rms"])
+
+    def heads_qkv(h, w, b, wq, wk):
+        n = h.shape[1]
+        qkv = linear(h, w, b)
+        q, k, v = (qkv[..., i * d:(i + 1) * d].reshape(B, n, Hh, dh).transpose(0, 2, 1, 3)
+                   for i in range(3))
+        return rms_norm(q, wq, eps), rms_norm(k, wk, eps), v
+
+    qc, kc, vc = heads_qkv(modulate(layer_norm(Xc, eps), mc[0], mc[1]), wl["cqkv_w"],
+                           wl["cqkv_b"], 1.0 + rms[2], 1.0 + rms[3])
+    qi, ki, vi = heads_qkv(modulate(layer_norm(Xi, eps), mi[0], mi[1]), wl["qkv_w"],
+                           wl["qkv_b"], 1.0 + rms[0], 1.0 + rms[1])
+    a = attention(np.concatenate([qc, qi], axis=2), np.concatenate([kc, ki], axis=2),
+                  np.concatenate([vc, vi], axis=2)).transpose(0, 2, 1, 3).reshape(B, L + T, d)
+    Xc = Xc + mc[2][:, None, :] * linear(a[:, :L], wl["co_w"], wl["co_b"])
+    Xi = Xi + mi[2][:, None, :] * linear(a[:, L:], wl["o_w"], wl["o_b"])
+
+    def ffn(X, m, pre):
+        h = modulate(layer_norm(X, eps), m[3], m[4])
+        f = linear(gelu_tanh(linear(h, wl[pre + "fc1_w"], wl[pre + "fc1_b"])),
+                   wl[pre + "fc2_w"], wl[pre + "fc2_b"])
+        return X + m[5][:, None, :] * f
+
+    return ffn(Xc, mc, "c"), ffn(Xi, mi, "")
+
+
+def mmdit_block_weights(w, l):
+    keys = ("qkv_w", "qkv_b", "o_w", "o_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b", "cqkv_w",
+            "cqkv_b", "co_w", "co_b", "cfc1_w", "cfc1_b", "cfc2_w", "cfc2_b", "qk_rms")
+    return {k: w[k][l] for k in keys}
+
+
+def mmdit_forward(cfg, w, x_t, t, ctx, pooled, taps=None):
+    """MMDiT denoiser: image latent x_t [B, C, H, W], time t [B], text
+    embeddings ctx [B, L, ctx_dim], pooled vector [B, cond_dim].  Returns
+    [B, Cout, H, W]."""
+    x = _f64(x_t)
+    B = x.shape[0]
+    C, H, W, p, d, N = cfg["C"], cfg["H"], cfg["W"], cfg["p"], cfg["d"], cfg["N"]
+    gf, gh, gw = token_grid(1, H, W, p, 1)
+    Xi = linear(patchify(x[:, :, None], p, 1), w["pe_w"], w["pe_b"]) + pos_embed_2d(gh, gw, d)[None]
+    Xc = linear(ctx, w["ctx_w"], w["ctx_b"])
+    _, temb, c = embed_condition(dict(cfg, num_classes=0), w, t, None, pooled)
+    mod_i = modulation(cfg, w, c)
+    mod_c = linear(silu(c), w["cada_w"], w["cada_b"])
+    if taps is not None:
+        taps.update(c=c, mod=mod_i, cmod=mod_c, Xi0=Xi.copy(), Xc0=Xc.copy(), Xi=[], Xc=[])
+    for l in range(N):
+        Xc, Xi = mmdit_block(cfg, mmdit_block_weights(w, l), Xc, Xi,
+                             mod_c[:, 6 * d * l:6 * d * (l + 1)], mod_i[:, 6 * d * l:6 * d * (l + 1)])
+        if taps is not None:
+            taps["Xi"].append(Xi.copy())
+            taps["Xc"].append(Xc.copy())
+    fb = 6 * d * N
+    Hf = modulate(layer_norm(Xi, cfg["ln_eps"]), mod_i[:, fb:fb + d], mod_i[:, fb + d:fb + 2 * d])
+    Y = linear(Hf, w["out_w"], w["out_b"])
+    out = unpatchify(Y, cfg["Cout"], 1, H, W, p, 1)
+    if taps is not None:
+        taps.update(Y=Y, out=out)
+    return out

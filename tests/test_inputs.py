@@ -43,4 +43,5 @@ def test_workload_token_counts():
     T = {n: dit_inputs.tokens(dit_inputs.workload(n)) for n in dit_inputs.WORKLOADS}
     assert T == {"dit_s8_f32": 16, "dit_b4_bf16": 64, "dit_xl2_256_cfg": 256,
                  "dit_xl2_512_cfg": 1024, "video_xl_spacetime": 24960,
-                 "dit_xl2_256_cfg_in_context": 256, "dit_xl2_256_cfg_cross_attention": 256}
+                 "dit_xl2_256_cfg_in_context": 256, "dit_xl2_256_cfg_cross_attention": 256,
+                 "mmdit_d24_512": 1024}
