@@ -14,20 +14,22 @@ DIT_OK, DIT_EINVAL, DIT_EUNSUPPORTED, DIT_EWORKSPACE, DIT_EHIP = 0, -1, -2, -3, 
 DIT_F32, DIT_BF16 = 0, 1
 DIT_EPI_BIAS, DIT_EPI_GELU, DIT_EPI_GATED = 0, 1, 2
 DIT_SAMPLER_DDPM, DIT_SAMPLER_DPMPP_2M, DIT_SAMPLER_RF_EULER = 0, 1, 2
-DIT_COND_ADALN_ZERO, DIT_COND_IN_CONTEXT, DIT_COND_CROSS_ATTN = 0, 1, 2
+DIT_COND_ADALN_ZERO, DIT_COND_IN_CONTEXT, DIT_COND_CROSS_ATTN, DIT_COND_MMDIT = 0, 1, 2, 3
 
 
 class DitConfig(C.Structure):
     _fields_ = [(n, C.c_int) for n in (
         "in_channels", "out_channels", "frames", "height", "width", "patch", "patch_t",
         "hidden", "depth", "heads", "mlp_hidden", "num_classes", "cond_dim", "freq_dim",
-        "qk_norm", "rope3d", "dtype")] + [("ln_eps", C.c_float), ("conditioning", C.c_int)]
+        "qk_norm", "rope3d", "dtype")] + [("ln_eps", C.c_float)] + [
+        (n, C.c_int) for n in ("conditioning", "ctx_len", "ctx_dim")]
 
 
 WEIGHT_FIELDS = ("pe_w", "pe_b", "t1_w", "t1_b", "t2_w", "t2_b", "y_table", "pool_w", "pool_b",
                  "ada_w", "ada_b", "qkv_w", "qkv_b", "o_w", "o_b", "fc1_w", "fc1_b", "fc2_w",
                  "fc2_b", "out_w", "out_b", "ln_p", "final_ln", "xq_w", "xq_b", "xkv_w",
-                 "xkv_b", "xo_w", "xo_b")
+                 "xkv_b", "xo_w", "xo_b", "ctx_w", "ctx_b", "cada_w", "cada_b", "cqkv_w",
+                 "cqkv_b", "co_w", "co_b", "cfc1_w", "cfc1_b", "cfc2_w", "cfc2_b", "qk_rms")
 
 
 class DitWeights(C.Structure):
@@ -59,6 +61,9 @@ EXPORTS = {
     "dit_cfg_forward_taps": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int,
                                        C.c_float, C.c_int, C.c_void_p, C.POINTER(DitTaps),
                                        C.c_void_p, C.c_size_t, C.c_void_p]),
+    "dit_forward_ctx": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_int, C.c_void_p, C.POINTER(DitTaps), C.c_void_p,
+                                  C.c_size_t, C.c_void_p]),
     "dit_status_string": (C.c_char_p, [C.c_int]),
     "dit_last_error_message": (C.c_char_p, []),
     "dit_patchify": (C.c_int, [C.c_void_p] + [C.c_int] * 8 + [C.c_void_p, C.c_void_p]),

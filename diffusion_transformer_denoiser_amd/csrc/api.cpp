@@ -60,8 +60,10 @@ struct dit_handle {
   // conditioning design; tokens per trunk row (T + 2 in-context, else T);
   // LayerNorms per block of the in-context / cross-attention designs
   int cond, Tt, nln;
+  int Lc;            // MMDiT: text tokens per row (0 otherwise)
+  int Tf;            // tokens per row of the stream the final layer decodes
   PatchGeom gin, gout;
-  PatchGeom gouty;   // gout with T = Tt: the decoder output's row stride
+  PatchGeom gouty;   // gout with T = Tf: the decoder output's row stride
   // Second stream for the two independent halves of a batch (created on the
   // first forward, on the device current then), and the fork / join events.
   // The mutex makes each call's fork-enqueue-join sequence atomic, so calls
@@ -94,7 +96,7 @@ bool ensure_aux(const dit_handle* h) {
 namespace {
 
 struct WsLayout {
-  size_t e, th, c, sc, pp, pe, mod, ctx, kv, X, H, qkv, o, G, Y, seg, total;
+  size_t e, th, c, sc, pp, pe, mod, cmod, ctx, kv, X, H, qkv, o, G, Y, seg, total;
 };
 
 // rows: conditioning rows; M: token rows of the trunk; packed: M tokens of
@@ -115,6 +117,7 @@ WsLayout ws_layout_m(const dit_handle* h, int rows, size_t M, bool packed) {
   L.pp = take(h->cond_dim > 0 ? R * h->d * 4 : 0);          // pooled projection
   L.pe = take(h->cfg.rope3d ? 0 : (packed ? M : (size_t)h->T) * h->d * 4);  // 2-D position table
   L.mod = take(R * h->mod_stride * 4);                        // 0 without adaLN
+  L.cmod = take(h->cond == DIT_COND_MMDIT ? R * 6 * h->N * h->d * 4 : 0);   // text stream
   L.ctx = take(h->cond == DIT_COND_CROSS_ATTN ? R * 2 * h->d * es : 0);      // context tokens
   // k | v of the context tokens for every block: [rows, 2, N, 2d]
   L.kv = take(h->cond == DIT_COND_CROSS_ATTN ? R * 2 * h->N * 2 * h->d * es : 0);
@@ -159,6 +162,7 @@ hipError_t linear(const dit_handle* h, int epi, const void* A, int lda, const vo
   a.lda = lda;
   a.a_dtype = 0;
   a.src_rows = M;
+  a.seg = ep.a_seg; a.skip = ep.a_skip; a.off = ep.a_off;
   return launch_gemm_valu(epi, A_PLAIN, a, W, 0, M, N, K, ep, s);
 }
 
@@ -318,6 +322,68 @@ int run_block_variant(const dit_handle* h, int l, int rows, float* X, const void
 
 // Trunk of `rows` rows.  Row r reads latent/time/pooled row r % src_rows; rows
 // r >= null_from take the null label.  Leaves the decoder output in ws Y.
+// One MMDiT block for `rows` rows: image stream Xi [rows * T, d], text stream
+// Xc [rows * Lc, d] (fp32, in place), modulations modi (rows of mod_stride)
+// and modc (rows of 6 N d).  The two streams' q | k | v land in one joint
+// buffer [rows, Lc + T, 3d] (text tokens first) through the GEMM output row
+// map, attention runs over the joint rows, and each stream's output
+// projection reads its own rows of the joint output through the A row map.
+int run_block_mmdit(const dit_handle* h, int l, int rows, float* Xi, float* Xc, const float* modi,
+                    const float* modc, void* ws, const WsLayout& L, hipStream_t s) {
+  const int d = h->d, T = h->T, Lc = h->Lc, J = T + Lc, es = h->es;
+  const int cms = 6 * h->N * d, base = 6 * d * l;
+  void* Hb = at<void>(ws, L.H);
+  void* O = at<void>(ws, L.o);
+  void* G = at<void>(ws, L.G);
+  void* qkv = at<void>(ws, L.qkv);
+  struct Stream {
+    float* X; const float* mod; int ms; int n; const void *qkv_w, *o_w, *fc1_w, *fc2_w;
+    const float *qkv_b, *o_b, *fc1_b, *fc2_b; int seg, skip, off;
+  };
+  const Stream st[2] = {
+      {Xc, modc, cms, Lc, h->w.cqkv_w, h->w.co_w, h->w.cfc1_w, h->w.cfc2_w, h->w.cqkv_b,
+       h->w.co_b, h->w.cfc1_b, h->w.cfc2_b, Lc, T, 0},
+      {Xi, modi, h->mod_stride, T, h->w.qkv_w, h->w.o_w, h->w.fc1_w, h->w.fc2_w, h->w.qkv_b,
+       h->w.o_b, h->w.fc1_b, h->w.fc2_b, T, Lc, Lc}};
+  for (const Stream& q : st) {
+    const int M = rows * q.n;
+    DIT_HIP(launch_ln_modulate(q.X, M, q.n, d, q.mod, q.ms, base, base + d, h->eps, Hb, h->dtype,
+                               s));
+    EpiParams ep = epi0();
+    ep.bias = q.qkv_b + (size_t)l * 3 * d;
+    ep.out = qkv; ep.ldo = 3 * d;
+    ep.o_seg = q.seg; ep.o_skip = q.skip; ep.o_off = q.off;
+    DIT_HIP(linear(h, EPI_BIAS_DT, Hb, d, woff(q.qkv_w, (size_t)l * 3 * d * d, es), M, 3 * d, d,
+                   ep, s));
+  }
+  DIT_HIP(launch_qk_rms(qkv, rows, h->heads, J, Lc, h->dh, h->dtype, h->eps,
+                        h->w.qk_rms + (size_t)l * 4 * h->dh, s));
+  DIT_HIP(launch_attention(qkv, rows, h->heads, J, h->dh, h->dtype, O, s));
+  for (const Stream& q : st) {
+    const int M = rows * q.n;
+    EpiParams ep = epi0();
+    ep.bias = q.o_b + (size_t)l * d;
+    ep.out = q.X; ep.ldo = d;
+    ep.mod = q.mod; ep.mod_stride = q.ms; ep.gate_off = base + 2 * d; ep.T = q.n;
+    ep.a_seg = q.seg; ep.a_skip = q.skip; ep.a_off = q.off;
+    DIT_HIP(linear(h, EPI_GATED, O, d, woff(q.o_w, (size_t)l * d * d, es), M, d, d, ep, s));
+    DIT_HIP(launch_ln_modulate(q.X, M, q.n, d, q.mod, q.ms, base + 3 * d, base + 4 * d, h->eps, Hb,
+                               h->dtype, s));
+    ep = epi0();
+    ep.bias = q.fc1_b + (size_t)l * h->hid;
+    ep.out = G; ep.ldo = h->hid;
+    DIT_HIP(linear(h, EPI_GELU, Hb, d, woff(q.fc1_w, (size_t)l * h->hid * d, es), M, h->hid, d,
+                   ep, s));
+    ep = epi0();
+    ep.bias = q.fc2_b + (size_t)l * d;
+    ep.out = q.X; ep.ldo = d;
+    ep.mod = q.mod; ep.mod_stride = q.ms; ep.gate_off = base + 5 * d; ep.T = q.n;
+    DIT_HIP(linear(h, EPI_GATED, G, h->hid, woff(q.fc2_w, (size_t)l * d * h->hid, es), M, d,
+                   h->hid, ep, s));
+  }
+  return DIT_OK;
+}
+
 // Conditioning of `rows` rows: c (time embedding, + class row, + pooled
 // projection), SiLU(c) and all modulation vectors for adaLN-Zero; the two
 // conditioning tokens (and the context keys / values) for the other designs.
@@ -327,7 +393,7 @@ int run_conditioning(const dit_handle* h, const float* t, const int32_t* y, cons
                      int rows, int src_rows, int null_from, void* ws, const WsLayout& L,
                      hipStream_t s) {
   const int d = h->d, T = h->T;
-  const bool ada = h->cond == DIT_COND_ADALN_ZERO;
+  const bool ada = h->cond == DIT_COND_ADALN_ZERO || h->cond == DIT_COND_MMDIT;
   float* e = at<float>(ws, L.e);
   float* th = at<float>(ws, L.th);
   float* c = at<float>(ws, L.c);
@@ -403,6 +469,12 @@ int run_conditioning(const dit_handle* h, const float* t, const int32_t* y, cons
     ep = epi0();
     ep.bias = h->w.ada_b; ep.out = mod; ep.ldo = h->mod_stride;
     DIT_HIP(linear(h, EPI_BIAS_F32, sc, d, h->w.ada_w, rows, h->mod_stride, d, ep, s));
+    if (h->cond == DIT_COND_MMDIT) {
+      // the text stream's modulation vectors of every block
+      ep = epi0();
+      ep.bias = h->w.cada_b; ep.out = at<float>(ws, L.cmod); ep.ldo = 6 * h->N * d;
+      DIT_HIP(linear(h, EPI_BIAS_F32, sc, d, h->w.cada_w, rows, 6 * h->N * d, d, ep, s));
+    }
   } else {
     // The time and class embeddings as two tokens after each row's patch
     // tokens (in-context) or as each row's two context tokens.
@@ -424,10 +496,14 @@ int run_conditioning(const dit_handle* h, const float* t, const int32_t* y, cons
 }
 
 int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_t* y,
-              const float* pooled, int rows, int src_rows, int null_from, void* ws,
-              const WsLayout& L, const dit_taps* taps, hipStream_t s) {
-  const int d = h->d, T = h->T, Tt = h->Tt, M = rows * Tt;
-  const bool ada = h->cond == DIT_COND_ADALN_ZERO;
+              const float* pooled, const void* ctx, int rows, int src_rows, int null_from,
+              void* ws, const WsLayout& L, const dit_taps* taps, hipStream_t s) {
+  const int d = h->d, T = h->T, Tt = h->Tt, Tf = h->Tf, M = rows * Tt;
+  const bool mm = h->cond == DIT_COND_MMDIT;
+  const bool ada = h->cond == DIT_COND_ADALN_ZERO || mm;
+  // MMDiT: the image stream's rows * T tokens, then the text stream's rows * Lc
+  const float* cmod = at<float>(ws, L.cmod);
+  float* Xtext = at<float>(ws, L.X) + (size_t)rows * T * d;
   float* c = at<float>(ws, L.c);
   float* mod = at<float>(ws, L.mod);
   float* X = at<float>(ws, L.X);
@@ -444,7 +520,14 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
     pe = at<float>(ws, L.pe);
     DIT_HIP(launch_pos_embed_table(h->gh, h->gw, d, pe, s));
   }
-  DIT_HIP(patch_embed(h, x_t, src_rows, h->gin, pe, rows * T, Tt - T, X, s));
+  DIT_HIP(patch_embed(h, x_t, src_rows, h->gin, pe, rows * T, Tf - T, X, s));
+  if (mm) {
+    // text embeddings [rows * Lc, ctx_dim] -> the text stream
+    EpiParams ec = epi0();
+    ec.bias = h->w.ctx_b; ec.out = Xtext; ec.ldo = d;
+    DIT_HIP(linear(h, EPI_BIAS_F32, ctx, h->cfg.ctx_dim, h->w.ctx_w, rows * h->Lc, d,
+                   h->cfg.ctx_dim, ec, s));
+  }
 
   if (taps) {
     if (taps->c) DIT_HIP(hipMemcpyAsync(taps->c, c, (size_t)rows * d * 4, hipMemcpyDeviceToDevice, s));
@@ -467,10 +550,10 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
   auto final_layer = [&](float* Xg, const float* modg, int Mg, void* Hg, float* Yg,
                          hipStream_t st) -> int {
     if (ada)
-      DIT_HIP(launch_ln_modulate(Xg, Mg, Tt, d, modg, h->mod_stride, fb, fb + d, h->eps, Hg,
+      DIT_HIP(launch_ln_modulate(Xg, Mg, Tf, d, modg, h->mod_stride, fb, fb + d, h->eps, Hg,
                                  h->dtype, st));
     else
-      DIT_HIP(launch_ln_modulate(Xg, Mg, Tt, d, h->w.final_ln, 0, 0, d, h->eps, Hg, h->dtype, st));
+      DIT_HIP(launch_ln_modulate(Xg, Mg, Tf, d, h->w.final_ln, 0, 0, d, h->eps, Hg, h->dtype, st));
     EpiParams ef = epi0();
     ef.bias = h->w.out_b; ef.out = Yg; ef.ldo = h->kout;
     DIT_HIP(linear(h, EPI_BIAS_F32, Hg, d, h->w.out_w, Mg, h->kout, d, ef, st));
@@ -478,6 +561,9 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
   };
   auto one_block = [&](int l, int r0, int nr, float* Xg, const float* modg, const WsLayout& Lg,
                        hipStream_t st) -> int {
+    if (mm)
+      return run_block_mmdit(h, l, nr, Xg, Xtext + (size_t)r0 * h->Lc * d, modg,
+                             cmod + (size_t)r0 * 6 * h->N * d, ws, Lg, st);
     if (ada) return run_block(h, l, nr, Xg, modg, h->mod_stride, 6 * d * l, ws, Lg, nullptr,
                               nullptr, st);
     const size_t es = h->es;
@@ -486,19 +572,20 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
                              ws, Lg, st);
   };
   auto blocks_and_final = [&](int r0, int nr, hipStream_t st) -> int {
-    const size_t m0 = (size_t)r0 * Tt, es = h->es;
+    // scratch regions hold Tt tokens per row; the decoded stream Tf
+    const size_t m0 = (size_t)r0 * Tt, f0 = (size_t)r0 * Tf, es = h->es;
     WsLayout Lh = L;
     Lh.H += m0 * d * es;
     Lh.qkv += m0 * 3 * d * es;
     Lh.o += m0 * d * es;
     Lh.G += m0 * h->hid * es;
-    float* Xh = X + m0 * d;
+    float* Xh = X + f0 * d;
     const float* modh = mod + (size_t)r0 * h->mod_stride;
     for (int l = 0; l < h->N; ++l) {
       int rc = one_block(l, r0, nr, Xh, modh, Lh, st);
       if (rc) return rc;
     }
-    return final_layer(Xh, modh, nr * Tt, at<void>(ws, Lh.H), Y + m0 * h->kout, st);
+    return final_layer(Xh, modh, nr * Tf, at<void>(ws, Lh.H), Y + f0 * h->kout, st);
   };
 
   const int parts = rows < DIT_SPLIT ? rows : DIT_SPLIT;
@@ -532,11 +619,12 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
                              hipMemcpyDeviceToDevice, s));
   }
   {
-    int rc = final_layer(X, mod, M, Hb, Y, s);
+    int rc = final_layer(X, mod, rows * Tf, Hb, Y, s);
     if (rc) return rc;
   }
   if (taps && taps->y_final)
-    DIT_HIP(hipMemcpyAsync(taps->y_final, Y, (size_t)M * h->kout * 4, hipMemcpyDeviceToDevice, s));
+    DIT_HIP(hipMemcpyAsync(taps->y_final, Y, (size_t)rows * Tf * h->kout * 4,
+                           hipMemcpyDeviceToDevice, s));
   return DIT_OK;
 }
 
@@ -563,10 +651,15 @@ int check_ws(const dit_handle* h, int rows, const void* ws, size_t ws_bytes, WsL
 }
 
 int forward_impl(dit_handle* h, const void* x_t, const float* t, const int32_t* y,
-                 const float* pooled, int B, float* out, const dit_taps* taps, void* ws,
-                 size_t ws_bytes, void* stream) {
+                 const float* pooled, const void* ctx, int B, float* out, const dit_taps* taps,
+                 void* ws, size_t ws_bytes, void* stream) {
   if (!h) return fail(DIT_EINVAL, "handle is NULL");
   if (!x_t || !t || !out) return fail(DIT_EINVAL, "x_t, t and out must be non-NULL");
+  if (h->cond == DIT_COND_MMDIT && !ctx)
+    return fail(DIT_EINVAL, "the MMDiT design needs text embeddings (dit_forward_ctx)");
+  if (h->cond != DIT_COND_MMDIT && ctx)
+    return fail(DIT_EINVAL, "text embeddings are only taken by the MMDiT design");
+  if (ctx && ((uintptr_t)ctx & 15)) return fail(DIT_EINVAL, "ctx must be 16-byte aligned");
   if (B <= 0) return fail(DIT_EINVAL, "B must be positive (got %d)", B);
   if (h->ncls > 0 && !y) return fail(DIT_EINVAL, "class labels y are required");
   if (h->cond_dim > 0 && !pooled) return fail(DIT_EINVAL, "pooled conditioning is required");
@@ -574,7 +667,7 @@ int forward_impl(dit_handle* h, const void* x_t, const float* t, const int32_t* 
   int rc = check_ws(h, B, ws, ws_bytes, &L);
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
-  rc = run_trunk(h, x_t, t, y, pooled, B, B, B, ws, L, taps, s);
+  rc = run_trunk(h, x_t, t, y, pooled, ctx, B, B, B, ws, L, taps, s);
   if (rc) return rc;
   DIT_HIP(launch_unpatchify(at<float>(ws, L.Y), B, 0, h->gouty, h->cfg.out_channels, 0, 0.0f, 0,
                             out, s));
@@ -589,6 +682,7 @@ int cfg_forward_impl(dit_handle* h, const void* x_t, const float* t, const int32
   if (Bh <= 0 || Bh > (1 << 29)) return fail(DIT_EINVAL, "Bh must be positive (got %d)", Bh);
   if (h->ncls <= 0) return fail(DIT_EINVAL, "guidance needs a class table with a null label");
   if (h->cond_dim > 0) return fail(DIT_EUNSUPPORTED, "guidance with pooled conditioning");
+  if (h->cond == DIT_COND_MMDIT) return fail(DIT_EUNSUPPORTED, "guidance with the MMDiT design");
   if (guided < 1 || guided > h->cfg.out_channels)
     return fail(DIT_EINVAL, "guided_channels must be in [1, %d]", h->cfg.out_channels);
   if (!std::isfinite(scale)) return fail(DIT_EINVAL, "guidance scale must be finite");
@@ -596,7 +690,7 @@ int cfg_forward_impl(dit_handle* h, const void* x_t, const float* t, const int32
   int rc = check_ws(h, 2 * Bh, ws, ws_bytes, &L);
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
-  rc = run_trunk(h, x_t, t, y, nullptr, 2 * Bh, Bh, Bh, ws, L, taps, s);
+  rc = run_trunk(h, x_t, t, y, nullptr, nullptr, 2 * Bh, Bh, Bh, ws, L, taps, s);
   if (rc) return rc;
   DIT_HIP(launch_unpatchify(at<float>(ws, L.Y), Bh, Bh, h->gouty, h->cfg.out_channels, guided,
                             scale, 1, out, s));
@@ -883,10 +977,28 @@ int dit_create(const dit_config* cfg, const dit_weights* w, dit_handle** out) {
     return fail(DIT_EUNSUPPORTED, "3-D RoPE needs head dim divisible by 6 with even thirds");
   if (c.qk_norm != 0 && c.qk_norm != 1) return fail(DIT_EINVAL, "qk_norm must be 0 or 1");
   if (c.rope3d != 0 && c.rope3d != 1) return fail(DIT_EINVAL, "rope3d must be 0 or 1");
-  if (c.conditioning < DIT_COND_ADALN_ZERO || c.conditioning > DIT_COND_CROSS_ATTN)
+  if (c.conditioning < DIT_COND_ADALN_ZERO || c.conditioning > DIT_COND_MMDIT)
     return fail(DIT_EINVAL, "unknown conditioning design %d", c.conditioning);
-  const bool ada = c.conditioning == DIT_COND_ADALN_ZERO;
+  const bool mm = c.conditioning == DIT_COND_MMDIT;
+  const bool ada = c.conditioning == DIT_COND_ADALN_ZERO || mm;
   const bool xattn = c.conditioning == DIT_COND_CROSS_ATTN;
+  if (mm) {
+    if (c.num_classes != 0 || c.cond_dim <= 0)
+      return fail(DIT_EUNSUPPORTED, "the MMDiT design takes a pooled vector and no class table");
+    if (c.ctx_len <= 0 || c.ctx_dim <= 0 || c.ctx_dim % 64)
+      return fail(DIT_EUNSUPPORTED, "MMDiT needs ctx_len > 0 and ctx_dim a positive multiple of 64");
+    if (c.rope3d || c.qk_norm || gf != 1)
+      return fail(DIT_EUNSUPPORTED, "MMDiT takes images (frames / patch_t == 1), no RoPE or qk_norm");
+    if (!w->ctx_w || !w->ctx_b || !w->cada_w || !w->cada_b || !w->cqkv_w || !w->cqkv_b ||
+        !w->co_w || !w->co_b || !w->cfc1_w || !w->cfc1_b || !w->cfc2_w || !w->cfc2_b ||
+        !w->qk_rms)
+      return fail(DIT_EINVAL, "an MMDiT weight pointer is NULL");
+    const void* mp[] = {w->ctx_w, w->cada_w, w->cqkv_w, w->co_w, w->cfc1_w, w->cfc2_w};
+    for (const void* p : mp)
+      if ((uintptr_t)p & 15) return fail(DIT_EINVAL, "GEMM weights must be 16-byte aligned");
+  } else if (c.ctx_len != 0 || c.ctx_dim != 0) {
+    return fail(DIT_EINVAL, "ctx_len / ctx_dim are for the MMDiT design only (set them to 0)");
+  }
   if (!ada && (c.num_classes <= 0 || c.cond_dim > 0))
     return fail(DIT_EUNSUPPORTED,
                 "the in-context and cross-attention designs need a class table and no pooled "
@@ -906,7 +1018,7 @@ int dit_create(const dit_config* cfg, const dit_weights* w, dit_handle** out) {
   for (const void* p : ptrs)
     if ((uintptr_t)p & 15) return fail(DIT_EINVAL, "GEMM weights must be 16-byte aligned");
   const int64_t T = (int64_t)gf * (c.height / c.patch) * (c.width / c.patch);
-  if (T > (1 << 26)) return fail(DIT_EINVAL, "too many tokens");
+  if (T + (mm ? c.ctx_len : 0) > (1 << 26)) return fail(DIT_EINVAL, "too many tokens");
 
   dit_handle* h = new (std::nothrow) dit_handle;
   if (!h) return fail(DIT_EINVAL, "out of host memory");
@@ -921,13 +1033,15 @@ int dit_create(const dit_config* cfg, const dit_weights* w, dit_handle** out) {
   h->kin = c.patch_t * c.patch * c.patch * c.in_channels;
   h->kout = c.patch_t * c.patch * c.patch * c.out_channels;
   h->cond = c.conditioning;
-  h->Tt = h->T + (c.conditioning == DIT_COND_IN_CONTEXT ? 2 : 0);
+  h->Lc = mm ? c.ctx_len : 0;
+  h->Tt = h->T + (c.conditioning == DIT_COND_IN_CONTEXT ? 2 : 0) + h->Lc;
+  h->Tf = mm ? h->T : h->Tt;
   h->nln = xattn ? 3 : 2;
   h->mod_stride = ada ? (6 * c.depth + 2) * c.hidden : 0;
   h->gin = make_geom(c.in_channels, c.frames, c.height, c.width, c.patch, c.patch_t);
   h->gout = make_geom(c.out_channels, c.frames, c.height, c.width, c.patch, c.patch_t);
   h->gouty = h->gout;
-  h->gouty.T = h->Tt;
+  h->gouty.T = h->Tf;
   *out = h;
   return ok();
 }
@@ -951,13 +1065,20 @@ int dit_workspace_size(const dit_handle* h, int rows, size_t* bytes) {
 
 int dit_forward(dit_handle* h, const void* x_t, const float* t, const int32_t* y,
                 const float* pooled, int B, float* out, void* ws, size_t ws_bytes, void* stream) {
-  return forward_impl(h, x_t, t, y, pooled, B, out, nullptr, ws, ws_bytes, stream);
+  return forward_impl(h, x_t, t, y, pooled, nullptr, B, out, nullptr, ws, ws_bytes, stream);
 }
 
 int dit_forward_taps(dit_handle* h, const void* x_t, const float* t, const int32_t* y,
                      const float* pooled, int B, float* out, const dit_taps* taps, void* ws,
                      size_t ws_bytes, void* stream) {
-  return forward_impl(h, x_t, t, y, pooled, B, out, taps, ws, ws_bytes, stream);
+  return forward_impl(h, x_t, t, y, pooled, nullptr, B, out, taps, ws, ws_bytes, stream);
+}
+
+int dit_forward_ctx(dit_handle* h, const void* x_t, const float* t, const float* pooled,
+                    const void* ctx, int B, float* out, const dit_taps* taps, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (!ctx) return fail(DIT_EINVAL, "ctx must be non-NULL");
+  return forward_impl(h, x_t, t, nullptr, pooled, ctx, B, out, taps, ws, ws_bytes, stream);
 }
 
 int dit_cfg_forward(dit_handle* h, const void* x_t, const float* t, const int32_t* y, int Bh,
@@ -1131,6 +1252,8 @@ int dit_sample(dit_handle* h, const dit_sampler* sp, float* x, const int32_t* y,
   int rc = check_sampler(sp);
   if (rc) return rc;
   if (!x) return fail(DIT_EINVAL, "x must be non-NULL");
+  if (h->cond == DIT_COND_MMDIT)
+    return fail(DIT_EUNSUPPORTED, "the sampling loop does not take text embeddings (MMDiT)");
   const int C = h->cfg.in_channels, Cout = h->cfg.out_channels, S = sp->num_steps;
   rc = check_sample_model(C, Cout);
   if (rc) return rc;
@@ -1164,9 +1287,9 @@ int dit_sample(dit_handle* h, const dit_sampler* sp, float* x, const int32_t* y,
   const void* x_in = xm ? (const void*)xm : (const void*)x;
   for (int k = 0; k < S; ++k) {
     if (guided_channels > 0)
-      rc = run_trunk(h, x_in, tvec, y, nullptr, rows, B, B, ws, L, nullptr, s);
+      rc = run_trunk(h, x_in, tvec, y, nullptr, nullptr, rows, B, B, ws, L, nullptr, s);
     else
-      rc = run_trunk(h, x_in, tvec, y, pooled, B, B, B, ws, L, nullptr, s);
+      rc = run_trunk(h, x_in, tvec, y, pooled, nullptr, B, B, B, ws, L, nullptr, s);
     if (rc) return rc;
     SamplerStepArgs a;
     memset(&a, 0, sizeof a);

@@ -101,7 +101,17 @@ struct EpiParams {
   // gated residual of packed sequences: the gate row of output row m is
   // tok_seg[m] (sequences start at multiples of 32 rows); else m / T
   const int* tok_seg;
+  // Row maps (0 = identity): GEMM row m reads A row a_map(m) and the bias /
+  // bf16 epilogues write out row o_map(m), with
+  // map(m) = m + (m / seg) * skip + off.  They interleave two token streams
+  // of a row (MMDiT: text tokens, then image tokens) in one buffer.
+  int a_seg, a_skip, a_off;
+  int o_seg, o_skip, o_off;
 };
+
+__device__ __host__ __forceinline__ int64_t row_map(int64_t m, int seg, int skip, int off) {
+  return seg ? m + (m / seg) * skip + off : m;
+}
 
 // ---------------------------------------------------------------------------
 // Launchers (each returns hipGetLastError() after the launch).
@@ -152,6 +162,7 @@ struct ALoad {
   int a_dtype;          // 0 fp32, 1 bf16
   int src_rows;         // A_PLAIN: row r reads row r % src_rows; A_PATCH: latent rows
   PatchGeom g;          // A_PATCH only
+  int seg, skip, off;   // A_PLAIN: row map of the source row (see EpiParams), 0 = identity
 };
 hipError_t launch_gemm_valu(int epi, int asrc, const ALoad& a, const void* W, int w_dtype,
                             int M, int N, int K, const EpiParams& ep, hipStream_t s);
@@ -167,6 +178,11 @@ hipError_t launch_qk_norm_rope(void* qkv, int B, int heads, int T, int dh, int d
                                int qk_norm, float eps, int rope, int gh, int gw, hipStream_t s);
 hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, int dtype, void* o,
                             hipStream_t s);
+// RMSNorm with scale 1 + g of every head's q and k in the packed qkv [B*T, 3
+// H dh], in place: tokens t < L of a row use g4[2], g4[3] (q, k), the others
+// g4[0], g4[1] (g4 [4, dh]).
+hipError_t launch_qk_rms(void* qkv, int B, int heads, int T, int L, int dh, int dtype, float eps,
+                         const float* g4, hipStream_t s);
 
 // Packed sequences: sequence j owns tokens [tok[j], tok[j + 1]) of the packed
 // rows; attention stays inside each sequence (block-diagonal).  At most

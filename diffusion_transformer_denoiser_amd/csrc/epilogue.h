@@ -35,7 +35,7 @@ __device__ __forceinline__ void epi_apply(const EpiParams& ep, int m, int n, flo
     c[o] = v;
     ((DT*)ep.silu_out)[o] = from_f<DT>(silu_f(v));
   } else if constexpr (EPI == EPI_BIAS_DT) {
-    ((DT*)ep.out)[(int64_t)m * ep.ldo + n] = from_f<DT>(v);
+    ((DT*)ep.out)[row_map(m, ep.o_seg, ep.o_skip, ep.o_off) * ep.ldo + n] = from_f<DT>(v);
   } else if constexpr (EPI == EPI_GATED) {
     int b = ep.tok_seg ? ep.tok_seg[m] : m / ep.T;
     float g = ep.mod ? ep.mod[(int64_t)b * ep.mod_stride + ep.gate_off + n] : 1.0f;

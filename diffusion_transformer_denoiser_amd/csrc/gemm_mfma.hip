@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
     const bool is_a = c < NA;
     const int s = (w * (is_a ? NA : NB) + (is_a ? c : c - NA)) * 64 + lane;
     const int r = s / CPR, ch = (s % CPR) ^ row_key<BK>(r);
-    src[c] = is_a ? A + (int64_t)min(m0 + r, M - 1) * lda + ch * 8
+    src[c] = is_a ? A + row_map(min(m0 + r, M - 1), ep.a_seg, ep.a_skip, ep.a_off) * lda + ch * 8
                   : W + (int64_t)min(n0 + r, N - 1) * K + ch * 8;
   }
   int boff[L];
@@ -159,7 +159,8 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
   for (int c = 0; c < L; ++c)
     boff[c] = (int)((const char*)src[c] - (c < NA ? (const char*)A : (const char*)W));
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)A, (short)0, (int)(((int64_t)(M - 1) * lda + K) * 2), 0x00020000);
+      (void*)A, (short)0,
+      (int)((row_map(M - 1, ep.a_seg, ep.a_skip, ep.a_off) * lda + K) * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t wrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)((int64_t)N * K * 2), 0x00020000);
   auto copy = [&](int kt, int c) {
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
     // that have no gate (plain residual add), run a two-deep pipeline over
     // batches of 4 rows x TN columns per lane instead: batch q+1 is loaded
     // before batch q is stored.
-    if (full && (!ep.mod || ep.tok_seg || ep.T % 32 == 0)) {
+    if (full && !ep.o_seg && (!ep.mod || ep.tok_seg || ep.T % 32 == 0)) {
       float gv[TM][TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
       return;
     }
   } else if constexpr (EPI == EPI_BIAS_F32) {
-    if (full) {
+    if (full && !ep.o_seg) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -327,6 +328,7 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
       const bool odd = lane & 1;
       const uint32_t sel = odd ? 0x03020706u : 0x05040100u;   // (q.hi, p.hi) : (p.lo, q.lo)
       bf16_t* ot = (bf16_t*)ep.out + (int64_t)(mrow + odd) * ep.ldo + (ncol & ~1);
+      bf16_t* oc = (bf16_t*)ep.out + (ncol & ~1);   // row-mapped outputs
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -349,7 +351,12 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
             const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xB1, 0xF,
                                                                          0xF, false);
             const uint32_t word = __builtin_amdgcn_perm(other, mine, sel);
-            *(uint32_t*)(ot + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * ep.ldo + j * 32) = word;
+            const int rr = i * 32 + 8 * (r >> 2) + (r & 3);
+            if (ep.o_seg)
+              *(uint32_t*)(oc + row_map(mrow + odd + rr, ep.o_seg, ep.o_skip, ep.o_off) * ep.ldo +
+                           j * 32) = word;
+            else
+              *(uint32_t*)(ot + (int64_t)rr * ep.ldo + j * 32) = word;
           }
       return;
     }
@@ -366,7 +373,7 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
         const int n = ncol + j * 32;
         if (n >= N) continue;
         const float v = acc[i][j][r];
-        const int64_t o = (int64_t)m * ep.ldo + n;
+        const int64_t o = row_map(m, ep.o_seg, ep.o_skip, ep.o_off) * ep.ldo + n;
         if constexpr (EPI == EPI_BIAS_F32) {
           ((float*)ep.out)[o] = v;
         } else if constexpr (EPI == EPI_BIAS_DT) {
@@ -392,7 +399,8 @@ hipError_t run(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   // bf16 outputs are stored as 4-byte column pairs
   const int vec = ((uintptr_t)ep.out & 3) == 0 && ep.ldo % 2 == 0;
-  const bool buf = ((int64_t)(M - 1) * lda + K) * 2 < (1LL << 31) && (int64_t)N * K * 2 < (1LL << 31);
+  const bool buf = (row_map(M - 1, ep.a_seg, ep.a_skip, ep.a_off) * lda + K) * 2 < (1LL << 31) &&
+                   (int64_t)N * K * 2 < (1LL << 31);
 #define DIT_GEMM_LAUNCH(SWZ, BUF)                                                                 \
   gemm_bf16_kernel<EPI, BM, BN, BK, MINWG, SWZ, 1, BUF><<<tiles, 256, 0, s>>>(A, lda, W, M, N, K, \
                                                                            ep, vec)

@@ -19,7 +19,8 @@ __device__ __forceinline__ float load_a(const ALoad& a, int m, int k) {
     return to_f<AT>(((const AT*)a.ptr)[(int64_t)(b % a.src_rows) * row +
                                        patch_src_offset(a.g, tau, k)]);
   } else {
-    return to_f<AT>(((const AT*)a.ptr)[(int64_t)(m % a.src_rows) * a.lda + k]);
+    const int64_t row = row_map(m % a.src_rows, a.seg, a.skip, a.off);
+    return to_f<AT>(((const AT*)a.ptr)[row * a.lda + k]);
   }
 }
 

@@ -102,7 +102,9 @@ hipError_t launch_ln_modulate(const float* X, int M, int T, int d, const float* 
 template <int DH, typename DT>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(DT* __restrict__ qkv, int64_t rows,
                                                            int heads, int T, int qk_norm,
-                                                           float eps, int rope, int gh, int gw) {
+                                                           float eps, int rope, int gh, int gw,
+                                                           const float* __restrict__ rms_g,
+                                                           int L) {
   int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= 2 * rows) return;
   const int which = idx >= rows;                 // 0: q, 1: k
@@ -113,7 +115,19 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(DT* __restrict__ qkv,
   float x[DH];
 #pragma unroll
   for (int e = 0; e < DH; ++e) x[e] = to_f<DT>(p[e]);
-  if (qk_norm) {
+  if (qk_norm == 2) {
+    // RMSNorm with scale 1 + g; g of q or k of the text stream for the first
+    // L tokens of a row, of the image stream for the rest (rms_g [4, DH]:
+    // image q, image k, text q, text k)
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DH; ++e) ss += x[e] * x[e];
+    const float rr = 1.0f / sqrtf(ss * (1.0f / DH) + eps);
+    const int t = (int)(bt % T);
+    const float* g = rms_g + ((t < L ? 2 : 0) + which) * DH;
+#pragma unroll
+    for (int e = 0; e < DH; ++e) x[e] = x[e] * rr * (1.0f + g[e]);
+  } else if (qk_norm) {
     float s = 0.0f;
 #pragma unroll
     for (int e = 0; e < DH; ++e) s += x[e];
@@ -155,18 +169,43 @@ hipError_t launch_qk_norm_rope(void* qkv, int B, int heads, int T, int dh, int d
   if (dh == 72) {
     if (dtype == 1)
       qk_norm_rope_kernel<72, bf16_t><<<blocks, 256, 0, s>>>((bf16_t*)qkv, rows, heads, T,
-                                                             qk_norm, eps, rope, gh, gw);
+                                                             qk_norm, eps, rope, gh, gw, nullptr, 0);
     else
       qk_norm_rope_kernel<72, float><<<blocks, 256, 0, s>>>((float*)qkv, rows, heads, T, qk_norm,
-                                                            eps, rope, gh, gw);
+                                                            eps, rope, gh, gw, nullptr, 0);
   } else if (dh == 64) {
     if (rope) return hipErrorInvalidValue;
     if (dtype == 1)
       qk_norm_rope_kernel<64, bf16_t><<<blocks, 256, 0, s>>>((bf16_t*)qkv, rows, heads, T,
-                                                             qk_norm, eps, 0, gh, gw);
+                                                             qk_norm, eps, 0, gh, gw, nullptr, 0);
     else
       qk_norm_rope_kernel<64, float><<<blocks, 256, 0, s>>>((float*)qkv, rows, heads, T, qk_norm,
-                                                            eps, 0, gh, gw);
+                                                            eps, 0, gh, gw, nullptr, 0);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_rms(void* qkv, int B, int heads, int T, int L, int dh, int dtype, float eps,
+                         const float* g4, hipStream_t s) {
+  const int64_t rows = (int64_t)B * T * heads;
+  if (rows <= 0) return hipSuccess;
+  const int blocks = (int)((2 * rows + 255) / 256);
+  if (dh == 64) {
+    if (dtype == 1)
+      qk_norm_rope_kernel<64, bf16_t><<<blocks, 256, 0, s>>>((bf16_t*)qkv, rows, heads, T, 2, eps,
+                                                             0, 1, 1, g4, L);
+    else
+      qk_norm_rope_kernel<64, float><<<blocks, 256, 0, s>>>((float*)qkv, rows, heads, T, 2, eps, 0,
+                                                            1, 1, g4, L);
+  } else if (dh == 72) {
+    if (dtype == 1)
+      qk_norm_rope_kernel<72, bf16_t><<<blocks, 256, 0, s>>>((bf16_t*)qkv, rows, heads, T, 2, eps,
+                                                             0, 1, 1, g4, L);
+    else
+      qk_norm_rope_kernel<72, float><<<blocks, 256, 0, s>>>((float*)qkv, rows, heads, T, 2, eps, 0,
+                                                            1, 1, g4, L);
   } else {
     return hipErrorInvalidValue;
   }

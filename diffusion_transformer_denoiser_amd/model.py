@@ -21,7 +21,8 @@ import torch
 from . import _lib
 
 GEMM_WEIGHTS = ("pe_w", "t1_w", "t2_w", "pool_w", "ada_w", "qkv_w", "o_w", "fc1_w", "fc2_w",
-                "out_w", "xq_w", "xkv_w", "xo_w")
+                "out_w", "xq_w", "xkv_w", "xo_w", "ctx_w", "cada_w", "cqkv_w", "co_w", "cfc1_w",
+                "cfc2_w")
 
 
 def torch_dtype(code: int) -> torch.dtype:
@@ -43,7 +44,8 @@ def config_struct(cfg: dict) -> _lib.DitConfig:
         heads=cfg["heads"], mlp_hidden=cfg["mlp_hidden"], num_classes=cfg["num_classes"],
         cond_dim=cfg["cond_dim"], freq_dim=cfg["freq_dim"], qk_norm=cfg["qk_norm"],
         rope3d=cfg["rope3d"], dtype=cfg["dtype"], ln_eps=cfg["ln_eps"],
-        conditioning=cfg.get("conditioning", _lib.DIT_COND_ADALN_ZERO))
+        conditioning=cfg.get("conditioning", _lib.DIT_COND_ADALN_ZERO),
+        ctx_len=cfg.get("ctx_len", 0), ctx_dim=cfg.get("ctx_dim", 0))
 
 
 def upload(a, dtype: torch.dtype, device) -> torch.Tensor:
@@ -124,8 +126,12 @@ class DiT:
         self.handle = h
         self._ws = None
         self.T = (cfg["F"] // cfg["pt"]) * (cfg["H"] // cfg["p"]) * (cfg["W"] // cfg["p"])
-        # tokens per trunk row: the in-context design appends two
-        self.Tt = self.T + (2 if cfg.get("conditioning", 0) == _lib.DIT_COND_IN_CONTEXT else 0)
+        # tokens per trunk row: the in-context design appends two, MMDiT
+        # carries ctx_len text tokens beside the image tokens
+        cond = cfg.get("conditioning", 0)
+        self.Lc = cfg.get("ctx_len", 0) if cond == _lib.DIT_COND_MMDIT else 0
+        self.Tt = self.T + (2 if cond == _lib.DIT_COND_IN_CONTEXT else 0) + self.Lc
+        self.Tf = self.T if cond == _lib.DIT_COND_MMDIT else self.Tt   # decoded tokens per row
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -158,10 +164,11 @@ class DiT:
         f = dict(device=self.device, dtype=torch.float32)
         return dict(c=torch.empty(rows, c["d"], **f),
                     mod=(torch.empty(rows, (6 * c["N"] + 2) * c["d"], **f)
-                         if c.get("conditioning", 0) == _lib.DIT_COND_ADALN_ZERO else None),
+                         if c.get("conditioning", 0) in (_lib.DIT_COND_ADALN_ZERO,
+                                                         _lib.DIT_COND_MMDIT) else None),
                     x_embed=torch.empty(M, c["d"], **f),
                     x_blocks=torch.empty(c["N"], M, c["d"], **f),
-                    y_final=torch.empty(M, kout, **f))
+                    y_final=torch.empty(rows * self.Tf, kout, **f))
 
     @staticmethod
     def _taps_struct(taps):
@@ -185,6 +192,24 @@ class DiT:
                                            B, _ptr(out), self._taps_struct(taps), _ptr(ws),
                                            ws.numel(), _stream(self.device))
         _lib.check(rc)
+        return out
+
+    def forward_ctx(self, x_t, t, pooled, ctx, out=None, taps=None) -> torch.Tensor:
+        """MMDiT forward (``dit_forward_ctx``): ctx [B, ctx_len, ctx_dim] text
+        embeddings in the model dtype, pooled [B, cond_dim] fp32."""
+        B = x_t.shape[0]
+        self._check_input(x_t, t, None, pooled, B)
+        c = self.cfg
+        if (ctx.device != self.device or not ctx.is_contiguous() or ctx.dtype != self.dtype
+                or tuple(ctx.shape) != (B, c["ctx_len"], c["ctx_dim"])):
+            raise ValueError(f"ctx must be a contiguous {self.dtype} tensor "
+                             f"[{B}, {c['ctx_len']}, {c['ctx_dim']}] on {self.device}")
+        if out is None:
+            out = torch.empty(self.out_shape(B), device=self.device, dtype=torch.float32)
+        ws = self.workspace(B)
+        _lib.check(self.lib.dit_forward_ctx(self.handle, _ptr(x_t), _ptr(t), _ptr(pooled),
+                                            _ptr(ctx), B, _ptr(out), self._taps_struct(taps),
+                                            _ptr(ws), ws.numel(), _stream(self.device)))
         return out
 
     def cfg_forward(self, x_t, t, y, scale: float, guided: int, out=None, taps=None):

@@ -98,6 +98,15 @@ extern "C" {
 #define DIT_COND_ADALN_ZERO 0
 #define DIT_COND_IN_CONTEXT 1
 #define DIT_COND_CROSS_ATTN 2
+/* MMDiT (itwiki page, MMDiT section): ctx_len text tokens per row (a
+ * Linear(ctx_dim, d) of the given text embeddings) and the image patch tokens
+ * are one sequence for attention, but each stream has its own adaLN-Zero
+ * modulation, LayerNorms, QKV and output projections and FFN; q and k get a
+ * per-head RMSNorm with scale 1 + g (g per stream); the pooled vector and the
+ * time embedding enter through the modulations; the final layer reads the
+ * image stream.  Needs num_classes == 0, no rope3d, ctx_dim % 64 == 0; runs
+ * through dit_forward_ctx. */
+#define DIT_COND_MMDIT      3
 
 /* Model configuration.  Supported: hidden % 128 == 0, hidden <= 2048,
  * head dim hidden/heads in {64, 72}, mlp_hidden % 64 == 0, freq_dim even.
@@ -124,6 +133,8 @@ typedef struct dit_config {
   int dtype;         /* DIT_F32 or DIT_BF16: GEMM operand / activation dtype */
   float ln_eps;      /* LayerNorm epsilon (1e-6) */
   int conditioning;  /* DIT_COND_* */
+  int ctx_len;       /* MMDiT: text tokens per row (0 otherwise) */
+  int ctx_dim;       /* MMDiT: width of the text embeddings */
 } dit_config;
 
 /* Caller-owned device pointers.  "W" = model dtype, "f32" = float.
@@ -165,6 +176,21 @@ typedef struct dit_weights {
   const float* xkv_b;   /* f32 [N, 2d] */
   const void*  xo_w;    /* W   [N, d, d]   output projection */
   const float* xo_b;    /* f32 [N, d] */
+  /* MMDiT only: the text stream's weights (ada_w / qkv_w / ... above are the
+   * image stream's) */
+  const void*  ctx_w;   /* W   [d, ctx_dim] text-token embedding */
+  const float* ctx_b;   /* f32 [d] */
+  const void*  cada_w;  /* W   [6N d, d]   text-stream modulation (block order as ada_w) */
+  const float* cada_b;  /* f32 [6N d] */
+  const void*  cqkv_w;  /* W   [N, 3d, d] */
+  const float* cqkv_b;  /* f32 [N, 3d] */
+  const void*  co_w;    /* W   [N, d, d] */
+  const float* co_b;    /* f32 [N, d] */
+  const void*  cfc1_w;  /* W   [N, hid, d] */
+  const float* cfc1_b;  /* f32 [N, hid] */
+  const void*  cfc2_w;  /* W   [N, d, hid] */
+  const float* cfc2_b;  /* f32 [N, d] */
+  const float* qk_rms;  /* f32 [N, 4, dh] g of the image q, image k, text q, text k */
 } dit_weights;
 
 typedef struct dit_handle dit_handle;
@@ -207,6 +233,14 @@ int dit_forward(dit_handle* h, const void* x_t, const float* t, const int32_t* y
 int dit_cfg_forward(dit_handle* h, const void* x_t, const float* t, const int32_t* y, int Bh,
                     float s, int guided_channels, float* out, void* ws, size_t ws_bytes,
                     void* stream);
+
+/* MMDiT forward for B rows: ctx [B, ctx_len, ctx_dim] text embeddings in the
+ * model dtype; pooled as for dit_forward; out [B, Cout, H, W] fp32.  Taps (may
+ * be NULL): x_embed / x_blocks hold the image stream's B*T rows followed by
+ * the text stream's B*ctx_len rows. */
+int dit_forward_ctx(dit_handle* h, const void* x_t, const float* t, const float* pooled,
+                    const void* ctx, int B, float* out, const dit_taps* taps, void* ws,
+                    size_t ws_bytes, void* stream);
 
 /* dit_forward / dit_cfg_forward that also write the taps (may be NULL). */
 int dit_forward_taps(dit_handle* h, const void* x_t, const float* t, const int32_t* y,

@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
               "dit_status_string", "dit_patchify", "dit_unpatchify", "dit_timestep_embed",
               "dit_attention", "dit_linear", "dit_block_forward", "dit_sampler_coefficients",
               "dit_sampler_step", "dit_sample_workspace_size", "dit_sample",
-              "dit_packed_workspace_size", "dit_forward_packed"):
+              "dit_packed_workspace_size", "dit_forward_packed", "dit_forward_ctx"):
         assert n in names
     assert set(names) == set(_lib.EXPORTS), "binding and header disagree"
 
@@ -41,9 +41,9 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_config_struct_size_matches_header():
-    # 17 ints + 1 float + 1 int
-    assert C.sizeof(_lib.DitConfig) == 19 * 4
-    assert C.sizeof(_lib.DitWeights) == 29 * C.sizeof(C.c_void_p)
+    # 17 ints + 1 float + 3 ints
+    assert C.sizeof(_lib.DitConfig) == 21 * 4
+    assert C.sizeof(_lib.DitWeights) == 42 * C.sizeof(C.c_void_p)
 
 
 def _cfg(**kw):
@@ -81,7 +81,16 @@ def _create(cfg, w):
     (dict(frames=4), _lib.DIT_EUNSUPPORTED),       # 2-D PE with several frames
     (dict(rope3d=1, hidden=1024), _lib.DIT_EUNSUPPORTED),  # RoPE thirds of dh 64
     (dict(ln_eps=0.0), _lib.DIT_EINVAL),
-    (dict(conditioning=3), _lib.DIT_EINVAL),
+    (dict(conditioning=4), _lib.DIT_EINVAL),
+    (dict(ctx_len=7), _lib.DIT_EINVAL),                              # text tokens without MMDiT
+    (dict(conditioning=3, num_classes=0, cond_dim=64, ctx_len=7, ctx_dim=96),
+     _lib.DIT_EUNSUPPORTED),                                         # ctx_dim % 64
+    (dict(conditioning=3, num_classes=1000, cond_dim=64, ctx_len=7, ctx_dim=64),
+     _lib.DIT_EUNSUPPORTED),                                         # MMDiT takes no class table
+    (dict(conditioning=3, num_classes=0, cond_dim=0, ctx_len=7, ctx_dim=64),
+     _lib.DIT_EUNSUPPORTED),                                         # nor runs without a pooled vector
+    (dict(conditioning=3, num_classes=0, cond_dim=64, ctx_len=0, ctx_dim=64),
+     _lib.DIT_EUNSUPPORTED),
     (dict(conditioning=1, num_classes=0), _lib.DIT_EUNSUPPORTED),   # needs a class table
     (dict(conditioning=2, cond_dim=4096), _lib.DIT_EUNSUPPORTED),   # no pooled conditioning
 ])
@@ -109,6 +118,43 @@ def test_conditioning_designs_check_their_weights():
     assert rc == _lib.DIT_EINVAL
     rc, h = _create(_cfg(conditioning=0), _weights(ln_p=1, final_ln=1, xq_w=1))
     assert rc == _lib.DIT_OK
+    lib.dit_destroy(h)
+
+
+@needs_lib
+def test_mmdit_design_checks_weights_and_entry_points():
+    lib = _lib.load()
+    mm = dict(conditioning=3, num_classes=0, cond_dim=64, ctx_len=7, ctx_dim=64)
+    rc, _ = _create(_cfg(**mm), _weights(cfc2_w=1))
+    assert rc == _lib.DIT_EINVAL
+    rc, _ = _create(_cfg(**mm), _weights(qk_rms=1))
+    assert rc == _lib.DIT_EINVAL
+    rc, h = _create(_cfg(**mm), _weights(y_table=1))
+    assert rc == _lib.DIT_OK
+    try:
+        need = C.c_size_t()
+        assert lib.dit_workspace_size(h, 2, C.byref(need)) == 0
+        p = C.c_void_p(0x200000)
+        # the plain forward takes no text embeddings; the ctx entry needs them
+        assert lib.dit_forward(h, p, p, None, p, 2, p, p, need.value, None) == _lib.DIT_EINVAL
+        assert lib.dit_forward_ctx(h, p, p, p, None, 2, p, None, p, need.value,
+                                   None) == _lib.DIT_EINVAL
+        assert lib.dit_forward_ctx(h, p, p, p, p, 2, p, None, p, need.value - 1,
+                                   None) == _lib.DIT_EWORKSPACE
+        assert lib.dit_forward_ctx(h, p, p, None, p, 2, p, None, p, need.value,
+                                   None) == _lib.DIT_EINVAL        # pooled vector missing
+        assert lib.dit_block_forward(h, 0, 2, p, p, p, None, None, p, need.value,
+                                     None) == _lib.DIT_EUNSUPPORTED
+    finally:
+        lib.dit_destroy(h)
+    # the ctx entry rejects the other designs
+    rc, h = _create(_cfg(), _weights())
+    assert rc == _lib.DIT_OK
+    need = C.c_size_t()
+    assert lib.dit_workspace_size(h, 2, C.byref(need)) == 0
+    p = C.c_void_p(0x200000)
+    assert lib.dit_forward_ctx(h, p, p, None, p, 2, p, None, p, need.value,
+                               None) == _lib.DIT_EINVAL
     lib.dit_destroy(h)
 
 
