@@ -86,9 +86,25 @@ def blas_threads() -> int:
     return os.cpu_count() or 1
 
 
+def cpu_baseline_mmdit(cfg, w, inp, rows: int, trunk_rows: int):
+    """fp64 oracle on `rows` of the MMDiT workload's rows."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.mmdit_forward(cfg, w, inp["x_t"][:rows], inp["t"][:rows], inp["ctx"][:rows],
+                         inp["pooled"][:rows])
+    dt = time.perf_counter() - t0
+    return {"value": rows / trunk_rows / dt, "unit": "forwards/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"oracle.mmdit_forward (fp64 NumPy) on {rows} of {trunk_rows} rows (all "
+                      f"{cfg['N']} blocks): {dt:.2f} s; value scaled to whole {trunk_rows}-row "
+                      f"forwards"}
+
+
 def cpu_baseline(cfg, w, inp, rows: int, trunk_rows: int):
     """fp64 oracle on `rows` guided rows (2*rows trunk rows) of the workload."""
     import oracle
+    if cfg.get("conditioning", 0) == 3:
+        return cpu_baseline_mmdit(cfg, w, inp, rows, trunk_rows)
     t0 = time.perf_counter()
     oracle.cfg_forward(cfg, w, inp["x_t"][:rows], inp["t"][:rows], inp["y"][:rows],
                        cfg["scale"], cfg["guided"])
@@ -284,13 +300,15 @@ def main():
     rows = 2 * Bh if cfg["cfg"] else Bh
     T = dit_inputs.tokens(cfg)
     w = dit_inputs.make_weights(cfg)
-    inp = dit_inputs.make_inputs(cfg)
+    mmdit = cfg.get("conditioning", 0) == dit_inputs.COND_MMDIT
+    inp = dit_inputs.make_mmdit_inputs(cfg) if mmdit else dit_inputs.make_inputs(cfg)
     model = dm.DiT(cfg, w, dev)
     dt = dm.torch_dtype(cfg["dtype"])
     x = torch.from_numpy(inp["x_t"]).to(dt).to(dev)
     t = torch.from_numpy(inp["t"]).to(dev)
-    y = torch.from_numpy(inp["y"]).to(dev) if inp["y"] is not None else None
+    y = torch.from_numpy(inp["y"]).to(dev) if inp.get("y") is not None else None
     pooled = torch.from_numpy(inp["pooled"]).to(dev) if inp["pooled"] is not None else None
+    ctx = torch.from_numpy(inp["ctx"]).to(dt).to(dev) if mmdit else None
     out = torch.empty(model.out_shape(Bh), device=dev, dtype=torch.float32)
     if args.sample:
         return sample_main(args, cfg, model, dev)
@@ -298,7 +316,9 @@ def main():
         return packed_main(args, cfg, model, dev)
 
     def step():
-        if cfg["cfg"]:
+        if mmdit:
+            model.forward_ctx(x, t, pooled, ctx, out=out)
+        elif cfg["cfg"]:
             model.cfg_forward(x, t, y, cfg["scale"], cfg["guided"], out=out)
         else:
             model.forward(x, t, y, pooled, out=out)
@@ -312,7 +332,8 @@ def main():
     # Consecutive launches cycle through the model's per-block weights, as the forward does,
     # so no launch finds its weight matrix already cached.
     d, hid = cfg["d"], cfg["mlp_hidden"]
-    M = (rows // 2 if rows >= 2 else rows) * model.Tt   # tokens per trunk row
+    # (MMDiT: the image stream's fc1, its largest)
+    M = (rows // 2 if rows >= 2 else rows) * (model.Tf if mmdit else model.Tt)
     A = torch.randn(M, d, device=dev).to(dt)
     W1 = [model.tensors["fc1_w"][l] for l in range(cfg["N"])]
     b1 = [model.tensors["fc1_b"][l] for l in range(cfg["N"])]
@@ -381,13 +402,17 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg["dtype"] == dit_inputs.DTYPE_BF16 else "f32",
-        "data": "synthetic (seeded N(0,1) latents, U{0..999} t and labels, N(0,0.02) weights)",
-        "config": {"workload": cfg["name"], "guided_rows": Bh, "trunk_rows": rows, "tokens": T,
-                   "guidance_scale": cfg["scale"], "guided_channels": cfg["guided"],
-                   "parallelism": "single GPU"},
+        "data": ("synthetic (seeded N(0,1) latents and text embeddings, U(0,1) t, N(0,1) "
+                 "pooled vector, N(0,0.02) weights)" if mmdit else
+                 "synthetic (seeded N(0,1) latents, U{0..999} t and labels, N(0,0.02) weights)"),
+        "config": ({"workload": cfg["name"], "rows": rows, "image_tokens": T,
+                    "text_tokens": cfg["ctx_len"], "parallelism": "single GPU"} if mmdit else
+                   {"workload": cfg["name"], "guided_rows": Bh, "trunk_rows": rows, "tokens": T,
+                    "guidance_scale": cfg["scale"], "guided_channels": cfg["guided"],
+                    "parallelism": "single GPU"}),
         "tflops": round(tflops, 1),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "tokens_per_s": round(rows * T * 1000.0 / ms, 1),
+        "tokens_per_s": round(rows * model.Tt * 1000.0 / ms, 1),
         "images_per_s": round(Bh * 1000.0 / ms, 1),
         "gflop_per_forward": round(flop_fwd / 1e9, 1),
         "wall_s_timed": round(wall, 3),

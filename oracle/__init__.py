@@ -39,6 +39,13 @@ Pins (what each function is checked against, in tests/test_oracle_*.py):
                              (ancestral chain returns the data law, DDIM and
                              Euler first order, DPM-Solver++(2M) second
                              order, point masses hit exactly); DDIM identity
+  train_oracle               torch restatement of the forward equals forward;
+                             autograd gradients equal central finite
+                             differences of the numpy loss (stop-gradient
+                             mean frozen); posterior coefficients from the
+                             product of Gaussians; KL / NLL against numerical
+                             integration; constant-output closed form;
+                             AdamW first-step closed form
 Full-size forward values: parity unpinned beyond the stage pins above
 (the pages print no output tensors and no trained weights exist).
 """
@@ -52,3 +59,4 @@ from .dit_oracle import (  # noqa: F401
 )
 from . import flops  # noqa: F401
 from . import sampler_oracle  # noqa: F401
+from . import train_oracle  # noqa: F401

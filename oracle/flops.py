@@ -50,17 +50,35 @@ def gmac_per_image(N, d, T, p, C, Cout, freq_dim=256, pt=1, conditioning="adaLN-
     return (blocks + embed + decode + temb + final) / 1e9
 
 
-COND_NAMES = {0: "adaLN-Zero", 1: "in-context", 2: "cross-attention"}
+COND_NAMES = {0: "adaLN-Zero", 1: "in-context", 2: "cross-attention", 3: "MMDiT"}
+
+
+def gmac_mmdit(N, d, T, L, ctx_dim, p, C, Cout, freq_dim=256, mlp_ratio=4):
+    """GMAC for one row of the MMDiT model ([DiT-wiki] MMDiT section): per
+    block each stream's QKV, output projection and FFN ((4 + 2 mlp_ratio) d^2
+    per token; T image, L text tokens), joint attention over T + L tokens
+    (2 (T + L)^2 d) and both streams' modulation (2 x 6 d^2); the text-token
+    embedding L ctx_dim d; final modulation 2 d^2.  The pooled-vector
+    projection is added by gmac_for."""
+    f = 2 * mlp_ratio
+    J = T + L
+    blocks = N * ((4 + f) * J * d * d + 2 * J * J * d + 12 * d * d)
+    embed = T * p * p * C * d + L * ctx_dim * d
+    return (blocks + embed + T * d * p * p * Cout + freq_dim * d + d * d + 2 * d * d) / 1e9
 
 
 def gmac_for(cfg, conditioning=None):
     """GMAC per row for a workload dict (keys N, d, F, H, W, p, pt, C, Cout,
     freq_dim, mlp_hidden, and the conditioning design code, 0 = adaLN-Zero,
-    1 = in-context, 2 = cross-attention).  Adds the pooled-vector projection
+    1 = in-context, 2 = cross-attention, 3 = MMDiT with ctx_len, ctx_dim).  Adds the pooled-vector projection
     when present."""
     if conditioning is None:
         conditioning = COND_NAMES[cfg.get("conditioning", 0)]
     T = (cfg["F"] // cfg["pt"]) * (cfg["H"] // cfg["p"]) * (cfg["W"] // cfg["p"])
+    if conditioning == "MMDiT":
+        return gmac_mmdit(cfg["N"], cfg["d"], T, cfg["ctx_len"], cfg["ctx_dim"], cfg["p"],
+                          cfg["C"], cfg["Cout"], cfg["freq_dim"],
+                          cfg["mlp_hidden"] // cfg["d"]) + cfg["cond_dim"] * cfg["d"] / 1e9
     g = gmac_per_image(cfg["N"], cfg["d"], T, cfg["p"], cfg["C"], cfg["Cout"],
                        cfg["freq_dim"], cfg["pt"], conditioning,
                        mlp_ratio=cfg["mlp_hidden"] // cfg["d"])

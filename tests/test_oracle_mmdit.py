@@ -146,3 +146,30 @@ def test_forward_shapes_and_text_dependence():
     assert out.shape == (2, cfg["Cout"], 16, 16)
     out2 = oracle.mmdit_forward(cfg, w, inp["x_t"], inp["t"], inp["ctx"] * 0.5, inp["pooled"])
     assert np.abs(out2 - out).max() > 1e-6
+
+
+def test_mac_count_matches_closed_form(monkeypatch):
+    """Every product the oracle's MMDiT forward makes, counted as it runs,
+    equals the closed-form count the throughput figures use."""
+    from oracle import dit_oracle, flops
+    cfg = small_cfg()
+    w = dit_inputs.make_weights(cfg)
+    inp = dit_inputs.make_mmdit_inputs(cfg)
+    macs = {"n": 0}
+    lin0, att0 = dit_oracle.linear, dit_oracle.attention
+
+    def lin(x, wt, b=None):
+        x = np.asarray(x)
+        macs["n"] += int(np.prod(x.shape[:-1])) * wt.shape[0] * wt.shape[1]
+        return lin0(x, wt, b)
+
+    def att(q, k, v, q_chunk=2048):
+        B, H, Tq, dh = np.shape(q)
+        macs["n"] += 2 * B * H * Tq * np.shape(k)[2] * dh
+        return att0(q, k, v, q_chunk)
+
+    monkeypatch.setattr(dit_oracle, "linear", lin)
+    monkeypatch.setattr(dit_oracle, "attention", att)
+    oracle.mmdit_forward(cfg, w, inp["x_t"], inp["t"], inp["ctx"], inp["pooled"])
+    want = flops.gmac_for(cfg) * 1e9 * cfg["batch"]
+    assert macs["n"] == round(want)
