@@ -46,6 +46,17 @@ class DitSampler(C.Structure):
                 ("train_steps", C.c_int), ("beta_start", C.c_double), ("beta_end", C.c_double)]
 
 
+class DitTrainHparams(C.Structure):
+    _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
+                ("adam_eps", C.c_double), ("weight_decay", C.c_double),
+                ("ema_decay", C.c_double), ("train_steps", C.c_int),
+                ("beta_start", C.c_double), ("beta_end", C.c_double)]
+
+
+class DitTrainState(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("master", "grad", "m", "v", "ema")]
+
+
 EXPORTS = {
     "dit_create": (C.c_int, [C.POINTER(DitConfig), C.POINTER(DitWeights), C.POINTER(C.c_void_p)]),
     "dit_destroy": (None, [C.c_void_p]),
@@ -64,6 +75,14 @@ EXPORTS = {
     "dit_forward_ctx": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_int, C.c_void_p, C.POINTER(DitTaps), C.c_void_p,
                                   C.c_size_t, C.c_void_p]),
+    "dit_train_param_count": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t)]),
+    "dit_train_param_layout": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_size_t),
+                                         C.POINTER(C.c_size_t)]),
+    "dit_train_workspace_size": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_size_t)]),
+    "dit_train_step": (C.c_int, [C.c_void_p, C.POINTER(DitTrainHparams), C.c_int,
+                                 C.POINTER(DitTrainState), C.c_void_p, C.c_void_p, C.c_void_p,
+                                 C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_size_t,
+                                 C.c_void_p]),
     "dit_status_string": (C.c_char_p, [C.c_int]),
     "dit_last_error_message": (C.c_char_p, []),
     "dit_patchify": (C.c_int, [C.c_void_p] + [C.c_int] * 8 + [C.c_void_p, C.c_void_p]),

@@ -15,14 +15,9 @@
 
 #include "dit.h"
 #include "common.h"
+#include "internal.h"
 
-// Independent row groups of a call run on this many streams (the caller's and
-// DIT_SPLIT - 1 of the library's own).
-#ifndef DIT_SPLIT
-#define DIT_SPLIT 2
-#endif
-
-namespace {
+namespace dit_host {
 
 thread_local std::string g_err;
 
@@ -41,38 +36,14 @@ int ok() {
   return DIT_OK;
 }
 
-#define DIT_HIP(call)                                                                   \
-  do {                                                                                  \
-    hipError_t e_ = (call);                                                             \
-    if (e_ != hipSuccess) return fail(DIT_EHIP, "%s: %s", #call, hipGetErrorString(e_)); \
-  } while (0)
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-}  // namespace
+}  // namespace dit_host
 
-struct dit_handle {
-  dit_config cfg;
-  dit_weights w;
-  int d, N, heads, dh, hid, ncls, cond_dim, freq, dtype, es;
-  float eps;
-  int gf, gh, gw, T, kin, kout, mod_stride;
-  // conditioning design; tokens per trunk row (T + 2 in-context, else T);
-  // LayerNorms per block of the in-context / cross-attention designs
-  int cond, Tt, nln;
-  int Lc;            // MMDiT: text tokens per row (0 otherwise)
-  int Tf;            // tokens per row of the stream the final layer decodes
-  PatchGeom gin, gout;
-  PatchGeom gouty;   // gout with T = Tf: the decoder output's row stride
-  // Second stream for the two independent halves of a batch (created on the
-  // first forward, on the device current then), and the fork / join events.
-  // The mutex makes each call's fork-enqueue-join sequence atomic, so calls
-  // from several threads can share them.
-  mutable std::mutex mu;
-  mutable hipStream_t aux[DIT_SPLIT - 1] = {};
-  mutable hipEvent_t ev_fork = nullptr, ev_join[DIT_SPLIT - 1] = {};
-  mutable bool aux_ready = false, aux_failed = false;
-};
+using namespace dit_host;
+
+
 
 namespace {
 // Lazily creates the extra streams (default priority) and the events.
@@ -136,15 +107,9 @@ WsLayout ws_layout(const dit_handle* h, int rows) {
   return ws_layout_m(h, rows, (size_t)rows * h->Tt, false);
 }
 
-template <typename T>
-T* at(void* ws, size_t off) {
-  return (T*)((char*)ws + off);
-}
+}  // namespace
 
-const void* woff(const void* base, size_t elems, int es) {
-  return (const char*)base + elems * es;
-}
-
+namespace dit_host {
 EpiParams epi0() {
   EpiParams ep;
   memset(&ep, 0, sizeof ep);
@@ -165,6 +130,19 @@ hipError_t linear(const dit_handle* h, int epi, const void* A, int lda, const vo
   a.seg = ep.a_seg; a.skip = ep.a_skip; a.off = ep.a_off;
   return launch_gemm_valu(epi, A_PLAIN, a, W, 0, M, N, K, ep, s);
 }
+}  // namespace dit_host
+
+namespace {
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+const void* woff(const void* base, size_t elems, int es) {
+  return (const char*)base + elems * es;
+}
+
 
 // One adaLN-Zero block on the residual stream X [rows*T, d] (fp32, in place).
 // mod + base points at this block's (b1, g1, a1, b2, g2, a2) in rows of mod_stride.

@@ -34,7 +34,8 @@ namespace {
 template <int DH, int NWV, bool PK = false>
 __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16_t* __restrict__ QKV,
                                                            bf16_t* __restrict__ O, int H,
-                                                           int T_rows, float sl2, SeqTable seqs) {
+                                                           int T_rows, float sl2, SeqTable seqs,
+                                                           float* __restrict__ lse) {
   constexpr int KV = 64;                  // keys per tile
   constexpr int KLD = 72;                 // K tile row stride (elements), 144 B
   constexpr int VLD = KV + 4;             // V^T tile row stride (elements), 136 B
@@ -359,6 +360,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
     const float inv = 1.0f / l;
     const int q = q0 + 16 * qb + c16;
     if (q >= T) continue;
+    // natural-log log-sum-exp of the query's scaled scores: sum exp = 2^m_run l
+    if (lse && g == 0) lse[(int64_t)bh * T_rows + q] = (m_run[qb] + log2f(l)) * 0.6931471805599453f;
     bf16_t* orow = O + (tok0 + q) * H * DH + h * DH;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -373,7 +376,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
 template <int DH, bool PK = false>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ QKV,
                                                       float* __restrict__ O, int H, int T_rows,
-                                                      float scale, SeqTable seqs) {
+                                                      float scale, SeqTable seqs,
+                                                      float* __restrict__ lse) {
   constexpr int KT = 32;
   __shared__ float sK[KT][DH], sV[KT][DH];
   const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
@@ -423,6 +427,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
     }
   }
   if (qi < T) {
+    if (lse) lse[(int64_t)bh * T_rows + qi] = m + logf(l);
     float* orow = O + (tok0 + qi) * H * DH + h * DH;
     float inv = 1.0f / l;
 #pragma unroll
@@ -433,7 +438,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 }  // namespace
 
 hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, int dtype, void* o,
-                            hipStream_t s) {
+                            hipStream_t s, float* lse) {
   if (B <= 0 || T <= 0) return hipSuccess;
   if (dtype == 1) {
     const float sl2 = 1.4426950408889634f / sqrtf((float)dh);
@@ -456,10 +461,10 @@ hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, in
     dim3 grid((T + 32 * NWV - 1) / (32 * NWV), B * heads);                                    \
     if (dh == 64)                                                                             \
       attn_bf16_kernel<64, NWV><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o,     \
-                                                          heads, T, sl2, none);               \
+                                                          heads, T, sl2, none, lse);          \
     else                                                                                      \
       attn_bf16_kernel<72, NWV><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o,     \
-                                                          heads, T, sl2, none);               \
+                                                          heads, T, sl2, none, lse);          \
   }
     if (nwv == 4) DIT_ATTN_LAUNCH(4)
     else if (nwv == 3) DIT_ATTN_LAUNCH(3)
@@ -471,9 +476,11 @@ hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, in
     SeqTable none;
     none.n = 0;
     if (dh == 64)
-      attn_f32_kernel<64><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, T, scale, none);
+      attn_f32_kernel<64><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, T, scale, none,
+                                              lse);
     else if (dh == 72)
-      attn_f32_kernel<72><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, T, scale, none);
+      attn_f32_kernel<72><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, T, scale, none,
+                                              lse);
     else
       return hipErrorInvalidValue;
   }
@@ -494,10 +501,10 @@ hipError_t launch_attention_packed(const void* qkv, const SeqTable& seqs_in, int
     dim3 grid(seqs.blk[seqs.n], heads);
     if (dh == 64)
       attn_f32_kernel<64, true><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, 0,
-                                                    scale, seqs);
+                                                    scale, seqs, nullptr);
     else
       attn_f32_kernel<72, true><<<grid, 64, 0, s>>>((const float*)qkv, (float*)o, heads, 0,
-                                                    scale, seqs);
+                                                    scale, seqs, nullptr);
     return hipGetLastError();
   }
   constexpr int NWV = 4;
@@ -505,10 +512,10 @@ hipError_t launch_attention_packed(const void* qkv, const SeqTable& seqs_in, int
   dim3 grid(seqs.blk[seqs.n], heads);
   if (dh == 64)
     attn_bf16_kernel<64, NWV, true><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o,
-                                                              heads, 0, sl2, seqs);
+                                                              heads, 0, sl2, seqs, nullptr);
   else
     attn_bf16_kernel<72, NWV, true><<<grid, 64 * NWV, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o,
-                                                              heads, 0, sl2, seqs);
+                                                              heads, 0, sl2, seqs, nullptr);
   return hipGetLastError();
 }
 

@@ -75,6 +75,7 @@ enum EpiKind {
   EPI_GELU = 5,         // out_dtype[m, n] = GELU_tanh(C + bias[n])
   EPI_PATCH = 6,        // X[m + (m / T) out_skip, n] = C + bias[n] (+ pe_tab[m % T, n])
   EPI_SILU_DT = 7,      // out_dtype[m, n] = SiLU(C + bias[n])                  (timestep MLP)
+  EPI_ATOMIC_F32 = 8,   // out_f32[m, n] += C, atomically (split-K partial sums; bias null)
 };
 
 struct EpiParams {
@@ -107,6 +108,11 @@ struct EpiParams {
   // of a row (MMDiT: text tokens, then image tokens) in one buffer.
   int a_seg, a_skip, a_off;
   int o_seg, o_skip, o_off;
+  // Row stride of W in elements (0: K).  Split-K: with ksplit > 0 the
+  // reduction is cut into slices of ksplit (the last one shorter), one grid
+  // layer each, whose partial sums the EPI_ATOMIC_F32 epilogue adds up.
+  int ldw;
+  int ksplit;
 };
 
 __device__ __host__ __forceinline__ int64_t row_map(int64_t m, int seg, int skip, int off) {
@@ -176,8 +182,10 @@ hipError_t launch_ln_modulate(const float* X, int M, int T, int d, const float* 
                               void* H, int dtype, hipStream_t s, const int* tok_seg = nullptr);
 hipError_t launch_qk_norm_rope(void* qkv, int B, int heads, int T, int dh, int dtype,
                                int qk_norm, float eps, int rope, int gh, int gw, hipStream_t s);
+// lse (optional, [B heads T]): natural-log log-sum-exp of each query's scaled
+// scores, for the backward pass.
 hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, int dtype, void* o,
-                            hipStream_t s);
+                            hipStream_t s, float* lse = nullptr);
 // RMSNorm with scale 1 + g of every head's q and k in the packed qkv [B*T, 3
 // H dh], in place: tokens t < L of a row use g4[2], g4[3] (q, k), the others
 // g4[0], g4[1] (g4 [4, dh]).

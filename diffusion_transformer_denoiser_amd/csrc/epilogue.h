@@ -50,5 +50,7 @@ __device__ __forceinline__ void epi_apply(const EpiParams& ep, int m, int n, flo
     ((float*)ep.out)[orow * ep.ldo + n] = v;
   } else if constexpr (EPI == EPI_SILU_DT) {
     ((DT*)ep.out)[(int64_t)m * ep.ldo + n] = from_f<DT>(silu_f(v));
+  } else if constexpr (EPI == EPI_ATOMIC_F32) {
+    unsafeAtomicAdd(&((float*)ep.out)[(int64_t)m * ep.ldo + n], v);
   }
 }

@@ -127,6 +127,13 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
   tile_coords<SWZ>(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int half = lane >> 5;
+  const int64_t ldw = ep.ldw ? ep.ldw : K;
+  if (gridDim.y > 1) {   // split-K: this grid layer's slice of the reduction
+    const int kb = blockIdx.y * ep.ksplit;
+    A += kb;
+    W += kb;
+    K = min(ep.ksplit, K - kb);
+  }
 
   // Accumulators start at the bias.  acc[i][j][r] is output column
   // ncol + 32 j, row mrow + 32 i + 8 (r / 4) + (r % 4).
@@ -136,7 +143,8 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int col = ncol + j * 32;
-    const float b = ep.bias ? (col < N ? 1.0f : 0.0f) * ep.bias[min(col, N - 1)] : 0.0f;
+    const float b = ep.bias && blockIdx.y == 0 ? (col < N ? 1.0f : 0.0f) * ep.bias[min(col, N - 1)]
+                                               : 0.0f;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
     const int s = (w * (is_a ? NA : NB) + (is_a ? c : c - NA)) * 64 + lane;
     const int r = s / CPR, ch = (s % CPR) ^ row_key<BK>(r);
     src[c] = is_a ? A + row_map(min(m0 + r, M - 1), ep.a_seg, ep.a_skip, ep.a_off) * lda + ch * 8
-                  : W + (int64_t)min(n0 + r, N - 1) * K + ch * 8;
+                  : W + (int64_t)min(n0 + r, N - 1) * ldw + ch * 8;
   }
   int boff[L];
 #pragma unroll
@@ -162,7 +170,8 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
       (void*)A, (short)0,
       (int)((row_map(M - 1, ep.a_seg, ep.a_skip, ep.a_off) * lda + K) * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t wrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)((int64_t)N * K * 2), 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)(((int64_t)(N - 1) * ldw + K) * 2),
+                                        0x00020000);
   auto copy = [&](int kt, int c) {
     char* st = smem + (kt & 1) * STAGE_BYTES +
                (c < NA ? (w * NA + c) * 1024 : A_BYTES + (w * NB + c - NA) * 1024);
@@ -320,6 +329,8 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
         }
       return;
     }
+  } else if constexpr (EPI == EPI_ATOMIC_F32) {
+    // split-K partial sums: element by element below
   } else {
     // bf16 outputs: each lane packs rows r, r+1 of its column; neighbouring
     // lanes (columns 2c, 2c+1) exchange those words (one DPP move) and each
@@ -382,6 +393,8 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
           ((bf16_t*)ep.out)[o] = f2bf(gelu_tanh_f(v));
         } else if constexpr (EPI == EPI_SILU_DT) {
           ((bf16_t*)ep.out)[o] = f2bf(silu_f(v));
+        } else if constexpr (EPI == EPI_ATOMIC_F32) {
+          unsafeAtomicAdd(&((float*)ep.out)[o], v);
         } else {
           static_assert(EPI == EPI_GATED, "epilogue");
           const int grow = ep.tok_seg ? ep.tok_seg[m] : m / ep.T;
@@ -399,10 +412,12 @@ hipError_t run(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   // bf16 outputs are stored as 4-byte column pairs
   const int vec = ((uintptr_t)ep.out & 3) == 0 && ep.ldo % 2 == 0;
+  const int64_t ldw = ep.ldw ? ep.ldw : K;
   const bool buf = (row_map(M - 1, ep.a_seg, ep.a_skip, ep.a_off) * lda + K) * 2 < (1LL << 31) &&
-                   (int64_t)N * K * 2 < (1LL << 31);
+                   ((int64_t)(N - 1) * ldw + K) * 2 < (1LL << 31);
+  const dim3 grid(tiles, ep.ksplit ? (K + ep.ksplit - 1) / ep.ksplit : 1);
 #define DIT_GEMM_LAUNCH(SWZ, BUF)                                                                 \
-  gemm_bf16_kernel<EPI, BM, BN, BK, MINWG, SWZ, 1, BUF><<<tiles, 256, 0, s>>>(A, lda, W, M, N, K, \
+  gemm_bf16_kernel<EPI, BM, BN, BK, MINWG, SWZ, 1, BUF><<<grid, 256, 0, s>>>(A, lda, W, M, N, K,  \
                                                                            ep, vec)
   if (buf) DIT_GEMM_LAUNCH(1, 1);
   else DIT_GEMM_LAUNCH(1, 0);
@@ -429,13 +444,17 @@ hipError_t pick(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
 hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, int M, int N,
                             int K, const EpiParams& ep, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (K % KSTEP || lda % 8) return hipErrorInvalidValue;
+  if (K % KSTEP || lda % 8 || (ep.ldw && (ep.ldw % 8 || ep.ldw < K))) return hipErrorInvalidValue;
+  if (ep.ksplit < 0 || ep.ksplit % KSTEP || (ep.ksplit && epi != EPI_ATOMIC_F32) ||
+      (epi == EPI_ATOMIC_F32 && ep.bias))
+    return hipErrorInvalidValue;
   switch (epi) {
     case EPI_BIAS_F32: return pick<EPI_BIAS_F32>(A, lda, W, M, N, K, ep, s);
     case EPI_BIAS_DT: return pick<EPI_BIAS_DT>(A, lda, W, M, N, K, ep, s);
     case EPI_GATED: return pick<EPI_GATED>(A, lda, W, M, N, K, ep, s);
     case EPI_GELU: return pick<EPI_GELU>(A, lda, W, M, N, K, ep, s);
     case EPI_SILU_DT: return pick<EPI_SILU_DT>(A, lda, W, M, N, K, ep, s);
+    case EPI_ATOMIC_F32: return pick<EPI_ATOMIC_F32>(A, lda, W, M, N, K, ep, s);
   }
   return hipErrorInvalidValue;
 }

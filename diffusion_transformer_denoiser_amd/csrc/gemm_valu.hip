@@ -39,13 +39,17 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(ALoad a, const WT* __res
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
 
-  for (int k0 = 0; k0 < K; k0 += BK) {
+  // split-K: grid layer z reduces over [kbeg, kend)
+  const int64_t ldw = ep.ldw ? ep.ldw : K;
+  const int kbeg = ep.ksplit ? blockIdx.z * ep.ksplit : 0;
+  const int kend = ep.ksplit ? min(K, kbeg + ep.ksplit) : K;
+  for (int k0 = kbeg; k0 < kend; k0 += BK) {
     const int m = m0 + lr, n = n0 + lr;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       int k = k0 + lk + u;
-      As[lk + u][lr] = (m < M && k < K) ? load_a<ASRC, AT>(a, m, k) : 0.0f;
-      Bs[lk + u][lr] = (n < N && k < K) ? to_f<WT>(W[(int64_t)n * K + k]) : 0.0f;
+      As[lk + u][lr] = (m < M && k < kend) ? load_a<ASRC, AT>(a, m, k) : 0.0f;
+      Bs[lk + u][lr] = (n < N && k < kend) ? to_f<WT>(W[(int64_t)n * ldw + k]) : 0.0f;
     }
     __syncthreads();
 #pragma unroll
@@ -76,7 +80,7 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(ALoad a, const WT* __res
 template <int EPI, int ASRC, typename AT, typename WT, typename DT>
 hipError_t run(const ALoad& a, const void* W, int M, int N, int K, const EpiParams& ep,
                hipStream_t s) {
-  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+  dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, ep.ksplit ? (K + ep.ksplit - 1) / ep.ksplit : 1);
   gemm_valu_kernel<EPI, ASRC, AT, WT, DT><<<grid, 256, 0, s>>>(a, (const WT*)W, M, N, K, ep);
   return hipGetLastError();
 }
@@ -109,6 +113,7 @@ hipError_t dispatch_epi(int epi, int asrc, const ALoad& a, const void* W, int M,
     case EPI_GATED: return dispatch_src<EPI_GATED, DT>(asrc, a, W, M, N, K, ep, s);
     case EPI_GELU: return dispatch_src<EPI_GELU, DT>(asrc, a, W, M, N, K, ep, s);
     case EPI_PATCH: return dispatch_src<EPI_PATCH, DT>(asrc, a, W, M, N, K, ep, s);
+    case EPI_ATOMIC_F32: return dispatch_src<EPI_ATOMIC_F32, DT>(asrc, a, W, M, N, K, ep, s);
   }
   return hipErrorInvalidValue;
 }
@@ -118,6 +123,9 @@ hipError_t dispatch_epi(int epi, int asrc, const ALoad& a, const void* W, int M,
 hipError_t launch_gemm_valu(int epi, int asrc, const ALoad& a, const void* W, int w_dtype,
                             int M, int N, int K, const EpiParams& ep, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (ep.ksplit < 0 || (ep.ksplit % BK) || (ep.ksplit && epi != EPI_ATOMIC_F32) ||
+      (epi == EPI_ATOMIC_F32 && ep.bias))
+    return hipErrorInvalidValue;
   if (w_dtype == 1) return dispatch_epi<bf16_t>(epi, asrc, a, W, M, N, K, ep, s);
   return dispatch_epi<float>(epi, asrc, a, W, M, N, K, ep, s);
 }

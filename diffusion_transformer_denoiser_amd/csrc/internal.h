@@ -1,0 +1,60 @@
+// Host-side internals shared by the C-ABI sources: the handle and the
+// helpers every entry point uses (status strings, the dtype-dispatching
+// linear layer).  Not part of the public interface.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "common.h"
+#include "dit.h"
+
+// Independent row groups of a call run on this many streams (the caller's and
+// DIT_SPLIT - 1 of the library's own).
+#ifndef DIT_SPLIT
+#define DIT_SPLIT 2
+#endif
+
+struct dit_handle {
+  dit_config cfg;
+  dit_weights w;
+  int d, N, heads, dh, hid, ncls, cond_dim, freq, dtype, es;
+  float eps;
+  int gf, gh, gw, T, kin, kout, mod_stride;
+  // conditioning design; tokens per trunk row (T + 2 in-context, else T);
+  // LayerNorms per block of the in-context / cross-attention designs
+  int cond, Tt, nln;
+  int Lc;            // MMDiT: text tokens per row (0 otherwise)
+  int Tf;            // tokens per row of the stream the final layer decodes
+  PatchGeom gin, gout;
+  PatchGeom gouty;   // gout with T = Tf: the decoder output's row stride
+  // Second stream for the two independent halves of a batch (created on the
+  // first forward, on the device current then), and the fork / join events.
+  // The mutex makes each call's fork-enqueue-join sequence atomic, so calls
+  // from several threads can share them.
+  mutable std::mutex mu;
+  mutable hipStream_t aux[DIT_SPLIT - 1] = {};
+  mutable hipEvent_t ev_fork = nullptr, ev_join[DIT_SPLIT - 1] = {};
+  mutable bool aux_ready = false, aux_failed = false;
+};
+
+namespace dit_host {
+// Records the message for dit_last_error_message and returns code.
+int fail(int code, const char* fmt, ...);
+// Clears the message; returns DIT_OK.
+int ok();
+size_t align256(size_t b);
+// Zero-initialised epilogue parameters.
+EpiParams epi0();
+// One linear layer C = A W^T with the epilogue: MFMA for bf16 models, VALU
+// for fp32 ones.
+hipError_t linear(const dit_handle* h, int epi, const void* A, int lda, const void* W, int M,
+                  int N, int K, const EpiParams& ep, hipStream_t s);
+}  // namespace dit_host
+
+#define DIT_HIP(call)                                                                    \
+  do {                                                                                   \
+    hipError_t e_ = (call);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return dit_host::fail(DIT_EHIP, "%s: %s", #call, hipGetErrorString(e_));           \
+  } while (0)

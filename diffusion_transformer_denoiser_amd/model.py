@@ -285,6 +285,62 @@ class DiT:
                                        _ptr(ws), ws.numel(), _stream(self.device)))
         return x
 
+    # -- training ---------------------------------------------------------------
+    def train_init(self):
+        """Allocate the fp32 training state (``dit_train_state``): master
+        weights copied from the model's current weights, zero Adam moments,
+        the EMA equal to the master weights, and the gradient buffer."""
+        n = C.c_size_t()
+        _lib.check(self.lib.dit_train_param_count(self.handle, C.byref(n)))
+        f = dict(device=self.device, dtype=torch.float32)
+        self.train_state = {k: torch.zeros(n.value, **f) for k in ("master", "grad", "m", "v", "ema")}
+        self.train_fields = {}
+        for i, name in enumerate(_lib.WEIGHT_FIELDS):
+            off, cnt = C.c_size_t(), C.c_size_t()
+            _lib.check(self.lib.dit_train_param_layout(self.handle, i, C.byref(off), C.byref(cnt)))
+            if cnt.value:
+                self.train_fields[name] = (off.value, cnt.value)
+                src = self.tensors[name].reshape(-1).float()
+                self.train_state["master"][off.value:off.value + cnt.value] = src
+        self.train_state["ema"].copy_(self.train_state["master"])
+        self._train_struct = _lib.DitTrainState(**{k: v.data_ptr()
+                                                   for k, v in self.train_state.items()})
+
+    def train_view(self, which: str, name: str) -> torch.Tensor:
+        """Field ``name`` of state buffer ``which`` ("master", "grad", "m",
+        "v", "ema"), shaped like the weight."""
+        off, cnt = self.train_fields[name]
+        return self.train_state[which][off:off + cnt].view(self.tensors[name].shape)
+
+    def train_step(self, x0, y, t, noise, step: int, lr=1e-4, beta1=0.9, beta2=0.999,
+                   adam_eps=1e-8, weight_decay=0.0, ema_decay=0.9999, train_steps=1000,
+                   beta_start=1e-4, beta_end=0.02, loss=None) -> torch.Tensor:
+        """One optimizer step (``dit_train_step``).  x0, noise: fp32 [B, C, H, W];
+        y, t: int32 [B].  Returns the device loss (L_simple, KL term)."""
+        B = x0.shape[0]
+        for name, a, dt in (("x0", x0, torch.float32), ("noise", noise, torch.float32),
+                            ("y", y, torch.int32), ("t", t, torch.int32)):
+            if a.device != self.device or not a.is_contiguous() or a.dtype != dt:
+                raise ValueError(f"{name} must be a contiguous {dt} tensor on {self.device}")
+        if not hasattr(self, "train_state"):
+            self.train_init()
+        hp = _lib.DitTrainHparams(lr=lr, beta1=beta1, beta2=beta2, adam_eps=adam_eps,
+                                  weight_decay=weight_decay, ema_decay=ema_decay,
+                                  train_steps=train_steps, beta_start=beta_start,
+                                  beta_end=beta_end)
+        n = C.c_size_t()
+        _lib.check(self.lib.dit_train_workspace_size(self.handle, B, C.byref(n)))
+        if self._ws is None or self._ws.numel() < n.value:
+            self._ws = None
+            self._ws = torch.empty(n.value, dtype=torch.uint8, device=self.device)
+        if loss is None:
+            loss = torch.empty(2, device=self.device, dtype=torch.float32)
+        _lib.check(self.lib.dit_train_step(self.handle, C.byref(hp), int(step),
+                                           C.byref(self._train_struct), _ptr(x0), _ptr(y),
+                                           _ptr(t), _ptr(noise), B, _ptr(loss), _ptr(self._ws),
+                                           self._ws.numel(), _stream(self.device)))
+        return loss
+
     def block_forward(self, layer: int, X, mod, X_out=None, o_branch=None, f_branch=None):
         B = mod.shape[0]
         if X_out is None:

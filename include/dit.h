@@ -403,6 +403,69 @@ int dit_forward_packed(dit_handle* h, int nseq, const int32_t* seq_fhw, const vo
                        const float* t, const int32_t* y, const float* pooled, float* out,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Training step ----
+ * One optimizer step of the adaLN-Zero class-conditional image model
+ * (cv-learn.com "Sora / DiT", Method, training-objective bullet; itwiki page,
+ * Results: AdamW, constant learning rate, no weight decay, weight EMA).
+ *   x_t  = sqrt(abar_t) x0 + sqrt(1 - abar_t) noise   (per row, integer t);
+ *   loss = mean over the B C H W latent elements of (eps_theta - noise)^2
+ *          + (Cout == 2C) mean over the same elements of the KL term of the
+ *          learned covariance: KL(q(x_{t-1} | x_t, x0) || p_theta(x_{t-1} | x_t))
+ *          for t > 0, -log N(x0; mu_theta, var_theta) for t = 0, with mu_theta
+ *          taken through a stop-gradient (the KL term trains only the
+ *          covariance channels); schedule and learned-variance
+ *          parameterisation as for the DDPM sampler above;
+ *   grad = d loss / d parameters (every field of the flat parameter layout);
+ *   AdamW on the fp32 master weights (bias-corrected, decoupled weight
+ *   decay), then ema = decay ema + (1 - decay) master, and the handle's
+ *   weight buffers receive the new master weights in the model dtype.
+ * Label dropout for guidance is the caller's choice of y (the null label
+ * num_classes is a valid label); data augmentation is the caller's x0.
+ * Needs the adaLN-Zero design, num_classes > 0, cond_dim == 0, no rope3d or
+ * qk_norm, frames == patch_t == 1; bf16 models also need B * T % 64 == 0.
+ *
+ * Flat parameter layout: the trained fields of dit_weights, in struct order
+ * (pe_w pe_b t1_w t1_b t2_w t2_b y_table ada_w ada_b qkv_w qkv_b o_w o_b
+ * fc1_w fc1_b fc2_w fc2_b out_w out_b), each at a 64-element aligned offset,
+ * with the shapes of dit_weights.  dit_train_param_layout gives field f's
+ * (offset, count) in elements, f = index of the field in dit_weights (0 =
+ * pe_w); count 0 for fields the step does not train. */
+typedef struct dit_train_hparams {
+  double lr;            /* 1e-4 */
+  double beta1, beta2;  /* 0.9, 0.999 */
+  double adam_eps;      /* 1e-8 */
+  double weight_decay;  /* 0 */
+  double ema_decay;     /* 0.9999 */
+  int train_steps;      /* diffusion steps of the schedule (1000) */
+  double beta_start, beta_end;   /* linear beta line (1e-4, 0.02) */
+} dit_train_hparams;
+
+/* Caller-owned fp32 device buffers of dit_train_param_count elements each:
+ * master weights (read and updated), gradient (written), Adam moments m, v
+ * (read and updated; zero before the first step) and the EMA (read and
+ * updated; the initial weights before the first step). */
+typedef struct dit_train_state {
+  float* master;
+  float* grad;
+  float* m;
+  float* v;
+  float* ema;
+} dit_train_state;
+
+int dit_train_param_count(const dit_handle* h, size_t* count);
+int dit_train_param_layout(const dit_handle* h, int field, size_t* offset, size_t* count);
+int dit_train_workspace_size(const dit_handle* h, int B, size_t* bytes);
+/* step: 1-based optimizer step number (bias correction).  x0, noise: device
+ * [B, C, H, W] fp32; y: device int32 [B] labels in [0, num_classes]; t:
+ * device int32 [B] in [0, train_steps) (a t outside makes the loss NaN);
+ * loss: device float[2] = (L_simple, KL term).  The handle's weight buffers
+ * must be writable device memory (they receive the updated weights).  Calls
+ * on one handle must not overlap. */
+int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
+                   const dit_train_state* st, const float* x0, const int32_t* y, const int32_t* t,
+                   const float* noise, int B, float* loss, void* ws, size_t ws_bytes,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,9 @@ def test_header_declares_the_boundary():
               "dit_status_string", "dit_patchify", "dit_unpatchify", "dit_timestep_embed",
               "dit_attention", "dit_linear", "dit_block_forward", "dit_sampler_coefficients",
               "dit_sampler_step", "dit_sample_workspace_size", "dit_sample",
-              "dit_packed_workspace_size", "dit_forward_packed", "dit_forward_ctx"):
+              "dit_packed_workspace_size", "dit_forward_packed", "dit_forward_ctx",
+              "dit_train_param_count", "dit_train_param_layout", "dit_train_workspace_size",
+              "dit_train_step"):
         assert n in names
     assert set(names) == set(_lib.EXPORTS), "binding and header disagree"
 
@@ -287,3 +289,56 @@ def test_packed_forward_validates_before_launch():
         assert lib.dit_packed_workspace_size(h, 1, fhw, C.byref(need)) == _lib.DIT_EUNSUPPORTED
     finally:
         lib.dit_destroy(h)
+
+
+@needs_lib
+def test_train_layout_and_validation():
+    lib = _lib.load()
+    rc, h = _create(_cfg(depth=2), _weights())
+    assert rc == _lib.DIT_OK
+    try:
+        n = C.c_size_t()
+        assert lib.dit_train_param_count(h, C.byref(n)) == 0
+        d, N, hid, kin, kout = 1152, 2, 4608, 16, 32
+        ms = (6 * N + 2) * d
+        sizes = {0: d * kin, 1: d, 2: d * 256, 3: d, 4: d * d, 5: d, 6: 1001 * d, 9: ms * d,
+                 10: ms, 11: N * 3 * d * d, 12: N * 3 * d, 13: N * d * d, 14: N * d,
+                 15: N * hid * d, 16: N * hid, 17: N * d * hid, 18: N * d, 19: kout * d,
+                 20: kout}
+        spans = []
+        for f in range(len(_lib.WEIGHT_FIELDS)):
+            off, cnt = C.c_size_t(), C.c_size_t()
+            assert lib.dit_train_param_layout(h, f, C.byref(off), C.byref(cnt)) == 0
+            assert cnt.value == sizes.get(f, 0), f
+            if cnt.value:
+                assert off.value % 64 == 0
+                spans.append((off.value, off.value + cnt.value))
+        spans.sort()
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+        assert spans[-1][1] <= n.value
+        ws = C.c_size_t()
+        assert lib.dit_train_workspace_size(h, 4, C.byref(ws)) == 0 and ws.value > 0
+        p = C.c_void_p(0x200000)
+        hp = _lib.DitTrainHparams(lr=1e-4, beta1=0.9, beta2=0.999, adam_eps=1e-8,
+                                  weight_decay=0.0, ema_decay=0.9999, train_steps=1000,
+                                  beta_start=1e-4, beta_end=0.02)
+        st = _lib.DitTrainState(master=0x300000, grad=0x300000, m=0x300000, v=0x300000,
+                                ema=0x300000)
+        step = lambda B, k=1, hpp=hp, sz=ws.value: lib.dit_train_step(
+            h, C.byref(hpp), k, C.byref(st), p, p, p, p, B, p, p, sz, None)
+        assert step(4, k=0) == _lib.DIT_EINVAL                  # step numbers start at 1
+        assert step(4, sz=ws.value - 1) == _lib.DIT_EWORKSPACE
+        assert step(5) == _lib.DIT_EWORKSPACE                    # sized for 4 rows
+        bad = _lib.DitTrainHparams(**{**{k: getattr(hp, k) for k, _ in hp._fields_}, "beta2": 1.0})
+        assert step(4, hpp=bad) == _lib.DIT_EINVAL
+        bad = _lib.DitTrainHparams(**{**{k: getattr(hp, k) for k, _ in hp._fields_}, "train_steps": 1})
+        assert step(4, hpp=bad) == _lib.DIT_EINVAL
+    finally:
+        lib.dit_destroy(h)
+    # bf16 training needs B * T % 64 == 0 (T = 256 here, so any B works); the
+    # other designs are rejected
+    rc, h = _create(_cfg(conditioning=1), _weights())
+    assert rc == _lib.DIT_OK
+    n = C.c_size_t()
+    assert lib.dit_train_param_count(h, C.byref(n)) == _lib.DIT_EUNSUPPORTED
+    lib.dit_destroy(h)
