@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -51,6 +52,8 @@ def parse():
                     help="time whole sampling loops (dit_sample) instead of single forwards")
     ap.add_argument("--sample-steps", type=int, default=25,
                     help="denoiser evaluations per sampling loop")
+    ap.add_argument("--train", action="store_true",
+                    help="time dit_train_step on the training workload (DiT-XL/2, batch 256)")
     ap.add_argument("--packed", action="store_true",
                     help="time packed mixed-resolution forwards (dit_forward_packed): 16 latents "
                          "of 32x32 and 4 of 64x64 in one call, against the same work as two "
@@ -114,6 +117,71 @@ def cpu_baseline(cfg, w, inp, rows: int, trunk_rows: int):
             "sample": f"oracle.cfg_forward (fp64 NumPy) on {rows} of {trunk_rows // 2} guided rows "
                       f"({2 * rows} of {trunk_rows} trunk rows, all 28 blocks): {dt:.2f} s; "
                       f"value scaled to whole {trunk_rows}-row forwards"}
+
+
+def train_main(args, cfg, model, dev):
+    """Training: each timed step is one dit_train_step (forward with saved
+    activations, loss, backward, AdamW + EMA) on one batch resident in HBM."""
+    import torch
+    import dit_inputs
+    from oracle import flops as oflops
+
+    B = cfg["batch"]
+    inp = dit_inputs.make_train_inputs(cfg)
+    x0, noise, t, y = (torch.from_numpy(inp[k]).to(dev) for k in ("x0", "noise", "t", "y"))
+    model.train_init()
+    loss = torch.empty(2, device=dev)
+    k = 0
+    for _ in range(args.warmup):
+        k += 1
+        model.train_step(x0, y, t, noise, step=k, loss=loss)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        k += 1
+        model.train_step(x0, y, t, noise, step=k, loss=loss)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    lv = loss.cpu().tolist()
+    assert all(math.isfinite(v) for v in lv), "non-finite loss"
+    # forward MACs x 3 (the backward computes two products per forward product)
+    flop_step = 3 * 2.0 * oflops.gmac_for(cfg) * 1e9 * B
+    cpu = None
+    if not args.skip_cpu_baseline:
+        from oracle import train_oracle as TR
+        w = {kk: v for kk, v in model.host_weights.items()}
+        t0 = time.perf_counter()
+        TR.gradients(cfg, w, inp["x0"][:1], inp["y"][:1], inp["t"][:1], inp["noise"][:1])
+        dt = time.perf_counter() - t0
+        cpu = {"value": 1.0 / (dt * B), "unit": "steps/s", "cores": blas_threads(),
+               "kind": "oracle",
+               "sample": f"train_oracle.gradients (fp64 torch autograd, all {cfg['N']} blocks) on 1 "
+                         f"of {B} rows: {dt:.2f} s; value scaled to whole {B}-row steps (no "
+                         f"optimizer update counted)"}
+    line = {
+        "metric": "DiT-XL/2 training steps/s (forward + backward + AdamW) on 1 MI355X",
+        "value": round(1000.0 / ms, 4),
+        "unit": "steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg["dtype"] == dit_inputs.DTYPE_BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) latents and noise, U{0..999} t, random labels with 10% "
+                "null, N(0,0.02) weights)",
+        "config": {"workload": cfg["name"], "batch": B, "tokens": dit_inputs.tokens(cfg),
+                   "parallelism": "single GPU"},
+        "images_per_s": round(B * 1000.0 / ms, 1),
+        "tflops": round(flop_step / (ms * 1e-3) / 1e12, 1),
+        "loss": [round(v, 5) for v in lv],
+        "wall_s_timed": round(wall, 3),
+        "roofline": None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def sample_main(args, cfg, model, dev):
@@ -295,6 +363,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dm.load()
     dev = torch.device("cuda", torch.cuda.current_device())
+    if args.train and args.workload == "dit_xl2_256_cfg":
+        args.workload = "dit_xl2_256_train"
     cfg = dit_inputs.workload(args.workload)
     Bh = cfg["batch"]
     rows = 2 * Bh if cfg["cfg"] else Bh
@@ -312,6 +382,9 @@ def main():
     out = torch.empty(model.out_shape(Bh), device=dev, dtype=torch.float32)
     if args.sample:
         return sample_main(args, cfg, model, dev)
+    if args.train:
+        model.host_weights = w
+        return train_main(args, cfg, model, dev)
     if args.packed:
         return packed_main(args, cfg, model, dev)
 

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libdit.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "embed.hip", "gemm_valu.hip", "gemm_mfma.hip", "layernorm.hip",
-           "attention.hip", "sampler.hip", "train.hip", "train_api.cpp"]
+           "attention.hip", "sampler.hip", "train.hip", "attention_bwd.hip", "train_api.cpp"]
 
 
 def hipcc() -> str:

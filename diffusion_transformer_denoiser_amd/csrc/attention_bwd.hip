@@ -1,0 +1,300 @@
+// Attention backward on the matrix cores (bf16 operands, fp32 accumulation),
+// dh in {64, 72}.
+//
+// With S = Q K^T, P = exp(S / sqrt(dh) - lse) (lse: the forward pass's
+// log-sum-exp per query) and D_q = sum_e dO_qe O_qe:
+//   dV = P^T dO,  dS = P (dO V^T - D),  dK = dS^T Q / sqrt(dh),  dQ = dS K / sqrt(dh).
+// Two kernels, each a loop over the other side's tiles:
+//   kv: a workgroup owns 64 keys of one (row, head), 16 per wave, and streams
+//       32-query tiles; per tile S and dO V^T (queries x keys) come out of
+//       v_mfma_f32_16x16x32_bf16 with each lane holding 4 queries of one key,
+//       which, for two 16-query blocks, is the B operand of dV^T = dO^T P and
+//       dK^T = Q^T dS once the queries inside each 32-query step are taken in
+//       the same order on the A side (a transposed copy of the tile in LDS,
+//       read as two 8-byte pieces);
+//   q:  a workgroup owns 64 queries, 16 per wave, and streams 32-key tiles;
+//       S^T and V dO^T (keys x queries) give the B operand of dQ^T = K^T dS^T.
+// P never leaves registers.  dh = 72 runs its third 32-wide k step with lanes
+// past dh 72 holding zeros.
+#include "common.h"
+#include "train.h"
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+
+namespace {
+
+constexpr int TQ = 32;            // tile of the streamed side
+constexpr int RLD = 72;           // row-major tile stride (elements)
+constexpr int TLD = TQ + 4;       // transposed tile stride (elements)
+
+template <int DH>
+struct Shape {
+  static constexpr int NCH = (DH + 31) / 32;    // 32-wide k steps over dh
+  static constexpr int NDB = (DH + 15) / 16;    // 16-row blocks of a dh x 16 accumulator
+  static constexpr int TR = NDB * 16;           // rows of a transposed tile
+};
+
+__device__ __forceinline__ bf16x8_t ld8(const bf16_t* p) { return *(const bf16x8_t*)p; }
+
+// A/B operand of dh chunk ch of row `row` of a row-major tile (stride RLD):
+// lane group g covers dh 32 ch + 8 g .. + 7; past dh the operand is zero.
+template <int DH>
+__device__ __forceinline__ bf16x8_t row_chunk(const bf16_t* tile, int row, int ch, int g) {
+  const int e = 32 * ch + 8 * g;
+  if (e >= DH) return bf16x8_t{};
+  return ld8(tile + row * RLD + e);
+}
+
+// Operand taken from a transposed tile (dh rows, TQ columns): row r, the 4
+// columns 4g .. 4g+3 then 16 + 4g .. 16 + 4g + 3.
+__device__ __forceinline__ bf16x8_t trans_chunk(const bf16_t* tt, int r, int g) {
+  const uint2 lo = *(const uint2*)(tt + r * TLD + 4 * g);
+  const uint2 hi = *(const uint2*)(tt + r * TLD + 16 + 4 * g);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+__device__ __forceinline__ bf16x8_t pack8(const floatx4& a, const floatx4& b) {
+  return __builtin_bit_cast(bf16x8_t, make_uint4(f2bf2(a[0], a[1]), f2bf2(a[2], a[3]),
+                                                 f2bf2(b[0], b[1]), f2bf2(b[2], b[3])));
+}
+
+// Stage TQ rows (row0 ..) of the dh slice at `src` (row stride ld elements)
+// into a row-major tile; rows at or past T are zero.
+template <int DH>
+__device__ __forceinline__ void stage_rows(bf16_t* tile, const bf16_t* src, int64_t ld, int row0,
+                                           int T, int tid) {
+  constexpr int CPR = DH / 8;   // 16-byte chunks per row
+  for (int c = tid; c < TQ * CPR; c += 256) {
+    const int r = c / CPR, e = (c - r * CPR) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row0 + r < T) v = *(const uint4*)(src + (int64_t)(row0 + r) * ld + e);
+    *(uint4*)(tile + r * RLD + e) = v;
+  }
+}
+
+// tt[e][r] = tile[r][e] for e < DH (rows DH .. TR-1 of tt stay as set up).
+template <int DH>
+__device__ __forceinline__ void transpose_tile(bf16_t* tt, const bf16_t* tile, int tid) {
+  for (int i = tid; i < TQ * DH; i += 256) {
+    const int r = i / DH, e = i - r * DH;
+    tt[e * TLD + r] = tile[r * RLD + e];
+  }
+}
+
+template <int DH>
+__global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict__ QKV,
+                                                        const bf16_t* __restrict__ dO,
+                                                        const float* __restrict__ lse,
+                                                        const float* __restrict__ Dv, int H, int T,
+                                                        float sl2, bf16_t* __restrict__ dQKV) {
+  using S = Shape<DH>;
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[TQ * RLD], sG[TQ * RLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sQT[S::TR * TLD], sGT[S::TR * TLD];
+  __shared__ float sL[TQ], sD[TQ];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
+  const int64_t ld = 3LL * H * DH, ldo = (int64_t)H * DH;
+  const bf16_t* Qb = QKV + (int64_t)b * T * ld + h * DH;
+  const bf16_t* Gb = dO + (int64_t)b * T * ldo + h * DH;
+  const int key = blockIdx.x * 64 + wave * 16 + c16;   // this lane's key (B-operand column)
+  const bool kval = key < T;
+
+  // This wave's K and V rows as B operands (zero past T and past dh).
+  bf16x8_t kf[S::NCH], vf[S::NCH];
+#pragma unroll
+  for (int ch = 0; ch < S::NCH; ++ch) {
+    const int e = 32 * ch + 8 * g;
+    const bool ok = kval && e < DH;
+    kf[ch] = ok ? ld8(Qb + (int64_t)key * ld + ldo + e) : bf16x8_t{};
+    vf[ch] = ok ? ld8(Qb + (int64_t)key * ld + 2 * ldo + e) : bf16x8_t{};
+  }
+  floatx4 dk[S::NDB], dv[S::NDB];
+#pragma unroll
+  for (int db = 0; db < S::NDB; ++db) {
+    dk[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    dv[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // rows DH .. TR-1 of the transposed tiles: zero once
+  for (int i = tid; i < (S::TR - DH) * TLD; i += 256) {
+    sQT[DH * TLD + i] = f2bf(0.0f);
+    sGT[DH * TLD + i] = f2bf(0.0f);
+  }
+  const float* L = lse + (int64_t)bh * T;
+  const float* Dd = Dv + (int64_t)bh * T;
+  const float LOG2E = 1.4426950408889634f;
+
+  for (int q0 = 0; q0 < T; q0 += TQ) {
+    __syncthreads();   // previous tile fully consumed
+    stage_rows<DH>(sQ, Qb, ld, q0, T, tid);
+    stage_rows<DH>(sG, Gb, ldo, q0, T, tid);
+    if (tid < TQ) {
+      const int q = q0 + tid;
+      sL[tid] = q < T ? L[q] * LOG2E : INFINITY;   // exp2(. - inf) = 0 for missing queries
+      sD[tid] = q < T ? Dd[q] : 0.0f;
+    }
+    __syncthreads();
+    transpose_tile<DH>(sQT, sQ, tid);
+    transpose_tile<DH>(sGT, sG, tid);
+    __syncthreads();
+
+    // S, dP (queries x this wave's keys): lane holds queries 16 qb + 4 g + r.
+    floatx4 s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      s[qb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      dp[qb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ch = 0; ch < S::NCH; ++ch) {
+        s[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_chunk<DH>(sQ, 16 * qb + c16, ch, g),
+                                                         kf[ch], s[qb], 0, 0, 0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_chunk<DH>(sG, 16 * qb + c16, ch, g),
+                                                          vf[ch], dp[qb], 0, 0, 0);
+      }
+    }
+    floatx4 p[2], ds[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qi = 16 * qb + 4 * g + r;
+        const float pv = __builtin_amdgcn_exp2f(s[qb][r] * sl2 - sL[qi]);
+        p[qb][r] = pv;
+        ds[qb][r] = pv * (dp[qb][r] - sD[qi]);
+      }
+    const bf16x8_t pf = pack8(p[0], p[1]);
+    const bf16x8_t dsf = pack8(ds[0], ds[1]);
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db) {
+      dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(trans_chunk(sGT, 16 * db + c16, g), pf,
+                                                        dv[db], 0, 0, 0);
+      dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(trans_chunk(sQT, 16 * db + c16, g), dsf,
+                                                        dk[db], 0, 0, 0);
+    }
+  }
+
+  // lane holds dh 16 db + 4 g + r of `key`
+  if (kval) {
+    const float scale = sl2 / LOG2E;
+    bf16_t* o = dQKV + ((int64_t)b * T + key) * ld + h * DH;
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db) {
+      const int e = 16 * db + 4 * g;
+      if (e < DH) {
+        *(uint2*)(o + ldo + e) = make_uint2(f2bf2(dk[db][0] * scale, dk[db][1] * scale),
+                                            f2bf2(dk[db][2] * scale, dk[db][3] * scale));
+        *(uint2*)(o + 2 * ldo + e) = make_uint2(f2bf2(dv[db][0], dv[db][1]),
+                                                f2bf2(dv[db][2], dv[db][3]));
+      }
+    }
+  }
+}
+
+template <int DH>
+__global__ __launch_bounds__(256) void attn_bwd_q_mfma(const bf16_t* __restrict__ QKV,
+                                                       const bf16_t* __restrict__ dO,
+                                                       const float* __restrict__ lse,
+                                                       const float* __restrict__ Dv, int H, int T,
+                                                       float sl2, bf16_t* __restrict__ dQKV) {
+  using S = Shape<DH>;
+  __shared__ __attribute__((aligned(16))) bf16_t sK[TQ * RLD], sV[TQ * RLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sKT[S::TR * TLD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
+  const int64_t ld = 3LL * H * DH, ldo = (int64_t)H * DH;
+  const bf16_t* Qb = QKV + (int64_t)b * T * ld + h * DH;
+  const bf16_t* Gb = dO + (int64_t)b * T * ldo + h * DH;
+  const int q = blockIdx.x * 64 + wave * 16 + c16;      // this lane's query (B-operand column)
+  const bool qval = q < T;
+  const float LOG2E = 1.4426950408889634f;
+
+  bf16x8_t qf[S::NCH], gf[S::NCH];
+#pragma unroll
+  for (int ch = 0; ch < S::NCH; ++ch) {
+    const int e = 32 * ch + 8 * g;
+    const bool ok = qval && e < DH;
+    qf[ch] = ok ? ld8(Qb + (int64_t)q * ld + e) : bf16x8_t{};
+    gf[ch] = ok ? ld8(Gb + (int64_t)q * ldo + e) : bf16x8_t{};
+  }
+  const float lq = qval ? lse[(int64_t)bh * T + q] * LOG2E : INFINITY;
+  const float dq_ = qval ? Dv[(int64_t)bh * T + q] : 0.0f;
+  floatx4 dq[S::NDB];
+#pragma unroll
+  for (int db = 0; db < S::NDB; ++db) dq[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = tid; i < (S::TR - DH) * TLD; i += 256) sKT[DH * TLD + i] = f2bf(0.0f);
+
+  for (int k0 = 0; k0 < T; k0 += TQ) {
+    __syncthreads();
+    stage_rows<DH>(sK, Qb + ldo, ld, k0, T, tid);
+    stage_rows<DH>(sV, Qb + 2 * ldo, ld, k0, T, tid);
+    __syncthreads();
+    transpose_tile<DH>(sKT, sK, tid);
+    __syncthreads();
+
+    // S^T, dP^T (keys x this wave's queries): lane holds keys 16 kb + 4 g + r.
+    floatx4 st[2], dpt[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      st[kb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      dpt[kb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ch = 0; ch < S::NCH; ++ch) {
+        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_chunk<DH>(sK, 16 * kb + c16, ch, g),
+                                                          qf[ch], st[kb], 0, 0, 0);
+        dpt[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_chunk<DH>(sV, 16 * kb + c16, ch, g),
+                                                           gf[ch], dpt[kb], 0, 0, 0);
+      }
+    }
+    floatx4 dst[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kj = k0 + 16 * kb + 4 * g + r;
+        const float pv = kj < T ? __builtin_amdgcn_exp2f(st[kb][r] * sl2 - lq) : 0.0f;
+        dst[kb][r] = pv * (dpt[kb][r] - dq_);
+      }
+    const bf16x8_t dsf = pack8(dst[0], dst[1]);
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db)
+      dq[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(trans_chunk(sKT, 16 * db + c16, g), dsf,
+                                                        dq[db], 0, 0, 0);
+  }
+
+  if (qval) {
+    const float scale = sl2 / LOG2E;
+    bf16_t* o = dQKV + ((int64_t)b * T + q) * ld + h * DH;
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db) {
+      const int e = 16 * db + 4 * g;
+      if (e < DH)
+        *(uint2*)(o + e) = make_uint2(f2bf2(dq[db][0] * scale, dq[db][1] * scale),
+                                      f2bf2(dq[db][2] * scale, dq[db][3] * scale));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention_bwd_mfma(const void* qkv, const void* dO, const float* lse,
+                                     const float* Dv, int B, int heads, int T, int dh,
+                                     void* dqkv, hipStream_t s) {
+  if (B <= 0 || T <= 0) return hipSuccess;
+  if ((dh != 64 && dh != 72) || (int64_t)B * heads > 65535) return hipErrorInvalidValue;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)dh);
+  const dim3 grid((T + 63) / 64, B * heads);
+  if (dh == 64) {
+    attn_bwd_kv_mfma<64><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
+                                              heads, T, sl2, (bf16_t*)dqkv);
+    attn_bwd_q_mfma<64><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
+                                             heads, T, sl2, (bf16_t*)dqkv);
+  } else {
+    attn_bwd_kv_mfma<72><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
+                                              heads, T, sl2, (bf16_t*)dqkv);
+    attn_bwd_q_mfma<72><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
+                                             heads, T, sl2, (bf16_t*)dqkv);
+  }
+  return hipGetLastError();
+}

@@ -61,5 +61,9 @@ hipError_t launch_class_grad(const float* dc, const int32_t* y, int B, int d, in
 hipError_t launch_attention_bwd(const void* qkv, const void* O, const void* dO, const float* lse,
                                 float* Dv, int B, int heads, int T, int dh, int dtype, void* dqkv,
                                 hipStream_t s);
+// The same on the matrix cores for bf16 (attention_bwd.hip), given Dv.
+hipError_t launch_attention_bwd_mfma(const void* qkv, const void* dO, const float* lse,
+                                     const float* Dv, int B, int heads, int T, int dh,
+                                     void* dqkv, hipStream_t s);
 hipError_t launch_adamw(float* p, const float* g, float* m, float* v, float* ema, int64_t n,
                         const AdamArgs& a, void* w, int w_dtype, hipStream_t s);

@@ -756,7 +756,15 @@ hipError_t launch_attention_bwd(const void* qkv, const void* O, const void* dO, 
   attn_bwd_q_kernel<DH, DT><<<grid, 256, 0, s>>>((const DT*)qkv, (const DT*)dO, lse, Dv, heads,  \
                                                  T, scale, (DT*)dqkv);
   if (dtype == 1) {
-    if (dh == 64) { DIT_AB(64, bf16_t) } else { DIT_AB(72, bf16_t) }
+    if (dh == 64)
+      attn_bwd_dot_kernel<64, bf16_t><<<blocks_for(tokens * heads), 256, 0, s>>>(
+          (const bf16_t*)O, (const bf16_t*)dO, heads, T, tokens, Dv);
+    else
+      attn_bwd_dot_kernel<72, bf16_t><<<blocks_for(tokens * heads), 256, 0, s>>>(
+          (const bf16_t*)O, (const bf16_t*)dO, heads, T, tokens, Dv);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_attention_bwd_mfma(qkv, dO, lse, Dv, B, heads, T, dh, dqkv, s);
   } else {
     if (dh == 64) { DIT_AB(64, float) } else { DIT_AB(72, float) }
   }

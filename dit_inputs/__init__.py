@@ -90,6 +90,10 @@ WORKLOADS = {
         num_classes=0, cond_dim=2048, freq_dim=256, qk_norm=0, rope3d=0, dtype=DTYPE_BF16,
         ln_eps=1e-6, batch=8, cfg=False, scale=1.0, guided=16, conditioning=COND_MMDIT,
         ctx_len=333, ctx_dim=4096, seed_idx=8),
+    # The pages' training setup: DiT-XL/2 on 256x256 ImageNet latents, batch 256.
+    "dit_xl2_256_train": dict(_image_config("XL", 2, 32, DTYPE_BF16, 256, False,
+                                            "DiT-XL/2 256x256 (32x32x4 latent) training, batch 256"),
+                              seed_idx=13),
     "dit_xl2_256_cfg_cross_attention": dict(
         _image_config("XL", 2, 32, DTYPE_BF16, 32, True,
                       "DiT-XL/2 256x256 cross-attention conditioning + CFG, 32 cond + 32 null rows"),
@@ -334,3 +338,22 @@ def make_mmdit_inputs(cfg: dict, seed: int | None = None, batch: int | None = No
             "t": f32_round(rng.uniform(0.0, 1.0, size=B)),
             "ctx": cast_to(rng.standard_normal((B, cfg["ctx_len"], cfg["ctx_dim"])), cfg["dtype"]),
             "pooled": f32_round(rng.standard_normal((B, cfg["cond_dim"])))}
+
+
+def make_train_inputs(cfg: dict, seed: int | None = None, batch: int | None = None,
+                      label_drop: float = 0.1) -> dict:
+    """Seeded inputs of one training step: clean latents x0 ~ N(0,1) and noise
+    ~ N(0,1) [B, C, H, W] fp32, integer steps t ~ U{0..999}, labels ~
+    U{0..num_classes-1} of which a fraction label_drop (drawn per row) is
+    replaced by the null label num_classes (training for guidance)."""
+    if seed is None:
+        seed = 4000 + cfg["seed_idx"]
+    B = cfg["batch"] if batch is None else batch
+    rng = np.random.default_rng(seed)
+    shape = (B, cfg["C"], cfg["H"], cfg["W"])
+    x0 = f32_round(rng.standard_normal(shape))
+    noise = f32_round(rng.standard_normal(shape))
+    t = rng.integers(0, 1000, size=B).astype(np.int32)
+    y = rng.integers(0, cfg["num_classes"], size=B).astype(np.int32)
+    y[rng.random(B) < label_drop] = cfg["num_classes"]
+    return {"x0": x0, "noise": noise, "t": t, "y": y}

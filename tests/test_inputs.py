@@ -44,4 +44,15 @@ def test_workload_token_counts():
     assert T == {"dit_s8_f32": 16, "dit_b4_bf16": 64, "dit_xl2_256_cfg": 256,
                  "dit_xl2_512_cfg": 1024, "video_xl_spacetime": 24960,
                  "dit_xl2_256_cfg_in_context": 256, "dit_xl2_256_cfg_cross_attention": 256,
-                 "mmdit_d24_512": 1024}
+                 "mmdit_d24_512": 1024, "dit_xl2_256_train": 256}
+
+
+def test_train_inputs_recipe():
+    cfg = dit_inputs.workload("dit_xl2_256_train")
+    a = dit_inputs.make_train_inputs(cfg)
+    b = dit_inputs.make_train_inputs(cfg)
+    assert all(np.array_equal(a[k], b[k]) for k in a)
+    assert a["x0"].shape == (256, 4, 32, 32) and a["x0"].dtype == np.float32
+    assert a["t"].dtype == np.int32 and a["t"].min() >= 0 and a["t"].max() <= 999
+    null = (a["y"] == 1000).mean()
+    assert 0.04 < null < 0.18 and a["y"].min() >= 0
