@@ -32,11 +32,22 @@ __device__ __forceinline__ float silu_f(float z) {
 }
 // tanh-approximate GELU: 0.5 z (1 + tanh(u)), u = sqrt(2/pi) (z + 0.044715 z^3),
 // evaluated through the identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)).
+// d/dz of the tanh-GELU: with s = sigmoid(2u) = (1 + tanh u) / 2,
+// u = sqrt(2/pi)(z + 0.044715 z^3): s + 2 z s (1 - s) du/dz.
+__device__ __forceinline__ float gelu_tanh_grad_f(float z);
+
 __device__ __forceinline__ float gelu_tanh_f(float z) {
   const float k2 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
   const float k3 = k2 * 0.044715f;
   const float u2 = z * fmaf(z * z, k3, k2);                             // -2u log2(e)
   return z * fast_rcp(1.0f + fast_exp2(u2));
+}
+
+__device__ __forceinline__ float gelu_tanh_grad_f(float z) {
+  const float k = 0.7978845608028654f;
+  const float k2 = -2.0f * k * 1.4426950408889634f;
+  const float sg = fast_rcp(1.0f + fast_exp2(z * fmaf(z * z, k2 * 0.044715f, k2)));
+  return sg + 2.0f * z * sg * (1.0f - sg) * k * fmaf(3.0f * 0.044715f, z * z, 1.0f);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -76,6 +87,8 @@ enum EpiKind {
   EPI_PATCH = 6,        // X[m + (m / T) out_skip, n] = C + bias[n] (+ pe_tab[m % T, n])
   EPI_SILU_DT = 7,      // out_dtype[m, n] = SiLU(C + bias[n])                  (timestep MLP)
   EPI_ATOMIC_F32 = 8,   // out_f32[m, n] += C, atomically (split-K partial sums; bias null)
+  EPI_GELU2 = 9,        // out_dtype[m, n] = GELU_tanh(C + bias[n]); aux_dtype[m, n] = C + bias[n]
+  EPI_DGELU = 10,       // out_dtype[m, n] = (C + bias[n]) GELU_tanh'(aux_dtype[m, n])
 };
 
 struct EpiParams {
@@ -113,10 +126,14 @@ struct EpiParams {
   // layer each, whose partial sums the EPI_ATOMIC_F32 epilogue adds up.
   int ldw;
   int ksplit;
+  // EPI_GELU2: the pre-activation output; EPI_DGELU: the pre-activation input
+  // (model dtype, row stride ldo)
+  void* aux;
 };
 
+// (m < 2^31 and seg > 0: 32-bit unsigned division)
 __device__ __host__ __forceinline__ int64_t row_map(int64_t m, int seg, int skip, int off) {
-  return seg ? m + (m / seg) * skip + off : m;
+  return seg ? m + (int64_t)((uint32_t)m / (uint32_t)seg) * skip + off : m;
 }
 
 // ---------------------------------------------------------------------------

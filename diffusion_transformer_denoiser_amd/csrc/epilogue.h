@@ -52,5 +52,11 @@ __device__ __forceinline__ void epi_apply(const EpiParams& ep, int m, int n, flo
     ((DT*)ep.out)[(int64_t)m * ep.ldo + n] = from_f<DT>(silu_f(v));
   } else if constexpr (EPI == EPI_ATOMIC_F32) {
     unsafeAtomicAdd(&((float*)ep.out)[(int64_t)m * ep.ldo + n], v);
+  } else if constexpr (EPI == EPI_GELU2) {
+    ((DT*)ep.out)[(int64_t)m * ep.ldo + n] = from_f<DT>(gelu_tanh_f(v));
+    ((DT*)ep.aux)[(int64_t)m * ep.ldo + n] = from_f<DT>(v);
+  } else if constexpr (EPI == EPI_DGELU) {
+    const float z = to_f<DT>(((const DT*)ep.aux)[(int64_t)m * ep.ldo + n]);
+    ((DT*)ep.out)[(int64_t)m * ep.ldo + n] = from_f<DT>(v * gelu_tanh_grad_f(z));
   }
 }

@@ -340,6 +340,29 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
       const uint32_t sel = odd ? 0x03020706u : 0x05040100u;   // (q.hi, p.hi) : (p.lo, q.lo)
       bf16_t* ot = (bf16_t*)ep.out + (int64_t)(mrow + odd) * ep.ldo + (ncol & ~1);
       bf16_t* oc = (bf16_t*)ep.out + (ncol & ~1);   // row-mapped outputs
+      // EPI_GELU2 also stores the pre-activation; EPI_DGELU reads it first
+      // (all loads before the stores: one counter tracks both)
+      bf16_t* ot2 = nullptr;
+      if constexpr (EPI == EPI_GELU2) ot2 = (bf16_t*)ep.aux + (int64_t)(mrow + odd) * ep.ldo + (ncol & ~1);
+      [[maybe_unused]] uint32_t pk[TM][TN][8];
+      if constexpr (EPI == EPI_DGELU) {
+        const uint16_t* pa = (const uint16_t*)ep.aux + (int64_t)mrow * ep.ldo + ncol;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+              const int r = (p >> 1) * 4 + (p & 1) * 2;
+              const int rr = i * 32 + 8 * (r >> 2) + (r & 3);
+              pk[i][j][p] = (uint32_t)pa[(int64_t)rr * ep.ldo + j * 32] |
+                            ((uint32_t)pa[(int64_t)(rr + 1) * ep.ldo + j * 32] << 16);
+            }
+      }
+      // SEG: rows go through the output row map (only the q | k | v epilogue
+      // has one); the choice is made once, outside the store loop
+      auto emit = [&](auto seg_tag) {
+        constexpr bool SEG = decltype(seg_tag)::value;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -354,6 +377,17 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
             } else if constexpr (EPI == EPI_SILU_DT) {
               v0 = silu_f(v0);
               v1 = silu_f(v1);
+            } else if constexpr (EPI == EPI_DGELU) {
+              v0 *= gelu_tanh_grad_f(__uint_as_float(pk[i][j][p] << 16));
+              v1 *= gelu_tanh_grad_f(__uint_as_float(pk[i][j][p] & 0xFFFF0000u));
+            } else if constexpr (EPI == EPI_GELU2) {
+              const uint32_t mp = f2bf2(v0, v1);
+              const uint32_t op = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mp, 0xB1, 0xF,
+                                                                        0xF, false);
+              const int rr2 = i * 32 + 8 * (r >> 2) + (r & 3);
+              *(uint32_t*)(ot2 + (int64_t)rr2 * ep.ldo + j * 32) = __builtin_amdgcn_perm(op, mp, sel);
+              v0 = gelu_tanh_f(v0);
+              v1 = gelu_tanh_f(v1);
             } else {
               static_assert(EPI == EPI_BIAS_DT, "epilogue");
             }
@@ -363,16 +397,26 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
                                                                          0xF, false);
             const uint32_t word = __builtin_amdgcn_perm(other, mine, sel);
             const int rr = i * 32 + 8 * (r >> 2) + (r & 3);
-            if (ep.o_seg)
+            if constexpr (SEG)
               *(uint32_t*)(oc + row_map(mrow + odd + rr, ep.o_seg, ep.o_skip, ep.o_off) * ep.ldo +
                            j * 32) = word;
             else
               *(uint32_t*)(ot + (int64_t)rr * ep.ldo + j * 32) = word;
           }
+      };
+      if constexpr (EPI == EPI_BIAS_DT) {
+        if (ep.o_seg) emit(std::true_type{});
+        else emit(std::false_type{});
+      } else {
+        emit(std::false_type{});
+      }
       return;
     }
   }
-  // Ragged or unaligned tiles: element by element with bounds checks.
+  // Ragged or unaligned tiles: element by element with bounds checks (the
+  // output row map, used by the q | k | v epilogue only, chosen once).
+  auto ragged = [&](auto seg_tag) {
+    constexpr bool SEG = decltype(seg_tag)::value;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -384,7 +428,7 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
         const int n = ncol + j * 32;
         if (n >= N) continue;
         const float v = acc[i][j][r];
-        const int64_t o = row_map(m, ep.o_seg, ep.o_skip, ep.o_off) * ep.ldo + n;
+        const int64_t o = (SEG ? row_map(m, ep.o_seg, ep.o_skip, ep.o_off) : (int64_t)m) * ep.ldo + n;
         if constexpr (EPI == EPI_BIAS_F32) {
           ((float*)ep.out)[o] = v;
         } else if constexpr (EPI == EPI_BIAS_DT) {
@@ -395,6 +439,12 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
           ((bf16_t*)ep.out)[o] = f2bf(silu_f(v));
         } else if constexpr (EPI == EPI_ATOMIC_F32) {
           unsafeAtomicAdd(&((float*)ep.out)[o], v);
+        } else if constexpr (EPI == EPI_GELU2) {
+          ((bf16_t*)ep.out)[o] = f2bf(gelu_tanh_f(v));
+          ((bf16_t*)ep.aux)[o] = f2bf(v);
+        } else if constexpr (EPI == EPI_DGELU) {
+          const float z = __uint_as_float((uint32_t)((const uint16_t*)ep.aux)[o] << 16);
+          ((bf16_t*)ep.out)[o] = f2bf(v * gelu_tanh_grad_f(z));
         } else {
           static_assert(EPI == EPI_GATED, "epilogue");
           const int grow = ep.tok_seg ? ep.tok_seg[m] : m / ep.T;
@@ -404,6 +454,13 @@ __global__ __launch_bounds__(256, MINWG) void gemm_bf16_kernel(const bf16_t* __r
         }
       }
     }
+  };
+  if constexpr (EPI == EPI_BIAS_DT) {
+    if (ep.o_seg) ragged(std::true_type{});
+    else ragged(std::false_type{});
+  } else {
+    ragged(std::false_type{});
+  }
 }
 
 template <int EPI, int BM, int BN, int BK, int MINWG>
@@ -455,6 +512,8 @@ hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, 
     case EPI_GELU: return pick<EPI_GELU>(A, lda, W, M, N, K, ep, s);
     case EPI_SILU_DT: return pick<EPI_SILU_DT>(A, lda, W, M, N, K, ep, s);
     case EPI_ATOMIC_F32: return pick<EPI_ATOMIC_F32>(A, lda, W, M, N, K, ep, s);
+    case EPI_GELU2: return pick<EPI_GELU2>(A, lda, W, M, N, K, ep, s);
+    case EPI_DGELU: return pick<EPI_DGELU>(A, lda, W, M, N, K, ep, s);
   }
   return hipErrorInvalidValue;
 }

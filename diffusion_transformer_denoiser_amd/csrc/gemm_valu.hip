@@ -114,6 +114,8 @@ hipError_t dispatch_epi(int epi, int asrc, const ALoad& a, const void* W, int M,
     case EPI_GELU: return dispatch_src<EPI_GELU, DT>(asrc, a, W, M, N, K, ep, s);
     case EPI_PATCH: return dispatch_src<EPI_PATCH, DT>(asrc, a, W, M, N, K, ep, s);
     case EPI_ATOMIC_F32: return dispatch_src<EPI_ATOMIC_F32, DT>(asrc, a, W, M, N, K, ep, s);
+    case EPI_GELU2: return dispatch_src<EPI_GELU2, DT>(asrc, a, W, M, N, K, ep, s);
+    case EPI_DGELU: return dispatch_src<EPI_DGELU, DT>(asrc, a, W, M, N, K, ep, s);
   }
   return hipErrorInvalidValue;
 }

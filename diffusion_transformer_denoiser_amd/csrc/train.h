@@ -26,10 +26,6 @@ hipError_t launch_train_noise(const float* x0, const float* eps, const float* co
 // Xout = Xin + mod[m / T, goff + n] * v (fp32, [M, d]).
 hipError_t launch_gate_residual(const float* Xin, const float* v, const float* mod, int ms,
                                 int goff, int T, int d, int64_t M, float* Xout, hipStream_t s);
-hipError_t launch_gelu(const void* pre, void* G, int64_t n, int dtype, hipStream_t s);
-// dpre = dG * GELU'(pre).
-hipError_t launch_dgelu(const float* dG, const void* pre, void* dpre, int64_t n, int dtype,
-                        hipStream_t s);
 hipError_t launch_silu_f32(const float* z, float* out, int64_t n, hipStream_t s);
 hipError_t launch_silu_bwd(const float* dout, const float* z, float* dz, int64_t n, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
@@ -42,6 +38,7 @@ hipError_t launch_cast_f32(const float* in, void* out, int64_t n, int dtype, hip
 hipError_t launch_train_loss(const float* Y, const float* eps, const float* coef,
                              const PatchGeom& gout, int C, int64_t M, int dtype, void* dY,
                              double* acc, float* loss, hipStream_t s);
+// d beta / d gamma are added into dmod (zero it first).
 hipError_t launch_ln_mod_bwd(const float* X, const float* dH, const float* mod, int ms, int shoff,
                              int scoff, int B, int T, int d, float eps, float* dX, float* dmod,
                              hipStream_t s);

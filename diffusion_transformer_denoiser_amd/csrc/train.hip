@@ -92,26 +92,6 @@ __global__ void gate_residual_kernel(const float* __restrict__ Xin, const float*
                                    x.w + g[3] * y.w);
 }
 
-template <typename DT>
-__global__ void gelu_kernel(const DT* __restrict__ pre, DT* __restrict__ G, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) G[i] = from_f<DT>(gelu_tanh_f(to_f<DT>(pre[i])));
-}
-
-// d/dz of 0.5 z (1 + tanh(u)), u = sqrt(2/pi) (z + 0.044715 z^3).
-__device__ __forceinline__ float gelu_tanh_grad(float z) {
-  const float k = 0.7978845608028654f;
-  const float th = tanhf(k * (z + 0.044715f * z * z * z));
-  return 0.5f * (1.0f + th) + 0.5f * z * (1.0f - th * th) * k * (1.0f + 3.0f * 0.044715f * z * z);
-}
-
-template <typename DT>
-__global__ void dgelu_kernel(const float* __restrict__ dG, const DT* __restrict__ pre,
-                             DT* __restrict__ dpre, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) dpre[i] = from_f<DT>(dG[i] * gelu_tanh_grad(to_f<DT>(pre[i])));
-}
-
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 __global__ void silu_f32_kernel(const float* __restrict__ z, float* __restrict__ out, int64_t n) {
@@ -222,10 +202,11 @@ __global__ void loss_finish_kernel(const double* __restrict__ acc, double inv_n,
 // ---------------------------------------------------------------------------
 // Backward of h = LN(x)(1 + gamma) + beta per token (LN without affine,
 // biased variance, eps inside the root), with (beta, gamma) of the token's
-// row.  One workgroup per batch row: its 4 waves take the row's tokens in
-// turn; lane l owns columns l + 64 i.  dX += (g - mean(g) - xhat mean(g xhat))
-// / sigma with g = dH (1 + gamma); d beta = sum over tokens of dH, d gamma =
-// sum of dH xhat, written to dmod at the same offsets as beta and gamma.
+// row.  gridDim.y workgroups per batch row: their 4 gridDim.y waves take the
+// row's tokens in turn; lane l owns columns l + 64 i.  dX += (g - mean(g) -
+// xhat mean(g xhat)) / sigma with g = dH (1 + gamma); d beta = sum over tokens
+// of dH, d gamma = sum of dH xhat, added (atomically) to dmod at the offsets of
+// beta and gamma, which must start at zero.
 template <int NC>
 __global__ __launch_bounds__(256) void ln_mod_bwd_kernel(const float* __restrict__ X,
                                                          const float* __restrict__ dH,
@@ -236,6 +217,7 @@ __global__ __launch_bounds__(256) void ln_mod_bwd_kernel(const float* __restrict
   constexpr int PER = 2 * NC, D = 128 * NC;
   __shared__ float red[4][2][D];
   const int b = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wg = blockIdx.y * 4 + w, nw = gridDim.y * 4;
   const float* gam = mod + (int64_t)b * ms + scoff;
   float g1[PER], sh[PER], shx[PER];
 #pragma unroll
@@ -244,7 +226,7 @@ __global__ __launch_bounds__(256) void ln_mod_bwd_kernel(const float* __restrict
     sh[i] = 0.0f;
     shx[i] = 0.0f;
   }
-  for (int t = w; t < T; t += 4) {
+  for (int t = wg; t < T; t += nw) {
     const int64_t row = ((int64_t)b * T + t) * D;
     float x[PER], dh[PER];
 #pragma unroll
@@ -285,8 +267,10 @@ __global__ __launch_bounds__(256) void ln_mod_bwd_kernel(const float* __restrict
   }
   __syncthreads();
   for (int n = threadIdx.x; n < D; n += 256) {
-    dmod[(int64_t)b * ms + shoff + n] = red[0][0][n] + red[1][0][n] + red[2][0][n] + red[3][0][n];
-    dmod[(int64_t)b * ms + scoff + n] = red[0][1][n] + red[1][1][n] + red[2][1][n] + red[3][1][n];
+    unsafeAtomicAdd(&dmod[(int64_t)b * ms + shoff + n],
+                    red[0][0][n] + red[1][0][n] + red[2][0][n] + red[3][0][n]);
+    unsafeAtomicAdd(&dmod[(int64_t)b * ms + scoff + n],
+                    red[0][1][n] + red[1][1][n] + red[2][1][n] + red[3][1][n]);
   }
 }
 
@@ -347,13 +331,64 @@ __global__ __launch_bounds__(256) void transpose_kernel(const IT* __restrict__ i
   }
 }
 
-// out[r] = sum over c < cols of in[r * ld + c]; one workgroup per row.
-template <typename IT>
+// bf16 -> bf16 transpose with 16-byte global accesses (R, Cc, ldi, ldo
+// multiples of 8, 16-byte aligned): a 64 x 64 tile is read as 8-element row
+// pieces, kept in LDS, and written as 8-element pieces of the output rows.
+template <int OP>
+__global__ __launch_bounds__(256) void transpose16_kernel(const bf16_t* __restrict__ in, int64_t R,
+                                                          int64_t Cc, int64_t ldi,
+                                                          bf16_t* __restrict__ out, int64_t ldo) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+  const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int id = tid + 256 * u, row = id >> 3, cc = (id & 7) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + row < R && c0 + cc < Cc) v = *(const uint4*)(in + (r0 + row) * ldi + c0 + cc);
+    if constexpr (OP == 1) {
+      uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        wv[i] = f2bf2(gelu_tanh_f(__uint_as_float(wv[i] << 16)),
+                      gelu_tanh_f(__uint_as_float(wv[i] & 0xFFFF0000u)));
+      v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    *(uint4*)&tile[row][cc] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int id = tid + 256 * u, oc = id >> 3, rr = (id & 7) * 8;
+    if (c0 + oc < Cc && r0 + rr < R) {
+      uint32_t wv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        wv[i] = (uint32_t)tile[rr + 2 * i][oc] | ((uint32_t)tile[rr + 2 * i + 1][oc] << 16);
+      *(uint4*)(out + (c0 + oc) * ldo + r0 + rr) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+  }
+}
+
+// out[r] = sum over c < cols of in[r * ld + c]; one workgroup per row.  VEC:
+// bf16 rows read 8 at a time (cols and ld multiples of 8, 16-byte aligned).
+template <typename IT, bool VEC>
 __global__ __launch_bounds__(256) void rowsum_kernel(const IT* __restrict__ in, int64_t cols,
                                                      int64_t ld, float* __restrict__ out) {
   const int64_t r = blockIdx.x;
   float s = 0.0f;
-  for (int64_t c = threadIdx.x; c < cols; c += 256) s += to_f<IT>(in[r * ld + c]);
+  if constexpr (VEC) {
+    const uint4* p = (const uint4*)(in + r * ld);
+    for (int64_t c = threadIdx.x; c < cols / 8; c += 256) {
+      const uint4 u = p[c];
+      const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s += __uint_as_float(wv[i] << 16) + __uint_as_float(wv[i] & 0xFFFF0000u);
+    }
+  } else {
+    for (int64_t c = threadIdx.x; c < cols; c += 256) s += to_f<IT>(in[r * ld + c]);
+  }
   __shared__ float red[4];
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
@@ -400,8 +435,20 @@ __global__ void attn_bwd_dot_kernel(const DT* __restrict__ O, const DT* __restri
   const DT* o = O + tok * H * DH + h * DH;
   const DT* g = dO + tok * H * DH + h * DH;
   float s = 0.0f;
+  if constexpr (sizeof(DT) == 2) {
+#pragma unroll
+    for (int c = 0; c < DH / 8; ++c) {
+      const uint4 a = ((const uint4*)o)[c], b = ((const uint4*)g)[c];
+      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s += __uint_as_float(av[i] << 16) * __uint_as_float(bv[i] << 16) +
+             __uint_as_float(av[i] & 0xFFFF0000u) * __uint_as_float(bv[i] & 0xFFFF0000u);
+    }
+  } else {
 #pragma unroll 8
-  for (int e = 0; e < DH; ++e) s += to_f<DT>(o[e]) * to_f<DT>(g[e]);
+    for (int e = 0; e < DH; ++e) s += to_f<DT>(o[e]) * to_f<DT>(g[e]);
+  }
   const int64_t b = tok / T;
   Dv[(b * H + h) * T + (tok - b * T)] = s;
 }
@@ -593,25 +640,6 @@ hipError_t launch_gate_residual(const float* Xin, const float* v, const float* m
   return hipGetLastError();
 }
 
-hipError_t launch_gelu(const void* pre, void* G, int64_t n, int dtype, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  if (dtype == 1)
-    gelu_kernel<bf16_t><<<blocks_for(n), 256, 0, s>>>((const bf16_t*)pre, (bf16_t*)G, n);
-  else
-    gelu_kernel<float><<<blocks_for(n), 256, 0, s>>>((const float*)pre, (float*)G, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_dgelu(const float* dG, const void* pre, void* dpre, int64_t n, int dtype,
-                        hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  if (dtype == 1)
-    dgelu_kernel<bf16_t><<<blocks_for(n), 256, 0, s>>>(dG, (const bf16_t*)pre, (bf16_t*)dpre, n);
-  else
-    dgelu_kernel<float><<<blocks_for(n), 256, 0, s>>>(dG, (const float*)pre, (float*)dpre, n);
-  return hipGetLastError();
-}
-
 hipError_t launch_silu_f32(const float* z, float* out, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   silu_f32_kernel<<<blocks_for(n), 256, 0, s>>>(z, out, n);
@@ -663,9 +691,14 @@ hipError_t launch_ln_mod_bwd(const float* X, const float* dH, const float* mod, 
                              hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (d % 128 || d > 2048) return hipErrorInvalidValue;
+  // about 1024 workgroups, each with at least one token per wave
+  int split = (1024 + B - 1) / B;
+  split = split > (T + 3) / 4 ? (T + 3) / 4 : split;
+  split = split < 1 ? 1 : (split > 16 ? 16 : split);
 #define DIT_LNB(NC)                                                                         \
   case NC:                                                                                  \
-    ln_mod_bwd_kernel<NC><<<B, 256, 0, s>>>(X, dH, mod, ms, shoff, scoff, T, eps, dX, dmod); \
+    ln_mod_bwd_kernel<NC><<<dim3(B, split), 256, 0, s>>>(X, dH, mod, ms, shoff, scoff, T, eps, \
+                                                        dX, dmod);                             \
     break;
   switch (d / 128) {
     DIT_LNB(1) DIT_LNB(2) DIT_LNB(3) DIT_LNB(4) DIT_LNB(5) DIT_LNB(6) DIT_LNB(7) DIT_LNB(8)
@@ -702,6 +735,14 @@ hipError_t launch_transpose(const void* in, int in_dtype, int64_t R, int64_t Cc,
   if (R <= 0 || Cc <= 0) return hipSuccess;
   if ((Cc + 63) / 64 > INT32_MAX || (R + 63) / 64 > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((Cc + 63) / 64), (unsigned)((R + 63) / 64));
+  if (in_dtype == 1 && out_dtype == 1 && R % 8 == 0 && Cc % 8 == 0 && ldi % 8 == 0 &&
+      ldo % 8 == 0 && ((uintptr_t)in & 15) == 0 && ((uintptr_t)out & 15) == 0) {
+    if (gelu)
+      transpose16_kernel<1><<<grid, 256, 0, s>>>((const bf16_t*)in, R, Cc, ldi, (bf16_t*)out, ldo);
+    else
+      transpose16_kernel<0><<<grid, 256, 0, s>>>((const bf16_t*)in, R, Cc, ldi, (bf16_t*)out, ldo);
+    return hipGetLastError();
+  }
 #define DIT_TR(IT, OT)                                                                         \
   if (gelu)                                                                                    \
     transpose_kernel<IT, OT, 1><<<grid, 256, 0, s>>>((const IT*)in, R, Cc, ldi, (OT*)out, ldo); \
@@ -718,10 +759,13 @@ hipError_t launch_transpose(const void* in, int in_dtype, int64_t R, int64_t Cc,
 hipError_t launch_rowsum(const void* in, int dtype, int rows, int64_t cols, int64_t ld, float* out,
                          hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (dtype == 1)
-    rowsum_kernel<bf16_t><<<rows, 256, 0, s>>>((const bf16_t*)in, cols, ld, out);
+  const bool vec = cols % 8 == 0 && ld % 8 == 0 && ((uintptr_t)in & 15) == 0;
+  if (dtype == 1 && vec)
+    rowsum_kernel<bf16_t, true><<<rows, 256, 0, s>>>((const bf16_t*)in, cols, ld, out);
+  else if (dtype == 1)
+    rowsum_kernel<bf16_t, false><<<rows, 256, 0, s>>>((const bf16_t*)in, cols, ld, out);
   else
-    rowsum_kernel<float><<<rows, 256, 0, s>>>((const float*)in, cols, ld, out);
+    rowsum_kernel<float, false><<<rows, 256, 0, s>>>((const float*)in, cols, ld, out);
   return hipGetLastError();
 }
 

@@ -101,7 +101,7 @@ int check_train(const dit_handle* h) {
 struct TrainLayout {
   size_t coef, tf, acc, xt, P, PT, e, t1pre, th, c, sc, mod, dmod, pe;
   size_t Xs, Xmid, H1, qkv, O, lse, o, H2, pre, f, G, Hf, Y;
-  size_t dY, dYT, dX, dH, dBr, dBrT, actT, dG, dpre, dpreT, dO, Dv, dqkv, dqkvT;
+  size_t dY, dYT, dX, dH, dBr, dBrT, actT, dpre, dpreT, dO, Dv, dqkv, dqkvT;
   size_t wqkv, wo, wfc1, wfc2, wout, wada, wt2;
   size_t dmod_dt, dmodT, scT, dsc, dc, dcT, thT, dth, dt1, dt1T, eT;
   size_t total;
@@ -154,7 +154,6 @@ TrainLayout train_layout(const dit_handle* h, int B) {
   L.dBr = take(M * d * es);
   L.dBrT = take(d * M * es);
   L.actT = take(hid * M * es > d * M * es ? hid * M * es : d * M * es);
-  L.dG = take(M * hid * 4);
   L.dpre = take(M * hid * es);
   L.dpreT = take(hid * M * es);
   L.dO = take(M * d * es);
@@ -316,6 +315,7 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
   const int64_t per_row = (int64_t)C * h->cfg.height * h->cfg.width;
   DIT_HIP(launch_train_noise(x0, noise, coef, per_row, per_row * B, dt, at<void>(ws, L.xt), s));
   DIT_HIP(launch_fill_f32(grad, (int64_t)P.total, 0.0f, s));
+  DIT_HIP(launch_fill_f32(dmod, (int64_t)B * ms, 0.0f, s));   // LN backward adds into it
   for (int l = 0; l < N; ++l) {
     DIT_HIP(launch_transpose(wl(F_QKV_W, l, (size_t)3 * d * d), dt, 3 * d, d, d,
                              at<char>(ws, L.wqkv) + (size_t)l * d * 3 * d * es, dt, 3 * d, 0, s));
@@ -398,10 +398,10 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
     DIT_HIP(launch_ln_modulate(Xm(l), (int)M, (int)T, d, mod, ms, base + 3 * d, base + 4 * d,
                                h->eps, H2(l), dt, s));
     ep = epi0();
-    ep.bias = (const float*)W_(F_FC1_B) + (size_t)l * hid; ep.out = PRE(l); ep.ldo = hid;
-    DIT_HIP(linear(h, EPI_BIAS_DT, H2(l), d, wl(F_FC1_W, l, (size_t)hid * d), (int)M, hid, d, ep,
+    ep.bias = (const float*)W_(F_FC1_B) + (size_t)l * hid; ep.out = Gs; ep.aux = PRE(l);
+    ep.ldo = hid;
+    DIT_HIP(linear(h, EPI_GELU2, H2(l), d, wl(F_FC1_W, l, (size_t)hid * d), (int)M, hid, d, ep,
                    s));
-    DIT_HIP(launch_gelu(PRE(l), Gs, M * hid, dt, s));
     ep = epi0();
     ep.bias = (const float*)W_(F_FC2_B) + (size_t)l * d; ep.out = fb_(l); ep.ldo = d;
     DIT_HIP(linear(h, EPI_BIAS_F32, Gs, hid, wl(F_FC2_W, l, (size_t)d * hid), (int)M, d, hid, ep,
@@ -443,7 +443,6 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
   // ---- blocks, last to first -------------------------------------------------------------
   void* dBr = at<void>(ws, L.dBr);
   void* dBrT = at<void>(ws, L.dBrT);
-  float* dG = at<float>(ws, L.dG);
   void* dpre = at<void>(ws, L.dpre);
   void* dpreT = at<void>(ws, L.dpreT);
   void* dO = at<void>(ws, L.dO);
@@ -458,10 +457,9 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
     DIT_HIP(launch_transpose(PRE(l), dt, M, hid, hid, actT, dt, M, 1, s));   // GELU(pre)^T
     DIT_HIP(wgrad(dBrT, actT, dt, d, hid, M, G_(F_FC2_W) + (size_t)l * d * hid, s));
     EpiParams ep = epi0();
-    ep.out = dG; ep.ldo = hid;
-    DIT_HIP(gemm_any(EPI_BIAS_F32, dBr, dt, d, at<char>(ws, L.wfc2) + (size_t)l * hid * d * es, dt,
+    ep.out = dpre; ep.aux = PRE(l); ep.ldo = hid;   // d pre = (df W2) GELU'(pre)
+    DIT_HIP(gemm_any(EPI_DGELU, dBr, dt, d, at<char>(ws, L.wfc2) + (size_t)l * hid * d * es, dt,
                      d, (int)M, hid, d, ep, s));
-    DIT_HIP(launch_dgelu(dG, PRE(l), dpre, M * hid, dt, s));
     DIT_HIP(launch_transpose(dpre, dt, M, hid, hid, dpreT, dt, M, 0, s));
     DIT_HIP(launch_rowsum(dpreT, dt, hid, M, M, G_(F_FC1_B) + (size_t)l * hid, s));
     DIT_HIP(launch_transpose(H2(l), dt, M, d, d, actT, dt, M, 0, s));
