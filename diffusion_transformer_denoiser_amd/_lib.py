@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdit.so")
 
 DIT_OK, DIT_EINVAL, DIT_EUNSUPPORTED, DIT_EWORKSPACE, DIT_EHIP = 0, -1, -2, -3, -4
 DIT_F32, DIT_BF16 = 0, 1
-DIT_EPI_BIAS, DIT_EPI_GELU, DIT_EPI_GATED = 0, 1, 2
+DIT_EPI_BIAS, DIT_EPI_GELU, DIT_EPI_GATED, DIT_EPI_ACCUM = 0, 1, 2, 3
 DIT_SAMPLER_DDPM, DIT_SAMPLER_DPMPP_2M, DIT_SAMPLER_RF_EULER = 0, 1, 2
 DIT_COND_ADALN_ZERO, DIT_COND_IN_CONTEXT, DIT_COND_CROSS_ATTN, DIT_COND_MMDIT = 0, 1, 2, 3
 

@@ -110,6 +110,17 @@ WsLayout ws_layout(const dit_handle* h, int rows) {
 }  // namespace
 
 namespace dit_host {
+int splitk_slice(bool mfma, int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = mfma ? ((M + (M <= 64 ? 63 : 127)) / (M <= 64 ? 64 : 128)) *
+                                   ((N + (N % 192 ? 127 : 191)) / (N % 192 ? 128 : 192))
+                             : ((M + 63) / 64) * ((N + 63) / 64);
+  const int kstep = mfma ? 64 : 16;
+  const int64_t want = tiles >= 1024 ? 1 : (1024 + tiles - 1) / tiles;
+  int64_t ks = (K + want - 1) / want;
+  ks = (ks + kstep - 1) / kstep * kstep;
+  return ks >= K ? 0 : (int)ks;
+}
+
 EpiParams epi0() {
   EpiParams ep;
   memset(&ep, 0, sizeof ep);
@@ -1122,8 +1133,11 @@ int dit_linear(int epilogue, const void* A, const void* W, const float* bias, in
     case DIT_EPI_BIAS: epi = EPI_BIAS_F32; break;
     case DIT_EPI_GELU: epi = EPI_GELU; break;
     case DIT_EPI_GATED: epi = EPI_GATED; break;
+    case DIT_EPI_ACCUM: epi = EPI_ATOMIC_F32; break;
     default: return fail(DIT_EINVAL, "unknown epilogue %d", epilogue);
   }
+  if (epilogue == DIT_EPI_ACCUM && bias)
+    return fail(DIT_EINVAL, "the accumulating epilogue takes no bias");
   if (epilogue == DIT_EPI_GATED && (!gate || T <= 0 || gate_stride < N))
     return fail(DIT_EINVAL, "gated epilogue needs gate, T > 0 and gate_stride >= N");
   if (dtype == DIT_BF16 && (K % 64 || ((uintptr_t)A & 15) || ((uintptr_t)W & 15)))
@@ -1131,6 +1145,7 @@ int dit_linear(int epilogue, const void* A, const void* W, const float* bias, in
   EpiParams ep = epi0();
   ep.bias = bias; ep.out = out; ep.ldo = N;
   ep.mod = gate; ep.mod_stride = gate_stride; ep.gate_off = 0; ep.T = T > 0 ? T : 1;
+  if (epilogue == DIT_EPI_ACCUM) ep.ksplit = splitk_slice(dtype == DIT_BF16, M, N, K);
   hipStream_t s = (hipStream_t)stream;
   if (dtype == DIT_BF16) {
     DIT_HIP(launch_gemm_mfma(epi, (const bf16_t*)A, K, (const bf16_t*)W, M, N, K, ep, s));

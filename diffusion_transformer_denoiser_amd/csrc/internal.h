@@ -46,6 +46,10 @@ int ok();
 size_t align256(size_t b);
 // Zero-initialised epilogue parameters.
 EpiParams epi0();
+// Split-K slice length for an EPI_ATOMIC_F32 product of M x N outputs over K
+// (0: no split): about 1024 workgroups, slices a multiple of the kernel's k
+// step (64 on the matrix cores, 16 on the VALU path).
+int splitk_slice(bool mfma, int64_t M, int64_t N, int64_t K);
 // One linear layer C = A W^T with the epilogue: MFMA for bf16 models, VALU
 // for fp32 ones.
 hipError_t linear(const dit_handle* h, int epi, const void* A, int lda, const void* W, int M,

@@ -201,16 +201,7 @@ hipError_t gemm_any(int epi, const void* A, int adt, int64_t lda, const void* W,
   ep.ldw = (int)ldw;
   const bool mfma = adt == 1 && wdt == 1 && K % 64 == 0 && lda % 8 == 0 && ldw % 8 == 0 &&
                     aligned16(A) && aligned16(W);
-  if (epi == EPI_ATOMIC_F32) {
-    const int64_t tiles = mfma ? (int64_t)((M + (M <= 64 ? 63 : 127)) / (M <= 64 ? 64 : 128)) *
-                                     ((N + (N % 192 ? 127 : 191)) / (N % 192 ? 128 : 192))
-                               : (int64_t)((M + 63) / 64) * ((N + 63) / 64);
-    const int kstep = mfma ? 64 : 16;
-    const int64_t want = tiles >= 1024 ? 1 : (1024 + tiles - 1) / tiles;
-    int64_t ks = (K + want - 1) / want;
-    ks = (ks + kstep - 1) / kstep * kstep;
-    ep.ksplit = ks >= K ? 0 : (int)ks;
-  }
+  if (epi == EPI_ATOMIC_F32) ep.ksplit = splitk_slice(mfma, M, N, K);
   if (mfma) return launch_gemm_mfma(epi, (const bf16_t*)A, (int)lda, (const bf16_t*)W, M, N, K, ep, s);
   ALoad a;
   memset(&a, 0, sizeof a);

@@ -287,6 +287,11 @@ int dit_attention(const void* qkv, int B, int H, int T, int dh, int dtype, void*
 #define DIT_EPI_BIAS  0
 #define DIT_EPI_GELU  1
 #define DIT_EPI_GATED 2
+/*   DIT_EPI_ACCUM: out fp32 [M, N] += A W^T (bias must be NULL): the weight-
+ *                  gradient product of a training step when A = dY^T, W = X^T.
+ *                  The reduction over K is split into slices whose partial
+ *                  sums are added atomically (summation order not fixed). */
+#define DIT_EPI_ACCUM 3
 int dit_linear(int epilogue, const void* A, const void* W, const float* bias, int M, int N,
                int K, int dtype, void* out, const float* gate, int gate_stride, int T,
                void* stream);

@@ -123,9 +123,38 @@ def test_linear_epilogues(M, N, K, dtype):
                 gate_stride=N + 8, T=T)
     gref = X0 + gate[np.arange(M) // T, :N] * ref
     e3 = rel_l2(np_(X) - X0, gref - X0)
-    log(f"  rel-L2 bias={e1:.2e} gelu={e2:.2e} gated-increment={e3:.2e}")
-    assert e1 <= tol and e3 <= tol
+    # accumulating (split-K, atomic) epilogue: out += A W^T
+    acc0 = rng.standard_normal((M, N)).astype(np.float32)
+    acc = torch.from_numpy(acc0).cuda()
+    dmod.linear(dmod.DIT_EPI_ACCUM, Ad, Wd, None, acc)
+    e4 = rel_l2(np_(acc) - acc0, ref - bias)
+    log(f"  rel-L2 bias={e1:.2e} gelu={e2:.2e} gated-increment={e3:.2e} accum={e4:.2e}")
+    assert e1 <= tol and e3 <= tol and e4 <= tol
     assert e2 <= (tol if dtype == "f32" else 4e-3)     # bf16 output rounding
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [(96, 200, 8192, "bf16"), (1152, 384, 16384, "bf16"),
+                                         (64, 130, 4096, "f32"), (32, 1152, 65536, "bf16")])
+def test_linear_accumulate_long_reduction(M, N, K, dtype):
+    """Weight-gradient shapes: few outputs, long reduction, split into slices
+    whose partial sums add atomically; twice in a row accumulates twice."""
+    log(f"accumulating linear {dtype} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    W = rng.standard_normal((N, K)).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    if dtype == "bf16":
+        A, W = _bf16(A), _bf16(W)
+    ref = A.astype(np.float64) @ W.astype(np.float64).T
+    Ad = torch.from_numpy(A).to(tdt).cuda()
+    Wd = torch.from_numpy(W).to(tdt).cuda()
+    out = torch.zeros((M, N), device="cuda", dtype=torch.float32)
+    dmod.linear(dmod.DIT_EPI_ACCUM, Ad, Wd, None, out)
+    e1 = rel_l2(np_(out), ref)
+    dmod.linear(dmod.DIT_EPI_ACCUM, Ad, Wd, None, out)
+    e2 = rel_l2(np_(out), 2 * ref)
+    log(f"  rel-L2 once={e1:.2e} twice={e2:.2e}")
+    assert e1 <= 1e-5 and e2 <= 1e-5
 
 
 # --- attention ---------------------------------------------------------------------------
