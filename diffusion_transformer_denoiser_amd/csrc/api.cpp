@@ -115,8 +115,24 @@ int splitk_slice(bool mfma, int64_t M, int64_t N, int64_t K) {
                                    ((N + (N % 192 ? 127 : 191)) / (N % 192 ? 128 : 192))
                              : ((M + 63) / 64) * ((N + 63) / 64);
   const int kstep = mfma ? 64 : 16;
-  const int64_t want = tiles >= 1024 ? 1 : (1024 + tiles - 1) / tiles;
-  int64_t ks = (K + want - 1) / want;
+  // Workgroups resident at once: 256 CUs x 2 (the MFMA kernel's LDS allows
+  // two per CU); the VALU kernel fits more.  Take the fewest slices whose
+  // grid fills its last wave of resident workgroups to 92% or more (more
+  // slices only add atomic traffic), else the best fill found.
+  const int64_t slots = mfma ? 512 : 1024;
+  const int64_t max_s = K / kstep < 256 ? K / kstep : 256;
+  int64_t best = 1;
+  double best_fill = 0.0;
+  for (int64_t sp = 1; sp <= max_s; ++sp) {
+    const int64_t wg = tiles * sp, waves = (wg + slots - 1) / slots;
+    const double fill = (double)wg / (double)(waves * slots);
+    if (fill > best_fill + 0.02) {
+      best_fill = fill;
+      best = sp;
+    }
+    if (fill >= 0.92) break;
+  }
+  int64_t ks = (K + best - 1) / best;
   ks = (ks + kstep - 1) / kstep * kstep;
   return ks >= K ? 0 : (int)ks;
 }
