@@ -10,8 +10,8 @@
 //       v_mfma_f32_16x16x32_bf16 with each lane holding 4 queries of one key,
 //       which, for two 16-query blocks, is the B operand of dV^T = dO^T P and
 //       dK^T = Q^T dS once the queries inside each 32-query step are taken in
-//       the same order on the A side (a transposed copy of the tile in LDS,
-//       read as two 8-byte pieces);
+//       the same order on the A side (two transposing LDS reads of the
+//       row-major tile);
 //   q:  a workgroup owns 64 queries, 16 per wave, and streams 32-key tiles;
 //       S^T and V dO^T (keys x queries) give the B operand of dQ^T = K^T dS^T.
 // P never leaves registers.  dh = 72 runs its third 32-wide k step with lanes
@@ -26,13 +26,12 @@ namespace {
 
 constexpr int TQ = 32;            // tile of the streamed side
 constexpr int RLD = 72;           // row-major tile stride (elements)
-constexpr int TLD = TQ + 4;       // transposed tile stride (elements)
+constexpr int TSZ = TQ * RLD + 16;   // + 16: transposing reads past dh 72 of the last row stay inside
 
 template <int DH>
 struct Shape {
   static constexpr int NCH = (DH + 31) / 32;    // 32-wide k steps over dh
   static constexpr int NDB = (DH + 15) / 16;    // 16-row blocks of a dh x 16 accumulator
-  static constexpr int TR = NDB * 16;           // rows of a transposed tile
 };
 
 __device__ __forceinline__ bf16x8_t ld8(const bf16_t* p) { return *(const bf16x8_t*)p; }
@@ -46,12 +45,20 @@ __device__ __forceinline__ bf16x8_t row_chunk(const bf16_t* tile, int row, int c
   return ld8(tile + row * RLD + e);
 }
 
-// Operand taken from a transposed tile (dh rows, TQ columns): row r, the 4
-// columns 4g .. 4g+3 then 16 + 4g .. 16 + 4g + 3.
-__device__ __forceinline__ bf16x8_t trans_chunk(const bf16_t* tt, int r, int g) {
-  const uint2 lo = *(const uint2*)(tt + r * TLD + 4 * g);
-  const uint2 hi = *(const uint2*)(tt + r * TLD + 16 + 4 * g);
-  return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+// A operand over dh rows 16 db .. 16 db + 15 (lane c16: dh 16 db + c16) and
+// the 8 tile rows 4g .. 4g+3, 16 + 4g .. 16 + 4g + 3 of a row-major tile, by
+// two transposing LDS reads: lane c16 of group g addresses row 4g + c16 / 4,
+// columns 16 db + 4 (c16 % 4) .. + 3, and receives column 16 db + c16 of the
+// group's 4 rows.  Lanes past dh 72 read finite neighbouring data that only
+// reaches accumulator rows past dh, which are never stored.
+__device__ __forceinline__ bf16x8_t tr_operand(const bf16_t* tile, int db, int g, int c16) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const bf16_t* p = tile + (4 * g + (c16 >> 2)) * RLD + 16 * db + 4 * (c16 & 3);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+  const v4i16 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p + 16 * RLD));
+  return __builtin_bit_cast(bf16x8_t, (__attribute__((ext_vector_type(8))) short){
+                                          lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 }
 
 __device__ __forceinline__ bf16x8_t pack8(const floatx4& a, const floatx4& b) {
@@ -73,14 +80,6 @@ __device__ __forceinline__ void stage_rows(bf16_t* tile, const bf16_t* src, int6
   }
 }
 
-// tt[e][r] = tile[r][e] for e < DH (rows DH .. TR-1 of tt stay as set up).
-template <int DH>
-__device__ __forceinline__ void transpose_tile(bf16_t* tt, const bf16_t* tile, int tid) {
-  for (int i = tid; i < TQ * DH; i += 256) {
-    const int r = i / DH, e = i - r * DH;
-    tt[e * TLD + r] = tile[r * RLD + e];
-  }
-}
 
 template <int DH>
 __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict__ QKV,
@@ -89,8 +88,7 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict
                                                         const float* __restrict__ Dv, int H, int T,
                                                         float sl2, bf16_t* __restrict__ dQKV) {
   using S = Shape<DH>;
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[TQ * RLD], sG[TQ * RLD];
-  __shared__ __attribute__((aligned(16))) bf16_t sQT[S::TR * TLD], sGT[S::TR * TLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[TSZ], sG[TSZ];
   __shared__ float sL[TQ], sD[TQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -116,10 +114,9 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict
     dk[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     dv[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  // rows DH .. TR-1 of the transposed tiles: zero once
-  for (int i = tid; i < (S::TR - DH) * TLD; i += 256) {
-    sQT[DH * TLD + i] = f2bf(0.0f);
-    sGT[DH * TLD + i] = f2bf(0.0f);
+  if (tid < 16) {   // the pad after each tile: finite values
+    sQ[TQ * RLD + tid] = f2bf(0.0f);
+    sG[TQ * RLD + tid] = f2bf(0.0f);
   }
   const float* L = lse + (int64_t)bh * T;
   const float* Dd = Dv + (int64_t)bh * T;
@@ -134,9 +131,6 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict
       sL[tid] = q < T ? L[q] * LOG2E : INFINITY;   // exp2(. - inf) = 0 for missing queries
       sD[tid] = q < T ? Dd[q] : 0.0f;
     }
-    __syncthreads();
-    transpose_tile<DH>(sQT, sQ, tid);
-    transpose_tile<DH>(sGT, sG, tid);
     __syncthreads();
 
     // S, dP (queries x this wave's keys): lane holds queries 16 qb + 4 g + r.
@@ -167,10 +161,10 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict
     const bf16x8_t dsf = pack8(ds[0], ds[1]);
 #pragma unroll
     for (int db = 0; db < S::NDB; ++db) {
-      dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(trans_chunk(sGT, 16 * db + c16, g), pf,
-                                                        dv[db], 0, 0, 0);
-      dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(trans_chunk(sQT, 16 * db + c16, g), dsf,
-                                                        dk[db], 0, 0, 0);
+      dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand(sG, db, g, c16), pf, dv[db],
+                                                        0, 0, 0);
+      dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand(sQ, db, g, c16), dsf, dk[db],
+                                                        0, 0, 0);
     }
   }
 
@@ -198,8 +192,7 @@ __global__ __launch_bounds__(256) void attn_bwd_q_mfma(const bf16_t* __restrict_
                                                        const float* __restrict__ Dv, int H, int T,
                                                        float sl2, bf16_t* __restrict__ dQKV) {
   using S = Shape<DH>;
-  __shared__ __attribute__((aligned(16))) bf16_t sK[TQ * RLD], sV[TQ * RLD];
-  __shared__ __attribute__((aligned(16))) bf16_t sKT[S::TR * TLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sK[TSZ], sV[TSZ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
@@ -223,14 +216,15 @@ __global__ __launch_bounds__(256) void attn_bwd_q_mfma(const bf16_t* __restrict_
   floatx4 dq[S::NDB];
 #pragma unroll
   for (int db = 0; db < S::NDB; ++db) dq[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int i = tid; i < (S::TR - DH) * TLD; i += 256) sKT[DH * TLD + i] = f2bf(0.0f);
+  if (tid < 16) {
+    sK[TQ * RLD + tid] = f2bf(0.0f);
+    sV[TQ * RLD + tid] = f2bf(0.0f);
+  }
 
   for (int k0 = 0; k0 < T; k0 += TQ) {
     __syncthreads();
     stage_rows<DH>(sK, Qb + ldo, ld, k0, T, tid);
     stage_rows<DH>(sV, Qb + 2 * ldo, ld, k0, T, tid);
-    __syncthreads();
-    transpose_tile<DH>(sKT, sK, tid);
     __syncthreads();
 
     // S^T, dP^T (keys x this wave's queries): lane holds keys 16 kb + 4 g + r.
@@ -259,8 +253,8 @@ __global__ __launch_bounds__(256) void attn_bwd_q_mfma(const bf16_t* __restrict_
     const bf16x8_t dsf = pack8(dst[0], dst[1]);
 #pragma unroll
     for (int db = 0; db < S::NDB; ++db)
-      dq[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(trans_chunk(sKT, 16 * db + c16, g), dsf,
-                                                        dq[db], 0, 0, 0);
+      dq[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand(sK, db, g, c16), dsf, dq[db],
+                                                        0, 0, 0);
   }
 
   if (qval) {
