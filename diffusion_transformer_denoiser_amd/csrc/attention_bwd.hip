@@ -12,7 +12,7 @@
 //       dK^T = Q^T dS once the queries inside each 32-query step are taken in
 //       the same order on the A side (two transposing LDS reads of the
 //       row-major tile);
-//   q:  a workgroup owns 64 queries, 16 per wave, and streams 32-key tiles;
+//   q:  a workgroup owns 64 queries, 16 per wave, and streams 64-key tiles;
 //       S^T and V dO^T (keys x queries) give the B operand of dQ^T = K^T dS^T.
 // P never leaves registers.  dh = 72 runs its third 32-wide k step with lanes
 // past dh 72 holding zeros.
@@ -24,9 +24,15 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 namespace {
 
-constexpr int TQ = 32;            // tile of the streamed side
+// Tiles of the streamed side are NB x 32 rows (the dK/dV kernel measured
+// fastest with 32, the dQ kernel with 64), stored row-major with stride RLD
+// and 16 elements of padding (transposing reads past dh 72 of the last row).
 constexpr int RLD = 72;           // row-major tile stride (elements)
-constexpr int TSZ = TQ * RLD + 16;   // + 16: transposing reads past dh 72 of the last row stay inside
+template <int NB>
+struct Tile {
+  static constexpr int TQ = 32 * NB;
+  static constexpr int SZ = TQ * RLD + 16;
+};
 
 template <int DH>
 struct Shape {
@@ -68,7 +74,7 @@ __device__ __forceinline__ bf16x8_t pack8(const floatx4& a, const floatx4& b) {
 
 // Stage TQ rows (row0 ..) of the dh slice at `src` (row stride ld elements)
 // into a row-major tile; rows at or past T are zero.
-template <int DH>
+template <int DH, int TQ>
 __device__ __forceinline__ void stage_rows(bf16_t* tile, const bf16_t* src, int64_t ld, int row0,
                                            int T, int tid) {
   constexpr int CPR = DH / 8;   // 16-byte chunks per row
@@ -81,14 +87,15 @@ __device__ __forceinline__ void stage_rows(bf16_t* tile, const bf16_t* src, int6
 }
 
 
-template <int DH>
+template <int DH, int NB>
 __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict__ QKV,
                                                         const bf16_t* __restrict__ dO,
                                                         const float* __restrict__ lse,
                                                         const float* __restrict__ Dv, int H, int T,
                                                         float sl2, bf16_t* __restrict__ dQKV) {
   using S = Shape<DH>;
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[TSZ], sG[TSZ];
+  constexpr int TQ = Tile<NB>::TQ;
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[Tile<NB>::SZ], sG[Tile<NB>::SZ];
   __shared__ float sL[TQ], sD[TQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -124,8 +131,8 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict
 
   for (int q0 = 0; q0 < T; q0 += TQ) {
     __syncthreads();   // previous tile fully consumed
-    stage_rows<DH>(sQ, Qb, ld, q0, T, tid);
-    stage_rows<DH>(sG, Gb, ldo, q0, T, tid);
+    stage_rows<DH, TQ>(sQ, Qb, ld, q0, T, tid);
+    stage_rows<DH, TQ>(sG, Gb, ldo, q0, T, tid);
     if (tid < TQ) {
       const int q = q0 + tid;
       sL[tid] = q < T ? L[q] * LOG2E : INFINITY;   // exp2(. - inf) = 0 for missing queries
@@ -134,9 +141,9 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict
     __syncthreads();
 
     // S, dP (queries x this wave's keys): lane holds queries 16 qb + 4 g + r.
-    floatx4 s[2], dp[2];
+    floatx4 s[2 * NB], dp[2 * NB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < 2 * NB; ++qb) {
       s[qb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
       dp[qb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -147,9 +154,9 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict
                                                           vf[ch], dp[qb], 0, 0, 0);
       }
     }
-    floatx4 p[2], ds[2];
+    floatx4 p[2 * NB], ds[2 * NB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < 2 * NB; ++qb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int qi = 16 * qb + 4 * g + r;
@@ -157,14 +164,17 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict
         p[qb][r] = pv;
         ds[qb][r] = pv * (dp[qb][r] - sD[qi]);
       }
-    const bf16x8_t pf = pack8(p[0], p[1]);
-    const bf16x8_t dsf = pack8(ds[0], ds[1]);
 #pragma unroll
-    for (int db = 0; db < S::NDB; ++db) {
-      dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand(sG, db, g, c16), pf, dv[db],
-                                                        0, 0, 0);
-      dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand(sQ, db, g, c16), dsf, dk[db],
-                                                        0, 0, 0);
+    for (int j = 0; j < NB; ++j) {   // 32-query step j: blocks 2j, 2j + 1
+      const bf16x8_t pf = pack8(p[2 * j], p[2 * j + 1]);
+      const bf16x8_t dsf = pack8(ds[2 * j], ds[2 * j + 1]);
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand(sG + 32 * j * RLD, db, g, c16),
+                                                          pf, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand(sQ + 32 * j * RLD, db, g, c16),
+                                                          dsf, dk[db], 0, 0, 0);
+      }
     }
   }
 
@@ -185,14 +195,15 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict
   }
 }
 
-template <int DH>
+template <int DH, int NB>
 __global__ __launch_bounds__(256) void attn_bwd_q_mfma(const bf16_t* __restrict__ QKV,
                                                        const bf16_t* __restrict__ dO,
                                                        const float* __restrict__ lse,
                                                        const float* __restrict__ Dv, int H, int T,
                                                        float sl2, bf16_t* __restrict__ dQKV) {
   using S = Shape<DH>;
-  __shared__ __attribute__((aligned(16))) bf16_t sK[TSZ], sV[TSZ];
+  constexpr int TQ = Tile<NB>::TQ;
+  __shared__ __attribute__((aligned(16))) bf16_t sK[Tile<NB>::SZ], sV[Tile<NB>::SZ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
@@ -223,14 +234,14 @@ __global__ __launch_bounds__(256) void attn_bwd_q_mfma(const bf16_t* __restrict_
 
   for (int k0 = 0; k0 < T; k0 += TQ) {
     __syncthreads();
-    stage_rows<DH>(sK, Qb + ldo, ld, k0, T, tid);
-    stage_rows<DH>(sV, Qb + 2 * ldo, ld, k0, T, tid);
+    stage_rows<DH, TQ>(sK, Qb + ldo, ld, k0, T, tid);
+    stage_rows<DH, TQ>(sV, Qb + 2 * ldo, ld, k0, T, tid);
     __syncthreads();
 
     // S^T, dP^T (keys x this wave's queries): lane holds keys 16 kb + 4 g + r.
-    floatx4 st[2], dpt[2];
+    floatx4 st[2 * NB], dpt[2 * NB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2 * NB; ++kb) {
       st[kb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
       dpt[kb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -241,20 +252,23 @@ __global__ __launch_bounds__(256) void attn_bwd_q_mfma(const bf16_t* __restrict_
                                                            gf[ch], dpt[kb], 0, 0, 0);
       }
     }
-    floatx4 dst[2];
+    floatx4 dst[2 * NB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2 * NB; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kj = k0 + 16 * kb + 4 * g + r;
         const float pv = kj < T ? __builtin_amdgcn_exp2f(st[kb][r] * sl2 - lq) : 0.0f;
         dst[kb][r] = pv * (dpt[kb][r] - dq_);
       }
-    const bf16x8_t dsf = pack8(dst[0], dst[1]);
 #pragma unroll
-    for (int db = 0; db < S::NDB; ++db)
-      dq[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand(sK, db, g, c16), dsf, dq[db],
-                                                        0, 0, 0);
+    for (int j = 0; j < NB; ++j) {   // 32-key step j
+      const bf16x8_t dsf = pack8(dst[2 * j], dst[2 * j + 1]);
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db)
+        dq[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand(sK + 32 * j * RLD, db, g, c16),
+                                                          dsf, dq[db], 0, 0, 0);
+    }
   }
 
   if (qval) {
@@ -280,14 +294,14 @@ hipError_t launch_attention_bwd_mfma(const void* qkv, const void* dO, const floa
   const float sl2 = 1.4426950408889634f / sqrtf((float)dh);
   const dim3 grid((T + 63) / 64, B * heads);
   if (dh == 64) {
-    attn_bwd_kv_mfma<64><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
+    attn_bwd_kv_mfma<64, 1><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
                                               heads, T, sl2, (bf16_t*)dqkv);
-    attn_bwd_q_mfma<64><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
+    attn_bwd_q_mfma<64, 2><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
                                              heads, T, sl2, (bf16_t*)dqkv);
   } else {
-    attn_bwd_kv_mfma<72><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
+    attn_bwd_kv_mfma<72, 1><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
                                               heads, T, sl2, (bf16_t*)dqkv);
-    attn_bwd_q_mfma<72><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
+    attn_bwd_q_mfma<72, 2><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
                                              heads, T, sl2, (bf16_t*)dqkv);
   }
   return hipGetLastError();
