@@ -72,19 +72,31 @@ __device__ __forceinline__ bf16x8_t pack8(const floatx4& a, const floatx4& b) {
                                                  f2bf2(b[0], b[1]), f2bf2(b[2], b[3])));
 }
 
-// Stage TQ rows (row0 ..) of the dh slice at `src` (row stride ld elements)
-// into a row-major tile; rows at or past T are zero.
+// Staging of TQ rows (row0 ..) of the dh slice at `src` (row stride ld
+// elements) into a row-major tile, in two halves so the next tile's global
+// loads are in flight while the current one is consumed: load() fills this
+// thread's registers (rows at or past T read as zeros), store() writes them.
 template <int DH, int TQ>
-__device__ __forceinline__ void stage_rows(bf16_t* tile, const bf16_t* src, int64_t ld, int row0,
-                                           int T, int tid) {
-  constexpr int CPR = DH / 8;   // 16-byte chunks per row
-  for (int c = tid; c < TQ * CPR; c += 256) {
-    const int r = c / CPR, e = (c - r * CPR) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row0 + r < T) v = *(const uint4*)(src + (int64_t)(row0 + r) * ld + e);
-    *(uint4*)(tile + r * RLD + e) = v;
+struct Stager {
+  static constexpr int CPR = DH / 8;                 // 16-byte chunks per row
+  static constexpr int PER = (TQ * CPR + 255) / 256;  // chunks per thread
+  uint4 v[PER];
+  __device__ __forceinline__ void load(const bf16_t* src, int64_t ld, int row0, int T, int tid) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + 256 * u, r = c / CPR, e = (c - r * CPR) * 8;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (c < TQ * CPR && row0 + r < T) v[u] = *(const uint4*)(src + (int64_t)(row0 + r) * ld + e);
+    }
   }
-}
+  __device__ __forceinline__ void store(bf16_t* tile, int tid) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + 256 * u, r = c / CPR, e = (c - r * CPR) * 8;
+      if (c < TQ * CPR) *(uint4*)(tile + r * RLD + e) = v[u];
+    }
+  }
+};
 
 
 template <int DH, int NB>
@@ -95,8 +107,8 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict
                                                         float sl2, bf16_t* __restrict__ dQKV) {
   using S = Shape<DH>;
   constexpr int TQ = Tile<NB>::TQ;
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[Tile<NB>::SZ], sG[Tile<NB>::SZ];
-  __shared__ float sL[TQ], sD[TQ];
+  __shared__ __attribute__((aligned(16))) bf16_t sQb[2][Tile<NB>::SZ], sGb[2][Tile<NB>::SZ];
+  __shared__ float sLb[2][TQ], sDb[2][TQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
@@ -122,23 +134,51 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict
     dv[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   }
   if (tid < 16) {   // the pad after each tile: finite values
-    sQ[TQ * RLD + tid] = f2bf(0.0f);
-    sG[TQ * RLD + tid] = f2bf(0.0f);
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      sQb[bb][TQ * RLD + tid] = f2bf(0.0f);
+      sGb[bb][TQ * RLD + tid] = f2bf(0.0f);
+    }
   }
   const float* L = lse + (int64_t)bh * T;
   const float* Dd = Dv + (int64_t)bh * T;
   const float LOG2E = 1.4426950408889634f;
-
-  for (int q0 = 0; q0 < T; q0 += TQ) {
-    __syncthreads();   // previous tile fully consumed
-    stage_rows<DH, TQ>(sQ, Qb, ld, q0, T, tid);
-    stage_rows<DH, TQ>(sG, Gb, ldo, q0, T, tid);
+  Stager<DH, TQ> stq, stg;
+  float lv = 0.0f, dv_ = 0.0f;
+  // per-query constants of tile rows: exp2(. - inf) = 0 for missing queries
+  auto load_consts = [&](int q0) {
     if (tid < TQ) {
       const int q = q0 + tid;
-      sL[tid] = q < T ? L[q] * LOG2E : INFINITY;   // exp2(. - inf) = 0 for missing queries
-      sD[tid] = q < T ? Dd[q] : 0.0f;
+      lv = q < T ? L[q] * LOG2E : INFINITY;
+      dv_ = q < T ? Dd[q] : 0.0f;
     }
-    __syncthreads();
+  };
+  auto store_consts = [&](int bb) {
+    if (tid < TQ) {
+      sLb[bb][tid] = lv;
+      sDb[bb][tid] = dv_;
+    }
+  };
+  stq.load(Qb, ld, 0, T, tid);
+  stg.load(Gb, ldo, 0, T, tid);
+  load_consts(0);
+  stq.store(sQb[0], tid);
+  stg.store(sGb[0], tid);
+  store_consts(0);
+  __syncthreads();
+
+  for (int it = 0, q0 = 0; q0 < T; ++it, q0 += TQ) {
+    const int bb = it & 1;
+    const bool more = q0 + TQ < T;
+    if (more) {   // next tile's loads in flight during this one
+      stq.load(Qb, ld, q0 + TQ, T, tid);
+      stg.load(Gb, ldo, q0 + TQ, T, tid);
+      load_consts(q0 + TQ);
+    }
+    const bf16_t* sQ = sQb[bb];
+    const bf16_t* sG = sGb[bb];
+    const float* sL = sLb[bb];
+    const float* sD = sDb[bb];
 
     // S, dP (queries x this wave's keys): lane holds queries 16 qb + 4 g + r.
     floatx4 s[2 * NB], dp[2 * NB];
@@ -176,6 +216,13 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_mfma(const bf16_t* __restrict
                                                           dsf, dk[db], 0, 0, 0);
       }
     }
+    // the other buffer was last read in the previous iteration, before its barrier
+    if (more) {
+      stq.store(sQb[bb ^ 1], tid);
+      stg.store(sGb[bb ^ 1], tid);
+      store_consts(bb ^ 1);
+    }
+    __syncthreads();
   }
 
   // lane holds dh 16 db + 4 g + r of `key`
@@ -203,7 +250,7 @@ __global__ __launch_bounds__(256) void attn_bwd_q_mfma(const bf16_t* __restrict_
                                                        float sl2, bf16_t* __restrict__ dQKV) {
   using S = Shape<DH>;
   constexpr int TQ = Tile<NB>::TQ;
-  __shared__ __attribute__((aligned(16))) bf16_t sK[Tile<NB>::SZ], sV[Tile<NB>::SZ];
+  __shared__ __attribute__((aligned(16))) bf16_t sKb[2][Tile<NB>::SZ], sVb[2][Tile<NB>::SZ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
@@ -228,15 +275,28 @@ __global__ __launch_bounds__(256) void attn_bwd_q_mfma(const bf16_t* __restrict_
 #pragma unroll
   for (int db = 0; db < S::NDB; ++db) dq[db] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   if (tid < 16) {
-    sK[TQ * RLD + tid] = f2bf(0.0f);
-    sV[TQ * RLD + tid] = f2bf(0.0f);
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      sKb[bb][TQ * RLD + tid] = f2bf(0.0f);
+      sVb[bb][TQ * RLD + tid] = f2bf(0.0f);
+    }
   }
+  Stager<DH, TQ> stk, stv;
+  stk.load(Qb + ldo, ld, 0, T, tid);
+  stv.load(Qb + 2 * ldo, ld, 0, T, tid);
+  stk.store(sKb[0], tid);
+  stv.store(sVb[0], tid);
+  __syncthreads();
 
-  for (int k0 = 0; k0 < T; k0 += TQ) {
-    __syncthreads();
-    stage_rows<DH, TQ>(sK, Qb + ldo, ld, k0, T, tid);
-    stage_rows<DH, TQ>(sV, Qb + 2 * ldo, ld, k0, T, tid);
-    __syncthreads();
+  for (int it = 0, k0 = 0; k0 < T; ++it, k0 += TQ) {
+    const int bb = it & 1;
+    const bool more = k0 + TQ < T;
+    if (more) {
+      stk.load(Qb + ldo, ld, k0 + TQ, T, tid);
+      stv.load(Qb + 2 * ldo, ld, k0 + TQ, T, tid);
+    }
+    const bf16_t* sK = sKb[bb];
+    const bf16_t* sV = sVb[bb];
 
     // S^T, dP^T (keys x this wave's queries): lane holds keys 16 kb + 4 g + r.
     floatx4 st[2 * NB], dpt[2 * NB];
@@ -269,6 +329,11 @@ __global__ __launch_bounds__(256) void attn_bwd_q_mfma(const bf16_t* __restrict_
         dq[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_operand(sK + 32 * j * RLD, db, g, c16),
                                                           dsf, dq[db], 0, 0, 0);
     }
+    if (more) {
+      stk.store(sKb[bb ^ 1], tid);
+      stv.store(sVb[bb ^ 1], tid);
+    }
+    __syncthreads();
   }
 
   if (qval) {
