@@ -12,7 +12,7 @@
 //       dK^T = Q^T dS once the queries inside each 32-query step are taken in
 //       the same order on the A side (two transposing LDS reads of the
 //       row-major tile);
-//   q:  a workgroup owns 64 queries, 16 per wave, and streams 64-key tiles;
+//   q:  a workgroup owns 64 queries, 16 per wave, and streams 32-key tiles;
 //       S^T and V dO^T (keys x queries) give the B operand of dQ^T = K^T dS^T.
 // P never leaves registers.  dh = 72 runs its third 32-wide k step with lanes
 // past dh 72 holding zeros.
@@ -24,8 +24,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 namespace {
 
-// Tiles of the streamed side are NB x 32 rows (the dK/dV kernel measured
-// fastest with 32, the dQ kernel with 64), stored row-major with stride RLD
+// Tiles of the streamed side are NB x 32 rows (with the next tile prefetched,
+// both kernels measured fastest at NB = 1), stored row-major with stride RLD
 // and 16 elements of padding (transposing reads past dh 72 of the last row).
 constexpr int RLD = 72;           // row-major tile stride (elements)
 template <int NB>
@@ -361,12 +361,12 @@ hipError_t launch_attention_bwd_mfma(const void* qkv, const void* dO, const floa
   if (dh == 64) {
     attn_bwd_kv_mfma<64, 1><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
                                               heads, T, sl2, (bf16_t*)dqkv);
-    attn_bwd_q_mfma<64, 2><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
+    attn_bwd_q_mfma<64, 1><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
                                              heads, T, sl2, (bf16_t*)dqkv);
   } else {
     attn_bwd_kv_mfma<72, 1><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
                                               heads, T, sl2, (bf16_t*)dqkv);
-    attn_bwd_q_mfma<72, 2><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
+    attn_bwd_q_mfma<72, 1><<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)dO, lse, Dv,
                                              heads, T, sl2, (bf16_t*)dqkv);
   }
   return hipGetLastError();
