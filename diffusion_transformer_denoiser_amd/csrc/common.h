@@ -187,6 +187,12 @@ struct ALoad {
   PatchGeom g;          // A_PATCH only
   int seg, skip, off;   // A_PLAIN: row map of the source row (see EpiParams), 0 = identity
 };
+// out[i, j] += sum_r A[r, i] B[r, j] (fp32, atomically): A [R, Mi] and B [R, Nj]
+// bf16, row strides lda, ldb; Mi, Nj multiples of 8, R a multiple of 64,
+// 16-byte aligned.  The weight gradient of a layer from its row-major input
+// and output gradient.
+hipError_t launch_gemm_tn(const bf16_t* A, int lda, const bf16_t* B, int ldb, int Mi, int Nj,
+                          int R, float* out, int ldo, hipStream_t s);
 hipError_t launch_gemm_valu(int epi, int asrc, const ALoad& a, const void* W, int w_dtype,
                             int M, int N, int K, const EpiParams& ep, hipStream_t s);
 hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, int M, int N,

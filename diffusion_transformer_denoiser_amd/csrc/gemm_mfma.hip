@@ -496,6 +496,147 @@ hipError_t pick(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
   return run<EPI, 128, 128, 64, 2>(A, lda, W, M, N, K, ep, s);
 }
 
+// ---------------------------------------------------------------------------
+// Weight-gradient product C[i, j] += sum_r A[r, i] B[r, j] ("TN": both
+// operands stored with the reduction index r as the row, i.e. row-major
+// activations and output gradients of a layer, with no transposed copy).
+// 128 x 192 tiles over 4 waves (2 x 2, each 64 x 96 as 2 x 3 blocks of
+// v_mfma_f32_32x32x16_bf16), r consumed in 64-row slices through two LDS
+// stages filled by direct global->LDS copies.  A stage holds each operand as
+// 64 rows (r) of its tile width (A 128 bf16 = 16 chunks of 16 B, B 192 = 24
+// chunks); chunk c of row r sits at (c + 4 (r % 4)) mod chunks, so the 4
+// consecutive rows that one transposing read touches start in 4 different
+// 64-byte quarters of the banks.  The MFMA operands (8 consecutive r of one
+// column per lane) come from pairs of ds_read_b64_tr_b16.  The grid's second
+// dimension splits r (ksplit rows per layer, a multiple of 64) and every layer
+// adds its partial sums atomically.
+__global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const bf16_t* __restrict__ A, int lda,
+                                                         const bf16_t* __restrict__ B, int ldb,
+                                                         int Mi, int Nj, int R, int ksplit,
+                                                         float* __restrict__ out, int ldo) {
+  constexpr int BM = 128, BN = 192, BK = 64, TM = 2, TN = 3;
+  constexpr int CA = BM / 8, CB = BN / 8;                     // chunks per row
+  constexpr int OPA = BK * BM * 2, OPB = BK * BN * 2;         // bytes per operand tile
+  constexpr int STAGE = OPA + OPB;
+  constexpr int NCA = OPA / 1024 / 4, NCB = OPB / 1024 / 4;   // 1 KB copies per wave (4, 6)
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int tiles_n = (Nj + BN - 1) / BN, tiles_m = (Mi + BM - 1) / BM;
+  int tm, tn;
+  tile_coords<1>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int i0 = tm * BM, j0 = tn * BN;
+  // this layer's slice of the reduction
+  const int rb = blockIdx.y * ksplit;
+  const int Rl = min(ksplit, R - rb);
+  A += (int64_t)rb * lda;
+  B += (int64_t)rb * ldb;
+
+  // Copy slot sl of an operand tile with C chunks per row: LDS row sl / C,
+  // stored chunk p = sl % C, which holds logical chunk (p - 4 (row % 4)) mod C
+  // of global row r0 + row.  Columns past the operand's width read a clamped
+  // (valid) chunk; their outputs are never stored.
+  int aoff[NCA], boff[NCB];
+#pragma unroll
+  for (int c = 0; c < NCA; ++c) {
+    const int sl = (w * NCA + c) * 64 + lane, row = sl / CA;
+    const int lc = (sl % CA - 4 * (row & 3) + 4 * CA) % CA;
+    aoff[c] = row * lda + min(i0 + lc * 8, Mi - 8);
+  }
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) {
+    const int sl = (w * NCB + c) * 64 + lane, row = sl / CB;
+    const int lc = (sl % CB - 4 * (row & 3) + 4 * CB) % CB;
+    boff[c] = row * ldb + min(j0 + lc * 8, Nj - 8);
+  }
+  auto copy = [&](int kt) {
+    char* st = smem + (kt & 1) * STAGE;
+    const int64_t ra = (int64_t)kt * BK * lda, rbb = (int64_t)kt * BK * ldb;
+#pragma unroll
+    for (int c = 0; c < NCA; ++c)
+      __builtin_amdgcn_global_load_lds((const void*)(A + ra + aoff[c]),
+                                       (lds_void*)(st + (w * NCA + c) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int c = 0; c < NCB; ++c)
+      __builtin_amdgcn_global_load_lds((const void*)(B + rbb + boff[c]),
+                                       (lds_void*)(st + OPA + (w * NCB + c) * 1024), 16, 0, 0);
+  };
+
+  // Transposing reads: lane s of 16-lane group G reads row 16 kk + 8 (G / 2) +
+  // s / 4 (+ 4 for the second read), columns col + 16 (G % 2) + 4 (s % 4) ..
+  // + 3, and receives column col + 16 (G % 2) + s of the 4 rows: the MFMA
+  // operand layout (lane l: column l % 32, rows 8 (l / 32) .. + 7).
+  const int G = lane >> 4, sx = lane & 15;
+  auto frag = [&](const char* op, int C, int col, int kk) {
+    const int c = col + 16 * (G & 1) + 4 * (sx & 3);
+    const int r0 = 16 * kk + 8 * (G >> 1) + (sx >> 2), r1 = r0 + 4;
+    const char* p0 = op + r0 * C * 16 + ((((c >> 3) + 4 * (r0 & 3)) % C) << 4) + (c & 7) * 2;
+    const char* p1 = op + r1 * C * 16 + ((((c >> 3) + 4 * (r1 & 3)) % C) << 4) + (c & 7) * 2;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p0);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p1);
+    return __builtin_bit_cast(bf16x8_t, (__attribute__((ext_vector_type(8))) short){
+                                            lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+  };
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = Rl / BK;
+  copy(0);
+  if (nk > 1) {
+    copy(1);
+    wait_vmcnt<NCA + NCB>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  bare_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* st = smem + (kt & 1) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8_t fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[i] = frag(st, CA, wm * 64 + i * 32, kk);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[j] = frag(st + OPA, CB, wn * 96 + j * 32, kk);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    // this stage is read (by this wave; the barrier covers the others) and
+    // slice kt + 1, the only copies in flight, has landed
+    wait_lgkm0();
+    wait_vmcnt<0>();
+    bare_barrier();
+    if (kt + 2 < nk) copy(kt + 2);
+  }
+
+  // lane: column j0 + wn 96 + 32 j + lane % 32, rows i0 + wm 64 + 32 i + 4 (lane / 32) + 8 (r / 4) + r % 4
+  const int ncol = j0 + wn * 96 + (lane & 31);
+  const int mrow = i0 + wm * 64 + 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = mrow + i * 32 + 8 * (r >> 2) + (r & 3);
+      if (m >= Mi) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = ncol + j * 32;
+        if (n < Nj) unsafeAtomicAdd(&out[(int64_t)m * ldo + n], acc[i][j][r]);
+      }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, int M, int N,
@@ -516,4 +657,33 @@ hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, 
     case EPI_DGELU: return pick<EPI_DGELU>(A, lda, W, M, N, K, ep, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_tn(const bf16_t* A, int lda, const bf16_t* B, int ldb, int Mi, int Nj,
+                          int R, float* out, int ldo, hipStream_t s) {
+  if (Mi <= 0 || Nj <= 0 || R <= 0) return hipSuccess;
+  if (Mi % 8 || Nj % 8 || R % 64 || lda % 8 || ldb % 8 || lda < Mi || ldb < Nj ||
+      ((uintptr_t)A & 15) || ((uintptr_t)B & 15))
+    return hipErrorInvalidValue;
+  if ((int64_t)(R - 1) * lda + lda > INT32_MAX || (int64_t)(R - 1) * ldb + ldb > INT32_MAX)
+    return hipErrorInvalidValue;   // 32-bit element offsets inside the kernel
+  const int tiles = ((Mi + 127) / 128) * ((Nj + 191) / 192);
+  // fewest reduction layers whose grid fills whole waves of 512 resident
+  // workgroups (two per CU) to 92% or more
+  int best = 1;
+  double best_fill = 0.0;
+  for (int sp = 1; sp <= R / 64 && sp <= 256; ++sp) {
+    const int64_t wg = (int64_t)tiles * sp, waves = (wg + 511) / 512;
+    const double fill = (double)wg / (double)(waves * 512);
+    if (fill > best_fill + 0.02) {
+      best_fill = fill;
+      best = sp;
+    }
+    if (fill >= 0.92) break;
+  }
+  int ks = (R + best - 1) / best;
+  ks = (ks + 63) / 64 * 64;
+  const dim3 grid(tiles, (R + ks - 1) / ks);
+  gemm_tn_kernel<<<grid, 256, 0, s>>>(A, lda, B, ldb, Mi, Nj, R, ks, out, ldo);
+  return hipGetLastError();
 }

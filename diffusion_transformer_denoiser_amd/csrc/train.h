@@ -51,6 +51,10 @@ hipError_t launch_rowsum(const void* in, int dtype, int rows, int64_t cols, int6
                          hipStream_t s);
 hipError_t launch_colsum(const float* in, int rows, int64_t cols, int64_t ld, float* out,
                          hipStream_t s);
+// out[c] += column sums of a tall bf16 matrix (cols, ld multiples of 8); out
+// must start at zero.
+hipError_t launch_colsum_tall_bf16(const void* in, int64_t rows, int64_t cols, int64_t ld,
+                                  float* out, hipStream_t s);
 hipError_t launch_class_grad(const float* dc, const int32_t* y, int B, int d, int ncls, float* gy,
                              hipStream_t s);
 // dqkv [B T, 3 H dh] from qkv, O, dO (dtype) and the forward's log-sum-exp

@@ -396,6 +396,42 @@ __global__ __launch_bounds__(256) void rowsum_kernel(const IT* __restrict__ in, 
   if (threadIdx.x == 0) out[r] = red[0] + red[1] + red[2] + red[3];
 }
 
+// out[c] += sum over r < rows of in[r * ld + c] for tall matrices: a
+// workgroup covers 256 columns (32 lanes of 8 adjacent columns, 16-byte
+// loads) of 512 rows, its 8 row lanes taking every 8th row; the row lanes
+// combine in LDS and each column's partial sum adds atomically (out must
+// start at zero).
+__global__ __launch_bounds__(256) void colsum_tall_bf16_kernel(const bf16_t* __restrict__ in,
+                                                               int64_t rows, int64_t cols,
+                                                               int64_t ld, float* __restrict__ out) {
+  __shared__ float red[8][257];
+  const int cl = threadIdx.x & 31, rl = threadIdx.x >> 5;
+  const int64_t c8 = (int64_t)blockIdx.x * 32 + cl;
+  const int64_t r0 = (int64_t)blockIdx.y * 512, r1 = min(rows, r0 + 512);
+  float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (c8 * 8 < cols) {
+    for (int64_t r = r0 + rl; r < r1; r += 8) {
+      const uint4 u = *(const uint4*)(in + r * ld + c8 * 8);
+      const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[2 * i] += __uint_as_float(wv[i] << 16);
+        s[2 * i + 1] += __uint_as_float(wv[i] & 0xFFFF0000u);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[rl][cl * 8 + i] = s[i];
+  __syncthreads();
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c < cols) {
+    float t = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t += red[k][threadIdx.x];
+    unsafeAtomicAdd(&out[c], t);
+  }
+}
+
 // out[c] = sum over r < rows of in[r * ld + c]; one thread per column.
 __global__ void colsum_kernel(const float* __restrict__ in, int rows, int64_t cols, int64_t ld,
                               float* __restrict__ out) {
@@ -766,6 +802,16 @@ hipError_t launch_rowsum(const void* in, int dtype, int rows, int64_t cols, int6
     rowsum_kernel<bf16_t, false><<<rows, 256, 0, s>>>((const bf16_t*)in, cols, ld, out);
   else
     rowsum_kernel<float, false><<<rows, 256, 0, s>>>((const float*)in, cols, ld, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum_tall_bf16(const void* in, int64_t rows, int64_t cols, int64_t ld,
+                                  float* out, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (cols % 8 || ld % 8 || ((uintptr_t)in & 15) || (rows + 511) / 512 > 65535)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((cols + 255) / 256), (unsigned)((rows + 511) / 512));
+  colsum_tall_bf16_kernel<<<grid, 256, 0, s>>>((const bf16_t*)in, rows, cols, ld, out);
   return hipGetLastError();
 }
 

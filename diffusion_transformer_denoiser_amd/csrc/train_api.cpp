@@ -22,6 +22,13 @@
 
 using namespace dit_host;
 
+// Propagates a non-zero status of a host helper.
+#define DIT_RC(call)         \
+  do {                       \
+    const int rc_ = (call);  \
+    if (rc_) return rc_;     \
+  } while (0)
+
 namespace {
 
 constexpr int kNumFields = 42;   // pointers in dit_weights
@@ -123,7 +130,7 @@ TrainLayout train_layout(const dit_handle* h, int B) {
   L.acc = take(16);
   L.xt = take(lat * es);
   L.P = take(M * kin * es);
-  L.PT = take(kin * M * es);
+  L.PT = 0;
   L.e = take(Bz * h->freq * 4);
   L.t1pre = take(Bz * d * 4);
   L.th = take(Bz * d * 4);
@@ -143,23 +150,25 @@ TrainLayout train_layout(const dit_handle* h, int B) {
   L.H2 = take(N * M * d * es);
   L.pre = take(N * M * hid * es);
   L.f = take(N * M * d * 4);
-  L.G = take(M * hid * es);
+  L.G = take(N * M * hid * es);   // GELU(pre) of every block (weight gradients of fc2)
   L.Hf = take(M * d * es);
   L.Y = take(M * kout * 4);
   // backward scratch
   L.dY = take(M * kout * es);
-  L.dYT = take(kout * M * es);
+  // transposed operands of the fp32 path (bf16 reads the row-major ones)
+  const bool f32 = h->dtype != DIT_BF16;
+  L.dYT = 0;
   L.dX = take(M * d * 4);
   L.dH = take(M * d * 4);
   L.dBr = take(M * d * es);
-  L.dBrT = take(d * M * es);
-  L.actT = take(hid * M * es > d * M * es ? hid * M * es : d * M * es);
+  L.dBrT = 0;
+  L.actT = take(f32 ? (hid > 3 * d ? hid : 3 * d) * M * es : 0);
   L.dpre = take(M * hid * es);
-  L.dpreT = take(hid * M * es);
+  L.dpreT = take(f32 ? (hid > 3 * d ? hid : 3 * d) * M * es : 0);
   L.dO = take(M * d * es);
   L.Dv = take(Bz * h->heads * T * 4);
   L.dqkv = take(M * 3 * d * es);
-  L.dqkvT = take(3 * d * M * es);
+  L.dqkvT = 0;
   // transposed weights (model dtype)
   L.wqkv = take(N * d * 3 * d * es);
   L.wo = take(N * d * d * es);
@@ -220,6 +229,26 @@ hipError_t wgrad(const void* dCT, const void* AT, int dt, int N, int K, int64_t 
   ep.out = out;
   ep.ldo = K;
   return gemm_any(EPI_ATOMIC_F32, dCT, dt, R, AT, dt, R, N, K, (int)R, ep, s);
+}
+
+// Gradients of a linear layer from its row-major output gradient dC [R, N]
+// (row stride ldc) and input X [R, K] (row stride ldx), both in dtype dt:
+// weight gW [N, K] += dC^T X and, if gb, bias gb [N] += column sums of dC
+// (both fp32, zeroed beforehand).  bf16: the TN kernel reads the operands as
+// they are; fp32: they are transposed into tC [N, R] and tX [K, R] first.
+int layer_grads(int dt, const void* dC, int64_t ldc, const void* X, int64_t ldx, int N, int K,
+                int64_t R, float* gW, float* gb, void* tC, void* tX, hipStream_t s) {
+  if (dt == DIT_BF16) {
+    DIT_HIP(launch_gemm_tn((const bf16_t*)dC, (int)ldc, (const bf16_t*)X, (int)ldx, N, K, (int)R,
+                           gW, K, s));
+    if (gb) DIT_HIP(launch_colsum_tall_bf16(dC, R, N, ldc, gb, s));
+    return DIT_OK;
+  }
+  DIT_HIP(launch_transpose(dC, dt, R, N, ldc, tC, dt, R, 0, s));
+  DIT_HIP(launch_transpose(X, dt, R, K, ldx, tX, dt, R, 0, s));
+  if (gb) DIT_HIP(launch_rowsum(tC, dt, N, R, R, gb, s));
+  DIT_HIP(wgrad(tC, tX, dt, N, K, R, gW, s));
+  return DIT_OK;
 }
 
 }  // namespace
@@ -372,7 +401,7 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
   auto H2 = [&](int l) { return at<char>(ws, L.H2) + (size_t)l * Md * es; };
   auto PRE = [&](int l) { return at<char>(ws, L.pre) + (size_t)l * M * hid * es; };
   auto fb_ = [&](int l) { return at<float>(ws, L.f) + (size_t)l * Md; };
-  void* Gs = at<void>(ws, L.G);
+  auto Gl = [&](int l) { return at<char>(ws, L.G) + (size_t)l * M * hid * es; };
   for (int l = 0; l < N; ++l) {
     const int base = 6 * d * l;
     DIT_HIP(launch_ln_modulate(Xl(l), (int)M, (int)T, d, mod, ms, base, base + d, h->eps, H1(l),
@@ -389,14 +418,14 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
     DIT_HIP(launch_ln_modulate(Xm(l), (int)M, (int)T, d, mod, ms, base + 3 * d, base + 4 * d,
                                h->eps, H2(l), dt, s));
     ep = epi0();
-    ep.bias = (const float*)W_(F_FC1_B) + (size_t)l * hid; ep.out = Gs; ep.aux = PRE(l);
+    ep.bias = (const float*)W_(F_FC1_B) + (size_t)l * hid; ep.out = Gl(l); ep.aux = PRE(l);
     ep.ldo = hid;
     DIT_HIP(linear(h, EPI_GELU2, H2(l), d, wl(F_FC1_W, l, (size_t)hid * d), (int)M, hid, d, ep,
                    s));
     ep = epi0();
     ep.bias = (const float*)W_(F_FC2_B) + (size_t)l * d; ep.out = fb_(l); ep.ldo = d;
-    DIT_HIP(linear(h, EPI_BIAS_F32, Gs, hid, wl(F_FC2_W, l, (size_t)d * hid), (int)M, d, hid, ep,
-                   s));
+    DIT_HIP(linear(h, EPI_BIAS_F32, Gl(l), hid, wl(F_FC2_W, l, (size_t)d * hid), (int)M, d, hid,
+                   ep, s));
     DIT_HIP(launch_gate_residual(Xm(l), fb_(l), mod, ms, base + 5 * d, (int)T, d, M, Xl(l + 1), s));
   }
   const int fbo = 6 * d * N;
@@ -416,13 +445,10 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
   // ---- final layer backward --------------------------------------------------------------
   float* dX = at<float>(ws, L.dX);
   float* dH = at<float>(ws, L.dH);
-  void* actT = at<void>(ws, L.actT);
+  void* tC = at<void>(ws, L.dpreT);   // fp32 path only: transposed operands
+  void* tX = at<void>(ws, L.actT);
   {
-    void* dYT = at<void>(ws, L.dYT);
-    DIT_HIP(launch_transpose(dY, dt, M, kout, kout, dYT, dt, M, 0, s));
-    DIT_HIP(launch_rowsum(dYT, dt, kout, M, M, G_(F_OUT_B), s));
-    DIT_HIP(launch_transpose(Hf, dt, M, d, d, actT, dt, M, 0, s));
-    DIT_HIP(wgrad(dYT, actT, dt, kout, d, M, G_(F_OUT_W), s));
+    DIT_RC(layer_grads(dt, dY, kout, Hf, d, kout, d, M, G_(F_OUT_W), G_(F_OUT_B), tC, tX, s));
     EpiParams ep = epi0();
     ep.out = dH; ep.ldo = d;
     DIT_HIP(gemm_any(EPI_BIAS_F32, dY, dt, kout, at<void>(ws, L.wout), dt, kout, (int)M, d, kout,
@@ -433,50 +459,40 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
 
   // ---- blocks, last to first -------------------------------------------------------------
   void* dBr = at<void>(ws, L.dBr);
-  void* dBrT = at<void>(ws, L.dBrT);
   void* dpre = at<void>(ws, L.dpre);
-  void* dpreT = at<void>(ws, L.dpreT);
   void* dO = at<void>(ws, L.dO);
   void* dqkv = at<void>(ws, L.dqkv);
-  void* dqkvT = at<void>(ws, L.dqkvT);
   for (int l = N - 1; l >= 0; --l) {
     const int base = 6 * d * l;
-    // FFN branch: X_{l+1} = X_mid + a2 f
+    // FFN branch: X_{l+1} = X_mid + a2 f, f = GELU(pre) W2^T + b2
     DIT_HIP(launch_gate_bwd(dX, fb_(l), mod, ms, base + 5 * d, B, (int)T, d, dt, dBr, dmod, s));
-    DIT_HIP(launch_transpose(dBr, dt, M, d, d, dBrT, dt, M, 0, s));
-    DIT_HIP(launch_rowsum(dBrT, dt, d, M, M, G_(F_FC2_B) + (size_t)l * d, s));
-    DIT_HIP(launch_transpose(PRE(l), dt, M, hid, hid, actT, dt, M, 1, s));   // GELU(pre)^T
-    DIT_HIP(wgrad(dBrT, actT, dt, d, hid, M, G_(F_FC2_W) + (size_t)l * d * hid, s));
+    DIT_RC(layer_grads(dt, dBr, d, Gl(l), hid, d, hid, M, G_(F_FC2_W) + (size_t)l * d * hid,
+                        G_(F_FC2_B) + (size_t)l * d, tC, tX, s));
     EpiParams ep = epi0();
     ep.out = dpre; ep.aux = PRE(l); ep.ldo = hid;   // d pre = (df W2) GELU'(pre)
     DIT_HIP(gemm_any(EPI_DGELU, dBr, dt, d, at<char>(ws, L.wfc2) + (size_t)l * hid * d * es, dt,
                      d, (int)M, hid, d, ep, s));
-    DIT_HIP(launch_transpose(dpre, dt, M, hid, hid, dpreT, dt, M, 0, s));
-    DIT_HIP(launch_rowsum(dpreT, dt, hid, M, M, G_(F_FC1_B) + (size_t)l * hid, s));
-    DIT_HIP(launch_transpose(H2(l), dt, M, d, d, actT, dt, M, 0, s));
-    DIT_HIP(wgrad(dpreT, actT, dt, hid, d, M, G_(F_FC1_W) + (size_t)l * hid * d, s));
+    DIT_RC(layer_grads(dt, dpre, hid, H2(l), d, hid, d, M, G_(F_FC1_W) + (size_t)l * hid * d,
+                        G_(F_FC1_B) + (size_t)l * hid, tC, tX, s));
     ep = epi0();
     ep.out = dH; ep.ldo = d;
     DIT_HIP(gemm_any(EPI_BIAS_F32, dpre, dt, hid, at<char>(ws, L.wfc1) + (size_t)l * d * hid * es,
                      dt, hid, (int)M, d, hid, ep, s));
     DIT_HIP(launch_ln_mod_bwd(Xm(l), dH, mod, ms, base + 3 * d, base + 4 * d, B, (int)T, d, h->eps,
                               dX, dmod, s));
-    // attention branch: X_mid = X_l + a1 o
+    // attention branch: X_mid = X_l + a1 o, o = O Wo^T + bo
     DIT_HIP(launch_gate_bwd(dX, ob(l), mod, ms, base + 2 * d, B, (int)T, d, dt, dBr, dmod, s));
-    DIT_HIP(launch_transpose(dBr, dt, M, d, d, dBrT, dt, M, 0, s));
-    DIT_HIP(launch_rowsum(dBrT, dt, d, M, M, G_(F_O_B) + (size_t)l * d, s));
-    DIT_HIP(launch_transpose(Ob(l), dt, M, d, d, actT, dt, M, 0, s));
-    DIT_HIP(wgrad(dBrT, actT, dt, d, d, M, G_(F_O_W) + (size_t)l * d * d, s));
+    DIT_RC(layer_grads(dt, dBr, d, Ob(l), d, d, d, M, G_(F_O_W) + (size_t)l * d * d,
+                        G_(F_O_B) + (size_t)l * d, tC, tX, s));
     ep = epi0();
     ep.out = dO; ep.ldo = d;
     DIT_HIP(gemm_any(EPI_BIAS_DT, dBr, dt, d, at<char>(ws, L.wo) + (size_t)l * d * d * es, dt, d,
                      (int)M, d, d, ep, s));
     DIT_HIP(launch_attention_bwd(QKV(l), Ob(l), dO, LSE(l), at<float>(ws, L.Dv), B, heads, (int)T,
                                  h->dh, dt, dqkv, s));
-    DIT_HIP(launch_transpose(dqkv, dt, M, 3 * d, 3 * d, dqkvT, dt, M, 0, s));
-    DIT_HIP(launch_rowsum(dqkvT, dt, 3 * d, M, M, G_(F_QKV_B) + (size_t)l * 3 * d, s));
-    DIT_HIP(launch_transpose(H1(l), dt, M, d, d, actT, dt, M, 0, s));
-    DIT_HIP(wgrad(dqkvT, actT, dt, 3 * d, d, M, G_(F_QKV_W) + (size_t)l * 3 * d * d, s));
+    DIT_RC(layer_grads(dt, dqkv, 3 * d, H1(l), d, 3 * d, d, M,
+                        G_(F_QKV_W) + (size_t)l * 3 * d * d, G_(F_QKV_B) + (size_t)l * 3 * d, tC,
+                        tX, s));
     ep = epi0();
     ep.out = dH; ep.ldo = d;
     DIT_HIP(gemm_any(EPI_BIAS_F32, dqkv, dt, 3 * d, at<char>(ws, L.wqkv) + (size_t)l * d * 3 * d * es,
@@ -485,13 +501,12 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
                               s));
   }
 
-  // ---- patch embedding ---------------------------------------------------------------
+  // ---- patch embedding: X_0 = patches W_pe^T + b_pe (+ fixed PE) ---------------------
   {
-    DIT_HIP(launch_transpose(dX, 0, M, d, d, dBrT, dt, M, 0, s));
-    DIT_HIP(launch_rowsum(dBrT, dt, d, M, M, G_(F_PE_B), s));
+    DIT_HIP(launch_cast_f32(dX, dBr, (int64_t)Md, dt, s));
     DIT_HIP(launch_patchify(at<void>(ws, L.xt), B, h->gin, dt, at<void>(ws, L.P), s));
-    DIT_HIP(launch_transpose(at<void>(ws, L.P), dt, M, kin, kin, at<void>(ws, L.PT), dt, M, 0, s));
-    DIT_HIP(wgrad(dBrT, at<void>(ws, L.PT), dt, d, kin, M, G_(F_PE_W), s));
+    DIT_RC(layer_grads(dt, dBr, d, at<void>(ws, L.P), kin, d, kin, M, G_(F_PE_W), G_(F_PE_B), tC,
+                        tX, s));
   }
 
   // ---- conditioning backward ---------------------------------------------------------
