@@ -599,18 +599,27 @@ __global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const bf16_t* __restric
   bare_barrier();
   for (int kt = 0; kt < nk; ++kt) {
     const char* st = smem + (kt & 1) * STAGE;
+    // fragments of k step kk + 1 are read while the MFMAs of step kk run
+    bf16x8_t fa[2][TM], fb[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[0][i] = frag(st, CA, wm * 64 + i * 32, 0);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[0][j] = frag(st + OPA, CB, wn * 96 + j * 32, 0);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t fa[TM], fb[TN];
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk + 1 < BK / 16) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = frag(st, CA, wm * 64 + i * 32, kk);
+        for (int i = 0; i < TM; ++i) fa[nxt][i] = frag(st, CA, wm * 64 + i * 32, kk + 1);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = frag(st + OPA, CB, wn * 96 + j * 32, kk);
+        for (int j = 0; j < TN; ++j) fb[nxt][j] = frag(st + OPA, CB, wn * 96 + j * 32, kk + 1);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0,
+                                                              0, 0);
     }
     // this stage is read (by this wave; the barrier covers the others) and
     // slice kt + 1, the only copies in flight, has landed
