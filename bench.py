@@ -151,24 +151,27 @@ def train_main(args, cfg, model, dev):
     # forward MACs x 3 (the backward computes two products per forward product)
     flop_step = 3 * 2.0 * oflops.gmac_for(cfg) * 1e9 * B
 
-    # Dominant kernel class of the step: the weight-gradient products (split-K
-    # MFMA GEMM accumulating atomically into fp32).  Timed alone at the FFN
-    # down-projection's shape, dW2 [d, 4d] = dF^T G over all B T tokens, on the
-    # same kernel through dit_linear's accumulating epilogue.
+    # Dominant kernel of the step: the weight-gradient product (TN MFMA GEMM
+    # over the row-major saved activations, split along the token reduction,
+    # accumulating atomically into fp32).  Timed alone at the FFN
+    # down-projection's shape, dW2 [d, 4d] += dF^T G over all B T tokens with
+    # dF [B T, d] and G [B T, 4d], through dit_linear_wgrad, on the stream it
+    # is launched on.
     import diffusion_transformer_denoiser_amd as dm
     d, hid = cfg["d"], cfg["mlp_hidden"]
     R = B * dit_inputs.tokens(cfg)
-    A = torch.randn(d, R, device=dev).to(torch.bfloat16)
-    W = torch.randn(hid, R, device=dev).to(torch.bfloat16)
+    dF = torch.randn(R, d, device=dev).to(torch.bfloat16)
+    G = torch.randn(R, hid, device=dev).to(torch.bfloat16)
     acc = torch.zeros(d, hid, device=dev)
     for _ in range(10):
-        dm.linear(dm.DIT_EPI_ACCUM, A, W, None, acc)
+        dm.linear_wgrad(dF, G, acc)
+    stream = torch.cuda.current_stream(dev)
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    k0.record()
+    k0.record(stream)
     nk = max(10, args.kernel_launches // 4)
     for _ in range(nk):
-        dm.linear(dm.DIT_EPI_ACCUM, A, W, None, acc)
-    k1.record()
+        dm.linear_wgrad(dF, G, acc)
+    k1.record(stream)
     torch.cuda.synchronize()
     kms = k0.elapsed_time(k1) / nk
     kflop = 2.0 * d * hid * R
@@ -176,8 +179,8 @@ def train_main(args, cfg, model, dev):
     roofline = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
                 "algorithmic_bytes": (d + hid) * R * 2 + d * hid * 4 * 2,
-                "kernel": f"gemm_bf16_kernel<EPI_ATOMIC_F32,128,192,64> split-K (FFN down-projection "
-                          f"weight gradient: M={d}, N={hid}, K={R})",
+                "kernel": f"gemm_tn_kernel (FFN down-projection weight gradient: dW [{d}, {hid}] "
+                          f"over R={R} rows)",
                 "avg_launch_ms": round(kms, 4)}
     cpu = None
     if not args.skip_cpu_baseline:

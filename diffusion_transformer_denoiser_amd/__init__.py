@@ -8,5 +8,5 @@ been built.
 """
 from ._lib import (DIT_BF16, DIT_EPI_ACCUM, DIT_EPI_BIAS, DIT_EPI_GATED, DIT_EPI_GELU, DIT_F32,  # noqa: F401
                    DitError, load)
-from .model import (DiT, Sampler, attention, config_struct, linear, patchify,  # noqa: F401
+from .model import (DiT, Sampler, attention, config_struct, linear, linear_wgrad, patchify,  # noqa: F401
                     timestep_embed, torch_dtype, unpatchify, upload)

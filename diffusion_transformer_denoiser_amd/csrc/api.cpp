@@ -137,6 +137,26 @@ int splitk_slice(bool mfma, int64_t M, int64_t N, int64_t K) {
   return ks >= K ? 0 : (int)ks;
 }
 
+hipError_t linear_wgrad(const void* dY, int64_t ldy, const void* X, int64_t ldx, int N, int K,
+                        int64_t R, int dtype, float* dW, int lddw, hipStream_t s) {
+  if (N <= 0 || K <= 0 || R <= 0) return hipSuccess;
+  if (dtype == DIT_BF16 && N % 8 == 0 && K % 8 == 0 && R % 64 == 0 && ldy % 8 == 0 &&
+      ldx % 8 == 0 && ((uintptr_t)dY & 15) == 0 && ((uintptr_t)X & 15) == 0 &&
+      R * (ldy > ldx ? ldy : ldx) <= INT32_MAX)
+    return launch_gemm_tn((const bf16_t*)dY, (int)ldy, (const bf16_t*)X, (int)ldx, N, K, (int)R,
+                          dW, lddw, s);
+  if (R > INT32_MAX || ldy > INT32_MAX || ldx > INT32_MAX) return hipErrorInvalidValue;
+  ALoad a;
+  memset(&a, 0, sizeof a);
+  a.ptr = dY; a.lda = (int)ldy; a.a_dtype = dtype == DIT_BF16 ? 1 : 0; a.src_rows = N; a.trans = 1;
+  EpiParams ep;
+  memset(&ep, 0, sizeof ep);
+  ep.out = dW; ep.ldo = lddw; ep.ldw = (int)ldx; ep.w_trans = 1;
+  ep.ksplit = splitk_slice(false, N, K, R);
+  return launch_gemm_valu(EPI_ATOMIC_F32, A_PLAIN, a, X, dtype == DIT_BF16 ? 1 : 0, N, K, (int)R,
+                          ep, s);
+}
+
 EpiParams epi0() {
   EpiParams ep;
   memset(&ep, 0, sizeof ep);
@@ -1171,6 +1191,18 @@ int dit_linear(int epilogue, const void* A, const void* W, const float* bias, in
     a.ptr = A; a.lda = K; a.a_dtype = 0; a.src_rows = M;
     DIT_HIP(launch_gemm_valu(epi, A_PLAIN, a, W, 0, M, N, K, ep, s));
   }
+  return ok();
+}
+
+int dit_linear_wgrad(const void* dY, int64_t ldy, const void* X, int64_t ldx, int N, int K,
+                     int64_t R, int dtype, float* dW, void* stream) {
+  if (!dY || !X || !dW) return fail(DIT_EINVAL, "dY, X and dW must be non-NULL");
+  if (N <= 0 || K <= 0 || R < 0) return fail(DIT_EINVAL, "N, K must be positive and R >= 0");
+  if (ldy < N || ldx < K) return fail(DIT_EINVAL, "row strides ldy >= N and ldx >= K");
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return fail(DIT_EINVAL, "dtype");
+  if (R > INT32_MAX || ldy > INT32_MAX || ldx > INT32_MAX)
+    return fail(DIT_EUNSUPPORTED, "R and the row strides must be below 2^31");
+  DIT_HIP(linear_wgrad(dY, ldy, X, ldx, N, K, R, dtype, dW, K, (hipStream_t)stream));
   return ok();
 }
 

@@ -129,6 +129,8 @@ struct EpiParams {
   // EPI_GELU2: the pre-activation output; EPI_DGELU: the pre-activation input
   // (model dtype, row stride ldo)
   void* aux;
+  // VALU kernel only: W element (n, k) at W[k * ldw + n] (stored transposed)
+  int w_trans;
 };
 
 // (m < 2^31 and seg > 0: 32-bit unsigned division)
@@ -186,6 +188,7 @@ struct ALoad {
   int src_rows;         // A_PLAIN: row r reads row r % src_rows; A_PATCH: latent rows
   PatchGeom g;          // A_PATCH only
   int seg, skip, off;   // A_PLAIN: row map of the source row (see EpiParams), 0 = identity
+  int trans;            // A_PLAIN: element (m, k) at ptr[k * lda + m] (the operand stored transposed)
 };
 // out[i, j] += sum_r A[r, i] B[r, j] (fp32, atomically): A [R, Mi] and B [R, Nj]
 // bf16, row strides lda, ldb; Mi, Nj multiples of 8, R a multiple of 64,

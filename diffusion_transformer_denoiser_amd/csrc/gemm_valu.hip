@@ -20,6 +20,7 @@ __device__ __forceinline__ float load_a(const ALoad& a, int m, int k) {
                                        patch_src_offset(a.g, tau, k)]);
   } else {
     const int64_t row = row_map(m % a.src_rows, a.seg, a.skip, a.off);
+    if (a.trans) return to_f<AT>(((const AT*)a.ptr)[(int64_t)k * a.lda + row]);
     return to_f<AT>(((const AT*)a.ptr)[row * a.lda + k]);
   }
 }
@@ -49,7 +50,9 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(ALoad a, const WT* __res
     for (int u = 0; u < 4; ++u) {
       int k = k0 + lk + u;
       As[lk + u][lr] = (m < M && k < kend) ? load_a<ASRC, AT>(a, m, k) : 0.0f;
-      Bs[lk + u][lr] = (n < N && k < kend) ? to_f<WT>(W[(int64_t)n * ldw + k]) : 0.0f;
+      Bs[lk + u][lr] = (n < N && k < kend)
+                           ? to_f<WT>(ep.w_trans ? W[(int64_t)k * ldw + n] : W[(int64_t)n * ldw + k])
+                           : 0.0f;
     }
     __syncthreads();
 #pragma unroll

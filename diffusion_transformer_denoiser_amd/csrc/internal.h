@@ -50,6 +50,12 @@ EpiParams epi0();
 // (0: no split): about 1024 workgroups, slices a multiple of the kernel's k
 // step (64 on the matrix cores, 16 on the VALU path).
 int splitk_slice(bool mfma, int64_t M, int64_t N, int64_t K);
+// Weight gradient dW [N, K] += dY^T X (fp32, atomically) from the row-major
+// output gradient dY [R, N] (row stride ldy) and input X [R, K] (row stride
+// ldx), both in dtype: the TN matrix-core kernel for bf16 when the shapes fit
+// it, else the VALU kernel reading both operands transposed.
+hipError_t linear_wgrad(const void* dY, int64_t ldy, const void* X, int64_t ldx, int N, int K,
+                        int64_t R, int dtype, float* dW, int lddw, hipStream_t s);
 // One linear layer C = A W^T with the epilogue: MFMA for bf16 models, VALU
 // for fp32 ones.
 hipError_t linear(const dit_handle* h, int epi, const void* A, int lda, const void* W, int M,

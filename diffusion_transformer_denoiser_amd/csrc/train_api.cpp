@@ -2,14 +2,13 @@
 // launch sequence of one optimizer step (forward with saved activations, loss,
 // backward, AdamW).  No device memory is allocated here.
 //
-// Products of the backward pass reuse the forward GEMM kernels, which compute
-// C = A W^T with both operands K-contiguous:
-//   input gradient  dA[M, K] = dC[M, N] W[N, K]  ->  A = dC, W-operand = W^T [K, N];
-//   weight gradient dW[N, K] = dC^T A            ->  A = dC^T [N, M], W-operand = A^T [K, M],
-// so the weights are transposed once per step and the activations that enter
-// weight gradients are transposed as they are needed.  Weight gradients reduce
-// over all B T tokens; their grids are split along that reduction and the
-// slices add their partial sums atomically into the zeroed gradient buffer.
+// Input gradients reuse the forward GEMM kernels, which compute C = A W^T with
+// both operands K-contiguous: dA[M, K] = dC[M, N] W[N, K] takes A = dC and the
+// W-operand W^T [K, N], so the weights are transposed once per step.  Weight
+// gradients dW[N, K] += dC^T A read dC and A row-major as saved (a transposing
+// matrix-core kernel for bf16, transposed addressing for fp32); they reduce
+// over all B T tokens, split along that reduction, and the slices add their
+// partial sums atomically into the zeroed gradient buffer.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -106,11 +105,11 @@ int check_train(const dit_handle* h) {
 }
 
 struct TrainLayout {
-  size_t coef, tf, acc, xt, P, PT, e, t1pre, th, c, sc, mod, dmod, pe;
+  size_t coef, tf, acc, xt, P, e, t1pre, th, c, sc, mod, dmod, pe;
   size_t Xs, Xmid, H1, qkv, O, lse, o, H2, pre, f, G, Hf, Y;
-  size_t dY, dYT, dX, dH, dBr, dBrT, actT, dpre, dpreT, dO, Dv, dqkv, dqkvT;
+  size_t dY, dX, dH, dBr, dpre, dO, Dv, dqkv;
   size_t wqkv, wo, wfc1, wfc2, wout, wada, wt2;
-  size_t dmod_dt, dmodT, scT, dsc, dc, dcT, thT, dth, dt1, dt1T, eT;
+  size_t dmod_dt, dsc, dc, dth, dt1;
   size_t total;
 };
 
@@ -130,7 +129,6 @@ TrainLayout train_layout(const dit_handle* h, int B) {
   L.acc = take(16);
   L.xt = take(lat * es);
   L.P = take(M * kin * es);
-  L.PT = 0;
   L.e = take(Bz * h->freq * 4);
   L.t1pre = take(Bz * d * 4);
   L.th = take(Bz * d * 4);
@@ -155,20 +153,13 @@ TrainLayout train_layout(const dit_handle* h, int B) {
   L.Y = take(M * kout * 4);
   // backward scratch
   L.dY = take(M * kout * es);
-  // transposed operands of the fp32 path (bf16 reads the row-major ones)
-  const bool f32 = h->dtype != DIT_BF16;
-  L.dYT = 0;
   L.dX = take(M * d * 4);
   L.dH = take(M * d * 4);
   L.dBr = take(M * d * es);
-  L.dBrT = 0;
-  L.actT = take(f32 ? (hid > 3 * d ? hid : 3 * d) * M * es : 0);
   L.dpre = take(M * hid * es);
-  L.dpreT = take(f32 ? (hid > 3 * d ? hid : 3 * d) * M * es : 0);
   L.dO = take(M * d * es);
   L.Dv = take(Bz * h->heads * T * 4);
   L.dqkv = take(M * 3 * d * es);
-  L.dqkvT = 0;
   // transposed weights (model dtype)
   L.wqkv = take(N * d * 3 * d * es);
   L.wo = take(N * d * d * es);
@@ -179,16 +170,10 @@ TrainLayout train_layout(const dit_handle* h, int B) {
   L.wt2 = take(d * d * 4);
   // conditioning backward
   L.dmod_dt = take(Bz * ms * es);
-  L.dmodT = take(ms * Bz * es);
-  L.scT = take(d * Bz * es);
   L.dsc = take(Bz * d * 4);
   L.dc = take(Bz * d * 4);
-  L.dcT = take(d * Bz * 4);
-  L.thT = take(d * Bz * 4);
   L.dth = take(Bz * d * 4);
   L.dt1 = take(Bz * d * 4);
-  L.dt1T = take(d * Bz * 4);
-  L.eT = take((size_t)h->freq * Bz * 4);
   L.total = off;
   return L;
 }
@@ -221,33 +206,17 @@ hipError_t gemm_any(int epi, const void* A, int adt, int64_t lda, const void* W,
   return launch_gemm_valu(epi, A_PLAIN, a, W, wdt, M, N, K, ep, s);
 }
 
-// Weight gradient dW[N, K] += dC^T A from the transposed operands dCT [N, R]
-// and AT [K, R] (R = reduction rows, both dtype dt), into fp32 out (row stride K).
-hipError_t wgrad(const void* dCT, const void* AT, int dt, int N, int K, int64_t R, float* out,
-                 hipStream_t s) {
-  EpiParams ep = epi0();
-  ep.out = out;
-  ep.ldo = K;
-  return gemm_any(EPI_ATOMIC_F32, dCT, dt, R, AT, dt, R, N, K, (int)R, ep, s);
-}
-
 // Gradients of a linear layer from its row-major output gradient dC [R, N]
 // (row stride ldc) and input X [R, K] (row stride ldx), both in dtype dt:
 // weight gW [N, K] += dC^T X and, if gb, bias gb [N] += column sums of dC
-// (both fp32, zeroed beforehand).  bf16: the TN kernel reads the operands as
-// they are; fp32: they are transposed into tC [N, R] and tX [K, R] first.
+// (both fp32, zeroed beforehand).
 int layer_grads(int dt, const void* dC, int64_t ldc, const void* X, int64_t ldx, int N, int K,
-                int64_t R, float* gW, float* gb, void* tC, void* tX, hipStream_t s) {
-  if (dt == DIT_BF16) {
-    DIT_HIP(launch_gemm_tn((const bf16_t*)dC, (int)ldc, (const bf16_t*)X, (int)ldx, N, K, (int)R,
-                           gW, K, s));
-    if (gb) DIT_HIP(launch_colsum_tall_bf16(dC, R, N, ldc, gb, s));
-    return DIT_OK;
+                int64_t R, float* gW, float* gb, hipStream_t s) {
+  DIT_HIP(linear_wgrad(dC, ldc, X, ldx, N, K, R, dt, gW, K, s));
+  if (gb) {
+    if (dt == DIT_BF16) DIT_HIP(launch_colsum_tall_bf16(dC, R, N, ldc, gb, s));
+    else DIT_HIP(launch_colsum((const float*)dC, (int)R, N, ldc, gb, s));
   }
-  DIT_HIP(launch_transpose(dC, dt, R, N, ldc, tC, dt, R, 0, s));
-  DIT_HIP(launch_transpose(X, dt, R, K, ldx, tX, dt, R, 0, s));
-  if (gb) DIT_HIP(launch_rowsum(tC, dt, N, R, R, gb, s));
-  DIT_HIP(wgrad(tC, tX, dt, N, K, R, gW, s));
   return DIT_OK;
 }
 
@@ -445,10 +414,8 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
   // ---- final layer backward --------------------------------------------------------------
   float* dX = at<float>(ws, L.dX);
   float* dH = at<float>(ws, L.dH);
-  void* tC = at<void>(ws, L.dpreT);   // fp32 path only: transposed operands
-  void* tX = at<void>(ws, L.actT);
   {
-    DIT_RC(layer_grads(dt, dY, kout, Hf, d, kout, d, M, G_(F_OUT_W), G_(F_OUT_B), tC, tX, s));
+    DIT_RC(layer_grads(dt, dY, kout, Hf, d, kout, d, M, G_(F_OUT_W), G_(F_OUT_B), s));
     EpiParams ep = epi0();
     ep.out = dH; ep.ldo = d;
     DIT_HIP(gemm_any(EPI_BIAS_F32, dY, dt, kout, at<void>(ws, L.wout), dt, kout, (int)M, d, kout,
@@ -467,13 +434,13 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
     // FFN branch: X_{l+1} = X_mid + a2 f, f = GELU(pre) W2^T + b2
     DIT_HIP(launch_gate_bwd(dX, fb_(l), mod, ms, base + 5 * d, B, (int)T, d, dt, dBr, dmod, s));
     DIT_RC(layer_grads(dt, dBr, d, Gl(l), hid, d, hid, M, G_(F_FC2_W) + (size_t)l * d * hid,
-                        G_(F_FC2_B) + (size_t)l * d, tC, tX, s));
+                        G_(F_FC2_B) + (size_t)l * d, s));
     EpiParams ep = epi0();
     ep.out = dpre; ep.aux = PRE(l); ep.ldo = hid;   // d pre = (df W2) GELU'(pre)
     DIT_HIP(gemm_any(EPI_DGELU, dBr, dt, d, at<char>(ws, L.wfc2) + (size_t)l * hid * d * es, dt,
                      d, (int)M, hid, d, ep, s));
     DIT_RC(layer_grads(dt, dpre, hid, H2(l), d, hid, d, M, G_(F_FC1_W) + (size_t)l * hid * d,
-                        G_(F_FC1_B) + (size_t)l * hid, tC, tX, s));
+                        G_(F_FC1_B) + (size_t)l * hid, s));
     ep = epi0();
     ep.out = dH; ep.ldo = d;
     DIT_HIP(gemm_any(EPI_BIAS_F32, dpre, dt, hid, at<char>(ws, L.wfc1) + (size_t)l * d * hid * es,
@@ -483,7 +450,7 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
     // attention branch: X_mid = X_l + a1 o, o = O Wo^T + bo
     DIT_HIP(launch_gate_bwd(dX, ob(l), mod, ms, base + 2 * d, B, (int)T, d, dt, dBr, dmod, s));
     DIT_RC(layer_grads(dt, dBr, d, Ob(l), d, d, d, M, G_(F_O_W) + (size_t)l * d * d,
-                        G_(F_O_B) + (size_t)l * d, tC, tX, s));
+                        G_(F_O_B) + (size_t)l * d, s));
     ep = epi0();
     ep.out = dO; ep.ldo = d;
     DIT_HIP(gemm_any(EPI_BIAS_DT, dBr, dt, d, at<char>(ws, L.wo) + (size_t)l * d * d * es, dt, d,
@@ -491,8 +458,7 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
     DIT_HIP(launch_attention_bwd(QKV(l), Ob(l), dO, LSE(l), at<float>(ws, L.Dv), B, heads, (int)T,
                                  h->dh, dt, dqkv, s));
     DIT_RC(layer_grads(dt, dqkv, 3 * d, H1(l), d, 3 * d, d, M,
-                        G_(F_QKV_W) + (size_t)l * 3 * d * d, G_(F_QKV_B) + (size_t)l * 3 * d, tC,
-                        tX, s));
+                        G_(F_QKV_W) + (size_t)l * 3 * d * d, G_(F_QKV_B) + (size_t)l * 3 * d, s));
     ep = epi0();
     ep.out = dH; ep.ldo = d;
     DIT_HIP(gemm_any(EPI_BIAS_F32, dqkv, dt, 3 * d, at<char>(ws, L.wqkv) + (size_t)l * d * 3 * d * es,
@@ -505,18 +471,15 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
   {
     DIT_HIP(launch_cast_f32(dX, dBr, (int64_t)Md, dt, s));
     DIT_HIP(launch_patchify(at<void>(ws, L.xt), B, h->gin, dt, at<void>(ws, L.P), s));
-    DIT_RC(layer_grads(dt, dBr, d, at<void>(ws, L.P), kin, d, kin, M, G_(F_PE_W), G_(F_PE_B), tC,
-                        tX, s));
+    DIT_RC(layer_grads(dt, dBr, d, at<void>(ws, L.P), kin, d, kin, M, G_(F_PE_W), G_(F_PE_B), s));
   }
 
   // ---- conditioning backward ---------------------------------------------------------
   {
     // mod = SiLU(c) ada_w^T + ada_b
-    DIT_HIP(launch_colsum(dmod, B, ms, ms, G_(F_ADA_B), s));
-    DIT_HIP(launch_transpose(dmod, 0, B, ms, ms, at<void>(ws, L.dmodT), dt, B, 0, s));
-    DIT_HIP(launch_transpose(sc, dt, B, d, d, at<void>(ws, L.scT), dt, B, 0, s));
-    DIT_HIP(wgrad(at<void>(ws, L.dmodT), at<void>(ws, L.scT), dt, ms, d, B, G_(F_ADA_W), s));
     DIT_HIP(launch_cast_f32(dmod, at<void>(ws, L.dmod_dt), (int64_t)B * ms, dt, s));
+    DIT_RC(layer_grads(dt, at<void>(ws, L.dmod_dt), ms, sc, d, ms, d, B, G_(F_ADA_W), nullptr, s));
+    DIT_HIP(launch_colsum(dmod, B, ms, ms, G_(F_ADA_B), s));
     float* dsc = at<float>(ws, L.dsc);
     DIT_HIP(launch_fill_f32(dsc, (int64_t)B * d, 0.0f, s));
     EpiParams ep = epi0();
@@ -527,10 +490,7 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
     float* dc = at<float>(ws, L.dc);
     DIT_HIP(launch_silu_bwd(dsc, c, dc, (int64_t)B * d, s));
     DIT_HIP(launch_class_grad(dc, y, B, d, h->ncls, G_(F_Y), s));
-    DIT_HIP(launch_colsum(dc, B, d, d, G_(F_T2_B), s));
-    DIT_HIP(launch_transpose(dc, 0, B, d, d, at<void>(ws, L.dcT), 0, B, 0, s));
-    DIT_HIP(launch_transpose(th, 0, B, d, d, at<void>(ws, L.thT), 0, B, 0, s));
-    DIT_HIP(wgrad(at<void>(ws, L.dcT), at<void>(ws, L.thT), 0, d, d, B, G_(F_T2_W), s));
+    DIT_RC(layer_grads(0, dc, d, th, d, d, d, B, G_(F_T2_W), G_(F_T2_B), s));
     float* dth = at<float>(ws, L.dth);
     ep = epi0();
     ep.out = dth; ep.ldo = d;
@@ -538,10 +498,7 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
     // th = SiLU(e t1_w^T + t1_b)
     float* dt1 = at<float>(ws, L.dt1);
     DIT_HIP(launch_silu_bwd(dth, t1pre, dt1, (int64_t)B * d, s));
-    DIT_HIP(launch_colsum(dt1, B, d, d, G_(F_T1_B), s));
-    DIT_HIP(launch_transpose(dt1, 0, B, d, d, at<void>(ws, L.dt1T), 0, B, 0, s));
-    DIT_HIP(launch_transpose(e, 0, B, h->freq, h->freq, at<void>(ws, L.eT), 0, B, 0, s));
-    DIT_HIP(wgrad(at<void>(ws, L.dt1T), at<void>(ws, L.eT), 0, d, h->freq, B, G_(F_T1_W), s));
+    DIT_RC(layer_grads(0, dt1, d, e, h->freq, d, h->freq, B, G_(F_T1_W), G_(F_T1_B), s));
   }
 
   // ---- AdamW, EMA, model-dtype weights ---------------------------------------------

@@ -25,7 +25,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("dit_create", "dit_destroy", "dit_workspace_size", "dit_forward", "dit_cfg_forward",
               "dit_status_string", "dit_patchify", "dit_unpatchify", "dit_timestep_embed",
-              "dit_attention", "dit_linear", "dit_block_forward", "dit_sampler_coefficients",
+              "dit_attention", "dit_linear", "dit_linear_wgrad", "dit_block_forward", "dit_sampler_coefficients",
               "dit_sampler_step", "dit_sample_workspace_size", "dit_sample",
               "dit_packed_workspace_size", "dit_forward_packed", "dit_forward_ctx",
               "dit_train_param_count", "dit_train_param_layout", "dit_train_workspace_size",
@@ -250,6 +250,16 @@ def test_standalone_steps_validate_before_launch():
     assert lib.dit_linear(9, p, p, None, 4, 4, 64, 1, p, None, 0, 1, None) == _lib.DIT_EINVAL
     assert lib.dit_linear(0, p, p, None, 4, 4, 48, 1, p, None, 0, 1, None) == _lib.DIT_EUNSUPPORTED
     assert lib.dit_linear(2, p, p, None, 4, 4, 64, 1, p, None, 0, 1, None) == _lib.DIT_EINVAL
+    wg = lib.dit_linear_wgrad
+    assert wg(None, 8, p, 8, 8, 8, 64, 1, p, None) == _lib.DIT_EINVAL
+    assert wg(p, 8, p, 8, 8, 8, 64, 1, None, None) == _lib.DIT_EINVAL
+    assert wg(p, 8, p, 8, 0, 8, 64, 1, p, None) == _lib.DIT_EINVAL
+    assert wg(p, 8, p, 8, 8, 8, -1, 1, p, None) == _lib.DIT_EINVAL
+    assert wg(p, 4, p, 8, 8, 8, 64, 1, p, None) == _lib.DIT_EINVAL      # ldy < N
+    assert wg(p, 8, p, 4, 8, 8, 64, 1, p, None) == _lib.DIT_EINVAL      # ldx < K
+    assert wg(p, 8, p, 8, 8, 8, 64, 7, p, None) == _lib.DIT_EINVAL
+    assert wg(p, 8, p, 8, 8, 8, 1 << 31, 1, p, None) == _lib.DIT_EUNSUPPORTED
+    assert wg(p, 8, p, 8, 8, 8, 0, 1, p, None) == _lib.DIT_OK           # nothing to add
     assert lib.dit_status_string(_lib.DIT_EWORKSPACE) == b"workspace missing or too small"
 
 

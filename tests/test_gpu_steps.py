@@ -157,6 +157,38 @@ def test_linear_accumulate_long_reduction(M, N, K, dtype):
     assert e1 <= 1e-5 and e2 <= 1e-5
 
 
+@pytest.mark.parametrize("R,N,K,dtype,pad", [
+    (64, 8, 8, "bf16", 0),            # one reduction tile, one output tile
+    (4096, 1152, 4608, "bf16", 0),    # fc2 weight gradient of DiT-XL/2 at 16 images
+    (8192, 3456, 1152, "bf16", 8),    # qkv, strided rows
+    (1216, 200, 328, "bf16", 0),      # ragged output tiles on both sides
+    (300, 136, 72, "bf16", 0),        # R % 64 != 0: the vector-ALU path
+    (1000, 130, 70, "f32", 6),        # fp32, ragged everywhere, strided rows
+    (4096, 384, 1152, "f32", 0),
+])
+def test_linear_wgrad(R, N, K, dtype, pad):
+    """dW += dY^T X from row-major dY [R, N] and X [R, K] (rows of stride
+    N + pad, K + pad); a second call accumulates."""
+    log(f"linear_wgrad {dtype} R={R} N={N} K={K} pad={pad}")
+    rng = np.random.default_rng(R + 3 * N + 7 * K + pad)
+    dY = rng.standard_normal((R, N + pad)).astype(np.float32)
+    X = rng.standard_normal((R, K + pad)).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    if dtype == "bf16":
+        dY, X = _bf16(dY), _bf16(X)
+    ref = dY[:, :N].astype(np.float64).T @ X[:, :K].astype(np.float64)
+    dYd = torch.from_numpy(dY).to(tdt).cuda()[:, :N]
+    Xd = torch.from_numpy(X).to(tdt).cuda()[:, :K]
+    w0 = rng.standard_normal((N, K)).astype(np.float32)
+    dW = torch.from_numpy(w0).cuda()
+    dmod.linear_wgrad(dYd, Xd, dW)
+    e1 = rel_l2(np_(dW) - w0, ref)
+    dmod.linear_wgrad(dYd, Xd, dW)
+    e2 = rel_l2(np_(dW) - w0, 2 * ref)
+    log(f"  rel-L2 once={e1:.2e} twice={e2:.2e}")
+    assert e1 <= 1e-5 and e2 <= 1e-5
+
+
 # --- attention ---------------------------------------------------------------------------
 
 def _pack(q, k, v):
