@@ -61,12 +61,13 @@ def parse():
     return ap.parse_args()
 
 
-def measured_traffic(src_rel: str, kernel: str, shape):
-    """HBM bytes per launch of `kernel` at `shape` (M, N, K) from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE record (each scaled by the factor a plain copy of known size
-    gave), or None when there is no record for this shape or the kernel source changed."""
+def measured_traffic(rec_name: str, src_rel: str, kernel: str, shape):
+    """HBM bytes per launch of `kernel` at `shape` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE record profiles/`rec_name` (each counter scaled by the
+    factor a plain copy of known size gave), or None when there is no record for this
+    kernel and shape or the kernel source changed since it was taken."""
     import hashlib
-    rec_path = os.path.join(ROOT, "profiles", "gemm_fc1_hbm_counters.json")
+    rec_path = os.path.join(ROOT, "profiles", rec_name)
     try:
         rec = json.load(open(rec_path))
         src = open(os.path.join(ROOT, src_rel), "rb").read()
@@ -176,12 +177,23 @@ def train_main(args, cfg, model, dev):
     kms = k0.elapsed_time(k1) / nk
     kflop = 2.0 * d * hid * R
     k_tflops = kflop / (kms * 1e-3) / 1e12
+    traffic = measured_traffic("gemm_tn_wgrad_hbm_counters.json",
+                               "diffusion_transformer_denoiser_amd/csrc/gemm_mfma.hip",
+                               "gemm_tn_kernel", (d, hid, R))
     roofline = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE)",
                 "algorithmic_bytes": (d + hid) * R * 2 + d * hid * 4 * 2,
                 "kernel": f"gemm_tn_kernel (FFN down-projection weight gradient: dW [{d}, {hid}] "
                           f"over R={R} rows)",
                 "avg_launch_ms": round(kms, 4)}
+    if args.copy_mib:   # calibration copy for the HBM byte counters
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     cpu = None
     if not args.skip_cpu_baseline:
         from oracle import train_oracle as TR
@@ -474,7 +486,8 @@ def main():
     tflops = flop_fwd / (ms * 1e-3) / 1e12
     kflop = 2.0 * M * hid * d
     k_tflops = kflop / (kms * 1e-3) / 1e12
-    traffic = measured_traffic("diffusion_transformer_denoiser_amd/csrc/gemm_mfma.hip",
+    traffic = measured_traffic("gemm_fc1_hbm_counters.json",
+                               "diffusion_transformer_denoiser_amd/csrc/gemm_mfma.hip",
                                "gemm_bf16_kernel<5, 128, 192, 64, 2, 1, 1, 1>", (M, hid, d))
     roofline = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
