@@ -189,6 +189,32 @@ def test_linear_wgrad(R, N, K, dtype, pad):
     assert e1 <= 1e-5 and e2 <= 1e-5
 
 
+def test_linear_wgrad_full_size_sampled():
+    """The weight-gradient launch the training benchmark times: dW [1152, 4608] over
+    R = 65,536 rows of DiT-XL/2 at batch 256, bf16.  64 sampled entries against fp64
+    dot products of the same bf16 columns; the whole result against the fp32 product."""
+    R, N, K = 65536, 1152, 4608
+    log(f"linear_wgrad full size R={R} N={N} K={K}")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    dY = torch.randn(R, N, device="cuda", generator=g).to(torch.bfloat16)
+    X = torch.randn(R, K, device="cuda", generator=g).to(torch.bfloat16)
+    dW = torch.zeros(N, K, device="cuda")
+    dmod.linear_wgrad(dY, X, dW)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    ns, ks = rng.integers(0, N, 64), rng.integers(0, K, 64)
+    ns[:2], ks[:2] = (0, N - 1), (0, K - 1)      # corners: first and last tiles
+    a = np_(dY[:, torch.from_numpy(ns).cuda()].float()).astype(np.float64)
+    b = np_(X[:, torch.from_numpy(ks).cuda()].float()).astype(np.float64)
+    ref = (a * b).sum(axis=0)
+    got = np_(dW[torch.from_numpy(ns).cuda(), torch.from_numpy(ks).cuda()]).astype(np.float64)
+    e1 = rel_l2(got, ref)
+    full = dY.float().t().contiguous() @ X.float()
+    e2 = rel_l2(np_(dW), np_(full))
+    log(f"  sampled rel-L2 {e1:.2e}, whole vs fp32 product {e2:.2e}")
+    assert e1 <= 1e-5 and e2 <= 1e-5
+
+
 # --- attention ---------------------------------------------------------------------------
 
 def _pack(q, k, v):

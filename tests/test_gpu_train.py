@@ -137,3 +137,59 @@ def test_train_step_xl_width_two_blocks():
     log("  grad rel-L2: " + ", ".join(f"{n}={e:.1e}" for n, e in errs.items()))
     bad = {n: e for n, e in errs.items() if not e <= BF16_TOL}
     assert not bad, bad
+
+
+def _train_inputs_dev(cfg, B=None):
+    inp = dit_inputs.make_train_inputs(cfg, batch=B)
+    return to_dev(inp["x0"], inp["y"], inp["t"], inp["noise"])
+
+
+def test_train_step_full_size_batch_split_consistency():
+    """The training workload at full size (DiT-XL/2, batch 256, 28 blocks, bf16), as
+    the training benchmark runs it.  The loss is a mean over rows, so the loss and
+    every gradient of the 256-row batch must equal the mean of those of its two
+    128-row halves; only the summation order of the reductions over rows differs.
+    lr = 0 keeps the weights fixed across the three steps."""
+    cfg = dit_inputs.workload("dit_xl2_256_train")
+    B = cfg["batch"]
+    m = dmod.DiT(cfg, dit_inputs.make_weights(cfg), "cuda")
+    m.train_init()
+    x0, y, t, eps = _train_inputs_dev(cfg)
+    log(f"full-size training step: batch {B}, 28 blocks, bf16")
+    lf = np_(m.train_step(x0, y, t, eps, step=1, lr=0.0)).astype(np.float64)
+    gf = m.train_state["grad"].clone()
+    h = B // 2
+    la = np_(m.train_step(x0[:h], y[:h], t[:h], eps[:h], step=2, lr=0.0)).astype(np.float64)
+    ga = m.train_state["grad"].clone()
+    lb = np_(m.train_step(x0[h:], y[h:], t[h:], eps[h:], step=3, lr=0.0)).astype(np.float64)
+    gm = (ga + m.train_state["grad"]) * 0.5
+    torch.cuda.synchronize()
+    el = np.abs(lf - (la + lb) / 2) / np.abs(lf)
+    log(f"  loss full {lf}, halves {la} {lb}; rel diff {el}")
+    assert np.all(np.isfinite(lf)) and np.all(el <= 1e-5)
+    errs = {}
+    for name, (off, cnt) in m.train_fields.items():
+        errs[name] = rel_l2(np_(gf[off:off + cnt]), np_(gm[off:off + cnt]))
+    log("  grad rel-L2 full vs mean of halves: " + ", ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e <= 1e-4}
+    assert not bad, bad
+
+
+def test_train_step_full_depth_one_row_matches_oracle():
+    """One row through all 28 DiT-XL/2 blocks (bf16): both loss terms and every
+    gradient field against the fp64 oracle's autograd."""
+    cfg = dit_inputs.workload("dit_xl2_256_train", batch=1)
+    w = dit_inputs.make_weights(cfg)
+    m = dmod.DiT(cfg, w, "cuda")
+    inp = dit_inputs.make_train_inputs(cfg, batch=1)
+    inp["t"][0] = 500
+    log("full-depth training step, one row, bf16")
+    loss = np_(m.train_step(*to_dev(inp["x0"], inp["y"], inp["t"], inp["noise"]), step=1))
+    torch.cuda.synchronize()
+    ls, lv, g = TR.gradients(cfg, w, inp["x0"], inp["y"], inp["t"], inp["noise"])
+    log(f"  loss GPU {loss} oracle ({ls:.6f}, {lv:.6f})")
+    assert abs(loss[0] - ls) <= BF16_TOL * ls and abs(loss[1] - lv) <= BF16_TOL * abs(lv)
+    errs = {n: rel_l2(np_(m.train_view("grad", n)), g[n]) for n in TR.TRAIN_FIELDS}
+    log("  grad rel-L2: " + ", ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e <= BF16_TOL}
+    assert not bad, bad
