@@ -44,11 +44,9 @@ hipError_t launch_ln_mod_bwd(const float* X, const float* dH, const float* mod, 
                              hipStream_t s);
 hipError_t launch_gate_bwd(const float* dX, const float* v, const float* mod, int ms, int goff,
                            int B, int T, int d, int dtype, void* dv, float* dmod, hipStream_t s);
-// out[c, r] = in[r, c] (GELU applied when gelu != 0); dtypes 0 fp32, 1 bf16.
+// out[c, r] = in[r, c]; dtypes 0 fp32, 1 bf16.
 hipError_t launch_transpose(const void* in, int in_dtype, int64_t R, int64_t Cc, int64_t ldi,
-                            void* out, int out_dtype, int64_t ldo, int gelu, hipStream_t s);
-hipError_t launch_rowsum(const void* in, int dtype, int rows, int64_t cols, int64_t ld, float* out,
-                         hipStream_t s);
+                            void* out, int out_dtype, int64_t ldo, hipStream_t s);
 hipError_t launch_colsum(const float* in, int rows, int64_t cols, int64_t ld, float* out,
                          hipStream_t s);
 // out[c] += column sums of a tall bf16 matrix (cols, ld multiples of 8); out

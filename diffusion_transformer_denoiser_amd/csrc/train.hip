@@ -1,8 +1,8 @@
 // Device kernels of one training step of the adaLN-Zero DiT: the forward
 // process, the loss with its gradient at the decoder output, the backward
 // pieces that are not matrix products (LayerNorm + modulation, gated
-// residuals, GELU, attention, bias and modulation reductions, class-table
-// scatter), transposes that feed the weight-gradient products, and AdamW with
+// residuals, attention, bias and modulation reductions, class-table scatter),
+// the weight transposes that feed the input-gradient products, and AdamW with
 // the weight EMA.
 //
 // [Sora-cvl] Method / training objective bullet: x_t = sqrt(abar_t) x_0 +
@@ -310,8 +310,8 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
     dmod[(int64_t)b * ms + goff + n] = red[0][n] + red[1][n] + red[2][n] + red[3][n];
 }
 
-// out[c, r] = op(in[r, c]) for r < R, c < Cc; 64 x 64 tiles through LDS.
-template <typename IT, typename OT, int OP>
+// out[c, r] = in[r, c] for r < R, c < Cc; 64 x 64 tiles through LDS.
+template <typename IT, typename OT>
 __global__ __launch_bounds__(256) void transpose_kernel(const IT* __restrict__ in, int64_t R,
                                                         int64_t Cc, int64_t ldi,
                                                         OT* __restrict__ out, int64_t ldo) {
@@ -320,9 +320,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const IT* __restrict__ i
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int k = ty; k < 64; k += 4) {
     const int64_t r = r0 + k, c = c0 + tx;
-    float v = (r < R && c < Cc) ? to_f<IT>(in[r * ldi + c]) : 0.0f;
-    if constexpr (OP == 1) v = gelu_tanh_f(v);
-    tile[k][tx] = v;
+    tile[k][tx] = (r < R && c < Cc) ? to_f<IT>(in[r * ldi + c]) : 0.0f;
   }
   __syncthreads();
   for (int k = ty; k < 64; k += 4) {
@@ -334,7 +332,6 @@ __global__ __launch_bounds__(256) void transpose_kernel(const IT* __restrict__ i
 // bf16 -> bf16 transpose with 16-byte global accesses (R, Cc, ldi, ldo
 // multiples of 8, 16-byte aligned): a 64 x 64 tile is read as 8-element row
 // pieces, kept in LDS, and written as 8-element pieces of the output rows.
-template <int OP>
 __global__ __launch_bounds__(256) void transpose16_kernel(const bf16_t* __restrict__ in, int64_t R,
                                                           int64_t Cc, int64_t ldi,
                                                           bf16_t* __restrict__ out, int64_t ldo) {
@@ -346,14 +343,6 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const bf16_t* __restri
     const int id = tid + 256 * u, row = id >> 3, cc = (id & 7) * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (r0 + row < R && c0 + cc < Cc) v = *(const uint4*)(in + (r0 + row) * ldi + c0 + cc);
-    if constexpr (OP == 1) {
-      uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        wv[i] = f2bf2(gelu_tanh_f(__uint_as_float(wv[i] << 16)),
-                      gelu_tanh_f(__uint_as_float(wv[i] & 0xFFFF0000u)));
-      v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-    }
     *(uint4*)&tile[row][cc] = v;
   }
   __syncthreads();
@@ -368,32 +357,6 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const bf16_t* __restri
       *(uint4*)(out + (c0 + oc) * ldo + r0 + rr) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
   }
-}
-
-// out[r] = sum over c < cols of in[r * ld + c]; one workgroup per row.  VEC:
-// bf16 rows read 8 at a time (cols and ld multiples of 8, 16-byte aligned).
-template <typename IT, bool VEC>
-__global__ __launch_bounds__(256) void rowsum_kernel(const IT* __restrict__ in, int64_t cols,
-                                                     int64_t ld, float* __restrict__ out) {
-  const int64_t r = blockIdx.x;
-  float s = 0.0f;
-  if constexpr (VEC) {
-    const uint4* p = (const uint4*)(in + r * ld);
-    for (int64_t c = threadIdx.x; c < cols / 8; c += 256) {
-      const uint4 u = p[c];
-      const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s += __uint_as_float(wv[i] << 16) + __uint_as_float(wv[i] & 0xFFFF0000u);
-    }
-  } else {
-    for (int64_t c = threadIdx.x; c < cols; c += 256) s += to_f<IT>(in[r * ld + c]);
-  }
-  __shared__ float red[4];
-  s = wave_sum(s);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) out[r] = red[0] + red[1] + red[2] + red[3];
 }
 
 // out[c] += sum over r < rows of in[r * ld + c] for tall matrices: a
@@ -767,41 +730,22 @@ hipError_t launch_gate_bwd(const float* dX, const float* v, const float* mod, in
 }
 
 hipError_t launch_transpose(const void* in, int in_dtype, int64_t R, int64_t Cc, int64_t ldi,
-                            void* out, int out_dtype, int64_t ldo, int gelu, hipStream_t s) {
+                            void* out, int out_dtype, int64_t ldo, hipStream_t s) {
   if (R <= 0 || Cc <= 0) return hipSuccess;
   if ((Cc + 63) / 64 > INT32_MAX || (R + 63) / 64 > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((Cc + 63) / 64), (unsigned)((R + 63) / 64));
   if (in_dtype == 1 && out_dtype == 1 && R % 8 == 0 && Cc % 8 == 0 && ldi % 8 == 0 &&
       ldo % 8 == 0 && ((uintptr_t)in & 15) == 0 && ((uintptr_t)out & 15) == 0) {
-    if (gelu)
-      transpose16_kernel<1><<<grid, 256, 0, s>>>((const bf16_t*)in, R, Cc, ldi, (bf16_t*)out, ldo);
-    else
-      transpose16_kernel<0><<<grid, 256, 0, s>>>((const bf16_t*)in, R, Cc, ldi, (bf16_t*)out, ldo);
+    transpose16_kernel<<<grid, 256, 0, s>>>((const bf16_t*)in, R, Cc, ldi, (bf16_t*)out, ldo);
     return hipGetLastError();
   }
-#define DIT_TR(IT, OT)                                                                         \
-  if (gelu)                                                                                    \
-    transpose_kernel<IT, OT, 1><<<grid, 256, 0, s>>>((const IT*)in, R, Cc, ldi, (OT*)out, ldo); \
-  else                                                                                         \
-    transpose_kernel<IT, OT, 0><<<grid, 256, 0, s>>>((const IT*)in, R, Cc, ldi, (OT*)out, ldo);
+#define DIT_TR(IT, OT) \
+  transpose_kernel<IT, OT><<<grid, 256, 0, s>>>((const IT*)in, R, Cc, ldi, (OT*)out, ldo);
   if (in_dtype == 1 && out_dtype == 1) { DIT_TR(bf16_t, bf16_t) }
   else if (in_dtype == 1) { DIT_TR(bf16_t, float) }
   else if (out_dtype == 1) { DIT_TR(float, bf16_t) }
   else { DIT_TR(float, float) }
 #undef DIT_TR
-  return hipGetLastError();
-}
-
-hipError_t launch_rowsum(const void* in, int dtype, int rows, int64_t cols, int64_t ld, float* out,
-                         hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  const bool vec = cols % 8 == 0 && ld % 8 == 0 && ((uintptr_t)in & 15) == 0;
-  if (dtype == 1 && vec)
-    rowsum_kernel<bf16_t, true><<<rows, 256, 0, s>>>((const bf16_t*)in, cols, ld, out);
-  else if (dtype == 1)
-    rowsum_kernel<bf16_t, false><<<rows, 256, 0, s>>>((const bf16_t*)in, cols, ld, out);
-  else
-    rowsum_kernel<float, false><<<rows, 256, 0, s>>>((const float*)in, cols, ld, out);
   return hipGetLastError();
 }
 

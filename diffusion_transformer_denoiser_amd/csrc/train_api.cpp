@@ -307,17 +307,17 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
   DIT_HIP(launch_fill_f32(dmod, (int64_t)B * ms, 0.0f, s));   // LN backward adds into it
   for (int l = 0; l < N; ++l) {
     DIT_HIP(launch_transpose(wl(F_QKV_W, l, (size_t)3 * d * d), dt, 3 * d, d, d,
-                             at<char>(ws, L.wqkv) + (size_t)l * d * 3 * d * es, dt, 3 * d, 0, s));
+                             at<char>(ws, L.wqkv) + (size_t)l * d * 3 * d * es, dt, 3 * d, s));
     DIT_HIP(launch_transpose(wl(F_O_W, l, (size_t)d * d), dt, d, d, d,
-                             at<char>(ws, L.wo) + (size_t)l * d * d * es, dt, d, 0, s));
+                             at<char>(ws, L.wo) + (size_t)l * d * d * es, dt, d, s));
     DIT_HIP(launch_transpose(wl(F_FC1_W, l, (size_t)hid * d), dt, hid, d, d,
-                             at<char>(ws, L.wfc1) + (size_t)l * d * hid * es, dt, hid, 0, s));
+                             at<char>(ws, L.wfc1) + (size_t)l * d * hid * es, dt, hid, s));
     DIT_HIP(launch_transpose(wl(F_FC2_W, l, (size_t)d * hid), dt, d, hid, hid,
-                             at<char>(ws, L.wfc2) + (size_t)l * hid * d * es, dt, d, 0, s));
+                             at<char>(ws, L.wfc2) + (size_t)l * hid * d * es, dt, d, s));
   }
-  DIT_HIP(launch_transpose(W_(F_OUT_W), dt, kout, d, d, at<void>(ws, L.wout), dt, kout, 0, s));
-  DIT_HIP(launch_transpose(W_(F_ADA_W), dt, ms, d, d, at<void>(ws, L.wada), dt, ms, 0, s));
-  DIT_HIP(launch_transpose(W_(F_T2_W), dt, d, d, d, at<void>(ws, L.wt2), 0, d, 0, s));
+  DIT_HIP(launch_transpose(W_(F_OUT_W), dt, kout, d, d, at<void>(ws, L.wout), dt, kout, s));
+  DIT_HIP(launch_transpose(W_(F_ADA_W), dt, ms, d, d, at<void>(ws, L.wada), dt, ms, s));
+  DIT_HIP(launch_transpose(W_(F_T2_W), dt, d, d, d, at<void>(ws, L.wt2), 0, d, s));
 
   // ---- conditioning: c = t-MLP(e(t)) + y_table[y]; mod = Linear(SiLU(c)) ----------------
   float* e = at<float>(ws, L.e);
