@@ -14,6 +14,14 @@ Besides the headline number the line carries
                 after the forward loop (at the same sustained clocks);
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on
                 this host's cores.
+
+Other modes (same JSON line, their own metric):
+  --workload NAME   another forward configuration (its dominant kernel is fc1,
+                    or attention at T >= 4096); --skip-cpu-baseline for long ones
+  --train           one dit_train_step per step at DiT-XL/2 batch 256; roofline
+                    of the weight-gradient kernel (dit_linear_wgrad)
+  --sample KIND     whole dit_sample loops (ddpm, dpmpp_2m, rf_euler)
+  --packed          one packed call over latents of two sizes
 """
 from __future__ import annotations
 
@@ -395,7 +403,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
+        print(json.dumps({"error": "the denoiser runs on one GPU; multi-GPU runs are not "
                                    "supported (use --gpus 1)"}), flush=True)
         sys.exit(2)
 
