@@ -195,6 +195,9 @@ def train_main(args, cfg, model, dev):
                 "kernel": f"gemm_tn_kernel (FFN down-projection weight gradient: dW [{d}, {hid}] "
                           f"over R={R} rows)",
                 "avg_launch_ms": round(kms, 4)}
+    if traffic:   # counter-measured HBM bytes over the HIP-event launch time
+        roofline["hbm_gbs"] = round(traffic / (kms * 1e-3) / 1e9, 1)
+        roofline["hbm_frac"] = round(traffic / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
     if args.copy_mib:   # calibration copy for the HBM byte counters
         n = args.copy_mib * (1 << 20) // 4
         src = torch.randn(n, device=dev)
@@ -529,6 +532,9 @@ def main():
                     "kernel": f"gemm_bf16_kernel<EPI_GELU,128,192,64> (FFN fc1 of one row half: "
                               f"M={M}, N={hid}, K={d})",
                     "avg_launch_ms": round(kms, 4)}
+        if traffic:   # counter-measured HBM bytes over the HIP-event launch time
+            roofline["hbm_gbs"] = round(traffic / (kms * 1e-3) / 1e9, 1)
+            roofline["hbm_frac"] = round(traffic / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
 
     if args.copy_mib:
         n = args.copy_mib * (1 << 20) // 4
