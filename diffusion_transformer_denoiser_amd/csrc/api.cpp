@@ -16,6 +16,7 @@
 #include "dit.h"
 #include "common.h"
 #include "internal.h"
+#include "train.h"
 
 namespace dit_host {
 
@@ -138,13 +139,13 @@ int splitk_slice(bool mfma, int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t linear_wgrad(const void* dY, int64_t ldy, const void* X, int64_t ldx, int N, int K,
-                        int64_t R, int dtype, float* dW, int lddw, hipStream_t s) {
+                        int64_t R, int dtype, float* dW, int lddw, float* db, hipStream_t s) {
   if (N <= 0 || K <= 0 || R <= 0) return hipSuccess;
   if (dtype == DIT_BF16 && N % 8 == 0 && K % 8 == 0 && R % 64 == 0 && ldy % 8 == 0 &&
       ldx % 8 == 0 && ((uintptr_t)dY & 15) == 0 && ((uintptr_t)X & 15) == 0 &&
       R * (ldy > ldx ? ldy : ldx) <= INT32_MAX)
     return launch_gemm_tn((const bf16_t*)dY, (int)ldy, (const bf16_t*)X, (int)ldx, N, K, (int)R,
-                          dW, lddw, s);
+                          dW, lddw, db, s);
   if (R > INT32_MAX || ldy > INT32_MAX || ldx > INT32_MAX) return hipErrorInvalidValue;
   ALoad a;
   memset(&a, 0, sizeof a);
@@ -153,8 +154,12 @@ hipError_t linear_wgrad(const void* dY, int64_t ldy, const void* X, int64_t ldx,
   memset(&ep, 0, sizeof ep);
   ep.out = dW; ep.ldo = lddw; ep.ldw = (int)ldx; ep.w_trans = 1;
   ep.ksplit = splitk_slice(false, N, K, R);
-  return launch_gemm_valu(EPI_ATOMIC_F32, A_PLAIN, a, X, dtype == DIT_BF16 ? 1 : 0, N, K, (int)R,
-                          ep, s);
+  hipError_t e = launch_gemm_valu(EPI_ATOMIC_F32, A_PLAIN, a, X, dtype == DIT_BF16 ? 1 : 0, N, K,
+                                  (int)R, ep, s);
+  if (e != hipSuccess || !db) return e;
+  if (dtype != DIT_BF16) return launch_colsum((const float*)dY, (int)R, N, ldy, db, s);
+  if (N % 8 || ldy % 8 || ((uintptr_t)dY & 15)) return hipErrorInvalidValue;
+  return launch_colsum_tall_bf16(dY, R, N, ldy, db, s);
 }
 
 EpiParams epi0() {
@@ -1202,7 +1207,7 @@ int dit_linear_wgrad(const void* dY, int64_t ldy, const void* X, int64_t ldx, in
   if (dtype != DIT_F32 && dtype != DIT_BF16) return fail(DIT_EINVAL, "dtype");
   if (R > INT32_MAX || ldy > INT32_MAX || ldx > INT32_MAX)
     return fail(DIT_EUNSUPPORTED, "R and the row strides must be below 2^31");
-  DIT_HIP(linear_wgrad(dY, ldy, X, ldx, N, K, R, dtype, dW, K, (hipStream_t)stream));
+  DIT_HIP(linear_wgrad(dY, ldy, X, ldx, N, K, R, dtype, dW, K, nullptr, (hipStream_t)stream));
   return ok();
 }
 

@@ -193,9 +193,10 @@ struct ALoad {
 // out[i, j] += sum_r A[r, i] B[r, j] (fp32, atomically): A [R, Mi] and B [R, Nj]
 // bf16, row strides lda, ldb; Mi, Nj multiples of 8, R a multiple of 64,
 // 16-byte aligned.  The weight gradient of a layer from its row-major input
-// and output gradient.
+// and output gradient.  asum (optional): asum[i] += sum_r A[r, i], the bias
+// gradient, also atomically.
 hipError_t launch_gemm_tn(const bf16_t* A, int lda, const bf16_t* B, int ldb, int Mi, int Nj,
-                          int R, float* out, int ldo, hipStream_t s);
+                          int R, float* out, int ldo, float* asum, hipStream_t s);
 hipError_t launch_gemm_valu(int epi, int asrc, const ALoad& a, const void* W, int w_dtype,
                             int M, int N, int K, const EpiParams& ep, hipStream_t s);
 hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, int M, int N,

@@ -513,7 +513,8 @@ hipError_t pick(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
 __global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const bf16_t* __restrict__ A, int lda,
                                                          const bf16_t* __restrict__ B, int ldb,
                                                          int Mi, int Nj, int R, int ksplit,
-                                                         float* __restrict__ out, int ldo) {
+                                                         float* __restrict__ out, int ldo,
+                                                         float* __restrict__ asum) {
   constexpr int BM = 128, BN = 192, BK = 64, TM = 2, TN = 3;
   constexpr int CA = BM / 8, CB = BN / 8;                     // chunks per row
   constexpr int OPA = BK * BM * 2, OPB = BK * BN * 2;         // bytes per operand tile
@@ -588,6 +589,20 @@ __global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const bf16_t* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // Column sums of A (the bias gradient), taken by the waves with wn == 0 of
+  // the tiles in the first column (tn == 0) from the A fragments they already
+  // hold: per k step lane l adds 8 r of column l % 32; lanes l and l + 32
+  // (the other 8 r) combine at the end.
+  const bool csum = asum != nullptr && tn == 0 && wn == 0;
+  float cs[TM] = {};
+  auto colsum = [&](const bf16x8_t& f, float& acc) {
+    const uint4 u = __builtin_bit_cast(uint4, f);
+    const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc += __uint_as_float(wv[e] << 16) + __uint_as_float(wv[e] & 0xFFFF0000u);
+  };
+
   const int nk = Rl / BK;
   copy(0);
   if (nk > 1) {
@@ -620,6 +635,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const bf16_t* __restric
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0,
                                                               0, 0);
+      if (csum)
+#pragma unroll
+        for (int i = 0; i < TM; ++i) colsum(fa[cur][i], cs[i]);
     }
     // this stage is read (by this wave; the barrier covers the others) and
     // slice kt + 1, the only copies in flight, has landed
@@ -627,6 +645,15 @@ __global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const bf16_t* __restric
     wait_vmcnt<0>();
     bare_barrier();
     if (kt + 2 < nk) copy(kt + 2);
+  }
+
+  if (csum) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const float v = cs[i] + __shfl_xor(cs[i], 32, 64);
+      const int col = i0 + wm * 64 + i * 32 + lane;
+      if (lane < 32 && col < Mi) unsafeAtomicAdd(&asum[col], v);
+    }
   }
 
   // lane: column j0 + wn 96 + 32 j + lane % 32, rows i0 + wm 64 + 32 i + 4 (lane / 32) + 8 (r / 4) + r % 4
@@ -669,7 +696,7 @@ hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, 
 }
 
 hipError_t launch_gemm_tn(const bf16_t* A, int lda, const bf16_t* B, int ldb, int Mi, int Nj,
-                          int R, float* out, int ldo, hipStream_t s) {
+                          int R, float* out, int ldo, float* asum, hipStream_t s) {
   if (Mi <= 0 || Nj <= 0 || R <= 0) return hipSuccess;
   if (Mi % 8 || Nj % 8 || R % 64 || lda % 8 || ldb % 8 || lda < Mi || ldb < Nj ||
       ((uintptr_t)A & 15) || ((uintptr_t)B & 15))
@@ -693,6 +720,6 @@ hipError_t launch_gemm_tn(const bf16_t* A, int lda, const bf16_t* B, int ldb, in
   int ks = (R + best - 1) / best;
   ks = (ks + 63) / 64 * 64;
   const dim3 grid(tiles, (R + ks - 1) / ks);
-  gemm_tn_kernel<<<grid, 256, 0, s>>>(A, lda, B, ldb, Mi, Nj, R, ks, out, ldo);
+  gemm_tn_kernel<<<grid, 256, 0, s>>>(A, lda, B, ldb, Mi, Nj, R, ks, out, ldo, asum);
   return hipGetLastError();
 }

@@ -53,9 +53,12 @@ int splitk_slice(bool mfma, int64_t M, int64_t N, int64_t K);
 // Weight gradient dW [N, K] += dY^T X (fp32, atomically) from the row-major
 // output gradient dY [R, N] (row stride ldy) and input X [R, K] (row stride
 // ldx), both in dtype: the TN matrix-core kernel for bf16 when the shapes fit
-// it, else the VALU kernel reading both operands transposed.
+// it, else the VALU kernel reading both operands transposed.  db (optional):
+// db[n] += sum_r dY[r, n], the bias gradient (inside the TN kernel, else a
+// column-sum kernel; bf16 then needs N, ldy multiples of 8 and dY 16-byte
+// aligned).
 hipError_t linear_wgrad(const void* dY, int64_t ldy, const void* X, int64_t ldx, int N, int K,
-                        int64_t R, int dtype, float* dW, int lddw, hipStream_t s);
+                        int64_t R, int dtype, float* dW, int lddw, float* db, hipStream_t s);
 // One linear layer C = A W^T with the epilogue: MFMA for bf16 models, VALU
 // for fp32 ones.
 hipError_t linear(const dit_handle* h, int epi, const void* A, int lda, const void* W, int M,

@@ -212,11 +212,7 @@ hipError_t gemm_any(int epi, const void* A, int adt, int64_t lda, const void* W,
 // (both fp32, zeroed beforehand).
 int layer_grads(int dt, const void* dC, int64_t ldc, const void* X, int64_t ldx, int N, int K,
                 int64_t R, float* gW, float* gb, hipStream_t s) {
-  DIT_HIP(linear_wgrad(dC, ldc, X, ldx, N, K, R, dt, gW, K, s));
-  if (gb) {
-    if (dt == DIT_BF16) DIT_HIP(launch_colsum_tall_bf16(dC, R, N, ldc, gb, s));
-    else DIT_HIP(launch_colsum((const float*)dC, (int)R, N, ldc, gb, s));
-  }
+  DIT_HIP(linear_wgrad(dC, ldc, X, ldx, N, K, R, dt, gW, K, gb, s));
   return DIT_OK;
 }
 
