@@ -93,7 +93,7 @@ EXPORTS = {
                              C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_int, C.c_int,
                              C.c_void_p]),
     "dit_linear_wgrad": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_int, C.c_int,
-                                   C.c_int64, C.c_int, C.c_void_p, C.c_void_p]),
+                                   C.c_int64, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dit_block_forward": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                     C.c_void_p]),

@@ -1200,14 +1200,19 @@ int dit_linear(int epilogue, const void* A, const void* W, const float* bias, in
 }
 
 int dit_linear_wgrad(const void* dY, int64_t ldy, const void* X, int64_t ldx, int N, int K,
-                     int64_t R, int dtype, float* dW, void* stream) {
+                     int64_t R, int dtype, float* dW, float* db, void* stream) {
   if (!dY || !X || !dW) return fail(DIT_EINVAL, "dY, X and dW must be non-NULL");
   if (N <= 0 || K <= 0 || R < 0) return fail(DIT_EINVAL, "N, K must be positive and R >= 0");
   if (ldy < N || ldx < K) return fail(DIT_EINVAL, "row strides ldy >= N and ldx >= K");
   if (dtype != DIT_F32 && dtype != DIT_BF16) return fail(DIT_EINVAL, "dtype");
   if (R > INT32_MAX || ldy > INT32_MAX || ldx > INT32_MAX)
     return fail(DIT_EUNSUPPORTED, "R and the row strides must be below 2^31");
-  DIT_HIP(linear_wgrad(dY, ldy, X, ldx, N, K, R, dtype, dW, K, nullptr, (hipStream_t)stream));
+  const bool tn = dtype == DIT_BF16 && N % 8 == 0 && K % 8 == 0 && R % 64 == 0 && ldy % 8 == 0 &&
+                  ldx % 8 == 0 && ((uintptr_t)dY & 15) == 0 && ((uintptr_t)X & 15) == 0 &&
+                  R * (ldy > ldx ? ldy : ldx) <= INT32_MAX;
+  if (db && dtype == DIT_BF16 && !tn && (N % 8 || ldy % 8 || ((uintptr_t)dY & 15)))
+    return fail(DIT_EUNSUPPORTED, "bf16 bias gradient needs N, ldy multiples of 8 and aligned dY");
+  DIT_HIP(linear_wgrad(dY, ldy, X, ldx, N, K, R, dtype, dW, K, db, (hipStream_t)stream));
   return ok();
 }
 

@@ -47,6 +47,7 @@ hipError_t launch_gate_bwd(const float* dX, const float* v, const float* mod, in
 // out[c, r] = in[r, c]; dtypes 0 fp32, 1 bf16.
 hipError_t launch_transpose(const void* in, int in_dtype, int64_t R, int64_t Cc, int64_t ldi,
                             void* out, int out_dtype, int64_t ldo, hipStream_t s);
+// out[c] += column sums of in [rows, cols] (row stride ld), fp32.
 hipError_t launch_colsum(const float* in, int rows, int64_t cols, int64_t ld, float* out,
                          hipStream_t s);
 // out[c] += column sums of a tall bf16 matrix (cols, ld multiples of 8); out

@@ -395,14 +395,14 @@ __global__ __launch_bounds__(256) void colsum_tall_bf16_kernel(const bf16_t* __r
   }
 }
 
-// out[c] = sum over r < rows of in[r * ld + c]; one thread per column.
+// out[c] += sum over r < rows of in[r * ld + c]; one thread per column.
 __global__ void colsum_kernel(const float* __restrict__ in, int rows, int64_t cols, int64_t ld,
                               float* __restrict__ out) {
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= cols) return;
   float s = 0.0f;
   for (int r = 0; r < rows; ++r) s += in[r * ld + c];
-  out[c] = s;
+  out[c] += s;
 }
 
 // Class-table gradient: row y[b] of the table receives dc[b] (atomically: rows

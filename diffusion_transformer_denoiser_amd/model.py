@@ -420,15 +420,17 @@ def linear(epilogue: int, A, W, bias, out, gate=None, gate_stride=0, T=1):
     return out
 
 
-def linear_wgrad(dY, X, dW):
+def linear_wgrad(dY, X, dW, db=None):
     """dW [N, K] fp32 += dY^T X for dY [R, N], X [R, K] (2-D, unit column stride,
-    same dtype): the weight gradient of a linear layer."""
+    same dtype), and db [N] fp32 += column sums of dY if given: the weight and
+    bias gradients of a linear layer."""
     lib = _lib.load()
     R, N = dY.shape
     K = X.shape[1]
     assert X.shape[0] == R and tuple(dW.shape) == (N, K) and dW.dtype == torch.float32
     assert dY.stride(1) == 1 and X.stride(1) == 1 and dW.is_contiguous() and X.dtype == dY.dtype
     code = _lib.DIT_BF16 if dY.dtype == torch.bfloat16 else _lib.DIT_F32
+    assert db is None or (db.dtype == torch.float32 and db.numel() == N and db.is_contiguous())
     _lib.check(lib.dit_linear_wgrad(_ptr(dY), dY.stride(0), _ptr(X), X.stride(0), N, K, R, code,
-                                    _ptr(dW), _stream(dY.device)))
+                                    _ptr(dW), _ptr(db), _stream(dY.device)))
     return dW

@@ -471,21 +471,25 @@ int dit_train_step(dit_handle* h, const dit_train_hparams* hp, int step,
                    const float* noise, int B, float* loss, void* ws, size_t ws_bytes,
                    void* stream);
 
-/* Weight gradient of a linear layer y = x W^T + b over R rows, the product
- * that dominates the backward pass of the step above (cv-learn.com "Sora /
- * DiT", Method, training-objective bullet: the parameters follow the gradient
- * of that loss):  dW[N, K] += dY^T X  =  sum over r of dY[r, n] X[r, k].
+/* Weight and bias gradients of a linear layer y = x W^T + b over R rows, the
+ * product that dominates the backward pass of the step above (cv-learn.com
+ * "Sora / DiT", Method, training-objective bullet: the parameters follow the
+ * gradient of that loss):  dW[N, K] += dY^T X  =  sum over r of dY[r, n] X[r, k]
+ * and, when db is not NULL, db[n] += sum over r of dY[r, n] (device fp32 [N],
+ * added to atomically like dW).
  * dY: device [R, N] row-major with row stride ldy >= N; X: device [R, K]
  * row-major with row stride ldx >= K; both in dtype, read as stored (no
  * transposed copies).  dW: device fp32 [N, K] row-major, added to atomically
  * (zero it first for a fresh gradient; the summation order is not fixed).
  * bf16 with N, K, ldy, ldx multiples of 8, R % 64 == 0, R * max(ldy, ldx) <
  * 2^31 and 16-byte aligned dY, X runs on the matrix cores; other shapes and
- * fp32 on the vector ALUs.  R == 0 adds nothing.  DIT_EINVAL for NULL
- * pointers, N or K not positive, R negative, a short row stride or an unknown
- * dtype; DIT_EUNSUPPORTED for R >= 2^31. */
+ * fp32 on the vector ALUs (db then by a column-sum pass; bf16 needs N and
+ * ldy multiples of 8 and dY 16-byte aligned for it).  R == 0 adds nothing.
+ * DIT_EINVAL for NULL dY, X or dW, N or K not positive, R negative, a short
+ * row stride or an unknown dtype; DIT_EUNSUPPORTED for R >= 2^31 or a bias
+ * gradient the column-sum pass cannot take. */
 int dit_linear_wgrad(const void* dY, int64_t ldy, const void* X, int64_t ldx, int N, int K,
-                     int64_t R, int dtype, float* dW, void* stream);
+                     int64_t R, int dtype, float* dW, float* db, void* stream);
 
 #ifdef __cplusplus
 }

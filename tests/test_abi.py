@@ -251,15 +251,16 @@ def test_standalone_steps_validate_before_launch():
     assert lib.dit_linear(0, p, p, None, 4, 4, 48, 1, p, None, 0, 1, None) == _lib.DIT_EUNSUPPORTED
     assert lib.dit_linear(2, p, p, None, 4, 4, 64, 1, p, None, 0, 1, None) == _lib.DIT_EINVAL
     wg = lib.dit_linear_wgrad
-    assert wg(None, 8, p, 8, 8, 8, 64, 1, p, None) == _lib.DIT_EINVAL
-    assert wg(p, 8, p, 8, 8, 8, 64, 1, None, None) == _lib.DIT_EINVAL
-    assert wg(p, 8, p, 8, 0, 8, 64, 1, p, None) == _lib.DIT_EINVAL
-    assert wg(p, 8, p, 8, 8, 8, -1, 1, p, None) == _lib.DIT_EINVAL
-    assert wg(p, 4, p, 8, 8, 8, 64, 1, p, None) == _lib.DIT_EINVAL      # ldy < N
-    assert wg(p, 8, p, 4, 8, 8, 64, 1, p, None) == _lib.DIT_EINVAL      # ldx < K
-    assert wg(p, 8, p, 8, 8, 8, 64, 7, p, None) == _lib.DIT_EINVAL
-    assert wg(p, 8, p, 8, 8, 8, 1 << 31, 1, p, None) == _lib.DIT_EUNSUPPORTED
-    assert wg(p, 8, p, 8, 8, 8, 0, 1, p, None) == _lib.DIT_OK           # nothing to add
+    assert wg(None, 8, p, 8, 8, 8, 64, 1, p, None, None) == _lib.DIT_EINVAL
+    assert wg(p, 8, p, 8, 8, 8, 64, 1, None, None, None) == _lib.DIT_EINVAL
+    assert wg(p, 8, p, 8, 0, 8, 64, 1, p, None, None) == _lib.DIT_EINVAL
+    assert wg(p, 8, p, 8, 8, 8, -1, 1, p, None, None) == _lib.DIT_EINVAL
+    assert wg(p, 4, p, 8, 8, 8, 64, 1, p, None, None) == _lib.DIT_EINVAL      # ldy < N
+    assert wg(p, 8, p, 4, 8, 8, 64, 1, p, None, None) == _lib.DIT_EINVAL      # ldx < K
+    assert wg(p, 8, p, 8, 8, 8, 64, 7, p, None, None) == _lib.DIT_EINVAL
+    assert wg(p, 8, p, 8, 8, 8, 1 << 31, 1, p, None, None) == _lib.DIT_EUNSUPPORTED
+    assert wg(p, 8, p, 8, 8, 8, 0, 1, p, None, None) == _lib.DIT_OK           # nothing to add
+    assert wg(p, 8, p, 8, 6, 8, 64, 1, p, p, None) == _lib.DIT_EUNSUPPORTED  # bf16 bias, N % 8
     assert lib.dit_status_string(_lib.DIT_EWORKSPACE) == b"workspace missing or too small"
 
 

@@ -167,8 +167,8 @@ def test_linear_accumulate_long_reduction(M, N, K, dtype):
     (4096, 384, 1152, "f32", 0),
 ])
 def test_linear_wgrad(R, N, K, dtype, pad):
-    """dW += dY^T X from row-major dY [R, N] and X [R, K] (rows of stride
-    N + pad, K + pad); a second call accumulates."""
+    """dW += dY^T X and db += column sums of dY from row-major dY [R, N] and
+    X [R, K] (rows of stride N + pad, K + pad); a second call accumulates."""
     log(f"linear_wgrad {dtype} R={R} N={N} K={K} pad={pad}")
     rng = np.random.default_rng(R + 3 * N + 7 * K + pad)
     dY = rng.standard_normal((R, N + pad)).astype(np.float32)
@@ -180,13 +180,18 @@ def test_linear_wgrad(R, N, K, dtype, pad):
     dYd = torch.from_numpy(dY).to(tdt).cuda()[:, :N]
     Xd = torch.from_numpy(X).to(tdt).cuda()[:, :K]
     w0 = rng.standard_normal((N, K)).astype(np.float32)
+    b0 = rng.standard_normal(N).astype(np.float32)
     dW = torch.from_numpy(w0).cuda()
-    dmod.linear_wgrad(dYd, Xd, dW)
+    db = torch.from_numpy(b0).cuda()
+    bref = dY[:, :N].astype(np.float64).sum(axis=0)
+    dmod.linear_wgrad(dYd, Xd, dW, db)
     e1 = rel_l2(np_(dW) - w0, ref)
-    dmod.linear_wgrad(dYd, Xd, dW)
+    b1 = rel_l2(np_(db) - b0, bref)
+    dmod.linear_wgrad(dYd, Xd, dW, db)
     e2 = rel_l2(np_(dW) - w0, 2 * ref)
-    log(f"  rel-L2 once={e1:.2e} twice={e2:.2e}")
-    assert e1 <= 1e-5 and e2 <= 1e-5
+    b2 = rel_l2(np_(db) - b0, 2 * bref)
+    log(f"  rel-L2 dW once={e1:.2e} twice={e2:.2e}; db once={b1:.2e} twice={b2:.2e}")
+    assert e1 <= 1e-5 and e2 <= 1e-5 and b1 <= 1e-5 and b2 <= 1e-5
 
 
 def test_linear_wgrad_full_size_sampled():
@@ -199,7 +204,8 @@ def test_linear_wgrad_full_size_sampled():
     dY = torch.randn(R, N, device="cuda", generator=g).to(torch.bfloat16)
     X = torch.randn(R, K, device="cuda", generator=g).to(torch.bfloat16)
     dW = torch.zeros(N, K, device="cuda")
-    dmod.linear_wgrad(dY, X, dW)
+    db = torch.zeros(N, device="cuda")
+    dmod.linear_wgrad(dY, X, dW, db)
     torch.cuda.synchronize()
     rng = np.random.default_rng(3)
     ns, ks = rng.integers(0, N, 64), rng.integers(0, K, 64)
@@ -211,8 +217,9 @@ def test_linear_wgrad_full_size_sampled():
     e1 = rel_l2(got, ref)
     full = dY.float().t().contiguous() @ X.float()
     e2 = rel_l2(np_(dW), np_(full))
-    log(f"  sampled rel-L2 {e1:.2e}, whole vs fp32 product {e2:.2e}")
-    assert e1 <= 1e-5 and e2 <= 1e-5
+    e3 = rel_l2(np_(db), np_(dY.double().sum(dim=0)))
+    log(f"  sampled rel-L2 {e1:.2e}, whole vs fp32 product {e2:.2e}, bias {e3:.2e}")
+    assert e1 <= 1e-5 and e2 <= 1e-5 and e3 <= 1e-5
 
 
 # --- attention ---------------------------------------------------------------------------
