@@ -24,6 +24,10 @@ def test_multi_gpu_request_exits_with_message():
 
 @pytest.mark.gpu
 def test_short_run_prints_one_contract_line():
+    import torch
+    if torch.cuda.is_available():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()   # cached blocks of earlier tests go back to the device
     r = _run("--steps", "2", "--warmup", "1", "--skip-cpu-baseline", "--kernel-launches", "4")
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.strip().splitlines() if l.startswith("{")]
