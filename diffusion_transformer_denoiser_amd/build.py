@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdit.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "embed.hip", "gemm_valu.hip", "gemm_mfma.hip", "layernorm.hip",
+SOURCES = ["api.cpp", "embed.hip", "gemm_valu.hip", "gemm_mfma.hip", "gemm_wide.hip", "layernorm.hip",
            "attention.hip", "sampler.hip", "train.hip", "attention_bwd.hip", "train_api.cpp"]
 
 

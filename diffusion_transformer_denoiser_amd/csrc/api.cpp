@@ -8,7 +8,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -46,24 +45,6 @@ using namespace dit_host;
 
 
 
-namespace {
-// Lazily creates the extra streams (default priority) and the events.
-bool ensure_aux(const dit_handle* h) {
-  if (h->aux_ready) return true;
-  if (h->aux_failed) return false;
-  bool ok_ = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) == hipSuccess;
-  for (int i = 0; ok_ && i < DIT_SPLIT - 1; ++i)
-    ok_ = hipStreamCreateWithFlags(&h->aux[i], hipStreamNonBlocking) == hipSuccess &&
-          hipEventCreateWithFlags(&h->ev_join[i], hipEventDisableTiming) == hipSuccess;
-  if (!ok_) {
-    (void)hipGetLastError();
-    h->aux_failed = true;   // fall back to one stream
-    return false;
-  }
-  h->aux_ready = true;
-  return true;
-}
-}  // namespace
 
 namespace {
 
@@ -568,12 +549,9 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
       DIT_HIP(hipMemcpyAsync(taps->x_embed, X, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s));
   }
 
-  // Blocks and the final layer (LN + modulation (b_f, g_f), linear decoder).
-  // Rows are independent from here on: without taps, the rows split into up
-  // to DIT_SPLIT groups, the first on the caller's stream and the others on
-  // the library's streams, forked and joined with events, so one group's
-  // memory-bound kernels (LN, attention) run beside another group's GEMMs.
-  // Each group uses its own rows of every workspace region.
+  // Blocks and the final layer (LN + modulation (b_f, g_f), linear decoder),
+  // all rows at once on the caller's stream: at the image configurations
+  // every block product then fills whole waves of the wide-tile GEMM.
   const int fb = 6 * d * h->N;
   const char* kv_base = at<char>(ws, L.kv);
   // Final layer: LN + (adaLN modulation or the learned affine) + decoder.
@@ -601,46 +579,6 @@ int run_trunk(const dit_handle* h, const void* x_t, const float* t, const int32_
                              kv_base + ((size_t)r0 * 2 * h->N * 2 * d + (size_t)l * 2 * d) * es,
                              ws, Lg, st);
   };
-  auto blocks_and_final = [&](int r0, int nr, hipStream_t st) -> int {
-    // scratch regions hold Tt tokens per row; the decoded stream Tf
-    const size_t m0 = (size_t)r0 * Tt, f0 = (size_t)r0 * Tf, es = h->es;
-    WsLayout Lh = L;
-    Lh.H += m0 * d * es;
-    Lh.qkv += m0 * 3 * d * es;
-    Lh.o += m0 * d * es;
-    Lh.G += m0 * h->hid * es;
-    float* Xh = X + f0 * d;
-    const float* modh = mod + (size_t)r0 * h->mod_stride;
-    for (int l = 0; l < h->N; ++l) {
-      int rc = one_block(l, r0, nr, Xh, modh, Lh, st);
-      if (rc) return rc;
-    }
-    return final_layer(Xh, modh, nr * Tf, at<void>(ws, Lh.H), Y + f0 * h->kout, st);
-  };
-
-  const int parts = rows < DIT_SPLIT ? rows : DIT_SPLIT;
-  if (!taps && parts >= 2) {
-    std::lock_guard<std::mutex> lock(h->mu);
-    if (ensure_aux(h)) {
-      DIT_HIP(hipEventRecord(h->ev_fork, s));
-      for (int i = 0; i < parts - 1; ++i) DIT_HIP(hipStreamWaitEvent(h->aux[i], h->ev_fork, 0));
-      int rc = DIT_OK;
-      for (int i = 0; i < parts && !rc; ++i) {
-        const int r0 = (int)((int64_t)rows * i / parts), r1 = (int)((int64_t)rows * (i + 1) / parts);
-        rc = blocks_and_final(r0, r1 - r0, i == 0 ? s : h->aux[i - 1]);
-      }
-      // join even after an error, so the caller's stream still orders after
-      // everything that was enqueued on the other streams
-      bool joined = true;
-      for (int i = 0; i < parts - 1; ++i)
-        joined = hipEventRecord(h->ev_join[i], h->aux[i]) == hipSuccess &&
-                 hipStreamWaitEvent(s, h->ev_join[i], 0) == hipSuccess && joined;
-      if (rc) return rc;
-      if (!joined) return fail(DIT_EHIP, "stream join failed");
-      return DIT_OK;
-    }
-  }
-
   for (int l = 0; l < h->N; ++l) {
     int rc = one_block(l, 0, rows, X, mod, L, s);
     if (rc) return rc;
@@ -1076,15 +1014,7 @@ int dit_create(const dit_config* cfg, const dit_weights* w, dit_handle** out) {
   return ok();
 }
 
-void dit_destroy(dit_handle* h) {
-  if (!h) return;
-  for (int i = 0; i < DIT_SPLIT - 1; ++i) {
-    if (h->aux[i]) (void)hipStreamDestroy(h->aux[i]);
-    if (h->ev_join[i]) (void)hipEventDestroy(h->ev_join[i]);
-  }
-  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
-  delete h;
-}
+void dit_destroy(dit_handle* h) { delete h; }
 
 int dit_workspace_size(const dit_handle* h, int rows, size_t* bytes) {
   if (!h || !bytes) return fail(DIT_EINVAL, "handle and bytes must be non-NULL");
@@ -1445,35 +1375,8 @@ int dit_forward_packed(dit_handle* h, int nseq, const int32_t* seq_fhw, const vo
     DIT_HIP(linear(h, EPI_BIAS_F32, Hg, d, h->w.out_w, g.M, h->kout, d, ef, st));
     return DIT_OK;
   };
-  // Two groups of about equal token counts on two streams (as the batched
-  // forward does with its two row halves), forked and joined with events.
-  int split = 0;
-  if (nseq >= 2) {
-    int64_t best = INT64_MAX;
-    for (int j = 1; j < nseq; ++j) {
-      const int64_t diff = std::llabs(2LL * pk.seqs.tok[j] - pk.M);
-      if (diff < best) { best = diff; split = j; }
-    }
-  }
-  bool forked = false;
-  if (split > 0) {
-    std::lock_guard<std::mutex> lock(h->mu);
-    if (ensure_aux(h)) {
-      forked = true;
-      DIT_HIP(hipEventRecord(h->ev_fork, s));
-      DIT_HIP(hipStreamWaitEvent(h->aux[0], h->ev_fork, 0));
-      rc = group(0, split, s);
-      if (!rc) rc = group(split, nseq, h->aux[0]);
-      const bool joined = hipEventRecord(h->ev_join[0], h->aux[0]) == hipSuccess &&
-                          hipStreamWaitEvent(s, h->ev_join[0], 0) == hipSuccess;
-      if (rc) return rc;
-      if (!joined) return fail(DIT_EHIP, "stream join failed");
-    }
-  }
-  if (!forked) {
-    rc = group(0, nseq, s);
-    if (rc) return rc;
-  }
+  rc = group(0, nseq, s);
+  if (rc) return rc;
   int64_t ooff = 0;
   for (int j = 0; j < nseq; ++j) {
     const int F = seq_fhw[3 * j], H = seq_fhw[3 * j + 1], W = seq_fhw[3 * j + 2];

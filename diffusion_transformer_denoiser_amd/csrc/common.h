@@ -201,6 +201,12 @@ hipError_t launch_gemm_valu(int epi, int asrc, const ALoad& a, const void* W, in
                             int M, int N, int K, const EpiParams& ep, hipStream_t s);
 hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, int M, int N,
                             int K, const EpiParams& ep, hipStream_t s);
+// The wide-tile kernel (256-row tiles, one workgroup per CU) for the large
+// block products; launch_gemm_mfma picks it when the shape fills the chip.
+bool gemm_wide_supported(int epi, const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
+                         const EpiParams& ep);
+hipError_t launch_gemm_wide(int epi, const bf16_t* A, int lda, const bf16_t* W, int M, int N,
+                            int K, const EpiParams& ep, hipStream_t s);
 
 // Row m's modulation row is tok_seg[m] when tok_seg is given (packed
 // sequences), else m / T.

@@ -675,9 +675,16 @@ __global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const bf16_t* __restric
 
 }  // namespace
 
+#ifndef DIT_WIDE_MIN_TILES
+#define DIT_WIDE_MIN_TILES 256
+#endif
+
 hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, int M, int N,
                             int K, const EpiParams& ep, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (gemm_wide_supported(epi, A, lda, W, M, N, K, ep) &&
+      ((M + 255) / 256) * (N % 288 == 0 ? N / 288 : N / 256) >= DIT_WIDE_MIN_TILES)
+    return launch_gemm_wide(epi, A, lda, W, M, N, K, ep, s);
   if (K % KSTEP || lda % 8 || (ep.ldw && (ep.ldw % 8 || ep.ldw < K))) return hipErrorInvalidValue;
   if (ep.ksplit < 0 || ep.ksplit % KSTEP || (ep.ksplit && epi != EPI_ATOMIC_F32) ||
       (epi == EPI_ATOMIC_F32 && ep.bias))

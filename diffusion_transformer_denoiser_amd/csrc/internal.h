@@ -4,16 +4,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
-#include <mutex>
-
 #include "common.h"
 #include "dit.h"
-
-// Independent row groups of a call run on this many streams (the caller's and
-// DIT_SPLIT - 1 of the library's own).
-#ifndef DIT_SPLIT
-#define DIT_SPLIT 2
-#endif
 
 struct dit_handle {
   dit_config cfg;
@@ -28,14 +20,6 @@ struct dit_handle {
   int Tf;            // tokens per row of the stream the final layer decodes
   PatchGeom gin, gout;
   PatchGeom gouty;   // gout with T = Tf: the decoder output's row stride
-  // Second stream for the two independent halves of a batch (created on the
-  // first forward, on the device current then), and the fork / join events.
-  // The mutex makes each call's fork-enqueue-join sequence atomic, so calls
-  // from several threads can share them.
-  mutable std::mutex mu;
-  mutable hipStream_t aux[DIT_SPLIT - 1] = {};
-  mutable hipEvent_t ev_fork = nullptr, ev_join[DIT_SPLIT - 1] = {};
-  mutable bool aux_ready = false, aux_failed = false;
 };
 
 namespace dit_host {

@@ -32,15 +32,11 @@
  *     (weights, inputs, outputs, workspace).  They must stay valid until the
  *     enqueued work has completed.  The library never allocates or frees
  *     device memory and never changes the current device.
- *   - Work is enqueued on the caller's stream (a hipStream_t passed as void*;
- *     NULL is the default stream) and never synchronises it.  A device fault
- *     surfaces at the caller's next synchronisation.  A forward without taps
- *     runs half of its rows on a second stream the handle owns (created at
- *     the first forward, default priority, on the device current then),
- *     forked from and joined back into the caller's stream with events: the
- *     call is still ordered after earlier and before later work on the
- *     caller's stream.
- *   - A handle is immutable after dit_create; it may be used from several
+ *   - Work is enqueued on the caller's stream only (a hipStream_t passed as
+ *     void*; NULL is the default stream) and never synchronises it.  A device
+ *     fault surfaces at the caller's next synchronisation.
+ *   - A handle is immutable after dit_create and owns no device resources
+ *     (no streams, events or memory); it may be used from several
  *     threads/streams at once if every call has its own workspace.
  *   - No C++ exception crosses this interface.
  *
@@ -399,9 +395,7 @@ int dit_sample(dit_handle* h, const dit_sampler* sp, float* x, const int32_t* y,
  *   t, y, pooled  device, one entry (row) per sequence, as for dit_forward
  *   out      device: the outputs one after another, each [Cout, F_i, H_i, W_i] fp32
  * Needs the adaLN-Zero design with the 2-D position embedding, 1 <= nseq <= 64
- * and (H_i / p)(W_i / p) a multiple of 32 tokens for every sequence.
- * Like dit_forward, runs the blocks of two groups of sequences (split at about
- * half the tokens) on the caller's stream and the handle's second stream. */
+ * and (H_i / p)(W_i / p) a multiple of 32 tokens for every sequence. */
 int dit_packed_workspace_size(const dit_handle* h, int nseq, const int32_t* seq_fhw,
                               size_t* bytes);
 int dit_forward_packed(dit_handle* h, int nseq, const int32_t* seq_fhw, const void* x,

@@ -218,7 +218,7 @@ def test_zero_gate_block_is_identity_on_gpu():
 
 # --- full-size workloads, sampled rows ------------------------------------------------------------
 
-def _full_size_sampled(name, sample_rows, blocks):
+def _full_size_sampled(name, sample_rows, blocks, oracle_rows=()):
     cfg = dit_inputs.workload(name)
     w = dit_inputs.make_weights(cfg)
     inp = dit_inputs.make_inputs(cfg)
@@ -262,13 +262,24 @@ def _full_size_sampled(name, sample_rows, blocks):
     ep = oracle.unpatchify(Yall, cfg["Cout"], 1, cfg["H"], cfg["W"], cfg["p"])
     ref_out = oracle.cfg_combine(ep[:Bh], ep[Bh:], cfg["scale"], cfg["guided"])
     res["cfg_out"] = rel_l2(out, ref_out)
+    # The call bench.py times: no taps.  Same kernels, same launch sequence,
+    # so the output equals the tapped call's bit for bit; guided rows of it
+    # against the oracle's own guided forward of those rows.
+    out_nt = np_(m.cfg_forward(x, t, y, cfg["scale"], cfg["guided"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(out_nt, out), "untapped forward differs from the tapped one"
+    if oracle_rows:
+        r = list(oracle_rows)
+        ref_g = oracle.cfg_forward(cfg, w, inp["x_t"][r], inp["t"][r], inp["y"][r], cfg["scale"],
+                                   cfg["guided"])
+        res["cfg_forward_untapped"] = rel_l2(out_nt[r], ref_g)
     log(f"  {name} sampled rel-L2: " + ", ".join(f"{k}={v:.2e}" for k, v in res.items()))
     assert res["cfg_out"] <= 1e-6
     assert all(v <= BF16_TOL for v in res.values()), res
 
 
 def test_full_size_xl2_256_cfg_sampled():
-    _full_size_sampled("dit_xl2_256_cfg", [0, 33, 63], blocks=[0, 13, 27])
+    _full_size_sampled("dit_xl2_256_cfg", [0, 33, 63], blocks=[0, 13, 27], oracle_rows=(0, 31))
 
 
 def test_full_size_xl2_512_cfg_sampled():
@@ -322,8 +333,9 @@ def test_video_block_teacher_forced_full_length():
     mod = (rng.standard_normal((1, 6 * d)) * 0.2).astype(np.float32)
     m = _model(cfg, w)
     ob = torch.empty(T, d, device="cuda")
+    fb = torch.empty(T, d, device="cuda")
     Xo = np_(m.block_forward(0, torch.from_numpy(X).cuda(), torch.from_numpy(mod).cuda(),
-                             o_branch=ob))
+                             o_branch=ob, f_branch=fb))
     # oracle on a query subset: q/k/v of every token are needed, outputs only for the sample.
     wl = {kk: w[kk][0] for kk in BLOCK_KEYS}
     sh1, sc1 = mod[:, :d], mod[:, d:2 * d]
@@ -338,15 +350,27 @@ def test_video_block_teacher_forced_full_length():
     qs = np.array([0, 777, 12480, 24959])
     a = oracle.attention(q[:, :, qs], k, v).transpose(0, 2, 1, 3).reshape(1, len(qs), d)
     o_ref = oracle.linear(a, wl["o_w"], wl["o_b"])[0]
+    # the rest of the block is token-local: the residual after the attention
+    # branch, the FFN branch and the block output of the sampled tokens
+    g1, sh2, sc2, g2 = mod[:, 2 * d:3 * d], mod[:, 3 * d:4 * d], mod[:, 4 * d:5 * d], mod[:, 5 * d:]
+    X1 = X[qs].astype(np.float64) + g1 * o_ref
+    h2 = oracle.modulate(oracle.layer_norm(X1[None]), sh2, sc2)
+    f_ref = oracle.linear(oracle.gelu_tanh(oracle.linear(h2, wl["fc1_w"], wl["fc1_b"])),
+                          wl["fc2_w"], wl["fc2_b"])[0]
+    X_ref = X1 + g2 * f_ref
     err = rel_l2(np_(ob)[qs], o_ref)
-    log(f"video full-length block: attention branch sampled rel-L2 {err:.2e}")
-    assert err <= BF16_TOL
+    err_f = rel_l2(np_(fb)[qs], f_ref)
+    err_x = rel_l2(Xo[qs] - X[qs], X_ref - X[qs])
+    log(f"video full-length block sampled rel-L2: attention {err:.2e}, FFN {err_f:.2e}, "
+        f"block increment {err_x:.2e}")
+    assert err <= BF16_TOL and err_f <= BF16_TOL and err_x <= BF16_TOL
     assert np.isfinite(Xo).all()
 
 
-def test_fp32_narrow_decoder_uses_fused_final_layer():
-    """p = 2 gives p^2 Cout = 32 decoder outputs per token: the final LayerNorm,
-    modulation and decoder run fused (one wave per token); fp32 path."""
+def test_fp32_narrow_decoder():
+    """p = 2 gives p^2 Cout = 32 decoder outputs per token (a decoder product
+    narrower than any GEMM tile); fp32 path: final LayerNorm + modulation,
+    then the VALU GEMM with its bias epilogue."""
     cfg = dit_inputs.workload("dit_s8_f32", p=2, N=2)
     w = dit_inputs.make_weights(cfg)
     inp = dit_inputs.make_inputs(cfg)
