@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1389,3 +1390,68 @@ int dit_forward_packed(dit_handle* h, int nseq, const int32_t* seq_fhw, const vo
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Forward without a caller workspace, for callers that cannot allocate device
+// memory: code under HIP graph capture, tight serving loops, harnesses that
+// forbid allocation.  The workspace is a file-scope device array of
+// kNoallocScratchBytes; every GPU the library is loaded on holds its own copy
+// until the process ends.  The host uses only the address that
+// hipGetSymbolAddress returns for the current device (taken at the first call
+// on that device), never the array's name.  Calls on one GPU share the array:
+// calls that overlap on one GPU race.  The forward writes every workspace
+// region before reading it, so nothing needs clearing between calls.
+namespace {
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+namespace {
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DIT_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DIT_EUNSUPPORTED, "device ordinal %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DIT_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return DIT_OK;
+}
+}  // namespace
+
+extern "C" int dit_forward_noalloc(dit_handle* h, const void* x_t, const float* t,
+                                   const int32_t* y, const float* pooled, int B, float* out,
+                                   void* stream) {
+  // Everything dit_forward checks, and the size limit, before any HIP call.
+  if (!h) return fail(DIT_EINVAL, "handle is NULL");
+  if (!x_t || !t || !out) return fail(DIT_EINVAL, "x_t, t and out must be non-NULL");
+  if (h->cond == DIT_COND_MMDIT)
+    return fail(DIT_EUNSUPPORTED, "the MMDiT design has no workspace-free forward");
+  if (B <= 0) return fail(DIT_EINVAL, "B must be positive (got %d)", B);
+  if (h->ncls > 0 && !y) return fail(DIT_EINVAL, "class labels y are required");
+  if (h->cond_dim > 0 && !pooled) return fail(DIT_EINVAL, "pooled conditioning is required");
+  int rc = check_rows(h, B);
+  if (rc) return rc;
+  const size_t need = ws_layout(h, B).total;
+  if (need > kNoallocScratchBytes)
+    return fail(DIT_EWORKSPACE,
+                "B = %d needs %zu bytes of scratch; the static scratch holds %zu (use "
+                "dit_forward with a workspace)", B, need, kNoallocScratchBytes);
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc) return rc;
+  return forward_impl(h, x_t, t, y, pooled, nullptr, B, out, nullptr, ws, kNoallocScratchBytes,
+                      stream);
+}

@@ -194,6 +194,18 @@ class DiT:
         _lib.check(rc)
         return out
 
+    def forward_noalloc(self, x_t, t, y=None, pooled=None, out=None) -> torch.Tensor:
+        """``dit_forward_noalloc``: the forward on the library's static scratch
+        (no workspace tensor is allocated here either when ``out`` is given)."""
+        B = x_t.shape[0]
+        self._check_input(x_t, t, y, pooled, B)
+        if out is None:
+            out = torch.empty(self.out_shape(B), device=self.device, dtype=torch.float32)
+        _lib.check(self.lib.dit_forward_noalloc(self.handle, _ptr(x_t), _ptr(t), _ptr(y),
+                                                _ptr(pooled), B, _ptr(out),
+                                                _stream(self.device)))
+        return out
+
     def forward_ctx(self, x_t, t, pooled, ctx, out=None, taps=None) -> torch.Tensor:
         """MMDiT forward (``dit_forward_ctx``): ctx [B, ctx_len, ctx_dim] text
         embeddings in the model dtype, pooled [B, cond_dim] fp32."""

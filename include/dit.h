@@ -246,6 +246,17 @@ int dit_cfg_forward_taps(dit_handle* h, const void* x_t, const float* t, const i
                          int Bh, float s, int guided_channels, float* out,
                          const dit_taps* taps, void* ws, size_t ws_bytes, void* stream);
 
+/* dit_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  It uses a static scratch array of 64 MiB that the
+ * library holds on every GPU it is loaded on until the process ends (enough
+ * for a DiT-XL/2 256x256 forward of 8 rows).  Calls on one GPU share that
+ * array, so calls that overlap on one GPU race.  It calls no allocator.
+ * DIT_EWORKSPACE when B needs more scratch than that (nothing is launched);
+ * DIT_EUNSUPPORTED for the MMDiT design; otherwise as dit_forward. */
+int dit_forward_noalloc(dit_handle* h, const void* x_t, const float* t, const int32_t* y,
+                        const float* pooled, int B, float* out, void* stream);
+
 const char* dit_status_string(int status);
 const char* dit_last_error_message(void);
 

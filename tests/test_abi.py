@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
               "dit_sampler_step", "dit_sample_workspace_size", "dit_sample",
               "dit_packed_workspace_size", "dit_forward_packed", "dit_forward_ctx",
               "dit_train_param_count", "dit_train_param_layout", "dit_train_workspace_size",
-              "dit_train_step"):
+              "dit_train_step", "dit_forward_noalloc"):
         assert n in names
     assert set(names) == set(_lib.EXPORTS), "binding and header disagree"
 
@@ -191,6 +191,13 @@ def test_forward_validates_before_launch():
         assert lib.dit_cfg_forward(h, p, p, p, 32, float("nan"), 4, p, p, need.value, None) == _lib.DIT_EINVAL
         assert lib.dit_cfg_forward(h, p, p, p, 33, 1.5, 4, p, p, need.value, None) == _lib.DIT_EWORKSPACE
         assert lib.dit_block_forward(h, 2, 4, p, p, p, None, None, p, need.value, None) == _lib.DIT_EINVAL
+        # the workspace-free forward: the same checks, and 64 rows need more
+        # than its static scratch (refused before any HIP call)
+        assert lib.dit_forward_noalloc(h, p, p, p, None, 0, p, None) == _lib.DIT_EINVAL
+        assert lib.dit_forward_noalloc(h, None, p, p, None, 4, p, None) == _lib.DIT_EINVAL
+        assert lib.dit_forward_noalloc(h, p, p, None, None, 4, p, None) == _lib.DIT_EINVAL
+        assert lib.dit_forward_noalloc(h, p, p, p, None, 64, p, None) == _lib.DIT_EWORKSPACE
+        assert lib.dit_forward_noalloc(None, p, p, p, None, 4, p, None) == _lib.DIT_EINVAL
     finally:
         lib.dit_destroy(h)
 
