@@ -8,16 +8,23 @@ T = 256, d = 1152, 28 blocks, 16 heads), guidance scale 1.5 on all 4 noise
 channels; seeded synthetic inputs and N(0, 0.02) weights, resident in HBM
 before timing starts.  Prints one JSON line.
 
-Besides the headline number the line carries
-  roofline      the dominant kernel, timed alone with HIP events on the same
-                stream and launch configuration as in the forward pass, right
-                after the forward loop (at the same sustained clocks);
-  cpu_baseline  the fp64 oracle on a bounded sample of the same workload, on
-                this host's cores.
+Besides the headline number (K timed steps; the median of five more repeats
+of K steps is reported beside it) the line carries
+  kernels       every hot kernel of the forward timed alone with HIP events on
+                the stream it is launched on, at the forward's shapes and with
+                the forward's per-block weights, right after the forward loop
+                (at the same sustained clocks): average launch time, launches
+                per forward, algorithmic TFLOP/s and GB/s and their fractions
+                of the MI355X peaks;
+  roofline      the entry of that list with the largest time per forward;
+  peaks         the published peaks used, and CU count x max engine clock x
+                4096 bf16 FLOP per clock per CU read from rocminfo;
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload on
+                this host's cores, extrapolated to whole forwards (CPU model,
+                BLAS library and thread count stated).
 
 Other modes (same JSON line, their own metric):
-  --workload NAME   another forward configuration (its dominant kernel is fc1,
-                    or attention at T >= 4096); --skip-cpu-baseline for long ones
+  --workload NAME   another forward configuration; --skip-cpu-baseline for long ones
   --train           one dit_train_step per step at DiT-XL/2 batch 256; roofline
                     of the weight-gradient kernel (dit_linear_wgrad)
   --sample KIND     whole dit_sample loops (ddpm, dpmpp_2m, rf_euler)
@@ -29,6 +36,9 @@ import argparse
 import json
 import math
 import os
+import re
+import statistics
+import subprocess
 import sys
 import time
 
@@ -38,9 +48,10 @@ if ROOT not in sys.path:
 
 import numpy as np  # noqa: E402
 
-PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
-PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 METRIC = "DiT-XL/2 denoiser forwards/s + TFLOP/s (% MFMA peak) on 1 MI355X"
+REPEATS = 5
 
 
 def parse():
@@ -49,8 +60,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dit_xl2_256_cfg")
-    ap.add_argument("--kernel-launches", type=int, default=200,
-                    help="launches of the dominant kernel timed alone (after as many untimed)")
+    ap.add_argument("--kernel-launches", type=int, default=50,
+                    help="launches of each hot kernel timed alone (after a few untimed ones)")
+    ap.add_argument("--repeats", type=int, default=REPEATS,
+                    help="extra repeats of the K timed steps (their median is reported)")
     ap.add_argument("--cpu-rows", type=int, default=2,
                     help="guided rows of the workload the oracle runs for the CPU baseline")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
@@ -67,6 +80,100 @@ def parse():
                          "of 32x32 and 4 of 64x64 in one call, against the same work as two "
                          "batched calls")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Work counts (measurement only).
+
+def gmac_per_row(cfg) -> float:
+    """Multiply-accumulates (10^9) of one row's forward: every matrix product
+    (patch embedding, timestep MLP, pooled projection, per-block modulation,
+    q | k | v, attention scores and weighted sum, output projection, FFN, final
+    modulation, decoder), the unit of the conditioning-methods table of itwiki
+    "확산 트랜스포머" (118.6 for DiT-XL/2 at 256x256).  In-context rows carry two
+    more tokens and no modulation; cross-attention adds a query and an output
+    projection per token, key/value projections of two context tokens and
+    attention over them; MMDiT runs both streams' products and joint
+    attention."""
+    d, N = cfg["d"], cfg["N"]
+    T = (cfg["F"] // cfg["pt"]) * (cfg["H"] // cfg["p"]) * (cfg["W"] // cfg["p"])
+    r = cfg["mlp_hidden"] / d
+    kin = cfg["pt"] * cfg["p"] ** 2 * cfg["C"]
+    kout = cfg["pt"] * cfg["p"] ** 2 * cfg["Cout"]
+    cond = cfg.get("conditioning", 0)
+    per_tok = (4 + 2 * r) * d * d            # q | k | v, output projection, FFN
+    front = T * kin * d + cfg["freq_dim"] * d + d * d + cfg.get("cond_dim", 0) * d
+    back = T * d * kout
+    if cond == 3:                            # MMDiT: image + text streams, joint attention
+        J = T + cfg["ctx_len"]
+        blocks = N * (J * per_tok + 2 * J * J * d + 12 * d * d)
+        front += cfg["ctx_len"] * cfg["ctx_dim"] * d
+        back += 2 * d * d
+    elif cond == 1:                          # in-context: two more tokens, no modulation
+        T2 = T + 2
+        blocks = N * (T2 * per_tok + 2 * T2 * T2 * d)
+    elif cond == 2:                          # cross-attention: no modulation
+        blocks = N * (T * per_tok + 2 * T * T * d + 2 * T * d * d + 4 * d * d + 4 * T * d)
+    else:                                    # adaLN-Zero
+        blocks = N * (T * per_tok + 2 * T * T * d + 6 * d * d)
+        back += 2 * d * d
+    return (blocks + front + back) / 1e9
+
+
+def tokens_of(cfg) -> int:
+    return (cfg["F"] // cfg["pt"]) * (cfg["H"] // cfg["p"]) * (cfg["W"] // cfg["p"])
+
+
+# ---------------------------------------------------------------------------
+# Machine facts (printed beside the numbers).
+
+def rocminfo_peak():
+    """(compute units, max engine clock MHz, bf16 TFLOP/s = CUs x clock x 4096)
+    of the first gfx950 agent in rocminfo, or None."""
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except Exception:
+        return None
+    for block in txt.split("Agent ")[1:]:
+        if "gfx950" not in block:
+            continue
+        cu = re.search(r"Compute Unit:\s+(\d+)", block)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", block)
+        if cu and mhz:
+            cus, clk = int(cu.group(1)), int(mhz.group(1))
+            return cus, clk, round(cus * clk * 1e6 * 4096 / 1e12, 1)
+    return None
+
+
+def cpu_facts():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:
+        pass
+    return model, blas
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
 
 
 def measured_traffic(rec_name: str, src_rel: str, kernel: str, shape):
@@ -87,16 +194,8 @@ def measured_traffic(rec_name: str, src_rel: str, kernel: str, shape):
     return int(rec["traffic_bytes"])
 
 
-def blas_threads() -> int:
-    try:
-        from threadpoolctl import threadpool_info
-        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
-        if n:
-            return int(max(n))
-    except Exception:
-        pass
-    return os.cpu_count() or 1
-
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle (the only use of oracle/ here).
 
 def cpu_baseline_mmdit(cfg, w, inp, rows: int, trunk_rows: int):
     """fp64 oracle on `rows` of the MMDiT workload's rows."""
@@ -106,26 +205,191 @@ def cpu_baseline_mmdit(cfg, w, inp, rows: int, trunk_rows: int):
                          inp["pooled"][:rows])
     dt = time.perf_counter() - t0
     return {"value": rows / trunk_rows / dt, "unit": "forwards/s", "cores": blas_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "extrapolated": True,
             "sample": f"oracle.mmdit_forward (fp64 NumPy) on {rows} of {trunk_rows} rows (all "
                       f"{cfg['N']} blocks): {dt:.2f} s; value scaled to whole {trunk_rows}-row "
                       f"forwards"}
+
+
+def cpu_baseline_video(cfg, w, inp):
+    """fp64 oracle for the spacetime workload: the embedding and conditioning,
+    one full-length block (attention over all T tokens, in query chunks) and
+    the final layer, timed on this host; the forward is extrapolated as
+    embed + N x block + final."""
+    import oracle
+    d, N = cfg["d"], cfg["N"]
+    t0 = time.perf_counter()
+    _, _, c = oracle.embed_condition(cfg, w, inp["t"], None, inp["pooled"])
+    mod = oracle.modulation(cfg, w, c)
+    P = oracle.patchify(inp["x_t"], cfg["p"], cfg["pt"])
+    X = oracle.linear(P, w["pe_w"], w["pe_b"])
+    t_embed = time.perf_counter() - t0
+    rope = oracle.rope3d_tables(cfg["F"] // cfg["pt"], cfg["H"] // cfg["p"], cfg["W"] // cfg["p"],
+                                d // cfg["heads"])
+    t0 = time.perf_counter()
+    X, _, _ = oracle.block(cfg, oracle.block_weights(w, 0), X, mod[:, :6 * d], rope)
+    t_block = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    fb = 6 * d * N
+    H = oracle.modulate(oracle.layer_norm(X), mod[:, fb:fb + d], mod[:, fb + d:fb + 2 * d])
+    oracle.linear(H, w["out_w"], w["out_b"])
+    t_final = time.perf_counter() - t0
+    total = t_embed + N * t_block + t_final
+    return {"value": 1.0 / total, "unit": "forwards/s", "cores": blas_threads(), "kind": "oracle",
+            "extrapolated": True,
+            "sample": f"oracle (fp64 NumPy): embedding {t_embed:.2f} s + one full-length block "
+                      f"(T = {tokens_of(cfg)}, attention in 2048-query chunks) {t_block:.2f} s "
+                      f"x {N} blocks + final layer {t_final:.2f} s = {total:.1f} s per forward "
+                      f"(extrapolated from one block)"}
 
 
 def cpu_baseline(cfg, w, inp, rows: int, trunk_rows: int):
     """fp64 oracle on `rows` guided rows (2*rows trunk rows) of the workload."""
     import oracle
     if cfg.get("conditioning", 0) == 3:
-        return cpu_baseline_mmdit(cfg, w, inp, rows, trunk_rows)
-    t0 = time.perf_counter()
-    oracle.cfg_forward(cfg, w, inp["x_t"][:rows], inp["t"][:rows], inp["y"][:rows],
-                       cfg["scale"], cfg["guided"])
-    dt = time.perf_counter() - t0
-    frac = (2 * rows) / trunk_rows
-    return {"value": frac / dt, "unit": "forwards/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"oracle.cfg_forward (fp64 NumPy) on {rows} of {trunk_rows // 2} guided rows "
-                      f"({2 * rows} of {trunk_rows} trunk rows, all 28 blocks): {dt:.2f} s; "
-                      f"value scaled to whole {trunk_rows}-row forwards"}
+        r = cpu_baseline_mmdit(cfg, w, inp, rows, trunk_rows)
+    elif tokens_of(cfg) >= 4096:
+        r = cpu_baseline_video(cfg, w, inp)
+    elif cfg["cfg"]:
+        t0 = time.perf_counter()
+        oracle.cfg_forward(cfg, w, inp["x_t"][:rows], inp["t"][:rows], inp["y"][:rows],
+                           cfg["scale"], cfg["guided"])
+        dt = time.perf_counter() - t0
+        frac = (2 * rows) / trunk_rows
+        r = {"value": frac / dt, "unit": "forwards/s", "cores": blas_threads(), "kind": "oracle",
+             "extrapolated": True,
+             "sample": f"oracle.cfg_forward (fp64 NumPy) on {rows} of {trunk_rows // 2} guided "
+                       f"rows ({2 * rows} of {trunk_rows} trunk rows, all {cfg['N']} blocks): "
+                       f"{dt:.2f} s; value scaled to whole {trunk_rows}-row forwards"}
+    else:
+        t0 = time.perf_counter()
+        oracle.forward(cfg, w, inp["x_t"][:rows], inp["t"][:rows],
+                       None if inp.get("y") is None else inp["y"][:rows],
+                       None if inp.get("pooled") is None else inp["pooled"][:rows])
+        dt = time.perf_counter() - t0
+        r = {"value": rows / trunk_rows / dt, "unit": "forwards/s", "cores": blas_threads(),
+             "kind": "oracle", "extrapolated": True,
+             "sample": f"oracle.forward (fp64 NumPy) on {rows} of {trunk_rows} rows (all "
+                       f"{cfg['N']} blocks): {dt:.2f} s; value scaled to whole forwards"}
+    model, blas = cpu_facts()
+    r["cpu_model"] = model
+    r["blas"] = blas
+    return r
+
+
+# ---------------------------------------------------------------------------
+# Hot kernels timed alone.
+
+def time_launches(fn, n, stream):
+    """Average ms of one launch of fn over n launches (after 3 untimed), HIP
+    events on `stream` (the stream the library launches on)."""
+    import torch
+    for i in range(3):
+        fn(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def kernel_table(cfg, model, rows, n_launch, dev):
+    """The forward's hot kernels at its shapes, each timed alone: the four
+    block products (wide-tile MFMA GEMM with the forward's epilogue), attention
+    and LayerNorm + modulate.  Consecutive GEMM launches cycle through the
+    model's per-block weights, as the forward does, so no launch finds its
+    weight matrix already cached."""
+    import torch
+    import diffusion_transformer_denoiser_amd as dm
+    d, hid, H, N = cfg["d"], cfg["mlp_hidden"], cfg["heads"], cfg["N"]
+    T = model.Tt
+    M = rows * T
+    dt = dm.torch_dtype(cfg["dtype"])
+    es = 2 if dt == torch.bfloat16 else 4
+    stream = torch.cuda.current_stream(dev)
+    tw = model.tensors
+    g = torch.Generator(device=dev).manual_seed(7)
+    out = []
+
+    def entry(name, kernel, n_per_fwd, ms, flop, nbytes):
+        t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12) if flop else 0.0
+        t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+        bound = "mfma" if t_mfma >= t_hbm else "hbm"
+        tf = flop / (ms * 1e-3) / 1e12 if flop else None
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out.append({"name": name, "kernel": kernel, "launches_per_forward": n_per_fwd,
+                    "avg_launch_us": round(ms * 1e3, 2),
+                    "us_per_forward": round(ms * 1e3 * n_per_fwd, 1), "bound": bound,
+                    "tflops": round(tf, 1) if tf else None,
+                    "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4) if tf else None,
+                    "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "algorithmic_flop": flop, "algorithmic_bytes": nbytes})
+
+    Hb = torch.randn(M, d, device=dev, generator=g).to(dt)
+    Gb = torch.randn(M, hid, device=dev, generator=g).to(dt)
+    X = torch.randn(M, d, device=dev, generator=g)
+    gate = torch.randn((M + T - 1) // T, d, device=dev, generator=g) * 0.1
+    nb = N
+
+    def gemm(name, epi, A, Wkey, bkey, n_out, n_in, outbuf, gated):
+        Ws = [tw[Wkey][l] for l in range(nb)]
+        bs = [tw[bkey][l] for l in range(nb)]
+        if gated:
+            fn = lambda i: dm.linear(epi, A, Ws[i % nb], bs[i % nb], outbuf, gate=gate,
+                                     gate_stride=d, T=T)
+        else:
+            fn = lambda i: dm.linear(epi, A, Ws[i % nb], bs[i % nb], outbuf)
+        ms = time_launches(fn, n_launch, stream)
+        flop = 2.0 * M * n_out * n_in
+        ob = M * n_out * (4 if gated else es) * (2 if gated else 1)   # gated: read + write X
+        nbytes = M * n_in * es + n_out * n_in * es + n_out * 4 + ob
+        epin = {dm.DIT_EPI_BIAS_DT: "bias", dm.DIT_EPI_GELU: "bias + tanh-GELU",
+                dm.DIT_EPI_GATED: "bias + gated fp32 residual"}[epi]
+        entry(name, f"{name}: GEMM M={M} N={n_out} K={n_in}, {epin} epilogue", nb, ms, flop,
+              nbytes)
+
+    qkv = torch.empty(M, 3 * d, device=dev, dtype=dt)
+    G = torch.empty(M, hid, device=dev, dtype=dt)
+    gemm("qkv", dm.DIT_EPI_BIAS_DT, Hb, "qkv_w", "qkv_b", 3 * d, d, qkv, False)
+    gemm("out_proj", dm.DIT_EPI_GATED, Hb, "o_w", "o_b", d, d, X, True)
+    gemm("fc1", dm.DIT_EPI_GELU, Hb, "fc1_w", "fc1_b", hid, d, G, False)
+    gemm("fc2", dm.DIT_EPI_GATED, Gb, "fc2_w", "fc2_b", d, hid, X, True)
+    del G
+    # attention over the packed q | k | v of every row
+    qkv.normal_(generator=g)
+    dh = d // H
+    ms = time_launches(lambda i: dm.attention(qkv.view(rows, T, 3 * d), H), n_launch, stream)
+    entry("attention", f"attention: {rows} rows x {H} heads, T={T}, dh={dh}", N, ms,
+          4.0 * rows * H * T * T * dh, rows * T * 4 * d * es)
+    # LayerNorm + modulate (two per block and the final layer's)
+    mod = torch.randn(rows, 6 * d, device=dev, generator=g) * 0.1
+    Hn = torch.empty(M, d, device=dev, dtype=dt)
+    ms = time_launches(lambda i: dm.ln_modulate(X, mod, 0, d, T, Hn), n_launch, stream)
+    entry("layernorm", f"LayerNorm + modulate: M={M}, d={d}", 2 * N + 1, ms, 0.0,
+          M * d * (4 + es) + rows * 2 * d * 4)
+    del Hb, Gb, X, qkv, Hn
+    return out
+
+
+def roofline_of(top, traffic=None):
+    flop_bound = top["bound"] == "mfma"
+    r = {"bound": top["bound"],
+         "achieved": top["tflops"] if flop_bound else top["gbs"],
+         "peak": PEAK_BF16_TFLOPS if flop_bound else PEAK_HBM_GBS,
+         "unit": "TFLOP/s" if flop_bound else "GB/s",
+         "frac": top["mfma_frac"] if flop_bound else top["hbm_frac"],
+         "traffic": traffic,
+         "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE)",
+         "algorithmic_bytes": top["algorithmic_bytes"],
+         "kernel": top["kernel"],
+         "avg_launch_ms": round(top["avg_launch_us"] / 1e3, 5)}
+    if traffic:
+        gbs = traffic / (top["avg_launch_us"] * 1e-6) / 1e9
+        r["hbm_gbs"] = round(gbs, 1)
+        r["hbm_frac"] = round(gbs / PEAK_HBM_GBS, 4)
+    return r
 
 
 def train_main(args, cfg, model, dev):
@@ -133,7 +397,6 @@ def train_main(args, cfg, model, dev):
     activations, loss, backward, AdamW + EMA) on one batch resident in HBM."""
     import torch
     import dit_inputs
-    from oracle import flops as oflops
 
     B = cfg["batch"]
     inp = dit_inputs.make_train_inputs(cfg)
@@ -158,7 +421,7 @@ def train_main(args, cfg, model, dev):
     lv = loss.cpu().tolist()
     assert all(math.isfinite(v) for v in lv), "non-finite loss"
     # forward MACs x 3 (the backward computes two products per forward product)
-    flop_step = 3 * 2.0 * oflops.gmac_for(cfg) * 1e9 * B
+    flop_step = 3 * 2.0 * gmac_per_row(cfg) * 1e9 * B
 
     # Dominant kernel of the step: the weight-gradient product (TN MFMA GEMM
     # over the row-major saved activations, split along the token reduction,
@@ -245,7 +508,6 @@ def sample_main(args, cfg, model, dev):
     import torch
     import dit_inputs
     import diffusion_transformer_denoiser_amd as dm
-    from oracle import flops as oflops
 
     S = args.sample_steps
     Bh = cfg["batch"]
@@ -309,7 +571,7 @@ def sample_main(args, cfg, model, dev):
     per = {"ddpm": 4 * (3 + (1 if learned else 0)) + 4, "dpmpp_2m": 4 * 2 + 4 + 4,
            "rf_euler": 4 * 2 + 4}[args.sample]
     gbs = per * n_el / (kms * 1e-3) / 1e9
-    gmac_row = oflops.gmac_for(cfg)
+    gmac_row = gmac_per_row(cfg)
     flop_loop = 2.0 * gmac_row * 1e9 * rows * S
     line = {
         "metric": f"DiT sampling loop images/s ({args.sample}, {S} steps) on 1 MI355X",
@@ -343,7 +605,6 @@ def packed_main(args, cfg, model, dev):
     import torch
     import dit_inputs
     import diffusion_transformer_denoiser_amd as dm
-    from oracle import flops as oflops
 
     shapes = ([(64, 64)] + [(32, 32)] * 4) * 4
     rng = np.random.default_rng(4242)
@@ -381,7 +642,7 @@ def packed_main(args, cfg, model, dev):
         torch.cuda.synchronize()
         res[name] = e0.elapsed_time(e1) / args.steps
     tokens = sum((h // cfg["p"]) * (w // cfg["p"]) for h, w in shapes)
-    gmac = sum(oflops.gmac_for(dict(cfg, H=h, W=w)) for h, w in shapes)
+    gmac = sum(gmac_per_row(dict(cfg, H=h, W=w)) for h, w in shapes)
     ms = res["packed"]
     line = {
         "metric": "DiT-XL/2 packed mixed-resolution forward tokens/s on 1 MI355X",
@@ -402,6 +663,112 @@ def packed_main(args, cfg, model, dev):
     print(json.dumps(line), flush=True)
 
 
+def forward_main(args, cfg, model, dev, w, inp, x, t, y, pooled, ctx, out):
+    import torch
+    import dit_inputs
+    mmdit = cfg.get("conditioning", 0) == dit_inputs.COND_MMDIT
+    Bh = cfg["batch"]
+    rows = 2 * Bh if cfg["cfg"] else Bh
+
+    def step():
+        if mmdit:
+            model.forward_ctx(x, t, pooled, ctx, out=out)
+        elif cfg["cfg"]:
+            model.cfg_forward(x, t, y, cfg["scale"], cfg["guided"], out=out)
+        else:
+            model.forward(x, t, y, pooled, out=out)
+
+    def timed(k):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        ev0.record()
+        for _ in range(k):
+            step()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / k, time.perf_counter() - wall0
+
+    for _ in range(args.warmup):
+        step()
+    ms, wall = timed(args.steps)               # the contract's K timed steps
+    reps = [timed(args.steps)[0] for _ in range(args.repeats)]
+    assert torch.isfinite(out).all().item(), "non-finite output"
+
+    T = model.Tt
+    kernels = [] if mmdit else kernel_table(cfg, model, rows, args.kernel_launches, dev)
+    roofline = None
+    if kernels:
+        top = max(kernels, key=lambda k: k["us_per_forward"])
+        shape = {"qkv": (rows * T, 3 * cfg["d"], cfg["d"]), "out_proj": (rows * T, cfg["d"], cfg["d"]),
+                 "fc1": (rows * T, cfg["mlp_hidden"], cfg["d"]),
+                 "fc2": (rows * T, cfg["d"], cfg["mlp_hidden"])}.get(top["name"])
+        traffic = None
+        if shape:
+            traffic = measured_traffic(f"gemm_{top['name']}_hbm_counters.json",
+                                       "diffusion_transformer_denoiser_amd/csrc/gemm_wide.hip",
+                                       "gemm_wide_kernel", shape)
+        roofline = roofline_of(top, traffic)
+
+    if args.copy_mib:   # calibration copy for the HBM byte counters
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.skip_cpu_baseline:
+        cpu = cpu_baseline(cfg, w, inp, min(args.cpu_rows, Bh), rows)
+
+    flop_fwd = 2.0 * gmac_per_row(cfg) * 1e9 * rows
+    tflops = flop_fwd / (ms * 1e-3) / 1e12
+    peak_rocm = rocminfo_peak()
+    med = statistics.median(reps) if reps else ms
+    line = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms, 3),
+        "unit": "forwards/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg["dtype"] == dit_inputs.DTYPE_BF16 else "f32",
+        "data": ("synthetic (seeded N(0,1) latents and text embeddings, U(0,1) t, N(0,1) "
+                 "pooled vector, N(0,0.02) weights)" if mmdit else
+                 "synthetic (seeded N(0,1) latents, U(0,1) flow time, N(0,1) pooled vector, "
+                 "N(0,0.02) weights)" if cfg["cond_dim"] else
+                 "synthetic (seeded N(0,1) latents, U{0..999} t and labels, N(0,0.02) weights)"),
+        "config": ({"workload": cfg["name"], "rows": rows, "image_tokens": tokens_of(cfg),
+                    "text_tokens": cfg["ctx_len"], "parallelism": "single GPU"} if mmdit else
+                   {"workload": cfg["name"], "guided_rows": Bh if cfg["cfg"] else 0,
+                    "trunk_rows": rows, "tokens": tokens_of(cfg),
+                    "guidance_scale": cfg["scale"], "guided_channels": cfg["guided"],
+                    "parallelism": "single GPU"}),
+        "tflops": round(tflops, 1),
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "tokens_per_s": round(rows * T * 1000.0 / ms, 1),
+        "images_per_s": round(Bh * 1000.0 / ms, 1),
+        "gflop_per_forward": round(flop_fwd / 1e9, 1),
+        "wall_s_timed": round(wall, 3),
+        "repeats_ms_per_step": [round(r, 4) for r in reps],
+        "median_of_repeats": {"ms_per_step": round(med, 4), "value": round(1000.0 / med, 3),
+                              "tflops": round(flop_fwd / (med * 1e-3) / 1e12, 1)},
+        "peaks": {"bf16_tflops_published": PEAK_BF16_TFLOPS, "hbm_gbs_published": PEAK_HBM_GBS,
+                  "rocminfo": ({"compute_units": peak_rocm[0], "max_sclk_mhz": peak_rocm[1],
+                                "bf16_tflops_cu_x_clk_x_4096": peak_rocm[2]}
+                               if peak_rocm else None)},
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -413,7 +780,6 @@ def main():
     import torch
     import dit_inputs
     import diffusion_transformer_denoiser_amd as dm
-    from oracle import flops as oflops   # closed-form MAC count (numbers only)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dm.load()
@@ -422,8 +788,6 @@ def main():
         args.workload = "dit_xl2_256_train"
     cfg = dit_inputs.workload(args.workload)
     Bh = cfg["batch"]
-    rows = 2 * Bh if cfg["cfg"] else Bh
-    T = dit_inputs.tokens(cfg)
     w = dit_inputs.make_weights(cfg)
     mmdit = cfg.get("conditioning", 0) == dit_inputs.COND_MMDIT
     inp = dit_inputs.make_mmdit_inputs(cfg) if mmdit else dit_inputs.make_inputs(cfg)
@@ -442,144 +806,7 @@ def main():
         return train_main(args, cfg, model, dev)
     if args.packed:
         return packed_main(args, cfg, model, dev)
-
-    def step():
-        if mmdit:
-            model.forward_ctx(x, t, pooled, ctx, out=out)
-        elif cfg["cfg"]:
-            model.cfg_forward(x, t, y, cfg["scale"], cfg["guided"], out=out)
-        else:
-            model.forward(x, t, y, pooled, out=out)
-
-    # Dominant kernel: the FFN up-projection (N = 4d, K = d, bias + tanh-GELU epilogue), the
-    # same MFMA kernel, tile and shape as in the forward pass, timed alone.  The forward runs
-    # the two halves of its rows on two streams, so each launch there covers M = rows/2 * T.
-    # Its buffers are set up before the forward is timed, and it is timed right after the
-    # forward loop, with a warm-up of its own, so it runs at the same sustained clocks as
-    # inside the forward (an idle GPU needs ~0.1 s of load to reach them).
-    # Consecutive launches cycle through the model's per-block weights, as the forward does,
-    # so no launch finds its weight matrix already cached.
-    d, hid = cfg["d"], cfg["mlp_hidden"]
-    # (MMDiT: the image stream's fc1, its largest)
-    M = (rows // 2 if rows >= 2 else rows) * (model.Tf if mmdit else model.Tt)
-    A = torch.randn(M, d, device=dev).to(dt)
-    W1 = [model.tensors["fc1_w"][l] for l in range(cfg["N"])]
-    b1 = [model.tensors["fc1_b"][l] for l in range(cfg["N"])]
-    G = torch.empty(M, hid, device=dev, dtype=dt)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    nb = len(W1)
-    # At video length (T >= 4096) attention, not the FFN, dominates the forward; its
-    # kernel is timed alone instead, on one row half's q | k | v.
-    attn_dom = T >= 4096 and not mmdit
-    if attn_dom:
-        Ba, H = (rows // 2 if rows >= 2 else rows), cfg["heads"]
-        qkvs = [torch.randn(Ba, model.Tt, 3 * d, device=dev).to(dt) for _ in range(2)]
-        del A, G
-        def kernel(i):
-            dm.attention(qkvs[i % 2], H)
-    else:
-        def kernel(i):
-            dm.linear(dm.DIT_EPI_GELU, A, W1[i % nb], b1[i % nb], G)
-    for i in range(args.kernel_launches):
-        kernel(i)
-    k0.record()
-    for i in range(args.kernel_launches):
-        kernel(i)
-    k1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    kms = k0.elapsed_time(k1) / args.kernel_launches
-    assert torch.isfinite(out).all().item(), "non-finite output"
-
-    gmac_row = oflops.gmac_for(cfg)
-    flop_fwd = 2.0 * gmac_row * 1e9 * rows
-    tflops = flop_fwd / (ms * 1e-3) / 1e12
-    if attn_dom:
-        dh = d // H
-        kflop = 4.0 * Ba * H * model.Tt * model.Tt * dh
-        k_tflops = kflop / (kms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
-                    "traffic": None,
-                    "algorithmic_bytes": Ba * model.Tt * (3 * d + d) * 2,
-                    "kernel": f"attn_bf16_kernel<{dh}> (attention of {Ba} row(s): H={H}, "
-                              f"T={model.Tt}, dh={dh})",
-                    "avg_launch_ms": round(kms, 4)}
-    else:
-        kflop = 2.0 * M * hid * d
-        k_tflops = kflop / (kms * 1e-3) / 1e12
-        traffic = measured_traffic("gemm_fc1_hbm_counters.json",
-                                   "diffusion_transformer_denoiser_amd/csrc/gemm_mfma.hip",
-                                   "gemm_bf16_kernel<5, 128, 192, 64, 2, 1, 1, 1>", (M, hid, d))
-        roofline = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic,
-                    "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE)",
-                    "algorithmic_bytes": (M * d + hid * d) * 2 + hid * 4 + M * hid * 2,
-                    "kernel": f"gemm_bf16_kernel<EPI_GELU,128,192,64> (FFN fc1 of one row half: "
-                              f"M={M}, N={hid}, K={d})",
-                    "avg_launch_ms": round(kms, 4)}
-        if traffic:   # counter-measured HBM bytes over the HIP-event launch time
-            roofline["hbm_gbs"] = round(traffic / (kms * 1e-3) / 1e9, 1)
-            roofline["hbm_frac"] = round(traffic / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-
-    if args.copy_mib:
-        n = args.copy_mib * (1 << 20) // 4
-        src = torch.randn(n, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-
-    cpu = None
-    if not args.skip_cpu_baseline:
-        cpu = cpu_baseline(cfg, w, inp, min(args.cpu_rows, Bh), rows)
-
-    line = {
-        "metric": METRIC,
-        "value": round(1000.0 / ms, 3),
-        "unit": "forwards/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if cfg["dtype"] == dit_inputs.DTYPE_BF16 else "f32",
-        "data": ("synthetic (seeded N(0,1) latents and text embeddings, U(0,1) t, N(0,1) "
-                 "pooled vector, N(0,0.02) weights)" if mmdit else
-                 "synthetic (seeded N(0,1) latents, U(0,1) flow time, N(0,1) pooled vector, "
-                 "N(0,0.02) weights)" if cfg["cond_dim"] else
-                 "synthetic (seeded N(0,1) latents, U{0..999} t and labels, N(0,0.02) weights)"),
-        "config": ({"workload": cfg["name"], "rows": rows, "image_tokens": T,
-                    "text_tokens": cfg["ctx_len"], "parallelism": "single GPU"} if mmdit else
-                   {"workload": cfg["name"], "guided_rows": Bh, "trunk_rows": rows, "tokens": T,
-                    "guidance_scale": cfg["scale"], "guided_channels": cfg["guided"],
-                    "parallelism": "single GPU"}),
-        "tflops": round(tflops, 1),
-        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "tokens_per_s": round(rows * model.Tt * 1000.0 / ms, 1),
-        "images_per_s": round(Bh * 1000.0 / ms, 1),
-        "gflop_per_forward": round(flop_fwd / 1e9, 1),
-        "wall_s_timed": round(wall, 3),
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(line), flush=True)
+    return forward_main(args, cfg, model, dev, w, inp, x, t, y, pooled, ctx, out)
 
 
 if __name__ == "__main__":

@@ -6,7 +6,7 @@ the library's kernels.  Importing the package does not load the library;
 ``DiT(...)`` and the standalone functions do, and fail loudly if it has not
 been built.
 """
-from ._lib import (DIT_BF16, DIT_EPI_ACCUM, DIT_EPI_BIAS, DIT_EPI_GATED, DIT_EPI_GELU, DIT_F32,  # noqa: F401
-                   DitError, load)
-from .model import (DiT, Sampler, attention, config_struct, linear, linear_wgrad, patchify,  # noqa: F401
-                    timestep_embed, torch_dtype, unpatchify, upload)
+from ._lib import (DIT_BF16, DIT_EPI_ACCUM, DIT_EPI_BIAS, DIT_EPI_BIAS_DT, DIT_EPI_GATED,  # noqa: F401
+                   DIT_EPI_GELU, DIT_F32, DitError, load)
+from .model import (DiT, Sampler, attention, config_struct, linear, linear_wgrad,  # noqa: F401
+                    ln_modulate, patchify, timestep_embed, torch_dtype, unpatchify, upload)

@@ -1106,6 +1106,7 @@ int dit_linear(int epilogue, const void* A, const void* W, const float* bias, in
     case DIT_EPI_GELU: epi = EPI_GELU; break;
     case DIT_EPI_GATED: epi = EPI_GATED; break;
     case DIT_EPI_ACCUM: epi = EPI_ATOMIC_F32; break;
+    case DIT_EPI_BIAS_DT: epi = EPI_BIAS_DT; break;
     default: return fail(DIT_EINVAL, "unknown epilogue %d", epilogue);
   }
   if (epilogue == DIT_EPI_ACCUM && bias)
@@ -1130,6 +1131,21 @@ int dit_linear(int epilogue, const void* A, const void* W, const float* bias, in
   return ok();
 }
 
+int dit_ln_modulate(const float* X, int M, int T, int d, const float* mod, int mod_stride,
+                    int shift_off, int scale_off, float eps, void* H, int dtype, void* stream) {
+  if (!X || !mod || !H) return fail(DIT_EINVAL, "X, mod and H must be non-NULL");
+  if (M <= 0 || T <= 0 || d <= 0) return fail(DIT_EINVAL, "M, T, d must be positive");
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return fail(DIT_EINVAL, "dtype");
+  if (mod_stride < 0 || shift_off < 0 || scale_off < 0 ||
+      (mod_stride > 0 && (shift_off + d > mod_stride || scale_off + d > mod_stride)))
+    return fail(DIT_EINVAL, "the shift / scale vectors must lie inside a modulation row");
+  if (d % 128 || d > 2048 || !(eps > 0.0f))
+    return fail(DIT_EUNSUPPORTED, "LayerNorm width must be a multiple of 128 up to 2048, eps > 0");
+  DIT_HIP(launch_ln_modulate(X, M, T, d, mod, mod_stride, shift_off, scale_off, eps, H, dtype,
+                             (hipStream_t)stream));
+  return ok();
+}
+
 int dit_linear_wgrad(const void* dY, int64_t ldy, const void* X, int64_t ldx, int N, int K,
                      int64_t R, int dtype, float* dW, float* db, void* stream) {
   if (!dY || !X || !dW) return fail(DIT_EINVAL, "dY, X and dW must be non-NULL");
@@ -1143,6 +1159,9 @@ int dit_linear_wgrad(const void* dY, int64_t ldy, const void* X, int64_t ldx, in
                   R * (ldy > ldx ? ldy : ldx) <= INT32_MAX;
   if (db && dtype == DIT_BF16 && !tn && (N % 8 || ldy % 8 || ((uintptr_t)dY & 15)))
     return fail(DIT_EUNSUPPORTED, "bf16 bias gradient needs N, ldy multiples of 8 and aligned dY");
+  if (db && dtype == DIT_BF16 && !tn && R > kColsumTallMaxRows)
+    return fail(DIT_EUNSUPPORTED, "bf16 bias gradient of more than %lld rows",
+                (long long)kColsumTallMaxRows);
   DIT_HIP(linear_wgrad(dY, ldy, X, ldx, N, K, R, dtype, dW, K, db, (hipStream_t)stream));
   return ok();
 }

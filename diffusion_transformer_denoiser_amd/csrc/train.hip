@@ -395,14 +395,15 @@ __global__ __launch_bounds__(256) void colsum_tall_bf16_kernel(const bf16_t* __r
   }
 }
 
-// out[c] += sum over r < rows of in[r * ld + c]; one thread per column.
+// out[c] += sum over r < rows of in[r * ld + c]; one thread per column, the
+// column's sum added atomically (calls into one out may overlap).
 __global__ void colsum_kernel(const float* __restrict__ in, int rows, int64_t cols, int64_t ld,
                               float* __restrict__ out) {
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= cols) return;
   float s = 0.0f;
   for (int r = 0; r < rows; ++r) s += in[r * ld + c];
-  out[c] += s;
+  unsafeAtomicAdd(&out[c], s);
 }
 
 // Class-table gradient: row y[b] of the table receives dc[b] (atomically: rows
@@ -752,7 +753,7 @@ hipError_t launch_transpose(const void* in, int in_dtype, int64_t R, int64_t Cc,
 hipError_t launch_colsum_tall_bf16(const void* in, int64_t rows, int64_t cols, int64_t ld,
                                   float* out, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
-  if (cols % 8 || ld % 8 || ((uintptr_t)in & 15) || (rows + 511) / 512 > 65535)
+  if (cols % 8 || ld % 8 || ((uintptr_t)in & 15) || rows > kColsumTallMaxRows)
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)((cols + 255) / 256), (unsigned)((rows + 511) / 512));
   colsum_tall_bf16_kernel<<<grid, 256, 0, s>>>((const bf16_t*)in, rows, cols, ld, out);

@@ -432,6 +432,20 @@ def linear(epilogue: int, A, W, bias, out, gate=None, gate_stride=0, T=1):
     return out
 
 
+def ln_modulate(X, mod, shift_off, scale_off, T, H, eps=1e-6):
+    """H [M, d] = LN(X)(1 + mod[b, scale_off:+d]) + mod[b, shift_off:+d] with
+    b = m / T (``dit_ln_modulate``); X [M, d] fp32, mod [rows, stride] fp32,
+    H fp32 or bf16."""
+    lib = _lib.load()
+    M, d = X.shape
+    code = _lib.DIT_BF16 if H.dtype == torch.bfloat16 else _lib.DIT_F32
+    assert X.dtype == torch.float32 and X.is_contiguous() and H.is_contiguous()
+    assert mod.dtype == torch.float32 and mod.is_contiguous()
+    _lib.check(lib.dit_ln_modulate(_ptr(X), M, T, d, _ptr(mod), mod.shape[-1], shift_off,
+                                   scale_off, eps, _ptr(H), code, _stream(X.device)))
+    return H
+
+
 def linear_wgrad(dY, X, dW, db=None):
     """dW [N, K] fp32 += dY^T X for dY [R, N], X [R, K] (2-D, unit column stride,
     same dtype), and db [N] fp32 += column sums of dY if given: the weight and

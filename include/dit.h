@@ -299,9 +299,23 @@ int dit_attention(const void* qkv, int B, int H, int T, int dh, int dtype, void*
  *                  The reduction over K is split into slices whose partial
  *                  sums are added atomically (summation order not fixed). */
 #define DIT_EPI_ACCUM 3
+/*   DIT_EPI_BIAS_DT: out dtype [M, N] = A W^T + bias, rounded to the model
+ *                  dtype (the q | k | v in-projection's epilogue). */
+#define DIT_EPI_BIAS_DT 4
 int dit_linear(int epilogue, const void* A, const void* W, const float* bias, int M, int N,
                int K, int dtype, void* out, const float* gate, int gate_stride, int T,
                void* stream);
+
+/* LayerNorm and adaLN modulation (itwiki "확산 트랜스포머", adaLN-Zero
+ * equations: LN without affine, eps inside the square root, then
+ * LN(x)(1 + gamma) + beta):  H[m, :] = LN(X[m, :]) (1 + mod[b, scale_off ..]) +
+ * mod[b, shift_off ..] with b = m / T and the row of mod at b * mod_stride
+ * (mod_stride 0: one row for every token).  X: [M, d] fp32; mod fp32; H:
+ * [M, d] in dtype (rounded to nearest even for bf16).  d a multiple of 128 up
+ * to 2048.  The kernel the forward runs before the q | k | v and FFN-up
+ * products. */
+int dit_ln_modulate(const float* X, int M, int T, int d, const float* mod, int mod_stride,
+                    int shift_off, int scale_off, float eps, void* H, int dtype, void* stream);
 
 /* One adaLN-Zero block (DIT_EUNSUPPORTED for the other designs),
  * teacher-forced: X_out = block_l(X_in) with the given modulation

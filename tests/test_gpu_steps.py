@@ -128,9 +128,79 @@ def test_linear_epilogues(M, N, K, dtype):
     acc = torch.from_numpy(acc0).cuda()
     dmod.linear(dmod.DIT_EPI_ACCUM, Ad, Wd, None, acc)
     e4 = rel_l2(np_(acc) - acc0, ref - bias)
-    log(f"  rel-L2 bias={e1:.2e} gelu={e2:.2e} gated-increment={e3:.2e} accum={e4:.2e}")
+    # bias epilogue rounded to the model dtype (the q | k | v in-projection)
+    od = torch.empty((M, N), device="cuda", dtype=tdt)
+    dmod.linear(dmod.DIT_EPI_BIAS_DT, Ad, Wd, bd, od)
+    e5 = rel_l2(np_(od), ref)
+    log(f"  rel-L2 bias={e1:.2e} gelu={e2:.2e} gated-increment={e3:.2e} accum={e4:.2e} "
+        f"bias-dtype={e5:.2e}")
     assert e1 <= tol and e3 <= tol and e4 <= tol
     assert e2 <= (tol if dtype == "f32" else 4e-3)     # bf16 output rounding
+    assert e5 <= (tol if dtype == "f32" else 4e-3)
+
+
+# Shapes that take the wide-tile kernel (at least 256 tiles of 256 x 288 or
+# 256 x 256): the four block products at M = 16384, a ragged last row tile
+# (M = 16500: 116 rows) and the 256-wide variant (N = 1280).
+WIDE_SHAPES = [(16384, 3456, 1152), (16384, 1152, 1152), (16384, 4608, 1152),
+               (16384, 1152, 4608), (16500, 1152, 1152), (16384, 1280, 1152)]
+
+
+@pytest.mark.parametrize("M,N,K", WIDE_SHAPES)
+def test_linear_wide_tiles(M, N, K):
+    log(f"linear bf16 (wide tiles) M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + 3 * N + 7 * K)
+    A = _bf16(rng.standard_normal((M, K)).astype(np.float32))
+    W = _bf16((rng.standard_normal((N, K)) * 0.05).astype(np.float32))
+    bias = rng.standard_normal(N).astype(np.float32)
+    Ad = torch.from_numpy(A).to(torch.bfloat16).cuda()
+    Wd = torch.from_numpy(W).to(torch.bfloat16).cuda()
+    bd = torch.from_numpy(bias).cuda()
+    # rows checked against fp64: the first and last rows of the first, a
+    # middle and the last row tile, and every 97th row
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), [0, 255, 256, 8191, M - 117, M - 1]]))
+    ref = A[rows].astype(np.float64) @ W.astype(np.float64).T + bias
+    out = torch.full((M, N), float("nan"), device="cuda", dtype=torch.float32)
+    dmod.linear(dmod.DIT_EPI_BIAS, Ad, Wd, bd, out)
+    o = np_(out)
+    e1 = rel_l2(o[rows], ref)
+    g = torch.empty((M, N), device="cuda", dtype=torch.bfloat16)
+    dmod.linear(dmod.DIT_EPI_GELU, Ad, Wd, bd, g)
+    e2 = rel_l2(np_(g)[rows], oracle.gelu_tanh(ref))
+    od = torch.empty((M, N), device="cuda", dtype=torch.bfloat16)
+    dmod.linear(dmod.DIT_EPI_BIAS_DT, Ad, Wd, bd, od)
+    e3 = rel_l2(np_(od)[rows], ref)
+    T = 256
+    gate = rng.standard_normal(((M + T - 1) // T, N)).astype(np.float32)
+    X0 = rng.standard_normal((M, N)).astype(np.float32)
+    X = torch.from_numpy(X0).cuda()
+    dmod.linear(dmod.DIT_EPI_GATED, Ad, Wd, bd, X, gate=torch.from_numpy(gate).cuda(),
+                gate_stride=N, T=T)
+    Xg = np_(X)
+    e4 = rel_l2(Xg[rows] - X0[rows], gate[rows // T] * ref)
+    log(f"  rel-L2 bias={e1:.2e} gelu={e2:.2e} bias-dtype={e3:.2e} gated-increment={e4:.2e}")
+    assert np.isfinite(o).all() and np.isfinite(Xg).all()
+    assert e1 <= 1e-5 and e4 <= 1e-5
+    assert e2 <= 4e-3 and e3 <= 4e-3
+
+
+@pytest.mark.parametrize("M,T,d,dtype", [(512, 256, 1152, "bf16"), (300, 64, 768, "f32"),
+                                         (16384, 256, 1152, "bf16")])
+def test_ln_modulate(M, T, d, dtype):
+    log(f"LayerNorm + modulate {dtype} M={M} T={T} d={d}")
+    rng = np.random.default_rng(M + d)
+    X = (rng.standard_normal((M, d)) * 3 + 0.5).astype(np.float32)
+    rows = (M + T - 1) // T
+    stride = 6 * d + 8
+    mod = (rng.standard_normal((rows, stride)) * 0.3).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    H = torch.empty((M, d), device="cuda", dtype=tdt)
+    dmod.ln_modulate(torch.from_numpy(X).cuda(), torch.from_numpy(mod).cuda(), 3 * d, 4 * d, T, H)
+    b = np.arange(M) // T
+    ref = oracle.layer_norm(X) * (1.0 + mod[b, 4 * d:5 * d]) + mod[b, 3 * d:4 * d]
+    err = rel_l2(np_(H), ref)
+    log(f"  rel-L2 {err:.2e}")
+    assert err <= (1e-5 if dtype == "f32" else 4e-3)
 
 
 @pytest.mark.parametrize("M,N,K,dtype", [(96, 200, 8192, "bf16"), (1152, 384, 16384, "bf16"),

@@ -45,3 +45,9 @@ def test_short_run_prints_one_contract_line():
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 2500.0
     assert 0 < rf["frac"] < 1 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     assert "traffic" in rf
+    # the roofline is the hot kernel with the largest time per forward
+    ks = d["kernels"]
+    assert {k["name"] for k in ks} >= {"qkv", "out_proj", "fc1", "fc2", "attention", "layernorm"}
+    top = max(ks, key=lambda k: k["us_per_forward"])
+    assert rf["kernel"] == top["kernel"]
+    assert len(d["repeats_ms_per_step"]) == 5
