@@ -1090,6 +1090,10 @@ int dit_attention(const void* qkv, int B, int H, int T, int dh, int dtype, void*
   if (dh != 64 && dh != 72) return fail(DIT_EUNSUPPORTED, "head dim %d", dh);
   if ((int64_t)B * H > 65535) return fail(DIT_EUNSUPPORTED, "B * H > 65535");
   if ((uintptr_t)qkv & 15) return fail(DIT_EINVAL, "qkv must be 16-byte aligned");
+  if ((uintptr_t)o & 7) return fail(DIT_EINVAL, "o must be 8-byte aligned");
+  // one (row, head) slice is addressed with 32-bit byte offsets
+  if ((int64_t)T * 3 * H * dh * 4 >= (int64_t)1 << 31)
+    return fail(DIT_EUNSUPPORTED, "T * 3 H dh too large for one row");
   DIT_HIP(launch_attention(qkv, B, H, T, dh, dtype, o, (hipStream_t)stream));
   return ok();
 }
@@ -1141,6 +1145,10 @@ int dit_ln_modulate(const float* X, int M, int T, int d, const float* mod, int m
     return fail(DIT_EINVAL, "the shift / scale vectors must lie inside a modulation row");
   if (d % 128 || d > 2048 || !(eps > 0.0f))
     return fail(DIT_EUNSUPPORTED, "LayerNorm width must be a multiple of 128 up to 2048, eps > 0");
+  if (((uintptr_t)X & 15) || ((uintptr_t)H & 15) || ((uintptr_t)mod & 15) || mod_stride % 4 ||
+      shift_off % 4 || scale_off % 4)
+    return fail(DIT_EINVAL, "X, H and mod must be 16-byte aligned, mod_stride and the offsets "
+                            "multiples of 4");
   DIT_HIP(launch_ln_modulate(X, M, T, d, mod, mod_stride, shift_off, scale_off, eps, H, dtype,
                              (hipStream_t)stream));
   return ok();

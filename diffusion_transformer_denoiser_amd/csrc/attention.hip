@@ -22,9 +22,8 @@
 //
 // fp32 path: one thread per query, keys streamed through LDS (small shapes).
 #include "common.h"
+#include "mfma_util.h"
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
 
 namespace {
 
@@ -161,9 +160,11 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
         const bool isv = ii >= NCP / 2;
         const int ci = isv ? ii - NCP / 2 : ii;
         char* dst = (isv ? (char*)sV[buf] : (char*)sK[buf]) + ci * 1024;
-        const bf16_t* src = (isv ? Vb : Kb) + (int64_t)min(kv0 + drow[u], T - 1) * ld + dcol[u];
-        __builtin_amdgcn_global_load_lds((const void*)src,
-                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        const int off = (int)(((int64_t)min(kv0 + drow[u], T - 1) * ld + dcol[u]) * 2);
+        // buffer form: ordered by the explicit waits and barriers of the loop
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrs : krs, (lds_void*)dst, 16, off, 0, 0, 0);
+#endif
       }
     }
   };
@@ -373,6 +374,278 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
   }
 }
 
+// Short sequences (T <= 256, dh = 72): one workgroup of 8 waves owns every
+// query of one (row, head), 32 per wave, with the sequence's K and V resident
+// in LDS.  Workgroups are persistent over the (row, head) pairs; the next
+// pair's K, V and this wave's next queries are loaded into registers while
+// the current pair computes and are written to LDS between two barriers.
+// Per 64-key tile: S^T = K Q^T (24 MFMAs), exp2-domain weights, O^T += V^T
+// P^T (20 MFMAs).  V sits in LDS with a row stride of 80 whose column 72 is 1
+// and 73..79 are 0, so O^T row 72 is the sum of the (bf16) weights
+// themselves: the normaliser comes out of the same products as the
+// numerator.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// NT = ceil(T / 64) key tiles; RAG: T is not a multiple of 64 (mask keys >= T)
+template <int NT, bool RAG>
+__global__ __launch_bounds__(512) void attn_short_kernel(const bf16_t* __restrict__ QKV,
+                                                         bf16_t* __restrict__ O, int H, int T,
+                                                         int npairs, float sl2) {
+  constexpr int DH = 72, NWV = 8, KS = 72, VS = 80, NDB = 5;
+  constexpr int NCH = 256 * (DH / 8);               // 16-byte chunks of K (or V) per pair
+  constexpr int CPT = (NCH + 64 * NWV - 1) / (64 * NWV);
+  __shared__ __attribute__((aligned(16))) bf16_t sK[256 * KS];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[256 * VS];
+  __shared__ __attribute__((aligned(16))) uint4 zslot;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int64_t ld = 3LL * H * DH;                  // packed row stride
+  const int q0 = 32 * wave;
+  const bf16x8_t z8 = {};
+
+  // K / V chunk u of this thread: chunk c = tid + 512 u is row c / 9, 16-byte
+  // column c % 9 (rows past T read row T - 1: finite data whose weights are 0)
+  // In LDS, K chunk c sits at element 8 c (rows unpadded) and V chunk c at
+  // 8 (c + c / 9) (one pad chunk per row).  Offsets are recomputed at each
+  // use rather than held in registers across the pair.
+  const int ldb = (int)(ld * 2);
+  static_assert(KS == DH && VS == DH + 8, "LDS row strides");
+  const int nrec = (int)(((int64_t)(T - 1) * ld + DH) * 2);
+  uint4 kreg[CPT], vreg[CPT];
+  auto gload = [&](int p) {
+    const int b = p / H, h = p - b * H;
+    const bf16_t* Kb = QKV + (int64_t)b * T * ld + (int64_t)(H + h) * DH;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Kb, (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Kb + (int64_t)H * DH), (short)0, nrec, 0x00020000);
+    int t0 = tid;
+    asm volatile("" : "+v"(t0));
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = min(t0 + 64 * NWV * u, NCH - 1);
+      const int row = c / (DH / 8), col = c - row * (DH / 8);
+      const int off = min(row, T - 1) * ldb + col * 16;
+      kreg[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+      vreg[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+    }
+  };
+  auto sstore = [&]() {
+    int t0 = tid;
+    asm volatile("" : "+v"(t0));       // keep the address arithmetic here (not hoisted and spilled)
+#pragma unroll
+    for (int u = 0; u < CPT; ++u)
+      if (t0 + 64 * NWV * u < NCH) {
+        const int c = t0 + 64 * NWV * u;
+        *(uint4*)&sK[8 * c] = kreg[u];
+        *(uint4*)&sV[8 * (c + c / (DH / 8))] = vreg[u];
+      }
+  };
+  // This wave's 32 queries as MFMA B operands: dh 0..63 in qf, dh 64..71 in
+  // qt.  The loads are unconditional (row clamped to T - 1; lanes g > 0 of
+  // the tail read dh 72..95, inside the packed row); the selects that zero
+  // queries >= T and tail lanes g > 0 run when the pair starts.
+  auto load_q = [&](int p, bf16x8_t (&qf)[2][2], bf16x8_t (&qt)[2]) {
+    const int b = p / H, h = p - b * H;
+    const bf16_t* Qb = QKV + (int64_t)b * T * ld + h * DH;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const bf16_t* qr = Qb + (int64_t)min(q0 + 16 * qb + c16, T - 1) * ld;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) qf[qb][c] = *(const bf16x8_t*)(qr + 32 * c + 8 * g);
+      qt[qb] = *(const bf16x8_t*)(qr + 64 + 8 * g);
+    }
+  };
+
+  // Workgroup w runs on XCD w % 8 (round-robin dispatch).  With a grid that
+  // is a multiple of 8, XCD x takes the logical slots x G/8 .. (x+1) G/8 - 1,
+  // so the pairs it runs together are consecutive heads of the same rows:
+  // the cache lines that neighbouring heads' 144-byte slices share are
+  // fetched (and written) once, through that XCD's L2.
+  const int G = gridDim.x;
+  int pair = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  if (pair >= npairs) return;
+  if (tid < 256) *(uint4*)&sV[tid * VS + DH] = make_uint4(0x3F80u, 0, 0, 0);   // (1, 0, .., 0)
+  if (tid == 0) zslot = make_uint4(0, 0, 0, 0);
+  bf16x8_t qn[2][2], qtn[2];
+  load_q(pair, qn, qtn);
+  gload(pair);
+  sstore();
+  __syncthreads();
+
+  for (;;) {
+    const int next = pair + G;
+    bf16x8_t qf[2][2], qt[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const bool ok = q0 + 16 * qb + c16 < T;
+      qf[qb][0] = ok ? qn[qb][0] : z8;
+      qf[qb][1] = ok ? qn[qb][1] : z8;
+      qt[qb] = ok && g == 0 ? qtn[qb] : z8;
+    }
+    if (next < npairs) gload(next);    // in flight while this pair computes
+
+    floatx4 oacc[NDB][2];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // S^T[key, q] of 64-key tile t: 4 key blocks x 2 query blocks of 16 x 16
+    auto s_tile = [&](int t, floatx4 (&sa)[4][2]) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16_t* kr = sK + (64 * t + 16 * kb + c16) * KS;
+        const bf16x8_t k0 = *(const bf16x8_t*)(kr + 8 * g);
+        const bf16x8_t k1 = *(const bf16x8_t*)(kr + 32 + 8 * g);
+        const bf16x8_t kt = *(const bf16x8_t*)(g == 0 ? kr + 64 : (const bf16_t*)&zslot);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[qb][0], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[qb][1], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, qt[qb], acc, 0, 0, 0);
+          sa[kb][qb] = acc;
+        }
+      }
+      if (RAG && t == NT - 1) {        // keys >= T of the ragged last tile
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool out = 64 * t + 16 * kb + 4 * g + r >= T;
+            sa[kb][0][r] = out ? -INFINITY : sa[kb][0][r];
+            sa[kb][1][r] = out ? -INFINITY : sa[kb][1][r];
+          }
+      }
+    };
+    // O^T[d, q] += V^T[d, key] P^T[key, q] for tile t.  Key order inside a
+    // 32-key block j follows the weights: lane group g holds keys 4 g .. + 3
+    // and 16 + those.  Transposing reads: lane s of group g points at
+    // V[key 32 j + 4 g + s / 4 (+16)][d 16 db + 4 (s % 4)] and receives d
+    // 16 db + s of those 4 keys.
+    auto pv_tile = [&](int t, const bf16x8_t (&pw)[2][2]) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16_t* vb = sV + (64 * t + 32 * j + 4 * g + (c16 >> 2)) * VS + 4 * (c16 & 3);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(vb + 16 * db));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(vb + 16 * VS + 16 * db));
+          const bf16x8_t vf = __builtin_bit_cast(
+              bf16x8_t, (__attribute__((ext_vector_type(8))) short){lo[0], lo[1], lo[2], lo[3],
+                                                                    hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pw[qb][j], oacc[db][qb],
+                                                                   0, 0, 0);
+        }
+      }
+    };
+    // scaled (exp2-domain) maximum of a tile's scores for query block qb
+    auto tile_max = [&](const floatx4 (&sa)[4][2], int qb) {
+      float mx = sa[0][qb][0];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sa[kb][qb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      return mx * sl2;
+    };
+
+    // Software pipeline over the tiles: the MFMAs of PV(t-1) are issued among
+    // the maxima of tile t and those of S(t+1) among its weights, so that one
+    // wave keeps the matrix cores and the VALU busy together.  Weights are
+    // exp2(s sl2 - m_ref) against a reference maximum that is raised (and the
+    // output rescaled) only when a tile's maximum exceeds it by more than
+    // 2^RESCALE_SLACK, which keeps the weights finite and rarely branches.
+    constexpr float RESCALE_SLACK = 8.0f;
+    float m_ref[2];
+    floatx4 sc[4][2], sn[4][2];
+    bf16x8_t pw[2][2];
+    s_tile(0, sc);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t > 0) pv_tile(t - 1, pw);
+      const float mx0 = tile_max(sc, 0), mx1 = tile_max(sc, 1);
+      if (t == 0) {
+        m_ref[0] = mx0;
+        m_ref[1] = mx1;
+      } else if (__any(mx0 > m_ref[0] + RESCALE_SLACK || mx1 > m_ref[1] + RESCALE_SLACK)) {
+        const float mx[2] = {mx0, mx1};
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float m_new = fmaxf(m_ref[qb], mx[qb]);
+          const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
+          m_ref[qb] = m_new;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oacc[db][qb][r] *= alpha;
+        }
+      }
+      if (t + 1 < NT) s_tile(t + 1, sn);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float mneg = -m_ref[qb];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float pv[8];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pv[r] = __builtin_amdgcn_exp2f(fmaf(sc[2 * j][qb][r], sl2, mneg));
+            pv[4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[2 * j + 1][qb][r], sl2, mneg));
+          }
+          const uint4 u = make_uint4(f2bf2(pv[0], pv[1]), f2bf2(pv[2], pv[3]),
+                                     f2bf2(pv[4], pv[5]), f2bf2(pv[6], pv[7]));
+          pw[qb][j] = __builtin_bit_cast(bf16x8_t, u);
+        }
+      }
+      if (t + 1 < NT) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          sc[kb][0] = sn[kb][0];
+          sc[kb][1] = sn[kb][1];
+        }
+      }
+    }
+    // the next queries are loaded once the scores are dead (fewer live
+    // registers); the last products, the stores and the barriers cover them
+    if (next < npairs) load_q(next, qn, qtn);
+    pv_tile(NT - 1, pw);
+
+    // O^T row 72 (block 4, lane group 2, element 0) is the sum of the weights
+    // of query c16: divide and store O[b, q, h*DH + d]
+    {
+      const int b = pair / H, h = pair - b * H;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float l = __shfl(oacc[4][qb][0], 32 + c16, 64);
+        const float inv = 1.0f / l;
+        const int q = q0 + 16 * qb + c16;
+        if (q >= T) continue;
+        bf16_t* orow = O + ((int64_t)b * T + q) * H * DH + h * DH;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int d0 = 16 * db + 4 * g;
+          if (d0 + 3 < DH)
+            *(uint2*)(orow + d0) = make_uint2(f2bf2(oacc[db][qb][0] * inv, oacc[db][qb][1] * inv),
+                                              f2bf2(oacc[db][qb][2] * inv, oacc[db][qb][3] * inv));
+        }
+      }
+    }
+    if (next >= npairs) break;
+    __syncthreads();                   // every wave is done with this pair's K and V
+    sstore();
+    __syncthreads();
+    pair = next;
+  }
+}
+
 template <int DH, bool PK = false>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ QKV,
                                                       float* __restrict__ O, int H, int T_rows,
@@ -437,6 +710,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 
 }  // namespace
 
+// one resident workgroup of the short-sequence kernel per CU (8 waves of up
+// to 256 VGPRs fill a CU's register file)
+constexpr int kShortSlots = 256;
+
 hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, int dtype, void* o,
                             hipStream_t s, float* lse) {
   if (B <= 0 || T <= 0) return hipSuccess;
@@ -454,6 +731,22 @@ hipError_t launch_attention(const void* qkv, int B, int heads, int T, int dh, in
       if (waste < best) { best = waste; nwv = c; }
     }
     if (dh != 64 && dh != 72) return hipErrorInvalidValue;
+    if (dh == 72 && T <= 256 && !lse) {
+      // whole sequences resident in LDS, persistent over the (row, head) pairs
+      const int npairs = B * heads;
+      const int grid = npairs < kShortSlots ? npairs : kShortSlots;
+#define DIT_SHORT(NT, RAG)                                                                    \
+  attn_short_kernel<NT, RAG><<<grid, 512, 0, s>>>((const bf16_t*)qkv, (bf16_t*)o, heads, T, npairs, sl2)
+      const bool rag = T % 64 != 0;
+      switch ((T + 63) / 64) {
+        case 1: if (rag) DIT_SHORT(1, true); else DIT_SHORT(1, false); break;
+        case 2: if (rag) DIT_SHORT(2, true); else DIT_SHORT(2, false); break;
+        case 3: if (rag) DIT_SHORT(3, true); else DIT_SHORT(3, false); break;
+        default: if (rag) DIT_SHORT(4, true); else DIT_SHORT(4, false); break;
+      }
+#undef DIT_SHORT
+      return hipGetLastError();
+    }
     SeqTable none;
     none.n = 0;
 #define DIT_ATTN_LAUNCH(NWV)                                                                  \

@@ -5,81 +5,126 @@
 #define DIT_LOG2_1E4 13.287712379549449f
 
 // H[m, :] = LN(X[m, :]) * (1 + scale[b, :]) + shift[b, :],  b = m / T.
-// One wave per R consecutive rows; each lane holds NV float2 of every row
-// (d = 128 NV), so a row is read from HBM once and both moments come from
-// registers.  The loads of all R rows are issued before the first reduction,
-// which keeps R rows of memory traffic in flight per wave.
-template <int NV, typename DT, int R>
+// One wave per R consecutive rows.  d = 256 N4 + 128 N2: each lane holds N4
+// float4 and N2 float2 of every row (16-byte loads where the width allows),
+// so a row is read from HBM once and both moments come from registers.  The
+// loads of all R rows are issued before the first reduction, which keeps R
+// rows of memory traffic in flight per wave; the R rows share one read of
+// the shift and scale vectors when they belong to one batch row.
+template <int N4, int N2, typename DT, int R>
 __global__ __launch_bounds__(256) void ln_modulate_kernel(const float* __restrict__ X, int M,
                                                           int T, const float* __restrict__ mod,
                                                           int mod_stride, int shift_off,
                                                           int scale_off, float eps,
                                                           DT* __restrict__ H,
                                                           const int* __restrict__ tok_seg) {
-  constexpr int D = 128 * NV;
+  constexpr int D = 256 * N4 + 128 * N2;
   const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
   const int lane = threadIdx.x & 63;
   if (row0 >= M) return;
-  float2 v[R][NV];
+  float4 v4[R][N4 ? N4 : 1];
+  float2 v2[R][N2 ? N2 : 1];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float2* x2 = (const float2*)(X + (int64_t)min(row0 + r, M - 1) * D);
+    const float* x = X + (int64_t)min(row0 + r, M - 1) * D;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) v[r][i] = x2[lane + 64 * i];
+    for (int i = 0; i < N4; ++i) v4[r][i] = ((const float4*)x)[lane + 64 * i];
+#pragma unroll
+    for (int i = 0; i < N2; ++i) v2[r][i] = ((const float2*)(x + 256 * N4))[lane + 64 * i];
   }
+  // shift / scale of a batch row, in the same register layout as a row of X
+  float4 sh4[N4 ? N4 : 1], sc4[N4 ? N4 : 1];
+  float2 sh2[N2 ? N2 : 1], sc2[N2 ? N2 : 1];
+  auto load_mod = [&](int b) {
+    const float* sh = mod + (int64_t)b * mod_stride + shift_off;
+    const float* sc = mod + (int64_t)b * mod_stride + scale_off;
+#pragma unroll
+    for (int i = 0; i < N4; ++i) {
+      sh4[i] = ((const float4*)sh)[lane + 64 * i];
+      sc4[i] = ((const float4*)sc)[lane + 64 * i];
+    }
+#pragma unroll
+    for (int i = 0; i < N2; ++i) {
+      sh2[i] = ((const float2*)(sh + 256 * N4))[lane + 64 * i];
+      sc2[i] = ((const float2*)(sc + 256 * N4))[lane + 64 * i];
+    }
+  };
+  auto brow = [&](int row) { return tok_seg ? tok_seg[row] : row / T; };
+  const int rlast = min(row0 + R, M) - 1;
+  const bool shared = !tok_seg && row0 / T == rlast / T;
+  if (shared) load_mod(row0 / T);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int row = row0 + r;
     if (row >= M) break;
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) s += v[r][i].x + v[r][i].y;
+    for (int i = 0; i < N4; ++i) s += (v4[r][i].x + v4[r][i].y) + (v4[r][i].z + v4[r][i].w);
+#pragma unroll
+    for (int i = 0; i < N2; ++i) s += v2[r][i].x + v2[r][i].y;
     const float mean = wave_sum(s) * (1.0f / D);
     float q = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      float a = v[r][i].x - mean, b = v[r][i].y - mean;
+    for (int i = 0; i < N4; ++i) {
+      const float a = v4[r][i].x - mean, b = v4[r][i].y - mean;
+      const float c = v4[r][i].z - mean, e = v4[r][i].w - mean;
+      q += (a * a + b * b) + (c * c + e * e);
+    }
+#pragma unroll
+    for (int i = 0; i < N2; ++i) {
+      const float a = v2[r][i].x - mean, b = v2[r][i].y - mean;
       q += a * a + b * b;
     }
     const float var = wave_sum(q) * (1.0f / D);
     const float rstd = 1.0f / sqrtf(var + eps);
-    const int b = tok_seg ? tok_seg[row] : row / T;
-    const float2* sh = (const float2*)(mod + (int64_t)b * mod_stride + shift_off);
-    const float2* sc = (const float2*)(mod + (int64_t)b * mod_stride + scale_off);
+    if (!shared) load_mod(brow(row));
+    DT* h = H + (int64_t)row * D;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int c = lane + 64 * i;
-      float2 g = sc[c], t = sh[c];
-      float h0 = (v[r][i].x - mean) * rstd * (1.0f + g.x) + t.x;
-      float h1 = (v[r][i].y - mean) * rstd * (1.0f + g.y) + t.y;
-      if constexpr (sizeof(DT) == 2) {
-        ((uint32_t*)(H + (int64_t)row * D))[c] = f2bf2(h0, h1);
-      } else {
-        ((float2*)(H + (int64_t)row * D))[c] = make_float2(h0, h1);
-      }
+    for (int i = 0; i < N4; ++i) {
+      const float4 x = v4[r][i], g = sc4[i], t = sh4[i];
+      const float h0 = (x.x - mean) * rstd * (1.0f + g.x) + t.x;
+      const float h1 = (x.y - mean) * rstd * (1.0f + g.y) + t.y;
+      const float h2 = (x.z - mean) * rstd * (1.0f + g.z) + t.z;
+      const float h3 = (x.w - mean) * rstd * (1.0f + g.w) + t.w;
+      if constexpr (sizeof(DT) == 2)
+        ((uint2*)h)[lane + 64 * i] = make_uint2(f2bf2(h0, h1), f2bf2(h2, h3));
+      else
+        ((float4*)h)[lane + 64 * i] = make_float4(h0, h1, h2, h3);
+    }
+#pragma unroll
+    for (int i = 0; i < N2; ++i) {
+      const float2 x = v2[r][i], g = sc2[i], t = sh2[i];
+      const float h0 = (x.x - mean) * rstd * (1.0f + g.x) + t.x;
+      const float h1 = (x.y - mean) * rstd * (1.0f + g.y) + t.y;
+      if constexpr (sizeof(DT) == 2)
+        ((uint32_t*)(h + 256 * N4))[lane + 64 * i] = f2bf2(h0, h1);
+      else
+        ((float2*)(h + 256 * N4))[lane + 64 * i] = make_float2(h0, h1);
     }
   }
 }
 
+#ifndef DIT_LN_ROWS
+#define DIT_LN_ROWS 2
+#endif
 template <typename DT>
 static hipError_t ln_dispatch(const float* X, int M, int T, int d, const float* mod,
                               int mod_stride, int shift_off, int scale_off, float eps, DT* H,
                               const int* tok_seg, hipStream_t s) {
-  constexpr int R = 2;
+  constexpr int R = DIT_LN_ROWS;
   dim3 grid((M + 4 * R - 1) / (4 * R));
-#define DIT_LN_CASE(NV)                                                                      \
-  case NV:                                                                                   \
-    ln_modulate_kernel<NV, DT, R><<<grid, 256, 0, s>>>(X, M, T, mod, mod_stride, shift_off, \
-                                                       scale_off, eps, H, tok_seg);         \
-    break;
-  switch (d / 128) {
-    DIT_LN_CASE(1) DIT_LN_CASE(2) DIT_LN_CASE(3) DIT_LN_CASE(4) DIT_LN_CASE(5) DIT_LN_CASE(6)
-    DIT_LN_CASE(7) DIT_LN_CASE(8) DIT_LN_CASE(9) DIT_LN_CASE(10) DIT_LN_CASE(11)
-    DIT_LN_CASE(12) DIT_LN_CASE(13) DIT_LN_CASE(14) DIT_LN_CASE(15) DIT_LN_CASE(16)
-    default: return hipErrorInvalidValue;
+#define DIT_LN_CASE(N4, N2)                                                                    \
+  if (d == 256 * N4 + 128 * N2) {                                                              \
+    ln_modulate_kernel<N4, N2, DT, R><<<grid, 256, 0, s>>>(X, M, T, mod, mod_stride, shift_off, \
+                                                           scale_off, eps, H, tok_seg);       \
+    return hipGetLastError();                                                                  \
   }
+  DIT_LN_CASE(0, 1) DIT_LN_CASE(1, 0) DIT_LN_CASE(1, 1) DIT_LN_CASE(2, 0) DIT_LN_CASE(2, 1)
+  DIT_LN_CASE(3, 0) DIT_LN_CASE(3, 1) DIT_LN_CASE(4, 0) DIT_LN_CASE(4, 1) DIT_LN_CASE(5, 0)
+  DIT_LN_CASE(5, 1) DIT_LN_CASE(6, 0) DIT_LN_CASE(6, 1) DIT_LN_CASE(7, 0) DIT_LN_CASE(7, 1)
+  DIT_LN_CASE(8, 0)
 #undef DIT_LN_CASE
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_ln_modulate(const float* X, int M, int T, int d, const float* mod,

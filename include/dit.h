@@ -282,7 +282,9 @@ int dit_timestep_embed(const float* t, int B, int dim, float* e, void* stream);
  * (itwiki "확산 트랜스포머", Implementation: nn.MultiheadAttention(d, heads)).
  * qkv: [B, T, 3*H*dh] packed in-projection output, q | k | v, each with heads as
  * contiguous dh slices (16-byte aligned); o: [B, T, H*dh] (token-major, heads
- * concatenated), same dtype.  dh in {64, 72}; B*H <= 65535. */
+ * concatenated), same dtype, 8-byte aligned.  dh in {64, 72}; B*H <= 65535;
+ * T * 3H * dh * 4 < 2^31.  bf16 with dh 72 and T <= 256 runs whole sequences
+ * out of LDS, one persistent workgroup per CU. */
 int dit_attention(const void* qkv, int B, int H, int T, int dh, int dtype, void* o, void* stream);
 
 /* Linear layer with one of the fused epilogues of the forward pass,
@@ -312,8 +314,8 @@ int dit_linear(int epilogue, const void* A, const void* W, const float* bias, in
  * mod[b, shift_off ..] with b = m / T and the row of mod at b * mod_stride
  * (mod_stride 0: one row for every token).  X: [M, d] fp32; mod fp32; H:
  * [M, d] in dtype (rounded to nearest even for bf16).  d a multiple of 128 up
- * to 2048.  The kernel the forward runs before the q | k | v and FFN-up
- * products. */
+ * to 2048; X, H, mod 16-byte aligned, mod_stride and the offsets multiples of
+ * 4.  The kernel the forward runs before the q | k | v and FFN-up products. */
 int dit_ln_modulate(const float* X, int M, int T, int d, const float* mod, int mod_stride,
                     int shift_off, int scale_off, float eps, void* H, int dtype, void* stream);
 

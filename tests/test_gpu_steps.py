@@ -321,6 +321,23 @@ def test_attention_matches_oracle(T, dh, dtype):
     assert err <= (1e-5 if dtype == torch.float32 else 1e-2)
 
 
+@pytest.mark.parametrize("B,H,T", [(37, 16, 256), (37, 16, 131), (9, 32, 64)])
+def test_attention_many_sequences_bf16(B, H, T):
+    # more (row, head) pairs than one workgroup per CU, so each persistent
+    # workgroup of the short-sequence path runs two or three of them
+    log(f"attention B={B} H={H} T={T} dh=72 bf16")
+    dh = 72
+    rng = np.random.default_rng(B * 1000 + T)
+    q, k, v = (_bf16(rng.standard_normal((B, H, T, dh))) for _ in range(3))
+    qkv = torch.from_numpy(_pack(q, k, v)).to(torch.bfloat16).cuda()
+    o = np_(dmod.attention(qkv, H)).reshape(B, T, H, dh).transpose(0, 2, 1, 3)
+    ref = oracle.attention(q, k, v)
+    err = rel_l2(o, ref)
+    worst = max(rel_l2(o[b], ref[b]) for b in range(B))
+    log(f"  rel-L2 {err:.2e} worst row {worst:.2e}")
+    assert err <= 1e-2 and worst <= 1e-2
+
+
 def test_attention_special_cases_bf16():
     # all keys equal => uniform weights => mean of v; T = 1 => v.
     B, H, T, dh = 1, 2, 100, 72
