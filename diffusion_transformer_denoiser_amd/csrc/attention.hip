@@ -21,11 +21,15 @@
 // contiguous dh slices), read with its row stride; output o [B, T, H dh].
 //
 // fp32 path: one thread per query, keys streamed through LDS (small shapes).
+#include <type_traits>
+
 #include "common.h"
 #include "mfma_util.h"
 
 
 namespace {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // PK: packed sequences.  The grid is (query blocks of all sequences, heads);
 // a block finds its sequence in the by-value table and attends over that
@@ -53,13 +57,20 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
   // with transposing LDS reads.  dh = 64: registers stage the tiles and V is
   // transposed on the way into LDS.
   constexpr bool DMA = DH == 72;
-  constexpr int VSZ = DMA ? KV * DH + 16 : DH * VLD;   // + 16: reads past the last row stay inside
+  // dh 72: V rows of 80 in LDS; columns 72..79 hold (1, 0, .., 0), so row 72
+  // of O^T = V^T P^T is the sum of the tile's (bf16) weights: the softmax
+  // normaliser comes out of the same products as the numerator.
+  constexpr int VS = 80;
+  constexpr int VSZ = DMA ? KV * VS : DH * VLD;
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][KV * KLD];
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][VSZ];
   // 16 zero bytes: operand lanes past dh read here instead of taking a branch
   __shared__ __attribute__((aligned(16))) uint4 zslot;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform as far as the compiler can see (a lane-derived index would
+  // turn the per-wave choice of copy source into a loop over lanes)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   // Workgroups are dispatched round-robin over the 8 XCDs; when their count
   // allows, workgroup i runs logical block (i % 8) * (n / 8) + i / 8, so the
@@ -138,33 +149,49 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
         vreg[u][q] = __builtin_bit_cast(
             uint2, __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[u] + t0 + q * ldb, 0, 0));
   };
-  // DMA staging (dh = 72): each tile is 2 x 9 direct global->LDS copies of 64
-  // lanes x 16 bytes (chunk c of a tile is row c / 9, 16-byte column c % 9, at
-  // LDS byte 16 c); copy u of wave w is number w + NWV u.  Rows past T read
-  // row T - 1 instead: finite data whose scores are masked.
-  constexpr int NCP = 2 * KV * DH / 512;
+  // DMA staging (dh = 72): direct global->LDS copies of 64 lanes x 16 bytes,
+  // lane l of a copy landing at its LDS base + 16 l.  A K tile is 9 copies
+  // (slot c: row c / 9, 16-byte column c % 9); a V tile 10 (slot c: row
+  // c / 10, column c % 10), whose lanes on column 9, the (1, 0, .., 0) pad,
+  // stay inactive and leave it as written at the start.  Copy u of wave w is
+  // number w + NWV u.  Byte offsets inside a tile are fixed per lane; the
+  // tile's row offset rides in the scalar offset.  The rows of a ragged last
+  // tile past T read row T - 1: finite data whose weights are 0.
+  constexpr int NCK = KV * DH / 512, NCV = KV * VS / 512, NCP = NCK + NCV;
   constexpr int CPW = (NCP + NWV - 1) / NWV;
-  int drow[CPW], dcol[CPW];
+  int drow[CPW], doff[CPW];
+  uint32_t dpad = 0;                       // bit u: copy u's lane is a V pad slot
 #pragma unroll
   for (int u = 0; u < CPW; ++u) {
-    const int ci = (wave + NWV * u) % (NCP / 2);
-    const int c = ci * 64 + lane;
-    drow[u] = c / (DH / 8);
-    dcol[u] = (c - drow[u] * (DH / 8)) * 8;
+    const int ii = wave + NWV * u;
+    const bool isv = ii >= NCK;
+    const int c = (isv ? ii - NCK : ii) * 64 + lane;
+    const int per = isv ? VS / 8 : DH / 8;
+    const int row = c / per, col = c - row * per;
+    drow[u] = row;
+    doff[u] = (int)(((int64_t)row * ld + (col < DH / 8 ? col : 0) * 8) * 2);
+    if (isv && col == DH / 8) dpad |= 1u << u;
   }
   auto dma = [&](int kv0, int buf) {
+    const bool ragged = kv0 + KV > T;      // uniform
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
       const int ii = wave + NWV * u;                // wave-uniform
       if (ii < NCP) {
-        const bool isv = ii >= NCP / 2;
-        const int ci = isv ? ii - NCP / 2 : ii;
-        char* dst = (isv ? (char*)sV[buf] : (char*)sK[buf]) + ci * 1024;
-        const int off = (int)(((int64_t)min(kv0 + drow[u], T - 1) * ld + dcol[u]) * 2);
+        const bool isv = ii >= NCK;
+        char* dst = (isv ? (char*)sV[buf] : (char*)sK[buf]) + (isv ? ii - NCK : ii) * 1024;
+        int voff_ = doff[u], soff = kv0 * ldb;
+        if (ragged) {
+          voff_ += (min(kv0 + drow[u], T - 1) - drow[u]) * ldb;
+          soff = 0;
+        }
         // buffer form: ordered by the explicit waits and barriers of the loop
+        if (!(dpad >> u & 1)) {
 #if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrs : krs, (lds_void*)dst, 16, off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vrs : krs, (lds_void*)dst, 16, voff_, soff, 0,
+                                                   0);
 #endif
+        }
       }
     }
   };
@@ -214,10 +241,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
   const int ntiles = (T + KV - 1) / KV;
   if (tid == 0) zslot = make_uint4(0, 0, 0, 0);
   if constexpr (DMA) {
-    // Zero both tile buffers once: the pad after each V tile (read only by
-    // operand lanes past dh 72) then holds finite values.
-    for (int i = tid; i < 2 * KV * KLD / 8; i += NTH) ((uint4*)sK)[i] = make_uint4(0, 0, 0, 0);
-    for (int i = tid; i < 2 * VSZ / 8; i += NTH) ((uint4*)sV)[i] = make_uint4(0, 0, 0, 0);
+    // The (1, 0, .., 0) column chunk of every V row of both buffers, once.
+    for (int i = tid; i < 2 * KV; i += NTH)
+      *(uint4*)&sV[i / KV][(i % KV) * VS + DH] = make_uint4(0x3F80u, 0, 0, 0);
     __syncthreads();
     dma(0, 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed
@@ -226,7 +252,11 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
     sstore(0);
   }
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
+  // One 64-key tile; RAG: the last tile of a length that is not a multiple
+  // of 64 (keys >= T masked).  For dh 72 only that one tile carries the
+  // masking code; dh 64 tests at run time.
+  auto tile = [&](int it, auto rag_c) {
+    constexpr bool RAG = decltype(rag_c)::value;
     const int buf = it & 1, kv0 = it * KV;
     if (it + 1 < ntiles) {                   // next tile in flight during this one
       if constexpr (DMA) dma(kv0 + KV, buf ^ 1);
@@ -252,7 +282,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
         s[kb][qb] = a;
       }
     }
-    if (kv0 + KV > T) {                      // ragged last tile: drop keys >= T
+    if (RAG || (!DMA && kv0 + KV > T)) {     // ragged last tile: drop keys >= T
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -283,7 +313,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
         const float m_new = fmaxf(m_run[qb], mxs);
         const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
         m_run[qb] = m_new;
-        l_run[qb] *= alpha;
+        if constexpr (!DMA) l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -299,13 +329,14 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
           p[r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], sl2, mneg));
           p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s[kb + 1][qb][r], sl2, mneg));
         }
+        if constexpr (!DMA)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) ls += p[r];
+          for (int r = 0; r < 8; ++r) ls += p[r];
         uint4 u = make_uint4(f2bf2(p[0], p[1]), f2bf2(p[2], p[3]), f2bf2(p[4], p[5]),
                              f2bf2(p[6], p[7]));
         pf[qb][kb >> 1] = __builtin_bit_cast(bf16x8_t, u);
       }
-      l_run[qb] += ls;
+      if constexpr (!DMA) l_run[qb] += ls;
     }
 
     // O^T[dh, q] += V^T[dh, key] P^T[key, q]; key order within each 32-key step:
@@ -318,16 +349,13 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
         bf16x8_t vf;
         if constexpr (DMA) {
           // Transposing reads: lane s of 16-lane group g points at
-          // V[key 32 j + 4 g + s / 4 (+16)][dh 16 db + 4 (s % 4)]; lane s then
-          // holds dh 16 db + s of keys 32 j + 4 g .. +3 (and 16 + those).
-          // Lanes past dh 72 read neighbouring finite data that only reaches
-          // O^T rows past dh, which are never stored.
-          typedef short v4i16 __attribute__((ext_vector_type(4)));
-          const bf16_t* vb = &sV[buf][(32 * j + 4 * g + (c16 >> 2)) * DH + 16 * db + 4 * (c16 & 3)];
+          // V[key 32 j + 4 g + s / 4 (+16)][d 16 db + 4 (s % 4)]; lane s then
+          // holds d 16 db + s of keys 32 j + 4 g .. +3 (and 16 + those).
+          const bf16_t* vb = &sV[buf][(32 * j + 4 * g + (c16 >> 2)) * VS + 16 * db + 4 * (c16 & 3)];
           const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) v4i16*)vb);
           const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4i16*)(vb + 16 * DH));
+              (__attribute__((address_space(3))) v4i16*)(vb + 16 * VS));
           vf = __builtin_bit_cast(bf16x8_t, (__attribute__((ext_vector_type(8))) short){
                                                 lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         } else {
@@ -350,14 +378,27 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
       if (it + 1 < ntiles) sstore(buf ^ 1);
     }
     __syncthreads();
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (T % KV == 0 || !DMA) {           // (dh 64 keeps one loop body: registers)
+    for (int it = 0; it < ntiles; ++it) tile(it, F_{});
+  } else {
+    for (int it = 0; it + 1 < ntiles; ++it) tile(it, F_{});
+    tile(ntiles - 1, T_{});
   }
 
   // Normalise and store O[b, q, h*DH + dh] (token-major, heads concatenated).
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float l = l_run[qb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    float l;
+    if constexpr (DMA) {
+      l = __shfl(oacc[4][qb][0], 32 + c16, 64);   // O^T row 72: lane group 2, element 0
+    } else {
+      l = l_run[qb];
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+    }
     const float inv = 1.0f / l;
     const int q = q0 + 16 * qb + c16;
     if (q >= T) continue;
@@ -384,7 +425,6 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
 // and 73..79 are 0, so O^T row 72 is the sum of the (bf16) weights
 // themselves: the normaliser comes out of the same products as the
 // numerator.
-typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // NT = ceil(T / 64) key tiles; RAG: T is not a multiple of 64 (mask keys >= T)
 template <int NT, bool RAG>
