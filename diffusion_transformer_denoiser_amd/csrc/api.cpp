@@ -178,8 +178,6 @@ const void* woff(const void* base, size_t elems, int es) {
 }
 
 
-// One adaLN-Zero block on the residual stream X [rows*T, d] (fp32, in place).
-// mod + base points at this block's (b1, g1, a1, b2, g2, a2) in rows of mod_stride.
 // Patch embedding of M tokens (see launch_patch_embed); patch vectors whose
 // length is not a multiple of 16 go through the VALU GEMM with the patch
 // gather as its A loader.
@@ -205,6 +203,8 @@ struct Packed {
   SeqTable seqs;
 };
 
+// One adaLN-Zero block on the residual stream X [rows*T, d] (fp32, in place).
+// mod + base points at this block's (b1, g1, a1, b2, g2, a2) in rows of mod_stride.
 int run_block(const dit_handle* h, int l, int rows, float* X, const float* mod, int mod_stride,
               int base, void* ws, const WsLayout& L, float* o_branch, float* f_branch,
               hipStream_t s, const Packed* pk = nullptr) {

@@ -526,11 +526,33 @@ __global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const bf16_t* __restric
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
   const int tiles_n = (Nj + BN - 1) / BN, tiles_m = (Mi + BM - 1) / BM;
-  int tm, tn;
-  tile_coords<1>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b, in
+  // x-fastest order, on XCD b % 8), each with its own L2.  When the counts
+  // allow, XCD x takes one contiguous eighth of the tiles, cut across the
+  // wider operand, for every layer in turn: the tiles it runs together then
+  // share all of the narrow operand's columns and one eighth of the wide
+  // one's, and each reduction slab is fetched into that L2 once.
+  const int ntile = tiles_m * tiles_n;
+  const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+  int tm, tn, layer;
+  if ((ntile & 7) == 0) {
+    const int per = ntile >> 3, q = lin >> 3;
+    const int tl = (lin & 7) * per + q % per;
+    layer = q / per;
+    if (Nj >= Mi) {
+      tn = tl / tiles_m;
+      tm = tl - tn * tiles_m;
+    } else {
+      tm = tl / tiles_n;
+      tn = tl - tm * tiles_n;
+    }
+  } else {
+    tile_coords<1>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    layer = blockIdx.y;
+  }
   const int i0 = tm * BM, j0 = tn * BN;
   // this layer's slice of the reduction
-  const int rb = blockIdx.y * ksplit;
+  const int rb = layer * ksplit;
   const int Rl = min(ksplit, R - rb);
   A += (int64_t)rb * lda;
   B += (int64_t)rb * ldb;
