@@ -24,35 +24,11 @@
 #include <type_traits>
 
 #include "common.h"
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
-typedef __attribute__((address_space(3))) void lds_void;
+#include "mfma_util.h"
 
 namespace {
 
 constexpr int KSTEP = 64;   // K must be a multiple of this (every slice width used divides it)
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// s_waitcnt with only the LDS/scalar counter constrained to 0.
-__device__ __forceinline__ void wait_lgkm0() {
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
-}
-
-// Workgroup barrier without the release fence of __syncthreads() (which would
-// drain every outstanding copy); callers order memory with explicit waits.
-__device__ __forceinline__ void bare_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs (each with
 // its own L2): with SWZ, XCD x = b % 8 runs workgroups b = x, x + 8, ..., and
@@ -704,9 +680,16 @@ __global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const bf16_t* __restric
 hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, int M, int N,
                             int K, const EpiParams& ep, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (gemm_wide_supported(epi, A, lda, W, M, N, K, ep) &&
-      ((M + 255) / 256) * (N % 288 == 0 ? N / 288 : N / 256) >= DIT_WIDE_MIN_TILES)
-    return launch_gemm_wide(epi, A, lda, W, M, N, K, ep, s);
+  // The wide-tile kernel runs one persistent workgroup per CU, so it pays only
+  // when its tiles fill whole rounds of 256: at least 95% of the last round.
+  // Otherwise (e.g. M = 16,512 or 24,960 token rows) the 128 x 192 kernel
+  // below, two workgroups per CU, measured equal or faster.
+  if (gemm_wide_supported(epi, A, lda, W, M, N, K, ep)) {
+    const int64_t wt = (int64_t)((M + 255) / 256) * (N % 288 == 0 ? N / 288 : N / 256);
+    const int64_t slots = (wt + 255) / 256 * 256;
+    if (wt >= DIT_WIDE_MIN_TILES && wt * 20 >= slots * 19)
+      return launch_gemm_wide(epi, A, lda, W, M, N, K, ep, s);
+  }
   if (K % KSTEP || lda % 8 || (ep.ldw && (ep.ldw % 8 || ep.ldw < K))) return hipErrorInvalidValue;
   if (ep.ksplit < 0 || ep.ksplit % KSTEP || (ep.ksplit && epi != EPI_ATOMIC_F32) ||
       (epi == EPI_ATOMIC_F32 && ep.bias))
