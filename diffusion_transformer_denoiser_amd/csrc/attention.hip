@@ -172,8 +172,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
     doff[u] = (int)(((int64_t)row * ld + (col < DH / 8 ? col : 0) * 8) * 2);
     if (isv && col == DH / 8) dpad |= 1u << u;
   }
-  auto dma = [&](int kv0, int buf) {
-    const bool ragged = kv0 + KV > T;      // uniform
+  auto dma = [&](int kv0, int buf, auto rag_c) {
+    constexpr bool ragged = decltype(rag_c)::value;   // the tile reaches past T
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
       const int ii = wave + NWV * u;                // wave-uniform
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
         const bool isv = ii >= NCK;
         char* dst = (isv ? (char*)sV[buf] : (char*)sK[buf]) + (isv ? ii - NCK : ii) * 1024;
         int voff_ = doff[u], soff = kv0 * ldb;
-        if (ragged) {
+        if constexpr (ragged) {
           voff_ += (min(kv0 + drow[u], T - 1) - drow[u]) * ldb;
           soff = 0;
         }
@@ -245,7 +245,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
     for (int i = tid; i < 2 * KV; i += NTH)
       *(uint4*)&sV[i / KV][(i % KV) * VS + DH] = make_uint4(0x3F80u, 0, 0, 0);
     __syncthreads();
-    dma(0, 0);
+    if (ntiles == 1 && T % KV) dma(0, 0, std::true_type{});
+    else dma(0, 0, std::false_type{});
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed
   } else {
     gload(0);
@@ -255,11 +256,11 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
   // One 64-key tile; RAG: the last tile of a length that is not a multiple
   // of 64 (keys >= T masked).  For dh 72 only that one tile carries the
   // masking code; dh 64 tests at run time.
-  auto tile = [&](int it, auto rag_c) {
+  auto tile = [&](int it, auto rag_c, auto next_rag_c) {
     constexpr bool RAG = decltype(rag_c)::value;
     const int buf = it & 1, kv0 = it * KV;
     if (it + 1 < ntiles) {                   // next tile in flight during this one
-      if constexpr (DMA) dma(kv0 + KV, buf ^ 1);
+      if constexpr (DMA) dma(kv0 + KV, buf ^ 1, next_rag_c);
       else gload(kv0 + KV);
     }
 
@@ -382,10 +383,12 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
   using T_ = std::true_type;
   using F_ = std::false_type;
   if (T % KV == 0 || !DMA) {           // (dh 64 keeps one loop body: registers)
-    for (int it = 0; it < ntiles; ++it) tile(it, F_{});
+    for (int it = 0; it < ntiles; ++it) tile(it, F_{}, F_{});
   } else {
-    for (int it = 0; it + 1 < ntiles; ++it) tile(it, F_{});
-    tile(ntiles - 1, T_{});
+    // only the copy of the ragged last tile clamps its rows, only that tile masks
+    for (int it = 0; it + 2 < ntiles; ++it) tile(it, F_{}, F_{});
+    if (ntiles >= 2) tile(ntiles - 2, F_{}, T_{});
+    tile(ntiles - 1, T_{}, F_{});
   }
 
   // Normalise and store O[b, q, h*DH + dh] (token-major, heads concatenated).
