@@ -286,36 +286,69 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(const bf16_t* __restrict
       // one batch row (T % 16 == 0).  One column block at a time, the next
       // block's residual values loaded before the current block is stored.
       float* X = (float*)ep.out;
-      const float* gp[NI];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int brow = min(rbase - 4 * g + 16 * i, M - 1) / ep.T;
-        gp[i] = ep.mod ? ep.mod + (int64_t)brow * ep.mod_stride + ep.gate_off + cbase : nullptr;
-      }
-      auto xaddr = [&](int i, int r, int j) {
-        return X + (int64_t)(rbase + 16 * i + r) * ep.ldo + cbase + 16 * j;
-      };
       if (full) {
-        float xv[2][NI][4], gv[2][NI];
+        // Buffer addressing: one lane offset, the row offsets of (i, r) in
+        // scalar registers, the column block as the immediate.  Three column
+        // blocks of residual and gate loads are in flight; block j is stored
+        // before the loads of block j + 3 are issued.  Without a gate the
+        // loads read X and the gate is 1.
+        constexpr int D = 3;
+        const int ldb = ep.ldo * 4;
+        const __amdgpu_buffer_rsrc_t xrs =
+            __builtin_amdgcn_make_buffer_rsrc(X, (short)0, M * ldb, 0x00020000);
+        const int xo = rbase * ldb + cbase * 4;
+        const bool gated = ep.mod != nullptr;
+        const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
+            gated ? (void*)ep.mod : (void*)X, (short)0,
+            gated ? ((M - 1) / ep.T + 1) * ep.mod_stride * 4 : M * ldb, 0x00020000);
+        const int go = gated ? (ep.gate_off + cbase) * 4 : xo;
+        // scalar offsets: the wave index is uniform, which the compiler cannot see
+        const int wrow = __builtin_amdgcn_readfirstlane(em0 + wm * 64);
+        int gso[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          gso[i] = gated ? (min(wrow + 16 * i, M - 1) / ep.T) * ep.mod_stride * 4 : 0;
+        // the gate word is masked rather than selected, so that the loads stay
+        // unconditional and in issue order (no branch around them)
+        const uint32_t gmask = gated ? ~0u : 0u, gone = gated ? 0u : 0x3F800000u;
+        float xv[D][NI][4];
+        uint32_t gv[D][NI];
         auto load = [&](int j) {
 #pragma unroll
           for (int i = 0; i < NI; ++i) {
-            gv[j & 1][i] = gp[i] ? gp[i][16 * j] : 1.0f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) xv[j & 1][i][r] = *xaddr(i, r, j);
-          }
-        };
-        load(0);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          if (j + 1 < NJ) load(j + 1);
-#pragma unroll
-          for (int i = 0; i < NI; ++i)
+            gv[j % D][i] = __builtin_amdgcn_raw_buffer_load_b32(grs, go + 64 * j, gso[i], 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              *xaddr(i, r, j) = xv[j & 1][i][r] + gv[j & 1][i] * acc[i][j][r];
+              xv[j % D][i][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                  xrs, xo + 64 * j, (16 * i + r) * ldb, 0));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        };
+#pragma unroll
+        for (int j = 0; j < D; ++j) load(j);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            const float gt = __uint_as_float((gv[j % D][i] & gmask) | gone);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  __float_as_uint(__builtin_fmaf(gt, acc[i][j][r], xv[j % D][i][r])), xrs,
+                  xo + 64 * j, (16 * i + r) * ldb, 0);
+          }
+          if (j + D < NJ) load(j + D);
         }
       } else {
+        const float* gp[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int brow = min(rbase - 4 * g + 16 * i, M - 1) / ep.T;
+          gp[i] = ep.mod ? ep.mod + (int64_t)brow * ep.mod_stride + ep.gate_off + cbase : nullptr;
+        }
+        auto xaddr = [&](int i, int r, int j) {
+          return X + (int64_t)(rbase + 16 * i + r) * ep.ldo + cbase + 16 * j;
+        };
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -378,6 +411,10 @@ bool gemm_wide_supported(int epi, const bf16_t* A, int lda, const bf16_t* W, int
   if ((epi == EPI_BIAS_DT || epi == EPI_GELU) && (((uintptr_t)ep.out & 3) || ep.ldo % 2))
     return false;   // bf16 outputs stored as 4-byte column pairs
   if (epi == EPI_GATED && ep.mod && (ep.T <= 0 || ep.T % 16)) return false;
+  if (epi == EPI_GATED) {   // residual and gates through buffer descriptors
+    if (ep.ldo < N || (int64_t)M * ep.ldo * 4 >= (1LL << 31)) return false;
+    if (ep.mod && (int64_t)((M - 1) / ep.T + 1) * ep.mod_stride * 4 >= (1LL << 31)) return false;
+  }
   return true;
 }
 

@@ -268,6 +268,12 @@ def _full_size_sampled(name, sample_rows, blocks, oracle_rows=()):
     out_nt = np_(m.cfg_forward(x, t, y, cfg["scale"], cfg["guided"]))
     torch.cuda.synchronize()
     assert np.array_equal(out_nt, out), "untapped forward differs from the tapped one"
+    # The forward writes every workspace byte before it reads it: with the
+    # workspace filled with NaN bytes first, the output is unchanged bit for bit.
+    m.workspace(rows).fill_(0xFF)
+    out_p = np_(m.cfg_forward(x, t, y, cfg["scale"], cfg["guided"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(out_p, out_nt), "forward read workspace bytes it had not written"
     if oracle_rows:
         r = list(oracle_rows)
         ref_g = oracle.cfg_forward(cfg, w, inp["x_t"][r], inp["t"][r], inp["y"][r], cfg["scale"],

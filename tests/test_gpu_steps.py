@@ -184,6 +184,10 @@ def test_linear_wide_tiles(M, N, K):
     log(f"  rel-L2 bias={e1:.2e} gelu={e2:.2e} bias-dtype={e3:.2e} gated-increment={e4:.2e}")
     assert np.isfinite(o).all() and np.isfinite(Xg).all()
     assert e1 <= 1e-5 and e4 <= 1e-5
+    # every row: the gated update is X + gate * (the bias epilogue's fp32 output,
+    # the same accumulators), up to the fp32 rounding of the product and sum
+    upd = X0 + gate[np.arange(M) // T].astype(np.float64) * o
+    assert np.abs(Xg - upd).max() <= 2 ** -23 * (np.abs(upd).max() + np.abs(X0).max())
     assert e2 <= 4e-3 and e3 <= 4e-3
 
 
