@@ -31,6 +31,17 @@ namespace {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
+// 8 bf16 query features times the exp2-domain score scale, rounded to bf16
+// once (round to nearest even): scores then come out of the MFMA already in
+// the exp2 domain.
+__device__ __forceinline__ bf16x8_t scale_bf16x8(bf16x8_t v, float sc) {
+  const uint4 u = __builtin_bit_cast(uint4, v);
+  auto two = [&](uint32_t w) {
+    return f2bf2(__uint_as_float(w << 16) * sc, __uint_as_float(w & 0xFFFF0000u) * sc);
+  };
+  return __builtin_bit_cast(bf16x8_t, make_uint4(two(u.x), two(u.y), two(u.z), two(u.w)));
+}
+
 // PK: packed sequences.  The grid is (query blocks of all sequences, heads);
 // a block finds its sequence in the by-value table and attends over that
 // sequence's tokens only.
@@ -105,10 +116,10 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
     bool ok = q < T;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      qf[qb][c] = ok ? *(const bf16x8_t*)(Qb + q * ld + 32 * c + 8 * g) : z8;
+      qf[qb][c] = ok ? scale_bf16x8(*(const bf16x8_t*)(Qb + q * ld + 32 * c + 8 * g), sl2) : z8;
     qt[qb] = z8;   // dh 64..71 in lanes g == 0, zeros elsewhere
     if constexpr (TAIL)
-      if (ok && g == 0) qt[qb] = *(const bf16x8_t*)(Qb + q * ld + 64);
+      if (ok && g == 0) qt[qb] = scale_bf16x8(*(const bf16x8_t*)(Qb + q * ld + 64), sl2);
   }
 
   // Tile staging: global -> registers (issued one tile ahead) -> LDS.  Loads
@@ -231,7 +242,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
     }
   };
 
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+  // Reference maximum of the exp2-domain scores per query column; the first
+  // tile sets it, later tiles only raise it.
+  float m_run[2] = {0.0f, 0.0f}, l_run[2] = {0.0f, 0.0f};
   floatx4 oacc[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -264,7 +277,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
       else gload(kv0 + KV);
     }
 
-    // S^T blocks: 4 key blocks x 2 query blocks of 16x16.
+    // S^T blocks: 4 key blocks x 2 query blocks of 16x16, in the exp2 domain
+    // relative to the reference maximum: K (sl2 Q)^T - m_run (the
+    // accumulators start at -m_run).
     floatx4 s[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -276,7 +291,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
         kt = *(const bf16x8_t*)(g == 0 ? kr + 64 : (const bf16_t*)&zslot);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        floatx4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+        const float mi = -m_run[qb];
+        floatx4 a = {mi, mi, mi, mi};
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[qb][0], a, 0, 0, 0);
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[qb][1], a, 0, 0, 0);
         if constexpr (TAIL) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, qt[qb], a, 0, 0, 0);
@@ -296,9 +312,10 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
 
     // Online softmax in the exp2 domain.  Lane holds query column c16 of block
     // qb and keys 16 kb + 4 g + r; the 4 lanes sharing c16 combine by xor 16, 32.
-    // The running max m_run (scaled) is raised only when some query's tile max
-    // exceeds it by RESCALE_SLACK, so P stays <= 2^RESCALE_SLACK and O, l are
-    // rescaled rarely; l and O always share the same reference m_run.
+    // The first tile sets the reference maximum m_run; later it is raised only
+    // when some query's tile maximum exceeds it by RESCALE_SLACK, so P stays
+    // <= 2^RESCALE_SLACK and O, l are rescaled rarely; l and O always share
+    // the same reference.  The scores, relative to m_run, follow it.
     bf16x8_t pf[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -307,28 +324,35 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mxs = mx * sl2;
-      if (__any(mxs > m_run[qb] + RESCALE_SLACK)) {
-        const float m_new = fmaxf(m_run[qb], mxs);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        if constexpr (!DMA) l_run[qb] *= alpha;
+      // the test needs each lane's own maximum only; the query column's (over
+      // the 4 lanes sharing c16) is formed when the reference moves
+      if (__any(it == 0 || mx > RESCALE_SLACK)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // key 0 lies in the first tile, so its maximum is finite
+        const float delta = it == 0 ? mx : fmaxf(mx, 0.0f);
+        m_run[qb] += delta;
+        if (it > 0) {
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+          if constexpr (!DMA) l_run[qb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) oacc[db][qb][r] *= alpha;
+            for (int r = 0; r < 4; ++r) oacc[db][qb][r] *= alpha;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[kb][qb][r] -= delta;
       }
-      const float mneg = -m_run[qb];
       float ls = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 4; kb += 2) {
         float p[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], sl2, mneg));
-          p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s[kb + 1][qb][r], sl2, mneg));
+          p[r] = __builtin_amdgcn_exp2f(s[kb][qb][r]);
+          p[4 + r] = __builtin_amdgcn_exp2f(s[kb + 1][qb][r]);
         }
         if constexpr (!DMA)
 #pragma unroll
