@@ -73,7 +73,10 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
   // normaliser comes out of the same products as the numerator.
   constexpr int VS = 80;
   constexpr int VSZ = DMA ? KV * VS : DH * VLD;
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KV * KLD];
+  // K tiles carry 24 zero elements after their last row: the dh 64..95 operand
+  // reads of the last rows reach into them (see the score products)
+  constexpr int KPAD = 24;
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KV * KLD + KPAD];
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][VSZ];
   // 16 zero bytes: operand lanes past dh read here instead of taking a branch
   __shared__ __attribute__((aligned(16))) uint4 zslot;
@@ -245,6 +248,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
   // Reference maximum of the exp2-domain scores per query column; the first
   // tile sets it, later tiles only raise it.
   float m_run[2] = {0.0f, 0.0f}, l_run[2] = {0.0f, 0.0f};
+  floatx4 ainit[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};   // -m_run
+  // ds_bpermute byte addresses of lanes xor 16 and xor 32
+  const int bp16 = (lane ^ 16) << 2, bp32 = (lane ^ 32) << 2;
   floatx4 oacc[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -253,6 +259,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
 
   const int ntiles = (T + KV - 1) / KV;
   if (tid == 0) zslot = make_uint4(0, 0, 0, 0);
+  if (tid < 2 * KPAD / 8) *(uint4*)&sK[tid / (KPAD / 8)][KV * KLD + 8 * (tid % (KPAD / 8))] = make_uint4(0, 0, 0, 0);
   if constexpr (DMA) {
     // The (1, 0, .., 0) column chunk of every V row of both buffers, once.
     for (int i = tid; i < 2 * KV; i += NTH)
@@ -286,13 +293,14 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
       const bf16_t* kr = &sK[buf][(16 * kb + c16) * KLD];
       bf16x8_t k0 = *(const bf16x8_t*)(kr + 8 * g);
       bf16x8_t k1 = *(const bf16x8_t*)(kr + 32 + 8 * g);
+      // dh 64..95: lanes g > 0 read past dh 72 (the next row, or the zero pad
+      // after the last one); the query operand is zero there, so the products
+      // only need those values finite
       bf16x8_t kt = z8;
-      if constexpr (TAIL)
-        kt = *(const bf16x8_t*)(g == 0 ? kr + 64 : (const bf16_t*)&zslot);
+      if constexpr (TAIL) kt = *(const bf16x8_t*)(kr + 64 + 8 * g);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const float mi = -m_run[qb];
-        floatx4 a = {mi, mi, mi, mi};
+        floatx4 a = ainit[qb];
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[qb][0], a, 0, 0, 0);
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[qb][1], a, 0, 0, 0);
         if constexpr (TAIL) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, qt[qb], a, 0, 0, 0);
@@ -327,11 +335,12 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
       // the test needs each lane's own maximum only; the query column's (over
       // the 4 lanes sharing c16) is formed when the reference moves
       if (__any(it == 0 || mx > RESCALE_SLACK)) {
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(bp16, __float_as_int(mx))));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(bp32, __float_as_int(mx))));
         // key 0 lies in the first tile, so its maximum is finite
         const float delta = it == 0 ? mx : fmaxf(mx, 0.0f);
         m_run[qb] += delta;
+        ainit[qb] = floatx4{-m_run[qb], -m_run[qb], -m_run[qb], -m_run[qb]};
         if (it > 0) {
           const float alpha = __builtin_amdgcn_exp2f(-delta);
           if constexpr (!DMA) l_run[qb] *= alpha;
@@ -461,9 +470,10 @@ __global__ __launch_bounds__(512) void attn_short_kernel(const bf16_t* __restric
   constexpr int DH = 72, NWV = 8, KS = 72, VS = 80, NDB = 5;
   constexpr int NCH = 256 * (DH / 8);               // 16-byte chunks of K (or V) per pair
   constexpr int CPT = (NCH + 64 * NWV - 1) / (64 * NWV);
-  __shared__ __attribute__((aligned(16))) bf16_t sK[256 * KS];
+  // 24 zero elements after K's last row: the dh 64..95 operand reads of the
+  // last rows reach into them (see s_tile)
+  __shared__ __attribute__((aligned(16))) bf16_t sK[256 * KS + 24];
   __shared__ __attribute__((aligned(16))) bf16_t sV[256 * VS];
-  __shared__ __attribute__((aligned(16))) uint4 zslot;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -534,7 +544,7 @@ __global__ __launch_bounds__(512) void attn_short_kernel(const bf16_t* __restric
   int pair = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
   if (pair >= npairs) return;
   if (tid < 256) *(uint4*)&sV[tid * VS + DH] = make_uint4(0x3F80u, 0, 0, 0);   // (1, 0, .., 0)
-  if (tid == 0) zslot = make_uint4(0, 0, 0, 0);
+  if (tid < 3) *(uint4*)&sK[256 * KS + 8 * tid] = make_uint4(0, 0, 0, 0);
   bf16x8_t qn[2][2], qtn[2];
   load_q(pair, qn, qtn);
   gload(pair);
@@ -566,7 +576,10 @@ __global__ __launch_bounds__(512) void attn_short_kernel(const bf16_t* __restric
         const bf16_t* kr = sK + (64 * t + 16 * kb + c16) * KS;
         const bf16x8_t k0 = *(const bf16x8_t*)(kr + 8 * g);
         const bf16x8_t k1 = *(const bf16x8_t*)(kr + 32 + 8 * g);
-        const bf16x8_t kt = *(const bf16x8_t*)(g == 0 ? kr + 64 : (const bf16_t*)&zslot);
+        // dh 64..95: lanes g > 0 read past dh 72 (the next row, or the zero
+        // pad after the last one); their query operand is zero, so the
+        // products only need those values finite
+        const bf16x8_t kt = *(const bf16x8_t*)(kr + 64 + 8 * g);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
