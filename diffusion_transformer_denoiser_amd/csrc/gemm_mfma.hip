@@ -681,13 +681,15 @@ hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, 
                             int K, const EpiParams& ep, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   // The wide-tile kernel runs one persistent workgroup per CU, so it pays only
-  // when its tiles fill whole rounds of 256: at least 95% of the last round.
-  // Otherwise (e.g. M = 16,512 or 24,960 token rows) the 128 x 192 kernel
-  // below, two workgroups per CU, measured equal or faster.
+  // when its tiles fill its rounds of 256 workgroups: to 95% for the gated
+  // residual epilogue, whose read-modify-write the 128 x 192 kernel below (two
+  // workgroups per CU) overlaps with the other workgroup's products, and to
+  // 85% for the others (measured at M = 16,512 and 24,960 token rows).
   if (gemm_wide_supported(epi, A, lda, W, M, N, K, ep)) {
     const int64_t wt = (int64_t)((M + 255) / 256) * (N % 288 == 0 ? N / 288 : N / 256);
     const int64_t slots = (wt + 255) / 256 * 256;
-    if (wt >= DIT_WIDE_MIN_TILES && wt * 20 >= slots * 19)
+    const int64_t fill20 = epi == EPI_GATED ? 19 : 17;   // twentieths
+    if (wt >= DIT_WIDE_MIN_TILES && wt * 20 >= slots * fill20)
       return launch_gemm_wide(epi, A, lda, W, M, N, K, ep, s);
   }
   if (K % KSTEP || lda % 8 || (ep.ldw && (ep.ldw % 8 || ep.ldw < K))) return hipErrorInvalidValue;

@@ -140,13 +140,16 @@ def test_linear_epilogues(M, N, K, dtype):
 
 
 # Shapes around the wide-tile kernel (256 x 288 or 256 x 256 tiles, taken when
-# they fill whole rounds of 256 workgroups to 95%): the four block products at
-# M = 16384, a ragged last row tile (M = 16284: 156 rows; 256 tiles), the
-# 256-wide variant (N = 1024), and two shapes whose tiles would leave most of
-# a round empty and so take the 128 x 192 kernel (M = 16500; N = 1280).
+# they fill their rounds of 256 workgroups to 95%, or to 85% for the epilogues
+# without the gated residual): the four block products at M = 16384, a ragged
+# last row tile (M = 16284: 156 rows; 256 tiles), the 256-wide variant
+# (N = 1024), two shapes whose tiles would leave most of a round empty and so
+# take the 128 x 192 kernel (M = 16500; N = 1280), and one at 90% fill, where
+# the bias and GELU epilogues take the wide kernel and the gated one the
+# 128 x 192 kernel (M = 29440: 460 tiles).
 WIDE_SHAPES = [(16384, 3456, 1152), (16384, 1152, 1152), (16384, 4608, 1152),
                (16384, 1152, 4608), (16284, 1152, 1152), (16384, 1024, 1152),
-               (16500, 1152, 1152), (16384, 1280, 1152)]
+               (16500, 1152, 1152), (16384, 1280, 1152), (29440, 1152, 1152)]
 
 
 @pytest.mark.parametrize("M,N,K", WIDE_SHAPES)
