@@ -139,6 +139,26 @@ def test_train_step_xl_width_two_blocks():
     assert not bad, bad
 
 
+def test_train_step_xl_width_batch16():
+    """DiT-XL/2 width with one block at batch 16 (M = 4096 token rows, 16 row
+    tiles per product): both loss terms and every gradient against the fp64
+    oracle's autograd."""
+    cfg = dit_inputs.workload("dit_xl2_256_cfg", N=1, batch=16)
+    w = dit_inputs.make_weights(cfg)
+    m = dmod.DiT(cfg, w, "cuda")
+    x0, y, t, eps = make_batch(dict(cfg, batch=16), 23)
+    log("XL/2 width, N=1, B=16, bf16")
+    loss = np_(m.train_step(*to_dev(x0, y, t, eps), step=1))
+    torch.cuda.synchronize()
+    ls, lv, g = TR.gradients(cfg, w, x0, y, t, eps)
+    log(f"  loss GPU {loss} oracle ({ls:.6f}, {lv:.6f})")
+    assert abs(loss[0] - ls) <= BF16_TOL * ls and abs(loss[1] - lv) <= BF16_TOL * abs(lv)
+    errs = {n: rel_l2(np_(m.train_view("grad", n)), g[n]) for n in TR.TRAIN_FIELDS}
+    log("  grad rel-L2: " + ", ".join(f"{n}={e:.1e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e <= BF16_TOL}
+    assert not bad, bad
+
+
 def _train_inputs_dev(cfg, B=None):
     inp = dit_inputs.make_train_inputs(cfg, batch=B)
     return to_dev(inp["x0"], inp["y"], inp["t"], inp["noise"])
