@@ -348,6 +348,56 @@ def test_attention_many_sequences_bf16(B, H, T):
     assert err <= 1e-2 and worst <= 1e-2
 
 
+@pytest.mark.parametrize("T", [256, 300, 1024])
+def test_attention_growing_scores_rescale_bf16(T):
+    # Keys grow tile by tile, so each 64-key tile's largest score exceeds the
+    # previous ones by about 12 in the exp2 domain: every tile raises the
+    # reference maximum of the online softmax (T = 256 runs the short-sequence
+    # kernel, 300 and 1024 the streaming one).  A query of the opposite sign
+    # sees the scores fall instead, so only the first tile sets its reference.
+    B, H, dh = 1, 2, 72
+    rng = np.random.default_rng(T + 17)
+    tile = np.arange(T) // 64
+    q = np.ones((B, H, T, dh), np.float32)
+    q[:, :, 1::2] = -1.0
+    k = (tile[None, None, :, None] + 0.25 * rng.standard_normal((B, H, T, dh))).astype(np.float32)
+    v = rng.standard_normal((B, H, T, dh)).astype(np.float32)
+    q, k, v = _bf16(q), _bf16(k), _bf16(v)
+    qkv = torch.from_numpy(_pack(q, k, v)).to(torch.bfloat16).cuda()
+    o = np_(dmod.attention(qkv, H)).reshape(B, T, H, dh).transpose(0, 2, 1, 3)
+    ref = oracle.attention(q, k, v)
+    err = rel_l2(o, ref)
+    log(f"attention T={T} growing scores: rel-L2 {err:.2e}")
+    assert np.isfinite(o).all() and err <= 1e-2
+
+
+@pytest.mark.parametrize("T,jump", [(256, 1), (256, 3), (300, 4), (1024, 1), (1024, 9)])
+def test_attention_rescale_keeps_earlier_tiles_bf16(T, jump):
+    # Tile 0's 64 keys score 0; one key of tile `jump` scores 9 above them in
+    # the exp2 domain (past the online softmax's slack of 8, so the reference
+    # moves and the earlier output is rescaled); every other key scores -72.
+    # Tile 0 then holds 64 / (64 + 2^9), about 11%, of the weight: a wrong
+    # rescale factor or a missed shift of the pending scores shows in the output.
+    B, H, dh = 1, 2, 72
+    rng = np.random.default_rng(T * 7 + jump)
+    sl2 = 1.4426950408889634 / np.sqrt(dh)
+    q = np.ones((B, H, T, dh), np.float32)
+    k = np.full((B, H, T, dh), -1.0, np.float32)
+    k[:, :, :64] = 0.0
+    k[:, :, 64 * jump + 5] = 9.0 / sl2 / dh
+    v = rng.standard_normal((B, H, T, dh)).astype(np.float32)
+    q, k, v = _bf16(q), _bf16(k), _bf16(v)
+    qkv = torch.from_numpy(_pack(q, k, v)).to(torch.bfloat16).cuda()
+    o = np_(dmod.attention(qkv, H)).reshape(B, T, H, dh).transpose(0, 2, 1, 3)
+    ref = oracle.attention(q, k, v)
+    s = q[0, 0, 0].astype(np.float64) @ k[0, 0].astype(np.float64).T / np.sqrt(dh)
+    w0 = np.exp(s[:64]).sum() / np.exp(s).sum()
+    err = rel_l2(o, ref)
+    log(f"attention T={T}, jump at tile {jump}: weight of tile 0 {w0:.3f}, rel-L2 {err:.2e}")
+    assert 0.05 < w0 < 0.2
+    assert np.isfinite(o).all() and err <= 1e-2
+
+
 def test_attention_special_cases_bf16():
     # all keys equal => uniform weights => mean of v; T = 1 => v.
     B, H, T, dh = 1, 2, 100, 72
