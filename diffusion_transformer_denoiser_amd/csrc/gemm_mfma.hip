@@ -486,6 +486,11 @@ hipError_t pick(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
 // column per lane) come from pairs of ds_read_b64_tr_b16.  The grid's second
 // dimension splits r (ksplit rows per layer, a multiple of 64) and every layer
 // adds its partial sums atomically.
+// BUF: the copies go through buffer descriptors over the layer's slab of r
+// (32-bit byte offsets), which the compiler leaves to the explicit waits of
+// the loop; the plain global->LDS form makes it drain every copy in flight,
+// the next slice's included, before the first LDS read of each slice.
+template <bool BUF>
 __global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const bf16_t* __restrict__ A, int lda,
                                                          const bf16_t* __restrict__ B, int ldb,
                                                          int Mi, int Nj, int R, int ksplit,
@@ -550,17 +555,34 @@ __global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const bf16_t* __restric
     const int lc = (sl % CB - 4 * (row & 3) + 4 * CB) % CB;
     boff[c] = row * ldb + min(j0 + lc * 8, Nj - 8);
   }
+  [[maybe_unused]] const __amdgpu_buffer_rsrc_t ars =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, BUF ? Rl * lda * 2 : 0, 0x00020000);
+  [[maybe_unused]] const __amdgpu_buffer_rsrc_t brs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, BUF ? Rl * ldb * 2 : 0, 0x00020000);
   auto copy = [&](int kt) {
     char* st = smem + (kt & 1) * STAGE;
-    const int64_t ra = (int64_t)kt * BK * lda, rbb = (int64_t)kt * BK * ldb;
+    if constexpr (BUF) {
+#if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
-    for (int c = 0; c < NCA; ++c)
-      __builtin_amdgcn_global_load_lds((const void*)(A + ra + aoff[c]),
-                                       (lds_void*)(st + (w * NCA + c) * 1024), 16, 0, 0);
+      for (int c = 0; c < NCA; ++c)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void*)(st + (w * NCA + c) * 1024), 16,
+                                                 aoff[c] * 2, kt * BK * lda * 2, 0, 0);
 #pragma unroll
-    for (int c = 0; c < NCB; ++c)
-      __builtin_amdgcn_global_load_lds((const void*)(B + rbb + boff[c]),
-                                       (lds_void*)(st + OPA + (w * NCB + c) * 1024), 16, 0, 0);
+      for (int c = 0; c < NCB; ++c)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void*)(st + OPA + (w * NCB + c) * 1024),
+                                                 16, boff[c] * 2, kt * BK * ldb * 2, 0, 0);
+#endif
+    } else {
+      const int64_t ra = (int64_t)kt * BK * lda, rbb = (int64_t)kt * BK * ldb;
+#pragma unroll
+      for (int c = 0; c < NCA; ++c)
+        __builtin_amdgcn_global_load_lds((const void*)(A + ra + aoff[c]),
+                                         (lds_void*)(st + (w * NCA + c) * 1024), 16, 0, 0);
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+        __builtin_amdgcn_global_load_lds((const void*)(B + rbb + boff[c]),
+                                         (lds_void*)(st + OPA + (w * NCB + c) * 1024), 16, 0, 0);
+    }
   };
 
   // Transposing reads: lane s of 16-lane group G reads row 16 kk + 8 (G / 2) +
@@ -610,39 +632,38 @@ __global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const bf16_t* __restric
     wait_vmcnt<0>();
   }
   bare_barrier();
+  // Per slice: every fragment of the slice is read first; one barrier (the
+  // stage is read by every wave, slice kt + 1 has landed for every wave); the
+  // copies of slice kt + 2 refill the stage; then the MFMAs, from registers.
+  // The compiler makes each slice's first transposing read wait for all
+  // copies in flight, so those copies get one slice of MFMAs to land.
   for (int kt = 0; kt < nk; ++kt) {
     const char* st = smem + (kt & 1) * STAGE;
-    // fragments of k step kk + 1 are read while the MFMAs of step kk run
-    bf16x8_t fa[2][TM], fb[2][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[0][i] = frag(st, CA, wm * 64 + i * 32, 0);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) fb[0][j] = frag(st + OPA, CB, wn * 96 + j * 32, 0);
+    bf16x8_t fa[BK / 16][TM], fb[BK / 16][TN];
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk + 1 < BK / 16) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[nxt][i] = frag(st, CA, wm * 64 + i * 32, kk + 1);
+      for (int i = 0; i < TM; ++i) fa[kk][i] = frag(st, CA, wm * 64 + i * 32, kk);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[nxt][j] = frag(st + OPA, CB, wn * 96 + j * 32, kk + 1);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0,
-                                                              0, 0);
-      if (csum)
-#pragma unroll
-        for (int i = 0; i < TM; ++i) colsum(fa[cur][i], cs[i]);
+      for (int j = 0; j < TN; ++j) fb[kk][j] = frag(st + OPA, CB, wn * 96 + j * 32, kk);
     }
-    // this stage is read (by this wave; the barrier covers the others) and
-    // slice kt + 1, the only copies in flight, has landed
     wait_lgkm0();
     wait_vmcnt<0>();
     bare_barrier();
     if (kt + 2 < nk) copy(kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0,
+                                                              0, 0);
+      if (csum)
+#pragma unroll
+        for (int i = 0; i < TM; ++i) colsum(fa[kk][i], cs[i]);
+    }
   }
 
   if (csum) {
@@ -734,6 +755,9 @@ hipError_t launch_gemm_tn(const bf16_t* A, int lda, const bf16_t* B, int ldb, in
   int ks = (R + best - 1) / best;
   ks = (ks + 63) / 64 * 64;
   const dim3 grid(tiles, (R + ks - 1) / ks);
-  gemm_tn_kernel<<<grid, 256, 0, s>>>(A, lda, B, ldb, Mi, Nj, R, ks, out, ldo, asum);
+  if ((int64_t)ks * lda * 2 < (1LL << 31) && (int64_t)ks * ldb * 2 < (1LL << 31))
+    gemm_tn_kernel<true><<<grid, 256, 0, s>>>(A, lda, B, ldb, Mi, Nj, R, ks, out, ldo, asum);
+  else
+    gemm_tn_kernel<false><<<grid, 256, 0, s>>>(A, lda, B, ldb, Mi, Nj, R, ks, out, ldo, asum);
   return hipGetLastError();
 }
