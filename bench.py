@@ -52,6 +52,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 METRIC = "DiT-XL/2 denoiser forwards/s + TFLOP/s (% MFMA peak) on 1 MI355X"
 REPEATS = 5
+KERNEL_NAMES = ("layernorm", "qkv", "attention", "out_proj", "fc1", "fc2")
 
 
 def parse():
@@ -79,7 +80,11 @@ def parse():
                     help="time packed mixed-resolution forwards (dit_forward_packed): 16 latents "
                          "of 32x32 and 4 of 64x64 in one call, against the same work as two "
                          "batched calls")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.kernel_launches < 1:
+        ap.error("--kernel-launches must be at least 1: the roofline figure comes from "
+                 "the hot kernels timed alone")
+    return args
 
 
 # ---------------------------------------------------------------------------
@@ -295,12 +300,19 @@ def time_launches(fn, n, stream):
     return e0.elapsed_time(e1) / n
 
 
-def kernel_table(cfg, model, rows, n_launch, dev):
-    """The forward's hot kernels at its shapes, each timed alone: the four
-    block products (wide-tile MFMA GEMM with the forward's epilogue), attention
-    and LayerNorm + modulate.  Consecutive GEMM launches cycle through the
-    model's per-block weights, as the forward does, so no launch finds its
-    weight matrix already cached."""
+def kernel_table(cfg, model, rows, n_launch, dev, in_forward):
+    """The forward's hot kernels at its shapes: the four block products
+    (wide-tile MFMA GEMM with the forward's epilogue), attention and LayerNorm +
+    modulate.
+
+    in_forward: {kernel: [ms per launch]} from the library's launch timer over
+    forwards (a HIP event pair on the forward's stream around each launch);
+    where a kernel has such launches their average is its figure
+    (``"timing": "in forward"``).  Each kernel is also timed alone, n_launch
+    launches in a row (the GEMMs cycling through the blocks' weights, as the
+    forward does, so no launch finds its weight matrix cached), reported as
+    ``avg_launch_us_alone`` and used where the forward has no timed launches
+    of it (the designs without adaLN-Zero blocks)."""
     import torch
     import diffusion_transformer_denoiser_amd as dm
     d, hid, H, N = cfg["d"], cfg["mlp_hidden"], cfg["heads"], cfg["N"]
@@ -308,68 +320,80 @@ def kernel_table(cfg, model, rows, n_launch, dev):
     M = rows * T
     dt = dm.torch_dtype(cfg["dtype"])
     es = 2 if dt == torch.bfloat16 else 4
+    dh = d // H
     stream = torch.cuda.current_stream(dev)
     tw = model.tensors
     g = torch.Generator(device=dev).manual_seed(7)
-    out = []
-
-    def entry(name, kernel, n_per_fwd, ms, flop, nbytes):
-        t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12) if flop else 0.0
-        t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
-        bound = "mfma" if t_mfma >= t_hbm else "hbm"
-        tf = flop / (ms * 1e-3) / 1e12 if flop else None
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        out.append({"name": name, "kernel": kernel, "launches_per_forward": n_per_fwd,
-                    "avg_launch_us": round(ms * 1e3, 2),
-                    "us_per_forward": round(ms * 1e3 * n_per_fwd, 1), "bound": bound,
-                    "tflops": round(tf, 1) if tf else None,
-                    "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4) if tf else None,
-                    "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-                    "algorithmic_flop": flop, "algorithmic_bytes": nbytes})
 
     Hb = torch.randn(M, d, device=dev, generator=g).to(dt)
     Gb = torch.randn(M, hid, device=dev, generator=g).to(dt)
     X = torch.randn(M, d, device=dev, generator=g)
     gate = torch.randn((M + T - 1) // T, d, device=dev, generator=g) * 0.1
-    nb = N
-
-    def gemm(name, epi, A, Wkey, bkey, n_out, n_in, outbuf, gated):
-        Ws = [tw[Wkey][l] for l in range(nb)]
-        bs = [tw[bkey][l] for l in range(nb)]
-        if gated:
-            fn = lambda i: dm.linear(epi, A, Ws[i % nb], bs[i % nb], outbuf, gate=gate,
-                                     gate_stride=d, T=T)
-        else:
-            fn = lambda i: dm.linear(epi, A, Ws[i % nb], bs[i % nb], outbuf)
-        ms = time_launches(fn, n_launch, stream)
-        flop = 2.0 * M * n_out * n_in
-        ob = M * n_out * (4 if gated else es) * (2 if gated else 1)   # gated: read + write X
-        nbytes = M * n_in * es + n_out * n_in * es + n_out * 4 + ob
-        epin = {dm.DIT_EPI_BIAS_DT: "bias", dm.DIT_EPI_GELU: "bias + tanh-GELU",
-                dm.DIT_EPI_GATED: "bias + gated fp32 residual"}[epi]
-        entry(name, f"{name}: GEMM M={M} N={n_out} K={n_in}, {epin} epilogue", nb, ms, flop,
-              nbytes)
-
     qkv = torch.empty(M, 3 * d, device=dev, dtype=dt)
     G = torch.empty(M, hid, device=dev, dtype=dt)
-    gemm("qkv", dm.DIT_EPI_BIAS_DT, Hb, "qkv_w", "qkv_b", 3 * d, d, qkv, False)
-    gemm("out_proj", dm.DIT_EPI_GATED, Hb, "o_w", "o_b", d, d, X, True)
-    gemm("fc1", dm.DIT_EPI_GELU, Hb, "fc1_w", "fc1_b", hid, d, G, False)
-    gemm("fc2", dm.DIT_EPI_GATED, Gb, "fc2_w", "fc2_b", d, hid, X, True)
+
+    def gemm(epi, A, Wkey, bkey, outbuf, gated):
+        Ws = [tw[Wkey][l] for l in range(N)]
+        bs = [tw[bkey][l] for l in range(N)]
+        if gated:
+            fn = lambda i: dm.linear(epi, A, Ws[i % N], bs[i % N], outbuf, gate=gate,
+                                     gate_stride=d, T=T)
+        else:
+            fn = lambda i: dm.linear(epi, A, Ws[i % N], bs[i % N], outbuf)
+        return time_launches(fn, n_launch, stream)
+
+    alone = {
+        "qkv": gemm(dm.DIT_EPI_BIAS_DT, Hb, "qkv_w", "qkv_b", qkv, False),
+        "out_proj": gemm(dm.DIT_EPI_GATED, Hb, "o_w", "o_b", X, True),
+        "fc1": gemm(dm.DIT_EPI_GELU, Hb, "fc1_w", "fc1_b", G, False),
+        "fc2": gemm(dm.DIT_EPI_GATED, Gb, "fc2_w", "fc2_b", X, True),
+    }
     del G
-    # attention over the packed q | k | v of every row
-    qkv.normal_(generator=g)
-    dh = d // H
-    ms = time_launches(lambda i: dm.attention(qkv.view(rows, T, 3 * d), H), n_launch, stream)
-    entry("attention", f"attention: {rows} rows x {H} heads, T={T}, dh={dh}", N, ms,
-          4.0 * rows * H * T * T * dh, rows * T * 4 * d * es)
-    # LayerNorm + modulate (two per block and the final layer's)
+    qkv.normal_(generator=g)     # attention over the packed q | k | v of every row
+    alone["attention"] = time_launches(lambda i: dm.attention(qkv.view(rows, T, 3 * d), H),
+                                       n_launch, stream)
     mod = torch.randn(rows, 6 * d, device=dev, generator=g) * 0.1
     Hn = torch.empty(M, d, device=dev, dtype=dt)
-    ms = time_launches(lambda i: dm.ln_modulate(X, mod, 0, d, T, Hn), n_launch, stream)
-    entry("layernorm", f"LayerNorm + modulate: M={M}, d={d}", 2 * N + 1, ms, 0.0,
-          M * d * (4 + es) + rows * 2 * d * 4)
+    alone["layernorm"] = time_launches(lambda i: dm.ln_modulate(X, mod, 0, d, T, Hn), n_launch,
+                                       stream)
     del Hb, Gb, X, qkv, Hn
+
+    epin = {"qkv": "bias", "out_proj": "bias + gated fp32 residual", "fc1": "bias + tanh-GELU",
+            "fc2": "bias + gated fp32 residual"}
+    shapes = {"qkv": (3 * d, d, False), "out_proj": (d, d, True), "fc1": (hid, d, False),
+              "fc2": (d, hid, True)}
+    out = []
+    for name in ("qkv", "out_proj", "fc1", "fc2", "attention", "layernorm"):
+        if name in shapes:
+            n_out, n_in, gated = shapes[name]
+            flop = 2.0 * M * n_out * n_in
+            out_b = M * n_out * (4 if gated else es) * (2 if gated else 1)  # gated: read + write X
+            nbytes = M * n_in * es + n_out * n_in * es + n_out * 4 + out_b
+            desc = f"{name}: GEMM M={M} N={n_out} K={n_in}, {epin[name]} epilogue"
+            per_fwd = N
+        elif name == "attention":
+            flop, nbytes = 4.0 * rows * H * T * T * dh, rows * T * 4 * d * es
+            desc, per_fwd = f"attention: {rows} rows x {H} heads, T={T}, dh={dh}", N
+        else:
+            flop, nbytes = 0.0, M * d * (4 + es) + rows * 2 * d * 4
+            desc, per_fwd = f"LayerNorm + modulate: M={M}, d={d}", 2 * N + 1
+        runs = in_forward.get(name, [])
+        ms = sum(runs) / len(runs) if runs else alone[name]
+        t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12) if flop else 0.0
+        t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+        tf = flop / (ms * 1e-3) / 1e12 if flop else None
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out.append({"name": name, "kernel": desc, "launches_per_forward": per_fwd,
+                    "avg_launch_us": round(ms * 1e3, 2),
+                    "timing": "in forward" if runs else "alone",
+                    "launches_timed": len(runs) if runs else n_launch,
+                    "avg_launch_us_alone": round(alone[name] * 1e3, 2),
+                    "us_per_forward": round(ms * 1e3 * per_fwd, 1),
+                    "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+                    "tflops": round(tf, 1) if tf else None,
+                    "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4) if tf else None,
+                    "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "algorithmic_flop": flop, "algorithmic_bytes": nbytes})
     return out
 
 
@@ -666,6 +690,7 @@ def packed_main(args, cfg, model, dev):
 def forward_main(args, cfg, model, dev, w, inp, x, t, y, pooled, ctx, out):
     import torch
     import dit_inputs
+    import diffusion_transformer_denoiser_amd as dm
     mmdit = cfg.get("conditioning", 0) == dit_inputs.COND_MMDIT
     Bh = cfg["batch"]
     rows = 2 * Bh if cfg["cfg"] else Bh
@@ -695,8 +720,18 @@ def forward_main(args, cfg, model, dev, w, inp, x, t, y, pooled, ctx, out):
     reps = [timed(args.steps)[0] for _ in range(args.repeats)]
     assert torch.isfinite(out).all().item(), "non-finite output"
 
+    # The block kernels inside forwards: ceil(kernel_launches / depth) more
+    # forwards, identical to the timed ones but with the library's launch timer
+    # armed (an event pair around each of the blocks' launches).
     T = model.Tt
-    kernels = [] if mmdit else kernel_table(cfg, model, rows, args.kernel_launches, dev)
+    in_forward, timer_ms = {}, None
+    if not mmdit:
+        nf = -(-args.kernel_launches // cfg["N"])
+        dm.launch_timer_start(KERNEL_NAMES, nf * 7 * cfg["N"])
+        timer_ms = timed(nf)[0]
+        in_forward = dm.launch_timer_stop()
+    kernels = [] if mmdit else kernel_table(cfg, model, rows, args.kernel_launches, dev,
+                                            in_forward)
     roofline = None
     if kernels:
         top = max(kernels, key=lambda k: k["us_per_forward"])
@@ -763,6 +798,7 @@ def forward_main(args, cfg, model, dev, w, inp, x, t, y, pooled, ctx, out):
                                 "bf16_tflops_cu_x_clk_x_4096": peak_rocm[2]}
                                if peak_rocm else None)},
         "kernels": kernels,
+        "ms_per_step_launch_timer": round(timer_ms, 4) if timer_ms else None,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

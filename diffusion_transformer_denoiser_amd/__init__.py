@@ -8,5 +8,6 @@ been built.
 """
 from ._lib import (DIT_BF16, DIT_EPI_ACCUM, DIT_EPI_BIAS, DIT_EPI_BIAS_DT, DIT_EPI_GATED,  # noqa: F401
                    DIT_EPI_GELU, DIT_F32, DitError, load)
-from .model import (DiT, Sampler, attention, config_struct, linear, linear_wgrad,  # noqa: F401
-                    ln_modulate, patchify, timestep_embed, torch_dtype, unpatchify, upload)
+from .model import (DiT, Sampler, attention, config_struct, launch_timer_start,  # noqa: F401
+                    launch_timer_stop, linear, linear_wgrad, ln_modulate, patchify,
+                    timestep_embed, torch_dtype, unpatchify, upload)

@@ -15,6 +15,7 @@ DIT_F32, DIT_BF16 = 0, 1
 DIT_EPI_BIAS, DIT_EPI_GELU, DIT_EPI_GATED, DIT_EPI_ACCUM, DIT_EPI_BIAS_DT = 0, 1, 2, 3, 4
 DIT_SAMPLER_DDPM, DIT_SAMPLER_DPMPP_2M, DIT_SAMPLER_RF_EULER = 0, 1, 2
 DIT_COND_ADALN_ZERO, DIT_COND_IN_CONTEXT, DIT_COND_CROSS_ATTN, DIT_COND_MMDIT = 0, 1, 2, 3
+DIT_TIMER_KIND = {"layernorm": 0, "qkv": 1, "attention": 2, "out_proj": 3, "fc1": 4, "fc2": 5}
 
 
 class DitConfig(C.Structure):
@@ -116,6 +117,9 @@ EXPORTS = {
     "dit_forward_packed": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_int32), C.c_void_p,
                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                      C.c_size_t, C.c_void_p]),
+    "dit_launch_timer_start": (C.c_int, [C.c_uint, C.c_int]),
+    "dit_launch_timer_stop": (C.c_int, [C.POINTER(C.c_int), C.POINTER(C.c_float), C.c_int,
+                                        C.POINTER(C.c_int)]),
 }
 
 _lib = None

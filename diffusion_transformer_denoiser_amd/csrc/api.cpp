@@ -49,6 +49,52 @@ using namespace dit_host;
 
 namespace {
 
+// Launch timer of the calling thread (dit_launch_timer_start / _stop): event
+// pair i brackets the i-th timed launch; kinds[i] is its DIT_TIMER_* value.
+struct LaunchTimer {
+  unsigned mask = 0;
+  int cap = 0, used = 0;
+  bool open = false;           // pair `used` has its first event recorded
+  hipEvent_t* ev = nullptr;    // 2 * cap
+  int* kinds = nullptr;        // cap
+};
+thread_local LaunchTimer tl_timer;
+
+void timer_release(LaunchTimer& t) {
+  if (t.ev)
+    for (int i = 0; i < 2 * t.cap; ++i)
+      if (t.ev[i]) (void)hipEventDestroy(t.ev[i]);
+  delete[] t.ev;
+  delete[] t.kinds;
+  t = LaunchTimer{};
+}
+
+hipError_t timer_begin(int kind, hipStream_t s) {
+  LaunchTimer& t = tl_timer;
+  if (!((t.mask >> kind) & 1u) || t.used >= t.cap) return hipSuccess;
+  const hipError_t e = hipEventRecord(t.ev[2 * t.used], s);
+  t.open = e == hipSuccess;
+  return e;
+}
+
+hipError_t timer_end(int kind, hipStream_t s) {
+  LaunchTimer& t = tl_timer;
+  if (!t.open || !((t.mask >> kind) & 1u)) return hipSuccess;
+  t.open = false;
+  const hipError_t e = hipEventRecord(t.ev[2 * t.used + 1], s);
+  if (e == hipSuccess) t.kinds[t.used++] = kind;
+  return e;
+}
+
+// A launch of one of the block's kernels, bracketed by the thread's timer
+// events when that kernel is being timed.
+#define DIT_TIMED(kind, s, call)        \
+  do {                                  \
+    DIT_HIP(timer_begin((kind), (s)));  \
+    DIT_HIP(call);                      \
+    DIT_HIP(timer_end((kind), (s)));    \
+  } while (0)
+
 struct WsLayout {
   size_t e, th, c, sc, pp, pe, mod, cmod, ctx, kv, X, H, qkv, o, G, Y, seg, total;
 };
@@ -215,26 +261,28 @@ int run_block(const dit_handle* h, int l, int rows, float* X, const float* mod, 
   void* G = at<void>(ws, L.G);
   void* qkv = at<void>(ws, L.qkv);
 
-  DIT_HIP(launch_ln_modulate(X, M, T, d, mod, mod_stride, base, base + d, h->eps, Hb, h->dtype, s,
-                             ts));
+  DIT_TIMED(DIT_TIMER_LN, s, launch_ln_modulate(X, M, T, d, mod, mod_stride, base, base + d,
+                                                h->eps, Hb, h->dtype, s, ts));
 
   // Packed in-projection q | k | v [M, 3d] (heads as contiguous dh slices).
   EpiParams ep = epi0();
   ep.bias = h->w.qkv_b + (size_t)l * 3 * d;
   ep.out = qkv; ep.ldo = 3 * d;
-  DIT_HIP(linear(h, EPI_BIAS_DT, Hb, d, woff(h->w.qkv_w, (size_t)l * 3 * d * d, es), M, 3 * d, d,
-                 ep, s));
+  const void* qw = woff(h->w.qkv_w, (size_t)l * 3 * d * d, es);
+  DIT_TIMED(DIT_TIMER_QKV, s, linear(h, EPI_BIAS_DT, Hb, d, qw, M, 3 * d, d, ep, s));
 
   if (pk) {
     if (h->cfg.qk_norm)   // per-token LayerNorm of q and k (no rotary embedding when packed)
       DIT_HIP(launch_qk_norm_rope(qkv, 1, h->heads, M, h->dh, h->dtype, 1, h->eps, 0, h->gh,
                                   h->gw, s));
-    DIT_HIP(launch_attention_packed(qkv, pk->seqs, h->heads, h->dh, h->dtype, O, s));
+    DIT_TIMED(DIT_TIMER_ATTENTION, s,
+              launch_attention_packed(qkv, pk->seqs, h->heads, h->dh, h->dtype, O, s));
   } else {
     if (h->cfg.qk_norm || h->cfg.rope3d)
       DIT_HIP(launch_qk_norm_rope(qkv, rows, h->heads, T, h->dh, h->dtype, h->cfg.qk_norm, h->eps,
                                   h->cfg.rope3d, h->gh, h->gw, s));
-    DIT_HIP(launch_attention(qkv, rows, h->heads, T, h->dh, h->dtype, O, s));
+    DIT_TIMED(DIT_TIMER_ATTENTION, s,
+              launch_attention(qkv, rows, h->heads, T, h->dh, h->dtype, O, s));
   }
 
   const void* ow = woff(h->w.o_w, (size_t)l * d * d, es);
@@ -249,15 +297,15 @@ int run_block(const dit_handle* h, int l, int rows, float* X, const float* mod, 
   ep.out = X; ep.ldo = d;
   ep.mod = mod; ep.mod_stride = mod_stride; ep.gate_off = base + 2 * d; ep.T = T;
   ep.tok_seg = ts;
-  DIT_HIP(linear(h, EPI_GATED, O, d, ow, M, d, d, ep, s));
+  DIT_TIMED(DIT_TIMER_OUT_PROJ, s, linear(h, EPI_GATED, O, d, ow, M, d, d, ep, s));
 
-  DIT_HIP(launch_ln_modulate(X, M, T, d, mod, mod_stride, base + 3 * d, base + 4 * d, h->eps, Hb,
-                             h->dtype, s, ts));
+  DIT_TIMED(DIT_TIMER_LN, s, launch_ln_modulate(X, M, T, d, mod, mod_stride, base + 3 * d,
+                                                base + 4 * d, h->eps, Hb, h->dtype, s, ts));
   ep = epi0();
   ep.bias = h->w.fc1_b + (size_t)l * h->hid;
   ep.out = G; ep.ldo = h->hid;
-  DIT_HIP(linear(h, EPI_GELU, Hb, d, woff(h->w.fc1_w, (size_t)l * h->hid * d, es), M, h->hid, d,
-                 ep, s));
+  const void* w1 = woff(h->w.fc1_w, (size_t)l * h->hid * d, es);
+  DIT_TIMED(DIT_TIMER_FC1, s, linear(h, EPI_GELU, Hb, d, w1, M, h->hid, d, ep, s));
 
   const void* w2 = woff(h->w.fc2_w, (size_t)l * d * h->hid, es);
   if (f_branch) {
@@ -271,7 +319,7 @@ int run_block(const dit_handle* h, int l, int rows, float* X, const float* mod, 
   ep.out = X; ep.ldo = d;
   ep.mod = mod; ep.mod_stride = mod_stride; ep.gate_off = base + 5 * d; ep.T = T;
   ep.tok_seg = ts;
-  DIT_HIP(linear(h, EPI_GATED, G, h->hid, w2, M, d, h->hid, ep, s));
+  DIT_TIMED(DIT_TIMER_FC2, s, linear(h, EPI_GATED, G, h->hid, w2, M, d, h->hid, ep, s));
   return DIT_OK;
 }
 
@@ -1191,6 +1239,57 @@ int dit_block_forward(dit_handle* h, int layer, int B, const float* X_in, const 
     DIT_HIP(hipMemcpyAsync(X_out, X_in, (size_t)B * h->T * h->d * 4, hipMemcpyDeviceToDevice, s));
   rc = run_block(h, layer, B, X_out, mod, 6 * h->d, 0, ws, L, o_branch, f_branch, s);
   if (rc) return rc;
+  return ok();
+}
+
+int dit_launch_timer_start(unsigned kinds_mask, int capacity) {
+  if (kinds_mask == 0 || (kinds_mask >> DIT_TIMER_KINDS) != 0)
+    return fail(DIT_EINVAL, "kinds_mask 0x%x: needs a DIT_TIMER_* bit and no other", kinds_mask);
+  if (capacity < 1 || capacity > 65536)
+    return fail(DIT_EINVAL, "capacity %d outside [1, 65536]", capacity);
+  timer_release(tl_timer);
+  LaunchTimer t;
+  t.ev = new (std::nothrow) hipEvent_t[2 * (size_t)capacity]();
+  t.kinds = new (std::nothrow) int[capacity]();
+  t.cap = capacity;
+  if (!t.ev || !t.kinds) {
+    timer_release(t);
+    return fail(DIT_EHIP, "launch timer: no host memory for %d event pairs", capacity);
+  }
+  // Timing-only events: no system-scope fence (cache writeback and
+  // invalidation) at each record, which would slow the launches after it.
+  for (int i = 0; i < 2 * capacity; ++i) {
+    const hipError_t e = hipEventCreateWithFlags(&t.ev[i], hipEventDisableSystemFence);
+    if (e != hipSuccess) {
+      t.ev[i] = nullptr;
+      timer_release(t);
+      return fail(DIT_EHIP, "launch timer: hipEventCreate: %s", hipGetErrorString(e));
+    }
+  }
+  t.mask = kinds_mask;
+  tl_timer = t;
+  return ok();
+}
+
+int dit_launch_timer_stop(int* kinds, float* ms, int cap, int* count) {
+  if (!count) return fail(DIT_EINVAL, "count must be non-NULL");
+  if (cap < 0 || (cap > 0 && (!kinds || !ms)))
+    return fail(DIT_EINVAL, "cap %d needs kinds and ms of that length", cap);
+  *count = 0;
+  LaunchTimer& t = tl_timer;
+  if (!t.ev) return ok();
+  const int n = t.used;
+  hipError_t err = hipSuccess;
+  // every recorded event completes before the events are released
+  for (int i = 0; i < 2 * n + (t.open ? 1 : 0) && err == hipSuccess; ++i)
+    err = hipEventSynchronize(t.ev[i]);
+  for (int i = 0; i < n && i < cap && err == hipSuccess; ++i) {
+    err = hipEventElapsedTime(&ms[i], t.ev[2 * i], t.ev[2 * i + 1]);
+    kinds[i] = t.kinds[i];
+  }
+  timer_release(t);
+  if (err != hipSuccess) return fail(DIT_EHIP, "launch timer: %s", hipGetErrorString(err));
+  *count = n;
   return ok();
 }
 

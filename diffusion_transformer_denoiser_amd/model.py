@@ -460,3 +460,32 @@ def linear_wgrad(dY, X, dW, db=None):
     _lib.check(lib.dit_linear_wgrad(_ptr(dY), dY.stride(0), _ptr(X), X.stride(0), N, K, R, code,
                                     _ptr(dW), _ptr(db), _stream(dY.device)))
     return dW
+
+
+def launch_timer_start(kinds, capacity: int) -> None:
+    """Arm the calling thread's launch timer (``dit_launch_timer_start``): the
+    next `capacity` launches of the named block kernels ("layernorm", "qkv",
+    "attention", "out_proj", "fc1", "fc2") in this thread's forwards get a HIP
+    event pair around them."""
+    lib = _lib.load()
+    mask = 0
+    for k in kinds:
+        mask |= 1 << _lib.DIT_TIMER_KIND[k]
+    _lib.check(lib.dit_launch_timer_start(mask, capacity))
+
+
+def launch_timer_stop() -> dict:
+    """Wait for the timed launches, release the timer and return
+    {kernel name: [ms of each launch, in launch order]}."""
+    lib = _lib.load()
+    count = C.c_int(0)
+    names = {v: k for k, v in _lib.DIT_TIMER_KIND.items()}
+    cap = 65536
+    kinds = (C.c_int * cap)()
+    ms = (C.c_float * cap)()
+    _lib.check(lib.dit_launch_timer_stop(kinds, ms, cap, C.byref(count)))
+    out = {}
+    for i in range(min(count.value, cap)):
+        out.setdefault(names[kinds[i]], []).append(float(ms[i]))
+    return out
+

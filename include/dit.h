@@ -329,6 +329,48 @@ int dit_block_forward(dit_handle* h, int layer, int B, const float* X_in, const 
                       float* X_out, float* o_branch, float* f_branch, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* ---- Launch timing (measurement) ----
+ * Per-launch durations of the adaLN-Zero block's kernels (itwiki "확산
+ * 트랜스포머", adaLN-Zero equations and Implementation / adaLN-Zero block:
+ * LayerNorm + modulate, q | k | v, attention, the gated output projection,
+ * LayerNorm + modulate, the FFN's two products) inside real forwards, for
+ * roofline figures of the kernels as they run there.
+ *
+ * dit_launch_timer_start arms a timer for the calling thread: it creates
+ * 2 * capacity HIP events (host-side runtime objects on the current device;
+ * no device memory; timing-only, without the system-scope fence, so an event
+ * does not write back or invalidate caches) and, from then on, every forward
+ * that thread enqueues
+ * (dit_forward, dit_cfg_forward, their _taps and _noalloc forms,
+ * dit_forward_packed, dit_sample, dit_block_forward) records one event pair on
+ * its stream around each launch of a kernel whose DIT_TIMER_* bit is in
+ * kinds_mask, until capacity launches are timed; later launches run untimed.
+ * Handles and other threads are not affected.  A timer the thread already
+ * had is released first.  Forwards on another device than the one current at
+ * start fail with DIT_EHIP while the timer is armed.  Only the blocks of the
+ * adaLN-Zero design are timed.
+ *   DIT_EINVAL: kinds_mask 0 or with bits beyond DIT_TIMER_KINDS, capacity
+ *               outside [1, 65536];  DIT_EHIP: event creation failed (no timer
+ *               is left armed).
+ *
+ * dit_launch_timer_stop waits for the timed launches to finish, writes the
+ * first min(count, cap) of them in launch order (kinds[i] a DIT_TIMER_*
+ * value, ms[i] the time between the pair's events in milliseconds), sets
+ * *count to the number timed, releases the events and disarms the thread.
+ * Without an armed timer it sets *count = 0.
+ *   DIT_EINVAL: count NULL, cap < 0, or cap > 0 with kinds or ms NULL;
+ *   DIT_EHIP: waiting or reading an event failed (the events are still
+ *             released). */
+#define DIT_TIMER_LN        0   /* LayerNorm + modulate (two per block) */
+#define DIT_TIMER_QKV       1   /* q | k | v product */
+#define DIT_TIMER_ATTENTION 2
+#define DIT_TIMER_OUT_PROJ  3   /* output projection, gated residual epilogue */
+#define DIT_TIMER_FC1       4   /* FFN up-projection, GELU epilogue */
+#define DIT_TIMER_FC2       5   /* FFN down-projection, gated residual epilogue */
+#define DIT_TIMER_KINDS     6
+int dit_launch_timer_start(unsigned kinds_mask, int capacity);
+int dit_launch_timer_stop(int* kinds, float* ms, int cap, int* count);
+
 /* ---- Sampling around the denoiser ----
  * One reverse step updates the fp32 latent state x [B, C, F, H, W] from the
  * model's prediction.  Kinds:

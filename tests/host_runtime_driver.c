@@ -186,8 +186,38 @@ static void packed_checks(dit_handle* h) {
   CHECK(dit_packed_workspace_size(h, 0, fhw, &need) == DIT_EINVAL);
 }
 
+/* Launch timer: argument checks, and a start without a device either arms
+ * (then stop reports no timed launch) or fails with DIT_EHIP, leaving nothing
+ * armed. */
+static void timer_checks(void) {
+  int kinds[4], count = -1;
+  float ms[4];
+  CHECK(dit_launch_timer_start(0u, 16) == DIT_EINVAL);
+  CHECK(dit_launch_timer_start(1u << DIT_TIMER_KINDS, 16) == DIT_EINVAL);
+  CHECK(dit_launch_timer_start(1u << DIT_TIMER_FC1, 0) == DIT_EINVAL);
+  CHECK(dit_launch_timer_start(1u << DIT_TIMER_FC1, 65537) == DIT_EINVAL);
+  CHECK(dit_launch_timer_stop(kinds, ms, 4, NULL) == DIT_EINVAL);
+  CHECK(dit_launch_timer_stop(kinds, ms, -1, &count) == DIT_EINVAL);
+  CHECK(dit_launch_timer_stop(NULL, ms, 4, &count) == DIT_EINVAL);
+  CHECK(dit_launch_timer_stop(kinds, NULL, 4, &count) == DIT_EINVAL);
+  CHECK(dit_launch_timer_stop(NULL, NULL, 0, &count) == DIT_OK && count == 0);
+  for (int rep = 0; rep < 3; ++rep) {
+    const int rc = dit_launch_timer_start((1u << DIT_TIMER_KINDS) - 1u, 8 + rep);
+    CHECK(rc == DIT_OK || rc == DIT_EHIP);
+    count = -1;
+    CHECK(dit_launch_timer_stop(kinds, ms, 4, &count) == DIT_OK && count == 0);
+  }
+  /* a second start releases the first timer's events */
+  const int r1 = dit_launch_timer_start(1u << DIT_TIMER_QKV, 32);
+  const int r2 = dit_launch_timer_start(1u << DIT_TIMER_LN, 64);
+  CHECK(r1 == r2 && (r1 == DIT_OK || r1 == DIT_EHIP));
+  count = -1;
+  CHECK(dit_launch_timer_stop(kinds, ms, 4, &count) == DIT_OK && count == 0);
+}
+
 int main(void) {
   const dit_weights w = all_weights();
+  timer_checks();
 
   /* DiT-XL/2 at 256 and 512 (class-conditional, guided) */
   for (int res = 32; res <= 64; res *= 2) {

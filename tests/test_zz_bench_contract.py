@@ -48,6 +48,7 @@ def test_short_run_prints_one_contract_line():
     # the roofline is the hot kernel with the largest time per forward
     ks = d["kernels"]
     assert {k["name"] for k in ks} >= {"qkv", "out_proj", "fc1", "fc2", "attention", "layernorm"}
+    assert all(k["avg_launch_us"] > 0 and k["avg_launch_us_alone"] > 0 for k in ks)
     top = max(ks, key=lambda k: k["us_per_forward"])
     assert rf["kernel"] == top["kernel"]
     assert len(d["repeats_ms_per_step"]) == 5
