@@ -175,6 +175,10 @@ hipError_t linear_wgrad(const void* dY, int64_t ldy, const void* X, int64_t ldx,
     return launch_gemm_tn((const bf16_t*)dY, (int)ldy, (const bf16_t*)X, (int)ldx, N, K, (int)R,
                           dW, lddw, db, s);
   if (R > INT32_MAX || ldy > INT32_MAX || ldx > INT32_MAX) return hipErrorInvalidValue;
+  // the bias-gradient pass's limits are checked before dW is touched
+  if (db && dtype == DIT_BF16 &&
+      (N % 8 || ldy % 8 || ((uintptr_t)dY & 15) || R > kColsumTallMaxRows))
+    return hipErrorInvalidValue;
   ALoad a;
   memset(&a, 0, sizeof a);
   a.ptr = dY; a.lda = (int)ldy; a.a_dtype = dtype == DIT_BF16 ? 1 : 0; a.src_rows = N; a.trans = 1;
@@ -186,7 +190,6 @@ hipError_t linear_wgrad(const void* dY, int64_t ldy, const void* X, int64_t ldx,
                                   (int)R, ep, s);
   if (e != hipSuccess || !db) return e;
   if (dtype != DIT_BF16) return launch_colsum((const float*)dY, (int)R, N, ldy, db, s);
-  if (N % 8 || ldy % 8 || ((uintptr_t)dY & 15)) return hipErrorInvalidValue;
   return launch_colsum_tall_bf16(dY, R, N, ldy, db, s);
 }
 

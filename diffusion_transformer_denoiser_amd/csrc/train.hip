@@ -362,8 +362,8 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const bf16_t* __restri
 // out[c] += sum over r < rows of in[r * ld + c] for tall matrices: a
 // workgroup covers 256 columns (32 lanes of 8 adjacent columns, 16-byte
 // loads) of 512 rows, its 8 row lanes taking every 8th row; the row lanes
-// combine in LDS and each column's partial sum adds atomically (out must
-// start at zero).
+// combine in LDS and each column's partial sum adds atomically to out
+// (calls into one out may overlap).
 __global__ __launch_bounds__(256) void colsum_tall_bf16_kernel(const bf16_t* __restrict__ in,
                                                                int64_t rows, int64_t cols,
                                                                int64_t ld, float* __restrict__ out) {
