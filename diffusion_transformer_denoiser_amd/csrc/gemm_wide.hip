@@ -142,6 +142,7 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(const bf16_t* __restrict
   if (nk > 1) copies(1);
   bool relaxed = false;
   static_assert(2 * NI * NJ + CPW >= 63, "every whole-tile epilogue issues >= 63 - CPW memory ops");
+  static_assert(2 * NI * NJ >= 63, "a whole-tile epilogue issues >= 63 memory ops after slice 1's copies");
 
   for (;;) {
     // Accumulators start at the bias.  acc[i][j][r] is output row
@@ -195,6 +196,10 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(const bf16_t* __restrict
                 // every read of this slice has returned; slice kt + 1 has landed
                 // once this wave's copies of it are done and all waves pass
                 wait_lgkm0();
+                // In a tile's first slice after a whole-tile epilogue, at least 64
+                // epilogue stores were issued after the copies of slice 1, so 63
+                // outstanding operations already imply those copies have landed;
+                // the stores keep draining through this slice.
                 wait_vmcnt<0>();
                 bare_barrier();
               }
@@ -250,6 +255,39 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(const bf16_t* __restrict
       const bool even = (c16 & 1) == 0;
       const int col0 = en0 + wn * WN + (c16 & ~1);
       const int rodd = even ? 0 : 1;
+      auto value = [&](int i, int j, int r) {
+        const float x = acc[i][j][r];
+        if constexpr (EPI == EPI_GELU) return gelu_tanh_f(x);
+        else return x;
+      };
+      if (full && (int64_t)M * ep.ldo * 2 < (1LL << 31)) {
+        // Whole tile: each lane packs its own rows (0, 1) and (2, 3) to bf16
+        // pairs, takes the neighbour's pairs by one DPP move each and keeps
+        // one half of each with a byte permute (even lane: own low half, then
+        // the neighbour's low half; odd lane: the neighbour's high half, then
+        // its own).  Stores through buffer addressing: one lane offset, the
+        // row offsets in scalar registers, the column block as the immediate.
+        const int ldb = ep.ldo * 2;
+        const __amdgpu_buffer_rsrc_t ors =
+            __builtin_amdgcn_make_buffer_rsrc(out, (short)0, M * ldb, 0x00020000);
+        const int oo = (rbase + rodd) * ldb + col0 * 2;
+        const uint32_t sel = even ? 0x05040100u : 0x03020706u;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const uint32_t p01 = f2bf2(value(i, j, 0), value(i, j, 1));
+            const uint32_t p23 = f2bf2(value(i, j, 2), value(i, j, 3));
+            const uint32_t q01 =
+                (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p01, 0xB1, 0xF, 0xF, false);
+            const uint32_t q23 =
+                (uint32_t)__builtin_amdgcn_update_dpp(0, (int)p23, 0xB1, 0xF, 0xF, false);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(q01, p01, sel), ors,
+                                                  oo + 32 * j, (16 * i) * ldb, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_amdgcn_perm(q23, p23, sel), ors,
+                                                  oo + 32 * j, (16 * i + 2) * ldb, 0);
+          }
+      } else {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -269,6 +307,7 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(const bf16_t* __restrict
           if (full || row < M) *(uint32_t*)o = w0;
           if (full || row + 2 < M) *(uint32_t*)(o + 2 * (int64_t)ep.ldo) = w1;
         }
+      }
     } else if constexpr (EPI == EPI_BIAS_F32) {
       float* out = (float*)ep.out;
 #pragma unroll
