@@ -142,7 +142,6 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(const bf16_t* __restrict
   if (nk > 1) copies(1);
   bool relaxed = false;
   static_assert(2 * NI * NJ + CPW >= 63, "every whole-tile epilogue issues >= 63 - CPW memory ops");
-  static_assert(2 * NI * NJ >= 63, "a whole-tile epilogue issues >= 63 memory ops after slice 1's copies");
 
   for (;;) {
     // Accumulators start at the bias.  acc[i][j][r] is output row
@@ -196,10 +195,6 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(const bf16_t* __restrict
                 // every read of this slice has returned; slice kt + 1 has landed
                 // once this wave's copies of it are done and all waves pass
                 wait_lgkm0();
-                // In a tile's first slice after a whole-tile epilogue, at least 64
-                // epilogue stores were issued after the copies of slice 1, so 63
-                // outstanding operations already imply those copies have landed;
-                // the stores keep draining through this slice.
                 wait_vmcnt<0>();
                 bare_barrier();
               }
