@@ -51,7 +51,10 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
                                                            int T_rows, float sl2, SeqTable seqs,
                                                            float* __restrict__ lse) {
   constexpr int KV = 64;                  // keys per tile
-  constexpr int KLD = 72;                 // K tile row stride (elements), 144 B
+  // K tile row stride (elements), 160 B: the fragment reads of 16 rows x 2
+  // chunks that the LDS serves together land on distinct banks (144-byte
+  // rows put two of them on one bank)
+  constexpr int KLD = 80;
   constexpr int VLD = KV + 4;             // V^T tile row stride (elements), 136 B
   constexpr int NDB = (DH + 15) / 16;     // 16-row blocks of the O^T accumulator
   constexpr bool TAIL = (DH % 32) != 0;   // dh = 72: columns 64..71
@@ -164,14 +167,14 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
             uint2, __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[u] + t0 + q * ldb, 0, 0));
   };
   // DMA staging (dh = 72): direct global->LDS copies of 64 lanes x 16 bytes,
-  // lane l of a copy landing at its LDS base + 16 l.  A K tile is 9 copies
-  // (slot c: row c / 9, 16-byte column c % 9); a V tile 10 (slot c: row
-  // c / 10, column c % 10), whose lanes on column 9, the (1, 0, .., 0) pad,
-  // stay inactive and leave it as written at the start.  Copy u of wave w is
+  // lane l of a copy landing at its LDS base + 16 l.  A K tile and a V tile
+  // are 10 copies each (slot c: row c / 10, 16-byte column c % 10), whose
+  // lanes on column 9, the pad (zeros in K, (1, 0, .., 0) in V), stay
+  // inactive and leave it as written at the start.  Copy u of wave w is
   // number w + NWV u.  Byte offsets inside a tile are fixed per lane; the
   // tile's row offset rides in the scalar offset.  The rows of a ragged last
   // tile past T read row T - 1: finite data whose weights are 0.
-  constexpr int NCK = KV * DH / 512, NCV = KV * VS / 512, NCP = NCK + NCV;
+  constexpr int NCK = KV * KLD / 512, NCV = KV * VS / 512, NCP = NCK + NCV;
   constexpr int CPW = (NCP + NWV - 1) / NWV;
   int drow[CPW], doff[CPW];
   uint32_t dpad = 0;                       // bit u: copy u's lane is a V pad slot
@@ -180,11 +183,11 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
     const int ii = wave + NWV * u;
     const bool isv = ii >= NCK;
     const int c = (isv ? ii - NCK : ii) * 64 + lane;
-    const int per = isv ? VS / 8 : DH / 8;
+    const int per = isv ? VS / 8 : KLD / 8;
     const int row = c / per, col = c - row * per;
     drow[u] = row;
     doff[u] = (int)(((int64_t)row * ld + (col < DH / 8 ? col : 0) * 8) * 2);
-    if (isv && col == DH / 8) dpad |= 1u << u;
+    if (col == DH / 8) dpad |= 1u << u;
   }
   auto dma = [&](int kv0, int buf, auto rag_c) {
     constexpr bool ragged = decltype(rag_c)::value;   // the tile reaches past T
@@ -261,9 +264,12 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
   if (tid == 0) zslot = make_uint4(0, 0, 0, 0);
   if (tid < 2 * KPAD / 8) *(uint4*)&sK[tid / (KPAD / 8)][KV * KLD + 8 * (tid % (KPAD / 8))] = make_uint4(0, 0, 0, 0);
   if constexpr (DMA) {
-    // The (1, 0, .., 0) column chunk of every V row of both buffers, once.
-    for (int i = tid; i < 2 * KV; i += NTH)
+    // The (1, 0, .., 0) column chunk of every V row and the zero column chunk
+    // of every K row of both buffers, once.
+    for (int i = tid; i < 2 * KV; i += NTH) {
       *(uint4*)&sV[i / KV][(i % KV) * VS + DH] = make_uint4(0x3F80u, 0, 0, 0);
+      *(uint4*)&sK[i / KV][(i % KV) * KLD + DH] = make_uint4(0, 0, 0, 0);
+    }
     __syncthreads();
     if (ntiles == 1 && T % KV) dma(0, 0, std::true_type{});
     else dma(0, 0, std::false_type{});
@@ -293,9 +299,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
       const bf16_t* kr = &sK[buf][(16 * kb + c16) * KLD];
       bf16x8_t k0 = *(const bf16x8_t*)(kr + 8 * g);
       bf16x8_t k1 = *(const bf16x8_t*)(kr + 32 + 8 * g);
-      // dh 64..95: lanes g > 0 read past dh 72 (the next row, or the zero pad
-      // after the last one); the query operand is zero there, so the products
-      // only need those values finite
+      // dh 64..95: lanes g > 0 read past dh 72 (the row's zero pad column, the
+      // next row, or the zero pad after the last one); the query operand is
+      // zero there, so the products only need those values finite
       bf16x8_t kt = z8;
       if constexpr (TAIL) kt = *(const bf16x8_t*)(kr + 64 + 8 * g);
 #pragma unroll
@@ -467,7 +473,7 @@ template <int NT, bool RAG>
 __global__ __launch_bounds__(512) void attn_short_kernel(const bf16_t* __restrict__ QKV,
                                                          bf16_t* __restrict__ O, int H, int T,
                                                          int npairs, float sl2) {
-  constexpr int DH = 72, NWV = 8, KS = 72, VS = 80, NDB = 5;
+  constexpr int DH = 72, NWV = 8, KS = 80, VS = 80, NDB = 5;
   constexpr int NCH = 256 * (DH / 8);               // 16-byte chunks of K (or V) per pair
   constexpr int CPT = (NCH + 64 * NWV - 1) / (64 * NWV);
   // 24 zero elements after K's last row: the dh 64..95 operand reads of the
@@ -483,11 +489,12 @@ __global__ __launch_bounds__(512) void attn_short_kernel(const bf16_t* __restric
 
   // K / V chunk u of this thread: chunk c = tid + 512 u is row c / 9, 16-byte
   // column c % 9 (rows past T read row T - 1: finite data whose weights are 0)
-  // In LDS, K chunk c sits at element 8 c (rows unpadded) and V chunk c at
-  // 8 (c + c / 9) (one pad chunk per row).  Offsets are recomputed at each
+  // In LDS, K and V chunk c sit at element 8 (c + c / 9): rows of 80, one
+  // pad chunk per row (zeros in K, so that 16 rows x 2 chunks of a fragment
+  // read fall on distinct banks; (1, 0, .., 0) in V).  Offsets are recomputed at each
   // use rather than held in registers across the pair.
   const int ldb = (int)(ld * 2);
-  static_assert(KS == DH && VS == DH + 8, "LDS row strides");
+  static_assert(KS == DH + 8 && VS == DH + 8, "LDS row strides");
   const int nrec = (int)(((int64_t)(T - 1) * ld + DH) * 2);
   uint4 kreg[CPT], vreg[CPT];
   auto gload = [&](int p) {
@@ -515,7 +522,7 @@ __global__ __launch_bounds__(512) void attn_short_kernel(const bf16_t* __restric
     for (int u = 0; u < CPT; ++u)
       if (t0 + 64 * NWV * u < NCH) {
         const int c = t0 + 64 * NWV * u;
-        *(uint4*)&sK[8 * c] = kreg[u];
+        *(uint4*)&sK[8 * (c + c / (DH / 8))] = kreg[u];
         *(uint4*)&sV[8 * (c + c / (DH / 8))] = vreg[u];
       }
   };
@@ -543,7 +550,10 @@ __global__ __launch_bounds__(512) void attn_short_kernel(const bf16_t* __restric
   const int G = gridDim.x;
   int pair = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
   if (pair >= npairs) return;
-  if (tid < 256) *(uint4*)&sV[tid * VS + DH] = make_uint4(0x3F80u, 0, 0, 0);   // (1, 0, .., 0)
+  if (tid < 256) {
+    *(uint4*)&sV[tid * VS + DH] = make_uint4(0x3F80u, 0, 0, 0);   // (1, 0, .., 0)
+    *(uint4*)&sK[tid * KS + DH] = make_uint4(0, 0, 0, 0);
+  }
   if (tid < 3) *(uint4*)&sK[256 * KS + 8 * tid] = make_uint4(0, 0, 0, 0);
   bf16x8_t qn[2][2], qtn[2];
   load_q(pair, qn, qtn);
@@ -576,9 +586,9 @@ __global__ __launch_bounds__(512) void attn_short_kernel(const bf16_t* __restric
         const bf16_t* kr = sK + (64 * t + 16 * kb + c16) * KS;
         const bf16x8_t k0 = *(const bf16x8_t*)(kr + 8 * g);
         const bf16x8_t k1 = *(const bf16x8_t*)(kr + 32 + 8 * g);
-        // dh 64..95: lanes g > 0 read past dh 72 (the next row, or the zero
-        // pad after the last one); their query operand is zero, so the
-        // products only need those values finite
+        // dh 64..95: lanes g > 0 read past dh 72 (the row's zero pad column,
+        // the next row, or the zero pad after the last one); their query
+        // operand is zero, so the products only need those values finite
         const bf16x8_t kt = *(const bf16x8_t*)(kr + 64 + 8 * g);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
