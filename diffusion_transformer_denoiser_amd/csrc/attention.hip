@@ -177,7 +177,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void attn_bf16_kernel(const bf16
   constexpr int NCK = KV * KLD / 512, NCV = KV * VS / 512, NCP = NCK + NCV;
   constexpr int CPW = (NCP + NWV - 1) / NWV;
   int drow[CPW], doff[CPW];
-  uint32_t dpad = 0;                       // bit u: copy u's lane is a V pad slot
+  uint32_t dpad = 0;                       // bit u: copy u's lane is a K or V pad slot
 #pragma unroll
   for (int u = 0; u < CPW; ++u) {
     const int ii = wave + NWV * u;
@@ -490,9 +490,9 @@ __global__ __launch_bounds__(512) void attn_short_kernel(const bf16_t* __restric
   // K / V chunk u of this thread: chunk c = tid + 512 u is row c / 9, 16-byte
   // column c % 9 (rows past T read row T - 1: finite data whose weights are 0)
   // In LDS, K and V chunk c sit at element 8 (c + c / 9): rows of 80, one
-  // pad chunk per row (zeros in K, so that 16 rows x 2 chunks of a fragment
-  // read fall on distinct banks; (1, 0, .., 0) in V).  Offsets are recomputed at each
-  // use rather than held in registers across the pair.
+  // pad chunk per row (zeros in K, so that the 16 rows x 2 chunks of a
+  // fragment read fall on distinct banks; (1, 0, .., 0) in V).  Offsets are
+  // recomputed at each use rather than held in registers across the pair.
   const int ldb = (int)(ld * 2);
   static_assert(KS == DH + 8 && VS == DH + 8, "LDS row strides");
   const int nrec = (int)(((int64_t)(T - 1) * ld + DH) * 2);
