@@ -140,8 +140,10 @@ WsLayout ws_layout(const dit_handle* h, int rows) {
 
 namespace dit_host {
 int splitk_slice(bool mfma, int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = mfma ? ((M + (M <= 64 ? 63 : 127)) / (M <= 64 ? 64 : 128)) *
-                                   ((N + (N % 192 ? 127 : 191)) / (N % 192 ? 128 : 192))
+  // the MFMA kernel takes 64-row tiles for M <= 64 and when its 128-row
+  // tiles would number at most half the CUs
+  const int64_t t128 = mfma_tiles_128(M, N), ncol = t128 / ((M + 127) / 128);
+  const int64_t tiles = mfma ? (M <= 64 || t128 <= 128 ? (M + 63) / 64 * ncol : t128)
                              : ((M + 63) / 64) * ((N + 63) / 64);
   const int kstep = mfma ? 64 : 16;
   // Workgroups resident at once: 256 CUs x 2 (the MFMA kernel's LDS allows

@@ -199,6 +199,8 @@ hipError_t launch_gemm_tn(const bf16_t* A, int lda, const bf16_t* B, int ldb, in
                           int R, float* out, int ldo, float* asum, hipStream_t s);
 hipError_t launch_gemm_valu(int epi, int asrc, const ALoad& a, const void* W, int w_dtype,
                             int M, int N, int K, const EpiParams& ep, hipStream_t s);
+// 128-row tiles of an M x N product on the 128 x 192 (or 128 x 128) MFMA kernel.
+int64_t mfma_tiles_128(int64_t M, int64_t N);
 hipError_t launch_gemm_mfma(int epi, const bf16_t* A, int lda, const bf16_t* W, int M, int N,
                             int K, const EpiParams& ep, hipStream_t s);
 // The wide-tile kernel (256-row tiles, one workgroup per CU) for the large

@@ -458,13 +458,24 @@ hipError_t run(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
   return hipGetLastError();
 }
 
+}  // namespace
+
+int64_t mfma_tiles_128(int64_t M, int64_t N) {
+  return ((M + 127) / 128) * (N % 192 ? (N + 127) / 128 : N / 192);
+}
+
+namespace {
+
 template <int EPI>
 hipError_t pick(const bf16_t* A, int lda, const bf16_t* W, int M, int N, int K,
                 const EpiParams& ep, hipStream_t s) {
   // 128x192 tiles, 64-wide K slices, two LDS buffers (80 KB): two workgroups
   // per CU.  At most 64 rows (the per-row conditioning products) take 64-row
-  // tiles, so no MFMA work or LDS traffic goes to padding rows.
-  if (M <= 64) {
+  // tiles, so no MFMA work or LDS traffic goes to padding rows; so do products
+  // with at most half as many 128-row tiles as CUs, which doubles their
+  // workgroups.  Both tile heights accumulate every output in the same k order
+  // with the same MFMA, so the choice does not change a result bit.
+  if (M <= 64 || mfma_tiles_128(M, N) <= 128) {
     if (N % 192 == 0) return run<EPI, 64, 192, 64, 2>(A, lda, W, M, N, K, ep, s);
     return run<EPI, 64, 128, 64, 2>(A, lda, W, M, N, K, ep, s);
   }

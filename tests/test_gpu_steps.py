@@ -194,6 +194,36 @@ def test_linear_wide_tiles(M, N, K):
     assert e2 <= 4e-3 and e3 <= 4e-3
 
 
+# (N, K, M of the larger product): more than 128 tiles of 128 rows there, fewer
+# than 256 wide tiles (so the 128 x 192 kernel runs both)
+@pytest.mark.parametrize("N,K,big", [(768, 3072, 8192), (1152, 1152, 4096), (1152, 4608, 5632)])
+def test_linear_tile_height_bitwise(N, K, big):
+    """Products with at most 128 tiles of 128 rows run on 64-row tiles.  The first
+    2048 rows computed alone (64-row tiles) must equal, bit for bit, the same
+    rows inside a product large enough for 128-row tiles, for the bias, GELU and
+    gated residual epilogues: the tile height never changes the k order."""
+    log(f"linear tile heights N={N} K={K}: M = 2048 vs {big}")
+    rng = np.random.default_rng(N + K)
+    A = torch.from_numpy(_bf16(rng.standard_normal((big, K)).astype(np.float32))).to(torch.bfloat16).cuda()
+    W = torch.from_numpy(_bf16((rng.standard_normal((N, K)) * 0.05).astype(np.float32))).to(torch.bfloat16).cuda()
+    b = torch.from_numpy(rng.standard_normal(N).astype(np.float32)).cuda()
+    T = 64
+    gate = torch.from_numpy(rng.standard_normal(((big + T - 1) // T, N)).astype(np.float32)).cuda()
+    X0 = torch.from_numpy(rng.standard_normal((big, N)).astype(np.float32)).cuda()
+    for epi, dt in ((dmod.DIT_EPI_BIAS_DT, torch.bfloat16), (dmod.DIT_EPI_GELU, torch.bfloat16),
+                    (dmod.DIT_EPI_GATED, torch.float32)):
+        outs = []
+        for M in (2048, big):
+            if epi == dmod.DIT_EPI_GATED:
+                o = X0[:M].clone()
+                dmod.linear(epi, A[:M], W, b, o, gate=gate, gate_stride=N, T=T)
+            else:
+                o = torch.empty(M, N, device="cuda", dtype=dt)
+                dmod.linear(epi, A[:M], W, b, o)
+            outs.append(np_(o.float()))
+        assert np.array_equal(outs[0], outs[1][:2048]), f"epilogue {epi}: tile height changed a result"
+
+
 @pytest.mark.parametrize("M,T,d,dtype", [(512, 256, 1152, "bf16"), (300, 64, 768, "f32"),
                                          (16384, 256, 1152, "bf16")])
 def test_ln_modulate(M, T, d, dtype):
