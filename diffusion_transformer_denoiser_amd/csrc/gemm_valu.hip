@@ -123,6 +123,68 @@ hipError_t dispatch_epi(int epi, int asrc, const ALoad& a, const void* W, int M,
   return hipErrorInvalidValue;
 }
 
+// Products of at most GV_ROWS fp32 rows with bf16 weights, bias epilogue (the
+// pooled-vector projection of one to a few rows): the 64 x 64 tile kernel
+// would run N / 64 workgroups, each reading its weight rows 32 bytes at a time
+// for one useful row.  Here one wave owns one output column: its lanes read the
+// column's weight row 16 bytes at a time (lane l takes k = 8 l .. 8 l + 7 of
+// every 512) with the matching A values, accumulate in fp32, and combine their
+// partial sums by a fixed xor-shuffle tree, so the result is deterministic.
+constexpr int GV_ROWS = 8;
+
+template <int MR>
+__global__ __launch_bounds__(256) void gemv_bf16_kernel(ALoad a, const bf16_t* __restrict__ W,
+                                                        int M, int N, int K, EpiParams ep) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const int64_t ldw = ep.ldw ? ep.ldw : K;
+  const bf16_t* wr = W + (int64_t)n * ldw;
+  const float* arow[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+    arow[m] = (const float*)a.ptr + row_map(min(m, M - 1) % a.src_rows, a.seg, a.skip, a.off) * a.lda;
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+  for (int k0 = 8 * lane; k0 < K; k0 += 512) {
+    const uint4 wv = *(const uint4*)(wr + k0);
+    const uint32_t wp[4] = {wv.x, wv.y, wv.z, wv.w};
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[2 * i] = __uint_as_float(wp[i] << 16);
+      w[2 * i + 1] = __uint_as_float(wp[i] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const float4 a0 = *(const float4*)(arow[m] + k0), a1 = *(const float4*)(arow[m] + k0 + 4);
+      acc[m] = fmaf(a0.x, w[0], acc[m]);
+      acc[m] = fmaf(a0.y, w[1], acc[m]);
+      acc[m] = fmaf(a0.z, w[2], acc[m]);
+      acc[m] = fmaf(a0.w, w[3], acc[m]);
+      acc[m] = fmaf(a1.x, w[4], acc[m]);
+      acc[m] = fmaf(a1.y, w[5], acc[m]);
+      acc[m] = fmaf(a1.z, w[6], acc[m]);
+      acc[m] = fmaf(a1.w, w[7], acc[m]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    float v = acc[m];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0 && m < M) epi_apply<EPI_BIAS_F32, bf16_t>(ep, m, n, v);
+  }
+}
+
+template <int MR>
+hipError_t run_gemv(const ALoad& a, const void* W, int M, int N, int K, const EpiParams& ep,
+                    hipStream_t s) {
+  gemv_bf16_kernel<MR><<<(N + 3) / 4, 256, 0, s>>>(a, (const bf16_t*)W, M, N, K, ep);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_valu(int epi, int asrc, const ALoad& a, const void* W, int w_dtype,
@@ -131,6 +193,15 @@ hipError_t launch_gemm_valu(int epi, int asrc, const ALoad& a, const void* W, in
   if (ep.ksplit < 0 || (ep.ksplit % BK) || (ep.ksplit && epi != EPI_ATOMIC_F32) ||
       (epi == EPI_ATOMIC_F32 && ep.bias))
     return hipErrorInvalidValue;
+  const int64_t ldw = ep.ldw ? ep.ldw : K;
+  if (epi == EPI_BIAS_F32 && asrc == A_PLAIN && w_dtype == 1 && a.a_dtype == 0 && !a.trans &&
+      !ep.w_trans && !ep.ksplit && M <= GV_ROWS && K % 8 == 0 && ldw % 8 == 0 && a.lda % 4 == 0 &&
+      ((uintptr_t)W & 15) == 0 && ((uintptr_t)a.ptr & 15) == 0) {
+    if (M <= 1) return run_gemv<1>(a, W, M, N, K, ep, s);
+    if (M <= 2) return run_gemv<2>(a, W, M, N, K, ep, s);
+    if (M <= 4) return run_gemv<4>(a, W, M, N, K, ep, s);
+    return run_gemv<8>(a, W, M, N, K, ep, s);
+  }
   if (w_dtype == 1) return dispatch_epi<bf16_t>(epi, asrc, a, W, M, N, K, ep, s);
   return dispatch_epi<float>(epi, asrc, a, W, M, N, K, ep, s);
 }
